@@ -1,0 +1,28 @@
+"""Build the CPU oracle shared library (plain C, gcc, OpenMP).
+
+Test infrastructure: the oracle is the checker, never part of the product
+path.  ``build()`` always recompiles.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "dwconv_oracle.c")
+LIB = os.path.join(HERE, "libdwconv_oracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    # -O2 without -march=native: the library is built here and run on other
+    # hosts; -ffp-contract=off keeps every multiply and add a separate
+    # double-precision rounding, as the source reads.
+    cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC",
+           "-shared", "-o", LIB + ".tmp", SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
