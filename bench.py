@@ -1,0 +1,256 @@
+"""Benchmark: depthwise conv2d forward + input gradient on one MI355X.
+
+A step is one forward and one input gradient of the 512x512x256 3x3 NHWC
+workload (fp32 activations and weights), inputs resident in HBM.  The JSON
+line reports whole-step effective HBM bandwidth (algorithmic bytes: x+y+W+b
+for the forward, dy+dx+W for the input gradient), the roofline of the
+dominant kernel timed with HIP events on its own stream, the CPU oracle timed
+on a bounded sample, and a per-workload table (forward and input gradient,
+both layouts, back-to-back "warm" and cache-flushed "cold" kernel times).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-table] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+HEADLINE = "large_512x512x256_3x3"
+KERNEL_SRC = os.path.join(ROOT, "depthwise_convolution_amd", "csrc", "dwconv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_large_512x512x256_3x3_nhwc.json")
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    with open(KERNEL_SRC, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(op):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE, scaled by a copy-kernel calibration), or None when the counts
+    are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    rec = t.get("ops", {}).get(op)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def to_dev(torch, a):
+    return torch.from_numpy(a).to("cuda")
+
+
+def make_problem(torch, wl, layout, seed=0):
+    from depthwise_convolution_amd import workloads
+    inp = workloads.make_inputs(wl, layout, seed=seed)
+    t = {k: (None if v is None else to_dev(torch, v)) for k, v in inp.items()}
+    shape_x = tuple(inp["x"].shape)
+    t["y"] = torch.empty(tuple(inp["dy"].shape), dtype=torch.float32, device="cuda")
+    t["dx"] = torch.empty(shape_x, dtype=torch.float32, device="cuda")
+    return t
+
+
+def launch_fwd(dw, wl, t, layout, stream):
+    dw.dwconv2d_fwd(t["x"], t["w"], t["b"], t["y"], wl.stride, wl.dilation, layout, stream)
+
+
+def launch_ig(dw, wl, t, layout, stream):
+    dw.dwconv2d_input_grad(t["dy"], t["w"], t["dx"], wl.stride, wl.dilation, layout, stream)
+
+
+def time_kernel(torch, fn, stream, iters, flush=None):
+    """Per-launch kernel time (us) from HIP events recorded on `stream`."""
+    times = []
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    with torch.cuda.stream(stream):
+        for i in range(iters):
+            if flush is not None:
+                flush.add_(1.0)          # 1 GiB read+write: evicts L2 and the 256 MB MALL
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+    stream.synchronize()
+    for s, e in zip(starts, ends):
+        times.append(s.elapsed_time(e) * 1000.0)
+    return times
+
+
+def cpu_baseline(wl, rows=128):
+    """The oracle (as it stands) on the first `rows` rows of the workload's
+    image, forward and input gradient, scaled to the whole step."""
+    import numpy as np
+    import oracle
+    from depthwise_convolution_amd import workloads
+    sub = workloads.Workload(name=wl.name + "_rows", N=wl.N, H=rows, W=wl.W, C=wl.C, kH=wl.kH,
+                             kW=wl.kW, stride=wl.stride, dilation=wl.dilation)
+    inp = workloads.make_inputs(sub, workloads.NHWC, seed=0)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, workloads.NHWC,
+               nthreads=threads)
+    oracle.input_grad(inp["dy"], inp["w"], rows, wl.W, wl.stride, wl.dilation, workloads.NHWC,
+                      nthreads=threads)
+    dt = time.perf_counter() - t0
+    scale = wl.H / rows
+    step_s = dt * scale
+    gbs = (wl.fwd_bytes() + wl.ig_bytes()) / step_s / 1e9
+    del np
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image (1/{scale:g} of "
+                      f"the outputs), forward + input gradient, fp64 oracle, time scaled x{scale:g}",
+            "sample_seconds": round(dt, 3), "ms_per_step_est": round(step_s * 1e3, 1)}
+
+
+def per_config_table(torch, dw, iters=20):
+    from depthwise_convolution_amd import workloads
+    rows = []
+    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")   # 1 GiB
+    stream = torch.cuda.Stream()
+    for name, wl in workloads.WORKLOADS.items():
+        if "parity_only" in wl.tags:
+            continue
+        for layout in (workloads.NHWC, workloads.NCHW):
+            t = make_problem(torch, wl, layout, seed=0)
+            for op, fn, nbytes in (("fwd", launch_fwd, wl.fwd_bytes()),
+                                   ("ig", launch_ig, wl.ig_bytes())):
+                call = (lambda f=fn: f(dw, wl, t, layout, stream))
+                kname = dw.dwconv2d_describe(dw.OP_FWD if op == "fwd" else dw.OP_INPUT_GRAD,
+                                             wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
+                                             wl.dilation, layout, int(wl.fp16_weights),
+                                             op == "fwd")[0]
+                time_kernel(torch, call, stream, 3)
+                warm = statistics.median(time_kernel(torch, call, stream, iters))
+                cold = statistics.median(time_kernel(torch, call, stream, max(5, iters // 4),
+                                                     flush))
+                rows.append({"workload": name, "layout": workloads.LAYOUT_NAMES[layout],
+                             "op": op, "kernel": kname, "bytes": nbytes,
+                             "warm_us": round(warm, 2), "cold_us": round(cold, 2),
+                             "warm_GBs": round(nbytes / warm / 1e3, 1),
+                             "cold_GBs": round(nbytes / cold / 1e3, 1),
+                             "cold_pct_peak": round(100 * nbytes / cold / 1e3 / PEAK_HBM_GBS, 1)})
+            del t
+        _log(f"[table] {name} done")
+    del flush
+    return rows
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-table", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the operator shards over N and C with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import depthwise_convolution_amd as dw
+    from depthwise_convolution_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dw.lib()
+    wl = workloads.WORKLOADS[HEADLINE]
+    layout = workloads.NHWC
+    _log(f"[bench] generating {HEADLINE} inputs")
+    t = make_problem(torch, wl, layout, seed=0)
+    stream = torch.cuda.Stream()
+
+    def step():
+        launch_fwd(dw, wl, t, layout, stream)
+        launch_ig(dw, wl, t, layout, stream)
+
+    _log("[bench] warmup")
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, wall clock between device-wide synchronisations,
+    # plus HIP events on the launch stream around every kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            launch_fwd(dw, wl, t, layout, stream)
+            ev[i][1].record(stream)
+            launch_ig(dw, wl, t, layout, stream)
+            ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    ig_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    _log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms")
+
+    step_bytes = wl.fwd_bytes() + wl.ig_bytes()
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    fwd_avg, ig_avg = statistics.mean(fwd_us), statistics.mean(ig_us)
+    dom, dom_us, dom_bytes = (("fwd", fwd_avg, wl.fwd_bytes()) if fwd_avg >= ig_avg
+                              else ("ig", ig_avg, wl.ig_bytes()))
+    dom_kernel = dw.dwconv2d_describe(dw.OP_FWD if dom == "fwd" else dw.OP_INPUT_GRAD, wl.N,
+                                      wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation,
+                                      layout, 0, dom == "fwd")[0]
+    achieved = dom_bytes / dom_us / 1e3
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(dom), "kernel": dom_kernel,
+                "avg_launch_us": round(dom_us, 2),
+                "algorithmic_bytes_per_launch": dom_bytes}
+
+    result = {
+        "metric": "effective HBM bandwidth of depthwise conv2d forward + input-gradient "
+                  "(x+y+W+b and dy+dx+W bytes)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic, seeded numpy: x, dy ~ N(0,1); W ~ N(0,1/9); b ~ U(-0.1,0.1)",
+        "config": {"workload": HEADLINE, "N": wl.N, "H": wl.H, "W": wl.W, "C": wl.C,
+                   "kernel": f"{wl.kH}x{wl.kW}", "stride": wl.stride, "dilation": wl.dilation,
+                   "layout": "nhwc", "weights": "f32"},
+        "fwd_us": round(fwd_avg, 2), "ig_us": round(ig_avg, 2),
+        "fwd_pct_peak": round(100 * wl.fwd_bytes() / fwd_avg / 1e3 / PEAK_HBM_GBS, 1),
+        "ig_pct_peak": round(100 * wl.ig_bytes() / ig_avg / 1e3 / PEAK_HBM_GBS, 1),
+        "roofline": roofline,
+    }
+    del t
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        _log("[bench] cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        result["cpu_baseline"] = None
+    if not args.no_table:
+        _log("[bench] per-workload table")
+        result["per_config"] = per_config_table(torch, dw)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

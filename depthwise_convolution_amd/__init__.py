@@ -1,1 +1,229 @@
-"""Depthwise 2-D convolution for MI355X (gfx950): binding to the HIP library."""
+"""Depthwise 2-D convolution for MI355X (gfx950): Python binding of libdwconv.
+
+The binding only marshals arguments: every step of the computation runs in
+the HIP kernels of ``libdwconv.so`` (see ``include/dwconv.h`` for the C ABI).
+PyTorch provides device memory and the current stream.  If the library has
+not been built, every call raises ``RuntimeError``: there is no fallback.
+
+Names mirror the C ABI: ``dwconv2d_fwd``, ``dwconv2d_input_grad``,
+``dwconv2d_launch``, ``dwconv2d_describe``, ``dwconv2d_strerror``,
+``dwconv2d_version``; ``fwd`` and ``input_grad`` are the same calls with the
+output allocated here.
+
+Tensor shapes: NHWC tensors are ``(N, H, W, C)``, NCHW tensors
+``(N, C, H, W)``; weights ``(C, kH, kW)`` float32 or float16; bias ``(C,)``.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdwconv.so")
+
+# enumerations of include/dwconv.h
+NHWC, NCHW = 0, 1
+W_F32, W_F16 = 0, 1
+OP_FWD, OP_INPUT_GRAD = 0, 1
+STRATEGY_AUTO, STRATEGY_DIRECT, STRATEGY_TILED = 0, 1, 2
+STATUS = {
+    0: "OK", -1: "NULL_PTR", -2: "BAD_DIM", -3: "BAD_STRIDE", -4: "BAD_DILATION",
+    -5: "EVEN_KERNEL", -6: "BAD_LAYOUT", -7: "BAD_WTYPE", -8: "ALIAS", -9: "MISALIGNED",
+    -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY",
+}
+EXPORTS = ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
+           "dwconv2d_strerror", "dwconv2d_version")
+
+_lib = None
+
+
+class DwconvError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_strerror(status)})")
+
+
+def lib():
+    """The loaded libdwconv.so (ctypes), with argument types set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libdwconv.so not found at {LIB_PATH}: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()'); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    i, vp, ll = ctypes.c_int, ctypes.c_void_p, ctypes.c_longlong
+    L.dwconv2d_fwd.argtypes = [vp, vp, i, vp, vp] + [i] * 9 + [vp]
+    L.dwconv2d_input_grad.argtypes = [vp, vp, i, vp] + [i] * 9 + [vp]
+    L.dwconv2d_launch.argtypes = [i, vp, vp, i, vp, vp] + [i] * 10 + [vp]
+    L.dwconv2d_describe.argtypes = [i] * 13 + [ctypes.c_char_p, i, ctypes.POINTER(ll),
+                                               ctypes.POINTER(i)]
+    L.dwconv2d_strerror.argtypes = [i]
+    L.dwconv2d_strerror.restype = ctypes.c_char_p
+    for f in ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
+              "dwconv2d_version"):
+        getattr(L, f).restype = i
+    _lib = L
+    return L
+
+
+def _strerror(status):
+    try:
+        return lib().dwconv2d_strerror(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def dwconv2d_strerror(status):
+    return _strerror(status)
+
+
+def dwconv2d_version():
+    return lib().dwconv2d_version()
+
+
+# ---------------------------------------------------------------- marshalling
+def _layout_code(layout):
+    if layout in (NHWC, "nhwc", "NHWC"):
+        return NHWC
+    if layout in (NCHW, "nchw", "NCHW"):
+        return NCHW
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def _dims(t, layout):
+    if t.dim() != 4:
+        raise ValueError("activation tensors must be 4-D")
+    if layout == NHWC:
+        n, h, w, c = t.shape
+    else:
+        n, c, h, w = t.shape
+    return int(n), int(h), int(w), int(c)
+
+
+def _shape(layout, n, h, w, c):
+    return (n, h, w, c) if layout == NHWC else (n, c, h, w)
+
+
+def _check_dev(t, name, dtypes):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _wtype(w):
+    import torch
+    _check_dev(w, "w", (torch.float32, torch.float16))
+    if w.dim() != 3:
+        raise ValueError("w must be (C, kH, kW)")
+    return W_F16 if w.dtype == torch.float16 else W_F32
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_status(st, what):
+    if st != 0:
+        raise DwconvError(st, what)
+
+
+def _prepare(op, inp, w, b, out, H, W, stride, dilation, layout):
+    import torch
+    lay = _layout_code(layout)
+    _check_dev(inp, "input", (torch.float32,))
+    _check_dev(out, "output", (torch.float32,))
+    wt = _wtype(w)
+    C, kH, kW = (int(v) for v in w.shape)
+    if b is not None:
+        _check_dev(b, "b", (torch.float32,))
+        if tuple(b.shape) != (C,):
+            raise ValueError("b must be (C,)")
+    Ho, Wo = -(-H // stride), -(-W // stride)
+    N = int(inp.shape[0])
+    big, small = _shape(lay, N, H, W, C), _shape(lay, N, Ho, Wo, C)
+    want_in, want_out = (big, small) if op == OP_FWD else (small, big)
+    if tuple(inp.shape) != want_in or tuple(out.shape) != want_out:
+        raise ValueError(f"shape mismatch: input {tuple(inp.shape)} (want {want_in}), "
+                         f"output {tuple(out.shape)} (want {want_out})")
+    if not (inp.device == out.device == w.device) or (b is not None and b.device != out.device):
+        raise ValueError("all tensors must be on the same device")
+    return lay, wt, N, C, kH, kW
+
+
+def dwconv2d_launch(op, inp, w, b, out, H, W, stride=1, dilation=1, layout=NHWC,
+                    strategy=STRATEGY_AUTO, stream=None):
+    """Enqueue op (OP_FWD / OP_INPUT_GRAD) under `strategy` into `out`."""
+    lay, wt, N, C, kH, kW = _prepare(op, inp, w, b, out, H, W, stride, dilation, layout)
+    st = lib().dwconv2d_launch(op, _ptr(inp), _ptr(w), wt, _ptr(b), _ptr(out), N, H, W, C,
+                               kH, kW, stride, dilation, lay, strategy, _stream(out, stream))
+    _check_status(st, "dwconv2d_launch")
+    return out
+
+
+def dwconv2d_fwd(x, w, b, y, stride=1, dilation=1, layout=NHWC, stream=None):
+    """y = depthwise_conv(x; w, b), written into the preallocated y."""
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    lay, wt, N, C, kH, kW = _prepare(OP_FWD, x, w, b, y, H, W, stride, dilation, lay)
+    st = lib().dwconv2d_fwd(_ptr(x), _ptr(w), wt, _ptr(b), _ptr(y), N, H, W, C, kH, kW,
+                            stride, dilation, lay, _stream(y, stream))
+    _check_status(st, "dwconv2d_fwd")
+    return y
+
+
+def dwconv2d_input_grad(dy, w, dx, stride=1, dilation=1, layout=NHWC, stream=None):
+    """dx = input gradient of depthwise_conv for cotangent dy, into preallocated dx."""
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(dx, lay)
+    lay, wt, N, C, kH, kW = _prepare(OP_INPUT_GRAD, dy, w, None, dx, H, W, stride, dilation,
+                                     lay)
+    st = lib().dwconv2d_input_grad(_ptr(dy), _ptr(w), wt, _ptr(dx), N, H, W, C, kH, kW,
+                                   stride, dilation, lay, _stream(dx, stream))
+    _check_status(st, "dwconv2d_input_grad")
+    return dx
+
+
+def dwconv2d_describe(op, N, H, W, C, kH, kW, stride=1, dilation=1, layout=NHWC,
+                      wtype=W_F32, has_bias=False, strategy=STRATEGY_AUTO):
+    """(kernel name, grid, block) that a launch with these arguments would use."""
+    name = ctypes.create_string_buffer(128)
+    grid, block = ctypes.c_longlong(0), ctypes.c_int(0)
+    st = lib().dwconv2d_describe(op, wtype, int(bool(has_bias)), N, H, W, C, kH, kW, stride,
+                                 dilation, _layout_code(layout), strategy, name, 128,
+                                 ctypes.byref(grid), ctypes.byref(block))
+    _check_status(st, "dwconv2d_describe")
+    return name.value.decode(), grid.value, block.value
+
+
+# ------------------------------------------------------------- conveniences
+def fwd(x, w, b=None, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY_AUTO, stream=None):
+    """Allocate y and run the forward pass."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    y = torch.empty(_shape(lay, N, -(-H // stride), -(-W // stride), C), dtype=torch.float32,
+                    device=x.device)
+    return dwconv2d_launch(OP_FWD, x, w, b, y, H, W, stride, dilation, lay, strategy, stream)
+
+
+def input_grad(dy, w, H, W, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY_AUTO,
+               stream=None):
+    """Allocate dx of forward-input extents (H, W) and run the input gradient."""
+    import torch
+    lay = _layout_code(layout)
+    N, _, _, C = _dims(dy, lay)
+    dx = torch.empty(_shape(lay, N, H, W, C), dtype=torch.float32, device=dy.device)
+    return dwconv2d_launch(OP_INPUT_GRAD, dy, w, None, dx, H, W, stride, dilation, lay,
+                           strategy, stream)

@@ -1,0 +1,164 @@
+// dwconv_api.cpp -- the extern "C" entry points of libdwconv (include/dwconv.h).
+//
+// Order of work in every entry point: validate the arguments (pointers,
+// alignment, overlap, dimensions, enums) without touching the GPU, make the
+// plan, then enqueue one kernel.  Rejecting an unsupported configuration up
+// front follows the pages' lesson that a late failure (a verifier error deep
+// in a compiler pipeline, Reactant.jl issue #331) is worse than an early
+// ValueError (ExecuTorch's MLX conv-transpose weight path).
+#include "../../include/dwconv.h"
+#include "dwconv_internal.h"
+
+#include <cstdint>
+#include <cstring>
+
+using dwconv::Plan;
+using dwconv::Problem;
+
+namespace {
+
+struct Range {
+    std::uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void *p, long long bytes)
+{
+    const std::uintptr_t lo = reinterpret_cast<std::uintptr_t>(p);
+    return Range{lo, lo + static_cast<std::uintptr_t>(bytes)};
+}
+
+int check_pointers(const Problem &p, const float *in, const void *w, const float *b,
+                   const float *out)
+{
+    if (!in || !w || !out)
+        return DWCONV_ERR_NULL_PTR;
+    const std::uintptr_t f32_bits = reinterpret_cast<std::uintptr_t>(in) |
+                                    reinterpret_cast<std::uintptr_t>(out) |
+                                    reinterpret_cast<std::uintptr_t>(b);
+    if ((f32_bits & 3u) != 0)
+        return DWCONV_ERR_MISALIGNED;
+    const std::uintptr_t wbits = reinterpret_cast<std::uintptr_t>(w);
+    if ((p.wtype == DWCONV_W_F32 && (wbits & 3u)) || (wbits & 1u))
+        return DWCONV_ERR_MISALIGNED;
+    const long long Ho = (p.H + p.stride - 1) / p.stride, Wo = (p.W + p.stride - 1) / p.stride;
+    const long long big = 4LL * p.N * p.H * p.W * p.C, small = 4LL * p.N * Ho * Wo * p.C;
+    const long long in_bytes = p.op == DWCONV_OP_FWD ? big : small;
+    const long long out_bytes = p.op == DWCONV_OP_FWD ? small : big;
+    const long long w_bytes = (long long)p.C * p.kH * p.kW * (p.wtype == DWCONV_W_F16 ? 2 : 4);
+    const Range o = range_of(out, out_bytes);
+    if (overlap(o, range_of(in, in_bytes)) || overlap(o, range_of(w, w_bytes)))
+        return DWCONV_ERR_ALIAS;
+    if (b && overlap(o, range_of(b, 4LL * p.C)))
+        return DWCONV_ERR_ALIAS;
+    return DWCONV_OK;
+}
+
+int run(const Problem &p, const float *in, const void *w, const float *b, float *out,
+        int strategy, void *stream)
+{
+    int st = dwconv::validate_problem(p);
+    if (st != DWCONV_OK)
+        return st;
+    if (p.op == DWCONV_OP_INPUT_GRAD && b)
+        return DWCONV_ERR_BAD_OP;
+    st = check_pointers(p, in, w, b, out);
+    if (st != DWCONV_OK)
+        return st;
+    Plan pl;
+    const std::uintptr_t bits = reinterpret_cast<std::uintptr_t>(in) |
+                                reinterpret_cast<std::uintptr_t>(out);
+    st = dwconv::make_plan(p, strategy, bits, &pl);
+    if (st != DWCONV_OK)
+        return st;
+    return dwconv::launch_plan(p, pl, in, w, b, out, stream);
+}
+
+Problem problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int kH, int kW,
+                int stride, int dilation, int layout)
+{
+    Problem p;
+    p.op = op; p.wtype = wtype; p.layout = layout; p.has_bias = has_bias;
+    p.N = N; p.H = H; p.W = W; p.C = C; p.kH = kH; p.kW = kW;
+    p.stride = stride; p.dilation = dilation;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dwconv2d_fwd(const float *x, const void *w, int wtype, const float *b, float *y,
+                 int N, int H, int W, int C, int kH, int kW,
+                 int stride, int dilation, int layout, void *stream)
+{
+    const Problem p = problem(DWCONV_OP_FWD, wtype, b != nullptr, N, H, W, C, kH, kW,
+                              stride, dilation, layout);
+    return run(p, x, w, b, y, DWCONV_STRATEGY_AUTO, stream);
+}
+
+int dwconv2d_input_grad(const float *dy, const void *w, int wtype, float *dx,
+                        int N, int H, int W, int C, int kH, int kW,
+                        int stride, int dilation, int layout, void *stream)
+{
+    const Problem p = problem(DWCONV_OP_INPUT_GRAD, wtype, 0, N, H, W, C, kH, kW,
+                              stride, dilation, layout);
+    return run(p, dy, w, nullptr, dx, DWCONV_STRATEGY_AUTO, stream);
+}
+
+int dwconv2d_launch(int op, const float *in, const void *w, int wtype, const float *b,
+                    float *out, int N, int H, int W, int C, int kH, int kW,
+                    int stride, int dilation, int layout, int strategy, void *stream)
+{
+    const Problem p = problem(op, wtype, b != nullptr, N, H, W, C, kH, kW, stride, dilation,
+                              layout);
+    return run(p, in, w, b, out, strategy, stream);
+}
+
+int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int C,
+                      int kH, int kW, int stride, int dilation, int layout, int strategy,
+                      char *name, int name_len, long long *grid, int *block)
+{
+    const Problem p = problem(op, wtype, has_bias, N, H, W, C, kH, kW, stride, dilation,
+                              layout);
+    if (op == DWCONV_OP_INPUT_GRAD && has_bias)
+        return DWCONV_ERR_BAD_OP;
+    Plan pl;
+    const int st = dwconv::make_plan(p, strategy, 0, &pl);
+    if (st != DWCONV_OK)
+        return st;
+    if (name && name_len > 0) {
+        std::strncpy(name, pl.name, (size_t)name_len - 1);
+        name[name_len - 1] = '\0';
+    }
+    if (grid)
+        *grid = pl.grid;
+    if (block)
+        *block = pl.block;
+    return DWCONV_OK;
+}
+
+const char *dwconv2d_strerror(int status)
+{
+    switch (status) {
+    case DWCONV_OK: return "ok";
+    case DWCONV_ERR_NULL_PTR: return "null tensor pointer";
+    case DWCONV_ERR_BAD_DIM: return "bad dimension (< 1, or a tensor of 2^31 or more elements)";
+    case DWCONV_ERR_BAD_STRIDE: return "stride must be 1 or 2";
+    case DWCONV_ERR_BAD_DILATION: return "dilation must be >= 1 and d*(k-1) < 65536";
+    case DWCONV_ERR_EVEN_KERNEL: return "kernel extents must be odd (SAME padding)";
+    case DWCONV_ERR_BAD_LAYOUT: return "unknown layout";
+    case DWCONV_ERR_BAD_WTYPE: return "unknown weight type";
+    case DWCONV_ERR_ALIAS: return "output overlaps an input";
+    case DWCONV_ERR_MISALIGNED: return "misaligned tensor pointer";
+    case DWCONV_ERR_LAUNCH: return "kernel launch failed";
+    case DWCONV_ERR_BAD_OP: return "unknown op, or a bias given to the input gradient";
+    case DWCONV_ERR_BAD_STRATEGY: return "unknown strategy, or it does not apply to this problem";
+    default: return "unknown status";
+    }
+}
+
+int dwconv2d_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// dwconv_internal.h -- problem description, launch plan and the planner /
+// launcher interface shared by the host translation units of libdwconv.
+//
+// The planner (dwconv_plan.cpp) is plain C++ with no HIP runtime call, so the
+// validation and kernel selection it does can run on a host without a GPU.
+// The launcher (dwconv_kernels.hip) turns a plan into one kernel launch.
+#pragma once
+
+#include <cstdint>
+
+namespace dwconv {
+
+// One depthwise problem, as the C ABI receives it (see include/dwconv.h).
+struct Problem {
+    int op;        // DWCONV_OP_FWD or DWCONV_OP_INPUT_GRAD
+    int wtype;     // DWCONV_W_F32 / DWCONV_W_F16
+    int layout;    // DWCONV_LAYOUT_NHWC / DWCONV_LAYOUT_NCHW
+    int has_bias;
+    int N, H, W, C, kH, kW, stride, dilation;
+};
+
+enum Kind {
+    KIND_DIRECT_NHWC = 1,  // one thread per (n, row, col, channel vector); taps from global
+    KIND_DIRECT_NCHW = 2,  // one thread per (n, channel, row, col); taps from global
+    KIND_TILED_NHWC = 3,   // stride 1: LDS row chunks with halo, rolling row accumulators
+    KIND_TILED_NCHW = 4,   // stride 1: LDS row chunks of one plane, rolling row accumulators
+};
+
+// Compile-time shapes the tiled kernels are instantiated for.  A tiled plan
+// exists only for a (kH, kW, dilation) listed here; everything else runs the
+// direct kernels.  `vec` is the channels per thread of the NHWC kernel and
+// `gm` the number of window heights (R = (kH-1)*d + 1 rows) staged per LDS
+// chunk.
+struct TiledShape { int kH, kW, d, vec, gm; };
+constexpr TiledShape kTiledShapes[] = {
+    {3, 3, 1, 4, 2},
+    {5, 5, 1, 4, 1},
+    {7, 7, 1, 2, 1},
+    {7, 7, 2, 2, 1},
+    {1, 15, 1, 4, 4},
+    {1, 31, 1, 2, 4},
+};
+constexpr int kNumTiledShapes = sizeof(kTiledShapes) / sizeof(kTiledShapes[0]);
+
+// Output columns per thread of the tiled NCHW kernel.
+constexpr int kNchwQ = 4;
+
+struct Plan {
+    int kind;
+    int vec;            // NHWC: channels per thread (4 or 1)
+    int shape;          // tiled: index into kTiledShapes
+    int cl;             // tiled NHWC: threads across channels (8 or 16)
+    int tw;             // tiled: output columns per tile
+    int th;             // tiled: output rows per strip
+    int nct, nwt, nst;  // tiled: channel tiles, column tiles, strips (NHWC); nct = planes for NCHW
+    int pH, pW;
+    int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
+    long long total;    // direct: number of threads doing work
+    long long grid;     // workgroups
+    int block;          // threads per workgroup
+    char name[96];
+};
+
+// Validate dimensions and enums (not pointers).  Returns a DWCONV_ status.
+int validate_problem(const Problem &p);
+
+// Choose the kernel and its launch geometry.  `ptr_bits` is the bitwise OR
+// of the tensor pointers' addresses (0 when unknown); vector widths are only
+// chosen when it shows 16-byte alignment.  Returns a DWCONV_ status.
+int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
+
+// Enqueue the kernel of a plan made by make_plan on `stream` (a hipStream_t).
+// Returns DWCONV_OK, or DWCONV_ERR_LAUNCH if the runtime reports an error.
+int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w,
+                const float *b, float *out, void *stream);
+
+}  // namespace dwconv

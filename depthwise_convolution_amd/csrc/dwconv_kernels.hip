@@ -1,0 +1,495 @@
+// dwconv_kernels.hip -- gfx950 kernels of depthwise 2-D convolution and the
+// launcher that runs a plan.
+//
+// What is computed (LeanMlir "Depthwise" page): the forward equation
+//   y[c,h,w] = b[c] + sum_{kh,kw} x[c, h*s + kh*d - pH, w*s + kw*d - pW] * W[c,kh,kw]
+// (one filter per channel, no channel sum, zero padding), and the input
+// gradient in its reversed-kernel form, with stride 2 handled as the
+// zero-upsampled cotangent (only upsampled positions that are multiples of s
+// carry a value).
+//
+// Design (gfx950, 64-wide waves, HBM-bound): the channel axis is a batch
+// axis, so there is no contraction for the matrix cores; each output is a
+// kH*kW-tap dot product done with fp32 FMAs (cubek-convolution "depthwise"
+// module: the contraction is over window taps only, channels innermost so
+// consecutive lanes read consecutive channels, and the pass is
+// bandwidth-bound).  Weights are widened to fp32 once per thread (f16 by
+// value, never by reinterpreting bytes: the ggml PR's CPU-backend bug).
+//
+//  * direct kernels: one thread per output (NCHW) or per 4-channel output
+//    vector (NHWC); taps read from global memory through the caches.  They
+//    cover every valid problem and are the reference-free fallback.
+//  * tiled NHWC kernel (stride 1): a workgroup owns a strip of output rows
+//    of a (column tile x channel tile); it streams the input rows the strip
+//    needs through LDS in chunks of G rows (the tile plus the (kW-1)*d
+//    column halo, zero-filled outside the image), each thread reads its kW
+//    horizontal taps per input row from LDS and folds the row into R =
+//    (kH-1)*d + 1 rolling accumulators, one per output row in flight, so
+//    every input element is fetched from HBM about once and reused for all
+//    kH*kW taps.  Global loads for chunk k+1 are issued before chunk k is
+//    computed.  Workgroups are remapped so each XCD (own L2) walks a
+//    contiguous range of tiles, keeping halo re-reads in one L2.
+//
+// The input gradient at stride 1 is the same kernel with the kernel taps
+// reversed (loaded reversed into registers) and no bias.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dwconv_internal.h"
+#include "../../include/dwconv.h"
+
+namespace dwconv {
+
+namespace {
+
+typedef _Float16 half_t;
+
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(half_t v) { return (float)v; }
+
+// Workgroup ids are handed to the 8 XCDs round-robin; give each XCD a
+// contiguous range of logical tiles (neighbouring tiles share halos and
+// should hit the same L2).
+__device__ __forceinline__ int xcd_logical_id(int b, int nb)
+{
+    const int q = nb >> 3, r = nb & 7;
+    const int xcd = b & 7, k = b >> 3;
+    return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+template <int V> struct VecT;
+template <> struct VecT<1> { typedef float type; };
+template <> struct VecT<2> { typedef float2 type; };
+template <> struct VecT<4> { typedef float4 type; };
+
+template <int V>
+__device__ __forceinline__ void load_vec(const float *p, float (&v)[V])
+{
+    typedef typename VecT<V>::type T;
+    const T t = *reinterpret_cast<const T *>(p);
+    const float *f = reinterpret_cast<const float *>(&t);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        v[i] = f[i];
+}
+
+template <int V>
+__device__ __forceinline__ void store_vec(float *p, const float (&v)[V])
+{
+    typedef typename VecT<V>::type T;
+    T t;
+    float *f = reinterpret_cast<float *>(&t);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        f[i] = v[i];
+    *reinterpret_cast<T *>(p) = t;
+}
+
+struct DirectArgs {
+    int N, C, kH, kW, d, pH, pW;
+    int IH, IW, OH, OW;   // extents of the tensor read and the tensor written
+    int total;            // threads that do work
+};
+
+// ---------------------------------------------------------------------------
+// Direct NHWC: thread = (n, oh, ow, V consecutive channels).
+// Forward:  out[oh,ow] = b + sum_taps in[oh*S + kh*d - pH, ow*S + kw*d - pW] * W[kh,kw]
+// Input grad: th = oh + kh*d - pH on the upsampled grid (extent OH); a tap
+//   contributes when th is inside and a multiple of S, reading in[th/S] with
+//   the reversed tap W[kH-1-kh, kW-1-kw].
+// ---------------------------------------------------------------------------
+template <typename WT, int V, bool IG, int S>
+__global__ __launch_bounds__(256) void k_direct_nhwc(const float *__restrict__ in,
+                                                     const WT *__restrict__ w,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ out, DirectArgs a)
+{
+    const unsigned gt = blockIdx.x * 256u + threadIdx.x;
+    if (gt >= (unsigned)a.total)
+        return;
+    int t = (int)gt;
+    const int CV = a.C / V;
+    const int cv = t % CV;
+    t /= CV;
+    const int ow = t % a.OW;
+    t /= a.OW;
+    const int oh = t % a.OH;
+    const int n = t / a.OH;
+    const int c0 = cv * V;
+    const int kk = a.kH * a.kW;
+
+    float acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+        acc[v] = (!IG && bias) ? bias[c0 + v] : 0.0f;
+
+    for (int kh = 0; kh < a.kH; ++kh) {
+        int ih;
+        if (!IG) {
+            ih = oh * S + kh * a.d - a.pH;
+            if (ih < 0 || ih >= a.IH)
+                continue;
+        } else {
+            const int th = oh + kh * a.d - a.pH;
+            if (th < 0 || th >= a.OH || (S == 2 && (th & 1)))
+                continue;
+            ih = th / S;
+        }
+        for (int kw = 0; kw < a.kW; ++kw) {
+            int iw;
+            if (!IG) {
+                iw = ow * S + kw * a.d - a.pW;
+                if (iw < 0 || iw >= a.IW)
+                    continue;
+            } else {
+                const int tw = ow + kw * a.d - a.pW;
+                if (tw < 0 || tw >= a.OW || (S == 2 && (tw & 1)))
+                    continue;
+                iw = tw / S;
+            }
+            float xv[V];
+            load_vec<V>(in + ((n * a.IH + ih) * a.IW + iw) * a.C + c0, xv);
+            const int tap = IG ? (a.kH - 1 - kh) * a.kW + (a.kW - 1 - kw) : kh * a.kW + kw;
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                acc[v] = fmaf(widen(w[(c0 + v) * kk + tap]), xv[v], acc[v]);
+        }
+    }
+    store_vec<V>(out + ((n * a.OH + oh) * a.OW + ow) * a.C + c0, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Direct NCHW: thread = (n, c, oh, ow), consecutive threads along ow.
+// ---------------------------------------------------------------------------
+template <typename WT, bool IG, int S>
+__global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ in,
+                                                     const WT *__restrict__ w,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ out, DirectArgs a)
+{
+    const unsigned gt = blockIdx.x * 256u + threadIdx.x;
+    if (gt >= (unsigned)a.total)
+        return;
+    int t = (int)gt;
+    const int ow = t % a.OW;
+    t /= a.OW;
+    const int oh = t % a.OH;
+    t /= a.OH;
+    const int c = t % a.C;
+    const int n = t / a.C;
+    const int kk = a.kH * a.kW;
+    const float *plane = in + (n * a.C + c) * (a.IH * a.IW);
+    const WT *wc = w + c * kk;
+    float acc = (!IG && bias) ? bias[c] : 0.0f;
+    for (int kh = 0; kh < a.kH; ++kh) {
+        int ih;
+        if (!IG) {
+            ih = oh * S + kh * a.d - a.pH;
+            if (ih < 0 || ih >= a.IH)
+                continue;
+        } else {
+            const int th = oh + kh * a.d - a.pH;
+            if (th < 0 || th >= a.OH || (S == 2 && (th & 1)))
+                continue;
+            ih = th / S;
+        }
+        for (int kw = 0; kw < a.kW; ++kw) {
+            int iw;
+            if (!IG) {
+                iw = ow * S + kw * a.d - a.pW;
+                if (iw < 0 || iw >= a.IW)
+                    continue;
+            } else {
+                const int tw = ow + kw * a.d - a.pW;
+                if (tw < 0 || tw >= a.OW || (S == 2 && (tw & 1)))
+                    continue;
+                iw = tw / S;
+            }
+            const int tap = IG ? (a.kH - 1 - kh) * a.kW + (a.kW - 1 - kw) : kh * a.kW + kw;
+            acc = fmaf(widen(wc[tap]), plane[ih * a.IW + iw], acc);
+        }
+    }
+    out[((n * a.C + c) * a.OH + oh) * a.OW + ow] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Tiled NHWC, stride 1 (forward, or input gradient with reversed taps).
+// ---------------------------------------------------------------------------
+struct TiledArgs {
+    int N, C, H, W;         // image extents (input and output agree at stride 1)
+    int pH, pW;
+    int TH;                 // output rows per strip
+    int nct, nwt, nst;      // channel tiles, column tiles, strips
+    int nblocks;
+};
+
+template <int KH, int KW, int D, int VEC, int CL, int GM>
+struct TiledGeom {
+    static constexpr int LV = 4;                    // floats per global load
+    static constexpr int R = (KH - 1) * D + 1;      // rows of one window
+    static constexpr int G = R * GM;                // input rows per LDS chunk
+    static constexpr int TW = 256 / CL;             // output columns per tile
+    static constexpr int CG = CL * VEC;             // channels per tile
+    static constexpr int TWI = TW + (KW - 1) * D;   // input columns per tile
+    static constexpr int VPC = CG / LV;             // float4 per LDS column
+    static constexpr int VPR = TWI * VPC;           // float4 per LDS row
+    static constexpr int VCH = G * VPR;             // float4 per chunk
+    static constexpr int NV = (VCH + 255) / 256;    // float4 per thread per chunk
+    static constexpr int LDS_BYTES = VCH * 16;
+};
+
+template <typename WT, int KH, int KW, int D, int VEC, int CL, int GM, bool IG>
+__global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__ in,
+                                                       const void *__restrict__ wv,
+                                                       const float *__restrict__ bias,
+                                                       float *__restrict__ out, TiledArgs a)
+{
+    typedef TiledGeom<KH, KW, D, VEC, CL, GM> Gm;
+    constexpr int R = Gm::R, G = Gm::G, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
+    constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV;
+    __shared__ float4 lds[VCH];
+    const float *ldsf = reinterpret_cast<const float *>(lds);
+    const WT *w = reinterpret_cast<const WT *>(wv);
+
+    int tile = xcd_logical_id(blockIdx.x, a.nblocks);
+    const int ct = tile % a.nct;
+    tile /= a.nct;
+    const int wt = tile % a.nwt;
+    tile /= a.nwt;
+    const int st = tile % a.nst;
+    const int n = tile / a.nst;
+    const int c0 = ct * CG, w0 = wt * TW, h0 = st * a.TH;
+
+    const int tid = threadIdx.x;
+    const int q = tid % CL, p = tid / CL;
+    const int cq = c0 + q * VEC;     // first channel of this thread
+    const bool cvalid = cq < a.C;    // C % 4 == 0, so the whole vector is valid
+    const int ow = w0 + p;
+
+    // per-thread weights (reversed for the input gradient) and bias
+    float wr[KH][KW][VEC];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
+                wr[kh][kw][v] = cvalid ? widen(w[(cq + v) * (KH * KW) + tap]) : 0.0f;
+            }
+    float bv[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v)
+        bv[v] = (!IG && bias && cvalid) ? bias[cq + v] : 0.0f;
+
+    float acc[R][VEC];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            acc[r][v] = bv[v];
+
+    const int th_eff = min(a.TH, a.H - h0);
+    const int nrows = th_eff + R - 1;          // input rows this strip reads
+    const int nchunks = (nrows + G - 1) / G;
+    const int rbase = h0 - a.pH;               // image row of strip input row 0
+    const int cbase = w0 - a.pW;               // image column of LDS column 0
+    const int HW = a.H * a.W;
+
+    float4 stage[NV];
+    auto load_chunk = [&](int k) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = tid + i * 256;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < VCH) {
+                const int g = e / VPR;
+                const int rem = e - g * VPR;
+                const int col = rem / VPC;
+                const int cv = rem - col * VPC;
+                const int j = k * G + g;
+                const int row = rbase + j;
+                const int gc = cbase + col;
+                const int ch = c0 + cv * 4;
+                if (j < nrows && row >= 0 && row < a.H && gc >= 0 && gc < a.W && ch < a.C)
+                    v = *reinterpret_cast<const float4 *>(
+                        in + ((n * a.H + row) * a.W + gc) * a.C + ch);
+            }
+            stage[i] = v;
+        }
+    };
+
+    float *outp = out + (n * HW) * a.C;
+    load_chunk(0);
+    for (int k = 0; k < nchunks; ++k) {
+        if (k > 0)
+            __syncthreads();                   // all reads of the previous chunk done
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = tid + i * 256;
+            if (e < VCH)
+                lds[e] = stage[i];
+        }
+        __syncthreads();
+        if (k + 1 < nchunks)
+            load_chunk(k + 1);                 // in flight while this chunk is computed
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const int j = k * G + u;
+            if (j < nrows) {
+                float xv[KW][VEC];
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw) {
+                    const float *src = ldsf + ((u * TWI + p + kw * D) * CG + q * VEC);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        xv[kw][v] = src[v];
+                }
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh) {
+                    const int slot = ((u - kh * D) % R + R) % R;
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v)
+                            acc[slot][v] = fmaf(wr[kh][kw][v], xv[kw][v], acc[slot][v]);
+                }
+                // output row m = j - (R-1) has now received all its taps
+                const int done = (u + 1) % R;
+                const int m = j - (R - 1);
+                if (m >= 0 && cvalid && ow < a.W)
+                    store_vec<VEC>(outp + ((h0 + m) * a.W + ow) * a.C + cq, acc[done]);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    acc[done][v] = bv[v];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers
+// ---------------------------------------------------------------------------
+DirectArgs direct_args(const Problem &p, const Plan &pl)
+{
+    DirectArgs a;
+    a.N = p.N; a.C = p.C; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
+    a.pH = pl.pH; a.pW = pl.pW;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.total = (int)pl.total;
+    return a;
+}
+
+template <typename WT>
+void launch_direct(const Problem &p, const Plan &pl, const float *in, const void *wv,
+                   const float *b, float *out, hipStream_t st)
+{
+    const DirectArgs a = direct_args(p, pl);
+    const WT *w = reinterpret_cast<const WT *>(wv);
+    const dim3 grid((unsigned)pl.grid), block(256);
+    const bool ig = p.op == DWCONV_OP_INPUT_GRAD;
+    const int s = p.stride;
+#define DW_DIRECT_NHWC(V, IGV, SV) \
+    hipLaunchKernelGGL((k_direct_nhwc<WT, V, IGV, SV>), grid, block, 0, st, in, w, b, out, a)
+#define DW_DIRECT_NCHW(IGV, SV) \
+    hipLaunchKernelGGL((k_direct_nchw<WT, IGV, SV>), grid, block, 0, st, in, w, b, out, a)
+    if (pl.kind == KIND_DIRECT_NHWC) {
+        if (pl.vec == 4) {
+            if (!ig) { if (s == 1) DW_DIRECT_NHWC(4, false, 1); else DW_DIRECT_NHWC(4, false, 2); }
+            else     { if (s == 1) DW_DIRECT_NHWC(4, true, 1);  else DW_DIRECT_NHWC(4, true, 2); }
+        } else {
+            if (!ig) { if (s == 1) DW_DIRECT_NHWC(1, false, 1); else DW_DIRECT_NHWC(1, false, 2); }
+            else     { if (s == 1) DW_DIRECT_NHWC(1, true, 1);  else DW_DIRECT_NHWC(1, true, 2); }
+        }
+    } else {
+        if (!ig) { if (s == 1) DW_DIRECT_NCHW(false, 1); else DW_DIRECT_NCHW(false, 2); }
+        else     { if (s == 1) DW_DIRECT_NCHW(true, 1);  else DW_DIRECT_NCHW(true, 2); }
+    }
+#undef DW_DIRECT_NHWC
+#undef DW_DIRECT_NCHW
+}
+
+typedef void (*TiledFn)(const float *, const void *, const float *, float *, TiledArgs);
+
+// Kernel table for the tiled NHWC kernel: [shape][cl 8|16][f16w][ig].
+template <typename WT, int SH, int CL, bool IG>
+constexpr TiledFn tiled_fn()
+{
+    constexpr TiledShape t = kTiledShapes[SH];
+    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, CL, t.gm, IG>;
+}
+
+template <int SH>
+void fill_tiled_row(TiledFn (&row)[2][2][2])
+{
+    row[0][0][0] = tiled_fn<float, SH, 8, false>();
+    row[0][0][1] = tiled_fn<float, SH, 8, true>();
+    row[0][1][0] = tiled_fn<half_t, SH, 8, false>();
+    row[0][1][1] = tiled_fn<half_t, SH, 8, true>();
+    row[1][0][0] = tiled_fn<float, SH, 16, false>();
+    row[1][0][1] = tiled_fn<float, SH, 16, true>();
+    row[1][1][0] = tiled_fn<half_t, SH, 16, false>();
+    row[1][1][1] = tiled_fn<half_t, SH, 16, true>();
+}
+
+struct TiledTable {
+    TiledFn fn[kNumTiledShapes][2][2][2];
+    TiledTable()
+    {
+        static_assert(kNumTiledShapes == 6, "update the tiled kernel table");
+        fill_tiled_row<0>(fn[0]);
+        fill_tiled_row<1>(fn[1]);
+        fill_tiled_row<2>(fn[2]);
+        fill_tiled_row<3>(fn[3]);
+        fill_tiled_row<4>(fn[4]);
+        fill_tiled_row<5>(fn[5]);
+    }
+};
+
+int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const void *w,
+                      const float *b, float *out, hipStream_t st)
+{
+    static const TiledTable table;
+    if (pl.shape < 0 || pl.shape >= kNumTiledShapes || (pl.cl != 8 && pl.cl != 16))
+        return DWCONV_ERR_BAD_STRATEGY;
+    TiledFn f = table.fn[pl.shape][pl.cl == 16][p.wtype == DWCONV_W_F16]
+                        [p.op == DWCONV_OP_INPUT_GRAD];
+    TiledArgs a;
+    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.pH = pl.pH; a.pW = pl.pW;
+    a.TH = pl.th; a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
+    a.nblocks = (int)pl.grid;
+    hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
+                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a);
+    return DWCONV_OK;
+}
+
+}  // namespace
+
+// Run a validated plan on `stream`.  Returns a DWCONV_ status.
+int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w,
+                const float *b, float *out, void *stream_v)
+{
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    const float *bb = p.op == DWCONV_OP_FWD ? b : nullptr;
+    int st = DWCONV_OK;
+    switch (pl.kind) {
+    case KIND_DIRECT_NHWC:
+    case KIND_DIRECT_NCHW:
+        if (p.wtype == DWCONV_W_F16)
+            launch_direct<half_t>(p, pl, in, w, bb, out, stream);
+        else
+            launch_direct<float>(p, pl, in, w, bb, out, stream);
+        break;
+    case KIND_TILED_NHWC:
+        st = launch_tiled_nhwc(p, pl, in, w, bb, out, stream);
+        break;
+    default:
+        return DWCONV_ERR_BAD_STRATEGY;
+    }
+    if (st != DWCONV_OK)
+        return st;
+    return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
+}
+
+}  // namespace dwconv

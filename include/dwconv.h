@@ -1,0 +1,133 @@
+/*
+ * dwconv.h -- C ABI of the MI355X (gfx950) depthwise 2-D convolution library
+ * (libdwconv.so).  Plain pointers and sizes only.
+ *
+ * The operation (LeanMlir "Depthwise" page, forward equation, with stride s
+ * and dilation d, and the ggml CONV_2D_DW op of llama.cpp PR #21565 for the
+ * layouts and weight types):
+ *
+ *   y[n,c,ho,wo] = b[c] + sum_{kh<kH, kw<kW} x[n, c, ho*s + kh*d - pH,
+ *                                               wo*s + kw*d - pW] * W[c,kh,kw]
+ *
+ * one filter per channel and no sum over channels; positions outside the
+ * image contribute nothing (SAME zero padding), pH = d*(kH-1)/2,
+ * pW = d*(kW-1)/2, Ho = ceil(H/s), Wo = ceil(W/s).  Stride 2 keeps the even
+ * positions of the stride-1 result (LeanMlir "Depthwise", stride-2 SAME).
+ *
+ * Its input gradient (LeanMlir "Depthwise", reversed-kernel formula and the
+ * stride-2 input-VJP: zero-upsample dy onto the even positions, then the
+ * reversed-kernel stride-1 depthwise):
+ *
+ *   dx[n,c,h,w] = sum_{kh,kw} W[c, kH-1-kh, kW-1-kw] * u[n, c, h + kh*d - pH,
+ *                                                        w + kw*d - pW]
+ *   u[n,c,t,v]  = dy[n, c, t/s, v/s] if t and v are multiples of s, else 0.
+ *
+ * Shapes.  H and W are always the forward INPUT extents: x and dx are
+ * [N,H,W,C] (NHWC) or [N,C,H,W] (NCHW); y and dy are [N,Ho,Wo,C] or
+ * [N,C,Ho,Wo] in the same layout.  W (the weights) is [C][kH][kW] contiguous
+ * in both layouts, float32 or IEEE binary16; b is [C] float32 or NULL.
+ * Every tensor is dense in its layout (no strides).
+ *
+ * Ownership and execution.  All tensor pointers are DEVICE pointers owned by
+ * the caller.  The library allocates no memory and keeps no state between
+ * calls beyond a per-device property cache, so calls may be made from any
+ * host thread.  Work is enqueued asynchronously on `stream` (a hipStream_t;
+ * NULL means the default stream); a return of DWCONV_OK means "validated and
+ * enqueued".  The output (y or dx) is fully overwritten, never accumulated
+ * into.  Inputs and outputs must not overlap (no in-place operation).
+ *
+ * Errors.  Every argument is validated before anything is enqueued; a
+ * negative status means nothing was launched and the output is untouched.
+ */
+#ifndef DWCONV_H
+#define DWCONV_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define DWCONV_OK                0
+#define DWCONV_ERR_NULL_PTR     -1  /* input, weights or output pointer is NULL      */
+#define DWCONV_ERR_BAD_DIM      -2  /* N,H,W,C,kH,kW < 1, or a tensor has >= 2^31 elements */
+#define DWCONV_ERR_BAD_STRIDE   -3  /* stride not 1 or 2                             */
+#define DWCONV_ERR_BAD_DILATION -4  /* dilation < 1, or d*(k-1) >= 2^16              */
+#define DWCONV_ERR_EVEN_KERNEL  -5  /* kH or kW even: SAME padding needs an odd kernel */
+#define DWCONV_ERR_BAD_LAYOUT   -6  /* layout not NHWC or NCHW                       */
+#define DWCONV_ERR_BAD_WTYPE    -7  /* weight type not F32 or F16                    */
+#define DWCONV_ERR_ALIAS        -8  /* output bytes overlap an input's bytes         */
+#define DWCONV_ERR_MISALIGNED   -9  /* float pointer not 4-byte or half not 2-byte aligned */
+#define DWCONV_ERR_LAUNCH      -10  /* the HIP runtime reported an error at launch   */
+#define DWCONV_ERR_BAD_OP      -11  /* op not FWD or INPUT_GRAD                      */
+#define DWCONV_ERR_BAD_STRATEGY -12 /* strategy unknown, or not applicable to the problem */
+
+/* ---- enumerations (passed as int) -------------------------------------- */
+#define DWCONV_LAYOUT_NHWC 0   /* channel innermost (the ggml page's CWHN)    */
+#define DWCONV_LAYOUT_NCHW 1   /* channel outer     (the ggml page's WHCN)    */
+
+#define DWCONV_W_F32 0         /* weights are float32                         */
+#define DWCONV_W_F16 1         /* weights are IEEE binary16, widened exactly  */
+
+#define DWCONV_OP_FWD        0 /* y  = dwconv(x; W, b)                        */
+#define DWCONV_OP_INPUT_GRAD 1 /* dx = dwconv_input_grad(dy; W)               */
+
+/* Which tiling to run a problem under (cubek-convolution "depthwise" module:
+ * a strategy enum selects the tiling, one launch function runs it). */
+#define DWCONV_STRATEGY_AUTO   0 /* pick the fastest applicable kernel          */
+#define DWCONV_STRATEGY_DIRECT 1 /* one thread per output vector, taps from global memory;
+                                    applies to every valid problem               */
+#define DWCONV_STRATEGY_TILED  2 /* LDS-staged input rows with halo, register-blocked
+                                    output rows; applies where a tiled kernel exists
+                                    for the (layout, stride, kernel, dilation)    */
+
+/*
+ * Forward.  x: input [N,H,W,C] / [N,C,H,W] float32.  w: [C][kH][kW] of type
+ * wtype.  b: [C] float32 or NULL (no bias).  y: output [N,Ho,Wo,C] /
+ * [N,C,Ho,Wo] float32.  stride in {1,2}; dilation >= 1; kH, kW odd.
+ */
+int dwconv2d_fwd(const float *x, const void *w, int wtype, const float *b, float *y,
+                 int N, int H, int W, int C, int kH, int kW,
+                 int stride, int dilation, int layout, void *stream);
+
+/*
+ * Input gradient.  dy: [N,Ho,Wo,C] / [N,C,Ho,Wo] float32.  w as for the
+ * forward.  dx: output [N,H,W,C] / [N,C,H,W] float32.  H, W are the forward
+ * input extents.  No bias term.
+ */
+int dwconv2d_input_grad(const float *dy, const void *w, int wtype, float *dx,
+                        int N, int H, int W, int C, int kH, int kW,
+                        int stride, int dilation, int layout, void *stream);
+
+/*
+ * Either operation under an explicit strategy (DWCONV_STRATEGY_*).  `in` is
+ * x (forward) or dy (input gradient); `out` is y or dx; b must be NULL for
+ * the input gradient.  Same shapes, ownership and errors as above; an
+ * explicit strategy that does not apply returns DWCONV_ERR_BAD_STRATEGY.
+ */
+int dwconv2d_launch(int op, const float *in, const void *w, int wtype, const float *b,
+                    float *out, int N, int H, int W, int C, int kH, int kW,
+                    int stride, int dilation, int layout, int strategy, void *stream);
+
+/*
+ * Describe, without launching anything or touching the GPU, the kernel a
+ * dwconv2d_launch call with these arguments would run: writes a
+ * NUL-terminated kernel name (at most name_len bytes, truncated) into `name`
+ * and the grid and block sizes into grid[0], block[0] when those are not
+ * NULL.  Validates dimensions, stride, dilation, kernel size, layout, wtype,
+ * op and strategy as the launch would; pointer checks are skipped.
+ */
+int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int C,
+                      int kH, int kW, int stride, int dilation, int layout, int strategy,
+                      char *name, int name_len, long long *grid, int *block);
+
+/* Static text for a status code ("unknown status" for unknown codes). */
+const char *dwconv2d_strerror(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int dwconv2d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWCONV_H */

@@ -1,0 +1,176 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, and rejects every invalid argument before touching a device.
+
+Fake device addresses are used for the error paths; every call here returns
+before any HIP runtime call (validation comes first in every entry point).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import depthwise_convolution_amd as dw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dwconv.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dwconv2d_\w+)\s*\(", text)))
+
+
+def _header_defines():
+    return dict((m.group(1), int(m.group(2))) for m in
+                re.finditer(r"#define\s+(DWCONV_\w+)\s+(-?\d+)", open(HEADER).read()))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dw.LIB_PATH):
+        pytest.fail("libdwconv.so is not built (run __graft_entry__.build())")
+    return dw.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _header_functions()
+    assert set(names) == set(dw.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_constants_match_header():
+    d = _header_defines()
+    assert d["DWCONV_LAYOUT_NHWC"] == dw.NHWC and d["DWCONV_LAYOUT_NCHW"] == dw.NCHW
+    assert d["DWCONV_W_F32"] == dw.W_F32 and d["DWCONV_W_F16"] == dw.W_F16
+    assert d["DWCONV_OP_FWD"] == dw.OP_FWD and d["DWCONV_OP_INPUT_GRAD"] == dw.OP_INPUT_GRAD
+    assert d["DWCONV_STRATEGY_AUTO"] == dw.STRATEGY_AUTO
+    assert d["DWCONV_STRATEGY_DIRECT"] == dw.STRATEGY_DIRECT
+    assert d["DWCONV_STRATEGY_TILED"] == dw.STRATEGY_TILED
+    codes = {k[len("DWCONV_ERR_"):]: v for k, v in d.items() if k.startswith("DWCONV_ERR_")}
+    for name, v in codes.items():
+        assert dw.STATUS[v] == name
+
+
+def test_version_and_strerror(L):
+    assert L.dwconv2d_version() >= 100
+    for code in dw.STATUS:
+        s = L.dwconv2d_strerror(code).decode()
+        assert s and s != "unknown status"
+    assert L.dwconv2d_strerror(-999).decode() == "unknown status"
+
+
+# fake but well-aligned device addresses, far apart
+X, WP, B, Y = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000, 0x40_0000_0000
+VP = ctypes.c_void_p
+
+
+def _fwd(L, x=X, w=WP, wt=0, b=B, y=Y, N=1, H=8, W=8, C=4, kH=3, kW=3, s=1, d=1, lay=0):
+    return L.dwconv2d_fwd(VP(x) if x else None, VP(w) if w else None, wt,
+                          VP(b) if b else None, VP(y) if y else None,
+                          N, H, W, C, kH, kW, s, d, lay, None)
+
+
+def _ig(L, dy=X, w=WP, wt=0, dx=Y, N=1, H=8, W=8, C=4, kH=3, kW=3, s=1, d=1, lay=0):
+    return L.dwconv2d_input_grad(VP(dy) if dy else None, VP(w) if w else None, wt,
+                                 VP(dx) if dx else None, N, H, W, C, kH, kW, s, d, lay, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(x=0), -1), (dict(w=0), -1), (dict(y=0), -1),
+    (dict(N=0), -2), (dict(H=0), -2), (dict(W=-1), -2), (dict(C=0), -2), (dict(kH=0), -2),
+    (dict(N=2, H=1 << 15, W=1 << 15, C=1), -2),            # 2^31 elements
+    (dict(s=3), -3), (dict(s=0), -3),
+    (dict(d=0), -4), (dict(d=1 << 15, kH=5), -4),
+    (dict(kH=2), -5), (dict(kW=4), -5),
+    (dict(lay=2), -6), (dict(lay=-1), -6),
+    (dict(wt=2), -7),
+    (dict(y=X + 64), -8),                                  # output inside the input
+    (dict(y=WP - 32), -8),                                 # output runs into the weights
+    (dict(b=Y + 4), -8),                                   # bias inside the output
+    (dict(x=X + 2), -9), (dict(y=Y + 1), -9), (dict(b=B + 2), -9), (dict(w=WP + 2), -9),
+])
+def test_fwd_rejects(L, kwargs, code):
+    assert _fwd(L, **kwargs) == code
+
+
+def test_f16_weights_need_only_2_byte_alignment(L):
+    # a 2-byte aligned f16 pointer passes the alignment check and the call
+    # stops at the later overlap check; a 1-byte offset fails alignment
+    assert _fwd(L, w=WP + 2, wt=1, y=X + 64) == -8
+    assert _fwd(L, w=WP + 1, wt=1, y=X + 64) == -9
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dy=0), -1), (dict(dx=0), -1), (dict(H=0), -2), (dict(s=5), -3), (dict(d=-2), -4),
+    (dict(kW=6), -5), (dict(lay=3), -6), (dict(wt=-1), -7),
+    (dict(dx=X + 4), -8), (dict(dy=X + 1), -9),
+])
+def test_input_grad_rejects(L, kwargs, code):
+    assert _ig(L, **kwargs) == code
+
+
+def test_launch_rejects_bad_op_strategy_and_bias_on_input_grad(L):
+    args = [VP(X), VP(WP), 0, None, VP(Y), 1, 8, 8, 4, 3, 3, 1, 1, 0]
+    assert L.dwconv2d_launch(2, *args, 0, None) == -11
+    assert L.dwconv2d_launch(0, *args, 7, None) == -12
+    args_b = [VP(X), VP(WP), 0, VP(B), VP(Y), 1, 8, 8, 4, 3, 3, 1, 1, 0]
+    assert L.dwconv2d_launch(1, *args_b, 0, None) == -11
+    # a tiled strategy where no tiled kernel exists (9x9 kernel)
+    args9 = [VP(X), VP(WP), 0, None, VP(Y), 1, 32, 32, 16, 9, 9, 1, 1, 0]
+    assert L.dwconv2d_launch(0, *args9, 2, None) == -12
+
+
+# ------------------------------------------------------------- plan selection
+def test_describe_selects_kernels():
+    name, grid, block = dw.dwconv2d_describe(dw.OP_FWD, 1, 512, 512, 256, 3, 3)
+    assert name.startswith("tiled_nhwc_s1_k3x3_d1") and block == 256 and grid >= 1024
+    name, _, _ = dw.dwconv2d_describe(dw.OP_INPUT_GRAD, 1, 512, 512, 256, 3, 3)
+    assert name.startswith("tiled_nhwc_s1_k3x3_d1") and name.endswith("_ig_f32w")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 224, 224, 32, 3, 3, stride=2)
+    assert name.startswith("direct_nhwc_s2")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 30, 19, 131, 7, 7)
+    assert name.startswith("direct_nhwc_s1_v1")          # C % 4 != 0
+    name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 16, 16, 8, 3, 3)
+    assert name.startswith("direct_nhwc")                # too few channels for a tile
+    name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 16, 16, 8, 3, 3, strategy=dw.STRATEGY_TILED)
+    assert name.startswith("tiled_nhwc")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 56, 56, 128, 5, 5, wtype=dw.W_F16)
+    assert name.endswith("f16w")
+    name, grid, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 56, 56, 128, 5, 5,
+                                         strategy=dw.STRATEGY_DIRECT)
+    assert name.startswith("direct_nhwc_s1_v4") and grid == (56 * 56 * 32 + 255) // 256
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv2d_describe(dw.OP_FWD, 1, 8, 8, 4, 3, 3, stride=3)
+    assert e.value.status == -3
+
+
+@pytest.mark.parametrize("wl_name", ["large_512x512x256_3x3", "mobilenet_112x112x32_3x3",
+                                     "effnet_n32_56x56x128_5x5", "asr_n64_30x19x128_7x7_d2",
+                                     "asr_n64_1x24x256_1x31", "asr_n64_1x24x128_1x15"])
+def test_tiled_grid_covers_problem(wl_name):
+    """The tiled grid (strips x column tiles x channel tiles) covers every
+    output exactly: recompute it from the kernel name's tile sizes."""
+    from depthwise_convolution_amd.workloads import WORKLOADS
+    wl = WORKLOADS[wl_name]
+    name, grid, block = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                             wl.stride, wl.dilation)
+    assert name.startswith("tiled_nhwc")
+    vec = int(re.search(r"_v(\d+)_", name).group(1))
+    cl = int(re.search(r"_cl(\d+)_", name).group(1))
+    tw, cg = 256 // cl, cl * vec
+    nct, nwt = -(-wl.C // cg), -(-wl.W // tw)
+    assert grid % (wl.N * nct * nwt) == 0
+    nst = grid // (wl.N * nct * nwt)
+    th = -(-wl.H // nst)
+    assert (nst - 1) * th < wl.H <= nst * th
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 4, 4)
+    w = torch.zeros(4, 3, 3)
+    with pytest.raises(ValueError):
+        dw.fwd(x, w)
