@@ -93,12 +93,12 @@ def time_kernel(torch, fn, stream, iters, flush=None):
     return times
 
 
-def cpu_baseline(wl, rows=128):
+def cpu_baseline(wl, rows=None):
     """The oracle (as it stands) on the first `rows` rows of the workload's
     image, forward and input gradient, scaled to the whole step."""
-    import numpy as np
     import oracle
     from depthwise_convolution_amd import workloads
+    rows = wl.H if rows is None else rows
     sub = workloads.Workload(name=wl.name + "_rows", N=wl.N, H=rows, W=wl.W, C=wl.C, kH=wl.kH,
                              kW=wl.kW, stride=wl.stride, dilation=wl.dilation)
     inp = workloads.make_inputs(sub, workloads.NHWC, seed=0)
@@ -112,9 +112,8 @@ def cpu_baseline(wl, rows=128):
     scale = wl.H / rows
     step_s = dt * scale
     gbs = (wl.fwd_bytes() + wl.ig_bytes()) / step_s / 1e9
-    del np
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image (1/{scale:g} of "
+            "sample": f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image ({rows / wl.H:.3g} of "
                       f"the outputs), forward + input gradient, fp64 oracle, time scaled x{scale:g}",
             "sample_seconds": round(dt, 3), "ms_per_step_est": round(step_s * 1e3, 1)}
 
@@ -159,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-table", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -241,6 +242,16 @@ def main():
     }
     del t
     torch.cuda.empty_cache()
+    if args.calib_copy:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+        # readings calibrate the counters of the kernels above
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = src.numel() * 4
+        del src, dst
     if not args.no_cpu:
         _log("[bench] cpu baseline (oracle sample)")
         result["cpu_baseline"] = cpu_baseline(wl)

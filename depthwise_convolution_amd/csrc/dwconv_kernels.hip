@@ -29,6 +29,7 @@
 //    kH*kW taps.  Global loads for chunk k+1 are issued before chunk k is
 //    computed.  Workgroups are remapped so each XCD (own L2) walks a
 //    contiguous range of tiles, keeping halo re-reads in one L2.
+//  * every output store is non-temporal: outputs are write-once streams.
 //
 // The input gradient at stride 1 is the same kernel with the kernel taps
 // reversed (loaded reversed into registers) and no bias.
@@ -74,16 +75,24 @@ __device__ __forceinline__ void load_vec(const float *p, float (&v)[V])
         v[i] = f[i];
 }
 
+// Outputs are written once and never re-read by the kernel: store them
+// non-temporally so they stream to HBM instead of displacing the input rows
+// (and their halos) that neighbouring workgroups still read from L2.
+typedef float f4_ext __attribute__((ext_vector_type(4)));
+typedef float f2_ext __attribute__((ext_vector_type(2)));
+
 template <int V>
 __device__ __forceinline__ void store_vec(float *p, const float (&v)[V])
 {
-    typedef typename VecT<V>::type T;
-    T t;
-    float *f = reinterpret_cast<float *>(&t);
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-        f[i] = v[i];
-    *reinterpret_cast<T *>(p) = t;
+    if constexpr (V == 4) {
+        const f4_ext t = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(t, reinterpret_cast<f4_ext *>(p));
+    } else if constexpr (V == 2) {
+        const f2_ext t = {v[0], v[1]};
+        __builtin_nontemporal_store(t, reinterpret_cast<f2_ext *>(p));
+    } else {
+        __builtin_nontemporal_store(v[0], p);
+    }
 }
 
 struct DirectArgs {
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ i
             acc = fmaf(widen(wc[tap]), plane[ih * a.IW + iw], acc);
         }
     }
-    out[((n * a.C + c) * a.OH + oh) * a.OW + ow] = acc;
+    __builtin_nontemporal_store(acc, out + ((n * a.C + c) * a.OH + oh) * a.OW + ow);
 }
 
 // ---------------------------------------------------------------------------
