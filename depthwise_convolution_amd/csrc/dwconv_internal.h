@@ -26,21 +26,27 @@ enum Kind {
     KIND_TILED_NCHW = 4,   // stride 1: LDS row chunks of one plane, rolling row accumulators
 };
 
-// Compile-time shapes the tiled kernels are instantiated for.  A tiled plan
-// exists only for a (kH, kW, dilation) listed here; everything else runs the
-// direct kernels.  `vec` is the channels per thread of the NHWC kernel and
-// `gm` the number of window heights (R = (kH-1)*d + 1 rows) staged per LDS
-// chunk.
-struct TiledShape { int kH, kW, d, vec, gm; };
-constexpr TiledShape kTiledShapes[] = {
-    {3, 3, 1, 4, 2},
-    {5, 5, 1, 4, 1},
-    {7, 7, 1, 2, 1},
-    {7, 7, 2, 2, 1},
-    {1, 15, 1, 4, 4},
-    {1, 31, 1, 2, 4},
+// Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
+// for a (kH, kW, dilation) listed here; everything else runs the direct
+// kernels.  `vec`: channels per thread; `cl`: threads across channels; `px`:
+// adjacent output pixels per thread (a workgroup of 256 threads covers
+// cl*vec channels of px*256/cl pixels); `g`: input rows staged per
+// workgroup, which yields g - (kH-1)*d output rows.
+//
+// For each kernel shape the variants are listed in order of preference: the
+// order of their measured throughput on MI355X for channel counts that fill
+// their channel tile.  The planner takes the first one whose channel tile
+// the problem fills to at least 3/4.
+struct TiledVariant { int kH, kW, d, vec, cl, px, g; };
+constexpr TiledVariant kTiledVariants[] = {
+    {3, 3, 1, 4, 32, 2, 8},   {3, 3, 1, 4, 16, 1, 6},   {3, 3, 1, 4, 8, 1, 3},
+    {5, 5, 1, 4, 8, 1, 8},    {5, 5, 1, 4, 16, 1, 12},
+    {7, 7, 1, 1, 64, 1, 14},  {7, 7, 1, 2, 16, 1, 14},
+    {7, 7, 2, 2, 16, 1, 20},
+    {1, 15, 1, 4, 32, 1, 2},  {1, 15, 1, 4, 16, 1, 2},
+    {1, 31, 1, 2, 32, 1, 2},  {1, 31, 1, 2, 64, 1, 2},
 };
-constexpr int kNumTiledShapes = sizeof(kTiledShapes) / sizeof(kTiledShapes[0]);
+constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
 
 // Output columns per thread of the tiled NCHW kernel.
 constexpr int kNchwQ = 4;
@@ -48,10 +54,10 @@ constexpr int kNchwQ = 4;
 struct Plan {
     int kind;
     int vec;            // NHWC: channels per thread (4 or 1)
-    int shape;          // tiled: index into kTiledShapes
+    int variant;        // tiled: index into kTiledVariants
     int cl;             // tiled NHWC: threads across channels (8 or 16)
     int tw;             // tiled: output columns per tile
-    int th;             // tiled: output rows per strip
+    int th;             // tiled: output rows per workgroup
     int nct, nwt, nst;  // tiled: channel tiles, column tiles, strips (NHWC); nct = planes for NCHW
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op

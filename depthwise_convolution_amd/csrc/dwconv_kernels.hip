@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "dwconv_internal.h"
 #include "../../include/dwconv.h"
@@ -48,16 +49,6 @@ typedef _Float16 half_t;
 
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(half_t v) { return (float)v; }
-
-// Workgroup ids are handed to the 8 XCDs round-robin; give each XCD a
-// contiguous range of logical tiles (neighbouring tiles share halos and
-// should hit the same L2).
-__device__ __forceinline__ int xcd_logical_id(int b, int nb)
-{
-    const int q = nb >> 3, r = nb & 7;
-    const int xcd = b & 7, k = b >> 3;
-    return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
-}
 
 template <int V> struct VecT;
 template <> struct VecT<1> { typedef float type; };
@@ -93,6 +84,44 @@ __device__ __forceinline__ void store_vec(float *p, const float (&v)[V])
     } else {
         __builtin_nontemporal_store(v[0], p);
     }
+}
+
+// Raw buffer loads (gfx9 family buffer descriptors, stride 0): an offset at
+// or beyond the descriptor's byte count reads as zero in hardware, which
+// gives zero padding and tail handling without branches around the loads.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x7ffffff0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufWord3);
+}
+
+typedef unsigned int u4_ext __attribute__((ext_vector_type(4)));
+
+// Note: the 128-bit result must be reinterpreted as a whole vector; taking
+// its 32-bit lanes apart one by one has been seen to shrink the load to a
+// single dword on this compiler, leaving the other lanes undefined.
+__device__ __forceinline__ float4 buf_f4(__amdgpu_buffer_rsrc_t r, int off)
+{
+    const u4_ext t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const f4_ext f = __builtin_bit_cast(f4_ext, t);
+    return make_float4(f.x, f.y, f.z, f.w);
+}
+
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// One weight element, widened to fp32 (f16 by value).
+__device__ __forceinline__ float buf_w(__amdgpu_buffer_rsrc_t r, int idx, float *)
+{
+    return buf_f32(r, idx * 4);
+}
+__device__ __forceinline__ float buf_w(__amdgpu_buffer_rsrc_t r, int idx, half_t *)
+{
+    return (float)__builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, 0));
 }
 
 struct DirectArgs {
@@ -224,59 +253,120 @@ __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ i
 
 // ---------------------------------------------------------------------------
 // Tiled NHWC, stride 1 (forward, or input gradient with reversed taps).
+//
+// One workgroup = 256 threads = CL threads across channels x TW = 256/CL
+// pixels; each thread owns VEC consecutive channels of one output column.
+// The workgroup stages G input rows (its TH = G - R + 1 output rows plus the
+// (kH-1)*d row halo) of TW + (kW-1)*d columns (column halo) and CL*VEC
+// channels into LDS in one pass, together with its channels' weights, then
+// walks the rows: each thread reads its kW taps of a row from LDS and adds
+// the row into the R rolling accumulators of the output rows it touches;
+// after row u, output row u - (R-1) is complete and is stored.  Short-lived
+// workgroups with whole-pixel channel tiles keep the HBM traffic a linear
+// sweep, which is what streams fastest on MI355X.
 // ---------------------------------------------------------------------------
 struct TiledArgs {
     int N, C, H, W;         // image extents (input and output agree at stride 1)
     int pH, pW;
-    int TH;                 // output rows per strip
-    int nct, nwt, nst;      // channel tiles, column tiles, strips
-    int nblocks;
+    int nct, nwt, nst;      // channel tiles, column tiles, row tiles
 };
 
-template <int KH, int KW, int D, int VEC, int CL, int GM>
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G>
 struct TiledGeom {
-    static constexpr int LV = 4;                    // floats per global load
     static constexpr int R = (KH - 1) * D + 1;      // rows of one window
-    static constexpr int G = R * GM;                // input rows per LDS chunk
-    static constexpr int TW = 256 / CL;             // output columns per tile
-    static constexpr int CG = CL * VEC;             // channels per tile
-    static constexpr int TWI = TW + (KW - 1) * D;   // input columns per tile
-    static constexpr int VPC = CG / LV;             // float4 per LDS column
-    static constexpr int VPR = TWI * VPC;           // float4 per LDS row
-    static constexpr int VCH = G * VPR;             // float4 per chunk
-    static constexpr int NV = (VCH + 255) / 256;    // float4 per thread per chunk
-    static constexpr int LDS_BYTES = VCH * 16;
+    static constexpr int TH = G - R + 1;            // output rows per workgroup
+    static constexpr int TW = PX * 256 / CL;        // output columns per workgroup
+    static constexpr int CG = CL * VEC;             // channels per workgroup
+    static constexpr int TWI = TW + (KW - 1) * D;   // input columns staged
+    static constexpr int VPC = CG / 4;              // float4 per staged pixel
+    static constexpr int VPR = TWI * VPC;           // float4 per staged row
+    static constexpr int VCH = G * VPR;             // float4 staged
+    static constexpr int NV = (VCH + 255) / 256;    // float4 per thread
+    static constexpr int KK = KH * KW;
+    static constexpr int WF = CG * KK;              // weight floats per workgroup
+    static_assert(TH >= 1, "a workgroup must produce at least one output row");
+    static_assert(256 % CL == 0 && CG % 4 == 0, "bad channel tiling");
 };
 
-template <typename WT, int KH, int KW, int D, int VEC, int CL, int GM, bool IG>
+template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, bool IG>
 __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__ in,
                                                        const void *__restrict__ wv,
                                                        const float *__restrict__ bias,
                                                        float *__restrict__ out, TiledArgs a)
 {
-    typedef TiledGeom<KH, KW, D, VEC, CL, GM> Gm;
-    constexpr int R = Gm::R, G = Gm::G, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
-    constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV;
-    __shared__ float4 lds[VCH];
-    const float *ldsf = reinterpret_cast<const float *>(lds);
+    typedef TiledGeom<KH, KW, D, VEC, CL, PX, G> Gm;
+    constexpr int R = Gm::R, TH = Gm::TH, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
+    constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV, KK = Gm::KK;
+    constexpr int WF = Gm::WF;
+    __shared__ float4 lds[VCH + (WF + 3) / 4];
+    float *ldsx = reinterpret_cast<float *>(lds);
+    float *ldsw = ldsx + VCH * 4;
     const WT *w = reinterpret_cast<const WT *>(wv);
 
-    int tile = xcd_logical_id(blockIdx.x, a.nblocks);
+    int tile = blockIdx.x;
     const int ct = tile % a.nct;
     tile /= a.nct;
     const int wt = tile % a.nwt;
     tile /= a.nwt;
     const int st = tile % a.nst;
     const int n = tile / a.nst;
-    const int c0 = ct * CG, w0 = wt * TW, h0 = st * a.TH;
-
+    const int c0 = ct * CG, w0 = wt * TW, h0 = st * TH;
     const int tid = threadIdx.x;
-    const int q = tid % CL, p = tid / CL;
-    const int cq = c0 + q * VEC;     // first channel of this thread
-    const bool cvalid = cq < a.C;    // C % 4 == 0, so the whole vector is valid
-    const int ow = w0 + p;
+    const int nrows = min(TH, a.H - h0) + R - 1;   // staged rows that exist in the strip
+    const int rbase = h0 - a.pH, cbase = w0 - a.pW;
 
-    // per-thread weights (reversed for the input gradient) and bias
+    const int q = tid % CL, p = tid / CL;
+    const int cq = c0 + q * VEC;
+    const bool cvalid = cq < a.C;        // C % 4 == 0: the whole vector is valid
+    const int ow = w0 + p * PX;          // first of this thread's PX output columns
+
+    // 1. Issue every global load up front, the small L2-resident ones first:
+    // this workgroup's weights (contiguous in memory) and the thread's bias,
+    // then the input tile.  All are buffer loads: weights of channels >= C,
+    // a missing bias, and tile elements outside the image read as zero.
+    // Loads complete in order, so the weights can be written to LDS while
+    // the tile is still in flight.
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
+    constexpr int NW = (WF + 255) / 256;
+    float wst[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+        wst[i] = buf_w(rw, c0 * KK + tid + i * 256, (WT *)nullptr);
+    float bv[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v)
+        bv[v] = buf_f32(rb, (cq + v) * 4);
+    float4 stage[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * 256;
+        const int g = e / VPR;
+        const int rem = e - g * VPR;
+        const int col = rem / VPC;
+        const int cv = rem - col * VPC;
+        const int row = rbase + g, gc = cbase + col, ch = c0 + cv * 4;
+        const bool ok = e < VCH && g < nrows && row >= 0 && row < a.H && gc >= 0 &&
+                        gc < a.W && ch < a.C;
+        stage[i] = buf_f4(rx, ok ? ((row * a.W + gc) * a.C + ch) * 4 : kOutOfRange);
+    }
+    // 2. weights, then the tile, into LDS
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = tid + i * 256;
+        if (e < WF)
+            ldsw[e] = wst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * 256;
+        if (e < VCH)
+            lds[e] = stage[i];
+    }
+    __syncthreads();
+
+    // per-thread weights (reversed taps for the input gradient)
     float wr[KH][KW][VEC];
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh)
@@ -285,93 +375,57 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
-                wr[kh][kw][v] = cvalid ? widen(w[(cq + v) * (KH * KW) + tap]) : 0.0f;
+                wr[kh][kw][v] = ldsw[(q * VEC + v) * KK + tap];
             }
-    float bv[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v)
-        bv[v] = (!IG && bias && cvalid) ? bias[cq + v] : 0.0f;
-
-    float acc[R][VEC];
+    float acc[R][PX][VEC];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
-            acc[r][v] = bv[v];
-
-    const int th_eff = min(a.TH, a.H - h0);
-    const int nrows = th_eff + R - 1;          // input rows this strip reads
-    const int nchunks = (nrows + G - 1) / G;
-    const int rbase = h0 - a.pH;               // image row of strip input row 0
-    const int cbase = w0 - a.pW;               // image column of LDS column 0
-    const int HW = a.H * a.W;
-
-    float4 stage[NV];
-    auto load_chunk = [&](int k) {
+        for (int j = 0; j < PX; ++j)
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = tid + i * 256;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < VCH) {
-                const int g = e / VPR;
-                const int rem = e - g * VPR;
-                const int col = rem / VPC;
-                const int cv = rem - col * VPC;
-                const int j = k * G + g;
-                const int row = rbase + j;
-                const int gc = cbase + col;
-                const int ch = c0 + cv * 4;
-                if (j < nrows && row >= 0 && row < a.H && gc >= 0 && gc < a.W && ch < a.C)
-                    v = *reinterpret_cast<const float4 *>(
-                        in + ((n * a.H + row) * a.W + gc) * a.C + ch);
+            for (int v = 0; v < VEC; ++v)
+                acc[r][j][v] = bv[v];
+
+    // 3. walk the staged rows
+    constexpr int XW = PX + (KW - 1) * D;  // staged columns one thread reads per row
+    float *outp = out + (n * a.H * a.W) * a.C;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        if (u < nrows) {
+            float xv[XW][VEC];
+#pragma unroll
+            for (int i = 0; i < XW; ++i) {
+                const float *src = ldsx + ((u * TWI + p * PX + i) * CG + q * VEC);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    xv[i][v] = src[v];
             }
-            stage[i] = v;
-        }
-    };
-
-    float *outp = out + (n * HW) * a.C;
-    load_chunk(0);
-    for (int k = 0; k < nchunks; ++k) {
-        if (k > 0)
-            __syncthreads();                   // all reads of the previous chunk done
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = tid + i * 256;
-            if (e < VCH)
-                lds[e] = stage[i];
-        }
-        __syncthreads();
-        if (k + 1 < nchunks)
-            load_chunk(k + 1);                 // in flight while this chunk is computed
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            const int j = k * G + u;
-            if (j < nrows) {
-                float xv[KW][VEC];
-#pragma unroll
-                for (int kw = 0; kw < KW; ++kw) {
-                    const float *src = ldsf + ((u * TWI + p + kw * D) * CG + q * VEC);
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v)
-                        xv[kw][v] = src[v];
-                }
-#pragma unroll
-                for (int kh = 0; kh < KH; ++kh) {
-                    const int slot = ((u - kh * D) % R + R) % R;
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh * D;          // output row this tap row feeds
+                if (m >= 0 && m < TH) {
+                    const int slot = m % R;
 #pragma unroll
                     for (int kw = 0; kw < KW; ++kw)
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v)
-                            acc[slot][v] = fmaf(wr[kh][kw][v], xv[kw][v], acc[slot][v]);
-                }
-                // output row m = j - (R-1) has now received all its taps
-                const int done = (u + 1) % R;
-                const int m = j - (R - 1);
-                if (m >= 0 && cvalid && ow < a.W)
-                    store_vec<VEC>(outp + ((h0 + m) * a.W + ow) * a.C + cq, acc[done]);
+                        for (int j = 0; j < PX; ++j)
 #pragma unroll
-                for (int v = 0; v < VEC; ++v)
-                    acc[done][v] = bv[v];
+                            for (int v = 0; v < VEC; ++v)
+                                acc[slot][j][v] =
+                                    fmaf(wr[kh][kw][v], xv[j + kw * D][v], acc[slot][j][v]);
+                }
+            }
+            const int m = u - (R - 1);             // output row completed by row u
+            if (m >= 0) {
+#pragma unroll
+                for (int j = 0; j < PX; ++j) {
+                    if (cvalid && ow + j < a.W)
+                        store_vec<VEC>(outp + ((h0 + m) * a.W + ow + j) * a.C + cq,
+                                       acc[m % R][j]);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        acc[m % R][j][v] = bv[v];
+                }
             }
         }
     }
@@ -421,53 +475,44 @@ void launch_direct(const Problem &p, const Plan &pl, const float *in, const void
 
 typedef void (*TiledFn)(const float *, const void *, const float *, float *, TiledArgs);
 
-// Kernel table for the tiled NHWC kernel: [shape][cl 8|16][f16w][ig].
-template <typename WT, int SH, int CL, bool IG>
+// Kernel table of the tiled NHWC kernel: [variant][f16 weights][input grad].
+template <typename WT, int V, bool IG>
 constexpr TiledFn tiled_fn()
 {
-    constexpr TiledShape t = kTiledShapes[SH];
-    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, CL, t.gm, IG>;
+    constexpr TiledVariant t = kTiledVariants[V];
+    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, IG>;
 }
 
-template <int SH>
-void fill_tiled_row(TiledFn (&row)[2][2][2])
+template <int V>
+void fill_tiled(TiledFn (&row)[2][2])
 {
-    row[0][0][0] = tiled_fn<float, SH, 8, false>();
-    row[0][0][1] = tiled_fn<float, SH, 8, true>();
-    row[0][1][0] = tiled_fn<half_t, SH, 8, false>();
-    row[0][1][1] = tiled_fn<half_t, SH, 8, true>();
-    row[1][0][0] = tiled_fn<float, SH, 16, false>();
-    row[1][0][1] = tiled_fn<float, SH, 16, true>();
-    row[1][1][0] = tiled_fn<half_t, SH, 16, false>();
-    row[1][1][1] = tiled_fn<half_t, SH, 16, true>();
+    row[0][0] = tiled_fn<float, V, false>();
+    row[0][1] = tiled_fn<float, V, true>();
+    row[1][0] = tiled_fn<half_t, V, false>();
+    row[1][1] = tiled_fn<half_t, V, true>();
+}
+
+template <int... Vs>
+void fill_all_tiled(TiledFn (&fn)[kNumTiledVariants][2][2], std::integer_sequence<int, Vs...>)
+{
+    (fill_tiled<Vs>(fn[Vs]), ...);
 }
 
 struct TiledTable {
-    TiledFn fn[kNumTiledShapes][2][2][2];
-    TiledTable()
-    {
-        static_assert(kNumTiledShapes == 6, "update the tiled kernel table");
-        fill_tiled_row<0>(fn[0]);
-        fill_tiled_row<1>(fn[1]);
-        fill_tiled_row<2>(fn[2]);
-        fill_tiled_row<3>(fn[3]);
-        fill_tiled_row<4>(fn[4]);
-        fill_tiled_row<5>(fn[5]);
-    }
+    TiledFn fn[kNumTiledVariants][2][2];
+    TiledTable() { fill_all_tiled(fn, std::make_integer_sequence<int, kNumTiledVariants>()); }
 };
 
 int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const void *w,
                       const float *b, float *out, hipStream_t st)
 {
     static const TiledTable table;
-    if (pl.shape < 0 || pl.shape >= kNumTiledShapes || (pl.cl != 8 && pl.cl != 16))
+    if (pl.variant < 0 || pl.variant >= kNumTiledVariants)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledFn f = table.fn[pl.shape][pl.cl == 16][p.wtype == DWCONV_W_F16]
-                        [p.op == DWCONV_OP_INPUT_GRAD];
+    TiledFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][p.op == DWCONV_OP_INPUT_GRAD];
     TiledArgs a;
     a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.pH = pl.pH; a.pW = pl.pW;
-    a.TH = pl.th; a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
-    a.nblocks = (int)pl.grid;
+    a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                        p.op == DWCONV_OP_FWD ? b : nullptr, out, a);
     return DWCONV_OK;

@@ -18,11 +18,8 @@ namespace dwconv {
 namespace {
 
 constexpr long long kMaxElems = (1LL << 31) - 1;  // 32-bit element indexing
-constexpr int kNumCUs = 256;                       // MI355X compute units
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-constexpr bool kHaveTiledNchw = false;
 
 }  // namespace
 
@@ -48,86 +45,64 @@ int validate_problem(const Problem &p)
     return DWCONV_OK;
 }
 
-static int find_tiled_shape(const Problem &p)
-{
-    for (int i = 0; i < kNumTiledShapes; ++i)
-        if (kTiledShapes[i].kH == p.kH && kTiledShapes[i].kW == p.kW &&
-            kTiledShapes[i].d == p.dilation)
-            return i;
-    return -1;
-}
-
-// Strip height: aim for about eight workgroups per compute unit, keeping a
-// strip at least one window height tall when the image allows it.
-static int pick_strip_rows(int H, long long tiles_per_strip_row, int R)
-{
-    const long long target = 8LL * kNumCUs;
-    long long strips = (target + tiles_per_strip_row - 1) / tiles_per_strip_row;
-    if (strips < 1)
-        strips = 1;
-    int th = (int)std::max<long long>(1, (H + strips - 1) / strips);
-    th = std::max(th, std::min(H, R));
-    return std::min(th, 64);
-}
-
 static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    const int s = find_tiled_shape(p);
-    if (s < 0 || p.stride != 1 || p.layout != DWCONV_LAYOUT_NHWC)
+    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NHWC)
         return false;
     if (p.C % 4 != 0 || (ptr_bits & 15u) != 0)
         return false;
-    const TiledShape &ts = kTiledShapes[s];
-    const int R = (ts.kH - 1) * ts.d + 1;
+    // buffer-load byte offsets are 31-bit: one image and the weights must fit
+    if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+        return false;
+    // first variant of this kernel shape (table order = preference) whose
+    // channel tile the problem fills to at least 3/4; else the one it fills best
+    int best = -1;
+    double best_fill = -1.0;
+    for (int i = 0; i < kNumTiledVariants; ++i) {
+        const TiledVariant &v = kTiledVariants[i];
+        if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation)
+            continue;
+        const int cg = v.cl * v.vec;
+        const double fill = (double)p.C / (ceil_div(p.C, cg) * cg);
+        if (fill >= 0.75) {
+            best = i;
+            break;
+        }
+        if (fill > best_fill) {
+            best = i;
+            best_fill = fill;
+        }
+    }
+    if (best < 0)
+        return false;
+    const TiledVariant &v = kTiledVariants[best];
+    const int R = (v.kH - 1) * v.d + 1;
     pl->kind = KIND_TILED_NHWC;
-    pl->shape = s;
-    pl->vec = ts.vec;
-    pl->cl = (p.C / ts.vec <= 8) ? 8 : 16;
-    pl->tw = 256 / pl->cl;
-    const int cg = pl->cl * ts.vec;
-    pl->nct = ceil_div(p.C, cg);
+    pl->variant = best;
+    pl->vec = v.vec;
+    pl->cl = v.cl;
+    pl->tw = v.px * 256 / v.cl;
+    pl->th = v.g - R + 1;
+    pl->nct = ceil_div(p.C, v.cl * v.vec);
     pl->nwt = ceil_div(p.W, pl->tw);
-    pl->th = pick_strip_rows(p.H, (long long)p.N * pl->nct * pl->nwt, R);
     pl->nst = ceil_div(p.H, pl->th);
-    pl->grid = (long long)p.N * pl->nst * pl->nwt * pl->nct;
+    pl->grid = (long long)p.N * pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_%s_%s",
-                  ts.kH, ts.kW, ts.d, ts.vec, pl->cl, p.op ? "ig" : "fwd",
+    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_%s_%s",
+                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, p.op ? "ig" : "fwd",
                   p.wtype ? "f16w" : "f32w");
     return true;
 }
 
-static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
+static bool plan_tiled_nchw(const Problem &, std::uintptr_t, Plan *)
 {
-    if (!kHaveTiledNchw)
-        return false;
-    const int s = find_tiled_shape(p);
-    if (s < 0 || p.stride != 1 || p.layout != DWCONV_LAYOUT_NCHW)
-        return false;
-    if (p.W % kNchwQ != 0 || (ptr_bits & 15u) != 0)
-        return false;
-    const TiledShape &ts = kTiledShapes[s];
-    const int R = (ts.kH - 1) * ts.d + 1;
-    pl->kind = KIND_TILED_NCHW;
-    pl->shape = s;
-    pl->vec = 1;
-    pl->cl = 0;
-    pl->tw = 256 * kNchwQ;  // one workgroup spans up to 1024 output columns
-    pl->nct = p.N * p.C;    // planes
-    pl->nwt = ceil_div(p.W, pl->tw);
-    pl->th = pick_strip_rows(p.H, (long long)pl->nct * pl->nwt, R);
-    pl->nst = ceil_div(p.H, pl->th);
-    pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
-    pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s1_k%dx%d_d%d_%s_%s",
-                  ts.kH, ts.kW, ts.d, p.op ? "ig" : "fwd", p.wtype ? "f16w" : "f32w");
-    return true;
+    return false;   // no tiled NCHW kernel yet
 }
 
 static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     pl->block = 256;
-    pl->shape = -1;
+    pl->variant = -1;
     if (p.layout == DWCONV_LAYOUT_NHWC) {
         pl->kind = KIND_DIRECT_NHWC;
         pl->vec = (p.C % 4 == 0 && (ptr_bits & 15u) == 0) ? 4 : 1;

@@ -149,23 +149,25 @@ def test_describe_selects_kernels():
 
 @pytest.mark.parametrize("wl_name", ["large_512x512x256_3x3", "mobilenet_112x112x32_3x3",
                                      "effnet_n32_56x56x128_5x5", "asr_n64_30x19x128_7x7_d2",
-                                     "asr_n64_1x24x256_1x31", "asr_n64_1x24x128_1x15"])
+                                     "asr_n64_1x24x256_1x31", "asr_n64_1x24x128_1x15",
+                                     "asr_n1_30x19x128_7x7"])
 def test_tiled_grid_covers_problem(wl_name):
-    """The tiled grid (strips x column tiles x channel tiles) covers every
-    output exactly: recompute it from the kernel name's tile sizes."""
+    """The tiled grid (row tiles x column tiles x channel tiles x batch) covers
+    every output exactly once: recompute it from the tile sizes in the name."""
     from depthwise_convolution_amd.workloads import WORKLOADS
     wl = WORKLOADS[wl_name]
     name, grid, block = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
                                              wl.stride, wl.dilation)
-    assert name.startswith("tiled_nhwc")
+    assert name.startswith("tiled_nhwc") and block == 256
     vec = int(re.search(r"_v(\d+)_", name).group(1))
     cl = int(re.search(r"_cl(\d+)_", name).group(1))
-    tw, cg = 256 // cl, cl * vec
-    nct, nwt = -(-wl.C // cg), -(-wl.W // tw)
-    assert grid % (wl.N * nct * nwt) == 0
-    nst = grid // (wl.N * nct * nwt)
-    th = -(-wl.H // nst)
-    assert (nst - 1) * th < wl.H <= nst * th
+    px = int(re.search(r"_px(\d+)_", name).group(1))
+    g = int(re.search(r"_g(\d+)_", name).group(1))
+    th = g - (wl.kH - 1) * wl.dilation
+    tw, cg = px * 256 // cl, cl * vec
+    assert th >= 1 and cg % 4 == 0
+    nct, nwt, nst = -(-wl.C // cg), -(-wl.W // tw), -(-wl.H // th)
+    assert grid == wl.N * nct * nwt * nst
 
 
 def test_python_binding_rejects_cpu_tensors():
