@@ -23,7 +23,7 @@ enum Kind {
     KIND_DIRECT_NHWC = 1,  // one thread per (n, row, col, channel vector); taps from global
     KIND_DIRECT_NCHW = 2,  // one thread per (n, channel, row, col); taps from global
     KIND_TILED_NHWC = 3,   // stride 1: LDS row chunks with halo, rolling row accumulators
-    KIND_TILED_NCHW = 4,   // stride 1: LDS row chunks of one plane, rolling row accumulators
+    KIND_TILED_NCHW = 4,   // stride 1: LDS tiles of one or more planes, rolling row accumulators
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
@@ -48,8 +48,21 @@ constexpr TiledVariant kTiledVariants[] = {
 };
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
 
-// Output columns per thread of the tiled NCHW kernel.
-constexpr int kNchwQ = 4;
+// Compile-time variants of the tiled NCHW kernel (same preference rule).
+// A workgroup of 256 threads covers pb planes (channels) x tx threads per
+// plane row, tx = 256/pb chosen at plan time from W; each thread owns `q`
+// adjacent output columns; `g` input rows are staged per workgroup; `v4`
+// selects 16-byte loads (needs W % 4 == 0).
+struct TiledNchwVariant { int kH, kW, d, q, g, v4; };
+constexpr TiledNchwVariant kTiledNchwVariants[] = {
+    {3, 3, 1, 2, 8, 1},   {3, 3, 1, 2, 8, 0},
+    {5, 5, 1, 2, 12, 1},  {5, 5, 1, 2, 12, 0},
+    {7, 7, 1, 1, 14, 1},  {7, 7, 1, 1, 14, 0},
+    {7, 7, 2, 1, 20, 1},  {7, 7, 2, 1, 20, 0},
+    {1, 15, 1, 2, 2, 1},  {1, 15, 1, 2, 2, 0},
+    {1, 31, 1, 2, 2, 1},  {1, 31, 1, 2, 2, 0},
+};
+constexpr int kNumTiledNchwVariants = sizeof(kTiledNchwVariants) / sizeof(kTiledNchwVariants[0]);
 
 struct Plan {
     int kind;
@@ -58,7 +71,9 @@ struct Plan {
     int cl;             // tiled NHWC: threads across channels (8 or 16)
     int tw;             // tiled: output columns per tile
     int th;             // tiled: output rows per workgroup
-    int nct, nwt, nst;  // tiled: channel tiles, column tiles, strips (NHWC); nct = planes for NCHW
+    int nct, nwt, nst;  // tiled: channel tiles (NHWC) or plane groups (NCHW), column tiles, row tiles
+    int pb;             // tiled NCHW: planes per workgroup
+    int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
     long long total;    // direct: number of threads doing work

@@ -432,6 +432,186 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Tiled NCHW, stride 1 (forward, or input gradient with reversed taps).
+//
+// Channel-outer layout: each (n, c) plane is an image of its own, and the
+// weights of a plane are one kernel.  A workgroup of 256 threads covers PB
+// planes x TX threads per plane row (TX = 256/PB, a power of two >= W/Q so
+// narrow planes are packed several to a workgroup); each thread owns Q
+// adjacent output columns.  G input rows of every plane (the TH = G - R + 1
+// output rows plus the row halo) and HALO columns on each side are staged
+// in LDS in one pass, then the rows are walked with rolling accumulators as
+// in the NHWC kernel.  Loads are buffer loads over the whole tensor: rows
+// past the plane or the tensor read as zero, columns outside [0, W) are
+// given an out-of-range offset.
+// ---------------------------------------------------------------------------
+struct TiledNchwArgs {
+    int planes, C, H, W;
+    int pH, pW;
+    int tx_log2;            // threads per plane row = 1 << tx_log2 (>= 16)
+    int nct, nwt, nst;      // plane groups, column tiles, row tiles
+};
+
+template <int KH, int KW, int D, int Q, int G, bool V4>
+struct NchwGeom {
+    static constexpr int R = (KH - 1) * D + 1;
+    static constexpr int TH = G - R + 1;
+    static constexpr int KK = KH * KW;
+    static constexpr int PW = D * (KW - 1) / 2;
+    static constexpr int HALO = V4 ? (PW + 3) / 4 * 4 : PW;   // staged columns per side
+    static constexpr int LV = V4 ? 4 : 1;                      // floats per load
+    static constexpr int PBMAX = 16;                           // TX >= 16
+    // per-thread loads for the largest staged tile: G rows x (256*Q + PBMAX*2*HALO) floats
+    static constexpr int NV = (G * (256 * Q + PBMAX * 2 * HALO) / LV + 255) / 256;
+    static constexpr int NW = (PBMAX * KK + 255) / 256;
+    static_assert(TH >= 1, "a workgroup must produce at least one output row");
+};
+
+template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, bool IG>
+__global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__ in,
+                                                       const void *__restrict__ wv,
+                                                       const float *__restrict__ bias,
+                                                       float *__restrict__ out, TiledNchwArgs a)
+{
+    typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
+    constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, HALO = Gm::HALO, LV = Gm::LV;
+    constexpr int NV = Gm::NV, NW = Gm::NW;
+    extern __shared__ float4 lds4[];
+    float *lds = reinterpret_cast<float *>(lds4);
+    const WT *w = reinterpret_cast<const WT *>(wv);
+
+    const int txn = 1 << a.tx_log2, pbn = 256 >> a.tx_log2;
+    const int tw = txn * Q, twl = tw + 2 * HALO;       // staged floats per plane row
+    const int vpr = twl / LV;                          // loads per plane row
+    float *ldsw = lds + pbn * G * twl;
+
+    int tile = blockIdx.x;
+    const int pg = tile % a.nct;
+    tile /= a.nct;
+    const int wt = tile % a.nwt;
+    const int st = tile / a.nwt;
+    const int w0 = wt * tw, h0 = st * TH;
+    const int tid = threadIdx.x;
+    const int nrows = min(TH, a.H - h0) + R - 1;
+    const int rbase = h0 - a.pH, cbase = w0 - HALO;
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes * a.H * a.W * 4);
+
+    // 1. all loads up front: weights of the workgroup's planes, the bias, the tile
+    float wst[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = tid + i * 256;
+        const int pl = e / KK, tap = e - pl * KK;
+        const int plane = pg * pbn + pl;
+        const bool ok = pl < pbn && plane < a.planes;
+        wst[i] = buf_w(rw, ok ? (plane % a.C) * KK + tap : kOutOfRange / 4, (WT *)nullptr);
+    }
+    const int pli = tid >> a.tx_log2, tx = tid & (txn - 1);
+    const int my_plane = pg * pbn + pli;
+    const bool pvalid = my_plane < a.planes;
+    const float bval = buf_f32(rb, pvalid ? (my_plane % a.C) * 4 : kOutOfRange);
+    float sv[NV][LV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * 256;
+        const int pl = e / (G * vpr);
+        const int rem = e - pl * (G * vpr);
+        const int g = rem / vpr;
+        const int col = cbase + (rem - g * vpr) * LV;
+        const int plane = pg * pbn + pl, row = rbase + g;
+        const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && row < a.H &&
+                        col >= 0 && col < a.W;
+        const int off = ok ? ((plane * a.H + row) * a.W + col) * 4 : kOutOfRange;
+        if constexpr (V4) {
+            const float4 v = buf_f4(rx, off);
+            sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
+        } else {
+            sv[i][0] = buf_f32(rx, off);
+        }
+    }
+    // 2. into LDS
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = tid + i * 256;
+        if (e < pbn * KK)
+            ldsw[e] = wst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * 256;
+        if (e < pbn * G * vpr) {
+            if constexpr (V4)
+                lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
+            else
+                lds[e] = sv[i][0];
+        }
+    }
+    __syncthreads();
+
+    // 3. per-thread weights and rolling accumulators
+    float wr[KH][KW];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+            const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
+            wr[kh][kw] = ldsw[pli * KK + tap];
+        }
+    float acc[R][Q];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < Q; ++j)
+            acc[r][j] = bval;
+    constexpr int XW = Q + (KW - 1) * D;
+    const float *rowbase = lds + pli * G * twl + tx * Q + (HALO - Gm::PW);
+    const int oc = w0 + tx * Q;                        // first output column of this thread
+    float *outp = out + my_plane * a.H * a.W;
+    const bool vec_store = (Q > 1) && (a.W % Q == 0);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        if (u < nrows) {
+            float xv[XW];
+#pragma unroll
+            for (int i = 0; i < XW; ++i)
+                xv[i] = rowbase[u * twl + i];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh * D;
+                if (m >= 0 && m < TH) {
+                    const int slot = m % R;
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                        for (int j = 0; j < Q; ++j)
+                            acc[slot][j] = fmaf(wr[kh][kw], xv[j + kw * D], acc[slot][j]);
+                }
+            }
+            const int m = u - (R - 1);
+            if (m >= 0) {
+                float *dst = outp + (h0 + m) * a.W + oc;
+                if (pvalid) {
+                    if (vec_store && oc < a.W) {
+                        store_vec<Q>(dst, acc[m % R]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < Q; ++j)
+                            if (oc + j < a.W)
+                                __builtin_nontemporal_store(acc[m % R][j], dst + j);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < Q; ++j)
+                    acc[m % R][j] = bval;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
 DirectArgs direct_args(const Problem &p, const Plan &pl)
@@ -518,6 +698,58 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
     return DWCONV_OK;
 }
 
+typedef void (*TiledNchwFn)(const float *, const void *, const float *, float *, TiledNchwArgs);
+
+template <typename WT, int V, bool IG>
+constexpr TiledNchwFn tiled_nchw_fn()
+{
+    constexpr TiledNchwVariant t = kTiledNchwVariants[V];
+    return &k_tiled_nchw_s1<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), IG>;
+}
+
+template <int V>
+void fill_tiled_nchw(TiledNchwFn (&row)[2][2])
+{
+    row[0][0] = tiled_nchw_fn<float, V, false>();
+    row[0][1] = tiled_nchw_fn<float, V, true>();
+    row[1][0] = tiled_nchw_fn<half_t, V, false>();
+    row[1][1] = tiled_nchw_fn<half_t, V, true>();
+}
+
+template <int... Vs>
+void fill_all_tiled_nchw(TiledNchwFn (&fn)[kNumTiledNchwVariants][2][2],
+                         std::integer_sequence<int, Vs...>)
+{
+    (fill_tiled_nchw<Vs>(fn[Vs]), ...);
+}
+
+struct TiledNchwTable {
+    TiledNchwFn fn[kNumTiledNchwVariants][2][2];
+    TiledNchwTable()
+    {
+        fill_all_tiled_nchw(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+    }
+};
+
+int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
+                      const float *b, float *out, hipStream_t st)
+{
+    static const TiledNchwTable table;
+    if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
+        (pl.cl & (pl.cl - 1)) != 0)
+        return DWCONV_ERR_BAD_STRATEGY;
+    TiledNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][p.op == DWCONV_OP_INPUT_GRAD];
+    TiledNchwArgs a;
+    a.planes = p.N * p.C; a.C = p.C; a.H = p.H; a.W = p.W; a.pH = pl.pH; a.pW = pl.pW;
+    a.tx_log2 = 0;
+    while ((1 << a.tx_log2) < pl.cl)
+        ++a.tx_log2;
+    a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
+    hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
+                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a);
+    return DWCONV_OK;
+}
+
 }  // namespace
 
 // Run a validated plan on `stream`.  Returns a DWCONV_ status.
@@ -537,6 +769,9 @@ int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w
         break;
     case KIND_TILED_NHWC:
         st = launch_tiled_nhwc(p, pl, in, w, bb, out, stream);
+        break;
+    case KIND_TILED_NCHW:
+        st = launch_tiled_nchw(p, pl, in, w, bb, out, stream);
         break;
     default:
         return DWCONV_ERR_BAD_STRATEGY;

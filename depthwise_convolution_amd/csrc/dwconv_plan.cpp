@@ -94,9 +94,48 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     return true;
 }
 
-static bool plan_tiled_nchw(const Problem &, std::uintptr_t, Plan *)
+static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    return false;   // no tiled NCHW kernel yet
+    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NCHW)
+        return false;
+    // buffer-load byte offsets are 31-bit: the whole tensor and the weights must fit
+    if (4LL * p.N * p.C * p.H * p.W >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+        return false;
+    const bool v4ok = p.W % 4 == 0 && (ptr_bits & 15u) == 0;
+    int best = -1;
+    for (int i = 0; i < kNumTiledNchwVariants; ++i) {
+        const TiledNchwVariant &v = kTiledNchwVariants[i];
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation && (v.v4 == 0 || v4ok)) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const TiledNchwVariant &v = kTiledNchwVariants[best];
+    const int R = (v.kH - 1) * v.d + 1;
+    int tx = 16;                                 // threads per plane row: pow2 >= W/q, >= 16
+    while (tx < 256 && tx * v.q < p.W)
+        tx *= 2;
+    const int pW = v.d * (v.kW - 1) / 2;
+    const int halo = v.v4 ? (pW + 3) / 4 * 4 : pW;
+    pl->kind = KIND_TILED_NCHW;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = tx;
+    pl->pb = 256 / tx;
+    pl->tw = tx * v.q;
+    pl->th = v.g - R + 1;
+    pl->nct = ceil_div(p.N * p.C, pl->pb);
+    pl->nwt = ceil_div(p.W, pl->tw);
+    pl->nst = ceil_div(p.H, pl->th);
+    pl->lds_bytes = 4 * (pl->pb * v.g * (pl->tw + 2 * halo) + pl->pb * v.kH * v.kW);
+    pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s1_k%dx%d_d%d_q%d_g%d_%s_tx%d_%s_%s",
+                  v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, p.op ? "ig" : "fwd",
+                  p.wtype ? "f16w" : "f32w");
+    return true;
 }
 
 static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
