@@ -6,9 +6,10 @@ PyTorch provides device memory and the current stream.  If the library has
 not been built, every call raises ``RuntimeError``: there is no fallback.
 
 Names mirror the C ABI: ``dwconv2d_fwd``, ``dwconv2d_input_grad``,
-``dwconv2d_launch``, ``dwconv2d_describe``, ``dwconv2d_strerror``,
-``dwconv2d_version``; ``fwd`` and ``input_grad`` are the same calls with the
-output allocated here.
+``dwconv2d_launch``, ``dwconv2d_describe``, ``dwconv2d_weight_grad``,
+``dwconv2d_weight_grad_workspace_size``, ``dwconv2d_strerror``,
+``dwconv2d_version``; ``fwd``, ``input_grad`` and ``weight_grad`` are the
+same calls with the outputs (and the workspace) allocated here.
 
 Tensor shapes: NHWC tensors are ``(N, H, W, C)``, NCHW tensors
 ``(N, C, H, W)``; weights ``(C, kH, kW)`` float32 or float16; bias ``(C,)``.
@@ -21,14 +22,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdwconv.s
 # enumerations of include/dwconv.h
 NHWC, NCHW = 0, 1
 W_F32, W_F16 = 0, 1
-OP_FWD, OP_INPUT_GRAD = 0, 1
+OP_FWD, OP_INPUT_GRAD, OP_WEIGHT_GRAD = 0, 1, 2
 STRATEGY_AUTO, STRATEGY_DIRECT, STRATEGY_TILED = 0, 1, 2
 STATUS = {
     0: "OK", -1: "NULL_PTR", -2: "BAD_DIM", -3: "BAD_STRIDE", -4: "BAD_DILATION",
     -5: "EVEN_KERNEL", -6: "BAD_LAYOUT", -7: "BAD_WTYPE", -8: "ALIAS", -9: "MISALIGNED",
-    -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY",
+    -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY", -13: "WORKSPACE",
 }
 EXPORTS = ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
+           "dwconv2d_weight_grad", "dwconv2d_weight_grad_workspace_size",
            "dwconv2d_strerror", "dwconv2d_version")
 
 _lib = None
@@ -56,10 +58,12 @@ def lib():
     L.dwconv2d_launch.argtypes = [i, vp, vp, i, vp, vp] + [i] * 10 + [vp]
     L.dwconv2d_describe.argtypes = [i] * 13 + [ctypes.c_char_p, i, ctypes.POINTER(ll),
                                                ctypes.POINTER(i)]
+    L.dwconv2d_weight_grad_workspace_size.argtypes = [i] * 10 + [ctypes.POINTER(ll)]
+    L.dwconv2d_weight_grad.argtypes = [vp, vp, vp, vp, vp, ll] + [i] * 10 + [vp]
     L.dwconv2d_strerror.argtypes = [i]
     L.dwconv2d_strerror.restype = ctypes.c_char_p
     for f in ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
-              "dwconv2d_version"):
+              "dwconv2d_weight_grad", "dwconv2d_weight_grad_workspace_size", "dwconv2d_version"):
         getattr(L, f).restype = i
     _lib = L
     return L
@@ -227,3 +231,57 @@ def input_grad(dy, w, H, W, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY
     dx = torch.empty(_shape(lay, N, H, W, C), dtype=torch.float32, device=dy.device)
     return dwconv2d_launch(OP_INPUT_GRAD, dy, w, None, dx, H, W, stride, dilation, lay,
                            strategy, stream)
+
+
+def dwconv2d_weight_grad_workspace_size(N, H, W, C, kH, kW, stride=1, dilation=1, layout=NHWC,
+                                        strategy=STRATEGY_AUTO):
+    """Workspace bytes dwconv2d_weight_grad needs for these arguments."""
+    out = ctypes.c_longlong(0)
+    st = lib().dwconv2d_weight_grad_workspace_size(N, H, W, C, kH, kW, stride, dilation,
+                                                   _layout_code(layout), strategy,
+                                                   ctypes.byref(out))
+    _check_status(st, "dwconv2d_weight_grad_workspace_size")
+    return out.value
+
+
+def dwconv2d_weight_grad(x, dy, dw, db, workspace, stride=1, dilation=1, layout=NHWC,
+                         strategy=STRATEGY_AUTO, stream=None):
+    """dw (and db unless None) = weight / bias gradients for input x and cotangent dy."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    _check_dev(x, "x", (torch.float32,))
+    _check_dev(dy, "dy", (torch.float32,))
+    _check_dev(dw, "dw", (torch.float32,))
+    if dw.dim() != 3 or int(dw.shape[0]) != C:
+        raise ValueError("dw must be (C, kH, kW)")
+    kH, kW = int(dw.shape[1]), int(dw.shape[2])
+    if db is not None:
+        _check_dev(db, "db", (torch.float32,))
+        if tuple(db.shape) != (C,):
+            raise ValueError("db must be (C,)")
+    Ho, Wo = -(-H // stride), -(-W // stride)
+    if tuple(dy.shape) != _shape(lay, N, Ho, Wo, C):
+        raise ValueError(f"dy shape {tuple(dy.shape)} != {_shape(lay, N, Ho, Wo, C)}")
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().dwconv2d_weight_grad(_ptr(x), _ptr(dy), _ptr(dw), _ptr(db), _ptr(workspace),
+                                    nbytes, N, H, W, C, kH, kW, stride, dilation, lay, strategy,
+                                    _stream(dw, stream))
+    _check_status(st, "dwconv2d_weight_grad")
+    return dw, db
+
+
+def weight_grad(x, dy, kH, kW, stride=1, dilation=1, layout=NHWC, with_bias=True,
+                strategy=STRATEGY_AUTO, stream=None):
+    """Allocate dW (C, kH, kW), db (C,) and the workspace; run the weight gradient."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    nbytes = dwconv2d_weight_grad_workspace_size(N, H, W, C, kH, kW, stride, dilation, lay,
+                                                 strategy)
+    ws = torch.empty(max(1, (nbytes + 15) // 16) * 4, dtype=torch.float32, device=x.device)
+    dw = torch.empty((C, kH, kW), dtype=torch.float32, device=x.device)
+    db = torch.empty((C,), dtype=torch.float32, device=x.device) if with_bias else None
+    return dwconv2d_weight_grad(x, dy, dw, db, ws, stride, dilation, lay, strategy, stream)

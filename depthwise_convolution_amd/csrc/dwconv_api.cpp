@@ -58,6 +58,8 @@ int check_pointers(const Problem &p, const float *in, const void *w, const float
 int run(const Problem &p, const float *in, const void *w, const float *b, float *out,
         int strategy, void *stream)
 {
+    if (p.op != DWCONV_OP_FWD && p.op != DWCONV_OP_INPUT_GRAD)
+        return DWCONV_ERR_BAD_OP;
     int st = dwconv::validate_problem(p);
     if (st != DWCONV_OK)
         return st;
@@ -122,7 +124,7 @@ int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int 
 {
     const Problem p = problem(op, wtype, has_bias, N, H, W, C, kH, kW, stride, dilation,
                               layout);
-    if (op == DWCONV_OP_INPUT_GRAD && has_bias)
+    if ((op == DWCONV_OP_INPUT_GRAD || op == DWCONV_OP_WEIGHT_GRAD) && has_bias)
         return DWCONV_ERR_BAD_OP;
     Plan pl;
     const int st = dwconv::make_plan(p, strategy, 0, &pl);
@@ -137,6 +139,71 @@ int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int 
     if (block)
         *block = pl.block;
     return DWCONV_OK;
+}
+
+int dwconv2d_weight_grad_workspace_size(int N, int H, int W, int C, int kH, int kW,
+                                        int stride, int dilation, int layout, int strategy,
+                                        long long *bytes)
+{
+    if (!bytes)
+        return DWCONV_ERR_NULL_PTR;
+    const Problem p = problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, kH, kW,
+                              stride, dilation, layout);
+    // The plan depends on pointer alignment, which is not known here: report
+    // the larger of the aligned plan and the fallback plan.
+    Plan a, u;
+    int st = dwconv::make_plan(p, strategy, 0, &a);
+    if (st != DWCONV_OK)
+        return st;
+    const long long need_a = a.workspace;
+    long long need_u = 0;
+    if (dwconv::make_plan(p, strategy, 4, &u) == DWCONV_OK)
+        need_u = u.workspace;
+    *bytes = need_a > need_u ? need_a : need_u;
+    return DWCONV_OK;
+}
+
+int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
+                         void *workspace, long long workspace_bytes,
+                         int N, int H, int W, int C, int kH, int kW,
+                         int stride, int dilation, int layout, int strategy, void *stream)
+{
+    const Problem p = problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, kH, kW,
+                              stride, dilation, layout);
+    int st = dwconv::validate_problem(p);
+    if (st != DWCONV_OK)
+        return st;
+    if (!x || !dy || !dw)
+        return DWCONV_ERR_NULL_PTR;
+    const std::uintptr_t bits = reinterpret_cast<std::uintptr_t>(x) |
+                                reinterpret_cast<std::uintptr_t>(dy) |
+                                reinterpret_cast<std::uintptr_t>(dw) |
+                                reinterpret_cast<std::uintptr_t>(db);
+    if ((bits & 3u) != 0)
+        return DWCONV_ERR_MISALIGNED;
+    Plan pl;
+    st = dwconv::make_plan(p, strategy,
+                           reinterpret_cast<std::uintptr_t>(x) |
+                               reinterpret_cast<std::uintptr_t>(dy), &pl);
+    if (st != DWCONV_OK)
+        return st;
+    if (!workspace || (reinterpret_cast<std::uintptr_t>(workspace) & 15u) != 0 ||
+        workspace_bytes < pl.workspace)
+        return DWCONV_ERR_WORKSPACE;
+    const long long Ho = (H + stride - 1) / stride, Wo = (W + stride - 1) / stride;
+    const Range rx = range_of(x, 4LL * N * H * W * C), rg = range_of(dy, 4LL * N * Ho * Wo * C);
+    const Range rw = range_of(dw, 4LL * C * kH * kW), rws = range_of(workspace, pl.workspace);
+    const Range outs[3] = {rw, rws, db ? range_of(db, 4LL * C) : Range{0, 0}};
+    for (int i = 0; i < 3; ++i) {
+        if (outs[i].hi == outs[i].lo)
+            continue;
+        if (overlap(outs[i], rx) || overlap(outs[i], rg))
+            return DWCONV_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (outs[j].hi != outs[j].lo && overlap(outs[i], outs[j]))
+                return DWCONV_ERR_ALIAS;
+    }
+    return dwconv::launch_wgrad(p, pl, x, dy, dw, db, workspace, stream);
 }
 
 const char *dwconv2d_strerror(int status)
@@ -155,6 +222,7 @@ const char *dwconv2d_strerror(int status)
     case DWCONV_ERR_LAUNCH: return "kernel launch failed";
     case DWCONV_ERR_BAD_OP: return "unknown op, or a bias given to the input gradient";
     case DWCONV_ERR_BAD_STRATEGY: return "unknown strategy, or it does not apply to this problem";
+    case DWCONV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     default: return "unknown status";
     }
 }

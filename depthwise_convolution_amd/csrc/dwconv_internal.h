@@ -24,6 +24,8 @@ enum Kind {
     KIND_DIRECT_NCHW = 2,  // one thread per (n, channel, row, col); taps from global
     KIND_TILED_NHWC = 3,   // stride 1: LDS row chunks with halo, rolling row accumulators
     KIND_TILED_NCHW = 4,   // stride 1: LDS tiles of one or more planes, rolling row accumulators
+    KIND_WGRAD_DIRECT = 5, // weight gradient, any layout/stride: workgroup = (position chunk, channel)
+    KIND_WGRAD_TILED_NHWC = 6, // weight gradient, NHWC stride 1: LDS x tiles, strips of row tiles
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
@@ -47,6 +49,24 @@ constexpr TiledVariant kTiledVariants[] = {
     {1, 31, 1, 2, 32, 1, 2},  {1, 31, 1, 2, 64, 1, 2},
 };
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
+
+// Compile-time variants of the tiled NHWC weight-gradient kernel: workgroup
+// geometry as for the forward (vec, cl, px, g); `strip` row tiles of
+// g - (kH-1)*d rows are walked by one workgroup (its partial sums cover
+// them all, which keeps the number of partial sums per weight small).
+struct WgradVariant { int kH, kW, d, vec, cl, px, g, strip; };
+constexpr WgradVariant kWgradVariants[] = {
+    {3, 3, 1, 4, 16, 1, 6, 8},  {3, 3, 1, 4, 8, 1, 6, 8},
+    {5, 5, 1, 4, 16, 1, 8, 4},
+    {7, 7, 1, 2, 32, 1, 10, 4},
+    {7, 7, 2, 2, 32, 1, 16, 2},
+    {1, 15, 1, 4, 32, 1, 2, 8},
+    {1, 31, 1, 2, 32, 1, 2, 8},
+};
+constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);
+
+// Output positions one workgroup of the direct weight-gradient kernel sums.
+constexpr int kWgradChunk = 4096;
 
 // Compile-time variants of the tiled NCHW kernel (same preference rule).
 // A workgroup of 256 threads covers pb planes (channels) x tx threads per
@@ -74,6 +94,10 @@ struct Plan {
     int nct, nwt, nst;  // tiled: channel tiles (NHWC) or plane groups (NCHW), column tiles, row tiles
     int pb;             // tiled NCHW: planes per workgroup
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
+    int strip;          // weight gradient, tiled: row tiles per workgroup
+    long long chunks;   // weight gradient: partial sums per weight (rows of the workspace)
+    long long workspace;// weight gradient: workspace bytes
+    long long grid2;    // weight gradient: workgroups of the reduction kernel
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
     long long total;    // direct: number of threads doing work
@@ -89,6 +113,13 @@ int validate_problem(const Problem &p);
 // of the tensor pointers' addresses (0 when unknown); vector widths are only
 // chosen when it shows 16-byte alignment.  Returns a DWCONV_ status.
 int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
+
+// Plan the weight gradient (op DWCONV_OP_WEIGHT_GRAD).  Returns a status.
+int make_wgrad_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
+
+// Enqueue the two kernels of a weight-gradient plan.
+int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *dy, float *dw,
+                 float *db, void *workspace, void *stream);
 
 // Enqueue the kernel of a plan made by make_plan on `stream` (a hipStream_t).
 // Returns DWCONV_OK, or DWCONV_ERR_LAUNCH if the runtime reports an error.

@@ -114,6 +114,24 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+typedef unsigned int u2_ext __attribute__((ext_vector_type(2)));
+
+// V consecutive floats (V = 1, 2 or 4) with one buffer load of matching width.
+template <int V>
+__device__ __forceinline__ void buf_vec(__amdgpu_buffer_rsrc_t r, int off, float (&out)[V])
+{
+    if constexpr (V == 4) {
+        const float4 t = buf_f4(r, off);
+        out[0] = t.x; out[1] = t.y; out[2] = t.z; out[3] = t.w;
+    } else if constexpr (V == 2) {
+        const u2_ext t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        const f2_ext f = __builtin_bit_cast(f2_ext, t);
+        out[0] = f.x; out[1] = f.y;
+    } else {
+        out[0] = buf_f32(r, off);
+    }
+}
+
 // One weight element, widened to fp32 (f16 by value).
 __device__ __forceinline__ float buf_w(__amdgpu_buffer_rsrc_t r, int idx, float *)
 {
@@ -612,6 +630,251 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Weight and bias gradients (LeanMlir "Depthwise": weight-VJP, bias-gradient
+// closed form).  Two stages, deterministic (fixed summation order, no
+// atomics):
+//   stage 1 writes partial sums part[chunk][c][tap], tap = kh*kW + kw for
+//           dW and tap = kH*kW for db, each over one chunk of dy positions;
+//   stage 2 adds the chunks of every (c, tap) column in a fixed order.
+// ---------------------------------------------------------------------------
+struct WgradArgs {
+    int N, C, H, W, kH, kW, d, pH, pW;
+    int OH, OW;             // dy extents
+    int nct, nwt, nsp;      // tiled: channel tiles, column tiles, strips
+    int chunks;             // rows of part[]
+};
+
+__device__ __forceinline__ int elem_index(bool nhwc, int C, int H, int W, int n, int c, int h,
+                                          int w)
+{
+    return nhwc ? ((n * H + h) * W + w) * C + c : ((n * C + c) * H + h) * W + w;
+}
+
+// Deterministic sum of v over a 256-thread workgroup (fixed tree); the
+// result is valid in thread 0.  `red` holds 256 floats.
+__device__ __forceinline__ float block_sum_256(float v, float *red)
+{
+    const int tid = threadIdx.x;
+    red[tid] = v;
+    __syncthreads();
+#pragma unroll
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off)
+            red[tid] += red[tid + off];
+        __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// Stage 1, any layout and stride: workgroup = (chunk of kWgradChunk dy
+// positions, channel c); each thread strides over the chunk's positions.
+template <bool NHWC, int S>
+__global__ __launch_bounds__(256) void k_wgrad_direct(const float *__restrict__ x,
+                                                      const float *__restrict__ dy,
+                                                      float *__restrict__ part, WgradArgs a)
+{
+    __shared__ float red[256];
+    const int c = blockIdx.x % a.C;
+    const int ck = blockIdx.x / a.C;
+    const int total = a.N * a.OH * a.OW;
+    const int p0 = ck * kWgradChunk, p1 = min(p0 + kWgradChunk, total);
+    const int KK = a.kH * a.kW;
+    for (int tap = 0; tap <= KK; ++tap) {
+        const int kh = tap / a.kW, kw = tap - (tap / a.kW) * a.kW;
+        float acc = 0.0f;
+        for (int pp = p0 + threadIdx.x; pp < p1; pp += 256) {
+            const int wo = pp % a.OW;
+            const int t = pp / a.OW;
+            const int ho = t % a.OH;
+            const int n = t / a.OH;
+            const float g = dy[elem_index(NHWC, a.C, a.OH, a.OW, n, c, ho, wo)];
+            if (tap == KK) {
+                acc += g;
+            } else {
+                const int hi = ho * S + kh * a.d - a.pH, wi = wo * S + kw * a.d - a.pW;
+                if (hi >= 0 && hi < a.H && wi >= 0 && wi < a.W)
+                    acc = fmaf(x[elem_index(NHWC, a.C, a.H, a.W, n, c, hi, wi)], g, acc);
+            }
+        }
+        const float sum = block_sum_256(acc, red);
+        if (threadIdx.x == 0)
+            part[((long long)ck * a.C + c) * (KK + 1) + tap] = sum;
+    }
+}
+
+// Stage 1, NHWC stride 1: a workgroup (256 threads: CL across channels x
+// 256/CL pixel slots of PX columns) walks STRIP row tiles of one column
+// tile.  Per row tile it stages G input rows (+ column halo) in LDS and
+// loads its dy rows straight into registers (each dy element is used by one
+// thread only); every thread accumulates x*dy for all kH*kW taps of its
+// channels, and at the end the pixel slots are summed through LDS.
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int STRIP>
+__global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restrict__ x,
+                                                          const float *__restrict__ dy,
+                                                          float *__restrict__ part, WgradArgs a)
+{
+    constexpr int R = (KH - 1) * D + 1, TH = G - R + 1, TW = PX * 256 / CL, CG = CL * VEC;
+    constexpr int TWI = TW + (KW - 1) * D, VPC = CG / 4, VPR = TWI * VPC, VCH = G * VPR;
+    constexpr int NV = (VCH + 255) / 256, KK = KH * KW, NP = 256 / CL;
+    constexpr int XW = PX + (KW - 1) * D;
+    // the final per-(channel, tap) sums go through LDS in groups of TG taps
+    constexpr int TGF = (VCH * 4) / (256 * VEC);
+    constexpr int TG = TGF < 1 ? 1 : (TGF > KK + 1 ? KK + 1 : TGF);
+    constexpr int LDSF = (VCH * 4 > 256 * VEC * TG) ? VCH * 4 : 256 * VEC * TG;
+    __shared__ float4 lds4[(LDSF + 3) / 4];
+    float *lds = reinterpret_cast<float *>(lds4);
+
+    int tile = blockIdx.x;
+    const int ct = tile % a.nct;
+    tile /= a.nct;
+    const int chunk = tile;                 // (n, strip, column tile): row of part[]
+    const int wt = tile % a.nwt;
+    tile /= a.nwt;
+    const int sp = tile % a.nsp;
+    const int n = tile / a.nsp;
+    const int c0 = ct * CG, w0 = wt * TW;
+    const int tid = threadIdx.x;
+    const int q = tid % CL, p = tid / CL;
+    const int cq = c0 + q * VEC;
+    const int ow = w0 + p * PX;
+    const int cbase = w0 - a.pW;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
+
+    float acc[KK + 1][VEC];                 // taps kh*KW + kw, then the bias
+#pragma unroll
+    for (int t = 0; t <= KK; ++t)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            acc[t][v] = 0.0f;
+
+    const int t0 = sp * STRIP, t1 = min(t0 + STRIP, (a.H + TH - 1) / TH);
+    for (int tt = t0; tt < t1; ++tt) {
+        const int h0 = tt * TH;
+        const int nrows = min(TH, a.H - h0) + R - 1;
+        const int rbase = h0 - a.pH;
+        // this row tile's x rows (+ halo) and, per thread, its dy values
+        float4 stage[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = tid + i * 256;
+            const int g = e / VPR;
+            const int rem = e - g * VPR;
+            const int col = rem / VPC;
+            const int cv = rem - col * VPC;
+            const int row = rbase + g, gc = cbase + col, ch = c0 + cv * 4;
+            const bool ok = e < VCH && g < nrows && row >= 0 && row < a.H && gc >= 0 &&
+                            gc < a.W && ch < a.C;
+            stage[i] = buf_f4(rx, ok ? ((row * a.W + gc) * a.C + ch) * 4 : kOutOfRange);
+        }
+        float gv[TH][PX][VEC];
+#pragma unroll
+        for (int m = 0; m < TH; ++m)
+#pragma unroll
+            for (int j = 0; j < PX; ++j) {
+                const bool ok = h0 + m < a.H && ow + j < a.W && cq < a.C;
+                buf_vec<VEC>(rg, ok ? (((h0 + m) * a.W + ow + j) * a.C + cq) * 4 : kOutOfRange,
+                             gv[m][j]);
+            }
+        if (tt > t0)
+            __syncthreads();              // every thread done with the previous tile
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = tid + i * 256;
+            if (e < VCH)
+                lds4[e] = stage[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TH; ++m) {
+#pragma unroll
+            for (int j = 0; j < PX; ++j)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    acc[KK][v] += gv[m][j][v];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int u = m + kh * D;   // staged row of tap row kh for output row m
+                float xv[XW][VEC];
+#pragma unroll
+                for (int i = 0; i < XW; ++i) {
+                    const float *src = lds + ((u * TWI + p * PX + i) * CG + q * VEC);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        xv[i][v] = src[v];
+                }
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                    for (int j = 0; j < PX; ++j)
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v)
+                            acc[kh * KW + kw][v] =
+                                fmaf(xv[j + kw * D][v], gv[m][j][v], acc[kh * KW + kw][v]);
+            }
+        }
+    }
+
+    // sum the NP pixel slots of every (channel, tap) in a fixed order, TG taps at a time
+#pragma unroll
+    for (int tb = 0; tb <= KK; tb += TG) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TG; ++k)
+            if (tb + k <= KK)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    lds[(k * 256 + tid) * VEC + v] = acc[tb + k][v];
+        __syncthreads();
+        for (int e = tid; e < CG * TG; e += 256) {
+            const int k = e / CG, cl = e - k * CG;
+            const int qq = cl / VEC, v = cl - qq * VEC;
+            if (tb + k <= KK) {
+                float s = 0.0f;
+                for (int pp = 0; pp < NP; ++pp)
+                    s += lds[(k * 256 + pp * CL + qq) * VEC + v];
+                if (c0 + cl < a.C)
+                    part[((long long)chunk * a.C + c0 + cl) * (KK + 1) + tb + k] = s;
+            }
+        }
+    }
+}
+
+// Stage 2: 16 columns of part[] per workgroup, 16 threads per column each
+// summing every 16th chunk, then a fixed 16-way tree.
+__global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ part,
+                                                      float *__restrict__ dw,
+                                                      float *__restrict__ db, int chunks,
+                                                      int C, int KK)
+{
+    __shared__ float red[16][17];
+    const int cols = C * (KK + 1);
+    const int lane = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int col = blockIdx.x * 16 + lane;
+    float s = 0.0f;
+    if (col < cols)
+        for (int r = j; r < chunks; r += 16)
+            s += part[(long long)r * cols + col];
+    red[j][lane] = s;
+    __syncthreads();
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+        if (j < off)
+            red[j][lane] += red[j + off][lane];
+        __syncthreads();
+    }
+    if (j == 0 && col < cols) {
+        const int c = col / (KK + 1), tap = col - c * (KK + 1);
+        if (tap < KK)
+            dw[c * KK + tap] = red[0][lane];
+        else if (db)
+            db[c] = red[0][lane];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
 DirectArgs direct_args(const Problem &p, const Plan &pl)
@@ -750,6 +1013,26 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
     return DWCONV_OK;
 }
 
+typedef void (*WgradFn)(const float *, const float *, float *, WgradArgs);
+
+template <int V>
+constexpr WgradFn wgrad_fn()
+{
+    constexpr WgradVariant t = kWgradVariants[V];
+    return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.strip>;
+}
+
+template <int... Vs>
+void fill_wgrad(WgradFn (&fn)[kNumWgradVariants], std::integer_sequence<int, Vs...>)
+{
+    ((fn[Vs] = wgrad_fn<Vs>()), ...);
+}
+
+struct WgradTable {
+    WgradFn fn[kNumWgradVariants];
+    WgradTable() { fill_wgrad(fn, std::make_integer_sequence<int, kNumWgradVariants>()); }
+};
+
 }  // namespace
 
 // Run a validated plan on `stream`.  Returns a DWCONV_ status.
@@ -778,6 +1061,40 @@ int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w
     }
     if (st != DWCONV_OK)
         return st;
+    return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
+}
+
+int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *dy, float *dw,
+                 float *db, void *workspace, void *stream_v)
+{
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream_v);
+    float *part = reinterpret_cast<float *>(workspace);
+    WgradArgs a;
+    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
+    a.pH = pl.pH; a.pW = pl.pW; a.OH = pl.OH; a.OW = pl.OW;
+    a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.chunks = (int)pl.chunks;
+    if (pl.kind == KIND_WGRAD_TILED_NHWC) {
+        static const WgradTable table;
+        if (pl.variant < 0 || pl.variant >= kNumWgradVariants)
+            return DWCONV_ERR_BAD_STRATEGY;
+        hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x,
+                           dy, part, a);
+    } else if (pl.kind == KIND_WGRAD_DIRECT) {
+        const dim3 g((unsigned)pl.grid), b(256);
+        const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
+        if (nhwc && p.stride == 1)
+            hipLaunchKernelGGL((k_wgrad_direct<true, 1>), g, b, 0, st, x, dy, part, a);
+        else if (nhwc)
+            hipLaunchKernelGGL((k_wgrad_direct<true, 2>), g, b, 0, st, x, dy, part, a);
+        else if (p.stride == 1)
+            hipLaunchKernelGGL((k_wgrad_direct<false, 1>), g, b, 0, st, x, dy, part, a);
+        else
+            hipLaunchKernelGGL((k_wgrad_direct<false, 2>), g, b, 0, st, x, dy, part, a);
+    } else {
+        return DWCONV_ERR_BAD_STRATEGY;
+    }
+    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw, db,
+                       (int)pl.chunks, p.C, p.kH * p.kW);
     return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
 }
 

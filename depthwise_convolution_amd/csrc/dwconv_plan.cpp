@@ -25,7 +25,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 int validate_problem(const Problem &p)
 {
-    if (p.op != DWCONV_OP_FWD && p.op != DWCONV_OP_INPUT_GRAD)
+    if (p.op != DWCONV_OP_FWD && p.op != DWCONV_OP_INPUT_GRAD && p.op != DWCONV_OP_WEIGHT_GRAD)
         return DWCONV_ERR_BAD_OP;
     if (p.N < 1 || p.H < 1 || p.W < 1 || p.C < 1 || p.kH < 1 || p.kW < 1)
         return DWCONV_ERR_BAD_DIM;
@@ -159,6 +159,8 @@ static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 
 int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
 {
+    if (p.op == DWCONV_OP_WEIGHT_GRAD)
+        return make_wgrad_plan(p, strategy, ptr_bits, pl);
     int st = validate_problem(p);
     if (st != DWCONV_OK)
         return st;
@@ -193,6 +195,100 @@ int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (strategy == DWCONV_STRATEGY_TILED)
         return DWCONV_ERR_BAD_STRATEGY;
     plan_direct(p, ptr_bits, pl);
+    return DWCONV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradient.  Stage 1 writes partial sums [chunk][C][kH*kW + 1] (the
+// last column is the bias gradient) to the workspace; stage 2 adds the
+// chunks of every column in a fixed order.
+// ---------------------------------------------------------------------------
+static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
+{
+    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NHWC || p.C % 4 != 0 || (ptr_bits & 15u))
+        return false;
+    if (4LL * p.H * p.W * p.C >= (1LL << 31))
+        return false;
+    int best = -1;
+    double best_fill = -1.0;
+    for (int i = 0; i < kNumWgradVariants; ++i) {
+        const WgradVariant &v = kWgradVariants[i];
+        if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation)
+            continue;
+        const int cg = v.cl * v.vec;
+        const double fill = (double)p.C / (ceil_div(p.C, cg) * cg);
+        if (fill >= 0.75) {
+            best = i;
+            break;
+        }
+        if (fill > best_fill) {
+            best = i;
+            best_fill = fill;
+        }
+    }
+    if (best < 0)
+        return false;
+    const WgradVariant &v = kWgradVariants[best];
+    const int R = (v.kH - 1) * v.d + 1;
+    pl->kind = KIND_WGRAD_TILED_NHWC;
+    pl->variant = best;
+    pl->vec = v.vec;
+    pl->cl = v.cl;
+    pl->tw = v.px * 256 / v.cl;
+    pl->th = v.g - R + 1;
+    pl->strip = v.strip;
+    pl->nct = ceil_div(p.C, v.cl * v.vec);
+    pl->nwt = ceil_div(p.W, pl->tw);
+    pl->nst = ceil_div(ceil_div(p.H, pl->th), v.strip);   // strips
+    pl->chunks = (long long)p.N * pl->nst * pl->nwt;
+    pl->grid = pl->chunks * pl->nct;
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_s%d",
+                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.strip);
+    return true;
+}
+
+static void plan_wgrad_direct(const Problem &p, Plan *pl)
+{
+    const long long positions = (long long)p.N * pl->OH * pl->OW;   // dy positions
+    pl->kind = KIND_WGRAD_DIRECT;
+    pl->variant = -1;
+    pl->chunks = (positions + kWgradChunk - 1) / kWgradChunk;
+    pl->grid = pl->chunks * p.C;
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_direct_%s_s%d",
+                  p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride);
+}
+
+int make_wgrad_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
+{
+    int st = validate_problem(p);
+    if (st != DWCONV_OK)
+        return st;
+    if (strategy != DWCONV_STRATEGY_AUTO && strategy != DWCONV_STRATEGY_DIRECT &&
+        strategy != DWCONV_STRATEGY_TILED)
+        return DWCONV_ERR_BAD_STRATEGY;
+    std::memset(pl, 0, sizeof *pl);
+    pl->pH = p.dilation * (p.kH - 1) / 2;
+    pl->pW = p.dilation * (p.kW - 1) / 2;
+    pl->IH = p.H; pl->IW = p.W;
+    pl->OH = ceil_div(p.H, p.stride); pl->OW = ceil_div(p.W, p.stride);
+    bool tiled = false;
+    if (strategy != DWCONV_STRATEGY_DIRECT) {
+        Plan t = *pl;
+        tiled = plan_wgrad_tiled(p, ptr_bits, &t);
+        if (tiled)
+            *pl = t;
+        else if (strategy == DWCONV_STRATEGY_TILED)
+            return DWCONV_ERR_BAD_STRATEGY;
+    }
+    if (!tiled)
+        plan_wgrad_direct(p, pl);
+    const long long cols = (long long)p.C * (p.kH * p.kW + 1);
+    if (pl->chunks * cols >= (1LL << 31))
+        return DWCONV_ERR_BAD_DIM;
+    pl->workspace = 4 * pl->chunks * cols;
+    pl->grid2 = (cols + 15) / 16;
     return DWCONV_OK;
 }
 

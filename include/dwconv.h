@@ -60,6 +60,7 @@ extern "C" {
 #define DWCONV_ERR_LAUNCH      -10  /* the HIP runtime reported an error at launch   */
 #define DWCONV_ERR_BAD_OP      -11  /* op not FWD or INPUT_GRAD                      */
 #define DWCONV_ERR_BAD_STRATEGY -12 /* strategy unknown, or not applicable to the problem */
+#define DWCONV_ERR_WORKSPACE   -13  /* workspace NULL, misaligned or smaller than required */
 
 /* ---- enumerations (passed as int) -------------------------------------- */
 #define DWCONV_LAYOUT_NHWC 0   /* channel innermost (the ggml page's CWHN)    */
@@ -70,6 +71,7 @@ extern "C" {
 
 #define DWCONV_OP_FWD        0 /* y  = dwconv(x; W, b)                        */
 #define DWCONV_OP_INPUT_GRAD 1 /* dx = dwconv_input_grad(dy; W)               */
+#define DWCONV_OP_WEIGHT_GRAD 2 /* dW, db = dwconv_weight_grad(x, dy) (planning only) */
 
 /* Which tiling to run a problem under (cubek-convolution "depthwise" module:
  * a strategy enum selects the tiling, one launch function runs it). */
@@ -119,6 +121,33 @@ int dwconv2d_launch(int op, const float *in, const void *w, int wtype, const flo
 int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int C,
                       int kH, int kW, int stride, int dilation, int layout, int strategy,
                       char *name, int name_len, long long *grid, int *block);
+
+/*
+ * Weight and bias gradients (LeanMlir "Depthwise": the weight-VJP -- the
+ * forward is affine in W -- and the bias-gradient closed form):
+ *
+ *   dW[c,kh,kw] = sum_{n,ho,wo} x[n, c, ho*s + kh*d - pH, wo*s + kw*d - pW] * dy[n,c,ho,wo]
+ *   db[c]       = sum_{n,ho,wo} dy[n,c,ho,wo]
+ *
+ * over in-range input positions.  x: [N,H,W,C] / [N,C,H,W] float32; dy:
+ * [N,Ho,Wo,C] / [N,C,Ho,Wo] float32; dw: [C][kH][kW] float32 output; db: [C]
+ * float32 output or NULL.  Both outputs are overwritten.  The sums are
+ * deterministic (fixed order, no atomics): per-tile partial sums go to
+ * `workspace`, a caller-owned device buffer of at least the size that
+ * dwconv2d_weight_grad_workspace_size reports for the same arguments
+ * (16-byte aligned; its contents on entry do not matter), and a second
+ * kernel adds them up.  strategy: DWCONV_STRATEGY_AUTO / DIRECT / TILED as
+ * for dwconv2d_launch.  Errors as above, plus DWCONV_ERR_WORKSPACE when the
+ * workspace is NULL, misaligned or too small.
+ */
+int dwconv2d_weight_grad_workspace_size(int N, int H, int W, int C, int kH, int kW,
+                                        int stride, int dilation, int layout, int strategy,
+                                        long long *bytes);
+
+int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
+                         void *workspace, long long workspace_bytes,
+                         int N, int H, int W, int C, int kH, int kW,
+                         int stride, int dilation, int layout, int strategy, void *stream);
 
 /* Static text for a status code ("unknown status" for unknown codes). */
 const char *dwconv2d_strerror(int status);

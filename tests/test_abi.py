@@ -176,3 +176,52 @@ def test_python_binding_rejects_cpu_tensors():
     w = torch.zeros(4, 3, 3)
     with pytest.raises(ValueError):
         dw.fwd(x, w)
+
+
+# ------------------------------------------------------------- weight gradient
+WS = 0x50_0000_0000
+
+
+def _wg(L, x=X, dy=B, dw=Y, db=WP, ws=WS, ws_bytes=1 << 30, N=1, H=8, W=8, C=4, kH=3, kW=3,
+        s=1, d=1, lay=0, strat=0):
+    return L.dwconv2d_weight_grad(VP(x) if x else None, VP(dy) if dy else None,
+                                  VP(dw) if dw else None, VP(db) if db else None,
+                                  VP(ws) if ws else None, ws_bytes, N, H, W, C, kH, kW, s, d,
+                                  lay, strat, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(x=0), -1), (dict(dy=0), -1), (dict(dw=0), -1),
+    (dict(H=0), -2), (dict(s=3), -3), (dict(d=0), -4), (dict(kW=2), -5), (dict(lay=5), -6),
+    (dict(x=X + 2), -9), (dict(db=WP + 1), -9),
+    (dict(ws=0), -13), (dict(ws=WS + 4), -13), (dict(ws_bytes=16), -13),
+    (dict(dw=X + 16), -8), (dict(db=B + 8), -8), (dict(ws=Y), -8), (dict(db=WS + 64), -8),
+    (dict(strat=9), -12),
+])
+def test_weight_grad_rejects(L, kwargs, code):
+    assert _wg(L, **kwargs) == code
+
+
+def test_weight_grad_workspace_and_plans():
+    n = dw.dwconv2d_weight_grad_workspace_size(1, 512, 512, 256, 3, 3)
+    name, grid, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 512, 512, 256, 3, 3)
+    assert name.startswith("wgrad_tiled_nhwc") and n > 0 and n % (4 * 256 * 10) == 0
+    # the reported size covers the fallback plan too (used for misaligned pointers)
+    d = dw.dwconv2d_weight_grad_workspace_size(1, 512, 512, 256, 3, 3,
+                                                strategy=dw.STRATEGY_DIRECT)
+    assert n >= d
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 3, 3, stride=2)
+    assert name.startswith("wgrad_direct_nhwc_s2")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 3, 3, layout=dw.NCHW)
+    assert name.startswith("wgrad_direct_nchw")
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 8, 8, 4, 3, 3, has_bias=True)
+    assert e.value.status == -11
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 8, 8, 4, 9, 9, strategy=dw.STRATEGY_TILED)
+    assert e.value.status == -12
+
+
+def test_launch_rejects_weight_grad_op(L):
+    args = [VP(X), VP(WP), 0, None, VP(Y), 1, 8, 8, 4, 3, 3, 1, 1, 0]
+    assert L.dwconv2d_launch(2, *args, 0, None) == -11
