@@ -64,6 +64,12 @@ def make_problem(torch, wl, layout, seed=0):
     shape_x = tuple(inp["x"].shape)
     t["y"] = torch.empty(tuple(inp["dy"].shape), dtype=torch.float32, device="cuda")
     t["dx"] = torch.empty(shape_x, dtype=torch.float32, device="cuda")
+    import depthwise_convolution_amd as dw
+    nws = dw.dwconv2d_weight_grad_workspace_size(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                                 wl.stride, wl.dilation, layout)
+    t["ws"] = torch.empty(max(4, (nws + 15) // 16 * 4), dtype=torch.float32, device="cuda")
+    t["dW"] = torch.empty((wl.C, wl.kH, wl.kW), dtype=torch.float32, device="cuda")
+    t["db"] = torch.empty((wl.C,), dtype=torch.float32, device="cuda")
     return t
 
 
@@ -73,6 +79,17 @@ def launch_fwd(dw, wl, t, layout, stream):
 
 def launch_ig(dw, wl, t, layout, stream):
     dw.dwconv2d_input_grad(t["dy"], t["w"], t["dx"], wl.stride, wl.dilation, layout, stream)
+
+
+def launch_wgrad(dw, wl, t, layout, stream):
+    dw.dwconv2d_weight_grad(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride, wl.dilation,
+                            layout, dw.STRATEGY_AUTO, stream)
+
+
+def wgrad_bytes(wl):
+    """Algorithmic bytes of the weight + bias gradient: x + dy + dW + db."""
+    return (4 * wl.N * wl.H * wl.W * wl.C + 4 * wl.N * wl.Ho * wl.Wo * wl.C
+            + 4 * wl.C * wl.kH * wl.kW + 4 * wl.C)
 
 
 def time_kernel(torch, fn, stream, iters, flush=None):
@@ -129,11 +146,15 @@ def per_config_table(torch, dw, iters=20):
         for layout in (workloads.NHWC, workloads.NCHW):
             t = make_problem(torch, wl, layout, seed=0)
             for op, fn, nbytes in (("fwd", launch_fwd, wl.fwd_bytes()),
-                                   ("ig", launch_ig, wl.ig_bytes())):
+                                   ("ig", launch_ig, wl.ig_bytes()),
+                                   ("wgrad", launch_wgrad, wgrad_bytes(wl))):
+                if op == "wgrad" and wl.fp16_weights:
+                    continue              # the weight gradient does not read the weights
                 call = (lambda f=fn: f(dw, wl, t, layout, stream))
-                kname = dw.dwconv2d_describe(dw.OP_FWD if op == "fwd" else dw.OP_INPUT_GRAD,
-                                             wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
-                                             wl.dilation, layout, int(wl.fp16_weights),
+                opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
+                kname = dw.dwconv2d_describe(opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                             wl.stride, wl.dilation, layout,
+                                             0 if op == "wgrad" else int(wl.fp16_weights),
                                              op == "fwd")[0]
                 time_kernel(torch, call, stream, 3)
                 warm = statistics.median(time_kernel(torch, call, stream, iters))
@@ -213,16 +234,37 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     fwd_avg, ig_avg = statistics.mean(fwd_us), statistics.mean(ig_us)
-    dom, dom_us, dom_bytes = (("fwd", fwd_avg, wl.fwd_bytes()) if fwd_avg >= ig_avg
-                              else ("ig", ig_avg, wl.ig_bytes()))
+    dom, dom_bytes = ("fwd", wl.fwd_bytes()) if fwd_avg >= ig_avg else ("ig", wl.ig_bytes())
     dom_kernel = dw.dwconv2d_describe(dw.OP_FWD if dom == "fwd" else dw.OP_INPUT_GRAD, wl.N,
                                       wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation,
                                       layout, 0, dom == "fwd")[0]
+    # Dominant kernel's launch duration with the event overhead amortised: two
+    # events around 40 back-to-back launches that alternate between two
+    # disjoint buffer sets (256 MiB in / out each), so no launch finds its
+    # input in the 256 MB Infinity Cache.
+    alt = {"x": t["dy"] if dom == "fwd" else t["x"], "y": t["dx"] if dom == "fwd" else t["y"]}
+    assert t["x"].shape == t["dy"].shape, "the alternating-buffer timing needs stride 1"
+    k_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n_rep = 40
+    with torch.cuda.stream(stream):
+        for i in range(n_rep + 4):
+            if i == 4:
+                k_ev[0].record(stream)
+            if dom == "fwd":
+                src, dst = (t["x"], t["y"]) if i % 2 == 0 else (alt["x"], alt["y"])
+                dw.dwconv2d_fwd(src, t["w"], t["b"], dst, wl.stride, wl.dilation, layout, stream)
+            else:
+                src, dst = (t["dy"], t["dx"]) if i % 2 == 0 else (alt["y"], alt["x"])
+                dw.dwconv2d_input_grad(src, t["w"], dst, wl.stride, wl.dilation, layout, stream)
+        k_ev[1].record(stream)
+    torch.cuda.synchronize()
+    dom_us = k_ev[0].elapsed_time(k_ev[1]) * 1e3 / n_rep
     achieved = dom_bytes / dom_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": load_traffic(dom), "kernel": dom_kernel,
                 "avg_launch_us": round(dom_us, 2),
+                "avg_launch_us_events_each_launch": round(fwd_avg if dom == "fwd" else ig_avg, 2),
                 "algorithmic_bytes_per_launch": dom_bytes}
 
     result = {
@@ -240,6 +282,26 @@ def main():
         "ig_pct_peak": round(100 * wl.ig_bytes() / ig_avg / 1e3 / PEAK_HBM_GBS, 1),
         "roofline": roofline,
     }
+    # weight + bias gradient of the same workload (reads x and dy), timed on
+    # its own after the step loop: two kernels per call (partial sums, then
+    # their fixed-order reduction), timed together
+    wg = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            launch_wgrad(dw, wl, t, layout, stream)
+        for e in wg:
+            launch_fwd(dw, wl, t, layout, stream)     # evicts x/dy between calls like a step
+            e[0].record(stream)
+            launch_wgrad(dw, wl, t, layout, stream)
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    wg_us = statistics.mean(e[0].elapsed_time(e[1]) * 1e3 for e in wg)
+    result["wgrad"] = {
+        "kernel": dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                       wl.stride, wl.dilation, layout)[0],
+        "us": round(wg_us, 2), "algorithmic_bytes": wgrad_bytes(wl),
+        "GBs": round(wgrad_bytes(wl) / wg_us / 1e3, 1),
+        "pct_peak": round(100 * wgrad_bytes(wl) / wg_us / 1e3 / PEAK_HBM_GBS, 1)}
     del t
     torch.cuda.empty_cache()
     if args.calib_copy:
