@@ -6,6 +6,12 @@ It shares nothing with the HIP path (``depthwise_convolution_amd``); the only
 code both sides see is the seeded input generator, which holds none of the
 method's arithmetic.
 
+The general routines (``*_general``) take explicit per-side padding
+``pads = (top, bottom, left, right)`` (negative pads crop) and a channel multiplier ``mult``
+(output channel ``o`` reads input channel ``o // mult``; weights
+``(mult*C, kH, kW)``); ``same_pads`` and ``xla_same_pads`` give the two SAME
+paddings as explicit pads.
+
 All arithmetic is in ``dwconv_oracle.c`` (double-precision accumulation, one
 output at a time, the plain definitions from the LeanMlir "Depthwise" page:
 forward equation, reversed-kernel and direct input-gradient forms, stride-2 as
@@ -41,8 +47,12 @@ def _configure(lib):
     lib.dwo_dense_conv.argtypes = [_f32p, _f32p, _vp, _f64p] + [_i] * 10
     lib.dwo_weight_grad.argtypes = [_f32p, _f32p, _f64p, _vp] + [_i] * 10
     lib.dwo_bias_grad.argtypes = [_f32p, _f64p, _vp] + [_i] * 5
+    lib.dwo_fwd_general.argtypes = [_f32p, _vp, _i, _vp, _f64p, _vp] + [_i] * 15
+    lib.dwo_input_grad_general.argtypes = [_f32p, _vp, _i, _f64p, _vp] + [_i] * 15
+    lib.dwo_weight_grad_general.argtypes = [_f32p, _f32p, _f64p, _vp] + [_i] * 15
     for f in ("dwo_fwd", "dwo_input_grad", "dwo_input_grad_direct",
-              "dwo_dense_conv", "dwo_weight_grad", "dwo_bias_grad", "dwo_version"):
+              "dwo_dense_conv", "dwo_weight_grad", "dwo_bias_grad", "dwo_version",
+              "dwo_fwd_general", "dwo_input_grad_general", "dwo_weight_grad_general"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -197,3 +207,98 @@ def bias_grad(dy, layout=NHWC):
     S = np.empty_like(db)
     lib.dwo_bias_grad(dy, db, _ptr(S), N, Ho, Wo, C, layout)
     return db, S
+
+
+# ---------------------------------------------------------------------------
+# Explicit padding and channel multiplier
+# ---------------------------------------------------------------------------
+def same_pads(H, W, kH, kW, stride=1, dilation=1):
+    """Symmetric SAME padding (the LeanMlir forward equation's p = d*(k-1)/2 on
+    every side, odd kernels) as explicit (top, bottom, left, right) pads."""
+    assert kH % 2 == 1 and kW % 2 == 1
+    ph, pw = dilation * (kH - 1) // 2, dilation * (kW - 1) // 2
+    return (ph, ph, pw, pw)
+
+
+def xla_same_pads(H, W, kH, kW, stride=1, dilation=1):
+    """The LeanMlir page's stride-2 XLA-SAME as explicit pads: the stride-1
+    SAME result kept at the ODD positions.  Output row ho then reads input
+    rows 2*ho + 1 + kh*d - p, i.e. a top pad of p - 1; a bottom pad of p
+    makes the output extent floor(H/2), the number of odd positions.  (On
+    even extents with at least two taps per axis this is XLA's own SAME
+    padding.)  At stride 1 it is the symmetric SAME padding."""
+    ph, pw = same_pads(H, W, kH, kW, 1, dilation)[0::2]
+    if stride == 1:
+        return (ph, ph, pw, pw)
+    assert stride == 2
+    return (ph - 1, ph, pw - 1, pw)
+
+
+def out_extents_padded(H, W, kH, kW, stride, dilation, pads):
+    """Window positions that fit the padded input along each axis."""
+    t, b, l, r = pads
+    Ho = (H + t + b - dilation * (kH - 1) - 1) // stride + 1
+    Wo = (W + l + r - dilation * (kW - 1) - 1) // stride + 1
+    return Ho, Wo
+
+
+def fwd_general(x, w, b=None, stride=1, dilation=1, pads=None, mult=1, layout=NHWC,
+                nthreads=1, with_sum=True):
+    """Forward with explicit pads and channel multiplier.  x has C input
+    channels, w is (mult*C, kH, kW), b (mult*C,) or None.  pads None means
+    symmetric SAME.  Returns (y, S) with mult*C output channels."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w, wt = _weights(w)
+    N, H, W, C = _nhwc_dims(x.shape, layout)
+    kH, kW = w.shape[1], w.shape[2]
+    assert w.shape[0] == mult * C
+    if pads is None:
+        pads = same_pads(H, W, kH, kW, stride, dilation)
+    Ho, Wo = out_extents_padded(H, W, kH, kW, stride, dilation, pads)
+    assert Ho >= 1 and Wo >= 1
+    bb = None if b is None else np.ascontiguousarray(b, dtype=np.float32)
+    y = np.empty(_shape(layout, N, Ho, Wo, mult * C), np.float64)
+    S = np.empty_like(y) if with_sum else None
+    lib.dwo_fwd_general(x, _ptr(w), wt, _ptr(bb), y, _ptr(S), N, H, W, C, mult, kH, kW,
+                        stride, dilation, pads[0], pads[2], Ho, Wo, layout, nthreads)
+    return y, S
+
+
+def input_grad_general(dy, w, H, W, stride=1, dilation=1, pads=None, mult=1, layout=NHWC,
+                       nthreads=1, with_sum=True):
+    """Input gradient of fwd_general.  H, W are the forward input extents;
+    dy has mult*C channels.  Returns (dx, S) with C channels."""
+    lib = _load()
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    w, wt = _weights(w)
+    N, Ho, Wo, Co = _nhwc_dims(dy.shape, layout)
+    assert Co % mult == 0 and w.shape[0] == Co
+    C = Co // mult
+    kH, kW = w.shape[1], w.shape[2]
+    if pads is None:
+        pads = same_pads(H, W, kH, kW, stride, dilation)
+    assert (Ho, Wo) == out_extents_padded(H, W, kH, kW, stride, dilation, pads)
+    dx = np.empty(_shape(layout, N, H, W, C), np.float64)
+    S = np.empty_like(dx) if with_sum else None
+    lib.dwo_input_grad_general(dy, _ptr(w), wt, dx, _ptr(S), N, H, W, C, mult, kH, kW,
+                               stride, dilation, pads[0], pads[2], Ho, Wo, layout, nthreads)
+    return dx, S
+
+
+def weight_grad_general(x, dy, kH, kW, stride=1, dilation=1, pads=None, mult=1,
+                        layout=NHWC, nthreads=1):
+    """dW of fwd_general: (mult*C, kH, kW).  Returns (dW, S)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    N, H, W, C = _nhwc_dims(x.shape, layout)
+    if pads is None:
+        pads = same_pads(H, W, kH, kW, stride, dilation)
+    Ho, Wo = out_extents_padded(H, W, kH, kW, stride, dilation, pads)
+    assert _nhwc_dims(dy.shape, layout) == (N, Ho, Wo, mult * C)
+    dw = np.empty((mult * C, kH, kW), np.float64)
+    S = np.empty_like(dw)
+    lib.dwo_weight_grad_general(x, dy, dw, _ptr(S), N, H, W, C, mult, kH, kW,
+                                stride, dilation, pads[0], pads[2], Ho, Wo, layout, nthreads)
+    return dw, S

@@ -326,5 +326,151 @@ int dwo_bias_grad(const float *dy, double *db, double *S,
     return 0;
 }
 
+/* ================================================================== */
+/* General form: explicit per-side padding and a channel multiplier.    */
+/*                                                                      */
+/* [Lean] stride-2 XLA-SAME: the stride-1 SAME result kept at the ODD   */
+/* positions, with a backward that zero-upsamples the cotangent onto    */
+/* those same odd positions.  Keeping phase-1 positions equals reading  */
+/* input row ho*s + kh*d - pt with a top pad pt one smaller than the    */
+/* symmetric p, so both SAME variants are instances of one forward with */
+/* explicit pads (pt, pb, pl, pr); the output extents are the number of */
+/* window positions that fit: Ho = (H + pt + pb - d*(kH-1) - 1)/s + 1.  */
+/* [Reactant issue 331] grouped conv with groups = C_in and             */
+/* C_out = m*C_in (the "4 => 8, groups = 4" layer): output channel o    */
+/* reads input channel o/m only, with its own filter W[o] and bias b[o].*/
+/* m = 1 is the plain depthwise operator.                               */
+/* Here H, W, C are the INPUT extents and channels; y / dy have         */
+/* (N, m*C, Ho, Wo); W is [m*C][kH][kW]; b is [m*C] or NULL.            */
+/* ================================================================== */
+
+/* Forward.  [Lean] forward equation, with stride s, dilation d, top and */
+/* left pads pt, pl, and input channel o/m for output channel o:        */
+/*   y[n,o,ho,wo] = b[o] + sum_{kh,kw} x[n, o/m, ho*s+kh*d-pt,          */
+/*                                       wo*s+kw*d-pl] * W[o,kh,kw]     */
+/* over in-range input positions.                                        */
+int dwo_fwd_general(const float *x, const void *w, int wtype, const float *b,
+                    double *y, double *S,
+                    int N, int H, int W, int C, int m, int kH, int kW,
+                    int s, int d, int pt, int pl, int Ho, int Wo,
+                    int layout, int nthreads)
+{
+    const int Co = m * C;
+    long no;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+    for (no = 0; no < (long)N * Co; ++no) {
+        const int n = (int)(no / Co), o = (int)(no % Co), c = o / m;
+        for (int ho = 0; ho < Ho; ++ho)
+            for (int wo = 0; wo < Wo; ++wo) {
+                double acc = b ? (double)b[o] : 0.0, sabs = 0.0;
+                for (int kh = 0; kh < kH; ++kh) {
+                    const int hi = ho * s + kh * d - pt;
+                    if (hi < 0 || hi >= H)
+                        continue;
+                    for (int kw = 0; kw < kW; ++kw) {
+                        const int wi = wo * s + kw * d - pl;
+                        if (wi < 0 || wi >= W)
+                            continue;
+                        const double t = (double)x[at(layout, C, H, W, n, c, hi, wi)] *
+                                         wtap(w, wtype, kH, kW, o, kh, kw);
+                        acc += t;
+                        sabs += fabs(t);
+                    }
+                }
+                const size_t q = at(layout, Co, Ho, Wo, n, o, ho, wo);
+                y[q] = acc;
+                if (S)
+                    S[q] = sabs;
+            }
+    }
+    return 0;
+}
+
+/* Input gradient: the transpose of dwo_fwd_general.  [Lean] closed-form */
+/* input gradient, reconstructed-offset form: input position (h, w)     */
+/* receives dy[ho,wo]*W[kh,kw] exactly when ho*s + kh*d - pt = h and    */
+/* wo*s + kw*d - pl = w.  Enumerated by tap: ho = (h + pt - kh*d)/s     */
+/* must be a whole number in [0, Ho) (otherwise the upsampled cotangent */
+/* holds an inserted zero or padding there), likewise wo.  Input        */
+/* channel c collects the m output channels c*m .. c*m+m-1 that read it.*/
+int dwo_input_grad_general(const float *dy, const void *w, int wtype,
+                           double *dx, double *S,
+                           int N, int H, int W, int C, int m, int kH, int kW,
+                           int s, int d, int pt, int pl, int Ho, int Wo,
+                           int layout, int nthreads)
+{
+    const int Co = m * C;
+    long nc;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+    for (nc = 0; nc < (long)N * C; ++nc) {
+        const int n = (int)(nc / C), c = (int)(nc % C);
+        for (int h = 0; h < H; ++h)
+            for (int x_w = 0; x_w < W; ++x_w) {
+                double acc = 0.0, sabs = 0.0;
+                for (int j = 0; j < m; ++j) {
+                    const int o = c * m + j;
+                    for (int kh = 0; kh < kH; ++kh) {
+                        const int eh = h + pt - kh * d;          /* = ho * s */
+                        if (eh < 0 || eh % s != 0 || eh / s >= Ho)
+                            continue;
+                        for (int kw = 0; kw < kW; ++kw) {
+                            const int ew = x_w + pl - kw * d;
+                            if (ew < 0 || ew % s != 0 || ew / s >= Wo)
+                                continue;
+                            const double t = wtap(w, wtype, kH, kW, o, kh, kw) *
+                                (double)dy[at(layout, Co, Ho, Wo, n, o, eh / s, ew / s)];
+                            acc += t;
+                            sabs += fabs(t);
+                        }
+                    }
+                }
+                const size_t q = at(layout, C, H, W, n, c, h, x_w);
+                dx[q] = acc;
+                if (S)
+                    S[q] = sabs;
+            }
+    }
+    return 0;
+}
+
+/* Weight gradient of dwo_fwd_general.  [Lean] depthwise weight-VJP,    */
+/* with the general index map:                                           */
+/*   dW[o,kh,kw] = sum_{n,ho,wo} x[n, o/m, ho*s+kh*d-pt, wo*s+kw*d-pl] * */
+/*                 dy[n,o,ho,wo]   over in-range input positions.        */
+/* The bias gradient is dwo_bias_grad on dy (m*C channels).              */
+int dwo_weight_grad_general(const float *x, const float *dy, double *dw, double *S,
+                            int N, int H, int W, int C, int m, int kH, int kW,
+                            int s, int d, int pt, int pl, int Ho, int Wo,
+                            int layout, int nthreads)
+{
+    const int Co = m * C;
+    long t;
+#pragma omp parallel for schedule(dynamic) num_threads(nthreads > 0 ? nthreads : 1)
+    for (t = 0; t < (long)Co * kH * kW; ++t) {
+        const int o = (int)(t / ((long)kH * kW)), c = o / m;
+        const int kh = (int)((t / kW) % kH), kw = (int)(t % kW);
+        double acc = 0.0, sabs = 0.0;
+        for (int n = 0; n < N; ++n)
+            for (int ho = 0; ho < Ho; ++ho) {
+                const int hi = ho * s + kh * d - pt;
+                if (hi < 0 || hi >= H)
+                    continue;
+                for (int wo = 0; wo < Wo; ++wo) {
+                    const int wi = wo * s + kw * d - pl;
+                    if (wi < 0 || wi >= W)
+                        continue;
+                    const double p = (double)x[at(layout, C, H, W, n, c, hi, wi)] *
+                                     (double)dy[at(layout, Co, Ho, Wo, n, o, ho, wo)];
+                    acc += p;
+                    sabs += fabs(p);
+                }
+            }
+        dw[t] = acc;
+        if (S)
+            S[t] = sabs;
+    }
+    return 0;
+}
+
 /* Version tag so a stale build is detectable. */
-int dwo_version(void) { return 1; }
+int dwo_version(void) { return 2; }

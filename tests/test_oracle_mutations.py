@@ -49,6 +49,23 @@ MUTANTS = [
      "v = ldexp((double)(1024 + f), e - 24);", 0),
     ("half_read_as_raw_bits", "return dwo_half_to_double(((const uint16_t *)w)[i]);",
      "return (double)((const uint16_t *)w)[i];", 0),
+    ("general_fwd_reads_channel_o_mod_C",
+     "const int n = (int)(no / Co), o = (int)(no % Co), c = o / m;",
+     "const int n = (int)(no / Co), o = (int)(no % Co), c = o % C;", 0),
+    ("general_fwd_top_pad_sign", "const int hi = ho * s + kh * d - pt;",
+     "const int hi = ho * s + kh * d + pt;", 0),
+    ("general_fwd_left_pad_for_rows", "const int hi = ho * s + kh * d - pt;",
+     "const int hi = ho * s + kh * d - pl;", 0),
+    ("general_ig_odd_phase", "if (eh < 0 || eh % s != 0 || eh / s >= Ho)",
+     "if (eh < 0 || eh % s != s - 1 || eh / s >= Ho)", 0),
+    ("general_ig_one_replica_only", "for (int j = 0; j < m; ++j) {",
+     "for (int j = 0; j < 1; ++j) {", 0),
+    ("general_ig_row_bound_uses_H", "if (eh < 0 || eh % s != 0 || eh / s >= Ho)",
+     "if (eh < 0 || eh % s != 0 || eh >= H)", 0),
+    ("general_wgrad_reads_channel_o", "const int o = (int)(t / ((long)kH * kW)), c = o / m;",
+     "const int o = (int)(t / ((long)kH * kW)), c = o % C;", 0),
+    ("general_wgrad_left_pad_sign", "const int wi = wo * s + kw * d - pl;",
+     "const int wi = wo * s + kw * d + pl;", 1),
     ("weight_grad_swaps_dy_index", "(double)dy[at(layout, C, Ho, Wo, n, c, ho, wo)];\n                    acc += p;",
      "(double)dy[at(layout, C, Ho, Wo, n, c, wo % Ho, ho % Wo)];\n                    acc += p;", 0),
 ]
@@ -93,6 +110,24 @@ def _all_pins_pass(om):
         import torch  # noqa: F401
         for case in pins.SMALL_CASES[:5]:
             checks.append(lambda c=case: pins.test_matches_torch_cpu(om, c))
+    except ImportError:
+        pass
+    from tests import test_oracle_general_pins as gp
+    checks.append(lambda: gp.test_xla_same_pads_values(om))
+    checks.append(lambda: gp.test_symmetric_backward_is_wrong_for_xla_forward(om))
+    checks.append(lambda: gp.test_reactant_grouped_layer_shapes(om))
+    for layout in pins.LAYOUTS:
+        checks.append(lambda l=layout: gp.test_xla_same_stride2_is_odd_decimation(
+            om, (8, 6), (3, 3), 1, l))
+        checks.append(lambda l=layout: gp.test_multiplier_is_replicated_depthwise(om, 2, l))
+        for case in gp.GENERAL_CASES:
+            checks.append(lambda c=case, l=layout: gp.test_general_adjoint_identities(om, c, l))
+    checks.append(lambda: gp.test_symmetric_pads_reduce_to_same(om, (1, 7, 6, 2, 3, 3, 2, 1),
+                                                              pins.NHWC))
+    try:
+        import torch  # noqa: F401
+        for case in gp.GENERAL_CASES:
+            checks.append(lambda c=case: gp.test_general_matches_torch_cpu(om, c))
     except ImportError:
         pass
     for chk in checks:
