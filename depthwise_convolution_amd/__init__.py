@@ -8,11 +8,16 @@ not been built, every call raises ``RuntimeError``: there is no fallback.
 Names mirror the C ABI: ``dwconv2d_fwd``, ``dwconv2d_input_grad``,
 ``dwconv2d_launch``, ``dwconv2d_describe``, ``dwconv2d_weight_grad``,
 ``dwconv2d_weight_grad_workspace_size``, ``dwconv2d_strerror``,
-``dwconv2d_version``; ``fwd``, ``input_grad`` and ``weight_grad`` are the
-same calls with the outputs (and the workspace) allocated here.
+``dwconv2d_version``, and the general forms with explicit padding and a
+channel multiplier: ``dwconv2d_same_pads``, ``dwconv2d_out_extents``,
+``dwconv2d_launch_ex``, ``dwconv2d_describe_ex``, ``dwconv2d_weight_grad_ex``,
+``dwconv2d_weight_grad_workspace_size_ex``.  ``fwd``, ``input_grad`` and
+``weight_grad`` are the same calls with the outputs (and the workspace)
+allocated here; given ``pads`` or ``mult`` they use the general forms.
 
 Tensor shapes: NHWC tensors are ``(N, H, W, C)``, NCHW tensors
-``(N, C, H, W)``; weights ``(C, kH, kW)`` float32 or float16; bias ``(C,)``.
+``(N, C, H, W)``; weights ``(mult*C, kH, kW)`` float32 or float16; bias
+``(mult*C,)``; ``pads`` is ``(top, bottom, left, right)``.
 """
 import ctypes
 import os
@@ -24,14 +29,18 @@ NHWC, NCHW = 0, 1
 W_F32, W_F16 = 0, 1
 OP_FWD, OP_INPUT_GRAD, OP_WEIGHT_GRAD = 0, 1, 2
 STRATEGY_AUTO, STRATEGY_DIRECT, STRATEGY_TILED = 0, 1, 2
+PAD_SAME, PAD_XLA_SAME = 0, 1
 STATUS = {
     0: "OK", -1: "NULL_PTR", -2: "BAD_DIM", -3: "BAD_STRIDE", -4: "BAD_DILATION",
     -5: "EVEN_KERNEL", -6: "BAD_LAYOUT", -7: "BAD_WTYPE", -8: "ALIAS", -9: "MISALIGNED",
-    -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY", -13: "WORKSPACE",
+    -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY", -13: "WORKSPACE", -14: "BAD_PAD",
 }
 EXPORTS = ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
            "dwconv2d_weight_grad", "dwconv2d_weight_grad_workspace_size",
-           "dwconv2d_strerror", "dwconv2d_version")
+           "dwconv2d_strerror", "dwconv2d_version",
+           "dwconv2d_same_pads", "dwconv2d_out_extents", "dwconv2d_launch_ex",
+           "dwconv2d_describe_ex", "dwconv2d_weight_grad_workspace_size_ex",
+           "dwconv2d_weight_grad_ex")
 
 _lib = None
 
@@ -60,11 +69,19 @@ def lib():
                                                ctypes.POINTER(i)]
     L.dwconv2d_weight_grad_workspace_size.argtypes = [i] * 10 + [ctypes.POINTER(ll)]
     L.dwconv2d_weight_grad.argtypes = [vp, vp, vp, vp, vp, ll] + [i] * 10 + [vp]
+    ip = ctypes.POINTER(i)
+    L.dwconv2d_same_pads.argtypes = [i] * 7 + [ip]
+    L.dwconv2d_out_extents.argtypes = [i] * 6 + [ip, ip, ip]
+    L.dwconv2d_launch_ex.argtypes = [i, vp, vp, i, vp, vp] + [i] * 9 + [ip, i, i, vp]
+    L.dwconv2d_describe_ex.argtypes = [i] * 12 + [ip, i, i, ctypes.c_char_p, i,
+                                                  ctypes.POINTER(ll), ip]
+    L.dwconv2d_weight_grad_workspace_size_ex.argtypes = [i] * 9 + [ip, i, i, ctypes.POINTER(ll)]
+    L.dwconv2d_weight_grad_ex.argtypes = [vp, vp, vp, vp, vp, ll] + [i] * 9 + [ip, i, i, vp]
     L.dwconv2d_strerror.argtypes = [i]
     L.dwconv2d_strerror.restype = ctypes.c_char_p
-    for f in ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
-              "dwconv2d_weight_grad", "dwconv2d_weight_grad_workspace_size", "dwconv2d_version"):
-        getattr(L, f).restype = i
+    for f in EXPORTS:
+        if f != "dwconv2d_strerror":
+            getattr(L, f).restype = i
     _lib = L
     return L
 
@@ -212,25 +229,40 @@ def dwconv2d_describe(op, N, H, W, C, kH, kW, stride=1, dilation=1, layout=NHWC,
 
 
 # ------------------------------------------------------------- conveniences
-def fwd(x, w, b=None, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY_AUTO, stream=None):
-    """Allocate y and run the forward pass."""
+def fwd(x, w, b=None, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY_AUTO, stream=None,
+        pads=None, mult=1):
+    """Allocate y and run the forward pass (general form when pads or mult given)."""
     import torch
     lay = _layout_code(layout)
     N, H, W, C = _dims(x, lay)
-    y = torch.empty(_shape(lay, N, -(-H // stride), -(-W // stride), C), dtype=torch.float32,
-                    device=x.device)
-    return dwconv2d_launch(OP_FWD, x, w, b, y, H, W, stride, dilation, lay, strategy, stream)
+    if pads is None and mult == 1:
+        y = torch.empty(_shape(lay, N, -(-H // stride), -(-W // stride), C),
+                        dtype=torch.float32, device=x.device)
+        return dwconv2d_launch(OP_FWD, x, w, b, y, H, W, stride, dilation, lay, strategy,
+                               stream)
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    Ho, Wo = dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads)
+    y = torch.empty(_shape(lay, N, Ho, Wo, mult * C), dtype=torch.float32, device=x.device)
+    return dwconv2d_launch_ex(OP_FWD, x, w, b, y, H, W, stride, dilation, pads, mult, lay,
+                              strategy, stream)
 
 
 def input_grad(dy, w, H, W, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY_AUTO,
-               stream=None):
+               stream=None, pads=None, mult=1):
     """Allocate dx of forward-input extents (H, W) and run the input gradient."""
     import torch
     lay = _layout_code(layout)
-    N, _, _, C = _dims(dy, lay)
-    dx = torch.empty(_shape(lay, N, H, W, C), dtype=torch.float32, device=dy.device)
-    return dwconv2d_launch(OP_INPUT_GRAD, dy, w, None, dx, H, W, stride, dilation, lay,
-                           strategy, stream)
+    N, _, _, Cy = _dims(dy, lay)
+    if pads is None and mult == 1:
+        dx = torch.empty(_shape(lay, N, H, W, Cy), dtype=torch.float32, device=dy.device)
+        return dwconv2d_launch(OP_INPUT_GRAD, dy, w, None, dx, H, W, stride, dilation, lay,
+                               strategy, stream)
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    dx = torch.empty(_shape(lay, N, H, W, Cy // mult), dtype=torch.float32, device=dy.device)
+    return dwconv2d_launch_ex(OP_INPUT_GRAD, dy, w, None, dx, H, W, stride, dilation, pads,
+                              mult, lay, strategy, stream)
 
 
 def dwconv2d_weight_grad_workspace_size(N, H, W, C, kH, kW, stride=1, dilation=1, layout=NHWC,
@@ -274,14 +306,150 @@ def dwconv2d_weight_grad(x, dy, dw, db, workspace, stride=1, dilation=1, layout=
 
 
 def weight_grad(x, dy, kH, kW, stride=1, dilation=1, layout=NHWC, with_bias=True,
-                strategy=STRATEGY_AUTO, stream=None):
-    """Allocate dW (C, kH, kW), db (C,) and the workspace; run the weight gradient."""
+                strategy=STRATEGY_AUTO, stream=None, pads=None, mult=1):
+    """Allocate dW (mult*C, kH, kW), db (mult*C,) and the workspace; run the
+    weight gradient (general form when pads or mult given)."""
     import torch
     lay = _layout_code(layout)
     N, H, W, C = _dims(x, lay)
-    nbytes = dwconv2d_weight_grad_workspace_size(N, H, W, C, kH, kW, stride, dilation, lay,
-                                                 strategy)
+    general = pads is not None or mult != 1
+    if general:
+        pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+        nbytes = dwconv2d_weight_grad_workspace_size_ex(N, H, W, C, kH, kW, stride, dilation,
+                                                        pads, mult, lay, strategy)
+    else:
+        nbytes = dwconv2d_weight_grad_workspace_size(N, H, W, C, kH, kW, stride, dilation, lay,
+                                                     strategy)
     ws = torch.empty(max(1, (nbytes + 15) // 16) * 4, dtype=torch.float32, device=x.device)
-    dw = torch.empty((C, kH, kW), dtype=torch.float32, device=x.device)
-    db = torch.empty((C,), dtype=torch.float32, device=x.device) if with_bias else None
+    dw = torch.empty((mult * C, kH, kW), dtype=torch.float32, device=x.device)
+    db = torch.empty((mult * C,), dtype=torch.float32, device=x.device) if with_bias else None
+    if general:
+        return dwconv2d_weight_grad_ex(x, dy, dw, db, ws, stride, dilation, pads, mult, lay,
+                                       strategy, stream)
     return dwconv2d_weight_grad(x, dy, dw, db, ws, stride, dilation, lay, strategy, stream)
+
+
+# ------------------------------------------- explicit padding, channel multiplier
+def _pads_arg(pads):
+    if pads is None or len(pads) != 4:
+        raise ValueError("pads must be (top, bottom, left, right)")
+    return (ctypes.c_int * 4)(*(int(v) for v in pads))
+
+
+def _pads_or_same(pads, H, W, kH, kW, stride, dilation):
+    if pads is None:
+        return dwconv2d_same_pads(PAD_SAME, H, W, kH, kW, stride, dilation)
+    return tuple(int(v) for v in pads)
+
+
+def dwconv2d_same_pads(mode, H, W, kH, kW, stride=1, dilation=1):
+    """(top, bottom, left, right) of PAD_SAME or PAD_XLA_SAME."""
+    out = (ctypes.c_int * 4)()
+    st = lib().dwconv2d_same_pads(mode, H, W, kH, kW, stride, dilation, out)
+    _check_status(st, "dwconv2d_same_pads")
+    return tuple(out)
+
+
+def dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads):
+    """(Ho, Wo) of a padded problem."""
+    ho, wo = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().dwconv2d_out_extents(H, W, kH, kW, stride, dilation, _pads_arg(pads),
+                                    ctypes.byref(ho), ctypes.byref(wo))
+    _check_status(st, "dwconv2d_out_extents")
+    return ho.value, wo.value
+
+
+def _prepare_ex(op, inp, w, b, out, H, W, stride, dilation, pads, mult, layout):
+    import torch
+    lay = _layout_code(layout)
+    _check_dev(inp, "input", (torch.float32,))
+    _check_dev(out, "output", (torch.float32,))
+    wt = _wtype(w)
+    Co, kH, kW = (int(v) for v in w.shape)
+    if mult < 1 or Co % mult != 0:
+        raise ValueError("w must be (mult*C, kH, kW)")
+    C = Co // mult
+    if b is not None:
+        _check_dev(b, "b", (torch.float32,))
+        if tuple(b.shape) != (Co,):
+            raise ValueError("b must be (mult*C,)")
+    Ho, Wo = dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads)
+    N = int(inp.shape[0])
+    big, small = _shape(lay, N, H, W, C), _shape(lay, N, Ho, Wo, Co)
+    want_in, want_out = (big, small) if op == OP_FWD else (small, big)
+    if tuple(inp.shape) != want_in or tuple(out.shape) != want_out:
+        raise ValueError(f"shape mismatch: input {tuple(inp.shape)} (want {want_in}), "
+                         f"output {tuple(out.shape)} (want {want_out})")
+    if not (inp.device == out.device == w.device) or (b is not None and b.device != out.device):
+        raise ValueError("all tensors must be on the same device")
+    return lay, wt, N, C, kH, kW
+
+
+def dwconv2d_launch_ex(op, inp, w, b, out, H, W, stride=1, dilation=1, pads=None, mult=1,
+                       layout=NHWC, strategy=STRATEGY_AUTO, stream=None):
+    """Enqueue op (OP_FWD / OP_INPUT_GRAD) with explicit pads and channel multiplier."""
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    lay, wt, N, C, kH, kW = _prepare_ex(op, inp, w, b, out, H, W, stride, dilation, pads, mult,
+                                        layout)
+    st = lib().dwconv2d_launch_ex(op, _ptr(inp), _ptr(w), wt, _ptr(b), _ptr(out), N, H, W, C,
+                                  mult, kH, kW, stride, dilation, _pads_arg(pads), lay, strategy,
+                                  _stream(out, stream))
+    _check_status(st, "dwconv2d_launch_ex")
+    return out
+
+
+def dwconv2d_describe_ex(op, N, H, W, C, kH, kW, stride=1, dilation=1, pads=None, mult=1,
+                         layout=NHWC, wtype=W_F32, has_bias=False, strategy=STRATEGY_AUTO):
+    """(kernel name, grid, block) of a general-form launch."""
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    name = ctypes.create_string_buffer(128)
+    grid, block = ctypes.c_longlong(0), ctypes.c_int(0)
+    st = lib().dwconv2d_describe_ex(op, wtype, int(bool(has_bias)), N, H, W, C, mult, kH, kW,
+                                    stride, dilation, _pads_arg(pads), _layout_code(layout),
+                                    strategy, name, 128, ctypes.byref(grid), ctypes.byref(block))
+    _check_status(st, "dwconv2d_describe_ex")
+    return name.value.decode(), grid.value, block.value
+
+
+def dwconv2d_weight_grad_workspace_size_ex(N, H, W, C, kH, kW, stride=1, dilation=1, pads=None,
+                                           mult=1, layout=NHWC, strategy=STRATEGY_AUTO):
+    """Workspace bytes of dwconv2d_weight_grad_ex."""
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    out = ctypes.c_longlong(0)
+    st = lib().dwconv2d_weight_grad_workspace_size_ex(N, H, W, C, mult, kH, kW, stride,
+                                                      dilation, _pads_arg(pads),
+                                                      _layout_code(layout), strategy,
+                                                      ctypes.byref(out))
+    _check_status(st, "dwconv2d_weight_grad_workspace_size_ex")
+    return out.value
+
+
+def dwconv2d_weight_grad_ex(x, dy, dw, db, workspace, stride=1, dilation=1, pads=None, mult=1,
+                            layout=NHWC, strategy=STRATEGY_AUTO, stream=None):
+    """dw (mult*C, kH, kW) and db (mult*C,) unless None, general form."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    _check_dev(x, "x", (torch.float32,))
+    _check_dev(dy, "dy", (torch.float32,))
+    _check_dev(dw, "dw", (torch.float32,))
+    if dw.dim() != 3 or int(dw.shape[0]) != mult * C:
+        raise ValueError("dw must be (mult*C, kH, kW)")
+    kH, kW = int(dw.shape[1]), int(dw.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    if db is not None:
+        _check_dev(db, "db", (torch.float32,))
+        if tuple(db.shape) != (mult * C,):
+            raise ValueError("db must be (mult*C,)")
+    Ho, Wo = dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads)
+    if tuple(dy.shape) != _shape(lay, N, Ho, Wo, mult * C):
+        raise ValueError(f"dy shape {tuple(dy.shape)} != {_shape(lay, N, Ho, Wo, mult * C)}")
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().dwconv2d_weight_grad_ex(_ptr(x), _ptr(dy), _ptr(dw), _ptr(db), _ptr(workspace),
+                                       nbytes, N, H, W, C, mult, kH, kW, stride, dilation,
+                                       _pads_arg(pads), lay, strategy, _stream(dw, stream))
+    _check_status(st, "dwconv2d_weight_grad_ex")
+    return dw, db

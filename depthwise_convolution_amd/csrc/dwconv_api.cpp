@@ -42,21 +42,21 @@ int check_pointers(const Problem &p, const float *in, const void *w, const float
     const std::uintptr_t wbits = reinterpret_cast<std::uintptr_t>(w);
     if ((p.wtype == DWCONV_W_F32 && (wbits & 3u)) || (wbits & 1u))
         return DWCONV_ERR_MISALIGNED;
-    const long long Ho = (p.H + p.stride - 1) / p.stride, Wo = (p.W + p.stride - 1) / p.stride;
-    const long long big = 4LL * p.N * p.H * p.W * p.C, small = 4LL * p.N * Ho * Wo * p.C;
+    const long long co = (long long)p.mult * p.C;
+    const long long big = 4LL * p.N * p.H * p.W * p.C, small = 4LL * p.N * p.Ho * p.Wo * co;
     const long long in_bytes = p.op == DWCONV_OP_FWD ? big : small;
     const long long out_bytes = p.op == DWCONV_OP_FWD ? small : big;
-    const long long w_bytes = (long long)p.C * p.kH * p.kW * (p.wtype == DWCONV_W_F16 ? 2 : 4);
+    const long long w_bytes = co * p.kH * p.kW * (p.wtype == DWCONV_W_F16 ? 2 : 4);
     const Range o = range_of(out, out_bytes);
     if (overlap(o, range_of(in, in_bytes)) || overlap(o, range_of(w, w_bytes)))
         return DWCONV_ERR_ALIAS;
-    if (b && overlap(o, range_of(b, 4LL * p.C)))
+    if (b && overlap(o, range_of(b, 4LL * co)))
         return DWCONV_ERR_ALIAS;
     return DWCONV_OK;
 }
 
-int run(const Problem &p, const float *in, const void *w, const float *b, float *out,
-        int strategy, void *stream)
+int run(Problem p, const float *in, const void *w, const float *b, float *out, int strategy,
+        void *stream)
 {
     if (p.op != DWCONV_OP_FWD && p.op != DWCONV_OP_INPUT_GRAD)
         return DWCONV_ERR_BAD_OP;
@@ -77,54 +77,25 @@ int run(const Problem &p, const float *in, const void *w, const float *b, float 
     return dwconv::launch_plan(p, pl, in, w, b, out, stream);
 }
 
-Problem problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int kH, int kW,
-                int stride, int dilation, int layout)
+// Problem with explicit pads (host array top, bottom, left, right) and a
+// channel multiplier.  Returns DWCONV_ERR_NULL_PTR for a NULL pads array.
+int general_problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int mult,
+                    int kH, int kW, int stride, int dilation, const int *pads, int layout,
+                    Problem *p)
 {
-    Problem p;
-    p.op = op; p.wtype = wtype; p.layout = layout; p.has_bias = has_bias;
-    p.N = N; p.H = H; p.W = W; p.C = C; p.kH = kH; p.kW = kW;
-    p.stride = stride; p.dilation = dilation;
-    return p;
-}
-
-}  // namespace
-
-extern "C" {
-
-int dwconv2d_fwd(const float *x, const void *w, int wtype, const float *b, float *y,
-                 int N, int H, int W, int C, int kH, int kW,
-                 int stride, int dilation, int layout, void *stream)
-{
-    const Problem p = problem(DWCONV_OP_FWD, wtype, b != nullptr, N, H, W, C, kH, kW,
-                              stride, dilation, layout);
-    return run(p, x, w, b, y, DWCONV_STRATEGY_AUTO, stream);
-}
-
-int dwconv2d_input_grad(const float *dy, const void *w, int wtype, float *dx,
-                        int N, int H, int W, int C, int kH, int kW,
-                        int stride, int dilation, int layout, void *stream)
-{
-    const Problem p = problem(DWCONV_OP_INPUT_GRAD, wtype, 0, N, H, W, C, kH, kW,
-                              stride, dilation, layout);
-    return run(p, dy, w, nullptr, dx, DWCONV_STRATEGY_AUTO, stream);
-}
-
-int dwconv2d_launch(int op, const float *in, const void *w, int wtype, const float *b,
-                    float *out, int N, int H, int W, int C, int kH, int kW,
-                    int stride, int dilation, int layout, int strategy, void *stream)
-{
-    const Problem p = problem(op, wtype, b != nullptr, N, H, W, C, kH, kW, stride, dilation,
+    if (!pads)
+        return DWCONV_ERR_NULL_PTR;
+    *p = dwconv::same_problem(op, wtype, has_bias, N, H, W, C, kH, kW, stride, dilation,
                               layout);
-    return run(p, in, w, b, out, strategy, stream);
+    p->same = 0;
+    p->mult = mult;
+    p->pt = pads[0]; p->pb = pads[1]; p->pl = pads[2]; p->pr = pads[3];
+    return DWCONV_OK;
 }
 
-int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int C,
-                      int kH, int kW, int stride, int dilation, int layout, int strategy,
-                      char *name, int name_len, long long *grid, int *block)
+int describe(Problem p, int strategy, char *name, int name_len, long long *grid, int *block)
 {
-    const Problem p = problem(op, wtype, has_bias, N, H, W, C, kH, kW, stride, dilation,
-                              layout);
-    if ((op == DWCONV_OP_INPUT_GRAD || op == DWCONV_OP_WEIGHT_GRAD) && has_bias)
+    if ((p.op == DWCONV_OP_INPUT_GRAD || p.op == DWCONV_OP_WEIGHT_GRAD) && p.has_bias)
         return DWCONV_ERR_BAD_OP;
     Plan pl;
     const int st = dwconv::make_plan(p, strategy, 0, &pl);
@@ -141,14 +112,10 @@ int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int 
     return DWCONV_OK;
 }
 
-int dwconv2d_weight_grad_workspace_size(int N, int H, int W, int C, int kH, int kW,
-                                        int stride, int dilation, int layout, int strategy,
-                                        long long *bytes)
+int wgrad_workspace(Problem p, int strategy, long long *bytes)
 {
     if (!bytes)
         return DWCONV_ERR_NULL_PTR;
-    const Problem p = problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, kH, kW,
-                              stride, dilation, layout);
     // The plan depends on pointer alignment, which is not known here: report
     // the larger of the aligned plan and the fallback plan.
     Plan a, u;
@@ -163,13 +130,9 @@ int dwconv2d_weight_grad_workspace_size(int N, int H, int W, int C, int kH, int 
     return DWCONV_OK;
 }
 
-int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
-                         void *workspace, long long workspace_bytes,
-                         int N, int H, int W, int C, int kH, int kW,
-                         int stride, int dilation, int layout, int strategy, void *stream)
+int wgrad(Problem p, const float *x, const float *dy, float *dw, float *db, void *workspace,
+          long long workspace_bytes, int strategy, void *stream)
 {
-    const Problem p = problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, kH, kW,
-                              stride, dilation, layout);
     int st = dwconv::validate_problem(p);
     if (st != DWCONV_OK)
         return st;
@@ -190,10 +153,11 @@ int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
     if (!workspace || (reinterpret_cast<std::uintptr_t>(workspace) & 15u) != 0 ||
         workspace_bytes < pl.workspace)
         return DWCONV_ERR_WORKSPACE;
-    const long long Ho = (H + stride - 1) / stride, Wo = (W + stride - 1) / stride;
-    const Range rx = range_of(x, 4LL * N * H * W * C), rg = range_of(dy, 4LL * N * Ho * Wo * C);
-    const Range rw = range_of(dw, 4LL * C * kH * kW), rws = range_of(workspace, pl.workspace);
-    const Range outs[3] = {rw, rws, db ? range_of(db, 4LL * C) : Range{0, 0}};
+    const long long co = (long long)p.mult * p.C;
+    const Range rx = range_of(x, 4LL * p.N * p.H * p.W * p.C);
+    const Range rg = range_of(dy, 4LL * p.N * p.Ho * p.Wo * co);
+    const Range rw = range_of(dw, 4LL * co * p.kH * p.kW), rws = range_of(workspace, pl.workspace);
+    const Range outs[3] = {rw, rws, db ? range_of(db, 4LL * co) : Range{0, 0}};
     for (int i = 0; i < 3; ++i) {
         if (outs[i].hi == outs[i].lo)
             continue;
@@ -206,12 +170,164 @@ int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
     return dwconv::launch_wgrad(p, pl, x, dy, dw, db, workspace, stream);
 }
 
+}  // namespace
+
+extern "C" {
+
+int dwconv2d_fwd(const float *x, const void *w, int wtype, const float *b, float *y,
+                 int N, int H, int W, int C, int kH, int kW,
+                 int stride, int dilation, int layout, void *stream)
+{
+    const Problem p = dwconv::same_problem(DWCONV_OP_FWD, wtype, b != nullptr, N, H, W, C, kH,
+                                           kW, stride, dilation, layout);
+    return run(p, x, w, b, y, DWCONV_STRATEGY_AUTO, stream);
+}
+
+int dwconv2d_input_grad(const float *dy, const void *w, int wtype, float *dx,
+                        int N, int H, int W, int C, int kH, int kW,
+                        int stride, int dilation, int layout, void *stream)
+{
+    const Problem p = dwconv::same_problem(DWCONV_OP_INPUT_GRAD, wtype, 0, N, H, W, C, kH, kW,
+                                           stride, dilation, layout);
+    return run(p, dy, w, nullptr, dx, DWCONV_STRATEGY_AUTO, stream);
+}
+
+int dwconv2d_launch(int op, const float *in, const void *w, int wtype, const float *b,
+                    float *out, int N, int H, int W, int C, int kH, int kW,
+                    int stride, int dilation, int layout, int strategy, void *stream)
+{
+    const Problem p = dwconv::same_problem(op, wtype, b != nullptr, N, H, W, C, kH, kW, stride,
+                                           dilation, layout);
+    return run(p, in, w, b, out, strategy, stream);
+}
+
+int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int C,
+                      int kH, int kW, int stride, int dilation, int layout, int strategy,
+                      char *name, int name_len, long long *grid, int *block)
+{
+    const Problem p = dwconv::same_problem(op, wtype, has_bias, N, H, W, C, kH, kW, stride,
+                                           dilation, layout);
+    return describe(p, strategy, name, name_len, grid, block);
+}
+
+int dwconv2d_weight_grad_workspace_size(int N, int H, int W, int C, int kH, int kW,
+                                        int stride, int dilation, int layout, int strategy,
+                                        long long *bytes)
+{
+    const Problem p = dwconv::same_problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C,
+                                           kH, kW, stride, dilation, layout);
+    return wgrad_workspace(p, strategy, bytes);
+}
+
+int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
+                         void *workspace, long long workspace_bytes,
+                         int N, int H, int W, int C, int kH, int kW,
+                         int stride, int dilation, int layout, int strategy, void *stream)
+{
+    const Problem p = dwconv::same_problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C,
+                                           kH, kW, stride, dilation, layout);
+    return wgrad(p, x, dy, dw, db, workspace, workspace_bytes, strategy, stream);
+}
+
+int dwconv2d_same_pads(int mode, int H, int W, int kH, int kW, int stride, int dilation,
+                       int *pads)
+{
+    if (!pads)
+        return DWCONV_ERR_NULL_PTR;
+    if (H < 1 || W < 1 || kH < 1 || kW < 1)
+        return DWCONV_ERR_BAD_DIM;
+    if (stride != 1 && stride != 2)
+        return DWCONV_ERR_BAD_STRIDE;
+    if (dilation < 1 || (long long)dilation * ((kH > kW ? kH : kW) - 1) >= (1 << 16))
+        return DWCONV_ERR_BAD_DILATION;
+    if (kH % 2 == 0 || kW % 2 == 0)
+        return DWCONV_ERR_EVEN_KERNEL;
+    if (mode != DWCONV_PAD_SAME && mode != DWCONV_PAD_XLA_SAME)
+        return DWCONV_ERR_BAD_PAD;
+    const int ph = dilation * (kH - 1) / 2, pw = dilation * (kW - 1) / 2;
+    // XLA-SAME at stride 2 keeps the odd positions of the stride-1 result:
+    // one pad less before, and floor(n/2) outputs
+    const int shift = (mode == DWCONV_PAD_XLA_SAME && stride == 2) ? 1 : 0;
+    pads[0] = ph - shift; pads[1] = ph;
+    pads[2] = pw - shift; pads[3] = pw;
+    return DWCONV_OK;
+}
+
+int dwconv2d_out_extents(int H, int W, int kH, int kW, int stride, int dilation,
+                         const int *pads, int *Ho, int *Wo)
+{
+    Problem p;
+    int st = general_problem(DWCONV_OP_FWD, DWCONV_W_F32, 0, 1, H, W, 1, 1, kH, kW, stride,
+                             dilation, pads, DWCONV_LAYOUT_NHWC, &p);
+    if (st != DWCONV_OK)
+        return st;
+    st = dwconv::validate_problem(p);
+    if (st != DWCONV_OK)
+        return st;
+    if (Ho)
+        *Ho = p.Ho;
+    if (Wo)
+        *Wo = p.Wo;
+    return DWCONV_OK;
+}
+
+int dwconv2d_launch_ex(int op, const float *in, const void *w, int wtype, const float *b,
+                       float *out, int N, int H, int W, int C, int mult, int kH, int kW,
+                       int stride, int dilation, const int *pads, int layout, int strategy,
+                       void *stream)
+{
+    Problem p;
+    const int st = general_problem(op, wtype, b != nullptr, N, H, W, C, mult, kH, kW, stride,
+                                   dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    return run(p, in, w, b, out, strategy, stream);
+}
+
+int dwconv2d_describe_ex(int op, int wtype, int has_bias, int N, int H, int W, int C, int mult,
+                         int kH, int kW, int stride, int dilation, const int *pads, int layout,
+                         int strategy, char *name, int name_len, long long *grid, int *block)
+{
+    Problem p;
+    const int st = general_problem(op, wtype, has_bias, N, H, W, C, mult, kH, kW, stride,
+                                   dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    return describe(p, strategy, name, name_len, grid, block);
+}
+
+int dwconv2d_weight_grad_workspace_size_ex(int N, int H, int W, int C, int mult, int kH, int kW,
+                                           int stride, int dilation, const int *pads,
+                                           int layout, int strategy, long long *bytes)
+{
+    Problem p;
+    const int st = general_problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, mult, kH,
+                                   kW, stride, dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    return wgrad_workspace(p, strategy, bytes);
+}
+
+int dwconv2d_weight_grad_ex(const float *x, const float *dy, float *dw, float *db,
+                            void *workspace, long long workspace_bytes,
+                            int N, int H, int W, int C, int mult, int kH, int kW,
+                            int stride, int dilation, const int *pads, int layout, int strategy,
+                            void *stream)
+{
+    Problem p;
+    const int st = general_problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, mult, kH,
+                                   kW, stride, dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    return wgrad(p, x, dy, dw, db, workspace, workspace_bytes, strategy, stream);
+}
+
 const char *dwconv2d_strerror(int status)
 {
     switch (status) {
     case DWCONV_OK: return "ok";
     case DWCONV_ERR_NULL_PTR: return "null tensor pointer";
-    case DWCONV_ERR_BAD_DIM: return "bad dimension (< 1, or a tensor of 2^31 or more elements)";
+    case DWCONV_ERR_BAD_DIM: return "bad dimension (< 1, no output position, or a tensor of 2^31 or more elements)";
     case DWCONV_ERR_BAD_STRIDE: return "stride must be 1 or 2";
     case DWCONV_ERR_BAD_DILATION: return "dilation must be >= 1 and d*(k-1) < 65536";
     case DWCONV_ERR_EVEN_KERNEL: return "kernel extents must be odd (SAME padding)";
@@ -223,10 +339,11 @@ const char *dwconv2d_strerror(int status)
     case DWCONV_ERR_BAD_OP: return "unknown op, or a bias given to the input gradient";
     case DWCONV_ERR_BAD_STRATEGY: return "unknown strategy, or it does not apply to this problem";
     case DWCONV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DWCONV_ERR_BAD_PAD: return "pad out of range (|pad| >= 65536) or unknown padding mode";
     default: return "unknown status";
     }
 }
 
-int dwconv2d_version(void) { return 100; }
+int dwconv2d_version(void) { return 200; }
 
 }  // extern "C"

@@ -11,13 +11,25 @@
 namespace dwconv {
 
 // One depthwise problem, as the C ABI receives it (see include/dwconv.h).
+// C counts INPUT channels; the output has mult*C channels, output channel o
+// reading input channel o / mult (mult = 1: plain depthwise).  Zero padding
+// is explicit per side (pt, pb, pl, pr; negative values crop); the SAME entry
+// points fill in the symmetric pads d*(k-1)/2 and set `same`.
 struct Problem {
-    int op;        // DWCONV_OP_FWD or DWCONV_OP_INPUT_GRAD
+    int op;        // DWCONV_OP_FWD, DWCONV_OP_INPUT_GRAD or DWCONV_OP_WEIGHT_GRAD
     int wtype;     // DWCONV_W_F32 / DWCONV_W_F16
     int layout;    // DWCONV_LAYOUT_NHWC / DWCONV_LAYOUT_NCHW
     int has_bias;
     int N, H, W, C, kH, kW, stride, dilation;
+    int mult;             // channel multiplier (output channels per input channel)
+    int pt, pb, pl, pr;   // zero padding: top, bottom, left, right
+    int same;             // 1: symmetric SAME entry point (odd kernels required)
+    int Ho, Wo;           // output extents, set by validate_problem
 };
+
+// Problem with symmetric SAME padding and no channel multiplier.
+Problem same_problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int kH,
+                     int kW, int stride, int dilation, int layout);
 
 enum Kind {
     KIND_DIRECT_NHWC = 1,  // one thread per (n, row, col, channel vector); taps from global
@@ -94,6 +106,7 @@ struct Plan {
     int nct, nwt, nst;  // tiled: channel tiles (NHWC) or plane groups (NCHW), column tiles, row tiles
     int pb;             // tiled NCHW: planes per workgroup
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
+    int hl, twl;        // tiled NCHW: staged columns left of a tile, staged floats per row
     int strip;          // weight gradient, tiled: row tiles per workgroup
     long long chunks;   // weight gradient: partial sums per weight (rows of the workspace)
     long long workspace;// weight gradient: workspace bytes
@@ -106,16 +119,17 @@ struct Plan {
     char name[96];
 };
 
-// Validate dimensions and enums (not pointers).  Returns a DWCONV_ status.
-int validate_problem(const Problem &p);
+// Validate dimensions, pads and enums (not pointers) and set p.Ho, p.Wo.
+// Returns a DWCONV_ status.
+int validate_problem(Problem &p);
 
 // Choose the kernel and its launch geometry.  `ptr_bits` is the bitwise OR
 // of the tensor pointers' addresses (0 when unknown); vector widths are only
 // chosen when it shows 16-byte alignment.  Returns a DWCONV_ status.
-int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
+int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
 
 // Plan the weight gradient (op DWCONV_OP_WEIGHT_GRAD).  Returns a status.
-int make_wgrad_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
+int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
 
 // Enqueue the two kernels of a weight-gradient plan.
 int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *dy, float *dw,

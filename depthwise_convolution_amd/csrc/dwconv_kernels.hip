@@ -143,17 +143,22 @@ __device__ __forceinline__ float buf_w(__amdgpu_buffer_rsrc_t r, int idx, half_t
 }
 
 struct DirectArgs {
-    int N, C, kH, kW, d, pH, pW;
+    int N, CI, CO, mult;  // channels of the tensor read / written; channel multiplier
+    int kH, kW, d, pH, pW;
     int IH, IW, OH, OW;   // extents of the tensor read and the tensor written
     int total;            // threads that do work
 };
 
 // ---------------------------------------------------------------------------
-// Direct NHWC: thread = (n, oh, ow, V consecutive channels).
-// Forward:  out[oh,ow] = b + sum_taps in[oh*S + kh*d - pH, ow*S + kw*d - pW] * W[kh,kw]
-// Input grad: th = oh + kh*d - pH on the upsampled grid (extent OH); a tap
-//   contributes when th is inside and a multiple of S, reading in[th/S] with
-//   the reversed tap W[kH-1-kh, kW-1-kw].
+// Direct kernels.  A thread computes V consecutive channels r of one output
+// position of the tensor written.
+// Forward:  out[oh,ow,r] = b[r] + sum_taps in[oh*S + kh*d - pH, ow*S + kw*d - pW, r/mult]
+//                                           * W[r,kh,kw]
+// Input grad: th = oh + kh*d - pH on the zero-upsampled dy grid; a tap
+//   contributes when th >= 0 is a multiple of S and th/S is a row of dy,
+//   reading dy[th/S] with the reversed tap W[o, kH-1-kh, kW-1-kw], for each of
+//   the mult output channels o = r*mult + j that read input channel r.
+// V > 1 only with mult == 1 (consecutive channels of both tensors).
 // ---------------------------------------------------------------------------
 template <typename WT, int V, bool IG, int S>
 __global__ __launch_bounds__(256) void k_direct_nhwc(const float *__restrict__ in,
@@ -165,59 +170,66 @@ __global__ __launch_bounds__(256) void k_direct_nhwc(const float *__restrict__ i
     if (gt >= (unsigned)a.total)
         return;
     int t = (int)gt;
-    const int CV = a.C / V;
+    const int CV = a.CO / V;
     const int cv = t % CV;
     t /= CV;
     const int ow = t % a.OW;
     t /= a.OW;
     const int oh = t % a.OH;
     const int n = t / a.OH;
-    const int c0 = cv * V;
+    const int r0 = cv * V;
     const int kk = a.kH * a.kW;
+    const int nrep = IG ? a.mult : 1;
 
     float acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v)
-        acc[v] = (!IG && bias) ? bias[c0 + v] : 0.0f;
+        acc[v] = (!IG && bias) ? bias[r0 + v] : 0.0f;
 
-    for (int kh = 0; kh < a.kH; ++kh) {
-        int ih;
-        if (!IG) {
-            ih = oh * S + kh * a.d - a.pH;
-            if (ih < 0 || ih >= a.IH)
-                continue;
-        } else {
-            const int th = oh + kh * a.d - a.pH;
-            if (th < 0 || th >= a.OH || (S == 2 && (th & 1)))
-                continue;
-            ih = th / S;
-        }
-        for (int kw = 0; kw < a.kW; ++kw) {
-            int iw;
+    for (int j = 0; j < nrep; ++j) {
+        const int sc = IG ? r0 * a.mult + j : r0 / a.mult;   // channel of the tensor read
+        const int wc = IG ? sc : r0;                          // filter
+        for (int kh = 0; kh < a.kH; ++kh) {
+            int ih;
             if (!IG) {
-                iw = ow * S + kw * a.d - a.pW;
-                if (iw < 0 || iw >= a.IW)
+                ih = oh * S + kh * a.d - a.pH;
+                if (ih < 0 || ih >= a.IH)
                     continue;
             } else {
-                const int tw = ow + kw * a.d - a.pW;
-                if (tw < 0 || tw >= a.OW || (S == 2 && (tw & 1)))
+                const int th = oh + kh * a.d - a.pH;
+                if (th < 0 || (S == 2 && (th & 1)))
                     continue;
-                iw = tw / S;
+                ih = th / S;
+                if (ih >= a.IH)
+                    continue;
             }
-            float xv[V];
-            load_vec<V>(in + ((n * a.IH + ih) * a.IW + iw) * a.C + c0, xv);
-            const int tap = IG ? (a.kH - 1 - kh) * a.kW + (a.kW - 1 - kw) : kh * a.kW + kw;
+            for (int kw = 0; kw < a.kW; ++kw) {
+                int iw;
+                if (!IG) {
+                    iw = ow * S + kw * a.d - a.pW;
+                    if (iw < 0 || iw >= a.IW)
+                        continue;
+                } else {
+                    const int tw = ow + kw * a.d - a.pW;
+                    if (tw < 0 || (S == 2 && (tw & 1)))
+                        continue;
+                    iw = tw / S;
+                    if (iw >= a.IW)
+                        continue;
+                }
+                float xv[V];
+                load_vec<V>(in + ((n * a.IH + ih) * a.IW + iw) * a.CI + sc, xv);
+                const int tap = IG ? (a.kH - 1 - kh) * a.kW + (a.kW - 1 - kw) : kh * a.kW + kw;
 #pragma unroll
-            for (int v = 0; v < V; ++v)
-                acc[v] = fmaf(widen(w[(c0 + v) * kk + tap]), xv[v], acc[v]);
+                for (int v = 0; v < V; ++v)
+                    acc[v] = fmaf(widen(w[(wc + v) * kk + tap]), xv[v], acc[v]);
+            }
         }
     }
-    store_vec<V>(out + ((n * a.OH + oh) * a.OW + ow) * a.C + c0, acc);
+    store_vec<V>(out + ((n * a.OH + oh) * a.OW + ow) * a.CO + r0, acc);
 }
 
-// ---------------------------------------------------------------------------
-// Direct NCHW: thread = (n, c, oh, ow), consecutive threads along ow.
-// ---------------------------------------------------------------------------
+// Direct NCHW: thread = (n, r, oh, ow), consecutive threads along ow.
 template <typename WT, bool IG, int S>
 __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ in,
                                                      const WT *__restrict__ w,
@@ -232,41 +244,49 @@ __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ i
     t /= a.OW;
     const int oh = t % a.OH;
     t /= a.OH;
-    const int c = t % a.C;
-    const int n = t / a.C;
+    const int r = t % a.CO;
+    const int n = t / a.CO;
     const int kk = a.kH * a.kW;
-    const float *plane = in + (n * a.C + c) * (a.IH * a.IW);
-    const WT *wc = w + c * kk;
-    float acc = (!IG && bias) ? bias[c] : 0.0f;
-    for (int kh = 0; kh < a.kH; ++kh) {
-        int ih;
-        if (!IG) {
-            ih = oh * S + kh * a.d - a.pH;
-            if (ih < 0 || ih >= a.IH)
-                continue;
-        } else {
-            const int th = oh + kh * a.d - a.pH;
-            if (th < 0 || th >= a.OH || (S == 2 && (th & 1)))
-                continue;
-            ih = th / S;
-        }
-        for (int kw = 0; kw < a.kW; ++kw) {
-            int iw;
+    const int nrep = IG ? a.mult : 1;
+    float acc = (!IG && bias) ? bias[r] : 0.0f;
+    for (int j = 0; j < nrep; ++j) {
+        const int sc = IG ? r * a.mult + j : r / a.mult;
+        const float *plane = in + (n * a.CI + sc) * (a.IH * a.IW);
+        const WT *wc = w + (IG ? sc : r) * kk;
+        for (int kh = 0; kh < a.kH; ++kh) {
+            int ih;
             if (!IG) {
-                iw = ow * S + kw * a.d - a.pW;
-                if (iw < 0 || iw >= a.IW)
+                ih = oh * S + kh * a.d - a.pH;
+                if (ih < 0 || ih >= a.IH)
                     continue;
             } else {
-                const int tw = ow + kw * a.d - a.pW;
-                if (tw < 0 || tw >= a.OW || (S == 2 && (tw & 1)))
+                const int th = oh + kh * a.d - a.pH;
+                if (th < 0 || (S == 2 && (th & 1)))
                     continue;
-                iw = tw / S;
+                ih = th / S;
+                if (ih >= a.IH)
+                    continue;
             }
-            const int tap = IG ? (a.kH - 1 - kh) * a.kW + (a.kW - 1 - kw) : kh * a.kW + kw;
-            acc = fmaf(widen(wc[tap]), plane[ih * a.IW + iw], acc);
+            for (int kw = 0; kw < a.kW; ++kw) {
+                int iw;
+                if (!IG) {
+                    iw = ow * S + kw * a.d - a.pW;
+                    if (iw < 0 || iw >= a.IW)
+                        continue;
+                } else {
+                    const int tw = ow + kw * a.d - a.pW;
+                    if (tw < 0 || (S == 2 && (tw & 1)))
+                        continue;
+                    iw = tw / S;
+                    if (iw >= a.IW)
+                        continue;
+                }
+                const int tap = IG ? (a.kH - 1 - kh) * a.kW + (a.kW - 1 - kw) : kh * a.kW + kw;
+                acc = fmaf(widen(wc[tap]), plane[ih * a.IW + iw], acc);
+            }
         }
     }
-    __builtin_nontemporal_store(acc, out + ((n * a.C + c) * a.OH + oh) * a.OW + ow);
+    __builtin_nontemporal_store(acc, out + ((n * a.CO + r) * a.OH + oh) * a.OW + ow);
 }
 
 // ---------------------------------------------------------------------------
@@ -284,8 +304,9 @@ __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ i
 // sweep, which is what streams fastest on MI355X.
 // ---------------------------------------------------------------------------
 struct TiledArgs {
-    int N, C, H, W;         // image extents (input and output agree at stride 1)
-    int pH, pW;
+    int N, C;
+    int IH, IW, OH, OW;     // extents of the tensor read and the tensor written
+    int pH, pW;             // top / left zero padding of the tensor read
     int nct, nwt, nst;      // channel tiles, column tiles, row tiles
 };
 
@@ -330,7 +351,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
     const int n = tile / a.nst;
     const int c0 = ct * CG, w0 = wt * TW, h0 = st * TH;
     const int tid = threadIdx.x;
-    const int nrows = min(TH, a.H - h0) + R - 1;   // staged rows that exist in the strip
+    const int nrows = min(TH, a.OH - h0) + R - 1;  // staged rows that exist in the strip
     const int rbase = h0 - a.pH, cbase = w0 - a.pW;
 
     const int q = tid % CL, p = tid / CL;
@@ -346,7 +367,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
     // the tile is still in flight.
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in + n * a.IH * a.IW * a.C, a.IH * a.IW * a.C * 4);
     constexpr int NW = (WF + 255) / 256;
     float wst[NW];
 #pragma unroll
@@ -365,9 +386,9 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
         const int col = rem / VPC;
         const int cv = rem - col * VPC;
         const int row = rbase + g, gc = cbase + col, ch = c0 + cv * 4;
-        const bool ok = e < VCH && g < nrows && row >= 0 && row < a.H && gc >= 0 &&
-                        gc < a.W && ch < a.C;
-        stage[i] = buf_f4(rx, ok ? ((row * a.W + gc) * a.C + ch) * 4 : kOutOfRange);
+        const bool ok = e < VCH && g < nrows && row >= 0 && row < a.IH && gc >= 0 &&
+                        gc < a.IW && ch < a.C;
+        stage[i] = buf_f4(rx, ok ? ((row * a.IW + gc) * a.C + ch) * 4 : kOutOfRange);
     }
     // 2. weights, then the tile, into LDS
 #pragma unroll
@@ -406,7 +427,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 
     // 3. walk the staged rows
     constexpr int XW = PX + (KW - 1) * D;  // staged columns one thread reads per row
-    float *outp = out + (n * a.H * a.W) * a.C;
+    float *outp = out + (n * a.OH * a.OW) * a.C;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -437,8 +458,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
             if (m >= 0) {
 #pragma unroll
                 for (int j = 0; j < PX; ++j) {
-                    if (cvalid && ow + j < a.W)
-                        store_vec<VEC>(outp + ((h0 + m) * a.W + ow + j) * a.C + cq,
+                    if (cvalid && ow + j < a.OW)
+                        store_vec<VEC>(outp + ((h0 + m) * a.OW + ow + j) * a.C + cq,
                                        acc[m % R][j]);
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)
@@ -464,8 +485,10 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 // given an out-of-range offset.
 // ---------------------------------------------------------------------------
 struct TiledNchwArgs {
-    int planes, C, H, W;
-    int pH, pW;
+    int planes, C;
+    int IH, IW, OH, OW;     // extents of the tensor read and the tensor written
+    int pH, pW;             // top / left zero padding of the tensor read
+    int hl, twl;            // staged columns left of a tile; staged floats per plane row
     int tx_log2;            // threads per plane row = 1 << tx_log2 (>= 16)
     int nct, nwt, nst;      // plane groups, column tiles, row tiles
 };
@@ -475,12 +498,13 @@ struct NchwGeom {
     static constexpr int R = (KH - 1) * D + 1;
     static constexpr int TH = G - R + 1;
     static constexpr int KK = KH * KW;
-    static constexpr int PW = D * (KW - 1) / 2;
-    static constexpr int HALO = V4 ? (PW + 3) / 4 * 4 : PW;   // staged columns per side
     static constexpr int LV = V4 ? 4 : 1;                      // floats per load
+    // staged columns beyond a tile's own: the window's d*(kW-1), plus up to
+    // 3 columns of alignment with 16-byte loads
+    static constexpr int EXTRA = V4 ? (D * (KW - 1) + 3 + 3) / 4 * 4 : D * (KW - 1);
     static constexpr int PBMAX = 16;                           // TX >= 16
-    // per-thread loads for the largest staged tile: G rows x (256*Q + PBMAX*2*HALO) floats
-    static constexpr int NV = (G * (256 * Q + PBMAX * 2 * HALO) / LV + 255) / 256;
+    // per-thread loads for the largest staged tile: G rows x (256*Q + PBMAX*EXTRA) floats
+    static constexpr int NV = (G * (256 * Q + PBMAX * EXTRA) / LV + 255) / 256;
     static constexpr int NW = (PBMAX * KK + 255) / 256;
     static_assert(TH >= 1, "a workgroup must produce at least one output row");
 };
@@ -492,14 +516,14 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
                                                        float *__restrict__ out, TiledNchwArgs a)
 {
     typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
-    constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, HALO = Gm::HALO, LV = Gm::LV;
+    constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV;
     constexpr int NV = Gm::NV, NW = Gm::NW;
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
     const WT *w = reinterpret_cast<const WT *>(wv);
 
     const int txn = 1 << a.tx_log2, pbn = 256 >> a.tx_log2;
-    const int tw = txn * Q, twl = tw + 2 * HALO;       // staged floats per plane row
+    const int tw = txn * Q, twl = a.twl;               // staged floats per plane row
     const int vpr = twl / LV;                          // loads per plane row
     float *ldsw = lds + pbn * G * twl;
 
@@ -510,12 +534,12 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
     const int st = tile / a.nwt;
     const int w0 = wt * tw, h0 = st * TH;
     const int tid = threadIdx.x;
-    const int nrows = min(TH, a.H - h0) + R - 1;
-    const int rbase = h0 - a.pH, cbase = w0 - HALO;
+    const int nrows = min(TH, a.OH - h0) + R - 1;
+    const int rbase = h0 - a.pH, cbase = w0 - a.hl;
 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes * a.H * a.W * 4);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes * a.IH * a.IW * 4);
 
     // 1. all loads up front: weights of the workgroup's planes, the bias, the tile
     float wst[NW];
@@ -540,9 +564,9 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
         const int g = rem / vpr;
         const int col = cbase + (rem - g * vpr) * LV;
         const int plane = pg * pbn + pl, row = rbase + g;
-        const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && row < a.H &&
-                        col >= 0 && col < a.W;
-        const int off = ok ? ((plane * a.H + row) * a.W + col) * 4 : kOutOfRange;
+        const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && row < a.IH &&
+                        col >= 0 && col < a.IW;
+        const int off = ok ? ((plane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
         if constexpr (V4) {
             const float4 v = buf_f4(rx, off);
             sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
@@ -585,10 +609,10 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
         for (int j = 0; j < Q; ++j)
             acc[r][j] = bval;
     constexpr int XW = Q + (KW - 1) * D;
-    const float *rowbase = lds + pli * G * twl + tx * Q + (HALO - Gm::PW);
+    const float *rowbase = lds + pli * G * twl + tx * Q + (a.hl - a.pW);
     const int oc = w0 + tx * Q;                        // first output column of this thread
-    float *outp = out + my_plane * a.H * a.W;
-    const bool vec_store = (Q > 1) && (a.W % Q == 0);
+    float *outp = out + my_plane * a.OH * a.OW;
+    const bool vec_store = (Q > 1) && (a.OW % Q == 0);
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -610,14 +634,14 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
             }
             const int m = u - (R - 1);
             if (m >= 0) {
-                float *dst = outp + (h0 + m) * a.W + oc;
+                float *dst = outp + (h0 + m) * a.OW + oc;
                 if (pvalid) {
-                    if (vec_store && oc < a.W) {
+                    if (vec_store && oc < a.OW) {
                         store_vec<Q>(dst, acc[m % R]);
                     } else {
 #pragma unroll
                         for (int j = 0; j < Q; ++j)
-                            if (oc + j < a.W)
+                            if (oc + j < a.OW)
                                 __builtin_nontemporal_store(acc[m % R][j], dst + j);
                     }
                 }
@@ -638,7 +662,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
 //   stage 2 adds the chunks of every (c, tap) column in a fixed order.
 // ---------------------------------------------------------------------------
 struct WgradArgs {
-    int N, C, H, W, kH, kW, d, pH, pW;
+    int N, C, mult;         // C: channels of dy (and of dW); x has C / mult
+    int H, W, kH, kW, d, pH, pW;
     int OH, OW;             // dy extents
     int nct, nwt, nsp;      // tiled: channel tiles, column tiles, strips
     int chunks;             // rows of part[]
@@ -668,8 +693,9 @@ __device__ __forceinline__ float block_sum_256(float v, float *red)
     return r;
 }
 
-// Stage 1, any layout and stride: workgroup = (chunk of kWgradChunk dy
-// positions, channel c); each thread strides over the chunk's positions.
+// Stage 1, any layout, stride, padding and multiplier: workgroup = (chunk of
+// kWgradChunk dy positions, output channel c, which reads x channel c/mult);
+// each thread strides over the chunk's positions.
 template <bool NHWC, int S>
 __global__ __launch_bounds__(256) void k_wgrad_direct(const float *__restrict__ x,
                                                       const float *__restrict__ dy,
@@ -695,7 +721,8 @@ __global__ __launch_bounds__(256) void k_wgrad_direct(const float *__restrict__ 
             } else {
                 const int hi = ho * S + kh * a.d - a.pH, wi = wo * S + kw * a.d - a.pW;
                 if (hi >= 0 && hi < a.H && wi >= 0 && wi < a.W)
-                    acc = fmaf(x[elem_index(NHWC, a.C, a.H, a.W, n, c, hi, wi)], g, acc);
+                    acc = fmaf(x[elem_index(NHWC, a.C / a.mult, a.H, a.W, n, c / a.mult, hi, wi)],
+                               g, acc);
             }
         }
         const float sum = block_sum_256(acc, red);
@@ -741,7 +768,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     const int ow = w0 + p * PX;
     const int cbase = w0 - a.pW;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy + n * a.OH * a.OW * a.C, a.OH * a.OW * a.C * 4);
 
     float acc[KK + 1][VEC];                 // taps kh*KW + kw, then the bias
 #pragma unroll
@@ -750,10 +777,10 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
         for (int v = 0; v < VEC; ++v)
             acc[t][v] = 0.0f;
 
-    const int t0 = sp * STRIP, t1 = min(t0 + STRIP, (a.H + TH - 1) / TH);
+    const int t0 = sp * STRIP, t1 = min(t0 + STRIP, (a.OH + TH - 1) / TH);
     for (int tt = t0; tt < t1; ++tt) {
         const int h0 = tt * TH;
-        const int nrows = min(TH, a.H - h0) + R - 1;
+        const int nrows = min(TH, a.OH - h0) + R - 1;
         const int rbase = h0 - a.pH;
         // this row tile's x rows (+ halo) and, per thread, its dy values
         float4 stage[NV];
@@ -774,8 +801,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
         for (int m = 0; m < TH; ++m)
 #pragma unroll
             for (int j = 0; j < PX; ++j) {
-                const bool ok = h0 + m < a.H && ow + j < a.W && cq < a.C;
-                buf_vec<VEC>(rg, ok ? (((h0 + m) * a.W + ow + j) * a.C + cq) * 4 : kOutOfRange,
+                const bool ok = h0 + m < a.OH && ow + j < a.OW && cq < a.C;
+                buf_vec<VEC>(rg, ok ? (((h0 + m) * a.OW + ow + j) * a.C + cq) * 4 : kOutOfRange,
                              gv[m][j]);
             }
         if (tt > t0)
@@ -880,7 +907,10 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ 
 DirectArgs direct_args(const Problem &p, const Plan &pl)
 {
     DirectArgs a;
-    a.N = p.N; a.C = p.C; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
+    a.N = p.N; a.mult = p.mult;
+    a.CI = p.op == DWCONV_OP_FWD ? p.C : p.mult * p.C;   // channels of the tensor read
+    a.CO = p.op == DWCONV_OP_FWD ? p.mult * p.C : p.C;   // channels of the tensor written
+    a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
     a.pH = pl.pH; a.pW = pl.pW;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
     a.total = (int)pl.total;
@@ -954,7 +984,9 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
         return DWCONV_ERR_BAD_STRATEGY;
     TiledFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][p.op == DWCONV_OP_INPUT_GRAD];
     TiledArgs a;
-    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.pH = pl.pH; a.pW = pl.pW;
+    a.N = p.N; a.C = p.C;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                        p.op == DWCONV_OP_FWD ? b : nullptr, out, a);
@@ -1003,7 +1035,9 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
         return DWCONV_ERR_BAD_STRATEGY;
     TiledNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][p.op == DWCONV_OP_INPUT_GRAD];
     TiledNchwArgs a;
-    a.planes = p.N * p.C; a.C = p.C; a.H = p.H; a.W = p.W; a.pH = pl.pH; a.pW = pl.pW;
+    a.planes = p.N * p.C; a.C = p.C;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.pH = pl.pH; a.pW = pl.pW; a.hl = pl.hl; a.twl = pl.twl;
     a.tx_log2 = 0;
     while ((1 << a.tx_log2) < pl.cl)
         ++a.tx_log2;
@@ -1070,7 +1104,8 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     hipStream_t st = reinterpret_cast<hipStream_t>(stream_v);
     float *part = reinterpret_cast<float *>(workspace);
     WgradArgs a;
-    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
+    a.N = p.N; a.C = p.mult * p.C; a.mult = p.mult;
+    a.H = p.H; a.W = p.W; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
     a.pH = pl.pH; a.pW = pl.pW; a.OH = pl.OH; a.OW = pl.OW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.chunks = (int)pl.chunks;
     if (pl.kind == KIND_WGRAD_TILED_NHWC) {
@@ -1094,7 +1129,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         return DWCONV_ERR_BAD_STRATEGY;
     }
     hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw, db,
-                       (int)pl.chunks, p.C, p.kH * p.kW);
+                       (int)pl.chunks, p.mult * p.C, p.kH * p.kW);
     return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
 }
 

@@ -2,10 +2,15 @@
 // no HIP runtime calls).
 //
 // Shape rules (LeanMlir "Depthwise" page, forward equation, read with stride
-// s and dilation d): pH = d*(kH-1)/2, pW = d*(kW-1)/2 with odd kernels (SAME
-// padding), Ho = ceil(H/s), Wo = ceil(W/s).  Selecting the tiling from the
-// problem's extents mirrors the cubek-convolution "depthwise" module, whose
-// launch space is built from the problem extents and a tiling strategy.
+// s, dilation d and explicit zero padding pt/pb (rows), pl/pr (columns)):
+// output row ho reads input rows ho*s + kh*d - pt, and the output keeps the
+// window positions that fit, Ho = (H + pt + pb - d*(kH-1) - 1)/s + 1 (same
+// for columns).  SAME padding is pt = pb = d*(kH-1)/2 with odd kernels, so
+// Ho = ceil(H/s); the page's stride-2 XLA-SAME is pt = d*(kH-1)/2 - 1,
+// pb = d*(kH-1)/2 (the odd positions of the stride-1 result).  Selecting the
+// tiling from the problem's extents mirrors the cubek-convolution
+// "depthwise" module, whose launch space is built from the problem extents
+// and a tiling strategy.
 #include "dwconv_internal.h"
 #include "../../include/dwconv.h"
 
@@ -18,41 +23,93 @@ namespace dwconv {
 namespace {
 
 constexpr long long kMaxElems = (1LL << 31) - 1;  // 32-bit element indexing
+constexpr int kMaxPad = 1 << 16;                   // |pad| bound
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-int validate_problem(const Problem &p)
+Problem same_problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int kH,
+                     int kW, int stride, int dilation, int layout)
+{
+    Problem p;
+    std::memset(&p, 0, sizeof p);
+    p.op = op; p.wtype = wtype; p.layout = layout; p.has_bias = has_bias;
+    p.N = N; p.H = H; p.W = W; p.C = C; p.kH = kH; p.kW = kW;
+    p.stride = stride; p.dilation = dilation;
+    p.mult = 1;
+    p.same = 1;
+    // symmetric SAME pads; for even kernels validate_problem rejects the problem
+    const long long ph = (long long)dilation * (kH - 1) / 2, pw = (long long)dilation * (kW - 1) / 2;
+    p.pt = p.pb = (int)std::min<long long>(std::max<long long>(ph, 0), 1 << 20);
+    p.pl = p.pr = (int)std::min<long long>(std::max<long long>(pw, 0), 1 << 20);
+    return p;
+}
+
+int validate_problem(Problem &p)
 {
     if (p.op != DWCONV_OP_FWD && p.op != DWCONV_OP_INPUT_GRAD && p.op != DWCONV_OP_WEIGHT_GRAD)
         return DWCONV_ERR_BAD_OP;
-    if (p.N < 1 || p.H < 1 || p.W < 1 || p.C < 1 || p.kH < 1 || p.kW < 1)
+    if (p.N < 1 || p.H < 1 || p.W < 1 || p.C < 1 || p.kH < 1 || p.kW < 1 || p.mult < 1)
         return DWCONV_ERR_BAD_DIM;
+    const long long co = (long long)p.C * p.mult;
     const long long in_elems = (long long)p.N * p.H * p.W * p.C;
-    if (in_elems > kMaxElems || (long long)p.C * p.kH * p.kW > kMaxElems)
+    if (in_elems > kMaxElems || co * p.kH * p.kW > kMaxElems)
         return DWCONV_ERR_BAD_DIM;
     if (p.stride != 1 && p.stride != 2)
         return DWCONV_ERR_BAD_STRIDE;
     if (p.dilation < 1 || (long long)p.dilation * (std::max(p.kH, p.kW) - 1) >= (1 << 16))
         return DWCONV_ERR_BAD_DILATION;
-    if (p.kH % 2 == 0 || p.kW % 2 == 0)
+    if (p.same && (p.kH % 2 == 0 || p.kW % 2 == 0))
         return DWCONV_ERR_EVEN_KERNEL;
     if (p.layout != DWCONV_LAYOUT_NHWC && p.layout != DWCONV_LAYOUT_NCHW)
         return DWCONV_ERR_BAD_LAYOUT;
     if (p.wtype != DWCONV_W_F32 && p.wtype != DWCONV_W_F16)
         return DWCONV_ERR_BAD_WTYPE;
+    const int pads[4] = {p.pt, p.pb, p.pl, p.pr};
+    for (int i = 0; i < 4; ++i)
+        if (pads[i] <= -kMaxPad || pads[i] >= kMaxPad)
+            return DWCONV_ERR_BAD_PAD;
+    // window positions that fit the padded input (the numerators stay far
+    // from overflow: every term is below 2^31 / 4 in magnitude)
+    const long long nh = (long long)p.H + p.pt + p.pb - (long long)p.dilation * (p.kH - 1) - 1;
+    const long long nw = (long long)p.W + p.pl + p.pr - (long long)p.dilation * (p.kW - 1) - 1;
+    if (nh < 0 || nw < 0)
+        return DWCONV_ERR_BAD_DIM;
+    const long long Ho = nh / p.stride + 1, Wo = nw / p.stride + 1;
+    if ((long long)p.N * Ho * Wo * co > kMaxElems)
+        return DWCONV_ERR_BAD_DIM;
+    p.Ho = (int)Ho;
+    p.Wo = (int)Wo;
     return DWCONV_OK;
+}
+
+// Effective zero padding and the extents of the tensors read and written,
+// per op.  The input gradient runs the reversed-kernel form over dy, which
+// is a stride-1 correlation of the zero-upsampled dy with top pad
+// d*(kH-1) - pt (and left pad d*(kW-1) - pl).
+static void set_extents(const Problem &p, Plan *pl)
+{
+    if (p.op == DWCONV_OP_INPUT_GRAD) {
+        pl->IH = p.Ho; pl->IW = p.Wo; pl->OH = p.H; pl->OW = p.W;
+        pl->pH = p.dilation * (p.kH - 1) - p.pt;
+        pl->pW = p.dilation * (p.kW - 1) - p.pl;
+    } else {
+        // forward reads x and writes y; the weight gradient reads x and dy
+        pl->IH = p.H; pl->IW = p.W; pl->OH = p.Ho; pl->OW = p.Wo;
+        pl->pH = p.pt;
+        pl->pW = p.pl;
+    }
 }
 
 static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NHWC)
+    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
         return false;
     if (p.C % 4 != 0 || (ptr_bits & 15u) != 0)
         return false;
     // buffer-load byte offsets are 31-bit: one image and the weights must fit
-    if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+    if (4LL * pl->IH * pl->IW * p.C >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
         return false;
     // first variant of this kernel shape (table order = preference) whose
     // channel tile the problem fills to at least 3/4; else the one it fills best
@@ -84,8 +141,8 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->tw = v.px * 256 / v.cl;
     pl->th = v.g - R + 1;
     pl->nct = ceil_div(p.C, v.cl * v.vec);
-    pl->nwt = ceil_div(p.W, pl->tw);
-    pl->nst = ceil_div(p.H, pl->th);
+    pl->nwt = ceil_div(pl->OW, pl->tw);
+    pl->nst = ceil_div(pl->OH, pl->th);
     pl->grid = (long long)p.N * pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_%s_%s",
@@ -96,12 +153,13 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 
 static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NCHW)
+    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NCHW)
         return false;
-    // buffer-load byte offsets are 31-bit: the whole tensor and the weights must fit
-    if (4LL * p.N * p.C * p.H * p.W >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+    // buffer-load byte offsets are 31-bit: the tensor read and the weights must fit
+    const long long planes = (long long)p.N * p.C;
+    if (4LL * planes * pl->IH * pl->IW >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
         return false;
-    const bool v4ok = p.W % 4 == 0 && (ptr_bits & 15u) == 0;
+    const bool v4ok = pl->IW % 4 == 0 && (ptr_bits & 15u) == 0;
     int best = -1;
     for (int i = 0; i < kNumTiledNchwVariants; ++i) {
         const TiledNchwVariant &v = kTiledNchwVariants[i];
@@ -115,21 +173,26 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     const TiledNchwVariant &v = kTiledNchwVariants[best];
     const int R = (v.kH - 1) * v.d + 1;
     int tx = 16;                                 // threads per plane row: pow2 >= W/q, >= 16
-    while (tx < 256 && tx * v.q < p.W)
+    while (tx < 256 && tx * v.q < pl->OW)
         tx *= 2;
-    const int pW = v.d * (v.kW - 1) / 2;
-    const int halo = v.v4 ? (pW + 3) / 4 * 4 : pW;
+    // staged columns of a plane row: from w0 - hl (hl = the left pad rounded
+    // up to whole 16-byte loads) over the tile's tw + d*(kW-1) input columns
+    const int lv = v.v4 ? 4 : 1;
+    const int hl = v.v4 ? -((-pl->pW) & ~3) : pl->pW;   // ceil to a multiple of 4
+    const int span = (hl - pl->pW) + tx * v.q + v.d * (v.kW - 1);
     pl->kind = KIND_TILED_NCHW;
     pl->variant = best;
     pl->vec = 1;
     pl->cl = tx;
     pl->pb = 256 / tx;
     pl->tw = tx * v.q;
+    pl->hl = hl;
+    pl->twl = (span + lv - 1) / lv * lv;
     pl->th = v.g - R + 1;
-    pl->nct = ceil_div(p.N * p.C, pl->pb);
-    pl->nwt = ceil_div(p.W, pl->tw);
-    pl->nst = ceil_div(p.H, pl->th);
-    pl->lds_bytes = 4 * (pl->pb * v.g * (pl->tw + 2 * halo) + pl->pb * v.kH * v.kW);
+    pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
+    pl->nwt = ceil_div(pl->OW, pl->tw);
+    pl->nst = ceil_div(pl->OH, pl->th);
+    pl->lds_bytes = 4 * (pl->pb * v.g * pl->twl + pl->pb * v.kH * v.kW);
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s1_k%dx%d_d%d_q%d_g%d_%s_tx%d_%s_%s",
@@ -140,16 +203,18 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 
 static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
+    // channels of the tensor written: mult*C for the forward, C for the input gradient
+    const long long cres = p.op == DWCONV_OP_FWD ? (long long)p.mult * p.C : p.C;
     pl->block = 256;
     pl->variant = -1;
     if (p.layout == DWCONV_LAYOUT_NHWC) {
         pl->kind = KIND_DIRECT_NHWC;
-        pl->vec = (p.C % 4 == 0 && (ptr_bits & 15u) == 0) ? 4 : 1;
-        pl->total = (long long)p.N * pl->OH * pl->OW * (p.C / pl->vec);
+        pl->vec = (p.mult == 1 && p.C % 4 == 0 && (ptr_bits & 15u) == 0) ? 4 : 1;
+        pl->total = (long long)p.N * pl->OH * pl->OW * (cres / pl->vec);
     } else {
         pl->kind = KIND_DIRECT_NCHW;
         pl->vec = 1;
-        pl->total = (long long)p.N * p.C * pl->OH * pl->OW;
+        pl->total = (long long)p.N * cres * pl->OH * pl->OW;
     }
     pl->grid = (pl->total + pl->block - 1) / pl->block;
     std::snprintf(pl->name, sizeof pl->name, "direct_%s_s%d_v%d_%s_%s",
@@ -157,7 +222,7 @@ static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
                   p.op ? "ig" : "fwd", p.wtype ? "f16w" : "f32w");
 }
 
-int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
+int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
 {
     if (p.op == DWCONV_OP_WEIGHT_GRAD)
         return make_wgrad_plan(p, strategy, ptr_bits, pl);
@@ -168,14 +233,7 @@ int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         strategy != DWCONV_STRATEGY_TILED)
         return DWCONV_ERR_BAD_STRATEGY;
     std::memset(pl, 0, sizeof *pl);
-    const int Ho = ceil_div(p.H, p.stride), Wo = ceil_div(p.W, p.stride);
-    pl->pH = p.dilation * (p.kH - 1) / 2;
-    pl->pW = p.dilation * (p.kW - 1) / 2;
-    if (p.op == DWCONV_OP_FWD) {
-        pl->IH = p.H; pl->IW = p.W; pl->OH = Ho; pl->OW = Wo;
-    } else {
-        pl->IH = Ho; pl->IW = Wo; pl->OH = p.H; pl->OW = p.W;
-    }
+    set_extents(p, pl);
     if (strategy == DWCONV_STRATEGY_DIRECT) {
         plan_direct(p, ptr_bits, pl);
         return DWCONV_OK;
@@ -205,9 +263,10 @@ int make_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
 // ---------------------------------------------------------------------------
 static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NHWC || p.C % 4 != 0 || (ptr_bits & 15u))
+    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC || p.C % 4 != 0 ||
+        (ptr_bits & 15u))
         return false;
-    if (4LL * p.H * p.W * p.C >= (1LL << 31))
+    if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.Ho * p.Wo * p.C >= (1LL << 31))
         return false;
     int best = -1;
     double best_fill = -1.0;
@@ -238,8 +297,8 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     pl->th = v.g - R + 1;
     pl->strip = v.strip;
     pl->nct = ceil_div(p.C, v.cl * v.vec);
-    pl->nwt = ceil_div(p.W, pl->tw);
-    pl->nst = ceil_div(ceil_div(p.H, pl->th), v.strip);   // strips
+    pl->nwt = ceil_div(p.Wo, pl->tw);
+    pl->nst = ceil_div(ceil_div(p.Ho, pl->th), v.strip);   // strips
     pl->chunks = (long long)p.N * pl->nst * pl->nwt;
     pl->grid = pl->chunks * pl->nct;
     pl->block = 256;
@@ -254,13 +313,13 @@ static void plan_wgrad_direct(const Problem &p, Plan *pl)
     pl->kind = KIND_WGRAD_DIRECT;
     pl->variant = -1;
     pl->chunks = (positions + kWgradChunk - 1) / kWgradChunk;
-    pl->grid = pl->chunks * p.C;
+    pl->grid = pl->chunks * p.mult * p.C;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "wgrad_direct_%s_s%d",
                   p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride);
 }
 
-int make_wgrad_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
+int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
 {
     int st = validate_problem(p);
     if (st != DWCONV_OK)
@@ -269,10 +328,7 @@ int make_wgrad_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Pla
         strategy != DWCONV_STRATEGY_TILED)
         return DWCONV_ERR_BAD_STRATEGY;
     std::memset(pl, 0, sizeof *pl);
-    pl->pH = p.dilation * (p.kH - 1) / 2;
-    pl->pW = p.dilation * (p.kW - 1) / 2;
-    pl->IH = p.H; pl->IW = p.W;
-    pl->OH = ceil_div(p.H, p.stride); pl->OW = ceil_div(p.W, p.stride);
+    set_extents(p, pl);
     bool tiled = false;
     if (strategy != DWCONV_STRATEGY_DIRECT) {
         Plan t = *pl;
@@ -284,7 +340,7 @@ int make_wgrad_plan(const Problem &p, int strategy, std::uintptr_t ptr_bits, Pla
     }
     if (!tiled)
         plan_wgrad_direct(p, pl);
-    const long long cols = (long long)p.C * (p.kH * p.kW + 1);
+    const long long cols = (long long)p.mult * p.C * (p.kH * p.kW + 1);
     if (pl->chunks * cols >= (1LL << 31))
         return DWCONV_ERR_BAD_DIM;
     pl->workspace = 4 * pl->chunks * cols;

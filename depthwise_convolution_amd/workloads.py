@@ -8,9 +8,16 @@ Shapes are the ones the pages time or test: the ggml PR's perf table
 (llama.cpp PR #21565, "Performance (Apple M5)": [W,H,C,N] = [19,30,128,1] 7x7,
 [24,1,128,1] 1x15, [24,1,256,1] 1x31, [512,512,256,1] 3x3, [112,112,32,1] 3x3,
 [56,56,128,1] 5x5), the ASR shapes and edge cases of its review thread
-(dilation, prime channel count, batch > 1), and the MobileNetV2 stride-2
-downsampling of the LeanMlir "Depthwise" page.  No dataset stands behind any
-of them: every value is drawn here.
+(dilation, prime channel count, batch > 1), the MobileNetV2 stride-2
+downsampling of the LeanMlir "Depthwise" page (SAME and XLA-SAME), and the
+grouped "4 => 8, groups = 4" layer of Reactant.jl issue 331 (a channel
+multiplier).  No dataset stands behind any of them: every value is drawn
+here.
+
+A workload's padding is SAME (d*(k-1)/2 on every side) unless it names
+explicit ``pads = (top, bottom, left, right)``; ``mult`` output channels are
+computed per input channel.  The output extents below are only the sizes of
+the arrays to draw (window positions that fit the padded input).
 
 Draw order and dtype: numpy ``default_rng(seed)``, in the order x, W, b, dy,
 each drawn in float64 over the logical [N, H, W, C] (or [C, kH, kW]) shape and
@@ -42,32 +49,54 @@ class Workload:
     dy_dist: str = "normal1"
     fp16_weights: bool = False
     bias: bool = True
+    pads: tuple = None           # (top, bottom, left, right); None = SAME
+    mult: int = 1                # output channels per input channel
     tags: tuple = field(default=())
 
     @property
+    def general(self):
+        """True when the workload needs the explicit-padding / multiplier form."""
+        return self.pads is not None or self.mult != 1
+
+    @property
     def Ho(self):
-        return (self.H + self.stride - 1) // self.stride
+        if self.pads is None:
+            return (self.H + self.stride - 1) // self.stride
+        t, b = self.pads[0], self.pads[1]
+        return (self.H + t + b - self.dilation * (self.kH - 1) - 1) // self.stride + 1
 
     @property
     def Wo(self):
-        return (self.W + self.stride - 1) // self.stride
+        if self.pads is None:
+            return (self.W + self.stride - 1) // self.stride
+        l, r = self.pads[2], self.pads[3]
+        return (self.W + l + r - self.dilation * (self.kW - 1) - 1) // self.stride + 1
+
+    @property
+    def Co(self):
+        return self.mult * self.C
 
     @property
     def wbytes(self):
-        return self.C * self.kH * self.kW * (2 if self.fp16_weights else 4)
+        return self.Co * self.kH * self.kW * (2 if self.fp16_weights else 4)
 
     def fwd_bytes(self):
         """Algorithmic bytes of one forward: x + y + W + b."""
-        return (4 * self.N * self.H * self.W * self.C + 4 * self.N * self.Ho * self.Wo * self.C
-                + self.wbytes + (4 * self.C if self.bias else 0))
+        return (4 * self.N * self.H * self.W * self.C + 4 * self.N * self.Ho * self.Wo * self.Co
+                + self.wbytes + (4 * self.Co if self.bias else 0))
 
     def ig_bytes(self):
         """Algorithmic bytes of one input gradient: dy + dx + W."""
-        return (4 * self.N * self.Ho * self.Wo * self.C + 4 * self.N * self.H * self.W * self.C
+        return (4 * self.N * self.Ho * self.Wo * self.Co + 4 * self.N * self.H * self.W * self.C
                 + self.wbytes)
 
+    def wgrad_bytes(self):
+        """Algorithmic bytes of the weight + bias gradient: x + dy + dW + db."""
+        return (4 * self.N * self.H * self.W * self.C + 4 * self.N * self.Ho * self.Wo * self.Co
+                + 4 * self.Co * self.kH * self.kW + 4 * self.Co)
+
     def fwd_flops(self):
-        return 2 * self.N * self.Ho * self.Wo * self.C * self.kH * self.kW
+        return 2 * self.N * self.Ho * self.Wo * self.Co * self.kH * self.kW
 
 
 def _w(name, N, H, W, C, k, **kw):
@@ -103,6 +132,17 @@ WORKLOADS = {w.name: w for w in [
     _w("prime_n1_1x24x131_1x15", 1, 1, 24, 131, (1, 15), **_U, tags=("parity_only",)),
     _w("prime_n64_1x24x131_1x15", 64, 1, 24, 131, (1, 15), **_U, tags=("parity_only",)),
     _w("large_512x512x256_3x3", 1, 512, 512, 256, (3, 3), tags=("target", "large")),
+    # explicit padding: the page's stride-2 XLA-SAME (odd positions kept) on
+    # the MobileNetV2 downsampling shape, and VALID (no padding) at stride 1
+    _w("mobilenet_s2_xla_224x224x32_3x3", 1, 224, 224, 32, (3, 3), stride=2,
+       pads=(0, 1, 0, 1), tags=("general",)),
+    _w("effnet_n32_56x56x128_5x5_valid", 32, 56, 56, 128, (5, 5), pads=(0, 0, 0, 0),
+       tags=("general",)),
+    # channel multiplier: the Reactant.jl layer (4 => 8, groups = 4, 3x3, no
+    # padding, 4x4 input) and a multiplier of 2 on the MobileNet shape
+    _w("reactant_4x4x4_3x3_m2_valid", 1, 4, 4, 4, (3, 3), pads=(0, 0, 0, 0), mult=2, **_U,
+       tags=("general", "parity_only")),
+    _w("mobilenet_m2_112x112x32_3x3", 1, 112, 112, 32, (3, 3), mult=2, tags=("general",)),
 ]}
 
 
@@ -143,17 +183,17 @@ def make_inputs(wl: Workload, layout=NHWC, seed=0, integer=False):
     rng = np.random.default_rng(seed)
     kk = wl.kH * wl.kW
     xs = (wl.N, wl.H, wl.W, wl.C)
-    ys = (wl.N, wl.Ho, wl.Wo, wl.C)
-    ws = (wl.C, wl.kH, wl.kW)
+    ys = (wl.N, wl.Ho, wl.Wo, wl.Co)
+    ws = (wl.Co, wl.kH, wl.kW)
     if integer:
         x = _draw(rng, "int3", xs)
         w = _draw(rng, "int3", ws)
-        b = _draw(rng, "int2", (wl.C,))
+        b = _draw(rng, "int2", (wl.Co,))
         dy = _draw(rng, "int3", ys)
     else:
         x = _draw(rng, wl.x_dist, xs)
         w = _draw(rng, wl.w_dist, ws, kk)
-        b = rng.uniform(-0.1, 0.1, (wl.C,))
+        b = rng.uniform(-0.1, 0.1, (wl.Co,))
         dy = _draw(rng, wl.dy_dist, ys)
     x = x.astype(np.float32)
     dy = dy.astype(np.float32)

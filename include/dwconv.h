@@ -61,6 +61,7 @@ extern "C" {
 #define DWCONV_ERR_BAD_OP      -11  /* op not FWD or INPUT_GRAD                      */
 #define DWCONV_ERR_BAD_STRATEGY -12 /* strategy unknown, or not applicable to the problem */
 #define DWCONV_ERR_WORKSPACE   -13  /* workspace NULL, misaligned or smaller than required */
+#define DWCONV_ERR_BAD_PAD     -14  /* a pad with |pad| >= 2^16, or an unknown padding mode */
 
 /* ---- enumerations (passed as int) -------------------------------------- */
 #define DWCONV_LAYOUT_NHWC 0   /* channel innermost (the ggml page's CWHN)    */
@@ -72,6 +73,11 @@ extern "C" {
 #define DWCONV_OP_FWD        0 /* y  = dwconv(x; W, b)                        */
 #define DWCONV_OP_INPUT_GRAD 1 /* dx = dwconv_input_grad(dy; W)               */
 #define DWCONV_OP_WEIGHT_GRAD 2 /* dW, db = dwconv_weight_grad(x, dy) (planning only) */
+
+/* Padding modes of dwconv2d_same_pads. */
+#define DWCONV_PAD_SAME     0  /* symmetric: d*(k-1)/2 on every side (odd kernels)   */
+#define DWCONV_PAD_XLA_SAME 1  /* LeanMlir "Depthwise" stride-2 XLA-SAME: the stride-1
+                                  SAME result kept at the ODD positions               */
 
 /* Which tiling to run a problem under (cubek-convolution "depthwise" module:
  * a strategy enum selects the tiling, one launch function runs it). */
@@ -148,6 +154,84 @@ int dwconv2d_weight_grad(const float *x, const float *dy, float *dw, float *db,
                          void *workspace, long long workspace_bytes,
                          int N, int H, int W, int C, int kH, int kW,
                          int stride, int dilation, int layout, int strategy, void *stream);
+
+/* ---- general form: explicit padding and a channel multiplier -----------
+ *
+ * The operation with explicit zero padding pads = {top, bottom, left, right}
+ * (a host array of 4 ints; negative values crop) and a channel multiplier
+ * mult >= 1 (grouped convolution with groups = C input channels and
+ * mult*C output channels, the "4 => 8, groups = 4" layer of Reactant.jl
+ * issue 331; output channel o reads input channel o / mult):
+ *
+ *   y[n,o,ho,wo] = b[o] + sum_{kh,kw} x[n, o/mult, ho*s + kh*d - top,
+ *                                          wo*s + kw*d - left] * W[o,kh,kw]
+ *
+ * over in-range input positions; the output keeps every window position
+ * that fits the padded input:
+ *
+ *   Ho = (H + top + bottom - d*(kH-1) - 1) / s + 1   (floor; must be >= 1)
+ *   Wo = (W + left + right - d*(kW-1) - 1) / s + 1
+ *
+ * The input gradient is its transpose (each input position collects
+ * W[o,kh,kw] * dy[n,o,ho,wo] over the mult output channels o reading it and
+ * the (ho, kh) with ho*s + kh*d - top = h, likewise for columns): the
+ * zero-upsampled dy placed on the positions the forward kept, run through
+ * the reversed-kernel correlation.  The weight and bias gradients are
+ *
+ *   dW[o,kh,kw] = sum_{n,ho,wo} x[n, o/mult, ho*s+kh*d-top, wo*s+kw*d-left] * dy[n,o,ho,wo]
+ *   db[o]       = sum_{n,ho,wo} dy[n,o,ho,wo]
+ *
+ * Kernel extents may be even here (the pads are explicit).  Shapes: x, dx
+ * [N,H,W,C] / [N,C,H,W]; y, dy [N,Ho,Wo,mult*C] / [N,mult*C,Ho,Wo]; W
+ * [mult*C][kH][kW] (the same bytes as a transposed convolution's
+ * [C_in][C_out/groups][kH][kW] weight for dy -> dx, ExecuTorch MLX
+ * conv-transpose weight page); b [mult*C] or NULL.  Ownership, execution
+ * and errors as for the SAME entry points, plus DWCONV_ERR_NULL_PTR for a
+ * NULL pads array and DWCONV_ERR_BAD_PAD.  With pads from
+ * dwconv2d_same_pads(DWCONV_PAD_SAME, ...) and mult = 1 every call below is
+ * the SAME entry point of the same name.
+ */
+
+/* Pads of a padding mode (DWCONV_PAD_SAME or DWCONV_PAD_XLA_SAME) for odd
+ * kernels: writes {top, bottom, left, right} to pads[0..3].  SAME gives
+ * d*(k-1)/2 everywhere; XLA_SAME at stride 2 gives top = d*(kH-1)/2 - 1,
+ * bottom = d*(kH-1)/2 (same for columns), so that Ho = floor(H/2) and
+ * output row ho is the stride-1 SAME row 2*ho + 1 (at stride 1 it equals
+ * SAME).  On even extents with kernels of two or more taps these are XLA's
+ * own SAME pads.  Host only. */
+int dwconv2d_same_pads(int mode, int H, int W, int kH, int kW, int stride, int dilation,
+                       int *pads);
+
+/* Output extents Ho, Wo (either may be NULL) of a padded problem; validates
+ * as the launch would.  Host only. */
+int dwconv2d_out_extents(int H, int W, int kH, int kW, int stride, int dilation,
+                         const int *pads, int *Ho, int *Wo);
+
+/* dwconv2d_launch with explicit pads and a channel multiplier.  C is the
+ * number of INPUT channels (x, dx); y, dy, W and b have mult*C. */
+int dwconv2d_launch_ex(int op, const float *in, const void *w, int wtype, const float *b,
+                       float *out, int N, int H, int W, int C, int mult, int kH, int kW,
+                       int stride, int dilation, const int *pads, int layout, int strategy,
+                       void *stream);
+
+/* dwconv2d_describe with explicit pads and a channel multiplier (op may be
+ * DWCONV_OP_WEIGHT_GRAD). */
+int dwconv2d_describe_ex(int op, int wtype, int has_bias, int N, int H, int W, int C, int mult,
+                         int kH, int kW, int stride, int dilation, const int *pads, int layout,
+                         int strategy, char *name, int name_len, long long *grid, int *block);
+
+/* Weight and bias gradients with explicit pads and a channel multiplier:
+ * dw is [mult*C][kH][kW], db [mult*C] or NULL; workspace as for
+ * dwconv2d_weight_grad, sized by dwconv2d_weight_grad_workspace_size_ex. */
+int dwconv2d_weight_grad_workspace_size_ex(int N, int H, int W, int C, int mult, int kH, int kW,
+                                           int stride, int dilation, const int *pads,
+                                           int layout, int strategy, long long *bytes);
+
+int dwconv2d_weight_grad_ex(const float *x, const float *dy, float *dw, float *db,
+                            void *workspace, long long workspace_bytes,
+                            int N, int H, int W, int C, int mult, int kH, int kW,
+                            int stride, int dilation, const int *pads, int layout, int strategy,
+                            void *stream);
 
 /* Static text for a status code ("unknown status" for unknown codes). */
 const char *dwconv2d_strerror(int status);

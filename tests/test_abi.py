@@ -225,3 +225,122 @@ def test_weight_grad_workspace_and_plans():
 def test_launch_rejects_weight_grad_op(L):
     args = [VP(X), VP(WP), 0, None, VP(Y), 1, 8, 8, 4, 3, 3, 1, 1, 0]
     assert L.dwconv2d_launch(2, *args, 0, None) == -11
+
+
+# ------------------------------------------- explicit padding, channel multiplier
+def _pads(*v):
+    return (ctypes.c_int * 4)(*v)
+
+
+def _fwd_ex(L, x=X, w=WP, wt=0, b=B, y=Y, N=1, H=8, W=8, C=4, m=1, kH=3, kW=3, s=1, d=1,
+            pads=(1, 1, 1, 1), lay=0, strat=0, op=0):
+    return L.dwconv2d_launch_ex(op, VP(x) if x else None, VP(w) if w else None, wt,
+                                VP(b) if b else None, VP(y) if y else None,
+                                N, H, W, C, m, kH, kW, s, d,
+                                _pads(*pads) if pads is not None else None, lay, strat, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(pads=None), -1), (dict(x=0), -1),
+    (dict(m=0), -2), (dict(C=0), -2),
+    (dict(pads=(-8, 0, 0, 0)), -2),                    # no window position fits (Ho < 1)
+    (dict(H=1, pads=(0, 0, 0, 0)), -2),
+    (dict(pads=(1 << 16, 0, 0, 0)), -14), (dict(pads=(0, 0, 0, -(1 << 16))), -14),
+    (dict(s=3), -3), (dict(d=0), -4), (dict(lay=4), -6), (dict(wt=3), -7),
+    (dict(op=2), -11), (dict(op=1), -11),              # weight-grad op; bias with input grad
+    (dict(y=X + 64), -8), (dict(x=X + 2), -9), (dict(strat=5), -12),
+])
+def test_launch_ex_rejects(L, kwargs, code):
+    assert _fwd_ex(L, **kwargs) == code
+
+
+def test_launch_ex_accepts_even_kernels_and_crops(L):
+    # even kernels are valid with explicit pads (the SAME entry points reject
+    # them), and so are negative pads while a window position still fits; the
+    # call stops at the overlap check, after validation
+    assert _fwd_ex(L, kH=2, kW=4, pads=(0, 1, 1, 2), y=X + 64) == -8
+    assert _fwd_ex(L, pads=(-1, 0, -2, 1), y=X + 64) == -8
+    assert _fwd_ex(L, m=3, y=X + 64) == -8
+    assert _fwd(L, kH=2, y=X + 64) == -5
+
+
+def test_same_pads_and_out_extents():
+    """The host helpers against the oracle's own pad rules (XLA-SAME: the
+    stride-1 SAME result kept at the odd positions)."""
+    import oracle
+    for H, W in ((8, 8), (7, 10), (1, 5), (224, 224)):
+        for k in ((3, 3), (5, 5), (7, 7), (1, 15), (3, 1)):
+            for s in (1, 2):
+                for d in (1, 2):
+                    same = dw.dwconv2d_same_pads(dw.PAD_SAME, H, W, k[0], k[1], s, d)
+                    assert same == oracle.same_pads(H, W, k[0], k[1], s, d)
+                    xla = dw.dwconv2d_same_pads(dw.PAD_XLA_SAME, H, W, k[0], k[1], s, d)
+                    assert xla == oracle.xla_same_pads(H, W, k[0], k[1], s, d)
+                    for pads in (same, xla):
+                        want = oracle.out_extents_padded(H, W, k[0], k[1], s, d, pads)
+                        if min(want) < 1:
+                            with pytest.raises(dw.DwconvError) as e:
+                                dw.dwconv2d_out_extents(H, W, k[0], k[1], s, d, pads)
+                            assert e.value.status == -2
+                        else:
+                            assert dw.dwconv2d_out_extents(H, W, k[0], k[1], s, d, pads) == want
+                    assert dw.dwconv2d_out_extents(H, W, k[0], k[1], s, d, same) == \
+                        (-(-H // s), -(-W // s))
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv2d_same_pads(dw.PAD_SAME, 8, 8, 2, 3)
+    assert e.value.status == -5
+    with pytest.raises(dw.DwconvError) as e:
+        dw.dwconv2d_same_pads(7, 8, 8, 3, 3)
+    assert e.value.status == -14
+
+
+def test_describe_ex_plans():
+    """Same plans as the SAME entry points for SAME pads; tiled kernels at
+    stride 1 with any pads; direct kernels for a multiplier; even kernels
+    run direct."""
+    same = dw.dwconv2d_describe(dw.OP_FWD, 1, 512, 512, 256, 3, 3)
+    assert dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 512, 512, 256, 3, 3, pads=(1, 1, 1, 1)) == same
+    name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 512, 512, 256, 3, 3, pads=(0, 0, 0, 0))
+    assert name.startswith("tiled_nhwc_s1") and grid < same[1]   # 510 x 510 outputs
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 56, 56, 128, 5, 5,
+                                         pads=(0, 4, 3, 1), layout=dw.NCHW)
+    assert name.startswith("tiled_nchw_s1")
+    name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 112, 112, 32, 3, 3, mult=2)
+    assert name.startswith("direct_nhwc_s1_v1") and grid == (112 * 112 * 64 + 255) // 256
+    name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 112, 112, 32, 3, 3, mult=2,
+                                            layout=dw.NCHW)
+    assert name.startswith("direct_nchw_s1") and grid == (112 * 112 * 32 + 255) // 256
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 16, 16, 32, 2, 2, pads=(0, 1, 0, 1))
+    assert name.startswith("direct_nhwc")
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 224, 224, 32, 3, 3, stride=2,
+                                         pads=dw.dwconv2d_same_pads(dw.PAD_XLA_SAME, 224, 224,
+                                                                    3, 3, 2))
+    assert name.startswith("direct_nhwc_s2")
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, 1, 64, 64, 32, 3, 3,
+                                         pads=(0, 2, 2, 0))
+    assert name.startswith("wgrad_tiled_nhwc")
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, 1, 64, 64, 32, 3, 3, mult=2)
+    assert name.startswith("wgrad_direct")
+    a = dw.dwconv2d_weight_grad_workspace_size_ex(2, 9, 9, 5, 3, 3, mult=3, layout=dw.NCHW)
+    assert a % (4 * 15 * 10) == 0 and a > 0
+
+
+def test_tiled_nchw_staging_covers_every_tap():
+    """The NCHW tile stages columns [w0 - hl, w0 - hl + twl) of each row: for
+    any left pad the columns a thread reads, w - left + kw*d for its outputs,
+    must fall inside that window (checked by recomputing the planner's hl,
+    twl rule for every tile width the planner picks)."""
+    for k, d, v4 in (((3, 3), 1, 4), ((5, 5), 1, 4), ((7, 7), 2, 4), ((1, 31), 1, 1),
+                     ((7, 7), 1, 1)):
+        for left in range(-5, 3 * d * (k[1] - 1)):
+            hl = -((-left) & ~3) if v4 == 4 else left
+            assert hl >= left and hl - left < v4
+            for tw in (32, 64, 256, 512):
+                span = (hl - left) + tw + d * (k[1] - 1)
+                twl = (span + v4 - 1) // v4 * v4
+                # first column read (output 0, tap 0) and last (output tw-1, last tap)
+                first = (0 - left) - (0 - hl)
+                last = (tw - 1 - left + d * (k[1] - 1)) - (0 - hl)
+                assert 0 <= first and last < twl
+                extra = (d * (k[1] - 1) + 3 + 3) // 4 * 4 if v4 == 4 else d * (k[1] - 1)
+                assert twl <= tw + extra

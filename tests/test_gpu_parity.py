@@ -39,13 +39,25 @@ def _oracle_case(wl_name, layout, op, integer=False, seed=0):
     import oracle
     wl = WORKLOADS[wl_name]
     inp = wlmod.make_inputs(wl, layout, seed=seed, integer=integer)
+    return (inp,) + _oracle(wl, inp, layout, op)
+
+
+def _oracle(wl, inp, layout, op):
+    """Oracle result and magnitude sums (SAME routines, or the general ones
+    for explicit pads / a channel multiplier)."""
+    import oracle
+    if wl.general:
+        if op == dw.OP_FWD:
+            return oracle.fwd_general(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation,
+                                      wl.pads, wl.mult, layout, nthreads=NTHREADS)
+        return oracle.input_grad_general(inp["dy"], inp["w"], wl.H, wl.W, wl.stride,
+                                         wl.dilation, wl.pads, wl.mult, layout,
+                                         nthreads=NTHREADS)
     if op == dw.OP_FWD:
-        ref, S = oracle.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, layout,
-                            nthreads=NTHREADS)
-    else:
-        ref, S = oracle.input_grad(inp["dy"], inp["w"], wl.H, wl.W, wl.stride, wl.dilation,
-                                   layout, nthreads=NTHREADS)
-    return inp, ref, S
+        return oracle.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, layout,
+                          nthreads=NTHREADS)
+    return oracle.input_grad(inp["dy"], inp["w"], wl.H, wl.W, wl.stride, wl.dilation, layout,
+                             nthreads=NTHREADS)
 
 
 def _run_gpu(torch, wl, inp, layout, op, strategy=dw.STRATEGY_AUTO):
@@ -53,10 +65,12 @@ def _run_gpu(torch, wl, inp, layout, op, strategy=dw.STRATEGY_AUTO):
     if op == dw.OP_FWD:
         x = _dev(torch, inp["x"])
         b = None if inp["b"] is None else _dev(torch, inp["b"])
-        out = dw.fwd(x, w, b, wl.stride, wl.dilation, layout, strategy)
+        out = dw.fwd(x, w, b, wl.stride, wl.dilation, layout, strategy, pads=wl.pads,
+                     mult=wl.mult)
     else:
         dy = _dev(torch, inp["dy"])
-        out = dw.input_grad(dy, w, wl.H, wl.W, wl.stride, wl.dilation, layout, strategy)
+        out = dw.input_grad(dy, w, wl.H, wl.W, wl.stride, wl.dilation, layout, strategy,
+                            pads=wl.pads, mult=wl.mult)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -114,11 +128,15 @@ def test_workload_parity_each_strategy(torch, wl_name, layout, op, strategy):
 
 
 def _describe(wl, layout, op, strategy, wtype=None):
+    wt = wtype if wtype is not None else int(wl.fp16_weights)
     try:
+        if wl.general:
+            return dw.dwconv2d_describe_ex(op, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
+                                           wl.dilation, wl.pads, wl.mult, layout, wt,
+                                           op == dw.OP_FWD and wl.bias, strategy)
         return dw.dwconv2d_describe(op, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
-                                    wl.dilation, layout,
-                                    wtype if wtype is not None else int(wl.fp16_weights),
-                                    op == dw.OP_FWD and wl.bias, strategy)
+                                    wl.dilation, layout, wt, op == dw.OP_FWD and wl.bias,
+                                    strategy)
     except dw.DwconvError as e:
         if e.status == -12:
             return None, None, None
@@ -127,7 +145,9 @@ def _describe(wl, layout, op, strategy, wtype=None):
 
 INT_WL = ["tiny_16x16x8_3x3", "mobilenet_112x112x32_3x3", "mobilenet_s2_224x224x32_3x3",
           "effnet_n1_56x56x128_5x5", "asr_n1_30x19x128_7x7_d2", "asr_n1_1x24x256_1x31",
-          "prime_n1_30x19x131_7x7", "large_512x512x256_3x3"]
+          "prime_n1_30x19x131_7x7", "large_512x512x256_3x3",
+          "mobilenet_s2_xla_224x224x32_3x3", "effnet_n32_56x56x128_5x5_valid",
+          "mobilenet_m2_112x112x32_3x3", "reactant_4x4x4_3x3_m2_valid"]
 INT_CASES = [(n, l, o, s) for n in INT_WL for l in LAYOUTS for o in (dw.OP_FWD, dw.OP_INPUT_GRAD)
              for s in (dw.STRATEGY_AUTO, dw.STRATEGY_DIRECT)]
 
@@ -280,3 +300,68 @@ def test_runs_on_a_side_stream(torch):
         dw.dwconv2d_fwd(x, w, b, y)
     s.synchronize()
     _assert_within_bound(y.cpu().numpy(), ref, S, "side stream")
+
+
+# ----------------------------------------------------------------------------
+# Explicit padding (negative = crop), even kernels, channel multipliers, at
+# random small shapes under every strategy (stride-1 tiled kernels run any
+# pads; multipliers run the direct kernels)
+# ----------------------------------------------------------------------------
+def _random_general_cases(count=36, seed=4321):
+    rng = np.random.default_rng(seed)
+    U = dict(x_dist="uniform1", w_dist="uniform1", dy_dist="uniform1")
+    out = []
+    while len(out) < count:
+        kh, kw = (int(v) for v in rng.choice([1, 2, 3, 4, 5, 7], 2))
+        if len(out) % 3 == 0:       # a kernel shape with tiled variants
+            kh, kw = [(3, 3), (5, 5), (7, 7), (1, 15)][len(out) % 4]
+        s, d = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        if (kh, kw) == (1, 15) or (kh, kw) == (5, 5):
+            d = 1
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        pads = tuple(int(v) for v in rng.integers(-1, 2 * d * max(kh, kw) // 2 + 2, 4))
+        m = int(rng.choice([1, 1, 2, 3]))
+        C = int(rng.choice([4, 8, 12, 16, 20, 36, 3, 7]))
+        wl = wlmod.Workload(f"g{len(out)}", int(rng.integers(1, 3)), H, W, C, kh, kw, stride=s,
+                            dilation=d, pads=pads, mult=m, **U)
+        if wl.Ho < 1 or wl.Wo < 1:
+            continue
+        out.append(wl)
+    return out
+
+
+GENERAL = _random_general_cases()
+
+
+@pytest.mark.parametrize("idx", range(len(GENERAL)),
+                         ids=[f"{p.name}-k{p.kH}x{p.kW}-s{p.stride}-d{p.dilation}-m{p.mult}-"
+                              f"p{'_'.join(map(str, p.pads))}" for p in GENERAL])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_random_padded_and_multiplier_shapes(torch, idx, layout):
+    wl = GENERAL[idx]
+    print(f"\n[case] {wl}", flush=True)
+    inp = wlmod.make_inputs(wl, layout, seed=100 + idx)
+    for op in (dw.OP_FWD, dw.OP_INPUT_GRAD):
+        ref, S = _oracle(wl, inp, layout, op)
+        for strategy in (dw.STRATEGY_AUTO, dw.STRATEGY_DIRECT, dw.STRATEGY_TILED):
+            name, _, _ = _describe(wl, layout, op, strategy)
+            if name is None:
+                continue
+            got = _run_gpu(torch, wl, inp, layout, op, strategy)
+            _assert_within_bound(got, ref, S, f"{wl.name} op={op} {name}")
+
+
+def test_xla_same_matches_odd_positions_of_stride1(torch):
+    """On the GPU too: the XLA-SAME stride-2 forward equals the stride-1 SAME
+    forward kept at the odd positions, bit for bit on integer inputs."""
+    wl = WORKLOADS["mobilenet_s2_xla_224x224x32_3x3"]
+    for layout in LAYOUTS:
+        inp = wlmod.make_inputs(wl, layout, seed=9, integer=True)
+        x, w, b = _dev(torch, inp["x"]), _dev(torch, inp["w"]), _dev(torch, inp["b"])
+        pads = dw.dwconv2d_same_pads(dw.PAD_XLA_SAME, wl.H, wl.W, wl.kH, wl.kW, 2)
+        assert pads == wl.pads
+        y2 = dw.fwd(x, w, b, 2, 1, layout, pads=pads)
+        y1 = dw.fwd(x, w, b, 1, 1, layout)
+        torch.cuda.synchronize()
+        a, c = from_layout(y2.cpu().numpy(), layout), from_layout(y1.cpu().numpy(), layout)
+        np.testing.assert_array_equal(a, c[:, 1::2, 1::2])

@@ -33,8 +33,13 @@ def _dev(t, a):
 
 def _ref(wl, inp, layout):
     import oracle
-    dW, SW = oracle.weight_grad(inp["x"], inp["dy"], wl.kH, wl.kW, wl.stride, wl.dilation,
-                                layout, nthreads=NTHREADS)
+    if wl.general:
+        dW, SW = oracle.weight_grad_general(inp["x"], inp["dy"], wl.kH, wl.kW, wl.stride,
+                                            wl.dilation, wl.pads, wl.mult, layout,
+                                            nthreads=NTHREADS)
+    else:
+        dW, SW = oracle.weight_grad(inp["x"], inp["dy"], wl.kH, wl.kW, wl.stride, wl.dilation,
+                                    layout, nthreads=NTHREADS)
     db, Sb = oracle.bias_grad(inp["dy"], layout)
     return dW, SW, db, Sb
 
@@ -42,9 +47,24 @@ def _ref(wl, inp, layout):
 def _gpu(torch, wl, inp, layout, strategy=dw.STRATEGY_AUTO):
     x, g = _dev(torch, inp["x"]), _dev(torch, inp["dy"])
     dW, db = dw.weight_grad(x, g, wl.kH, wl.kW, wl.stride, wl.dilation, layout,
-                            strategy=strategy)
+                            strategy=strategy, pads=wl.pads, mult=wl.mult)
     torch.cuda.synchronize()
     return dW.cpu().numpy(), db.cpu().numpy()
+
+
+def _has_strategy(wl, layout, strategy):
+    try:
+        if wl.general:
+            dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                    wl.stride, wl.dilation, wl.pads, wl.mult, layout, 0, False,
+                                    strategy)
+        else:
+            dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                 wl.stride, wl.dilation, layout, 0, False, strategy)
+    except dw.DwconvError as e:
+        assert e.status == -12
+        return False
+    return True
 
 
 def _check(got, ref, S, what):
@@ -75,23 +95,18 @@ def test_weight_grad_full_size(torch, wl_name, layout):
 @pytest.mark.parametrize("wl_name", ["tiny_16x16x8_3x3", "mobilenet_112x112x32_3x3",
                                      "mobilenet_s2_224x224x32_3x3", "effnet_n1_56x56x128_5x5",
                                      "asr_n1_30x19x128_7x7_d2", "asr_n1_1x24x256_1x31",
-                                     "prime_n1_30x19x131_7x7"])
+                                     "prime_n1_30x19x131_7x7", "mobilenet_s2_xla_224x224x32_3x3",
+                                     "effnet_n32_56x56x128_5x5_valid",
+                                     "mobilenet_m2_112x112x32_3x3", "reactant_4x4x4_3x3_m2_valid"])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("strategy", [dw.STRATEGY_DIRECT, dw.STRATEGY_TILED])
 def test_weight_grad_integer_bit_exact(torch, wl_name, layout, strategy):
-    import oracle
     wl = WORKLOADS[wl_name]
-    try:
-        dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
-                             wl.dilation, layout, 0, False, strategy)
-    except dw.DwconvError as e:
-        assert e.status == -12
+    if not _has_strategy(wl, layout, strategy):
         pytest.skip("no kernel of this strategy for the problem")
     print(f"\n[case] wgrad int {wl_name} layout={layout} strategy={strategy}", flush=True)
     inp = wlmod.make_inputs(wl, layout, seed=4, integer=True)
-    dW, _ = oracle.weight_grad(inp["x"], inp["dy"], wl.kH, wl.kW, wl.stride, wl.dilation,
-                               layout, nthreads=NTHREADS)
-    db, _ = oracle.bias_grad(inp["dy"], layout)
+    dW, _, db, _ = _ref(wl, inp, layout)
     gW, gb = _gpu(torch, wl, inp, layout, strategy)
     np.testing.assert_array_equal(gW, dW.astype(np.float32))
     np.testing.assert_array_equal(gb, db.astype(np.float32))
@@ -145,3 +160,26 @@ def test_weight_grad_random_shapes(torch, idx, layout):
         gW, gb = _gpu(torch, wl, inp, layout, strategy)
         _check(gW, dW, SW, f"dW {wl}")
         _check(gb, db, Sb, f"db {wl}")
+
+
+def _general_cases():
+    from tests.test_gpu_parity import _random_general_cases
+    return _random_general_cases(count=24, seed=777)
+
+
+GENERAL = _general_cases()
+
+
+@pytest.mark.parametrize("idx", range(len(GENERAL)))
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_weight_grad_padded_and_multiplier_shapes(torch, idx, layout):
+    wl = GENERAL[idx]
+    print(f"\n[case] wgrad {wl}", flush=True)
+    inp = wlmod.make_inputs(wl, layout, seed=200 + idx)
+    dW, SW, db, Sb = _ref(wl, inp, layout)
+    for strategy in (dw.STRATEGY_AUTO, dw.STRATEGY_DIRECT, dw.STRATEGY_TILED):
+        if not _has_strategy(wl, layout, strategy):
+            continue
+        gW, gb = _gpu(torch, wl, inp, layout, strategy)
+        _check(gW, dW, SW, f"dW {wl} strategy={strategy}")
+        _check(gb, db, Sb, f"db {wl} strategy={strategy}")

@@ -358,3 +358,9 @@ def test_workload_table_shapes():
     s2 = W["mobilenet_s2_224x224x32_3x3"]
     assert (s2.Ho, s2.Wo) == (112, 112) and s2.fwd_bytes() == 8_029_440
     assert W["effnet_n1_56x56x128_5x5_f16w"].fwd_bytes() == 3_218_176
+    xla = W["mobilenet_s2_xla_224x224x32_3x3"]
+    assert (xla.Ho, xla.Wo) == (112, 112) and xla.fwd_bytes() == s2.fwd_bytes()
+    m2 = W["mobilenet_m2_112x112x32_3x3"]
+    assert m2.Co == 64 and m2.fwd_bytes() == 4 * 112 * 112 * (32 + 64) + 64 * 9 * 4 + 64 * 4
+    rl = W["reactant_4x4x4_3x3_m2_valid"]
+    assert (rl.Ho, rl.Wo, rl.Co) == (2, 2, 8)
