@@ -65,31 +65,60 @@ def make_problem(torch, wl, layout, seed=0):
     t["y"] = torch.empty(tuple(inp["dy"].shape), dtype=torch.float32, device="cuda")
     t["dx"] = torch.empty(shape_x, dtype=torch.float32, device="cuda")
     import depthwise_convolution_amd as dw
-    nws = dw.dwconv2d_weight_grad_workspace_size(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
-                                                 wl.stride, wl.dilation, layout)
+    if wl.general:
+        nws = dw.dwconv2d_weight_grad_workspace_size_ex(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                                        wl.stride, wl.dilation, wl.pads,
+                                                        wl.mult, layout)
+    else:
+        nws = dw.dwconv2d_weight_grad_workspace_size(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                                     wl.stride, wl.dilation, layout)
     t["ws"] = torch.empty(max(4, (nws + 15) // 16 * 4), dtype=torch.float32, device="cuda")
-    t["dW"] = torch.empty((wl.C, wl.kH, wl.kW), dtype=torch.float32, device="cuda")
-    t["db"] = torch.empty((wl.C,), dtype=torch.float32, device="cuda")
+    t["dW"] = torch.empty((wl.Co, wl.kH, wl.kW), dtype=torch.float32, device="cuda")
+    t["db"] = torch.empty((wl.Co,), dtype=torch.float32, device="cuda")
     return t
 
 
 def launch_fwd(dw, wl, t, layout, stream):
-    dw.dwconv2d_fwd(t["x"], t["w"], t["b"], t["y"], wl.stride, wl.dilation, layout, stream)
+    if wl.general:
+        dw.dwconv2d_launch_ex(dw.OP_FWD, t["x"], t["w"], t["b"], t["y"], wl.H, wl.W, wl.stride,
+                              wl.dilation, wl.pads, wl.mult, layout, dw.STRATEGY_AUTO, stream)
+    else:
+        dw.dwconv2d_fwd(t["x"], t["w"], t["b"], t["y"], wl.stride, wl.dilation, layout, stream)
 
 
 def launch_ig(dw, wl, t, layout, stream):
-    dw.dwconv2d_input_grad(t["dy"], t["w"], t["dx"], wl.stride, wl.dilation, layout, stream)
+    if wl.general:
+        dw.dwconv2d_launch_ex(dw.OP_INPUT_GRAD, t["dy"], t["w"], None, t["dx"], wl.H, wl.W,
+                              wl.stride, wl.dilation, wl.pads, wl.mult, layout,
+                              dw.STRATEGY_AUTO, stream)
+    else:
+        dw.dwconv2d_input_grad(t["dy"], t["w"], t["dx"], wl.stride, wl.dilation, layout, stream)
 
 
 def launch_wgrad(dw, wl, t, layout, stream):
-    dw.dwconv2d_weight_grad(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride, wl.dilation,
-                            layout, dw.STRATEGY_AUTO, stream)
+    if wl.general:
+        dw.dwconv2d_weight_grad_ex(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
+                                   wl.dilation, wl.pads, wl.mult, layout, dw.STRATEGY_AUTO,
+                                   stream)
+    else:
+        dw.dwconv2d_weight_grad(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
+                                wl.dilation, layout, dw.STRATEGY_AUTO, stream)
 
 
 def wgrad_bytes(wl):
     """Algorithmic bytes of the weight + bias gradient: x + dy + dW + db."""
-    return (4 * wl.N * wl.H * wl.W * wl.C + 4 * wl.N * wl.Ho * wl.Wo * wl.C
-            + 4 * wl.C * wl.kH * wl.kW + 4 * wl.C)
+    return wl.wgrad_bytes()
+
+
+def describe(dw, wl, op, layout):
+    """Kernel name of an op of a workload under the AUTO strategy."""
+    wt = 0 if op == dw.OP_WEIGHT_GRAD else int(wl.fp16_weights)
+    if wl.general:
+        return dw.dwconv2d_describe_ex(op, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
+                                       wl.dilation, wl.pads, wl.mult, layout, wt,
+                                       op == dw.OP_FWD)[0]
+    return dw.dwconv2d_describe(op, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
+                                wl.dilation, layout, wt, op == dw.OP_FWD)[0]
 
 
 def time_kernel(torch, fn, stream, iters, flush=None):
@@ -152,10 +181,7 @@ def per_config_table(torch, dw, iters=20):
                     continue              # the weight gradient does not read the weights
                 call = (lambda f=fn: f(dw, wl, t, layout, stream))
                 opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
-                kname = dw.dwconv2d_describe(opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
-                                             wl.stride, wl.dilation, layout,
-                                             0 if op == "wgrad" else int(wl.fp16_weights),
-                                             op == "fwd")[0]
+                kname = describe(dw, wl, opc, layout)
                 time_kernel(torch, call, stream, 3)
                 warm = statistics.median(time_kernel(torch, call, stream, iters))
                 cold = statistics.median(time_kernel(torch, call, stream, max(5, iters // 4),

@@ -302,3 +302,56 @@ def weight_grad_general(x, dy, kH, kW, stride=1, dilation=1, pads=None, mult=1,
     lib.dwo_weight_grad_general(x, dy, dw, _ptr(S), N, H, W, C, mult, kH, kW,
                                 stride, dilation, pads[0], pads[2], Ho, Wo, layout, nthreads)
     return dw, S
+
+
+# ---------------------------------------------------------------------------
+# Epilogue fusions and the SGD step
+# ---------------------------------------------------------------------------
+ACT_NONE, ACT_RELU, ACT_RELU6, ACT_SILU = 0, 1, 2, 3
+
+
+def _chan(v, layout, ndim=4):
+    """Per-channel vector shaped to broadcast over an activation array."""
+    v = np.asarray(v, np.float64)
+    return v.reshape((1, 1, 1, -1)) if layout == NHWC else v.reshape((1, -1, 1, 1))
+
+
+def batchnorm_act(z, bn=None, eps=1e-5, act=ACT_NONE, layout=NHWC):
+    """Inference-form BatchNorm and activation applied to a convolution result
+    z (float64), per output channel.  bn = (gamma, beta, mean, var) or None:
+        t = (z - mean) * gamma / sqrt(var + eps) + beta
+    act: ACT_NONE (t), ACT_RELU max(t, 0), ACT_RELU6 min(max(t, 0), 6),
+    ACT_SILU t * sigmoid(t) = t / (1 + exp(-t)).  The LeanMlir page names
+    the fused depthwise + BatchNorm codegen only; these are the textbook
+    definitions of the layers of the networks it names (MobileNetV2: ReLU6,
+    EfficientNet: SiLU).  Returns (y, inv) with inv = gamma / sqrt(var + eps)
+    per channel (ones without BatchNorm)."""
+    z = np.asarray(z, np.float64)
+    if bn is not None:
+        gamma, beta, mean, var = (np.asarray(v, np.float64) for v in bn)
+        inv = gamma / np.sqrt(var + np.float64(np.float32(eps)))
+        t = (z - _chan(mean, layout)) * _chan(inv, layout) + _chan(beta, layout)
+    else:
+        inv = None
+        t = z
+    if act == ACT_NONE:
+        y = t
+    elif act == ACT_RELU:
+        y = np.maximum(t, 0.0)
+    elif act == ACT_RELU6:
+        y = np.minimum(np.maximum(t, 0.0), 6.0)
+    elif act == ACT_SILU:
+        with np.errstate(over="ignore"):
+            y = t / (1.0 + np.exp(-t))
+    else:
+        raise ValueError(act)
+    return y, inv
+
+
+def sgd_step(w, b, dw, db, lr):
+    """The LeanMlir page's SGD steps for the depthwise weights and bias:
+    W - lr * dW and b - lr * db (float64)."""
+    w_new = np.asarray(w, np.float64) - np.float64(np.float32(lr)) * np.asarray(dw, np.float64)
+    b_new = None if b is None else (np.asarray(b, np.float64)
+                                    - np.float64(np.float32(lr)) * np.asarray(db, np.float64))
+    return w_new, b_new
