@@ -11,7 +11,10 @@ Names mirror the C ABI: ``dwconv2d_fwd``, ``dwconv2d_input_grad``,
 ``dwconv2d_version``, and the general forms with explicit padding and a
 channel multiplier: ``dwconv2d_same_pads``, ``dwconv2d_out_extents``,
 ``dwconv2d_launch_ex``, ``dwconv2d_describe_ex``, ``dwconv2d_weight_grad_ex``,
-``dwconv2d_weight_grad_workspace_size_ex``.  ``fwd``, ``input_grad`` and
+``dwconv2d_weight_grad_workspace_size_ex``; the fused epilogues
+``dwconv2d_fwd_bn_act_ex`` (BatchNorm + activation in the forward's store)
+and ``dwconv2d_weight_grad_sgd_ex`` (SGD step in the weight-gradient
+reduction).  ``fwd``, ``input_grad`` and
 ``weight_grad`` are the same calls with the outputs (and the workspace)
 allocated here; given ``pads`` or ``mult`` they use the general forms.
 
@@ -30,17 +33,19 @@ W_F32, W_F16 = 0, 1
 OP_FWD, OP_INPUT_GRAD, OP_WEIGHT_GRAD = 0, 1, 2
 STRATEGY_AUTO, STRATEGY_DIRECT, STRATEGY_TILED = 0, 1, 2
 PAD_SAME, PAD_XLA_SAME = 0, 1
+ACT_NONE, ACT_RELU, ACT_RELU6, ACT_SILU = 0, 1, 2, 3
 STATUS = {
     0: "OK", -1: "NULL_PTR", -2: "BAD_DIM", -3: "BAD_STRIDE", -4: "BAD_DILATION",
     -5: "EVEN_KERNEL", -6: "BAD_LAYOUT", -7: "BAD_WTYPE", -8: "ALIAS", -9: "MISALIGNED",
     -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY", -13: "WORKSPACE", -14: "BAD_PAD",
+    -15: "BAD_EPILOGUE",
 }
 EXPORTS = ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
            "dwconv2d_weight_grad", "dwconv2d_weight_grad_workspace_size",
            "dwconv2d_strerror", "dwconv2d_version",
            "dwconv2d_same_pads", "dwconv2d_out_extents", "dwconv2d_launch_ex",
            "dwconv2d_describe_ex", "dwconv2d_weight_grad_workspace_size_ex",
-           "dwconv2d_weight_grad_ex")
+           "dwconv2d_weight_grad_ex", "dwconv2d_fwd_bn_act_ex", "dwconv2d_weight_grad_sgd_ex")
 
 _lib = None
 
@@ -77,6 +82,11 @@ def lib():
                                                   ctypes.POINTER(ll), ip]
     L.dwconv2d_weight_grad_workspace_size_ex.argtypes = [i] * 9 + [ip, i, i, ctypes.POINTER(ll)]
     L.dwconv2d_weight_grad_ex.argtypes = [vp, vp, vp, vp, vp, ll] + [i] * 9 + [ip, i, i, vp]
+    f32 = ctypes.c_float
+    L.dwconv2d_fwd_bn_act_ex.argtypes = ([vp, vp, i, vp, vp, vp, vp, vp, f32, i, vp] + [i] * 9 +
+                                         [ip, i, i, vp])
+    L.dwconv2d_weight_grad_sgd_ex.argtypes = ([vp, vp, vp, vp, f32, vp, vp, vp, ll] + [i] * 9 +
+                                              [ip, i, i, vp])
     L.dwconv2d_strerror.argtypes = [i]
     L.dwconv2d_strerror.restype = ctypes.c_char_p
     for f in EXPORTS:
@@ -453,3 +463,104 @@ def dwconv2d_weight_grad_ex(x, dy, dw, db, workspace, stride=1, dilation=1, pads
                                        _pads_arg(pads), lay, strategy, _stream(dw, stream))
     _check_status(st, "dwconv2d_weight_grad_ex")
     return dw, db
+
+
+
+# ------------------------------------------------------------- fused epilogues
+def _act_code(act):
+    names = {"none": ACT_NONE, "relu": ACT_RELU, "relu6": ACT_RELU6, "silu": ACT_SILU}
+    if isinstance(act, str):
+        if act.lower() not in names:
+            raise ValueError(f"unknown activation {act!r}")
+        return names[act.lower()]
+    return int(act)
+
+
+def dwconv2d_fwd_bn_act_ex(x, w, b, y, bn=None, eps=1e-5, act=ACT_NONE, stride=1, dilation=1,
+                           pads=None, mult=1, layout=NHWC, strategy=STRATEGY_AUTO, stream=None):
+    """y = act(BatchNorm(conv(x; w, b))) in one pass; bn = (gamma, beta, mean, var)
+    float32 GPU tensors of mult*C elements, or None."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    lay, wt, N, C, kH, kW = _prepare_ex(OP_FWD, x, w, b, y, H, W, stride, dilation, pads, mult,
+                                        lay)
+    ptrs = [None] * 4
+    if bn is not None:
+        if len(bn) != 4:
+            raise ValueError("bn must be (gamma, beta, mean, var)")
+        for k, t in enumerate(bn):
+            _check_dev(t, ("gamma", "beta", "mean", "var")[k], (torch.float32,))
+            if tuple(t.shape) != (mult * C,):
+                raise ValueError("BatchNorm arrays must be (mult*C,)")
+            ptrs[k] = _ptr(t)
+    st = lib().dwconv2d_fwd_bn_act_ex(_ptr(x), _ptr(w), wt, _ptr(b), *ptrs, float(eps),
+                                      _act_code(act), _ptr(y), N, H, W, C, mult, kH, kW, stride,
+                                      dilation, _pads_arg(pads), lay, strategy, _stream(y, stream))
+    _check_status(st, "dwconv2d_fwd_bn_act_ex")
+    return y
+
+
+def fwd_bn_act(x, w, b=None, bn=None, eps=1e-5, act=ACT_NONE, stride=1, dilation=1,
+               layout=NHWC, strategy=STRATEGY_AUTO, stream=None, pads=None, mult=1):
+    """Allocate y and run the forward with the fused BatchNorm / activation."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    Ho, Wo = dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads)
+    y = torch.empty(_shape(lay, N, Ho, Wo, mult * C), dtype=torch.float32, device=x.device)
+    return dwconv2d_fwd_bn_act_ex(x, w, b, y, bn, eps, act, stride, dilation, pads, mult, lay,
+                                  strategy, stream)
+
+
+def dwconv2d_weight_grad_sgd_ex(x, dy, w, b, lr, workspace, dw=None, db=None, stride=1,
+                                dilation=1, pads=None, mult=1, layout=NHWC,
+                                strategy=STRATEGY_AUTO, stream=None):
+    """In place: w -= lr * dW, b -= lr * db (b may be None); dw, db optionally
+    receive the gradients."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    for name, t in (("x", x), ("dy", dy), ("w", w)):
+        _check_dev(t, name, (torch.float32,))
+    if w.dim() != 3 or int(w.shape[0]) != mult * C:
+        raise ValueError("w must be (mult*C, kH, kW) float32")
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    for name, t, shape in (("b", b, (mult * C,)), ("dw", dw, tuple(w.shape)),
+                           ("db", db, (mult * C,))):
+        if t is not None:
+            _check_dev(t, name, (torch.float32,))
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be {shape}")
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    Ho, Wo = dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads)
+    if tuple(dy.shape) != _shape(lay, N, Ho, Wo, mult * C):
+        raise ValueError(f"dy shape {tuple(dy.shape)} != {_shape(lay, N, Ho, Wo, mult * C)}")
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().dwconv2d_weight_grad_sgd_ex(_ptr(x), _ptr(dy), _ptr(w), _ptr(b), float(lr),
+                                           _ptr(dw), _ptr(db), _ptr(workspace), nbytes, N, H, W,
+                                           C, mult, kH, kW, stride, dilation, _pads_arg(pads), lay,
+                                           strategy, _stream(w, stream))
+    _check_status(st, "dwconv2d_weight_grad_sgd_ex")
+    return w, b
+
+
+def weight_grad_sgd(x, dy, w, b, lr, stride=1, dilation=1, layout=NHWC, strategy=STRATEGY_AUTO,
+                    stream=None, pads=None, mult=1):
+    """Allocate the workspace and apply the fused SGD step to w (and b) in place."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    kH, kW = int(w.shape[1]), int(w.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    nbytes = dwconv2d_weight_grad_workspace_size_ex(N, H, W, C, kH, kW, stride, dilation, pads,
+                                                    mult, lay, strategy)
+    ws = torch.empty(max(1, (nbytes + 15) // 16) * 4, dtype=torch.float32, device=x.device)
+    return dwconv2d_weight_grad_sgd_ex(x, dy, w, b, lr, ws, None, None, stride, dilation, pads,
+                                       mult, lay, strategy, stream)

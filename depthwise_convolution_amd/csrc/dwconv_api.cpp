@@ -9,6 +9,7 @@
 #include "../../include/dwconv.h"
 #include "dwconv_internal.h"
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -56,7 +57,7 @@ int check_pointers(const Problem &p, const float *in, const void *w, const float
 }
 
 int run(Problem p, const float *in, const void *w, const float *b, float *out, int strategy,
-        void *stream)
+        void *stream, const dwconv::Epilogue *epi = nullptr)
 {
     if (p.op != DWCONV_OP_FWD && p.op != DWCONV_OP_INPUT_GRAD)
         return DWCONV_ERR_BAD_OP;
@@ -74,7 +75,7 @@ int run(Problem p, const float *in, const void *w, const float *b, float *out, i
     st = dwconv::make_plan(p, strategy, bits, &pl);
     if (st != DWCONV_OK)
         return st;
-    return dwconv::launch_plan(p, pl, in, w, b, out, stream);
+    return dwconv::launch_plan(p, pl, in, w, b, out, stream, epi);
 }
 
 // Problem with explicit pads (host array top, bottom, left, right) and a
@@ -131,17 +132,20 @@ int wgrad_workspace(Problem p, int strategy, long long *bytes)
 }
 
 int wgrad(Problem p, const float *x, const float *dy, float *dw, float *db, void *workspace,
-          long long workspace_bytes, int strategy, void *stream)
+          long long workspace_bytes, int strategy, void *stream, float *w_upd = nullptr,
+          float *b_upd = nullptr, float lr = 0.0f)
 {
     int st = dwconv::validate_problem(p);
     if (st != DWCONV_OK)
         return st;
-    if (!x || !dy || !dw)
+    if (!x || !dy || (!dw && !w_upd))
         return DWCONV_ERR_NULL_PTR;
     const std::uintptr_t bits = reinterpret_cast<std::uintptr_t>(x) |
                                 reinterpret_cast<std::uintptr_t>(dy) |
                                 reinterpret_cast<std::uintptr_t>(dw) |
-                                reinterpret_cast<std::uintptr_t>(db);
+                                reinterpret_cast<std::uintptr_t>(db) |
+                                reinterpret_cast<std::uintptr_t>(w_upd) |
+                                reinterpret_cast<std::uintptr_t>(b_upd);
     if ((bits & 3u) != 0)
         return DWCONV_ERR_MISALIGNED;
     Plan pl;
@@ -156,18 +160,23 @@ int wgrad(Problem p, const float *x, const float *dy, float *dw, float *db, void
     const long long co = (long long)p.mult * p.C;
     const Range rx = range_of(x, 4LL * p.N * p.H * p.W * p.C);
     const Range rg = range_of(dy, 4LL * p.N * p.Ho * p.Wo * co);
-    const Range rw = range_of(dw, 4LL * co * p.kH * p.kW), rws = range_of(workspace, pl.workspace);
-    const Range outs[3] = {rw, rws, db ? range_of(db, 4LL * co) : Range{0, 0}};
-    for (int i = 0; i < 3; ++i) {
+    const Range none{0, 0};
+    const long long wbytes = 4LL * co * p.kH * p.kW;
+    // everything the call writes: gradients, workspace, updated weights / bias
+    const Range outs[5] = {dw ? range_of(dw, wbytes) : none, range_of(workspace, pl.workspace),
+                           db ? range_of(db, 4LL * co) : none,
+                           w_upd ? range_of(w_upd, wbytes) : none,
+                           (w_upd && b_upd) ? range_of(b_upd, 4LL * co) : none};
+    for (int i = 0; i < 5; ++i) {
         if (outs[i].hi == outs[i].lo)
             continue;
         if (overlap(outs[i], rx) || overlap(outs[i], rg))
             return DWCONV_ERR_ALIAS;
-        for (int j = i + 1; j < 3; ++j)
+        for (int j = i + 1; j < 5; ++j)
             if (outs[j].hi != outs[j].lo && overlap(outs[i], outs[j]))
                 return DWCONV_ERR_ALIAS;
     }
-    return dwconv::launch_wgrad(p, pl, x, dy, dw, db, workspace, stream);
+    return dwconv::launch_wgrad(p, pl, x, dy, dw, db, workspace, stream, w_upd, b_upd, lr);
 }
 
 }  // namespace
@@ -308,6 +317,60 @@ int dwconv2d_weight_grad_workspace_size_ex(int N, int H, int W, int C, int mult,
     return wgrad_workspace(p, strategy, bytes);
 }
 
+int dwconv2d_fwd_bn_act_ex(const float *x, const void *w, int wtype, const float *b,
+                           const float *gamma, const float *beta, const float *mean,
+                           const float *var, float eps, int act, float *y,
+                           int N, int H, int W, int C, int mult, int kH, int kW, int stride,
+                           int dilation, const int *pads, int layout, int strategy, void *stream)
+{
+    Problem p;
+    int st = general_problem(DWCONV_OP_FWD, wtype, b != nullptr, N, H, W, C, mult, kH, kW, stride,
+                             dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    p.epi = 1;
+    if (act < DWCONV_ACT_NONE || act > DWCONV_ACT_SILU)
+        return DWCONV_ERR_BAD_EPILOGUE;
+    const int nbn = (gamma != nullptr) + (beta != nullptr) + (mean != nullptr) + (var != nullptr);
+    if (nbn != 0 && nbn != 4)
+        return DWCONV_ERR_BAD_EPILOGUE;
+    if (nbn == 4 && !(std::isfinite(eps) && eps >= 0.0f))
+        return DWCONV_ERR_BAD_EPILOGUE;
+    const float *bn[4] = {gamma, beta, mean, var};
+    if (nbn == 4) {
+        st = dwconv::validate_problem(p);   // Ho, Wo for the overlap checks
+        if (st != DWCONV_OK)
+            return st;
+        const Range ry = range_of(y, 4LL * p.N * p.Ho * p.Wo * p.mult * p.C);
+        for (int i = 0; i < 4; ++i) {
+            if (reinterpret_cast<std::uintptr_t>(bn[i]) & 3u)
+                return DWCONV_ERR_MISALIGNED;
+            if (y && overlap(ry, range_of(bn[i], 4LL * p.mult * p.C)))
+                return DWCONV_ERR_ALIAS;
+        }
+    }
+    const dwconv::Epilogue epi{gamma, beta, mean, var, eps, act};
+    return run(p, x, w, b, y, strategy, stream, &epi);
+}
+
+int dwconv2d_weight_grad_sgd_ex(const float *x, const float *dy, float *w, float *b, float lr,
+                                float *dw, float *db, void *workspace, long long workspace_bytes,
+                                int N, int H, int W, int C, int mult, int kH, int kW, int stride,
+                                int dilation, const int *pads, int layout, int strategy,
+                                void *stream)
+{
+    Problem p;
+    const int st = general_problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, mult, kH,
+                                   kW, stride, dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    if (!w)
+        return DWCONV_ERR_NULL_PTR;
+    if (!std::isfinite(lr))
+        return DWCONV_ERR_BAD_EPILOGUE;
+    return wgrad(p, x, dy, dw, db, workspace, workspace_bytes, strategy, stream, w, b, lr);
+}
+
 int dwconv2d_weight_grad_ex(const float *x, const float *dy, float *dw, float *db,
                             void *workspace, long long workspace_bytes,
                             int N, int H, int W, int C, int mult, int kH, int kW,
@@ -340,6 +403,8 @@ const char *dwconv2d_strerror(int status)
     case DWCONV_ERR_BAD_STRATEGY: return "unknown strategy, or it does not apply to this problem";
     case DWCONV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case DWCONV_ERR_BAD_PAD: return "pad out of range (|pad| >= 65536) or unknown padding mode";
+    case DWCONV_ERR_BAD_EPILOGUE:
+        return "bad epilogue: unknown activation, partial BatchNorm, bad eps or learning rate";
     default: return "unknown status";
     }
 }

@@ -24,8 +24,20 @@ struct Problem {
     int mult;             // channel multiplier (output channels per input channel)
     int pt, pb, pl, pr;   // zero padding: top, bottom, left, right
     int same;             // 1: symmetric SAME entry point (odd kernels required)
+    int epi;              // 1: forward with the BatchNorm / activation epilogue
     int Ho, Wo;           // output extents, set by validate_problem
 };
+
+// Forward epilogue: inference-form BatchNorm (gamma, beta, mean, var of the
+// output channels; all NULL for none) and an activation DWCONV_ACT_*.
+struct Epilogue {
+    const float *gamma, *beta, *mean, *var;
+    float eps;
+    int act;
+};
+
+// Compile-time modes of the tiled kernels.
+constexpr int kModeFwd = 0, kModeInputGrad = 1, kModeFwdEpilogue = 2;
 
 // Problem with symmetric SAME padding and no channel multiplier.
 Problem same_problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int kH,
@@ -132,12 +144,18 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
 int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *out);
 
 // Enqueue the two kernels of a weight-gradient plan.
+// Weight and bias gradients of a plan made by make_wgrad_plan.  dw and db
+// (either may be NULL) receive the gradients; when w_upd is not NULL the
+// fused SGD step w_upd -= lr * dW (and b_upd -= lr * db when b_upd is not
+// NULL) is applied in the same reduction.
 int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *dy, float *dw,
-                 float *db, void *workspace, void *stream);
+                 float *db, void *workspace, void *stream, float *w_upd = nullptr,
+                 float *b_upd = nullptr, float lr = 0.0f);
 
-// Enqueue the kernel of a plan made by make_plan on `stream` (a hipStream_t).
+// Enqueue the kernel of a plan made by make_plan on `stream` (a hipStream_t);
+// `epi` (forward only, may be NULL) is the fused epilogue.
 // Returns DWCONV_OK, or DWCONV_ERR_LAUNCH if the runtime reports an error.
 int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w,
-                const float *b, float *out, void *stream);
+                const float *b, float *out, void *stream, const Epilogue *epi = nullptr);
 
 }  // namespace dwconv

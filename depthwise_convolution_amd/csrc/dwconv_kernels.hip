@@ -142,6 +142,58 @@ __device__ __forceinline__ float buf_w(__amdgpu_buffer_rsrc_t r, int idx, half_t
     return (float)__builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, 0));
 }
 
+// ---------------------------------------------------------------------------
+// Forward epilogue: inference-form BatchNorm and an activation, applied per
+// output channel before the store (the LeanMlir page's fused depthwise +
+// BatchNorm codegen; textbook layer definitions):
+//   t = (z - mean) * gamma / sqrt(var + eps) + beta,   y = act(t)
+// with z the convolution result (bias included).  Without BatchNorm
+// (gamma == NULL) the affine step is the identity.
+// ---------------------------------------------------------------------------
+struct EpiArgs {
+    const float *gamma, *beta, *mean, *var;   // all NULL: no BatchNorm
+    float eps;
+    int act;                                  // DWCONV_ACT_*
+    int on;                                   // direct kernels: apply the epilogue
+};
+
+// Per-channel affine factors: y_pre = fmaf(z - mu, inv, be).
+struct EpiChan {
+    float mu, inv, be;
+};
+
+__device__ __forceinline__ float apply_act(float t, int act)
+{
+    if (act == DWCONV_ACT_RELU)
+        return fmaxf(t, 0.0f);
+    if (act == DWCONV_ACT_RELU6)
+        return fminf(fmaxf(t, 0.0f), 6.0f);
+    if (act == DWCONV_ACT_SILU)
+        return t / (1.0f + expf(-t));
+    return t;
+}
+
+__device__ __forceinline__ float apply_epi(float z, EpiChan e, int act)
+{
+    return apply_act(fmaf(z - e.mu, e.inv, e.be), act);
+}
+
+// Factors of channel c (c < channels) read through buffer descriptors.
+__device__ __forceinline__ EpiChan epi_chan(const EpiArgs &ep, int c, int channels)
+{
+    EpiChan e{0.0f, 1.0f, 0.0f};
+    if (ep.gamma) {
+        const int bytes = channels * 4;
+        const int off = c < channels ? c * 4 : kOutOfRange;
+        const float g = buf_f32(make_rsrc(ep.gamma, bytes), off);
+        const float v = buf_f32(make_rsrc(ep.var, bytes), off);
+        e.mu = buf_f32(make_rsrc(ep.mean, bytes), off);
+        e.be = buf_f32(make_rsrc(ep.beta, bytes), off);
+        e.inv = g / sqrtf(v + ep.eps);
+    }
+    return e;
+}
+
 struct DirectArgs {
     int N, CI, CO, mult;  // channels of the tensor read / written; channel multiplier
     int kH, kW, d, pH, pW;
@@ -164,7 +216,8 @@ template <typename WT, int V, bool IG, int S>
 __global__ __launch_bounds__(256) void k_direct_nhwc(const float *__restrict__ in,
                                                      const WT *__restrict__ w,
                                                      const float *__restrict__ bias,
-                                                     float *__restrict__ out, DirectArgs a)
+                                                     float *__restrict__ out, DirectArgs a,
+                                                     EpiArgs ep)
 {
     const unsigned gt = blockIdx.x * 256u + threadIdx.x;
     if (gt >= (unsigned)a.total)
@@ -226,6 +279,11 @@ __global__ __launch_bounds__(256) void k_direct_nhwc(const float *__restrict__ i
             }
         }
     }
+    if (!IG && ep.on) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            acc[v] = apply_epi(acc[v], epi_chan(ep, r0 + v, a.CO), ep.act);
+    }
     store_vec<V>(out + ((n * a.OH + oh) * a.OW + ow) * a.CO + r0, acc);
 }
 
@@ -234,7 +292,8 @@ template <typename WT, bool IG, int S>
 __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ in,
                                                      const WT *__restrict__ w,
                                                      const float *__restrict__ bias,
-                                                     float *__restrict__ out, DirectArgs a)
+                                                     float *__restrict__ out, DirectArgs a,
+                                                     EpiArgs ep)
 {
     const unsigned gt = blockIdx.x * 256u + threadIdx.x;
     if (gt >= (unsigned)a.total)
@@ -286,6 +345,8 @@ __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ i
             }
         }
     }
+    if (!IG && ep.on)
+        acc = apply_epi(acc, epi_chan(ep, r, a.CO), ep.act);
     __builtin_nontemporal_store(acc, out + ((n * a.CO + r) * a.OH + oh) * a.OW + ow);
 }
 
@@ -327,12 +388,14 @@ struct TiledGeom {
     static_assert(256 % CL == 0 && CG % 4 == 0, "bad channel tiling");
 };
 
-template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, bool IG>
+template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, int MODE>
 __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__ in,
                                                        const void *__restrict__ wv,
                                                        const float *__restrict__ bias,
-                                                       float *__restrict__ out, TiledArgs a)
+                                                       float *__restrict__ out, TiledArgs a,
+                                                       EpiArgs ep)
 {
+    constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
     typedef TiledGeom<KH, KW, D, VEC, CL, PX, G> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
     constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV, KK = Gm::KK;
@@ -416,6 +479,12 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
                 const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
                 wr[kh][kw][v] = ldsw[(q * VEC + v) * KK + tap];
             }
+    EpiChan ec[VEC];
+    if constexpr (EPI) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            ec[v] = epi_chan(ep, cq + v, a.C);
+    }
     float acc[R][PX][VEC];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -458,6 +527,11 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
             if (m >= 0) {
 #pragma unroll
                 for (int j = 0; j < PX; ++j) {
+                    if constexpr (EPI) {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v)
+                            acc[m % R][j][v] = apply_epi(acc[m % R][j][v], ec[v], ep.act);
+                    }
                     if (cvalid && ow + j < a.OW)
                         store_vec<VEC>(outp + ((h0 + m) * a.OW + ow + j) * a.C + cq,
                                        acc[m % R][j]);
@@ -509,12 +583,14 @@ struct NchwGeom {
     static_assert(TH >= 1, "a workgroup must produce at least one output row");
 };
 
-template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, bool IG>
+template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, int MODE>
 __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__ in,
                                                        const void *__restrict__ wv,
                                                        const float *__restrict__ bias,
-                                                       float *__restrict__ out, TiledNchwArgs a)
+                                                       float *__restrict__ out, TiledNchwArgs a,
+                                                       EpiArgs ep)
 {
+    constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
     typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV;
     constexpr int NV = Gm::NV, NW = Gm::NW;
@@ -602,6 +678,9 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
             const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
             wr[kh][kw] = ldsw[pli * KK + tap];
         }
+    EpiChan ec{0.0f, 1.0f, 0.0f};
+    if constexpr (EPI)
+        ec = epi_chan(ep, pvalid ? my_plane % a.C : a.C, a.C);
     float acc[R][Q];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -634,6 +713,11 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
             }
             const int m = u - (R - 1);
             if (m >= 0) {
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int j = 0; j < Q; ++j)
+                        acc[m % R][j] = apply_epi(acc[m % R][j], ec, ep.act);
+                }
                 float *dst = outp + (h0 + m) * a.OW + oc;
                 if (pvalid) {
                     if (vec_store && oc < a.OW) {
@@ -871,10 +955,13 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
 
 // Stage 2: 16 columns of part[] per workgroup, 16 threads per column each
 // summing every 16th chunk, then a fixed 16-way tree.
+// With w_upd, the LeanMlir page's SGD step is fused in: w_upd -= lr * dW and,
+// with b_upd, b_upd -= lr * db (one rounding each: fmaf(-lr, grad, old)).
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ part,
                                                       float *__restrict__ dw,
                                                       float *__restrict__ db, int chunks,
-                                                      int C, int KK)
+                                                      int C, int KK, float *__restrict__ w_upd,
+                                                      float *__restrict__ b_upd, float lr)
 {
     __shared__ float red[16][17];
     const int cols = C * (KK + 1);
@@ -894,10 +981,18 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ 
     }
     if (j == 0 && col < cols) {
         const int c = col / (KK + 1), tap = col - c * (KK + 1);
-        if (tap < KK)
-            dw[c * KK + tap] = red[0][lane];
-        else if (db)
-            db[c] = red[0][lane];
+        const float g = red[0][lane];
+        if (tap < KK) {
+            if (dw)
+                dw[c * KK + tap] = g;
+            if (w_upd)
+                w_upd[c * KK + tap] = fmaf(-lr, g, w_upd[c * KK + tap]);
+        } else {
+            if (db)
+                db[c] = g;
+            if (b_upd)
+                b_upd[c] = fmaf(-lr, g, b_upd[c]);
+        }
     }
 }
 
@@ -919,7 +1014,7 @@ DirectArgs direct_args(const Problem &p, const Plan &pl)
 
 template <typename WT>
 void launch_direct(const Problem &p, const Plan &pl, const float *in, const void *wv,
-                   const float *b, float *out, hipStream_t st)
+                   const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     const DirectArgs a = direct_args(p, pl);
     const WT *w = reinterpret_cast<const WT *>(wv);
@@ -927,9 +1022,9 @@ void launch_direct(const Problem &p, const Plan &pl, const float *in, const void
     const bool ig = p.op == DWCONV_OP_INPUT_GRAD;
     const int s = p.stride;
 #define DW_DIRECT_NHWC(V, IGV, SV) \
-    hipLaunchKernelGGL((k_direct_nhwc<WT, V, IGV, SV>), grid, block, 0, st, in, w, b, out, a)
+    hipLaunchKernelGGL((k_direct_nhwc<WT, V, IGV, SV>), grid, block, 0, st, in, w, b, out, a, ep)
 #define DW_DIRECT_NCHW(IGV, SV) \
-    hipLaunchKernelGGL((k_direct_nchw<WT, IGV, SV>), grid, block, 0, st, in, w, b, out, a)
+    hipLaunchKernelGGL((k_direct_nchw<WT, IGV, SV>), grid, block, 0, st, in, w, b, out, a, ep)
     if (pl.kind == KIND_DIRECT_NHWC) {
         if (pl.vec == 4) {
             if (!ig) { if (s == 1) DW_DIRECT_NHWC(4, false, 1); else DW_DIRECT_NHWC(4, false, 2); }
@@ -946,80 +1041,93 @@ void launch_direct(const Problem &p, const Plan &pl, const float *in, const void
 #undef DW_DIRECT_NCHW
 }
 
-typedef void (*TiledFn)(const float *, const void *, const float *, float *, TiledArgs);
+typedef void (*TiledFn)(const float *, const void *, const float *, float *, TiledArgs,
+                        EpiArgs);
 
-// Kernel table of the tiled NHWC kernel: [variant][f16 weights][input grad].
-template <typename WT, int V, bool IG>
+// Kernel table of the tiled NHWC kernel: [variant][f16 weights][mode].
+template <typename WT, int V, int MODE>
 constexpr TiledFn tiled_fn()
 {
     constexpr TiledVariant t = kTiledVariants[V];
-    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, IG>;
+    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, MODE>;
 }
 
 template <int V>
-void fill_tiled(TiledFn (&row)[2][2])
+void fill_tiled(TiledFn (&row)[2][3])
 {
-    row[0][0] = tiled_fn<float, V, false>();
-    row[0][1] = tiled_fn<float, V, true>();
-    row[1][0] = tiled_fn<half_t, V, false>();
-    row[1][1] = tiled_fn<half_t, V, true>();
+    row[0][0] = tiled_fn<float, V, kModeFwd>();
+    row[0][1] = tiled_fn<float, V, kModeInputGrad>();
+    row[0][2] = tiled_fn<float, V, kModeFwdEpilogue>();
+    row[1][0] = tiled_fn<half_t, V, kModeFwd>();
+    row[1][1] = tiled_fn<half_t, V, kModeInputGrad>();
+    row[1][2] = tiled_fn<half_t, V, kModeFwdEpilogue>();
 }
 
 template <int... Vs>
-void fill_all_tiled(TiledFn (&fn)[kNumTiledVariants][2][2], std::integer_sequence<int, Vs...>)
+void fill_all_tiled(TiledFn (&fn)[kNumTiledVariants][2][3], std::integer_sequence<int, Vs...>)
 {
     (fill_tiled<Vs>(fn[Vs]), ...);
 }
 
 struct TiledTable {
-    TiledFn fn[kNumTiledVariants][2][2];
+    TiledFn fn[kNumTiledVariants][2][3];
     TiledTable() { fill_all_tiled(fn, std::make_integer_sequence<int, kNumTiledVariants>()); }
 };
 
+int mode_of(const Problem &p, const EpiArgs &ep)
+{
+    if (p.op == DWCONV_OP_INPUT_GRAD)
+        return kModeInputGrad;
+    return ep.on ? kModeFwdEpilogue : kModeFwd;
+}
+
 int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const void *w,
-                      const float *b, float *out, hipStream_t st)
+                      const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     static const TiledTable table;
     if (pl.variant < 0 || pl.variant >= kNumTiledVariants)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][p.op == DWCONV_OP_INPUT_GRAD];
+    TiledFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
     TiledArgs a;
     a.N = p.N; a.C = p.C;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
     a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
-                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a);
+                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
     return DWCONV_OK;
 }
 
-typedef void (*TiledNchwFn)(const float *, const void *, const float *, float *, TiledNchwArgs);
+typedef void (*TiledNchwFn)(const float *, const void *, const float *, float *, TiledNchwArgs,
+                            EpiArgs);
 
-template <typename WT, int V, bool IG>
+template <typename WT, int V, int MODE>
 constexpr TiledNchwFn tiled_nchw_fn()
 {
     constexpr TiledNchwVariant t = kTiledNchwVariants[V];
-    return &k_tiled_nchw_s1<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), IG>;
+    return &k_tiled_nchw_s1<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), MODE>;
 }
 
 template <int V>
-void fill_tiled_nchw(TiledNchwFn (&row)[2][2])
+void fill_tiled_nchw(TiledNchwFn (&row)[2][3])
 {
-    row[0][0] = tiled_nchw_fn<float, V, false>();
-    row[0][1] = tiled_nchw_fn<float, V, true>();
-    row[1][0] = tiled_nchw_fn<half_t, V, false>();
-    row[1][1] = tiled_nchw_fn<half_t, V, true>();
+    row[0][0] = tiled_nchw_fn<float, V, kModeFwd>();
+    row[0][1] = tiled_nchw_fn<float, V, kModeInputGrad>();
+    row[0][2] = tiled_nchw_fn<float, V, kModeFwdEpilogue>();
+    row[1][0] = tiled_nchw_fn<half_t, V, kModeFwd>();
+    row[1][1] = tiled_nchw_fn<half_t, V, kModeInputGrad>();
+    row[1][2] = tiled_nchw_fn<half_t, V, kModeFwdEpilogue>();
 }
 
 template <int... Vs>
-void fill_all_tiled_nchw(TiledNchwFn (&fn)[kNumTiledNchwVariants][2][2],
+void fill_all_tiled_nchw(TiledNchwFn (&fn)[kNumTiledNchwVariants][2][3],
                          std::integer_sequence<int, Vs...>)
 {
     (fill_tiled_nchw<Vs>(fn[Vs]), ...);
 }
 
 struct TiledNchwTable {
-    TiledNchwFn fn[kNumTiledNchwVariants][2][2];
+    TiledNchwFn fn[kNumTiledNchwVariants][2][3];
     TiledNchwTable()
     {
         fill_all_tiled_nchw(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
@@ -1027,13 +1135,13 @@ struct TiledNchwTable {
 };
 
 int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
-                      const float *b, float *out, hipStream_t st)
+                      const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     static const TiledNchwTable table;
     if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
         (pl.cl & (pl.cl - 1)) != 0)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][p.op == DWCONV_OP_INPUT_GRAD];
+    TiledNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
     TiledNchwArgs a;
     a.planes = p.N * p.C; a.C = p.C;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
@@ -1043,7 +1151,7 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
         ++a.tx_log2;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
-                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a);
+                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
     return DWCONV_OK;
 }
 
@@ -1071,24 +1179,31 @@ struct WgradTable {
 
 // Run a validated plan on `stream`.  Returns a DWCONV_ status.
 int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w,
-                const float *b, float *out, void *stream_v)
+                const float *b, float *out, void *stream_v, const Epilogue *epi)
 {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     const float *bb = p.op == DWCONV_OP_FWD ? b : nullptr;
+    EpiArgs ep{nullptr, nullptr, nullptr, nullptr, 0.0f, DWCONV_ACT_NONE, 0};
+    if (epi && p.op == DWCONV_OP_FWD) {
+        ep.gamma = epi->gamma; ep.beta = epi->beta; ep.mean = epi->mean; ep.var = epi->var;
+        ep.eps = epi->eps;
+        ep.act = epi->act;
+        ep.on = 1;
+    }
     int st = DWCONV_OK;
     switch (pl.kind) {
     case KIND_DIRECT_NHWC:
     case KIND_DIRECT_NCHW:
         if (p.wtype == DWCONV_W_F16)
-            launch_direct<half_t>(p, pl, in, w, bb, out, stream);
+            launch_direct<half_t>(p, pl, in, w, bb, out, stream, ep);
         else
-            launch_direct<float>(p, pl, in, w, bb, out, stream);
+            launch_direct<float>(p, pl, in, w, bb, out, stream, ep);
         break;
     case KIND_TILED_NHWC:
-        st = launch_tiled_nhwc(p, pl, in, w, bb, out, stream);
+        st = launch_tiled_nhwc(p, pl, in, w, bb, out, stream, ep);
         break;
     case KIND_TILED_NCHW:
-        st = launch_tiled_nchw(p, pl, in, w, bb, out, stream);
+        st = launch_tiled_nchw(p, pl, in, w, bb, out, stream, ep);
         break;
     default:
         return DWCONV_ERR_BAD_STRATEGY;
@@ -1099,7 +1214,8 @@ int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w
 }
 
 int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *dy, float *dw,
-                 float *db, void *workspace, void *stream_v)
+                 float *db, void *workspace, void *stream_v, float *w_upd, float *b_upd,
+                 float lr)
 {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream_v);
     float *part = reinterpret_cast<float *>(workspace);
@@ -1129,7 +1245,8 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         return DWCONV_ERR_BAD_STRATEGY;
     }
     hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw, db,
-                       (int)pl.chunks, p.mult * p.C, p.kH * p.kW);
+                       (int)pl.chunks, p.mult * p.C, p.kH * p.kW, w_upd,
+                       w_upd ? b_upd : nullptr, lr);
     return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
 }
 

@@ -27,6 +27,13 @@ constexpr int kMaxPad = 1 << 16;                   // |pad| bound
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+const char *op_tag(const dwconv::Problem &p)
+{
+    if (p.op == DWCONV_OP_INPUT_GRAD)
+        return "ig";
+    return p.epi ? "fwd_epi" : "fwd";
+}
+
 }  // namespace
 
 Problem same_problem(int op, int wtype, int has_bias, int N, int H, int W, int C, int kH,
@@ -146,7 +153,7 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->grid = (long long)p.N * pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_%s_%s",
-                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, p.op ? "ig" : "fwd",
+                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, op_tag(p),
                   p.wtype ? "f16w" : "f32w");
     return true;
 }
@@ -196,7 +203,7 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s1_k%dx%d_d%d_q%d_g%d_%s_tx%d_%s_%s",
-                  v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, p.op ? "ig" : "fwd",
+                  v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, op_tag(p),
                   p.wtype ? "f16w" : "f32w");
     return true;
 }
@@ -219,7 +226,7 @@ static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->grid = (pl->total + pl->block - 1) / pl->block;
     std::snprintf(pl->name, sizeof pl->name, "direct_%s_s%d_v%d_%s_%s",
                   p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride, pl->vec,
-                  p.op ? "ig" : "fwd", p.wtype ? "f16w" : "f32w");
+                  op_tag(p), p.wtype ? "f16w" : "f32w");
 }
 
 int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)

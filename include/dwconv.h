@@ -62,6 +62,9 @@ extern "C" {
 #define DWCONV_ERR_BAD_STRATEGY -12 /* strategy unknown, or not applicable to the problem */
 #define DWCONV_ERR_WORKSPACE   -13  /* workspace NULL, misaligned or smaller than required */
 #define DWCONV_ERR_BAD_PAD     -14  /* a pad with |pad| >= 2^16, or an unknown padding mode */
+#define DWCONV_ERR_BAD_EPILOGUE -15 /* unknown activation, BatchNorm pointers not all given
+                                       or all NULL, eps negative or not finite, or a
+                                       learning rate that is not finite               */
 
 /* ---- enumerations (passed as int) -------------------------------------- */
 #define DWCONV_LAYOUT_NHWC 0   /* channel innermost (the ggml page's CWHN)    */
@@ -78,6 +81,12 @@ extern "C" {
 #define DWCONV_PAD_SAME     0  /* symmetric: d*(k-1)/2 on every side (odd kernels)   */
 #define DWCONV_PAD_XLA_SAME 1  /* LeanMlir "Depthwise" stride-2 XLA-SAME: the stride-1
                                   SAME result kept at the ODD positions               */
+
+/* Activations of the fused forward epilogue. */
+#define DWCONV_ACT_NONE  0     /* y = t                                       */
+#define DWCONV_ACT_RELU  1     /* y = max(t, 0)                               */
+#define DWCONV_ACT_RELU6 2     /* y = min(max(t, 0), 6)   (MobileNetV2)       */
+#define DWCONV_ACT_SILU  3     /* y = t / (1 + exp(-t))   (EfficientNet)      */
 
 /* Which tiling to run a problem under (cubek-convolution "depthwise" module:
  * a strategy enum selects the tiling, one launch function runs it). */
@@ -232,6 +241,47 @@ int dwconv2d_weight_grad_ex(const float *x, const float *dy, float *dw, float *d
                             int N, int H, int W, int C, int mult, int kH, int kW,
                             int stride, int dilation, const int *pads, int layout, int strategy,
                             void *stream);
+
+/* ---- fused epilogues ----------------------------------------------------
+ *
+ * Forward with inference-form BatchNorm and an activation fused into the
+ * store (the LeanMlir page's fused depthwise + BatchNorm codegen; the
+ * activations of the networks it names), per output channel o:
+ *
+ *   z = conv(x; W, b)  (as dwconv2d_launch_ex),
+ *   t = (z - mean[o]) * gamma[o] / sqrt(var[o] + eps) + beta[o],   y = act(t)
+ *
+ * gamma, beta, mean, var: [mult*C] float32 device arrays, all four given or
+ * all NULL (then t = z); eps >= 0; act: DWCONV_ACT_*.  One pass: y is
+ * written once, already normalised and activated.  Errors as for
+ * dwconv2d_launch_ex, plus DWCONV_ERR_BAD_EPILOGUE (unknown act, some but
+ * not all BatchNorm arrays, eps negative or not finite) and
+ * DWCONV_ERR_ALIAS when y overlaps a BatchNorm array.
+ */
+int dwconv2d_fwd_bn_act_ex(const float *x, const void *w, int wtype, const float *b,
+                           const float *gamma, const float *beta, const float *mean,
+                           const float *var, float eps, int act, float *y,
+                           int N, int H, int W, int C, int mult, int kH, int kW, int stride,
+                           int dilation, const int *pads, int layout, int strategy, void *stream);
+
+/*
+ * Weight and bias gradients with the SGD step fused into their reduction
+ * (LeanMlir "Depthwise": the weight and bias SGD steps W - lr*dW and
+ * b - lr*db, at stride 1, stride 2 and XLA-SAME alike):
+ *
+ *   w[o,kh,kw] <- w[o,kh,kw] - lr * dW[o,kh,kw],   b[o] <- b[o] - lr * db[o]
+ *
+ * each rounded once (fused multiply-add).  w: [mult*C][kH][kW] float32,
+ * updated in place; b: [mult*C] float32 updated in place, or NULL; dw, db:
+ * optional outputs of the gradients themselves (NULL to skip).  lr must be
+ * finite.  Workspace and other arguments as for dwconv2d_weight_grad_ex;
+ * every array written must not overlap x, dy or another array written.
+ */
+int dwconv2d_weight_grad_sgd_ex(const float *x, const float *dy, float *w, float *b, float lr,
+                                float *dw, float *db, void *workspace, long long workspace_bytes,
+                                int N, int H, int W, int C, int mult, int kH, int kW, int stride,
+                                int dilation, const int *pads, int layout, int strategy,
+                                void *stream);
 
 /* Static text for a status code ("unknown status" for unknown codes). */
 const char *dwconv2d_strerror(int status);

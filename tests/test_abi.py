@@ -344,3 +344,47 @@ def test_tiled_nchw_staging_covers_every_tap():
                 assert 0 <= first and last < twl
                 extra = (d * (k[1] - 1) + 3 + 3) // 4 * 4 if v4 == 4 else d * (k[1] - 1)
                 assert twl <= tw + extra
+
+
+# ------------------------------------------------------------- fused epilogues
+G_, BE, MU, VA = 0x60_0000_0000, 0x61_0000_0000, 0x62_0000_0000, 0x63_0000_0000
+
+
+def _bn_act(L, x=X, w=WP, b=B, g=G_, be=BE, mu=MU, va=VA, eps=1e-5, act=2, y=Y, C=4, m=1,
+            pads=(1, 1, 1, 1)):
+    vp = lambda a: VP(a) if a else None
+    return L.dwconv2d_fwd_bn_act_ex(vp(x), vp(w), 0, vp(b), vp(g), vp(be), vp(mu), vp(va), eps,
+                                    act, vp(y), 1, 8, 8, C, m, 3, 3, 1, 1, _pads(*pads), 0, 0,
+                                    None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(act=4), -15), (dict(act=-1), -15), (dict(g=0), -15), (dict(va=0, mu=0), -15),
+    (dict(eps=-1.0), -15), (dict(eps=float("inf")), -15), (dict(eps=float("nan")), -15),
+    (dict(g=G_ + 2), -9), (dict(y=MU + 4), -8), (dict(y=X + 64), -8), (dict(x=0), -1),
+    (dict(pads=(-8, 0, 0, 0)), -2),
+])
+def test_fwd_bn_act_rejects(L, kwargs, code):
+    assert _bn_act(L, **kwargs) == code
+
+
+def test_fwd_bn_act_without_batchnorm_validates_like_forward(L):
+    # no BatchNorm arrays: eps is not looked at; the call stops at the overlap check
+    assert _bn_act(L, g=0, be=0, mu=0, va=0, eps=float("nan"), y=X + 64) == -8
+    assert _bn_act(L, act=0, y=X + 64) == -8
+
+
+def _sgd(L, x=X, dy=B, w=Y, b=WP, lr=0.1, dw=0, db=0, ws=WS, ws_bytes=1 << 30, C=4, m=1):
+    vp = lambda a: VP(a) if a else None
+    return L.dwconv2d_weight_grad_sgd_ex(vp(x), vp(dy), vp(w), vp(b), lr, vp(dw), vp(db), vp(ws),
+                                         ws_bytes, 1, 8, 8, C, m, 3, 3, 1, 1, _pads(1, 1, 1, 1),
+                                         0, 0, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(w=0), -1), (dict(x=0), -1), (dict(lr=float("nan")), -15), (dict(lr=float("inf")), -15),
+    (dict(w=Y + 2), -9), (dict(ws=0), -13), (dict(ws_bytes=16), -13),
+    (dict(w=X + 16), -8), (dict(b=B + 8), -8), (dict(dw=Y + 4), -8), (dict(db=WS + 32), -8),
+])
+def test_weight_grad_sgd_rejects(L, kwargs, code):
+    assert _sgd(L, **kwargs) == code
