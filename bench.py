@@ -75,6 +75,13 @@ def make_problem(torch, wl, layout, seed=0):
     t["ws"] = torch.empty(max(4, (nws + 15) // 16 * 4), dtype=torch.float32, device="cuda")
     t["dW"] = torch.empty((wl.Co, wl.kH, wl.kW), dtype=torch.float32, device="cuda")
     t["db"] = torch.empty((wl.Co,), dtype=torch.float32, device="cuda")
+    # inference BatchNorm of the output channels (gamma, beta, mean, var) and
+    # float32 weights / bias for the SGD step (updated in place by each call)
+    g = torch.Generator(device="cpu").manual_seed(seed + 1)
+    t["bn"] = tuple((torch.rand(wl.Co, generator=g) * s + o).to("cuda")
+                    for s, o in ((1.5, 0.5), (2.0, -1.0), (1.0, -0.5), (2.8, 0.2)))
+    t["w_sgd"] = torch.from_numpy(inp["w"].astype("float32")).to("cuda")
+    t["b_sgd"] = torch.zeros((wl.Co,), dtype=torch.float32, device="cuda")
     return t
 
 
@@ -103,6 +110,31 @@ def launch_wgrad(dw, wl, t, layout, stream):
     else:
         dw.dwconv2d_weight_grad(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
                                 wl.dilation, layout, dw.STRATEGY_AUTO, stream)
+
+
+def launch_fwd_bn_act(dw, wl, t, layout, stream):
+    """Forward with the fused BatchNorm + ReLU6 epilogue (MobileNetV2 block)."""
+    dw.dwconv2d_fwd_bn_act_ex(t["x"], t["w"], t["b"], t["y"], t["bn"], 1e-3, dw.ACT_RELU6,
+                              wl.stride, wl.dilation, wl.pads, wl.mult, layout,
+                              dw.STRATEGY_AUTO, stream)
+
+
+def launch_wgrad_sgd(dw, wl, t, layout, stream):
+    """Weight + bias gradient with the fused SGD step (w, b updated in place)."""
+    dw.dwconv2d_weight_grad_sgd_ex(t["x"], t["dy"], t["w_sgd"], t["b_sgd"], 1e-4, t["ws"],
+                                   None, None, wl.stride, wl.dilation, wl.pads, wl.mult, layout,
+                                   dw.STRATEGY_AUTO, stream)
+
+
+def fwd_bn_act_bytes(wl):
+    """x + y + W + b + the four BatchNorm arrays."""
+    return wl.fwd_bytes() + 16 * wl.Co
+
+
+def wgrad_sgd_bytes(wl):
+    """x + dy + W and b read and written (the gradients are not written)."""
+    return (4 * wl.N * wl.H * wl.W * wl.C + 4 * wl.N * wl.Ho * wl.Wo * wl.Co
+            + 8 * wl.Co * wl.kH * wl.kW + 8 * wl.Co)
 
 
 def wgrad_bytes(wl):
@@ -176,11 +208,14 @@ def per_config_table(torch, dw, iters=20):
             t = make_problem(torch, wl, layout, seed=0)
             for op, fn, nbytes in (("fwd", launch_fwd, wl.fwd_bytes()),
                                    ("ig", launch_ig, wl.ig_bytes()),
-                                   ("wgrad", launch_wgrad, wgrad_bytes(wl))):
-                if op == "wgrad" and wl.fp16_weights:
+                                   ("wgrad", launch_wgrad, wgrad_bytes(wl)),
+                                   ("fwd_bn_relu6", launch_fwd_bn_act, fwd_bn_act_bytes(wl)),
+                                   ("wgrad_sgd", launch_wgrad_sgd, wgrad_sgd_bytes(wl))):
+                if op.startswith("wgrad") and wl.fp16_weights:
                     continue              # the weight gradient does not read the weights
                 call = (lambda f=fn: f(dw, wl, t, layout, stream))
-                opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
+                opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD,
+                       "fwd_bn_relu6": dw.OP_FWD, "wgrad_sgd": dw.OP_WEIGHT_GRAD}[op]
                 kname = describe(dw, wl, opc, layout)
                 time_kernel(torch, call, stream, 3)
                 warm = statistics.median(time_kernel(torch, call, stream, iters))
@@ -308,26 +343,76 @@ def main():
         "ig_pct_peak": round(100 * wl.ig_bytes() / ig_avg / 1e3 / PEAK_HBM_GBS, 1),
         "roofline": roofline,
     }
-    # weight + bias gradient of the same workload (reads x and dy), timed on
-    # its own after the step loop: two kernels per call (partial sums, then
-    # their fixed-order reduction), timed together
-    wg = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            launch_wgrad(dw, wl, t, layout, stream)
-        for e in wg:
-            launch_fwd(dw, wl, t, layout, stream)     # evicts x/dy between calls like a step
-            e[0].record(stream)
-            launch_wgrad(dw, wl, t, layout, stream)
-            e[1].record(stream)
-    torch.cuda.synchronize()
-    wg_us = statistics.mean(e[0].elapsed_time(e[1]) * 1e3 for e in wg)
+    # Weight gradient, fused epilogues: timed like the roofline launch (two
+    # events around back-to-back launches alternating between two disjoint
+    # buffer sets, so no launch reads what the previous one left in the
+    # 256 MB Infinity Cache).  The second set for the weight gradient is a
+    # copy of x and dy.
+    x2, dy2 = t["x"].clone(), t["dy"].clone()
+    ws, dW, db, bn = t["ws"], t["dW"], t["db"], t["bn"]
+
+    def amortised(calls, n=40, what=""):
+        """Median per-call time (us) of n back-to-back calls with an event
+        between consecutive calls; a stall of the whole device (seen now and
+        then on this machine, tens of milliseconds, outside any kernel's
+        control) would otherwise dominate a mean, so it is reported apart."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        with torch.cuda.stream(stream):
+            for c in calls:
+                c()
+            ev[0].record(stream)
+            for i in range(n):
+                calls[i % len(calls)]()
+                ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+        med = statistics.median(us)
+        if max(us) > 3 * med:
+            _log(f"[bench] {what}: one call took {max(us):.0f} us (median {med:.1f} us)")
+        return med
+
+    def wgrad_call(xx, gg):
+        return lambda: dw.dwconv2d_weight_grad(xx, gg, dW, db, ws, wl.stride, wl.dilation,
+                                               layout, dw.STRATEGY_AUTO, stream)
+
+    def sgd_call(xx, gg):
+        return lambda: dw.dwconv2d_weight_grad_sgd_ex(xx, gg, t["w_sgd"], t["b_sgd"], 1e-4, ws,
+                                                      None, None, wl.stride, wl.dilation, None,
+                                                      1, layout, dw.STRATEGY_AUTO, stream)
+
+    def fused_call(src, dst):
+        return lambda: dw.dwconv2d_fwd_bn_act_ex(src, t["w"], t["b"], dst, bn, 1e-3,
+                                                 dw.ACT_RELU6, wl.stride, wl.dilation, None, 1,
+                                                 layout, dw.STRATEGY_AUTO, stream)
+
+    def fwd_call(src, dst):
+        return lambda: dw.dwconv2d_fwd(src, t["w"], t["b"], dst, wl.stride, wl.dilation, layout,
+                                       stream)
+
+    wg_us = amortised([wgrad_call(t["x"], t["dy"]), wgrad_call(x2, dy2)], what="wgrad")
+    sgd_us = amortised([sgd_call(t["x"], t["dy"]), sgd_call(x2, dy2)], what="wgrad_sgd")
+    fwd_ref_us = amortised([fwd_call(t["x"], t["y"]), fwd_call(t["dy"], t["dx"])], what="fwd")
+    epi_us = amortised([fused_call(t["x"], t["y"]), fused_call(t["dy"], t["dx"])],
+                       what="fwd_bn_relu6")
+    del x2, dy2
     result["wgrad"] = {
         "kernel": dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
                                        wl.stride, wl.dilation, layout)[0],
         "us": round(wg_us, 2), "algorithmic_bytes": wgrad_bytes(wl),
         "GBs": round(wgrad_bytes(wl) / wg_us / 1e3, 1),
-        "pct_peak": round(100 * wgrad_bytes(wl) / wg_us / 1e3 / PEAK_HBM_GBS, 1)}
+        "pct_peak": round(100 * wgrad_bytes(wl) / wg_us / 1e3 / PEAK_HBM_GBS, 1),
+        "timing": "median over 40 back-to-back calls (partial sums + reduction each) with an "
+                  "event between calls, alternating between two copies of x and dy"}
+    result["fused"] = {
+        "timing": "median over 40 back-to-back calls with an event between calls, "
+                  "alternating between two disjoint buffer sets",
+        "fwd_bn_relu6_us": round(epi_us, 2), "fwd_us_same_timing": round(fwd_ref_us, 2),
+        "fwd_bn_relu6_pct_peak": round(100 * fwd_bn_act_bytes(wl) / epi_us / 1e3 /
+                                       PEAK_HBM_GBS, 1),
+        "wgrad_sgd_us": round(sgd_us, 2),
+        "wgrad_sgd_pct_peak": round(100 * wgrad_sgd_bytes(wl) / sgd_us / 1e3 / PEAK_HBM_GBS, 1),
+        "note": "one pass each: the BatchNorm + ReLU6 epilogue is applied in the forward's "
+                "store, the SGD step in the weight-gradient reduction"}
     del t
     torch.cuda.empty_cache()
     if args.calib_copy:

@@ -48,7 +48,7 @@ enum Kind {
     KIND_DIRECT_NCHW = 2,  // one thread per (n, channel, row, col); taps from global
     KIND_TILED_NHWC = 3,   // stride 1: LDS row chunks with halo, rolling row accumulators
     KIND_TILED_NCHW = 4,   // stride 1: LDS tiles of one or more planes, rolling row accumulators
-    KIND_WGRAD_DIRECT = 5, // weight gradient, any layout/stride: workgroup = (position chunk, channel)
+    KIND_WGRAD_DIRECT = 5, // weight gradient, any layout/stride: lanes along the contiguous axis
     KIND_WGRAD_TILED_NHWC = 6, // weight gradient, NHWC stride 1: LDS x tiles, strips of row tiles
 };
 
@@ -57,20 +57,25 @@ enum Kind {
 // kernels.  `vec`: channels per thread; `cl`: threads across channels; `px`:
 // adjacent output pixels per thread (a workgroup of 256 threads covers
 // cl*vec channels of px*256/cl pixels); `g`: input rows staged per
-// workgroup, which yields g - (kH-1)*d output rows.
+// workgroup, which yields g - (kH-1)*d output rows; `lv`: floats per staging
+// load (4: needs C % 4 == 0 and 16-byte aligned tensors; 1: any C).
 //
 // For each kernel shape the variants are listed in order of preference: the
 // order of their measured throughput on MI355X for channel counts that fill
 // their channel tile.  The planner takes the first one whose channel tile
 // the problem fills to at least 3/4.
-struct TiledVariant { int kH, kW, d, vec, cl, px, g; };
+struct TiledVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr TiledVariant kTiledVariants[] = {
-    {3, 3, 1, 4, 32, 2, 8},   {3, 3, 1, 4, 16, 1, 6},   {3, 3, 1, 4, 8, 1, 3},
-    {5, 5, 1, 4, 8, 1, 8},    {5, 5, 1, 4, 16, 1, 12},
-    {7, 7, 1, 1, 64, 1, 14},  {7, 7, 1, 2, 16, 1, 14},
-    {7, 7, 2, 2, 16, 1, 20},
-    {1, 15, 1, 4, 32, 1, 2},  {1, 15, 1, 4, 16, 1, 2},
-    {1, 31, 1, 2, 32, 1, 2},  {1, 31, 1, 2, 64, 1, 2},
+    {3, 3, 1, 4, 32, 2, 8, 4},   {3, 3, 1, 4, 16, 1, 6, 4},   {3, 3, 1, 4, 8, 1, 3, 4},
+    {5, 5, 1, 4, 8, 1, 8, 4},    {5, 5, 1, 4, 16, 1, 12, 4},
+    {7, 7, 1, 1, 64, 1, 14, 4},  {7, 7, 1, 2, 16, 1, 14, 4},
+    {7, 7, 2, 2, 16, 1, 20, 4},
+    {1, 15, 1, 4, 32, 1, 2, 4},  {1, 15, 1, 4, 16, 1, 2, 4},
+    {1, 31, 1, 2, 32, 1, 2, 4},  {1, 31, 1, 2, 64, 1, 2, 4},
+    // scalar staging (lv = 1): any channel count, e.g. a prime one
+    {3, 3, 1, 1, 32, 2, 8, 1},   {5, 5, 1, 1, 32, 1, 12, 1},
+    {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 20, 1},
+    {1, 15, 1, 1, 32, 1, 2, 1},  {1, 31, 1, 1, 32, 1, 2, 1},
 };
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
 
@@ -89,8 +94,6 @@ constexpr WgradVariant kWgradVariants[] = {
 };
 constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);
 
-// Output positions one workgroup of the direct weight-gradient kernel sums.
-constexpr int kWgradChunk = 4096;
 
 // Compile-time variants of the tiled NCHW kernel (same preference rule).
 // A workgroup of 256 threads covers pb planes (channels) x tx threads per

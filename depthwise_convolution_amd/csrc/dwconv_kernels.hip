@@ -157,9 +157,10 @@ struct EpiArgs {
     int on;                                   // direct kernels: apply the epilogue
 };
 
-// Per-channel affine factors: y_pre = fmaf(z - mu, inv, be).
+// Per-channel affine factors: y_pre = fmaf(z - mu, inv, be).  epi_load
+// issues the loads (inv holds gamma, var the variance until epi_finish).
 struct EpiChan {
-    float mu, inv, be;
+    float mu, inv, be, var;
 };
 
 __device__ __forceinline__ float apply_act(float t, int act)
@@ -169,8 +170,36 @@ __device__ __forceinline__ float apply_act(float t, int act)
     if (act == DWCONV_ACT_RELU6)
         return fminf(fmaxf(t, 0.0f), 6.0f);
     if (act == DWCONV_ACT_SILU)
-        return t / (1.0f + expf(-t));
+        return __fdividef(t, 1.0f + __expf(-t));
     return t;
+}
+
+// Factors of channel c (c < channels) read through buffer descriptors.
+__device__ __forceinline__ EpiChan epi_load(const EpiArgs &ep, int c, int channels)
+{
+    EpiChan e{0.0f, 1.0f, 0.0f, 0.0f};
+    if (ep.gamma) {
+        const int bytes = channels * 4;
+        const int off = c < channels ? c * 4 : kOutOfRange;
+        e.inv = buf_f32(make_rsrc(ep.gamma, bytes), off);
+        e.var = buf_f32(make_rsrc(ep.var, bytes), off);
+        e.mu = buf_f32(make_rsrc(ep.mean, bytes), off);
+        e.be = buf_f32(make_rsrc(ep.beta, bytes), off);
+    }
+    return e;
+}
+
+__device__ __forceinline__ void epi_finish(EpiChan &e, const EpiArgs &ep)
+{
+    if (ep.gamma)
+        e.inv = e.inv / sqrtf(e.var + ep.eps);
+}
+
+__device__ __forceinline__ EpiChan epi_chan(const EpiArgs &ep, int c, int channels)
+{
+    EpiChan e = epi_load(ep, c, channels);
+    epi_finish(e, ep);
+    return e;
 }
 
 __device__ __forceinline__ float apply_epi(float z, EpiChan e, int act)
@@ -178,20 +207,29 @@ __device__ __forceinline__ float apply_epi(float z, EpiChan e, int act)
     return apply_act(fmaf(z - e.mu, e.inv, e.be), act);
 }
 
-// Factors of channel c (c < channels) read through buffer descriptors.
-__device__ __forceinline__ EpiChan epi_chan(const EpiArgs &ep, int c, int channels)
+// The epilogue over a block of N values (value i of channel factors e[i % NE]),
+// with one branch on the activation for the whole block.  SiLU uses the
+// hardware exponential and reciprocal (a few ulp, far inside the tolerance
+// its tests derive).
+template <int N, int NE>
+__device__ __forceinline__ void epi_block(float (&v)[N], const EpiChan (&e)[NE], int act)
 {
-    EpiChan e{0.0f, 1.0f, 0.0f};
-    if (ep.gamma) {
-        const int bytes = channels * 4;
-        const int off = c < channels ? c * 4 : kOutOfRange;
-        const float g = buf_f32(make_rsrc(ep.gamma, bytes), off);
-        const float v = buf_f32(make_rsrc(ep.var, bytes), off);
-        e.mu = buf_f32(make_rsrc(ep.mean, bytes), off);
-        e.be = buf_f32(make_rsrc(ep.beta, bytes), off);
-        e.inv = g / sqrtf(v + ep.eps);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = fmaf(v[i] - e[i % NE].mu, e[i % NE].inv, e[i % NE].be);
+    if (act == DWCONV_ACT_RELU) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = fmaxf(v[i], 0.0f);
+    } else if (act == DWCONV_ACT_RELU6) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = fminf(fmaxf(v[i], 0.0f), 6.0f);
+    } else if (act == DWCONV_ACT_SILU) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = __fdividef(v[i], 1.0f + __expf(-v[i]));
     }
-    return e;
 }
 
 struct DirectArgs {
@@ -371,24 +409,28 @@ struct TiledArgs {
     int nct, nwt, nst;      // channel tiles, column tiles, row tiles
 };
 
-template <int KH, int KW, int D, int VEC, int CL, int PX, int G>
+// LV: floats per staging load, 4 (16-byte loads: C % 4 == 0, 16-byte
+// aligned tensors) or 1 (any channel count).
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV>
 struct TiledGeom {
     static constexpr int R = (KH - 1) * D + 1;      // rows of one window
     static constexpr int TH = G - R + 1;            // output rows per workgroup
     static constexpr int TW = PX * 256 / CL;        // output columns per workgroup
     static constexpr int CG = CL * VEC;             // channels per workgroup
     static constexpr int TWI = TW + (KW - 1) * D;   // input columns staged
-    static constexpr int VPC = CG / 4;              // float4 per staged pixel
-    static constexpr int VPR = TWI * VPC;           // float4 per staged row
-    static constexpr int VCH = G * VPR;             // float4 staged
-    static constexpr int NV = (VCH + 255) / 256;    // float4 per thread
+    static constexpr int VPC = CG / LV;             // loads per staged pixel
+    static constexpr int VPR = TWI * VPC;           // loads per staged row
+    static constexpr int VCH = G * VPR;             // loads staged
+    static constexpr int NV = (VCH + 255) / 256;    // loads per thread
+    static constexpr int XF4 = (VCH * LV + 3) / 4;  // staged tile, in float4
     static constexpr int KK = KH * KW;
     static constexpr int WF = CG * KK;              // weight floats per workgroup
     static_assert(TH >= 1, "a workgroup must produce at least one output row");
-    static_assert(256 % CL == 0 && CG % 4 == 0, "bad channel tiling");
+    static_assert(256 % CL == 0 && CG % LV == 0 && (LV == 4 || LV == 1), "bad channel tiling");
+    static_assert(LV == 4 || VEC == 1, "scalar staging computes one channel per thread");
 };
 
-template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, int MODE>
+template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int MODE>
 __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__ in,
                                                        const void *__restrict__ wv,
                                                        const float *__restrict__ bias,
@@ -396,13 +438,13 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
                                                        EpiArgs ep)
 {
     constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
-    typedef TiledGeom<KH, KW, D, VEC, CL, PX, G> Gm;
+    typedef TiledGeom<KH, KW, D, VEC, CL, PX, G, LV> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
     constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV, KK = Gm::KK;
-    constexpr int WF = Gm::WF;
-    __shared__ float4 lds[VCH + (WF + 3) / 4];
+    constexpr int WF = Gm::WF, XF4 = Gm::XF4;
+    __shared__ float4 lds[XF4 + (WF + 3) / 4];
     float *ldsx = reinterpret_cast<float *>(lds);
-    float *ldsw = ldsx + VCH * 4;
+    float *ldsw = ldsx + XF4 * 4;
     const WT *w = reinterpret_cast<const WT *>(wv);
 
     int tile = blockIdx.x;
@@ -419,7 +461,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 
     const int q = tid % CL, p = tid / CL;
     const int cq = c0 + q * VEC;
-    const bool cvalid = cq < a.C;        // C % 4 == 0: the whole vector is valid
+    const bool cvalid = cq < a.C;        // LV == 4: C % 4 == 0, so the whole vector is valid
     const int ow = w0 + p * PX;          // first of this thread's PX output columns
 
     // 1. Issue every global load up front, the small L2-resident ones first:
@@ -440,7 +482,14 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 #pragma unroll
     for (int v = 0; v < VEC; ++v)
         bv[v] = buf_f32(rb, (cq + v) * 4);
-    float4 stage[NV];
+    EpiChan ec[VEC];
+    if constexpr (EPI) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            ec[v] = epi_load(ep, cq + v, a.C);
+    }
+    typedef typename VecT<LV>::type LoadT;
+    LoadT stage[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
@@ -448,10 +497,14 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
         const int rem = e - g * VPR;
         const int col = rem / VPC;
         const int cv = rem - col * VPC;
-        const int row = rbase + g, gc = cbase + col, ch = c0 + cv * 4;
+        const int row = rbase + g, gc = cbase + col, ch = c0 + cv * LV;
         const bool ok = e < VCH && g < nrows && row >= 0 && row < a.IH && gc >= 0 &&
                         gc < a.IW && ch < a.C;
-        stage[i] = buf_f4(rx, ok ? ((row * a.IW + gc) * a.C + ch) * 4 : kOutOfRange);
+        const int off = ok ? ((row * a.IW + gc) * a.C + ch) * 4 : kOutOfRange;
+        if constexpr (LV == 4)
+            stage[i] = buf_f4(rx, off);
+        else
+            stage[i] = buf_f32(rx, off);
     }
     // 2. weights, then the tile, into LDS
 #pragma unroll
@@ -464,7 +517,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
         if (e < VCH)
-            lds[e] = stage[i];
+            reinterpret_cast<LoadT *>(lds)[e] = stage[i];
     }
     __syncthreads();
 
@@ -479,11 +532,10 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
                 const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
                 wr[kh][kw][v] = ldsw[(q * VEC + v) * KK + tap];
             }
-    EpiChan ec[VEC];
     if constexpr (EPI) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v)
-            ec[v] = epi_chan(ep, cq + v, a.C);
+            epi_finish(ec[v], ep);
     }
     float acc[R][PX][VEC];
 #pragma unroll
@@ -527,11 +579,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
             if (m >= 0) {
 #pragma unroll
                 for (int j = 0; j < PX; ++j) {
-                    if constexpr (EPI) {
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v)
-                            acc[m % R][j][v] = apply_epi(acc[m % R][j][v], ec[v], ep.act);
-                    }
+                    if constexpr (EPI)
+                        epi_block(acc[m % R][j], ec, ep.act);
                     if (cvalid && ow + j < a.OW)
                         store_vec<VEC>(outp + ((h0 + m) * a.OW + ow + j) * a.C + cq,
                                        acc[m % R][j]);
@@ -631,6 +680,9 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
     const int my_plane = pg * pbn + pli;
     const bool pvalid = my_plane < a.planes;
     const float bval = buf_f32(rb, pvalid ? (my_plane % a.C) * 4 : kOutOfRange);
+    EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
+    if constexpr (EPI)
+        ec = epi_load(ep, pvalid ? my_plane % a.C : a.C, a.C);
     float sv[NV][LV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -678,9 +730,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
             const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
             wr[kh][kw] = ldsw[pli * KK + tap];
         }
-    EpiChan ec{0.0f, 1.0f, 0.0f};
     if constexpr (EPI)
-        ec = epi_chan(ep, pvalid ? my_plane % a.C : a.C, a.C);
+        epi_finish(ec, ep);
     float acc[R][Q];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -714,9 +765,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
             const int m = u - (R - 1);
             if (m >= 0) {
                 if constexpr (EPI) {
-#pragma unroll
-                    for (int j = 0; j < Q; ++j)
-                        acc[m % R][j] = apply_epi(acc[m % R][j], ec, ep.act);
+                    const EpiChan e1[1] = {ec};
+                    epi_block(acc[m % R], e1, ep.act);
                 }
                 float *dst = outp + (h0 + m) * a.OW + oc;
                 if (pvalid) {
@@ -753,65 +803,122 @@ struct WgradArgs {
     int chunks;             // rows of part[]
 };
 
-__device__ __forceinline__ int elem_index(bool nhwc, int C, int H, int W, int n, int c, int h,
-                                          int w)
-{
-    return nhwc ? ((n * H + h) * W + w) * C + c : ((n * C + c) * H + h) * W + w;
-}
+// Stage 1, any layout, stride, padding and multiplier.  Lanes run along the
+// contiguous axis so every load of a wave is one coalesced run: in NHWC
+// `cl` consecutive output channels x 256/cl position slots, in NCHW 256
+// consecutive positions of one output channel's plane.  A workgroup sums
+// one chunk of `ppc` dy positions; the kH*kW taps and the bias column go in
+// groups of 8 register accumulators (dy is re-read, from cache, once per
+// group), and the slots of a channel are added in LDS in a fixed order.
+// Output channel c reads x channel c / mult.
+struct WgradGenArgs {
+    int N, C, mult;         // C: channels of dy (and of dW); x has C / mult
+    int H, W, OH, OW;       // x extents, dy extents
+    int kH, kW, d, pH, pW;
+    int cl, ncg;            // NHWC: channel lanes (16, 32 or 64), channel groups
+    int ppc;                // dy positions per chunk
+    int cpi;                // NCHW: chunks per image
+};
 
-// Deterministic sum of v over a 256-thread workgroup (fixed tree); the
-// result is valid in thread 0.  `red` holds 256 floats.
-__device__ __forceinline__ float block_sum_256(float v, float *red)
-{
-    const int tid = threadIdx.x;
-    red[tid] = v;
-    __syncthreads();
-#pragma unroll
-    for (int off = 128; off > 0; off >>= 1) {
-        if (tid < off)
-            red[tid] += red[tid + off];
-        __syncthreads();
-    }
-    const float r = red[0];
-    __syncthreads();
-    return r;
-}
+constexpr int kWgradTapGroup = 8;
 
-// Stage 1, any layout, stride, padding and multiplier: workgroup = (chunk of
-// kWgradChunk dy positions, output channel c, which reads x channel c/mult);
-// each thread strides over the chunk's positions.
 template <bool NHWC, int S>
-__global__ __launch_bounds__(256) void k_wgrad_direct(const float *__restrict__ x,
-                                                      const float *__restrict__ dy,
-                                                      float *__restrict__ part, WgradArgs a)
+__global__ __launch_bounds__(256) void k_wgrad_gen(const float *__restrict__ x,
+                                                   const float *__restrict__ dy,
+                                                   float *__restrict__ part, WgradGenArgs a)
 {
-    __shared__ float red[256];
-    const int c = blockIdx.x % a.C;
-    const int ck = blockIdx.x / a.C;
-    const int total = a.N * a.OH * a.OW;
-    const int p0 = ck * kWgradChunk, p1 = min(p0 + kWgradChunk, total);
+    __shared__ float red[kWgradTapGroup][256];
+    const int tid = threadIdx.x;
     const int KK = a.kH * a.kW;
-    for (int tap = 0; tap <= KK; ++tap) {
-        const int kh = tap / a.kW, kw = tap - (tap / a.kW) * a.kW;
-        float acc = 0.0f;
-        for (int pp = p0 + threadIdx.x; pp < p1; pp += 256) {
-            const int wo = pp % a.OW;
-            const int t = pp / a.OW;
-            const int ho = t % a.OH;
-            const int n = t / a.OH;
-            const float g = dy[elem_index(NHWC, a.C, a.OH, a.OW, n, c, ho, wo)];
-            if (tap == KK) {
-                acc += g;
-            } else {
-                const int hi = ho * S + kh * a.d - a.pH, wi = wo * S + kw * a.d - a.pW;
-                if (hi >= 0 && hi < a.H && wi >= 0 && wi < a.W)
-                    acc = fmaf(x[elem_index(NHWC, a.C / a.mult, a.H, a.W, n, c / a.mult, hi, wi)],
-                               g, acc);
+    const int CI = a.C / a.mult;
+    const int per_img = a.OH * a.OW;
+    int chunk, c, slot, nslot, p0, p1, n_fixed = 0;
+    if (NHWC) {
+        const int cg = blockIdx.x % a.ncg;
+        chunk = blockIdx.x / a.ncg;
+        c = cg * a.cl + tid % a.cl;
+        slot = tid / a.cl;
+        nslot = 256 / a.cl;
+        p0 = chunk * a.ppc;                               // over (n, ho, wo) of all images
+        p1 = min(p0 + a.ppc, a.N * per_img);
+    } else {
+        c = blockIdx.x % a.C;
+        chunk = blockIdx.x / a.C;                         // (n, range within the plane)
+        n_fixed = chunk / a.cpi;
+        slot = tid;
+        nslot = 256;
+        p0 = (chunk - n_fixed * a.cpi) * a.ppc;           // within image n_fixed
+        p1 = min(p0 + a.ppc, per_img);
+    }
+    const bool cvalid = c < a.C;
+    const int ci = c / a.mult;
+    for (int tg = 0; tg <= KK; tg += kWgradTapGroup) {
+        float acc[kWgradTapGroup];
+        int th[kWgradTapGroup], tw[kWgradTapGroup];       // tap offsets; th = -1: bias column
+#pragma unroll
+        for (int t = 0; t < kWgradTapGroup; ++t) {
+            acc[t] = 0.0f;
+            const int tap = tg + t;
+            th[t] = tap < KK ? (tap / a.kW) * a.d - a.pH : -(1 << 30);
+            tw[t] = tap < KK ? (tap % a.kW) * a.d - a.pW : 0;
+        }
+        if (cvalid) {
+            for (int pp = p0 + slot; pp < p1; pp += nslot) {
+                int n, rem;
+                if (NHWC) {
+                    n = pp / per_img;
+                    rem = pp - n * per_img;
+                } else {
+                    n = n_fixed;
+                    rem = pp;
+                }
+                const int ho = rem / a.OW, wo = rem - (rem / a.OW) * a.OW;
+                const float g = NHWC ? dy[((n * a.OH + ho) * a.OW + wo) * a.C + c]
+                                     : dy[((n * a.C + c) * a.OH + ho) * a.OW + wo];
+#pragma unroll
+                for (int t = 0; t < kWgradTapGroup; ++t) {
+                    const int hi = ho * S + th[t], wi = wo * S + tw[t];
+                    if (hi >= 0 && hi < a.H && wi >= 0 && wi < a.W) {
+                        const float xv = NHWC ? x[((n * a.H + hi) * a.W + wi) * CI + ci]
+                                              : x[((n * CI + ci) * a.H + hi) * a.W + wi];
+                        acc[t] = fmaf(xv, g, acc[t]);
+                    } else if (tg + t == KK) {
+                        acc[t] += g;                      // the bias column
+                    }
+                }
             }
         }
-        const float sum = block_sum_256(acc, red);
-        if (threadIdx.x == 0)
-            part[((long long)ck * a.C + c) * (KK + 1) + tap] = sum;
+        // add the slots of each channel in a fixed order
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kWgradTapGroup; ++t)
+            red[t][tid] = acc[t];
+        __syncthreads();
+        if (NHWC) {
+            // thread e sums column (tap e / cl, lane e % cl) over the slots
+            for (int e = tid; e < kWgradTapGroup * a.cl; e += 256) {
+                const int t = e / a.cl, lane = e - t * a.cl;
+                const int cc = (blockIdx.x % a.ncg) * a.cl + lane;
+                if (tg + t <= KK && cc < a.C) {
+                    float sum = 0.0f;
+                    for (int sl = 0; sl < nslot; ++sl)
+                        sum += red[t][sl * a.cl + lane];
+                    part[((long long)chunk * a.C + cc) * (KK + 1) + tg + t] = sum;
+                }
+            }
+        } else {
+            // fixed tree over the 256 positions, all 8 taps at once
+#pragma unroll
+            for (int off = 128; off > 0; off >>= 1) {
+                if (tid < off)
+#pragma unroll
+                    for (int t = 0; t < kWgradTapGroup; ++t)
+                        red[t][tid] += red[t][tid + off];
+                __syncthreads();
+            }
+            if (tid < kWgradTapGroup && tg + tid <= KK)
+                part[((long long)chunk * a.C + c) * (KK + 1) + tg + tid] = red[tid][0];
+        }
     }
 }
 
@@ -1049,7 +1156,7 @@ template <typename WT, int V, int MODE>
 constexpr TiledFn tiled_fn()
 {
     constexpr TiledVariant t = kTiledVariants[V];
-    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, MODE>;
+    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE>;
 }
 
 template <int V>
@@ -1231,16 +1338,21 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x,
                            dy, part, a);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
-        const dim3 g((unsigned)pl.grid), b(256);
+        WgradGenArgs g;
+        g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;
+        g.H = p.H; g.W = p.W; g.OH = pl.OH; g.OW = pl.OW;
+        g.kH = p.kH; g.kW = p.kW; g.d = p.dilation; g.pH = pl.pH; g.pW = pl.pW;
+        g.cl = pl.cl; g.ncg = pl.nct; g.ppc = pl.tw; g.cpi = pl.nwt;
+        const dim3 gr((unsigned)pl.grid), b(256);
         const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
         if (nhwc && p.stride == 1)
-            hipLaunchKernelGGL((k_wgrad_direct<true, 1>), g, b, 0, st, x, dy, part, a);
+            hipLaunchKernelGGL((k_wgrad_gen<true, 1>), gr, b, 0, st, x, dy, part, g);
         else if (nhwc)
-            hipLaunchKernelGGL((k_wgrad_direct<true, 2>), g, b, 0, st, x, dy, part, a);
+            hipLaunchKernelGGL((k_wgrad_gen<true, 2>), gr, b, 0, st, x, dy, part, g);
         else if (p.stride == 1)
-            hipLaunchKernelGGL((k_wgrad_direct<false, 1>), g, b, 0, st, x, dy, part, a);
+            hipLaunchKernelGGL((k_wgrad_gen<false, 1>), gr, b, 0, st, x, dy, part, g);
         else
-            hipLaunchKernelGGL((k_wgrad_direct<false, 2>), g, b, 0, st, x, dy, part, a);
+            hipLaunchKernelGGL((k_wgrad_gen<false, 2>), gr, b, 0, st, x, dy, part, g);
     } else {
         return DWCONV_ERR_BAD_STRATEGY;
     }

@@ -113,8 +113,7 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
         return false;
-    if (p.C % 4 != 0 || (ptr_bits & 15u) != 0)
-        return false;
+    const bool v4ok = p.C % 4 == 0 && (ptr_bits & 15u) == 0;   // 16-byte staging loads
     // buffer-load byte offsets are 31-bit: one image and the weights must fit
     if (4LL * pl->IH * pl->IW * p.C >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
         return false;
@@ -124,7 +123,7 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     double best_fill = -1.0;
     for (int i = 0; i < kNumTiledVariants; ++i) {
         const TiledVariant &v = kTiledVariants[i];
-        if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation)
+        if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation || (v.lv == 4 && !v4ok))
             continue;
         const int cg = v.cl * v.vec;
         const double fill = (double)p.C / (ceil_div(p.C, cg) * cg);
@@ -152,8 +151,8 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->nst = ceil_div(pl->OH, pl->th);
     pl->grid = (long long)p.N * pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_%s_%s",
-                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, op_tag(p),
+    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_%s_%s",
+                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "", op_tag(p),
                   p.wtype ? "f16w" : "f32w");
     return true;
 }
@@ -316,14 +315,51 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
 
 static void plan_wgrad_direct(const Problem &p, Plan *pl)
 {
-    const long long positions = (long long)p.N * pl->OH * pl->OW;   // dy positions
+    // any layout / stride / padding / multiplier: the generic kernel, with
+    // lanes along the contiguous axis and chunks sized for >= ~2048 workgroups
+    const long long co = (long long)p.mult * p.C;
+    const long long per_img = (long long)pl->OH * pl->OW;
+    const long long target_wg = 2048;
     pl->kind = KIND_WGRAD_DIRECT;
     pl->variant = -1;
-    pl->chunks = (positions + kWgradChunk - 1) / kWgradChunk;
-    pl->grid = pl->chunks * p.mult * p.C;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "wgrad_direct_%s_s%d",
-                  p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride);
+    if (p.layout == DWCONV_LAYOUT_NHWC) {
+        int cl = 16;
+        double best = -1.0;
+        for (int c : {64, 32, 16}) {                      // widest lane run that fills >= 3/4
+            const double fill = (double)co / ((co + c - 1) / c * c);
+            if (fill >= 0.75) {
+                cl = c;
+                break;
+            }
+            if (fill > best) {
+                best = fill;
+                cl = c;
+            }
+        }
+        const long long ncg = (co + cl - 1) / cl, slots = 256 / cl;
+        const long long total = p.N * per_img;
+        const long long ppt = std::min<long long>(32, std::max<long long>(2, total * ncg / (slots * target_wg)));
+        const long long ppc = slots * ppt;
+        pl->cl = cl;
+        pl->nct = (int)ncg;
+        pl->tw = (int)ppc;
+        pl->nwt = 0;
+        pl->chunks = (total + ppc - 1) / ppc;
+        pl->grid = pl->chunks * ncg;
+    } else {
+        const long long ppt = std::min<long long>(16, std::max<long long>(2, p.N * per_img * co / (256 * target_wg)));
+        const long long ppc = 256 * ppt;
+        const long long cpi = (per_img + ppc - 1) / ppc;
+        pl->cl = 256;
+        pl->nct = 1;
+        pl->tw = (int)ppc;
+        pl->nwt = (int)cpi;
+        pl->chunks = p.N * cpi;
+        pl->grid = pl->chunks * co;
+    }
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_direct_%s_s%d_cl%d_ppc%d",
+                  p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride, pl->cl, pl->tw);
 }
 
 int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
