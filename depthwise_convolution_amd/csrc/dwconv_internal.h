@@ -50,6 +50,7 @@ enum Kind {
     KIND_TILED_NCHW = 4,   // stride 1: LDS tiles of one or more planes, rolling row accumulators
     KIND_WGRAD_DIRECT = 5, // weight gradient, any layout/stride: lanes along the contiguous axis
     KIND_WGRAD_TILED_NHWC = 6, // weight gradient, NHWC stride 1: LDS x tiles, strips of row tiles
+    KIND_WGRAD_TILED_NCHW = 7, // weight gradient, NCHW stride 1: LDS x plane rows, dy in registers
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
@@ -122,6 +123,7 @@ struct Plan {
     int pb;             // tiled NCHW: planes per workgroup
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
     int hl, twl;        // tiled NCHW: staged columns left of a tile, staged floats per row
+    int pb2;            // weight gradient, tiled NCHW: row tiles per plane
     int strip;          // weight gradient, tiled: row tiles per workgroup
     long long chunks;   // weight gradient: partial sums per weight (rows of the workspace)
     long long workspace;// weight gradient: workspace bytes

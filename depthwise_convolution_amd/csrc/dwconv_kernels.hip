@@ -1060,6 +1060,151 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     }
 }
 
+// Stage 1, NCHW stride 1: the NCHW forward's tiling with the roles of the
+// operands changed.  A workgroup covers pb dy planes x tx threads per plane
+// row (Q adjacent columns each) and walks `strip` row tiles of one column
+// tile; per row tile it stages the G x rows (+ column halo) of its planes'
+// input planes in LDS and loads its dy values into registers, and every
+// thread accumulates x*dy for all kH*kW taps (and dy for the bias) of its
+// plane.  The tx threads of each plane are then added with a fixed tree in
+// LDS, TG taps at a time.
+struct WgradNchwArgs {
+    int planes, C, mult;        // dy planes (N * C), dy channels, channel multiplier
+    int H, W, OH, OW;           // x extents, dy extents
+    int pH, pW, hl, twl;        // pads; staged columns left of a tile, staged floats per row
+    int tx_log2;
+    int nct, nwt, nsp, strip;   // plane groups, column tiles, strips, row tiles per strip
+    int nrt;                    // row tiles per plane
+};
+
+template <int KH, int KW, int D, int Q, int G, bool V4>
+__global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restrict__ x,
+                                                          const float *__restrict__ dy,
+                                                          float *__restrict__ part,
+                                                          WgradNchwArgs a)
+{
+    typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
+    constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV, NV = Gm::NV;
+    constexpr int XW = Q + (KW - 1) * D;
+    constexpr int TG = (KK + 1) < 16 ? (KK + 1) : 16;
+    extern __shared__ float4 lds4[];
+    float *lds = reinterpret_cast<float *>(lds4);
+
+    const int txn = 1 << a.tx_log2, pbn = 256 >> a.tx_log2;
+    const int tw = txn * Q, twl = a.twl, vpr = twl / LV;
+    int tile = blockIdx.x;
+    const int pg = tile % a.nct;
+    tile /= a.nct;
+    const int wt = tile % a.nwt;
+    const int sp = tile / a.nwt;
+    const int w0 = wt * tw;
+    const int tid = threadIdx.x;
+    const int pli = tid >> a.tx_log2, tx = tid & (txn - 1);
+    const int my_plane = pg * pbn + pli;
+    const bool pvalid = my_plane < a.planes;
+    const int oc = w0 + tx * Q;
+    const int CI = a.C / a.mult;
+    const int cbase = w0 - a.hl;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (a.planes / a.C) * CI * a.H * a.W * 4);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy, a.planes * a.OH * a.OW * 4);
+    const float *rowbase = lds + pli * G * twl + tx * Q + (a.hl - a.pW);
+
+    float acc[KK + 1];
+#pragma unroll
+    for (int t = 0; t <= KK; ++t)
+        acc[t] = 0.0f;
+
+    const int t0 = sp * a.strip, t1 = min(t0 + a.strip, a.nrt);
+    for (int tt = t0; tt < t1; ++tt) {
+        const int h0 = tt * TH;
+        const int nrows = min(TH, a.OH - h0) + R - 1;
+        const int rbase = h0 - a.pH;
+        float sv[NV][LV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = tid + i * 256;
+            const int pl = e / (G * vpr);
+            const int rem = e - pl * (G * vpr);
+            const int g = rem / vpr;
+            const int col = cbase + (rem - g * vpr) * LV;
+            const int plane = pg * pbn + pl, row = rbase + g;
+            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && row < a.H &&
+                            col >= 0 && col < a.W;
+            // x plane read by dy plane (n, o): (n, o / mult)
+            const int xplane = (plane / a.C) * CI + (plane % a.C) / a.mult;
+            const int off = ok ? ((xplane * a.H + row) * a.W + col) * 4 : kOutOfRange;
+            if constexpr (V4) {
+                const float4 v = buf_f4(rx, off);
+                sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
+            } else {
+                sv[i][0] = buf_f32(rx, off);
+            }
+        }
+        float gv[TH][Q];
+#pragma unroll
+        for (int m = 0; m < TH; ++m)
+#pragma unroll
+            for (int j = 0; j < Q; ++j) {
+                const bool ok = pvalid && h0 + m < a.OH && oc + j < a.OW;
+                gv[m][j] = buf_f32(rg, ok ? ((my_plane * a.OH + h0 + m) * a.OW + oc + j) * 4
+                                          : kOutOfRange);
+            }
+        if (tt > t0)
+            __syncthreads();              // every thread done with the previous tile
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = tid + i * 256;
+            if (e < pbn * G * vpr) {
+                if constexpr (V4)
+                    lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
+                else
+                    lds[e] = sv[i][0];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TH; ++m) {
+#pragma unroll
+            for (int j = 0; j < Q; ++j)
+                acc[KK] += gv[m][j];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                float xv[XW];
+#pragma unroll
+                for (int i = 0; i < XW; ++i)
+                    xv[i] = rowbase[(m + kh * D) * twl + i];
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                    for (int j = 0; j < Q; ++j)
+                        acc[kh * KW + kw] = fmaf(xv[j + kw * D], gv[m][j], acc[kh * KW + kw]);
+            }
+        }
+    }
+
+    // add the tx threads of each plane: fixed tree in LDS, TG taps at a time
+    for (int tb = 0; tb <= KK; tb += TG) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TG; ++k)
+            if (tb + k <= KK)
+                lds[k * 256 + tid] = acc[tb + k];
+        __syncthreads();
+        for (int off = txn >> 1; off > 0; off >>= 1) {
+            if (tx < off)
+#pragma unroll
+                for (int k = 0; k < TG; ++k)
+                    lds[k * 256 + tid] += lds[k * 256 + tid + off];
+            __syncthreads();
+        }
+        if (tx < TG && tb + tx <= KK && pvalid) {
+            const int n = my_plane / a.C, o = my_plane % a.C;
+            const int chunk = (n * a.nwt + wt) * a.nsp + sp;
+            part[((long long)chunk * a.C + o) * (KK + 1) + tb + tx] = lds[tx * 256 + pli * txn];
+        }
+    }
+}
+
 // Stage 2: 16 columns of part[] per workgroup, 16 threads per column each
 // summing every 16th chunk, then a fixed 16-way tree.
 // With w_upd, the LeanMlir page's SGD step is fused in: w_upd -= lr * dW and,
@@ -1284,6 +1429,29 @@ struct WgradTable {
 
 }  // namespace
 
+typedef void (*WgradNchwFn)(const float *, const float *, float *, WgradNchwArgs);
+
+template <int V>
+constexpr WgradNchwFn wgrad_nchw_fn()
+{
+    constexpr TiledNchwVariant t = kTiledNchwVariants[V];
+    return &k_wgrad_tiled_nchw<t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0)>;
+}
+
+template <int... Vs>
+void fill_wgrad_nchw(WgradNchwFn (&fn)[kNumTiledNchwVariants], std::integer_sequence<int, Vs...>)
+{
+    ((fn[Vs] = wgrad_nchw_fn<Vs>()), ...);
+}
+
+struct WgradNchwTable {
+    WgradNchwFn fn[kNumTiledNchwVariants];
+    WgradNchwTable()
+    {
+        fill_wgrad_nchw(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+    }
+};
+
 // Run a validated plan on `stream`.  Returns a DWCONV_ status.
 int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w,
                 const float *b, float *out, void *stream_v, const Epilogue *epi)
@@ -1337,6 +1505,21 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
             return DWCONV_ERR_BAD_STRATEGY;
         hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x,
                            dy, part, a);
+    } else if (pl.kind == KIND_WGRAD_TILED_NCHW) {
+        static const WgradNchwTable table;
+        if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
+            (pl.cl & (pl.cl - 1)) != 0)
+            return DWCONV_ERR_BAD_STRATEGY;
+        WgradNchwArgs g;
+        g.planes = p.N * p.mult * p.C; g.C = p.mult * p.C; g.mult = p.mult;
+        g.H = p.H; g.W = p.W; g.OH = pl.OH; g.OW = pl.OW;
+        g.pH = pl.pH; g.pW = pl.pW; g.hl = pl.hl; g.twl = pl.twl;
+        g.tx_log2 = 0;
+        while ((1 << g.tx_log2) < pl.cl)
+            ++g.tx_log2;
+        g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.pb2;
+        hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes,
+                           st, x, dy, part, g);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
         WgradGenArgs g;
         g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;

@@ -313,6 +313,58 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     return true;
 }
 
+static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
+{
+    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NCHW)
+        return false;
+    const long long co = (long long)p.mult * p.C, planes = p.N * co;
+    if (4LL * p.N * p.C * p.H * p.W >= (1LL << 31) || 4LL * planes * p.Ho * p.Wo >= (1LL << 31))
+        return false;
+    const bool v4ok = p.W % 4 == 0 && (ptr_bits & 15u) == 0;
+    int best = -1;
+    for (int i = 0; i < kNumTiledNchwVariants; ++i) {
+        const TiledNchwVariant &v = kTiledNchwVariants[i];
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation && (v.v4 == 0 || v4ok)) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const TiledNchwVariant &v = kTiledNchwVariants[best];
+    const int R = (v.kH - 1) * v.d + 1;
+    int tx = 16;                                  // threads per dy plane row
+    while (tx < 256 && tx * v.q < p.Wo)
+        tx *= 2;
+    const int lv = v.v4 ? 4 : 1;
+    const int hl = v.v4 ? -((-pl->pW) & ~3) : pl->pW;
+    const int span = (hl - pl->pW) + tx * v.q + v.d * (v.kW - 1);
+    pl->kind = KIND_WGRAD_TILED_NCHW;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = tx;
+    pl->pb = 256 / tx;
+    pl->tw = tx * v.q;
+    pl->hl = hl;
+    pl->twl = (span + lv - 1) / lv * lv;
+    pl->th = v.g - R + 1;
+    pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
+    pl->nwt = ceil_div(p.Wo, pl->tw);
+    pl->pb2 = ceil_div(p.Ho, pl->th);                            // row tiles per plane
+    // strips of row tiles per workgroup: about 2048 workgroups, fewer partial sums
+    const long long tiles = (long long)pl->pb2 * pl->nct * pl->nwt;
+    pl->strip = (int)std::min<long long>(pl->pb2, std::max<long long>(1, (tiles + 2047) / 2048));
+    pl->nst = ceil_div(pl->pb2, pl->strip);
+    pl->chunks = (long long)p.N * pl->nwt * pl->nst;
+    pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
+    const int tg = std::min(p.kH * p.kW + 1, 16);
+    pl->lds_bytes = 4 * std::max(pl->pb * v.g * pl->twl, tg * 256);
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nchw_s1_k%dx%d_d%d_q%d_g%d_%s_tx%d_s%d",
+                  v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, pl->strip);
+    return true;
+}
+
 static void plan_wgrad_direct(const Problem &p, Plan *pl)
 {
     // any layout / stride / padding / multiplier: the generic kernel, with
@@ -375,7 +427,8 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     bool tiled = false;
     if (strategy != DWCONV_STRATEGY_DIRECT) {
         Plan t = *pl;
-        tiled = plan_wgrad_tiled(p, ptr_bits, &t);
+        tiled = p.layout == DWCONV_LAYOUT_NHWC ? plan_wgrad_tiled(p, ptr_bits, &t)
+                                               : plan_wgrad_tiled_nchw(p, ptr_bits, &t);
         if (tiled)
             *pl = t;
         else if (strategy == DWCONV_STRATEGY_TILED)

@@ -216,7 +216,10 @@ def test_weight_grad_workspace_and_plans():
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 3, 3, stride=2)
     assert name.startswith("wgrad_direct_nhwc_s2")
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 3, 3, layout=dw.NCHW)
-    assert name.startswith("wgrad_direct_nchw")
+    assert name.startswith("wgrad_tiled_nchw_s1")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 3, 3, stride=2,
+                                      layout=dw.NCHW)
+    assert name.startswith("wgrad_direct_nchw_s2")
     with pytest.raises(dw.DwconvError) as e:
         dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 8, 8, 4, 3, 3, has_bias=True)
     assert e.value.status == -11
