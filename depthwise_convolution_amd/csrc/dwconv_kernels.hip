@@ -1,12 +1,13 @@
 // dwconv_kernels.hip -- gfx950 kernels of depthwise 2-D convolution and the
-// launcher that runs a plan.
+// launchers that run a plan.
 //
 // What is computed (LeanMlir "Depthwise" page): the forward equation
 //   y[c,h,w] = b[c] + sum_{kh,kw} x[c, h*s + kh*d - pH, w*s + kw*d - pW] * W[c,kh,kw]
-// (one filter per channel, no channel sum, zero padding), and the input
-// gradient in its reversed-kernel form, with stride 2 handled as the
-// zero-upsampled cotangent (only upsampled positions that are multiples of s
-// carry a value).
+// (one filter per channel, no channel sum, zero padding; with a channel
+// multiplier m output channel o reads input channel o/m), its input gradient
+// in the reversed-kernel form with stride 2 handled as the zero-upsampled
+// cotangent (only upsampled positions that are multiples of s carry a
+// value), and its weight and bias gradients.
 //
 // Design (gfx950, 64-wide waves, HBM-bound): the channel axis is a batch
 // axis, so there is no contraction for the matrix cores; each output is a
@@ -16,23 +17,22 @@
 // bandwidth-bound).  Weights are widened to fp32 once per thread (f16 by
 // value, never by reinterpreting bytes: the ggml PR's CPU-backend bug).
 //
-//  * direct kernels: one thread per output (NCHW) or per 4-channel output
-//    vector (NHWC); taps read from global memory through the caches.  They
-//    cover every valid problem and are the reference-free fallback.
-//  * tiled NHWC kernel (stride 1): a workgroup owns a strip of output rows
-//    of a (column tile x channel tile); it streams the input rows the strip
-//    needs through LDS in chunks of G rows (the tile plus the (kW-1)*d
-//    column halo, zero-filled outside the image), each thread reads its kW
-//    horizontal taps per input row from LDS and folds the row into R =
-//    (kH-1)*d + 1 rolling accumulators, one per output row in flight, so
-//    every input element is fetched from HBM about once and reused for all
-//    kH*kW taps.  Global loads for chunk k+1 are issued before chunk k is
-//    computed.  Workgroups are remapped so each XCD (own L2) walks a
-//    contiguous range of tiles, keeping halo re-reads in one L2.
+//  * direct kernels: one thread per output (NCHW) or per channel vector
+//    (NHWC); taps read from global memory through the caches.  They cover
+//    every valid problem (stride 2, any pads, multipliers, even kernels).
+//  * tiled NHWC / NCHW kernels (stride 1): a short-lived workgroup stages the
+//    input rows its output rows need (tile plus (k-1)*d halo, zero outside
+//    the image, via raw buffer loads) and its weights in LDS in one load
+//    phase, then walks the rows: each thread reads its kW horizontal taps per
+//    staged row from LDS and folds the row into R = (kH-1)*d + 1 rolling
+//    accumulators, so every input element is fetched from HBM about once and
+//    reused for all kH*kW taps.  Compile-time modes: forward, input gradient
+//    (reversed taps, no bias), forward with the BatchNorm / activation
+//    epilogue.
+//  * weight gradient: per-chunk partial sums (tiled NHWC, tiled NCHW or the
+//    generic coalesced kernel), then a fixed-order reduction that can also
+//    apply the SGD step.
 //  * every output store is non-temporal: outputs are write-once streams.
-//
-// The input gradient at stride 1 is the same kernel with the kernel taps
-// reversed (loaded reversed into registers) and no bias.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
