@@ -800,6 +800,7 @@ struct WgradArgs {
     int H, W, kH, kW, d, pH, pW;
     int OH, OW;             // dy extents
     int nct, nwt, nsp;      // tiled: channel tiles, column tiles, strips
+    int strip;              // tiled: row tiles per strip
     int chunks;             // rows of part[]
 };
 
@@ -923,12 +924,12 @@ __global__ __launch_bounds__(256) void k_wgrad_gen(const float *__restrict__ x,
 }
 
 // Stage 1, NHWC stride 1: a workgroup (256 threads: CL across channels x
-// 256/CL pixel slots of PX columns) walks STRIP row tiles of one column
+// 256/CL pixel slots of PX columns) walks `strip` row tiles of one column
 // tile.  Per row tile it stages G input rows (+ column halo) in LDS and
 // loads its dy rows straight into registers (each dy element is used by one
 // thread only); every thread accumulates x*dy for all kH*kW taps of its
 // channels, and at the end the pixel slots are summed through LDS.
-template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int STRIP>
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G>
 __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restrict__ x,
                                                           const float *__restrict__ dy,
                                                           float *__restrict__ part, WgradArgs a)
@@ -968,7 +969,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
         for (int v = 0; v < VEC; ++v)
             acc[t][v] = 0.0f;
 
-    const int t0 = sp * STRIP, t1 = min(t0 + STRIP, (a.OH + TH - 1) / TH);
+    const int t0 = sp * a.strip, t1 = min(t0 + a.strip, (a.OH + TH - 1) / TH);
     for (int tt = t0; tt < t1; ++tt) {
         const int h0 = tt * TH;
         const int nrows = min(TH, a.OH - h0) + R - 1;
@@ -1205,35 +1206,56 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     }
 }
 
-// Stage 2: 16 columns of part[] per workgroup, 16 threads per column each
-// summing every 16th chunk, then a fixed 16-way tree.
+// Stage 2: 64 columns of part[] per workgroup, one per lane, so every wave
+// load is one coalesced run; wave w adds the chunks w, w+4, w+8, ... with 8
+// independent partial sums (8 loads in flight), combined in a fixed order,
+// and the 4 waves are added in a fixed order in LDS.  The result depends
+// only on the partial sums, never on timing.
 // With w_upd, the LeanMlir page's SGD step is fused in: w_upd -= lr * dW and,
 // with b_upd, b_upd -= lr * db (one rounding each: fmaf(-lr, grad, old)).
+constexpr int kReduceUnroll = 8;
+
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ part,
                                                       float *__restrict__ dw,
                                                       float *__restrict__ db, int chunks,
                                                       int C, int KK, float *__restrict__ w_upd,
                                                       float *__restrict__ b_upd, float lr)
 {
-    __shared__ float red[16][17];
+    __shared__ float red[4][64];
     const int cols = C * (KK + 1);
-    const int lane = threadIdx.x & 15, j = threadIdx.x >> 4;
-    const int col = blockIdx.x * 16 + lane;
-    float s = 0.0f;
-    if (col < cols)
-        for (int r = j; r < chunks; r += 16)
-            s += part[(long long)r * cols + col];
-    red[j][lane] = s;
-    __syncthreads();
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + lane;
+    const bool valid = col < cols;
+    float s[kReduceUnroll];
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) {
-        if (j < off)
-            red[j][lane] += red[j + off][lane];
-        __syncthreads();
+    for (int u = 0; u < kReduceUnroll; ++u)
+        s[u] = 0.0f;
+    if (valid) {
+        int r = wv;
+        for (; r + 4 * (kReduceUnroll - 1) < chunks; r += 4 * kReduceUnroll) {
+            float v[kReduceUnroll];
+#pragma unroll
+            for (int u = 0; u < kReduceUnroll; ++u)
+                v[u] = part[(long long)(r + 4 * u) * cols + col];
+#pragma unroll
+            for (int u = 0; u < kReduceUnroll; ++u)
+                s[u] += v[u];
+        }
+#pragma unroll
+        for (int u = 0; u < kReduceUnroll - 1; ++u)
+            if (r + 4 * u < chunks)
+                s[u] += part[(long long)(r + 4 * u) * cols + col];
     }
-    if (j == 0 && col < cols) {
+#pragma unroll
+    for (int w = kReduceUnroll / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int u = 0; u < w; ++u)
+            s[u] += s[u + w];
+    red[wv][lane] = s[0];
+    __syncthreads();
+    if (wv == 0 && valid) {
+        const float g = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
         const int c = col / (KK + 1), tap = col - c * (KK + 1);
-        const float g = red[0][lane];
         if (tap < KK) {
             if (dw)
                 dw[c * KK + tap] = g;
@@ -1413,7 +1435,7 @@ template <int V>
 constexpr WgradFn wgrad_fn()
 {
     constexpr WgradVariant t = kWgradVariants[V];
-    return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.strip>;
+    return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g>;
 }
 
 template <int... Vs>
@@ -1498,7 +1520,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     a.N = p.N; a.C = p.mult * p.C; a.mult = p.mult;
     a.H = p.H; a.W = p.W; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
     a.pH = pl.pH; a.pW = pl.pW; a.OH = pl.OH; a.OW = pl.OW;
-    a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.chunks = (int)pl.chunks;
+    a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.strip = pl.strip; a.chunks = (int)pl.chunks;
     if (pl.kind == KIND_WGRAD_TILED_NHWC) {
         static const WgradTable table;
         if (pl.variant < 0 || pl.variant >= kNumWgradVariants)

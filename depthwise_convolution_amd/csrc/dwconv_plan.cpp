@@ -267,6 +267,20 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
 // last column is the bias gradient) to the workspace; stage 2 adds the
 // chunks of every column in a fixed order.
 // ---------------------------------------------------------------------------
+// Row tiles per strip of a tiled weight-gradient plan: `base` workgroups
+// cover one strip of every (image, column tile, channel / plane group); the
+// strip count is the one nearest kWgradTargetWorkgroups / base (at least 1),
+// and the nrt row tiles are split evenly between the strips.  Few, long
+// strips keep the partial sums (and their reduction) small; the target keeps
+// about two workgroups per compute unit on a large image.
+static int wgrad_strip(int nrt, long long base)
+{
+    long long nsp = (2 * kWgradTargetWorkgroups + base) / (2 * base);   // round to nearest
+    nsp = std::max<long long>(1, std::min<long long>(nsp, nrt));
+    const long long strip = (nrt + nsp - 1) / nsp;
+    return (int)strip;
+}
+
 static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC || p.C % 4 != 0 ||
@@ -301,15 +315,16 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     pl->cl = v.cl;
     pl->tw = v.px * 256 / v.cl;
     pl->th = v.g - R + 1;
-    pl->strip = v.strip;
+    const int nrt = ceil_div(p.Ho, pl->th);                   // row tiles per image
     pl->nct = ceil_div(p.C, v.cl * v.vec);
     pl->nwt = ceil_div(p.Wo, pl->tw);
-    pl->nst = ceil_div(ceil_div(p.Ho, pl->th), v.strip);   // strips
+    pl->strip = wgrad_strip(nrt, (long long)p.N * pl->nct * pl->nwt);
+    pl->nst = ceil_div(nrt, pl->strip);                         // strips
     pl->chunks = (long long)p.N * pl->nst * pl->nwt;
     pl->grid = pl->chunks * pl->nct;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_s%d",
-                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.strip);
+                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, pl->strip);
     return true;
 }
 
@@ -351,9 +366,7 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(p.Wo, pl->tw);
     pl->pb2 = ceil_div(p.Ho, pl->th);                            // row tiles per plane
-    // strips of row tiles per workgroup: about 2048 workgroups, fewer partial sums
-    const long long tiles = (long long)pl->pb2 * pl->nct * pl->nwt;
-    pl->strip = (int)std::min<long long>(pl->pb2, std::max<long long>(1, (tiles + 2047) / 2048));
+    pl->strip = wgrad_strip(pl->pb2, (long long)pl->nct * pl->nwt);
     pl->nst = ceil_div(pl->pb2, pl->strip);
     pl->chunks = (long long)p.N * pl->nwt * pl->nst;
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
@@ -440,7 +453,7 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (pl->chunks * cols >= (1LL << 31))
         return DWCONV_ERR_BAD_DIM;
     pl->workspace = 4 * pl->chunks * cols;
-    pl->grid2 = (cols + 15) / 16;
+    pl->grid2 = (cols + 63) / 64;
     return DWCONV_OK;
 }
 
