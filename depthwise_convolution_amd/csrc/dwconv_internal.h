@@ -81,17 +81,21 @@ constexpr TiledVariant kTiledVariants[] = {
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
 
 // Compile-time variants of the tiled NHWC weight-gradient kernel: workgroup
-// geometry as for the forward (vec, cl, px, g).  A workgroup walks a strip of
+// geometry as for the forward (vec, cl, px, g, lv).  A workgroup walks a strip of
 // row tiles of g - (kH-1)*d rows (its partial sums cover them all); the
 // planner sizes the strips for about kWgradTargetWorkgroups workgroups.
-struct WgradVariant { int kH, kW, d, vec, cl, px, g; };
+struct WgradVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr WgradVariant kWgradVariants[] = {
-    {3, 3, 1, 4, 16, 1, 6},  {3, 3, 1, 4, 8, 1, 6},
-    {5, 5, 1, 4, 16, 1, 8},
-    {7, 7, 1, 2, 32, 1, 10},
-    {7, 7, 2, 2, 32, 1, 16},
-    {1, 15, 1, 4, 32, 1, 2},
-    {1, 31, 1, 2, 32, 1, 2},
+    {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
+    {5, 5, 1, 4, 16, 1, 8, 4},
+    {7, 7, 1, 2, 32, 1, 10, 4},
+    {7, 7, 2, 2, 32, 1, 16, 4},
+    {1, 15, 1, 4, 32, 1, 2, 4},
+    {1, 31, 1, 2, 32, 1, 2, 4},
+    // 4-byte staging (lv = 1): any channel count
+    {3, 3, 1, 1, 32, 1, 6, 1},  {5, 5, 1, 1, 32, 1, 8, 1},
+    {7, 7, 1, 1, 32, 1, 10, 1}, {7, 7, 2, 1, 32, 1, 16, 1},
+    {1, 15, 1, 1, 32, 1, 2, 1}, {1, 31, 1, 1, 32, 1, 2, 1},
 };
 constexpr long long kWgradTargetWorkgroups = 512;
 constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);

@@ -929,19 +929,23 @@ __global__ __launch_bounds__(256) void k_wgrad_gen(const float *__restrict__ x,
 // loads its dy rows straight into registers (each dy element is used by one
 // thread only); every thread accumulates x*dy for all kH*kW taps of its
 // channels, and at the end the pixel slots are summed through LDS.
-template <int KH, int KW, int D, int VEC, int CL, int PX, int G>
+// LV: floats per staging load, 4 (C % 4 == 0, 16-byte aligned tensors) or 1
+// (any C, one channel per thread).
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV>
 __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restrict__ x,
                                                           const float *__restrict__ dy,
                                                           float *__restrict__ part, WgradArgs a)
 {
+    static_assert(LV == 4 || (LV == 1 && VEC == 1), "scalar staging: one channel per thread");
     constexpr int R = (KH - 1) * D + 1, TH = G - R + 1, TW = PX * 256 / CL, CG = CL * VEC;
-    constexpr int TWI = TW + (KW - 1) * D, VPC = CG / 4, VPR = TWI * VPC, VCH = G * VPR;
+    constexpr int TWI = TW + (KW - 1) * D, VPC = CG / LV, VPR = TWI * VPC, VCH = G * VPR;
     constexpr int NV = (VCH + 255) / 256, KK = KH * KW, NP = 256 / CL;
     constexpr int XW = PX + (KW - 1) * D;
+    constexpr int XF = VCH * LV;            // staged floats
     // the final per-(channel, tap) sums go through LDS in groups of TG taps
-    constexpr int TGF = (VCH * 4) / (256 * VEC);
+    constexpr int TGF = XF / (256 * VEC);
     constexpr int TG = TGF < 1 ? 1 : (TGF > KK + 1 ? KK + 1 : TGF);
-    constexpr int LDSF = (VCH * 4 > 256 * VEC * TG) ? VCH * 4 : 256 * VEC * TG;
+    constexpr int LDSF = (XF > 256 * VEC * TG) ? XF : 256 * VEC * TG;
     __shared__ float4 lds4[(LDSF + 3) / 4];
     float *lds = reinterpret_cast<float *>(lds4);
 
@@ -975,7 +979,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
         const int nrows = min(TH, a.OH - h0) + R - 1;
         const int rbase = h0 - a.pH;
         // this row tile's x rows (+ halo) and, per thread, its dy values
-        float4 stage[NV];
+        typedef typename VecT<LV>::type LoadT;
+        LoadT stage[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = tid + i * 256;
@@ -983,10 +988,14 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
             const int rem = e - g * VPR;
             const int col = rem / VPC;
             const int cv = rem - col * VPC;
-            const int row = rbase + g, gc = cbase + col, ch = c0 + cv * 4;
+            const int row = rbase + g, gc = cbase + col, ch = c0 + cv * LV;
             const bool ok = e < VCH && g < nrows && row >= 0 && row < a.H && gc >= 0 &&
                             gc < a.W && ch < a.C;
-            stage[i] = buf_f4(rx, ok ? ((row * a.W + gc) * a.C + ch) * 4 : kOutOfRange);
+            const int off = ok ? ((row * a.W + gc) * a.C + ch) * 4 : kOutOfRange;
+            if constexpr (LV == 4)
+                stage[i] = buf_f4(rx, off);
+            else
+                stage[i] = buf_f32(rx, off);
         }
         float gv[TH][PX][VEC];
 #pragma unroll
@@ -1003,7 +1012,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
         for (int i = 0; i < NV; ++i) {
             const int e = tid + i * 256;
             if (e < VCH)
-                lds4[e] = stage[i];
+                reinterpret_cast<LoadT *>(lds4)[e] = stage[i];
         }
         __syncthreads();
 #pragma unroll
@@ -1435,7 +1444,7 @@ template <int V>
 constexpr WgradFn wgrad_fn()
 {
     constexpr WgradVariant t = kWgradVariants[V];
-    return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g>;
+    return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv>;
 }
 
 template <int... Vs>

@@ -283,16 +283,16 @@ static int wgrad_strip(int nrt, long long base)
 
 static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC || p.C % 4 != 0 ||
-        (ptr_bits & 15u))
+    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
         return false;
+    const bool v4ok = p.C % 4 == 0 && (ptr_bits & 15u) == 0;   // 16-byte staging loads
     if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.Ho * p.Wo * p.C >= (1LL << 31))
         return false;
     int best = -1;
     double best_fill = -1.0;
     for (int i = 0; i < kNumWgradVariants; ++i) {
         const WgradVariant &v = kWgradVariants[i];
-        if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation)
+        if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation || (v.lv == 4 && !v4ok))
             continue;
         const int cg = v.cl * v.vec;
         const double fill = (double)p.C / (ceil_div(p.C, cg) * cg);
@@ -323,8 +323,8 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     pl->chunks = (long long)p.N * pl->nst * pl->nwt;
     pl->grid = pl->chunks * pl->nct;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d_s%d",
-                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, pl->strip);
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_s%d",
+                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "", pl->strip);
     return true;
 }
 

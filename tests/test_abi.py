@@ -209,10 +209,13 @@ def test_weight_grad_workspace_and_plans():
     n = dw.dwconv2d_weight_grad_workspace_size(1, 512, 512, 256, 3, 3)
     name, grid, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 512, 512, 256, 3, 3)
     assert name.startswith("wgrad_tiled_nhwc") and n > 0 and n % (4 * 256 * 10) == 0
-    # the reported size covers the fallback plan too (used for misaligned pointers)
+    # each strategy reports the size of its own plans (AUTO: aligned and
+    # misaligned pointers, both tiled here; DIRECT: the generic kernel)
     d = dw.dwconv2d_weight_grad_workspace_size(1, 512, 512, 256, 3, 3,
                                                 strategy=dw.STRATEGY_DIRECT)
-    assert n >= d
+    assert d > 0 and d % (4 * 256 * 10) == 0
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7)
+    assert name.startswith("wgrad_tiled_nhwc") and "_l1_" in name    # any C, 4-byte staging
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 3, 3, stride=2)
     assert name.startswith("wgrad_direct_nhwc_s2")
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 3, 3, layout=dw.NCHW)
