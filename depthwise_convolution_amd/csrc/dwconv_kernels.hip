@@ -612,7 +612,7 @@ struct TiledNchwArgs {
     int IH, IW, OH, OW;     // extents of the tensor read and the tensor written
     int pH, pW;             // top / left zero padding of the tensor read
     int hl, twl;            // staged columns left of a tile; staged floats per plane row
-    int tx_log2;            // threads per plane row = 1 << tx_log2 (>= 16)
+    int txn, pbn;           // threads per plane row (16..256), planes per workgroup (256 / txn)
     int nct, nwt, nst;      // plane groups, column tiles, row tiles
 };
 
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
     float *lds = reinterpret_cast<float *>(lds4);
     const WT *w = reinterpret_cast<const WT *>(wv);
 
-    const int txn = 1 << a.tx_log2, pbn = 256 >> a.tx_log2;
+    const int txn = a.txn, pbn = a.pbn;
     const int tw = txn * Q, twl = a.twl;               // staged floats per plane row
     const int vpr = twl / LV;                          // loads per plane row
     float *ldsw = lds + pbn * G * twl;
@@ -676,9 +676,11 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
         const bool ok = pl < pbn && plane < a.planes;
         wst[i] = buf_w(rw, ok ? (plane % a.C) * KK + tap : kOutOfRange / 4, (WT *)nullptr);
     }
-    const int pli = tid >> a.tx_log2, tx = tid & (txn - 1);
+    // threads past pbn * txn (when txn does not divide 256) idle along
+    const int pli_raw = tid / txn, tx = tid - pli_raw * txn;
+    const int pli = min(pli_raw, pbn - 1);             // in-range LDS addresses for idle threads
     const int my_plane = pg * pbn + pli;
-    const bool pvalid = my_plane < a.planes;
+    const bool pvalid = pli_raw < pbn && my_plane < a.planes;
     const float bval = buf_f32(rb, pvalid ? (my_plane % a.C) * 4 : kOutOfRange);
     EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
     if constexpr (EPI)
@@ -1082,7 +1084,7 @@ struct WgradNchwArgs {
     int planes, C, mult;        // dy planes (N * C), dy channels, channel multiplier
     int H, W, OH, OW;           // x extents, dy extents
     int pH, pW, hl, twl;        // pads; staged columns left of a tile, staged floats per row
-    int tx_log2;
+    int txn, pbn;               // threads per plane row (16..256), planes per workgroup
     int nct, nwt, nsp, strip;   // plane groups, column tiles, strips, row tiles per strip
     int nrt;                    // row tiles per plane
 };
@@ -1100,7 +1102,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
 
-    const int txn = 1 << a.tx_log2, pbn = 256 >> a.tx_log2;
+    const int txn = a.txn, pbn = a.pbn;
     const int tw = txn * Q, twl = a.twl, vpr = twl / LV;
     int tile = blockIdx.x;
     const int pg = tile % a.nct;
@@ -1109,9 +1111,11 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     const int sp = tile / a.nwt;
     const int w0 = wt * tw;
     const int tid = threadIdx.x;
-    const int pli = tid >> a.tx_log2, tx = tid & (txn - 1);
+    // threads past pbn * txn (when txn does not divide 256) idle along
+    const int pli_raw = tid / txn, tx = tid - pli_raw * txn;
+    const int pli = min(pli_raw, pbn - 1);             // in-range LDS addresses for idle threads
     const int my_plane = pg * pbn + pli;
-    const bool pvalid = my_plane < a.planes;
+    const bool pvalid = pli_raw < pbn && my_plane < a.planes;
     const int oc = w0 + tx * Q;
     const int CI = a.C / a.mult;
     const int cbase = w0 - a.hl;
@@ -1200,8 +1204,20 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
             if (tb + k <= KK)
                 lds[k * 256 + tid] = acc[tb + k];
         __syncthreads();
-        for (int off = txn >> 1; off > 0; off >>= 1) {
-            if (tx < off)
+        // fold a non-power-of-two row onto its largest power-of-two prefix,
+        // then a binary tree (fixed order either way)
+        int p2 = 1;
+        while (2 * p2 <= txn)
+            p2 *= 2;
+        if (p2 < txn) {
+            if (pli_raw < pbn && tx < txn - p2)
+#pragma unroll
+                for (int k = 0; k < TG; ++k)
+                    lds[k * 256 + tid] += lds[k * 256 + tid + p2];
+            __syncthreads();
+        }
+        for (int off = p2 >> 1; off > 0; off >>= 1) {
+            if (pli_raw < pbn && tx < off)
 #pragma unroll
                 for (int k = 0; k < TG; ++k)
                     lds[k * 256 + tid] += lds[k * 256 + tid + off];
@@ -1422,16 +1438,15 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
 {
     static const TiledNchwTable table;
     if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
-        (pl.cl & (pl.cl - 1)) != 0)
+        pl.pb != 256 / pl.cl)
         return DWCONV_ERR_BAD_STRATEGY;
     TiledNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
     TiledNchwArgs a;
     a.planes = p.N * p.C; a.C = p.C;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
     a.pH = pl.pH; a.pW = pl.pW; a.hl = pl.hl; a.twl = pl.twl;
-    a.tx_log2 = 0;
-    while ((1 << a.tx_log2) < pl.cl)
-        ++a.tx_log2;
+    a.txn = pl.cl;
+    a.pbn = pl.pb;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
                        p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
@@ -1539,15 +1554,14 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     } else if (pl.kind == KIND_WGRAD_TILED_NCHW) {
         static const WgradNchwTable table;
         if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
-            (pl.cl & (pl.cl - 1)) != 0)
+            pl.pb != 256 / pl.cl)
             return DWCONV_ERR_BAD_STRATEGY;
         WgradNchwArgs g;
         g.planes = p.N * p.mult * p.C; g.C = p.mult * p.C; g.mult = p.mult;
         g.H = p.H; g.W = p.W; g.OH = pl.OH; g.OW = pl.OW;
         g.pH = pl.pH; g.pW = pl.pW; g.hl = pl.hl; g.twl = pl.twl;
-        g.tx_log2 = 0;
-        while ((1 << g.tx_log2) < pl.cl)
-            ++g.tx_log2;
+        g.txn = pl.cl;
+        g.pbn = pl.pb;
         g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.pb2;
         hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes,
                            st, x, dy, part, g);

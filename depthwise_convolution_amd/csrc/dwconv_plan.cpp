@@ -178,9 +178,9 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
         return false;
     const TiledNchwVariant &v = kTiledNchwVariants[best];
     const int R = (v.kH - 1) * v.d + 1;
-    int tx = 16;                                 // threads per plane row: pow2 >= W/q, >= 16
-    while (tx < 256 && tx * v.q < pl->OW)
-        tx *= 2;
+    // threads per plane row: ceil(Wo/q), at least 16, at most 256 (wider
+    // planes take several column tiles); 256/tx planes share a workgroup
+    const int tx = std::max(16, std::min(256, ceil_div(pl->OW, v.q)));
     // staged columns of a plane row: from w0 - hl (hl = the left pad rounded
     // up to whole 16-byte loads) over the tile's tw + d*(kW-1) input columns
     const int lv = v.v4 ? 4 : 1;
@@ -348,9 +348,7 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
         return false;
     const TiledNchwVariant &v = kTiledNchwVariants[best];
     const int R = (v.kH - 1) * v.d + 1;
-    int tx = 16;                                  // threads per dy plane row
-    while (tx < 256 && tx * v.q < p.Wo)
-        tx *= 2;
+    const int tx = std::max(16, std::min(256, ceil_div(p.Wo, v.q)));   // threads per dy row
     const int lv = v.v4 ? 4 : 1;
     const int hl = v.v4 ? -((-pl->pW) & ~3) : pl->pW;
     const int span = (hl - pl->pW) + tx * v.q + v.d * (v.kW - 1);
