@@ -233,6 +233,53 @@ def per_config_table(torch, dw, iters=20):
     return rows
 
 
+def graph_leg(torch, dw, reps=20):
+    """Launch-bound small problems: one training step (forward, input
+    gradient, weight + bias gradient: 4 kernels) of the 112x112x32 3x3 NHWC
+    workload, enqueued eagerly through the binding vs replayed from a HIP
+    graph that holds `reps` steps.  Per-step time from the wall clock between
+    device synchronisations."""
+    from depthwise_convolution_amd import workloads
+    wl = workloads.WORKLOADS["mobilenet_112x112x32_3x3"]
+    layout = workloads.NHWC
+    t = make_problem(torch, wl, layout, seed=0)
+    stream = torch.cuda.Stream()
+
+    def step():
+        launch_fwd(dw, wl, t, layout, stream)
+        launch_ig(dw, wl, t, layout, stream)
+        launch_wgrad(dw, wl, t, layout, stream)
+
+    def wall(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for _ in range(n):
+                fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6
+
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            step()
+    eager_us = min(wall(step, reps) for _ in range(3)) / reps
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                step()
+    torch.cuda.synchronize()
+    g.replay()
+    graph_us = min(wall(g.replay, 1) for _ in range(5)) / reps
+    nbytes = wl.fwd_bytes() + wl.ig_bytes() + wgrad_bytes(wl)
+    del g, t
+    return {"workload": wl.name + " nhwc", "step": "fwd + ig + wgrad (4 kernels)",
+            "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+            "graph_GBs": round(nbytes / graph_us / 1e3, 1),
+            "timing": f"best of 3 (eager) / 5 (graph) runs of {reps} steps, wall clock"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +470,7 @@ def main():
                 "store, the SGD step in the weight-gradient reduction"}
     del t
     torch.cuda.empty_cache()
+    result["graph"] = graph_leg(torch, dw)
     if args.calib_copy:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
         # readings calibrate the counters of the kernels above
