@@ -120,16 +120,19 @@ constexpr int kNumTiledNchwVariants = sizeof(kTiledNchwVariants) / sizeof(kTiled
 struct Plan {
     int kind;
     int vec;            // NHWC: channels per thread (4 or 1)
-    int variant;        // tiled: index into kTiledVariants
-    int cl;             // tiled NHWC: threads across channels (8 or 16)
+    int variant;        // tiled: index into the kernel's variant table
+    int cl;             // tiled NHWC: threads across channels; tiled NCHW: threads per
+                        // plane row; generic weight gradient (NHWC): channel lanes
     int tw;             // tiled: output columns per tile
-    int th;             // tiled: output rows per workgroup
-    int nct, nwt, nst;  // tiled: channel tiles (NHWC) or plane groups (NCHW), column tiles, row tiles
-    int pb;             // tiled NCHW: planes per workgroup
+    int th;             // tiled: output rows per workgroup (one row tile)
+    int nct, nwt, nst;  // tiled: channel tiles (NHWC) or plane groups (NCHW), column tiles,
+                        // row tiles (weight gradient: strips of row tiles)
+    int pb;             // tiled NCHW: planes per workgroup (256 / cl)
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
     int hl, twl;        // tiled NCHW: staged columns left of a tile, staged floats per row
-    int pb2;            // weight gradient, tiled NCHW: row tiles per plane
-    int strip;          // weight gradient, tiled: row tiles per workgroup
+    int nrt;            // weight gradient, tiled: row tiles per image / plane
+    int strip;          // weight gradient, tiled: row tiles per strip (per workgroup)
+    int ppc, cpi;       // weight gradient, generic: dy positions per chunk; NCHW chunks per image
     long long chunks;   // weight gradient: partial sums per weight (rows of the workspace)
     long long workspace;// weight gradient: workspace bytes
     long long grid2;    // weight gradient: workgroups of the reduction kernel

@@ -1562,7 +1562,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.pH = pl.pH; g.pW = pl.pW; g.hl = pl.hl; g.twl = pl.twl;
         g.txn = pl.cl;
         g.pbn = pl.pb;
-        g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.pb2;
+        g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.nrt;
         hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes,
                            st, x, dy, part, g);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
@@ -1570,7 +1570,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;
         g.H = p.H; g.W = p.W; g.OH = pl.OH; g.OW = pl.OW;
         g.kH = p.kH; g.kW = p.kW; g.d = p.dilation; g.pH = pl.pH; g.pW = pl.pW;
-        g.cl = pl.cl; g.ncg = pl.nct; g.ppc = pl.tw; g.cpi = pl.nwt;
+        g.cl = pl.cl; g.ncg = pl.nct; g.ppc = pl.ppc; g.cpi = pl.cpi;
         const dim3 gr((unsigned)pl.grid), b(256);
         const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
         if (nhwc && p.stride == 1)

@@ -315,11 +315,11 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     pl->cl = v.cl;
     pl->tw = v.px * 256 / v.cl;
     pl->th = v.g - R + 1;
-    const int nrt = ceil_div(p.Ho, pl->th);                   // row tiles per image
+    pl->nrt = ceil_div(p.Ho, pl->th);                            // row tiles per image
     pl->nct = ceil_div(p.C, v.cl * v.vec);
     pl->nwt = ceil_div(p.Wo, pl->tw);
-    pl->strip = wgrad_strip(nrt, (long long)p.N * pl->nct * pl->nwt);
-    pl->nst = ceil_div(nrt, pl->strip);                         // strips
+    pl->strip = wgrad_strip(pl->nrt, (long long)p.N * pl->nct * pl->nwt);
+    pl->nst = ceil_div(pl->nrt, pl->strip);                      // strips
     pl->chunks = (long long)p.N * pl->nst * pl->nwt;
     pl->grid = pl->chunks * pl->nct;
     pl->block = 256;
@@ -363,9 +363,9 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     pl->th = v.g - R + 1;
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(p.Wo, pl->tw);
-    pl->pb2 = ceil_div(p.Ho, pl->th);                            // row tiles per plane
-    pl->strip = wgrad_strip(pl->pb2, (long long)pl->nct * pl->nwt);
-    pl->nst = ceil_div(pl->pb2, pl->strip);
+    pl->nrt = ceil_div(p.Ho, pl->th);                            // row tiles per plane
+    pl->strip = wgrad_strip(pl->nrt, (long long)pl->nct * pl->nwt);
+    pl->nst = ceil_div(pl->nrt, pl->strip);
     pl->chunks = (long long)p.N * pl->nwt * pl->nst;
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     const int tg = std::min(p.kH * p.kW + 1, 16);
@@ -406,8 +406,7 @@ static void plan_wgrad_direct(const Problem &p, Plan *pl)
         const long long ppc = slots * ppt;
         pl->cl = cl;
         pl->nct = (int)ncg;
-        pl->tw = (int)ppc;
-        pl->nwt = 0;
+        pl->ppc = (int)ppc;
         pl->chunks = (total + ppc - 1) / ppc;
         pl->grid = pl->chunks * ncg;
     } else {
@@ -416,13 +415,13 @@ static void plan_wgrad_direct(const Problem &p, Plan *pl)
         const long long cpi = (per_img + ppc - 1) / ppc;
         pl->cl = 256;
         pl->nct = 1;
-        pl->tw = (int)ppc;
-        pl->nwt = (int)cpi;
+        pl->ppc = (int)ppc;
+        pl->cpi = (int)cpi;
         pl->chunks = p.N * cpi;
         pl->grid = pl->chunks * co;
     }
     std::snprintf(pl->name, sizeof pl->name, "wgrad_direct_%s_s%d_cl%d_ppc%d",
-                  p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride, pl->cl, pl->tw);
+                  p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride, pl->cl, pl->ppc);
 }
 
 int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
