@@ -80,6 +80,15 @@ constexpr TiledVariant kTiledVariants[] = {
 };
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
 
+// Variants of the tiled NHWC kernel at stride 2 (same fields; the tile
+// covers the stride-1 grid, so g >= kH*d + 1 leaves at least two rows, one
+// of them even).
+constexpr TiledVariant kTiledS2Variants[] = {
+    {3, 3, 1, 4, 8, 2, 6, 4},   {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 1, 32, 1, 6, 1},
+    {5, 5, 1, 4, 8, 1, 8, 4},   {5, 5, 1, 1, 32, 1, 8, 1},
+};
+constexpr int kNumTiledS2Variants = sizeof(kTiledS2Variants) / sizeof(kTiledS2Variants[0]);
+
 // Compile-time variants of the tiled NHWC weight-gradient kernel: workgroup
 // geometry as for the forward (vec, cl, px, g, lv).  A workgroup walks a strip of
 // row tiles of g - (kH-1)*d rows (its partial sums cover them all); the
@@ -138,6 +147,8 @@ struct Plan {
     long long grid2;    // weight gradient: workgroups of the reduction kernel
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
+                        // (tiled NHWC stride-2 forward: OH, OW = the stride-1 grid it tiles)
+    int YH, YW;         // tiled NHWC: extents of the tensor written
     long long total;    // direct: number of threads doing work
     long long grid;     // workgroups
     int block;          // threads per workgroup

@@ -404,7 +404,8 @@ __global__ __launch_bounds__(256) void k_direct_nchw(const float *__restrict__ i
 // ---------------------------------------------------------------------------
 struct TiledArgs {
     int N, C;
-    int IH, IW, OH, OW;     // extents of the tensor read and the tensor written
+    int IH, IW, OH, OW;     // extents of the tensor read, and of the grid the tiles cover
+    int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
     int pH, pW;             // top / left zero padding of the tensor read
     int nct, nwt, nst;      // channel tiles, column tiles, row tiles
 };
@@ -430,14 +431,29 @@ struct TiledGeom {
     static_assert(LV == 4 || VEC == 1, "scalar staging computes one channel per thread");
 };
 
-template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int MODE>
-__global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__ in,
-                                                       const void *__restrict__ wv,
-                                                       const float *__restrict__ bias,
-                                                       float *__restrict__ out, TiledArgs a,
-                                                       EpiArgs ep)
+//
+// Stride 2 (S == 2) reuses the stride-1 walk (LeanMlir "Depthwise": the
+// stride-2 conv is the stride-1 conv kept at every other position, and its
+// input-VJP is the stride-1 reversed-kernel conv of the zero-upsampled
+// cotangent):
+//  * forward: the tiles cover the stride-1 grid 2*Ho-1 x 2*Wo-1 (pads as
+//    given), only its even rows are accumulated and only its even positions
+//    stored, at y[r/2][c/2];
+//  * input gradient: dy is zero-upsampled while it is staged (a staged
+//    position takes dy[t/2][v/2] when both are even, else zero), and staged
+//    rows that are all zero are skipped.
+template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int MODE,
+          int S>
+__global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in,
+                                                    const void *__restrict__ wv,
+                                                    const float *__restrict__ bias,
+                                                    float *__restrict__ out, TiledArgs a,
+                                                    EpiArgs ep)
 {
     constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
+    constexpr bool UPS = S == 2 && IG;        // staged input is the zero-upsampled dy
+    constexpr bool DEC = S == 2 && !IG;       // output is the decimated stride-1 grid
+    static_assert(S == 1 || S == 2, "stride 1 or 2");
     typedef TiledGeom<KH, KW, D, VEC, CL, PX, G, LV> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
     constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV, KK = Gm::KK;
@@ -498,9 +514,15 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
         const int col = rem / VPC;
         const int cv = rem - col * VPC;
         const int row = rbase + g, gc = cbase + col, ch = c0 + cv * LV;
-        const bool ok = e < VCH && g < nrows && row >= 0 && row < a.IH && gc >= 0 &&
-                        gc < a.IW && ch < a.C;
-        const int off = ok ? ((row * a.IW + gc) * a.C + ch) * 4 : kOutOfRange;
+        bool ok = e < VCH && g < nrows && row >= 0 && gc >= 0 && ch < a.C;
+        int sr = row, sc = gc;                  // position in the tensor read
+        if constexpr (UPS) {
+            ok = ok && (row & 1) == 0 && (gc & 1) == 0;
+            sr = row >> 1;
+            sc = gc >> 1;
+        }
+        ok = ok && sr < a.IH && sc < a.IW;
+        const int off = ok ? ((sr * a.IW + sc) * a.C + ch) * 4 : kOutOfRange;
         if constexpr (LV == 4)
             stage[i] = buf_f4(rx, off);
         else
@@ -548,42 +570,51 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc_s1(const float *__restrict__
 
     // 3. walk the staged rows
     constexpr int XW = PX + (KW - 1) * D;  // staged columns one thread reads per row
-    float *outp = out + (n * a.OH * a.OW) * a.C;
+    float *outp = out + (n * a.YH * a.YW) * a.C;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
-            float xv[XW][VEC];
+            // a staged row of the upsampled dy at an odd position is all zero
+            if (!(UPS && ((rbase + u) & 1))) {
+                float xv[XW][VEC];
 #pragma unroll
-            for (int i = 0; i < XW; ++i) {
-                const float *src = ldsx + ((u * TWI + p * PX + i) * CG + q * VEC);
+                for (int i = 0; i < XW; ++i) {
+                    const float *src = ldsx + ((u * TWI + p * PX + i) * CG + q * VEC);
 #pragma unroll
-                for (int v = 0; v < VEC; ++v)
-                    xv[i][v] = src[v];
-            }
+                    for (int v = 0; v < VEC; ++v)
+                        xv[i][v] = src[v];
+                }
 #pragma unroll
-            for (int kh = 0; kh < KH; ++kh) {
-                const int m = u - kh * D;          // output row this tap row feeds
-                if (m >= 0 && m < TH) {
-                    const int slot = m % R;
+                for (int kh = 0; kh < KH; ++kh) {
+                    const int m = u - kh * D;      // output row this tap row feeds
+                    if (m >= 0 && m < TH && !(DEC && ((h0 + m) & 1))) {
+                        const int slot = m % R;
 #pragma unroll
-                    for (int kw = 0; kw < KW; ++kw)
+                        for (int kw = 0; kw < KW; ++kw)
 #pragma unroll
-                        for (int j = 0; j < PX; ++j)
+                            for (int j = 0; j < PX; ++j)
 #pragma unroll
-                            for (int v = 0; v < VEC; ++v)
-                                acc[slot][j][v] =
-                                    fmaf(wr[kh][kw][v], xv[j + kw * D][v], acc[slot][j][v]);
+                                for (int v = 0; v < VEC; ++v)
+                                    acc[slot][j][v] =
+                                        fmaf(wr[kh][kw][v], xv[j + kw * D][v], acc[slot][j][v]);
+                    }
                 }
             }
             const int m = u - (R - 1);             // output row completed by row u
             if (m >= 0) {
+                const int r = h0 + m;
 #pragma unroll
                 for (int j = 0; j < PX; ++j) {
                     if constexpr (EPI)
                         epi_block(acc[m % R][j], ec, ep.act);
-                    if (cvalid && ow + j < a.OW)
-                        store_vec<VEC>(outp + ((h0 + m) * a.OW + ow + j) * a.C + cq,
-                                       acc[m % R][j]);
+                    if constexpr (DEC) {
+                        const int c = ow + j;
+                        if (cvalid && (r & 1) == 0 && (c & 1) == 0 && (c >> 1) < a.YW)
+                            store_vec<VEC>(outp + (((r >> 1) * a.YW + (c >> 1)) * a.C + cq),
+                                           acc[m % R][j]);
+                    } else if (cvalid && ow + j < a.OW) {
+                        store_vec<VEC>(outp + ((r * a.OW + ow + j) * a.C + cq), acc[m % R][j]);
+                    }
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)
                         acc[m % R][j][v] = bv[v];
@@ -1343,34 +1374,40 @@ void launch_direct(const Problem &p, const Plan &pl, const float *in, const void
 typedef void (*TiledFn)(const float *, const void *, const float *, float *, TiledArgs,
                         EpiArgs);
 
-// Kernel table of the tiled NHWC kernel: [variant][f16 weights][mode].
-template <typename WT, int V, int MODE>
+// Kernel tables of the tiled NHWC kernel: [variant][f16 weights][mode], one
+// per stride (the stride-2 table is built from its own variant list).
+template <typename WT, int V, int MODE, int S>
 constexpr TiledFn tiled_fn()
 {
-    constexpr TiledVariant t = kTiledVariants[V];
-    return &k_tiled_nhwc_s1<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE>;
+    constexpr TiledVariant t = S == 1 ? kTiledVariants[V] : kTiledS2Variants[V];
+    return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, S>;
 }
 
-template <int V>
+template <int V, int S>
 void fill_tiled(TiledFn (&row)[2][3])
 {
-    row[0][0] = tiled_fn<float, V, kModeFwd>();
-    row[0][1] = tiled_fn<float, V, kModeInputGrad>();
-    row[0][2] = tiled_fn<float, V, kModeFwdEpilogue>();
-    row[1][0] = tiled_fn<half_t, V, kModeFwd>();
-    row[1][1] = tiled_fn<half_t, V, kModeInputGrad>();
-    row[1][2] = tiled_fn<half_t, V, kModeFwdEpilogue>();
+    row[0][0] = tiled_fn<float, V, kModeFwd, S>();
+    row[0][1] = tiled_fn<float, V, kModeInputGrad, S>();
+    row[0][2] = tiled_fn<float, V, kModeFwdEpilogue, S>();
+    row[1][0] = tiled_fn<half_t, V, kModeFwd, S>();
+    row[1][1] = tiled_fn<half_t, V, kModeInputGrad, S>();
+    row[1][2] = tiled_fn<half_t, V, kModeFwdEpilogue, S>();
 }
 
-template <int... Vs>
-void fill_all_tiled(TiledFn (&fn)[kNumTiledVariants][2][3], std::integer_sequence<int, Vs...>)
+template <int S, int NVAR, int... Vs>
+void fill_all_tiled(TiledFn (&fn)[NVAR][2][3], std::integer_sequence<int, Vs...>)
 {
-    (fill_tiled<Vs>(fn[Vs]), ...);
+    (fill_tiled<Vs, S>(fn[Vs]), ...);
 }
 
 struct TiledTable {
     TiledFn fn[kNumTiledVariants][2][3];
-    TiledTable() { fill_all_tiled(fn, std::make_integer_sequence<int, kNumTiledVariants>()); }
+    TiledFn fn2[kNumTiledS2Variants][2][3];
+    TiledTable()
+    {
+        fill_all_tiled<1>(fn, std::make_integer_sequence<int, kNumTiledVariants>());
+        fill_all_tiled<2>(fn2, std::make_integer_sequence<int, kNumTiledS2Variants>());
+    }
 };
 
 int mode_of(const Problem &p, const EpiArgs &ep)
@@ -1384,12 +1421,15 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
                       const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     static const TiledTable table;
-    if (pl.variant < 0 || pl.variant >= kNumTiledVariants)
+    const int nvar = p.stride == 1 ? kNumTiledVariants : kNumTiledS2Variants;
+    if (pl.variant < 0 || pl.variant >= nvar)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    TiledFn f = p.stride == 1 ? table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)]
+                              : table.fn2[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
     TiledArgs a;
     a.N = p.N; a.C = p.C;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,

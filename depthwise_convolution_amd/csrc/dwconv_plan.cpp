@@ -111,8 +111,10 @@ static void set_extents(const Problem &p, Plan *pl)
 
 static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
+    if (p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
         return false;
+    const TiledVariant *table = p.stride == 1 ? kTiledVariants : kTiledS2Variants;
+    const int nvar = p.stride == 1 ? kNumTiledVariants : kNumTiledS2Variants;
     const bool v4ok = p.C % 4 == 0 && (ptr_bits & 15u) == 0;   // 16-byte staging loads
     // buffer-load byte offsets are 31-bit: one image and the weights must fit
     if (4LL * pl->IH * pl->IW * p.C >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
@@ -121,8 +123,8 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     // channel tile the problem fills to at least 3/4; else the one it fills best
     int best = -1;
     double best_fill = -1.0;
-    for (int i = 0; i < kNumTiledVariants; ++i) {
-        const TiledVariant &v = kTiledVariants[i];
+    for (int i = 0; i < nvar; ++i) {
+        const TiledVariant &v = table[i];
         if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation || (v.lv == 4 && !v4ok))
             continue;
         const int cg = v.cl * v.vec;
@@ -138,7 +140,7 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     }
     if (best < 0)
         return false;
-    const TiledVariant &v = kTiledVariants[best];
+    const TiledVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
     pl->kind = KIND_TILED_NHWC;
     pl->variant = best;
@@ -146,14 +148,22 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->cl = v.cl;
     pl->tw = v.px * 256 / v.cl;
     pl->th = v.g - R + 1;
+    // the grid the tiles cover: the output, except at stride 2 forward, where
+    // it is the stride-1 grid (2*Ho-1 x 2*Wo-1) whose even positions are kept
+    pl->YH = pl->OH;
+    pl->YW = pl->OW;
+    if (p.stride == 2 && p.op != DWCONV_OP_INPUT_GRAD) {
+        pl->OH = 2 * pl->OH - 1;
+        pl->OW = 2 * pl->OW - 1;
+    }
     pl->nct = ceil_div(p.C, v.cl * v.vec);
     pl->nwt = ceil_div(pl->OW, pl->tw);
     pl->nst = ceil_div(pl->OH, pl->th);
     pl->grid = (long long)p.N * pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_%s_%s",
-                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "", op_tag(p),
-                  p.wtype ? "f16w" : "f32w");
+    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s%d_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_%s_%s",
+                  p.stride, v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "",
+                  op_tag(p), p.wtype ? "f16w" : "f32w");
     return true;
 }
 

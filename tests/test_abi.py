@@ -130,7 +130,9 @@ def test_describe_selects_kernels():
     name, _, _ = dw.dwconv2d_describe(dw.OP_INPUT_GRAD, 1, 512, 512, 256, 3, 3)
     assert name.startswith("tiled_nhwc_s1_k3x3_d1") and name.endswith("_ig_f32w")
     name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 224, 224, 32, 3, 3, stride=2)
-    assert name.startswith("direct_nhwc_s2")
+    assert name.startswith("tiled_nhwc_s2")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 224, 224, 32, 7, 7, stride=2)
+    assert name.startswith("direct_nhwc_s2")             # no stride-2 7x7 variant
     name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 30, 19, 131, 7, 7)
     assert name.startswith("tiled_nhwc_s1_k7x7") and "_l1_" in name   # C % 4 != 0: 4-byte staging
     name, _, _ = dw.dwconv2d_describe(dw.OP_FWD, 1, 30, 19, 131, 9, 9)
@@ -324,7 +326,10 @@ def test_describe_ex_plans():
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 224, 224, 32, 3, 3, stride=2,
                                          pads=dw.dwconv2d_same_pads(dw.PAD_XLA_SAME, 224, 224,
                                                                     3, 3, 2))
-    assert name.startswith("direct_nhwc_s2")
+    assert name.startswith("tiled_nhwc_s2")
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 224, 224, 32, 3, 3, stride=2,
+                                         pads=(0, 1, 0, 1), layout=dw.NCHW)
+    assert name.startswith("direct_nchw_s2")
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, 1, 64, 64, 32, 3, 3,
                                          pads=(0, 2, 2, 0))
     assert name.startswith("wgrad_tiled_nhwc")
