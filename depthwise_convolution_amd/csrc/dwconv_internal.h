@@ -126,6 +126,15 @@ constexpr TiledNchwVariant kTiledNchwVariants[] = {
 };
 constexpr int kNumTiledNchwVariants = sizeof(kTiledNchwVariants) / sizeof(kTiledNchwVariants[0]);
 
+// Variants of the tiled NCHW kernel at stride 2 (the tile covers the
+// stride-1 grid; the input gradient stages with 4-byte loads, v4 = 0).
+constexpr TiledNchwVariant kTiledNchwS2Variants[] = {
+    {3, 3, 1, 2, 8, 1}, {3, 3, 1, 2, 8, 0},
+    {5, 5, 1, 2, 12, 1}, {5, 5, 1, 2, 12, 0},
+};
+constexpr int kNumTiledNchwS2Variants =
+    sizeof(kTiledNchwS2Variants) / sizeof(kTiledNchwS2Variants[0]);
+
 struct Plan {
     int kind;
     int vec;            // NHWC: channels per thread (4 or 1)
@@ -148,7 +157,7 @@ struct Plan {
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
                         // (tiled NHWC stride-2 forward: OH, OW = the stride-1 grid it tiles)
-    int YH, YW;         // tiled NHWC: extents of the tensor written
+    int YH, YW;         // tiled: extents of the tensor written
     long long total;    // direct: number of threads doing work
     long long grid;     // workgroups
     int block;          // threads per workgroup

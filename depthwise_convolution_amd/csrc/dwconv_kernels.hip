@@ -640,7 +640,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
 // ---------------------------------------------------------------------------
 struct TiledNchwArgs {
     int planes, C;
-    int IH, IW, OH, OW;     // extents of the tensor read and the tensor written
+    int IH, IW, OH, OW;     // extents of the tensor read, and of the grid the tiles cover
+    int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
     int pH, pW;             // top / left zero padding of the tensor read
     int hl, twl;            // staged columns left of a tile; staged floats per plane row
     int txn, pbn;           // threads per plane row (16..256), planes per workgroup (256 / txn)
@@ -663,14 +664,20 @@ struct NchwGeom {
     static_assert(TH >= 1, "a workgroup must produce at least one output row");
 };
 
-template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, int MODE>
-__global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__ in,
-                                                       const void *__restrict__ wv,
-                                                       const float *__restrict__ bias,
-                                                       float *__restrict__ out, TiledNchwArgs a,
-                                                       EpiArgs ep)
+// Stride 2 (S == 2) as in the NHWC kernel: the forward tiles the stride-1
+// grid and keeps its even positions, the input gradient stages dy
+// zero-upsampled (4-byte loads only) and skips the all-zero rows.
+template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, int MODE, int S>
+__global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in,
+                                                    const void *__restrict__ wv,
+                                                    const float *__restrict__ bias,
+                                                    float *__restrict__ out, TiledNchwArgs a,
+                                                    EpiArgs ep)
 {
     constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
+    constexpr bool UPS = S == 2 && IG;        // staged input is the zero-upsampled dy
+    constexpr bool DEC = S == 2 && !IG;       // output is the decimated stride-1 grid
+    static_assert(!(UPS && V4), "upsampled staging uses 4-byte loads");
     typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV;
     constexpr int NV = Gm::NV, NW = Gm::NW;
@@ -725,9 +732,15 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
         const int g = rem / vpr;
         const int col = cbase + (rem - g * vpr) * LV;
         const int plane = pg * pbn + pl, row = rbase + g;
-        const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && row < a.IH &&
-                        col >= 0 && col < a.IW;
-        const int off = ok ? ((plane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
+        bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && col >= 0;
+        int sr = row, sc = col;                        // position in the tensor read
+        if constexpr (UPS) {
+            ok = ok && (row & 1) == 0 && (col & 1) == 0;
+            sr = row >> 1;
+            sc = col >> 1;
+        }
+        ok = ok && sr < a.IH && sc < a.IW;
+        const int off = ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange;
         if constexpr (V4) {
             const float4 v = buf_f4(rx, off);
             sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
@@ -774,25 +787,28 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
     constexpr int XW = Q + (KW - 1) * D;
     const float *rowbase = lds + pli * G * twl + tx * Q + (a.hl - a.pW);
     const int oc = w0 + tx * Q;                        // first output column of this thread
-    float *outp = out + my_plane * a.OH * a.OW;
-    const bool vec_store = (Q > 1) && (a.OW % Q == 0);
+    float *outp = out + my_plane * a.YH * a.YW;
+    const bool vec_store = !DEC && (Q > 1) && (a.OW % Q == 0);
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
-            float xv[XW];
+            // a staged row of the upsampled dy at an odd position is all zero
+            if (!(UPS && ((rbase + u) & 1))) {
+                float xv[XW];
 #pragma unroll
-            for (int i = 0; i < XW; ++i)
-                xv[i] = rowbase[u * twl + i];
+                for (int i = 0; i < XW; ++i)
+                    xv[i] = rowbase[u * twl + i];
 #pragma unroll
-            for (int kh = 0; kh < KH; ++kh) {
-                const int m = u - kh * D;
-                if (m >= 0 && m < TH) {
-                    const int slot = m % R;
+                for (int kh = 0; kh < KH; ++kh) {
+                    const int m = u - kh * D;
+                    if (m >= 0 && m < TH && !(DEC && ((h0 + m) & 1))) {
+                        const int slot = m % R;
 #pragma unroll
-                    for (int kw = 0; kw < KW; ++kw)
+                        for (int kw = 0; kw < KW; ++kw)
 #pragma unroll
-                        for (int j = 0; j < Q; ++j)
-                            acc[slot][j] = fmaf(wr[kh][kw], xv[j + kw * D], acc[slot][j]);
+                            for (int j = 0; j < Q; ++j)
+                                acc[slot][j] = fmaf(wr[kh][kw], xv[j + kw * D], acc[slot][j]);
+                    }
                 }
             }
             const int m = u - (R - 1);
@@ -801,8 +817,19 @@ __global__ __launch_bounds__(256) void k_tiled_nchw_s1(const float *__restrict__
                     const EpiChan e1[1] = {ec};
                     epi_block(acc[m % R], e1, ep.act);
                 }
-                float *dst = outp + (h0 + m) * a.OW + oc;
-                if (pvalid) {
+                const int r = h0 + m;
+                float *dst = outp + r * a.OW + oc;
+                if constexpr (DEC) {
+                    if (pvalid && (r & 1) == 0) {
+#pragma unroll
+                        for (int j = 0; j < Q; ++j) {
+                            const int c = oc + j;
+                            if ((c & 1) == 0 && (c >> 1) < a.YW)
+                                __builtin_nontemporal_store(
+                                    acc[m % R][j], outp + (r >> 1) * a.YW + (c >> 1));
+                        }
+                    }
+                } else if (pvalid) {
                     if (vec_store && oc < a.OW) {
                         store_vec<Q>(dst, acc[m % R]);
                     } else {
@@ -1379,8 +1406,13 @@ typedef void (*TiledFn)(const float *, const void *, const float *, float *, Til
 template <typename WT, int V, int MODE, int S>
 constexpr TiledFn tiled_fn()
 {
-    constexpr TiledVariant t = S == 1 ? kTiledVariants[V] : kTiledS2Variants[V];
-    return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, S>;
+    if constexpr (S == 1) {
+        constexpr TiledVariant t = kTiledVariants[V];
+        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 1>;
+    } else {
+        constexpr TiledVariant t = kTiledS2Variants[V];
+        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 2>;
+    }
 }
 
 template <int V, int S>
@@ -1440,36 +1472,45 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
 typedef void (*TiledNchwFn)(const float *, const void *, const float *, float *, TiledNchwArgs,
                             EpiArgs);
 
-template <typename WT, int V, int MODE>
+template <typename WT, int V, int MODE, int S>
 constexpr TiledNchwFn tiled_nchw_fn()
 {
-    constexpr TiledNchwVariant t = kTiledNchwVariants[V];
-    return &k_tiled_nchw_s1<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), MODE>;
+    if constexpr (S == 1) {
+        constexpr TiledNchwVariant t = kTiledNchwVariants[V];
+        return &k_tiled_nchw<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), MODE, 1>;
+    } else {
+        constexpr TiledNchwVariant t = kTiledNchwS2Variants[V];
+        if constexpr (MODE == kModeInputGrad && t.v4 != 0)
+            return nullptr;             // upsampled staging has no 16-byte form
+        else
+            return &k_tiled_nchw<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), MODE, 2>;
+    }
 }
 
-template <int V>
+template <int V, int S>
 void fill_tiled_nchw(TiledNchwFn (&row)[2][3])
 {
-    row[0][0] = tiled_nchw_fn<float, V, kModeFwd>();
-    row[0][1] = tiled_nchw_fn<float, V, kModeInputGrad>();
-    row[0][2] = tiled_nchw_fn<float, V, kModeFwdEpilogue>();
-    row[1][0] = tiled_nchw_fn<half_t, V, kModeFwd>();
-    row[1][1] = tiled_nchw_fn<half_t, V, kModeInputGrad>();
-    row[1][2] = tiled_nchw_fn<half_t, V, kModeFwdEpilogue>();
+    row[0][0] = tiled_nchw_fn<float, V, kModeFwd, S>();
+    row[0][1] = tiled_nchw_fn<float, V, kModeInputGrad, S>();
+    row[0][2] = tiled_nchw_fn<float, V, kModeFwdEpilogue, S>();
+    row[1][0] = tiled_nchw_fn<half_t, V, kModeFwd, S>();
+    row[1][1] = tiled_nchw_fn<half_t, V, kModeInputGrad, S>();
+    row[1][2] = tiled_nchw_fn<half_t, V, kModeFwdEpilogue, S>();
 }
 
-template <int... Vs>
-void fill_all_tiled_nchw(TiledNchwFn (&fn)[kNumTiledNchwVariants][2][3],
-                         std::integer_sequence<int, Vs...>)
+template <int S, int NVAR, int... Vs>
+void fill_all_tiled_nchw(TiledNchwFn (&fn)[NVAR][2][3], std::integer_sequence<int, Vs...>)
 {
-    (fill_tiled_nchw<Vs>(fn[Vs]), ...);
+    (fill_tiled_nchw<Vs, S>(fn[Vs]), ...);
 }
 
 struct TiledNchwTable {
     TiledNchwFn fn[kNumTiledNchwVariants][2][3];
+    TiledNchwFn fn2[kNumTiledNchwS2Variants][2][3];
     TiledNchwTable()
     {
-        fill_all_tiled_nchw(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+        fill_all_tiled_nchw<1>(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+        fill_all_tiled_nchw<2>(fn2, std::make_integer_sequence<int, kNumTiledNchwS2Variants>());
     }
 };
 
@@ -1477,13 +1518,19 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
                       const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     static const TiledNchwTable table;
-    if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
+    const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumTiledNchwS2Variants;
+    if (pl.variant < 0 || pl.variant >= nvar || pl.cl < 16 || pl.cl > 256 ||
         pl.pb != 256 / pl.cl)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    TiledNchwFn f = p.stride == 1
+                        ? table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)]
+                        : table.fn2[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    if (!f)
+        return DWCONV_ERR_BAD_STRATEGY;
     TiledNchwArgs a;
     a.planes = p.N * p.C; a.C = p.C;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW; a.hl = pl.hl; a.twl = pl.twl;
     a.txn = pl.cl;
     a.pbn = pl.pb;

@@ -169,16 +169,21 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 
 static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NCHW)
+    if (p.mult != 1 || p.layout != DWCONV_LAYOUT_NCHW)
         return false;
     // buffer-load byte offsets are 31-bit: the tensor read and the weights must fit
     const long long planes = (long long)p.N * p.C;
     if (4LL * planes * pl->IH * pl->IW >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
         return false;
-    const bool v4ok = pl->IW % 4 == 0 && (ptr_bits & 15u) == 0;
+    const TiledNchwVariant *table = p.stride == 1 ? kTiledNchwVariants : kTiledNchwS2Variants;
+    const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumTiledNchwS2Variants;
+    // 16-byte staging loads need whole aligned rows; the stride-2 input
+    // gradient stages the zero-upsampled dy element by element
+    const bool v4ok = pl->IW % 4 == 0 && (ptr_bits & 15u) == 0 &&
+                      !(p.stride == 2 && p.op == DWCONV_OP_INPUT_GRAD);
     int best = -1;
-    for (int i = 0; i < kNumTiledNchwVariants; ++i) {
-        const TiledNchwVariant &v = kTiledNchwVariants[i];
+    for (int i = 0; i < nvar; ++i) {
+        const TiledNchwVariant &v = table[i];
         if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation && (v.v4 == 0 || v4ok)) {
             best = i;
             break;
@@ -186,8 +191,16 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     }
     if (best < 0)
         return false;
-    const TiledNchwVariant &v = kTiledNchwVariants[best];
+    const TiledNchwVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
+    // the grid the tiles cover: the output, except at stride 2 forward, where
+    // it is the stride-1 grid (2*Ho-1 x 2*Wo-1) whose even positions are kept
+    pl->YH = pl->OH;
+    pl->YW = pl->OW;
+    if (p.stride == 2 && p.op != DWCONV_OP_INPUT_GRAD) {
+        pl->OH = 2 * pl->OH - 1;
+        pl->OW = 2 * pl->OW - 1;
+    }
     // threads per plane row: ceil(Wo/q), at least 16, at most 256 (wider
     // planes take several column tiles); 256/tx planes share a workgroup
     const int tx = std::max(16, std::min(256, ceil_div(pl->OW, v.q)));
@@ -211,8 +224,8 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->lds_bytes = 4 * (pl->pb * v.g * pl->twl + pl->pb * v.kH * v.kW);
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s1_k%dx%d_d%d_q%d_g%d_%s_tx%d_%s_%s",
-                  v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, op_tag(p),
+    std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s%d_k%dx%d_d%d_q%d_g%d_%s_tx%d_%s_%s",
+                  p.stride, v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, op_tag(p),
                   p.wtype ? "f16w" : "f32w");
     return true;
 }

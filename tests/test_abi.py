@@ -306,9 +306,9 @@ def test_same_pads_and_out_extents():
 
 
 def test_describe_ex_plans():
-    """Same plans as the SAME entry points for SAME pads; tiled kernels at
-    stride 1 with any pads; direct kernels for a multiplier; even kernels
-    run direct."""
+    """Same plans as the SAME entry points for SAME pads; tiled kernels with
+    any pads; direct kernels for a multiplier and for shapes without a tile;
+    even kernels run direct."""
     same = dw.dwconv2d_describe(dw.OP_FWD, 1, 512, 512, 256, 3, 3)
     assert dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 512, 512, 256, 3, 3, pads=(1, 1, 1, 1)) == same
     name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 512, 512, 256, 3, 3, pads=(0, 0, 0, 0))
@@ -329,7 +329,10 @@ def test_describe_ex_plans():
     assert name.startswith("tiled_nhwc_s2")
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 224, 224, 32, 3, 3, stride=2,
                                          pads=(0, 1, 0, 1), layout=dw.NCHW)
-    assert name.startswith("direct_nchw_s2")
+    assert name.startswith("tiled_nchw_s2") and "_v1_" in name   # upsampled: 4-byte staging
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 56, 56, 32, 7, 7, stride=2,
+                                         pads=(3, 3, 3, 3), layout=dw.NCHW)
+    assert name.startswith("direct_nchw_s2")                     # no stride-2 7x7 tile
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, 1, 64, 64, 32, 3, 3,
                                          pads=(0, 2, 2, 0))
     assert name.startswith("wgrad_tiled_nhwc")
