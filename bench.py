@@ -171,9 +171,10 @@ def time_kernel(torch, fn, stream, iters, flush=None):
     return times
 
 
-def cpu_baseline(wl, rows=None):
+def cpu_baseline(wl, rows=None, min_seconds=10.0):
     """The oracle (as it stands) on the first `rows` rows of the workload's
-    image, forward and input gradient, scaled to the whole step."""
+    image, forward and input gradient, repeated until about `min_seconds` of
+    CPU work; the mean pass is scaled to the whole step."""
     import oracle
     from depthwise_convolution_amd import workloads
     rows = wl.H if rows is None else rows
@@ -181,19 +182,25 @@ def cpu_baseline(wl, rows=None):
                              kW=wl.kW, stride=wl.stride, dilation=wl.dilation)
     inp = workloads.make_inputs(sub, workloads.NHWC, seed=0)
     threads = max(1, min(16, os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    oracle.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, workloads.NHWC,
-               nthreads=threads)
-    oracle.input_grad(inp["dy"], inp["w"], rows, wl.W, wl.stride, wl.dilation, workloads.NHWC,
-                      nthreads=threads)
-    dt = time.perf_counter() - t0
+    reps, total = 0, 0.0
+    while reps == 0 or total < min_seconds:
+        t0 = time.perf_counter()
+        oracle.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, workloads.NHWC,
+                   nthreads=threads)
+        oracle.input_grad(inp["dy"], inp["w"], rows, wl.W, wl.stride, wl.dilation,
+                          workloads.NHWC, nthreads=threads)
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
     scale = wl.H / rows
     step_s = dt * scale
     gbs = (wl.fwd_bytes() + wl.ig_bytes()) / step_s / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image ({rows / wl.H:.3g} of "
-                      f"the outputs), forward + input gradient, fp64 oracle, time scaled x{scale:g}",
-            "sample_seconds": round(dt, 3), "ms_per_step_est": round(step_s * 1e3, 1)}
+                      f"the outputs), forward + input gradient, fp64 oracle, mean of {reps} "
+                      f"passes, time scaled x{scale:g}",
+            "sample_seconds": round(total, 3), "passes": reps,
+            "ms_per_step_est": round(step_s * 1e3, 1)}
 
 
 def per_config_table(torch, dw, iters=20):
