@@ -65,6 +65,15 @@ def lib():
         raise RuntimeError(
             f"libdwconv.so not found at {LIB_PATH}: build it first "
             "(python -c 'import __graft_entry__ as g; g.build()'); there is no fallback path")
+    # torch carries its own copy of the HIP runtime.  Importing it first makes
+    # this library bind to that copy (same soname), so torch's streams and
+    # allocations are valid in its launches; loaded the other way round the
+    # process would hold two HIP runtimes, and a launch on a torch stream
+    # would be rejected by the wrong one.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     i, vp, ll = ctypes.c_int, ctypes.c_void_p, ctypes.c_longlong
     L.dwconv2d_fwd.argtypes = [vp, vp, i, vp, vp] + [i] * 9 + [vp]

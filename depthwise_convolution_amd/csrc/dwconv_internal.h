@@ -109,6 +109,15 @@ constexpr WgradVariant kWgradVariants[] = {
 constexpr long long kWgradTargetWorkgroups = 512;
 constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);
 
+// Variants of the tiled NHWC weight gradient at stride 2 (g = staged x rows
+// = 2*(dy rows) - 1 + (kH-1)*d).
+constexpr WgradVariant kWgradS2Variants[] = {
+    {3, 3, 1, 4, 8, 1, 7, 4},   {3, 3, 1, 4, 16, 1, 5, 4},
+    {5, 5, 1, 4, 8, 1, 7, 4},
+    {3, 3, 1, 1, 32, 1, 7, 1},  {5, 5, 1, 1, 32, 1, 7, 1},
+};
+constexpr int kNumWgradS2Variants = sizeof(kWgradS2Variants) / sizeof(kWgradS2Variants[0]);
+
 
 // Compile-time variants of the tiled NCHW kernel (same preference rule).
 // A workgroup of 256 threads covers pb planes (channels) x tx threads per
@@ -134,6 +143,15 @@ constexpr TiledNchwVariant kTiledNchwS2Variants[] = {
 };
 constexpr int kNumTiledNchwS2Variants =
     sizeof(kTiledNchwS2Variants) / sizeof(kTiledNchwS2Variants[0]);
+
+// Variants of the tiled NCHW weight gradient at stride 2 (g = staged x rows
+// = 2*(dy rows) - 1 + (kH-1)*d).
+constexpr TiledNchwVariant kWgradNchwS2Variants[] = {
+    {3, 3, 1, 2, 7, 1}, {3, 3, 1, 2, 7, 0},
+    {5, 5, 1, 2, 9, 1}, {5, 5, 1, 2, 9, 0},
+};
+constexpr int kNumWgradNchwS2Variants =
+    sizeof(kWgradNchwS2Variants) / sizeof(kWgradNchwS2Variants[0]);
 
 struct Plan {
     int kind;

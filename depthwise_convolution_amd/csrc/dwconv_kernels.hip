@@ -983,24 +983,29 @@ __global__ __launch_bounds__(256) void k_wgrad_gen(const float *__restrict__ x,
     }
 }
 
-// Stage 1, NHWC stride 1: a workgroup (256 threads: CL across channels x
-// 256/CL pixel slots of PX columns) walks `strip` row tiles of one column
-// tile.  Per row tile it stages G input rows (+ column halo) in LDS and
+// Stage 1, NHWC, stride S = 1 or 2: a workgroup (256 threads: CL across
+// channels x 256/CL pixel slots of PX dy columns) walks `strip` row tiles of
+// one column tile.  Per row tile it stages G input rows (+ column halo) in LDS and
 // loads its dy rows straight into registers (each dy element is used by one
 // thread only); every thread accumulates x*dy for all kH*kW taps of its
 // channels, and at the end the pixel slots are summed through LDS.
 // LV: floats per staging load, 4 (C % 4 == 0, 16-byte aligned tensors) or 1
-// (any C, one channel per thread).
-template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV>
+// (any C, one channel per thread).  At stride 2 a tile of TH x TW dy
+// positions reads 2*TH - 1 + (KH-1)*D rows and 2*TW - 1 + (KW-1)*D columns
+// of x, and dy position (m, j) meets x at (2m + kh*D, 2j + kw*D).
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int S>
 __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restrict__ x,
                                                           const float *__restrict__ dy,
                                                           float *__restrict__ part, WgradArgs a)
 {
     static_assert(LV == 4 || (LV == 1 && VEC == 1), "scalar staging: one channel per thread");
-    constexpr int R = (KH - 1) * D + 1, TH = G - R + 1, TW = PX * 256 / CL, CG = CL * VEC;
-    constexpr int TWI = TW + (KW - 1) * D, VPC = CG / LV, VPR = TWI * VPC, VCH = G * VPR;
-    constexpr int NV = (VCH + 255) / 256, KK = KH * KW, NP = 256 / CL;
-    constexpr int XW = PX + (KW - 1) * D;
+    static_assert(S == 1 || S == 2, "stride 1 or 2");
+    constexpr int R = (KH - 1) * D + 1, TW = PX * 256 / CL, CG = CL * VEC;
+    constexpr int TH = (G - R) / S + 1;     // dy rows per row tile
+    static_assert(G >= R && (G - R) % S == 0, "staged rows = S*(TH-1) + R");
+    constexpr int TWI = S * (TW - 1) + 1 + (KW - 1) * D, VPC = CG / LV, VPR = TWI * VPC;
+    constexpr int VCH = G * VPR, NV = (VCH + 255) / 256, KK = KH * KW, NP = 256 / CL;
+    constexpr int XW = S * (PX - 1) + 1 + (KW - 1) * D;
     constexpr int XF = VCH * LV;            // staged floats
     // the final per-(channel, tap) sums go through LDS in groups of TG taps
     constexpr int TGF = XF / (256 * VEC);
@@ -1022,7 +1027,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     const int q = tid % CL, p = tid / CL;
     const int cq = c0 + q * VEC;
     const int ow = w0 + p * PX;
-    const int cbase = w0 - a.pW;
+    const int cbase = S * w0 - a.pW;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy + n * a.OH * a.OW * a.C, a.OH * a.OW * a.C * 4);
 
@@ -1036,8 +1041,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     const int t0 = sp * a.strip, t1 = min(t0 + a.strip, (a.OH + TH - 1) / TH);
     for (int tt = t0; tt < t1; ++tt) {
         const int h0 = tt * TH;
-        const int nrows = min(TH, a.OH - h0) + R - 1;
-        const int rbase = h0 - a.pH;
+        const int nrows = S * (min(TH, a.OH - h0) - 1) + R;
+        const int rbase = S * h0 - a.pH;
         // this row tile's x rows (+ halo) and, per thread, its dy values
         typedef typename VecT<LV>::type LoadT;
         LoadT stage[NV];
@@ -1084,11 +1089,11 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
                     acc[KK][v] += gv[m][j][v];
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh) {
-                const int u = m + kh * D;   // staged row of tap row kh for output row m
+                const int u = S * m + kh * D;   // staged row of tap row kh for dy row m
                 float xv[XW][VEC];
 #pragma unroll
                 for (int i = 0; i < XW; ++i) {
-                    const float *src = lds + ((u * TWI + p * PX + i) * CG + q * VEC);
+                    const float *src = lds + ((u * TWI + S * p * PX + i) * CG + q * VEC);
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)
                         xv[i][v] = src[v];
@@ -1100,7 +1105,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
 #pragma unroll
                         for (int v = 0; v < VEC; ++v)
                             acc[kh * KW + kw][v] =
-                                fmaf(xv[j + kw * D][v], gv[m][j][v], acc[kh * KW + kw][v]);
+                                fmaf(xv[S * j + kw * D][v], gv[m][j][v], acc[kh * KW + kw][v]);
             }
         }
     }
@@ -1147,15 +1152,23 @@ struct WgradNchwArgs {
     int nrt;                    // row tiles per plane
 };
 
-template <int KH, int KW, int D, int Q, int G, bool V4>
+// At stride S = 2 a row tile of TH dy rows reads 2*TH - 1 + (kH-1)*d x rows,
+// a thread's Q dy columns meet x columns 2j + kw*d of its window, and the
+// staged x row of a tile is 2*tw - 1 + (kW-1)*d columns wide.
+template <int KH, int KW, int D, int Q, int G, bool V4, int S>
 __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restrict__ x,
                                                           const float *__restrict__ dy,
                                                           float *__restrict__ part,
                                                           WgradNchwArgs a)
 {
     typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
-    constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV, NV = Gm::NV;
-    constexpr int XW = Q + (KW - 1) * D;
+    static_assert(S == 1 || S == 2, "stride 1 or 2");
+    constexpr int R = Gm::R, KK = Gm::KK, LV = Gm::LV;
+    constexpr int TH = (G - R) / S + 1;                  // dy rows per row tile
+    static_assert(G >= R && (G - R) % S == 0, "staged rows = S*(TH-1) + R");
+    // per-thread loads for the largest staged tile: G rows x (256*S*Q + 16*EXTRA) floats
+    constexpr int NV = (G * (256 * S * Q + Gm::PBMAX * Gm::EXTRA) / LV + 255) / 256;
+    constexpr int XW = S * (Q - 1) + 1 + (KW - 1) * D;
     constexpr int TG = (KK + 1) < 16 ? (KK + 1) : 16;
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
@@ -1176,10 +1189,10 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     const bool pvalid = pli_raw < pbn && my_plane < a.planes;
     const int oc = w0 + tx * Q;
     const int CI = a.C / a.mult;
-    const int cbase = w0 - a.hl;
+    const int cbase = S * w0 - a.hl;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (a.planes / a.C) * CI * a.H * a.W * 4);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy, a.planes * a.OH * a.OW * 4);
-    const float *rowbase = lds + pli * G * twl + tx * Q + (a.hl - a.pW);
+    const float *rowbase = lds + pli * G * twl + S * tx * Q + (a.hl - a.pW);
 
     float acc[KK + 1];
 #pragma unroll
@@ -1189,8 +1202,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     const int t0 = sp * a.strip, t1 = min(t0 + a.strip, a.nrt);
     for (int tt = t0; tt < t1; ++tt) {
         const int h0 = tt * TH;
-        const int nrows = min(TH, a.OH - h0) + R - 1;
-        const int rbase = h0 - a.pH;
+        const int nrows = S * (min(TH, a.OH - h0) - 1) + R;
+        const int rbase = S * h0 - a.pH;
         float sv[NV][LV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -1244,12 +1257,13 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
                 float xv[XW];
 #pragma unroll
                 for (int i = 0; i < XW; ++i)
-                    xv[i] = rowbase[(m + kh * D) * twl + i];
+                    xv[i] = rowbase[(S * m + kh * D) * twl + i];
 #pragma unroll
                 for (int kw = 0; kw < KW; ++kw)
 #pragma unroll
                     for (int j = 0; j < Q; ++j)
-                        acc[kh * KW + kw] = fmaf(xv[j + kw * D], gv[m][j], acc[kh * KW + kw]);
+                        acc[kh * KW + kw] =
+                            fmaf(xv[S * j + kw * D], gv[m][j], acc[kh * KW + kw]);
             }
         }
     }
@@ -1542,46 +1556,63 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
 
 typedef void (*WgradFn)(const float *, const float *, float *, WgradArgs);
 
-template <int V>
+template <int V, int S>
 constexpr WgradFn wgrad_fn()
 {
-    constexpr WgradVariant t = kWgradVariants[V];
-    return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv>;
+    if constexpr (S == 1) {
+        constexpr WgradVariant t = kWgradVariants[V];
+        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 1>;
+    } else {
+        constexpr WgradVariant t = kWgradS2Variants[V];
+        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 2>;
+    }
 }
 
-template <int... Vs>
-void fill_wgrad(WgradFn (&fn)[kNumWgradVariants], std::integer_sequence<int, Vs...>)
+template <int S, int NVAR, int... Vs>
+void fill_wgrad(WgradFn (&fn)[NVAR], std::integer_sequence<int, Vs...>)
 {
-    ((fn[Vs] = wgrad_fn<Vs>()), ...);
+    ((fn[Vs] = wgrad_fn<Vs, S>()), ...);
 }
 
 struct WgradTable {
     WgradFn fn[kNumWgradVariants];
-    WgradTable() { fill_wgrad(fn, std::make_integer_sequence<int, kNumWgradVariants>()); }
+    WgradFn fn2[kNumWgradS2Variants];
+    WgradTable()
+    {
+        fill_wgrad<1>(fn, std::make_integer_sequence<int, kNumWgradVariants>());
+        fill_wgrad<2>(fn2, std::make_integer_sequence<int, kNumWgradS2Variants>());
+    }
 };
 
 }  // namespace
 
 typedef void (*WgradNchwFn)(const float *, const float *, float *, WgradNchwArgs);
 
-template <int V>
+template <int V, int S>
 constexpr WgradNchwFn wgrad_nchw_fn()
 {
-    constexpr TiledNchwVariant t = kTiledNchwVariants[V];
-    return &k_wgrad_tiled_nchw<t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0)>;
+    if constexpr (S == 1) {
+        constexpr TiledNchwVariant t = kTiledNchwVariants[V];
+        return &k_wgrad_tiled_nchw<t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), 1>;
+    } else {
+        constexpr TiledNchwVariant t = kWgradNchwS2Variants[V];
+        return &k_wgrad_tiled_nchw<t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), 2>;
+    }
 }
 
-template <int... Vs>
-void fill_wgrad_nchw(WgradNchwFn (&fn)[kNumTiledNchwVariants], std::integer_sequence<int, Vs...>)
+template <int S, int NVAR, int... Vs>
+void fill_wgrad_nchw(WgradNchwFn (&fn)[NVAR], std::integer_sequence<int, Vs...>)
 {
-    ((fn[Vs] = wgrad_nchw_fn<Vs>()), ...);
+    ((fn[Vs] = wgrad_nchw_fn<Vs, S>()), ...);
 }
 
 struct WgradNchwTable {
     WgradNchwFn fn[kNumTiledNchwVariants];
+    WgradNchwFn fn2[kNumWgradNchwS2Variants];
     WgradNchwTable()
     {
-        fill_wgrad_nchw(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+        fill_wgrad_nchw<1>(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+        fill_wgrad_nchw<2>(fn2, std::make_integer_sequence<int, kNumWgradNchwS2Variants>());
     }
 };
 
@@ -1634,13 +1665,15 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.strip = pl.strip; a.chunks = (int)pl.chunks;
     if (pl.kind == KIND_WGRAD_TILED_NHWC) {
         static const WgradTable table;
-        if (pl.variant < 0 || pl.variant >= kNumWgradVariants)
+        const int nvar = p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
+        if (pl.variant < 0 || pl.variant >= nvar)
             return DWCONV_ERR_BAD_STRATEGY;
-        hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x,
-                           dy, part, a);
+        hipLaunchKernelGGL(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
+                           dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy, part, a);
     } else if (pl.kind == KIND_WGRAD_TILED_NCHW) {
         static const WgradNchwTable table;
-        if (pl.variant < 0 || pl.variant >= kNumTiledNchwVariants || pl.cl < 16 || pl.cl > 256 ||
+        const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumWgradNchwS2Variants;
+        if (pl.variant < 0 || pl.variant >= nvar || pl.cl < 16 || pl.cl > 256 ||
             pl.pb != 256 / pl.cl)
             return DWCONV_ERR_BAD_STRATEGY;
         WgradNchwArgs g;
@@ -1650,8 +1683,8 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.txn = pl.cl;
         g.pbn = pl.pb;
         g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.nrt;
-        hipLaunchKernelGGL(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes,
-                           st, x, dy, part, g);
+        hipLaunchKernelGGL(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
+                           dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, x, dy, part, g);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
         WgradGenArgs g;
         g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;

@@ -306,15 +306,17 @@ static int wgrad_strip(int nrt, long long base)
 
 static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
+    if (p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
         return false;
     const bool v4ok = p.C % 4 == 0 && (ptr_bits & 15u) == 0;   // 16-byte staging loads
     if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.Ho * p.Wo * p.C >= (1LL << 31))
         return false;
+    const WgradVariant *table = p.stride == 1 ? kWgradVariants : kWgradS2Variants;
+    const int nvar = p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
     int best = -1;
     double best_fill = -1.0;
-    for (int i = 0; i < kNumWgradVariants; ++i) {
-        const WgradVariant &v = kWgradVariants[i];
+    for (int i = 0; i < nvar; ++i) {
+        const WgradVariant &v = table[i];
         if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation || (v.lv == 4 && !v4ok))
             continue;
         const int cg = v.cl * v.vec;
@@ -330,14 +332,14 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     }
     if (best < 0)
         return false;
-    const WgradVariant &v = kWgradVariants[best];
+    const WgradVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
     pl->kind = KIND_WGRAD_TILED_NHWC;
     pl->variant = best;
     pl->vec = v.vec;
     pl->cl = v.cl;
-    pl->tw = v.px * 256 / v.cl;
-    pl->th = v.g - R + 1;
+    pl->tw = v.px * 256 / v.cl;                                  // dy columns per tile
+    pl->th = (v.g - R) / p.stride + 1;                           // dy rows per row tile
     pl->nrt = ceil_div(p.Ho, pl->th);                            // row tiles per image
     pl->nct = ceil_div(p.C, v.cl * v.vec);
     pl->nwt = ceil_div(p.Wo, pl->tw);
@@ -346,22 +348,25 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     pl->chunks = (long long)p.N * pl->nst * pl->nwt;
     pl->grid = pl->chunks * pl->nct;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s1_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_s%d",
-                  v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "", pl->strip);
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s%d_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_s%d",
+                  p.stride, v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "",
+                  pl->strip);
     return true;
 }
 
 static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.stride != 1 || p.layout != DWCONV_LAYOUT_NCHW)
+    if (p.layout != DWCONV_LAYOUT_NCHW)
         return false;
     const long long co = (long long)p.mult * p.C, planes = p.N * co;
     if (4LL * p.N * p.C * p.H * p.W >= (1LL << 31) || 4LL * planes * p.Ho * p.Wo >= (1LL << 31))
         return false;
+    const TiledNchwVariant *table = p.stride == 1 ? kTiledNchwVariants : kWgradNchwS2Variants;
+    const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumWgradNchwS2Variants;
     const bool v4ok = p.W % 4 == 0 && (ptr_bits & 15u) == 0;
     int best = -1;
-    for (int i = 0; i < kNumTiledNchwVariants; ++i) {
-        const TiledNchwVariant &v = kTiledNchwVariants[i];
+    for (int i = 0; i < nvar; ++i) {
+        const TiledNchwVariant &v = table[i];
         if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation && (v.v4 == 0 || v4ok)) {
             best = i;
             break;
@@ -369,12 +374,14 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     }
     if (best < 0)
         return false;
-    const TiledNchwVariant &v = kTiledNchwVariants[best];
+    const TiledNchwVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
     const int tx = std::max(16, std::min(256, ceil_div(p.Wo, v.q)));   // threads per dy row
     const int lv = v.v4 ? 4 : 1;
     const int hl = v.v4 ? -((-pl->pW) & ~3) : pl->pW;
-    const int span = (hl - pl->pW) + tx * v.q + v.d * (v.kW - 1);
+    // staged x columns of a row: the left alignment, then the s*(tw-1) + 1
+    // columns the tile's dy columns meet, then the window's d*(kW-1)
+    const int span = (hl - pl->pW) + p.stride * (tx * v.q - 1) + 1 + v.d * (v.kW - 1);
     pl->kind = KIND_WGRAD_TILED_NCHW;
     pl->variant = best;
     pl->vec = 1;
@@ -383,7 +390,7 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     pl->tw = tx * v.q;
     pl->hl = hl;
     pl->twl = (span + lv - 1) / lv * lv;
-    pl->th = v.g - R + 1;
+    pl->th = (v.g - R) / p.stride + 1;                           // dy rows per row tile
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(p.Wo, pl->tw);
     pl->nrt = ceil_div(p.Ho, pl->th);                            // row tiles per plane
@@ -394,8 +401,8 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     const int tg = std::min(p.kH * p.kW + 1, 16);
     pl->lds_bytes = 4 * std::max(pl->pb * v.g * pl->twl, tg * 256);
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nchw_s1_k%dx%d_d%d_q%d_g%d_%s_tx%d_s%d",
-                  v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, pl->strip);
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nchw_s%d_k%dx%d_d%d_q%d_g%d_%s_tx%d_s%d",
+                  p.stride, v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, pl->strip);
     return true;
 }
 

@@ -219,10 +219,15 @@ def test_weight_grad_workspace_and_plans():
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7)
     assert name.startswith("wgrad_tiled_nhwc") and "_l1_" in name    # any C, 4-byte staging
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 3, 3, stride=2)
-    assert name.startswith("wgrad_direct_nhwc_s2")
+    assert name.startswith("wgrad_tiled_nhwc_s2")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 7, 7, stride=2)
+    assert name.startswith("wgrad_direct_nhwc_s2")                  # no stride-2 7x7 tile
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 3, 3, layout=dw.NCHW)
     assert name.startswith("wgrad_tiled_nchw_s1")
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 3, 3, stride=2,
+                                      layout=dw.NCHW)
+    assert name.startswith("wgrad_tiled_nchw_s2")
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 2, 9, 9, 5, 7, 7, stride=2,
                                       layout=dw.NCHW)
     assert name.startswith("wgrad_direct_nchw_s2")
     with pytest.raises(dw.DwconvError) as e:
@@ -405,3 +410,18 @@ def _sgd(L, x=X, dy=B, w=Y, b=WP, lr=0.1, dw=0, db=0, ws=WS, ws_bytes=1 << 30, C
 ])
 def test_weight_grad_sgd_rejects(L, kwargs, code):
     assert _sgd(L, **kwargs) == code
+
+
+def test_binding_shares_torch_hip_runtime():
+    """Loading the library through the binding before anything imports torch
+    must still leave one HIP runtime in the process (the one torch uses), so
+    that torch's streams and pointers are valid in the library's launches."""
+    import subprocess
+    import sys
+    code = ("import depthwise_convolution_amd as dw; dw.lib(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
