@@ -680,7 +680,13 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     static_assert(!(UPS && V4), "upsampled staging uses 4-byte loads");
     typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV;
-    constexpr int NV = Gm::NV, NW = Gm::NW;
+    constexpr int NW = Gm::NW;
+    // loads per thread: the whole tile, or with the upsampled dy only its
+    // even rows, one dy element per pair of staged columns (the twl/2 pairs
+    // of a row: twl is even then)
+    constexpr int NV = UPS ? ((G + 1) / 2 * ((256 * Q + Gm::PBMAX * Gm::EXTRA) / 2 + Gm::PBMAX) +
+                              255) / 256
+                           : Gm::NV;
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
     const WT *w = reinterpret_cast<const WT *>(wv);
@@ -724,28 +730,38 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     if constexpr (EPI)
         ec = epi_load(ep, pvalid ? my_plane % a.C : a.C, a.C);
     float sv[NV][LV];
+    // upsampled staging: rows g0, g0+2, ... of the tile are the even
+    // (upsampled) rows; a pair k of staged columns (2k, 2k+1) holds one dy
+    // element at its even column and a zero at the other
+    const int g0 = rbase & 1, ge_n = (G - g0 + 1) / 2, hp = twl / 2, c1 = cbase & 1;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
-        const int pl = e / (G * vpr);
-        const int rem = e - pl * (G * vpr);
-        const int g = rem / vpr;
-        const int col = cbase + (rem - g * vpr) * LV;
-        const int plane = pg * pbn + pl, row = rbase + g;
-        bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && col >= 0;
-        int sr = row, sc = col;                        // position in the tensor read
         if constexpr (UPS) {
-            ok = ok && (row & 1) == 0 && (col & 1) == 0;
-            sr = row >> 1;
-            sc = col >> 1;
-        }
-        ok = ok && sr < a.IH && sc < a.IW;
-        const int off = ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange;
-        if constexpr (V4) {
-            const float4 v = buf_f4(rx, off);
-            sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
+            const int pl = e / (ge_n * hp);
+            const int rem = e - pl * (ge_n * hp);
+            const int ge = rem / hp, k = rem - ge * hp;
+            const int g = g0 + 2 * ge;
+            const int plane = pg * pbn + pl, row = rbase + g, col = cbase + 2 * k + c1;
+            const int sr = row >> 1, sc = col >> 1;    // position in dy (row, col are even)
+            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
+                            col >= 0 && sr < a.IH && sc < a.IW;
+            sv[i][0] = buf_f32(rx, ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange);
         } else {
-            sv[i][0] = buf_f32(rx, off);
+            const int pl = e / (G * vpr);
+            const int rem = e - pl * (G * vpr);
+            const int g = rem / vpr;
+            const int col = cbase + (rem - g * vpr) * LV;
+            const int plane = pg * pbn + pl, row = rbase + g;
+            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
+                            row < a.IH && col >= 0 && col < a.IW;
+            const int off = ok ? ((plane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
+            if constexpr (V4) {
+                const float4 v = buf_f4(rx, off);
+                sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
+            } else {
+                sv[i][0] = buf_f32(rx, off);
+            }
         }
     }
     // 2. into LDS
@@ -758,7 +774,15 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
-        if (e < pbn * G * vpr) {
+        if constexpr (UPS) {
+            if (e < pbn * ge_n * hp) {
+                const int pl = e / (ge_n * hp);
+                const int rem = e - pl * (ge_n * hp);
+                const int ge = rem / hp, k = rem - ge * hp;
+                float2 *dst = reinterpret_cast<float2 *>(lds + (pl * G + g0 + 2 * ge) * twl);
+                dst[k] = c1 ? make_float2(0.0f, sv[i][0]) : make_float2(sv[i][0], 0.0f);
+            }
+        } else if (e < pbn * G * vpr) {
             if constexpr (V4)
                 lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
             else

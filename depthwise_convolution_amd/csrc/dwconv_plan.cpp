@@ -217,6 +217,8 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->tw = tx * v.q;
     pl->hl = hl;
     pl->twl = (span + lv - 1) / lv * lv;
+    if (p.stride == 2 && p.op == DWCONV_OP_INPUT_GRAD)
+        pl->twl += pl->twl & 1;             // upsampled dy is staged in column pairs
     pl->th = v.g - R + 1;
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(pl->OW, pl->tw);
