@@ -1193,7 +1193,6 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     // per-thread loads for the largest staged tile: G rows x (256*S*Q + 16*EXTRA) floats
     constexpr int NV = (G * (256 * S * Q + Gm::PBMAX * Gm::EXTRA) / LV + 255) / 256;
     constexpr int XW = S * (Q - 1) + 1 + (KW - 1) * D;
-    constexpr int TG = (KK + 1) < 16 ? (KK + 1) : 16;
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
 
@@ -1292,37 +1291,27 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
         }
     }
 
-    // add the tx threads of each plane: fixed tree in LDS, TG taps at a time
-    for (int tb = 0; tb <= KK; tb += TG) {
-        __syncthreads();
+    // add the tx threads of each plane: every thread parks its KK + 1 sums in
+    // LDS, then each (plane, tap) column is added over the plane's threads in
+    // thread order (one pass, fixed order)
+    constexpr int KP = (KK + 1) | 1;                   // odd row stride: no bank conflicts
+    __syncthreads();                                   // every thread done with the tile
 #pragma unroll
-        for (int k = 0; k < TG; ++k)
-            if (tb + k <= KK)
-                lds[k * 256 + tid] = acc[tb + k];
-        __syncthreads();
-        // fold a non-power-of-two row onto its largest power-of-two prefix,
-        // then a binary tree (fixed order either way)
-        int p2 = 1;
-        while (2 * p2 <= txn)
-            p2 *= 2;
-        if (p2 < txn) {
-            if (pli_raw < pbn && tx < txn - p2)
-#pragma unroll
-                for (int k = 0; k < TG; ++k)
-                    lds[k * 256 + tid] += lds[k * 256 + tid + p2];
-            __syncthreads();
-        }
-        for (int off = p2 >> 1; off > 0; off >>= 1) {
-            if (pli_raw < pbn && tx < off)
-#pragma unroll
-                for (int k = 0; k < TG; ++k)
-                    lds[k * 256 + tid] += lds[k * 256 + tid + off];
-            __syncthreads();
-        }
-        if (tx < TG && tb + tx <= KK && pvalid) {
-            const int n = my_plane / a.C, o = my_plane % a.C;
+    for (int t = 0; t <= KK; ++t)
+        lds[tid * KP + t] = acc[t];
+    __syncthreads();
+    const int n_cols = pbn * (KK + 1);
+    for (int e = tid; e < n_cols; e += 256) {
+        const int pl = e / (KK + 1), t = e - pl * (KK + 1);
+        const int plane = pg * pbn + pl;
+        if (plane < a.planes) {
+            const float *col = lds + pl * txn * KP + t;
+            float sum = 0.0f;
+            for (int j = 0; j < txn; ++j)
+                sum += col[j * KP];
+            const int n = plane / a.C, o = plane % a.C;
             const int chunk = (n * a.nwt + wt) * a.nsp + sp;
-            part[((long long)chunk * a.C + o) * (KK + 1) + tb + tx] = lds[tx * 256 + pli * txn];
+            part[((long long)chunk * a.C + o) * (KK + 1) + t] = sum;
         }
     }
 }
