@@ -23,7 +23,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 HEADLINE = "large_512x512x256_3x3"
-KERNEL_SRC = os.path.join(ROOT, "depthwise_convolution_amd", "csrc", "dwconv_kernels.hip")
+# the sources that decide the headline kernel's code and plan: a change to any
+# of them makes the recorded traffic counts stale
+KERNEL_SRCS = [os.path.join(ROOT, "depthwise_convolution_amd", "csrc", f)
+               for f in ("dwconv_internal.h", "dwconv_device.h", "dwconv_tiled_nhwc.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_large_512x512x256_3x3_nhwc.json")
 
 
@@ -33,8 +36,9 @@ def _log(msg):
 
 def kernel_source_digest():
     h = hashlib.sha256()
-    with open(KERNEL_SRC, "rb") as f:
-        h.update(f.read())
+    for src in KERNEL_SRCS:
+        with open(src, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 

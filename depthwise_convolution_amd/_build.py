@@ -2,6 +2,7 @@
 
 ``build()`` always recompiles (a stale library is worse than a slow build).
 """
+import concurrent.futures
 import os
 import subprocess
 import tempfile
@@ -10,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdwconv.so")
 HOST_SOURCES = ["dwconv_api.cpp", "dwconv_plan.cpp"]
-HIP_SOURCES = ["dwconv_kernels.hip"]
+HIP_SOURCES = ["dwconv_direct.hip", "dwconv_tiled_nhwc.hip", "dwconv_tiled_nchw.hip",
+               "dwconv_wgrad.hip", "dwconv_launch.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,11 +37,15 @@ def build(verbose: bool = False, extra_hipcc=()) -> str:
             o = os.path.join(tmp, src + ".o")
             _run(["g++", *GXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", o], verbose)
             objs.append(o)
-        for src in HIP_SOURCES:
-            o = os.path.join(tmp, src + ".o")
-            _run([hipcc, *HIPCC_FLAGS, *extra_hipcc, "-c", os.path.join(CSRC, src), "-o", o],
-                 verbose)
-            objs.append(o)
+        # the kernel files compile independently: one hipcc each, in parallel
+        hip_objs = [os.path.join(tmp, src + ".o") for src in HIP_SOURCES]
+        jobs = max(1, min(len(HIP_SOURCES), os.cpu_count() or 1))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            for f in [pool.submit(_run, [hipcc, *HIPCC_FLAGS, *extra_hipcc, "-c",
+                                         os.path.join(CSRC, src), "-o", o], verbose)
+                      for src, o in zip(HIP_SOURCES, hip_objs)]:
+                f.result()
+        objs += hip_objs
         out_tmp = LIB + ".tmp"
         _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", out_tmp, *objs],
              verbose)

@@ -3,7 +3,8 @@
 //
 // The planner (dwconv_plan.cpp) is plain C++ with no HIP runtime call, so the
 // validation and kernel selection it does can run on a host without a GPU.
-// The launcher (dwconv_kernels.hip) turns a plan into one kernel launch.
+// The launchers (dwconv_launch.hip, dwconv_wgrad.hip) turn a plan into kernel
+// launches.
 #pragma once
 
 #include <cstdint>

@@ -1,0 +1,315 @@
+// dwconv_tiled_nchw.hip -- the tiled NCHW kernel (stride 1 or 2; forward,
+// input gradient, forward with the epilogue) and its launcher.
+#include "dwconv_device.h"
+
+namespace dwconv {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Tiled NCHW (forward, or input gradient with reversed taps).
+//
+// Channel-outer layout: each (n, c) plane is an image of its own, and the
+// weights of a plane are one kernel.  A workgroup of 256 threads covers PB
+// planes x TX threads per plane row (TX = 256/PB, a power of two >= W/Q so
+// narrow planes are packed several to a workgroup); each thread owns Q
+// adjacent output columns.  G input rows of every plane (the TH = G - R + 1
+// output rows plus the row halo) and HALO columns on each side are staged
+// in LDS in one pass, then the rows are walked with rolling accumulators as
+// in the NHWC kernel.  Loads are buffer loads over the whole tensor: rows
+// past the plane or the tensor read as zero, columns outside [0, W) are
+// given an out-of-range offset.
+// ---------------------------------------------------------------------------
+struct TiledNchwArgs {
+    int planes, C;
+    int IH, IW, OH, OW;     // extents of the tensor read, and of the grid the tiles cover
+    int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
+    int pH, pW;             // top / left zero padding of the tensor read
+    int hl, twl;            // staged columns left of a tile; staged floats per plane row
+    int txn, pbn;           // threads per plane row (16..256), planes per workgroup (256 / txn)
+    int nct, nwt, nst;      // plane groups, column tiles, row tiles
+};
+
+
+// Stride 2 (S == 2) as in the NHWC kernel: the forward tiles the stride-1
+// grid and keeps its even positions, the input gradient stages dy
+// zero-upsampled (4-byte loads only) and skips the all-zero rows.
+template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, int MODE, int S>
+__global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in,
+                                                    const void *__restrict__ wv,
+                                                    const float *__restrict__ bias,
+                                                    float *__restrict__ out, TiledNchwArgs a,
+                                                    EpiArgs ep)
+{
+    constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
+    constexpr bool UPS = S == 2 && IG;        // staged input is the zero-upsampled dy
+    constexpr bool DEC = S == 2 && !IG;       // output is the decimated stride-1 grid
+    static_assert(!(UPS && V4), "upsampled staging uses 4-byte loads");
+    typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
+    constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV;
+    constexpr int NW = Gm::NW;
+    // loads per thread: the whole tile, or with the upsampled dy only its
+    // even rows, one dy element per pair of staged columns (the twl/2 pairs
+    // of a row: twl is even then)
+    constexpr int NV = UPS ? ((G + 1) / 2 * ((256 * Q + Gm::PBMAX * Gm::EXTRA) / 2 + Gm::PBMAX) +
+                              255) / 256
+                           : Gm::NV;
+    extern __shared__ float4 lds4[];
+    float *lds = reinterpret_cast<float *>(lds4);
+    const WT *w = reinterpret_cast<const WT *>(wv);
+
+    const int txn = a.txn, pbn = a.pbn;
+    const int tw = txn * Q, twl = a.twl;               // staged floats per plane row
+    const int vpr = twl / LV;                          // loads per plane row
+    float *ldsw = lds + pbn * G * twl;
+
+    int tile = blockIdx.x;
+    const int pg = tile % a.nct;
+    tile /= a.nct;
+    const int wt = tile % a.nwt;
+    const int st = tile / a.nwt;
+    const int w0 = wt * tw, h0 = st * TH;
+    const int tid = threadIdx.x;
+    const int nrows = min(TH, a.OH - h0) + R - 1;
+    const int rbase = h0 - a.pH, cbase = w0 - a.hl;
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes * a.IH * a.IW * 4);
+
+    // 1. all loads up front: weights of the workgroup's planes, the bias, the tile
+    float wst[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = tid + i * 256;
+        const int pl = e / KK, tap = e - pl * KK;
+        const int plane = pg * pbn + pl;
+        const bool ok = pl < pbn && plane < a.planes;
+        wst[i] = buf_w(rw, ok ? (plane % a.C) * KK + tap : kOutOfRange / 4, (WT *)nullptr);
+    }
+    // threads past pbn * txn (when txn does not divide 256) idle along
+    const int pli_raw = tid / txn, tx = tid - pli_raw * txn;
+    const int pli = min(pli_raw, pbn - 1);             // in-range LDS addresses for idle threads
+    const int my_plane = pg * pbn + pli;
+    const bool pvalid = pli_raw < pbn && my_plane < a.planes;
+    const float bval = buf_f32(rb, pvalid ? (my_plane % a.C) * 4 : kOutOfRange);
+    EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
+    if constexpr (EPI)
+        ec = epi_load(ep, pvalid ? my_plane % a.C : a.C, a.C);
+    float sv[NV][LV];
+    // upsampled staging: rows g0, g0+2, ... of the tile are the even
+    // (upsampled) rows; a pair k of staged columns (2k, 2k+1) holds one dy
+    // element at its even column and a zero at the other
+    const int g0 = rbase & 1, ge_n = (G - g0 + 1) / 2, hp = twl / 2, c1 = cbase & 1;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * 256;
+        if constexpr (UPS) {
+            const int pl = e / (ge_n * hp);
+            const int rem = e - pl * (ge_n * hp);
+            const int ge = rem / hp, k = rem - ge * hp;
+            const int g = g0 + 2 * ge;
+            const int plane = pg * pbn + pl, row = rbase + g, col = cbase + 2 * k + c1;
+            const int sr = row >> 1, sc = col >> 1;    // position in dy (row, col are even)
+            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
+                            col >= 0 && sr < a.IH && sc < a.IW;
+            sv[i][0] = buf_f32(rx, ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange);
+        } else {
+            const int pl = e / (G * vpr);
+            const int rem = e - pl * (G * vpr);
+            const int g = rem / vpr;
+            const int col = cbase + (rem - g * vpr) * LV;
+            const int plane = pg * pbn + pl, row = rbase + g;
+            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
+                            row < a.IH && col >= 0 && col < a.IW;
+            const int off = ok ? ((plane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
+            if constexpr (V4) {
+                const float4 v = buf_f4(rx, off);
+                sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
+            } else {
+                sv[i][0] = buf_f32(rx, off);
+            }
+        }
+    }
+    // 2. into LDS
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = tid + i * 256;
+        if (e < pbn * KK)
+            ldsw[e] = wst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * 256;
+        if constexpr (UPS) {
+            if (e < pbn * ge_n * hp) {
+                const int pl = e / (ge_n * hp);
+                const int rem = e - pl * (ge_n * hp);
+                const int ge = rem / hp, k = rem - ge * hp;
+                float2 *dst = reinterpret_cast<float2 *>(lds + (pl * G + g0 + 2 * ge) * twl);
+                dst[k] = c1 ? make_float2(0.0f, sv[i][0]) : make_float2(sv[i][0], 0.0f);
+            }
+        } else if (e < pbn * G * vpr) {
+            if constexpr (V4)
+                lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
+            else
+                lds[e] = sv[i][0];
+        }
+    }
+    __syncthreads();
+
+    // 3. per-thread weights and rolling accumulators
+    float wr[KH][KW];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+            const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
+            wr[kh][kw] = ldsw[pli * KK + tap];
+        }
+    if constexpr (EPI)
+        epi_finish(ec, ep);
+    float acc[R][Q];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < Q; ++j)
+            acc[r][j] = bval;
+    constexpr int XW = Q + (KW - 1) * D;
+    const float *rowbase = lds + pli * G * twl + tx * Q + (a.hl - a.pW);
+    const int oc = w0 + tx * Q;                        // first output column of this thread
+    float *outp = out + my_plane * a.YH * a.YW;
+    const bool vec_store = !DEC && (Q > 1) && (a.OW % Q == 0);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        if (u < nrows) {
+            // a staged row of the upsampled dy at an odd position is all zero
+            if (!(UPS && ((rbase + u) & 1))) {
+                float xv[XW];
+#pragma unroll
+                for (int i = 0; i < XW; ++i)
+                    xv[i] = rowbase[u * twl + i];
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh) {
+                    const int m = u - kh * D;
+                    if (m >= 0 && m < TH && !(DEC && ((h0 + m) & 1))) {
+                        const int slot = m % R;
+#pragma unroll
+                        for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                            for (int j = 0; j < Q; ++j)
+                                acc[slot][j] = fmaf(wr[kh][kw], xv[j + kw * D], acc[slot][j]);
+                    }
+                }
+            }
+            const int m = u - (R - 1);
+            if (m >= 0) {
+                if constexpr (EPI) {
+                    const EpiChan e1[1] = {ec};
+                    epi_block(acc[m % R], e1, ep.act);
+                }
+                const int r = h0 + m;
+                float *dst = outp + r * a.OW + oc;
+                if constexpr (DEC) {
+                    if (pvalid && (r & 1) == 0) {
+#pragma unroll
+                        for (int j = 0; j < Q; ++j) {
+                            const int c = oc + j;
+                            if ((c & 1) == 0 && (c >> 1) < a.YW)
+                                __builtin_nontemporal_store(
+                                    acc[m % R][j], outp + (r >> 1) * a.YW + (c >> 1));
+                        }
+                    }
+                } else if (pvalid) {
+                    if (vec_store && oc < a.OW) {
+                        store_vec<Q>(dst, acc[m % R]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < Q; ++j)
+                            if (oc + j < a.OW)
+                                __builtin_nontemporal_store(acc[m % R][j], dst + j);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < Q; ++j)
+                    acc[m % R][j] = bval;
+            }
+        }
+    }
+}
+
+typedef void (*TiledNchwFn)(const float *, const void *, const float *, float *, TiledNchwArgs,
+                            EpiArgs);
+
+template <typename WT, int V, int MODE, int S>
+constexpr TiledNchwFn tiled_nchw_fn()
+{
+    if constexpr (S == 1) {
+        constexpr TiledNchwVariant t = kTiledNchwVariants[V];
+        return &k_tiled_nchw<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), MODE, 1>;
+    } else {
+        constexpr TiledNchwVariant t = kTiledNchwS2Variants[V];
+        if constexpr (MODE == kModeInputGrad && t.v4 != 0)
+            return nullptr;             // upsampled staging has no 16-byte form
+        else
+            return &k_tiled_nchw<WT, t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), MODE, 2>;
+    }
+}
+
+template <int V, int S>
+void fill_tiled_nchw(TiledNchwFn (&row)[2][3])
+{
+    row[0][0] = tiled_nchw_fn<float, V, kModeFwd, S>();
+    row[0][1] = tiled_nchw_fn<float, V, kModeInputGrad, S>();
+    row[0][2] = tiled_nchw_fn<float, V, kModeFwdEpilogue, S>();
+    row[1][0] = tiled_nchw_fn<half_t, V, kModeFwd, S>();
+    row[1][1] = tiled_nchw_fn<half_t, V, kModeInputGrad, S>();
+    row[1][2] = tiled_nchw_fn<half_t, V, kModeFwdEpilogue, S>();
+}
+
+template <int S, int NVAR, int... Vs>
+void fill_all_tiled_nchw(TiledNchwFn (&fn)[NVAR][2][3], std::integer_sequence<int, Vs...>)
+{
+    (fill_tiled_nchw<Vs, S>(fn[Vs]), ...);
+}
+
+struct TiledNchwTable {
+    TiledNchwFn fn[kNumTiledNchwVariants][2][3];
+    TiledNchwFn fn2[kNumTiledNchwS2Variants][2][3];
+    TiledNchwTable()
+    {
+        fill_all_tiled_nchw<1>(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+        fill_all_tiled_nchw<2>(fn2, std::make_integer_sequence<int, kNumTiledNchwS2Variants>());
+    }
+};
+
+}  // namespace
+
+int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
+                      const float *b, float *out, hipStream_t st, const EpiArgs &ep)
+{
+    static const TiledNchwTable table;
+    const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumTiledNchwS2Variants;
+    if (pl.variant < 0 || pl.variant >= nvar || pl.cl < 16 || pl.cl > 256 ||
+        pl.pb != 256 / pl.cl)
+        return DWCONV_ERR_BAD_STRATEGY;
+    TiledNchwFn f = p.stride == 1
+                        ? table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)]
+                        : table.fn2[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    if (!f)
+        return DWCONV_ERR_BAD_STRATEGY;
+    TiledNchwArgs a;
+    a.planes = p.N * p.C; a.C = p.C;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.YH = pl.YH; a.YW = pl.YW;
+    a.pH = pl.pH; a.pW = pl.pW; a.hl = pl.hl; a.twl = pl.twl;
+    a.txn = pl.cl;
+    a.pbn = pl.pb;
+    a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
+    hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
+                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
+    return DWCONV_OK;
+}
+
+
+}  // namespace dwconv
