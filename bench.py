@@ -460,6 +460,71 @@ def main():
     fwd_ref_us = amortised([fwd_call(t["x"], t["y"]), fwd_call(t["dy"], t["dx"])], what="fwd")
     epi_us = amortised([fused_call(t["x"], t["y"]), fused_call(t["dy"], t["dx"])],
                        what="fwd_bn_relu6")
+    # practical ceilings in the same run: a device copy of the headline
+    # forward's bytes (256 MiB read + 256 MiB written, alternating two buffer
+    # pairs like the roofline leg) and the smallest launch of this library
+    c_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        for src, dst in ((t["x"], t["y"]), (t["dy"], t["dx"])):
+            dst.copy_(src)
+        c_ev[0].record(stream)
+        for i in range(n_rep):
+            if i % 2 == 0:
+                t["y"].copy_(t["x"])
+            else:
+                t["dx"].copy_(t["dy"])
+        c_ev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_us = c_ev[0].elapsed_time(c_ev[1]) * 1e3 / n_rep
+    # the same bytes through torch's elementwise kernel (out = in * 1)
+    with torch.cuda.stream(stream):
+        torch.mul(t["x"], 1.0, out=t["y"])
+        c_ev[0].record(stream)
+        for i in range(n_rep):
+            if i % 2 == 0:
+                torch.mul(t["x"], 1.0, out=t["y"])
+            else:
+                torch.mul(t["dy"], 1.0, out=t["dx"])
+        c_ev[1].record(stream)
+    torch.cuda.synchronize()
+    ew_us = c_ev[0].elapsed_time(c_ev[1]) * 1e3 / n_rep
+    copy_bytes = 2 * t["x"].numel() * 4
+    from depthwise_convolution_amd import workloads as _wls
+    tiny = _wls.WORKLOADS["tiny_16x16x8_3x3"]
+    tt = make_problem(torch, tiny, layout, seed=0)
+    # GPU-side time of the smallest launch: 20 forwards of 16x16x8 captured in
+    # a graph, replayed (the host cost of the Python binding is not in it)
+    g_tiny = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        launch_fwd(dw, tiny, tt, layout, stream)
+    stream.synchronize()
+    with torch.cuda.graph(g_tiny, stream=stream):
+        for _ in range(20):
+            launch_fwd(dw, tiny, tt, layout, stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g_tiny.replay()
+        c_ev[0].record(stream)
+        for _ in range(5):
+            g_tiny.replay()
+        c_ev[1].record(stream)
+    torch.cuda.synchronize()
+    tiny_us = c_ev[0].elapsed_time(c_ev[1]) * 1e3 / 100
+    del g_tiny, tt
+    best_copy_gbs = copy_bytes / min(copy_us, ew_us) / 1e3
+    result["ceilings"] = {
+        "copy_bytes": copy_bytes,
+        "runtime_copy_us": round(copy_us, 2),
+        "runtime_copy_GBs": round(copy_bytes / copy_us / 1e3, 1),
+        "elementwise_copy_us": round(ew_us, 2),
+        "elementwise_copy_GBs": round(copy_bytes / ew_us / 1e3, 1),
+        "headline_frac_of_best_copy": round(result["roofline"]["achieved"] / best_copy_gbs, 3),
+        "tiny_fwd_launch_us_in_graph": round(tiny_us, 2),
+        "timing": "copies: two events around 40 back-to-back copies alternating x->y and "
+                  "dy->dx (256 MiB each way), as the roofline leg times its kernel; the "
+                  "runtime copy is Tensor.copy_ (device-to-device memcpy), the elementwise "
+                  "copy torch.mul(src, 1, out=dst); tiny launch: 20 forwards of 16x16x8 3x3 "
+                  "captured in a HIP graph, replayed 5 times, per launch"}
     del x2, dy2
     result["wgrad"] = {
         "kernel": dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
