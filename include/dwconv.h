@@ -30,8 +30,8 @@
  *
  * Ownership and execution.  All tensor pointers are DEVICE pointers owned by
  * the caller.  The library allocates no memory and keeps no state between
- * calls beyond a per-device property cache, so calls may be made from any
- * host thread.  Work is enqueued asynchronously on `stream` (a hipStream_t;
+ * calls (its kernel tables are filled once, on first use, under the C++
+ * static-initialisation guard), so calls may be made from any host thread.  Work is enqueued asynchronously on `stream` (a hipStream_t;
  * NULL means the default stream); a return of DWCONV_OK means "validated and
  * enqueued".  The output (y or dx) is fully overwritten, never accumulated
  * into.  Inputs and outputs must not overlap (no in-place operation).
