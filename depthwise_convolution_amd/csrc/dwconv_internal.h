@@ -90,6 +90,14 @@ constexpr TiledVariant kTiledS2Variants[] = {
 };
 constexpr int kNumTiledS2Variants = sizeof(kTiledS2Variants) / sizeof(kTiledS2Variants[0]);
 
+// Variants of the tiled NHWC kernel with a channel multiplier of 2 (stride
+// 1; cl*vec counts output channels; 16-byte staging, vec a multiple of 2).
+constexpr TiledVariant kTiledM2Variants[] = {
+    {3, 3, 1, 4, 32, 2, 8, 4},  {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 3, 4},
+    {5, 5, 1, 4, 8, 1, 10, 4},  {5, 5, 1, 4, 16, 1, 12, 4},
+};
+constexpr int kNumTiledM2Variants = sizeof(kTiledM2Variants) / sizeof(kTiledM2Variants[0]);
+
 // Compile-time variants of the tiled NHWC weight-gradient kernel: workgroup
 // geometry as for the forward (vec, cl, px, g, lv).  A workgroup walks a strip of
 // row tiles of g - (kH-1)*d rows (its partial sums cover them all); the
@@ -118,6 +126,14 @@ constexpr WgradVariant kWgradS2Variants[] = {
     {3, 3, 1, 1, 32, 1, 7, 1},  {5, 5, 1, 1, 32, 1, 7, 1},
 };
 constexpr int kNumWgradS2Variants = sizeof(kWgradS2Variants) / sizeof(kWgradS2Variants[0]);
+
+// Variants of the tiled NHWC weight gradient with a channel multiplier of 2
+// (stride 1; cl*vec counts dy channels; 16-byte staging).
+constexpr WgradVariant kWgradM2Variants[] = {
+    {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
+    {5, 5, 1, 4, 16, 1, 8, 4},
+};
+constexpr int kNumWgradM2Variants = sizeof(kWgradM2Variants) / sizeof(kWgradM2Variants[0]);
 
 
 // Compile-time variants of the tiled NCHW kernel (same preference rule).

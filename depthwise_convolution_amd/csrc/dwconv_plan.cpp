@@ -111,13 +111,20 @@ static void set_extents(const Problem &p, Plan *pl)
 
 static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
+    if (p.layout != DWCONV_LAYOUT_NHWC)
         return false;
-    const TiledVariant *table = p.stride == 1 ? kTiledVariants : kTiledS2Variants;
-    const int nvar = p.stride == 1 ? kNumTiledVariants : kNumTiledS2Variants;
+    // a channel multiplier of 2 has its own variants (stride 1, 16-byte staging)
+    const bool m2 = p.mult == 2;
+    if ((p.mult != 1 && !m2) || (m2 && (p.stride != 1 || p.C % 4 != 0)))
+        return false;
+    const TiledVariant *table = m2 ? kTiledM2Variants
+                                   : p.stride == 1 ? kTiledVariants : kTiledS2Variants;
+    const int nvar = m2 ? kNumTiledM2Variants
+                        : p.stride == 1 ? kNumTiledVariants : kNumTiledS2Variants;
     const bool v4ok = p.C % 4 == 0 && (ptr_bits & 15u) == 0;   // 16-byte staging loads
+    const long long co = (long long)p.mult * p.C;               // channels of the tile walk
     // buffer-load byte offsets are 31-bit: one image and the weights must fit
-    if (4LL * pl->IH * pl->IW * p.C >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+    if (4LL * pl->IH * pl->IW * co >= (1LL << 31) || 4LL * co * p.kH * p.kW >= (1LL << 31))
         return false;
     // first variant of this kernel shape (table order = preference) whose
     // channel tile the problem fills to at least 3/4; else the one it fills best
@@ -128,7 +135,7 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
         if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation || (v.lv == 4 && !v4ok))
             continue;
         const int cg = v.cl * v.vec;
-        const double fill = (double)p.C / (ceil_div(p.C, cg) * cg);
+        const double fill = (double)co / (ceil_div((int)co, cg) * cg);
         if (fill >= 0.75) {
             best = i;
             break;
@@ -156,13 +163,14 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
         pl->OH = 2 * pl->OH - 1;
         pl->OW = 2 * pl->OW - 1;
     }
-    pl->nct = ceil_div(p.C, v.cl * v.vec);
+    pl->nct = ceil_div((int)co, v.cl * v.vec);
     pl->nwt = ceil_div(pl->OW, pl->tw);
     pl->nst = ceil_div(pl->OH, pl->th);
     pl->grid = (long long)p.N * pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nhwc_s%d_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_%s_%s",
-                  p.stride, v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "",
+    std::snprintf(pl->name, sizeof pl->name,
+                  "tiled_nhwc_s%d_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s%s_%s_%s", p.stride, v.kH, v.kW,
+                  v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "", m2 ? "_m2" : "",
                   op_tag(p), p.wtype ? "f16w" : "f32w");
     return true;
 }
@@ -308,13 +316,20 @@ static int wgrad_strip(int nrt, long long base)
 
 static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.mult != 1 || p.layout != DWCONV_LAYOUT_NHWC)
+    if (p.layout != DWCONV_LAYOUT_NHWC)
         return false;
+    // a channel multiplier of 2 has its own variants (stride 1, 16-byte staging)
+    const bool m2 = p.mult == 2;
+    if ((p.mult != 1 && !m2) || (m2 && (p.stride != 1 || p.C % 4 != 0)))
+        return false;
+    const long long co = (long long)p.mult * p.C;               // dy channels
     const bool v4ok = p.C % 4 == 0 && (ptr_bits & 15u) == 0;   // 16-byte staging loads
-    if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.Ho * p.Wo * p.C >= (1LL << 31))
+    if (4LL * p.H * p.W * p.C >= (1LL << 31) || 4LL * p.Ho * p.Wo * co >= (1LL << 31))
         return false;
-    const WgradVariant *table = p.stride == 1 ? kWgradVariants : kWgradS2Variants;
-    const int nvar = p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
+    const WgradVariant *table = m2 ? kWgradM2Variants
+                                   : p.stride == 1 ? kWgradVariants : kWgradS2Variants;
+    const int nvar = m2 ? kNumWgradM2Variants
+                        : p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
     int best = -1;
     double best_fill = -1.0;
     for (int i = 0; i < nvar; ++i) {
@@ -322,7 +337,7 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
         if (v.kH != p.kH || v.kW != p.kW || v.d != p.dilation || (v.lv == 4 && !v4ok))
             continue;
         const int cg = v.cl * v.vec;
-        const double fill = (double)p.C / (ceil_div(p.C, cg) * cg);
+        const double fill = (double)co / (ceil_div((int)co, cg) * cg);
         if (fill >= 0.75) {
             best = i;
             break;
@@ -343,15 +358,16 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     pl->tw = v.px * 256 / v.cl;                                  // dy columns per tile
     pl->th = (v.g - R) / p.stride + 1;                           // dy rows per row tile
     pl->nrt = ceil_div(p.Ho, pl->th);                            // row tiles per image
-    pl->nct = ceil_div(p.C, v.cl * v.vec);
+    pl->nct = ceil_div((int)co, v.cl * v.vec);
     pl->nwt = ceil_div(p.Wo, pl->tw);
     pl->strip = wgrad_strip(pl->nrt, (long long)p.N * pl->nct * pl->nwt);
     pl->nst = ceil_div(pl->nrt, pl->strip);                      // strips
     pl->chunks = (long long)p.N * pl->nst * pl->nwt;
     pl->grid = pl->chunks * pl->nct;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nhwc_s%d_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s_s%d",
-                  p.stride, v.kH, v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "",
+    std::snprintf(pl->name, sizeof pl->name,
+                  "wgrad_tiled_nhwc_s%d_k%dx%d_d%d_v%d_cl%d_px%d_g%d%s%s_s%d", p.stride, v.kH,
+                  v.kW, v.d, v.vec, v.cl, v.px, v.g, v.lv == 1 ? "_l1" : "", m2 ? "_m2" : "",
                   pl->strip);
     return true;
 }

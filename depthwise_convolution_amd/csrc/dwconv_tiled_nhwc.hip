@@ -21,7 +21,9 @@ namespace {
 // sweep, which is what streams fastest on MI355X.
 // ---------------------------------------------------------------------------
 struct TiledArgs {
-    int N, C;
+    int N, C;               // C: channels of the tile walk (the forward's output channels,
+                            // the input gradient's dy channels)
+    int CR, CW;             // channels of the tensor read / written (C, or C / multiplier)
     int IH, IW, OH, OW;     // extents of the tensor read, and of the grid the tiles cover
     int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
     int pH, pW;             // top / left zero padding of the tensor read
@@ -60,8 +62,16 @@ struct TiledGeom {
 //  * input gradient: dy is zero-upsampled while it is staged (a staged
 //    position takes dy[t/2][v/2] when both are even, else zero), and staged
 //    rows that are all zero are skipped.
+//
+// Channel multiplier M (output channel o reads input channel o/M): the walk
+// runs over the forward's output channels (= the input gradient's dy
+// channels) either way.
+//  * forward: the x tile is loaded with the input channels only and each
+//    value is written to LDS M times, once per output channel that reads it;
+//  * input gradient: dx channel c sums the M dy channels c*M .. c*M+M-1, so
+//    a thread's VEC accumulators are added in groups of M at the store.
 template <typename WT, int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int MODE,
-          int S>
+          int S, int M = 1>
 __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in,
                                                     const void *__restrict__ wv,
                                                     const float *__restrict__ bias,
@@ -72,9 +82,15 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     constexpr bool UPS = S == 2 && IG;        // staged input is the zero-upsampled dy
     constexpr bool DEC = S == 2 && !IG;       // output is the decimated stride-1 grid
     static_assert(S == 1 || S == 2, "stride 1 or 2");
+    static_assert(M == 1 || (M == 2 && LV == 4 && VEC % M == 0 && S == 1),
+                  "multiplier 2: 16-byte staging, whole groups of M channels per thread");
+    constexpr bool XM = M > 1 && !IG;         // x staged with 1/M of the walk's channels
     typedef TiledGeom<KH, KW, D, VEC, CL, PX, G, LV> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, TW = Gm::TW, CG = Gm::CG, TWI = Gm::TWI;
-    constexpr int VPC = Gm::VPC, VPR = Gm::VPR, VCH = Gm::VCH, NV = Gm::NV, KK = Gm::KK;
+    constexpr int KK = Gm::KK;
+    // loads per staged pixel / row / tile, and per thread
+    constexpr int VPC = XM ? CG / (M * LV) : Gm::VPC, VPR = TWI * VPC, VCH = G * VPR;
+    constexpr int NV = (VCH + 255) / 256;
     constexpr int WF = Gm::WF, XF4 = Gm::XF4;
     __shared__ float4 lds[XF4 + (WF + 3) / 4];
     float *ldsx = reinterpret_cast<float *>(lds);
@@ -106,7 +122,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     // the tile is still in flight.
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in + n * a.IH * a.IW * a.C, a.IH * a.IW * a.C * 4);
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(in + n * a.IH * a.IW * a.CR, a.IH * a.IW * a.CR * 4);
     constexpr int NW = (WF + 255) / 256;
     float wst[NW];
 #pragma unroll
@@ -131,8 +148,10 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
         const int rem = e - g * VPR;
         const int col = rem / VPC;
         const int cv = rem - col * VPC;
-        const int row = rbase + g, gc = cbase + col, ch = c0 + cv * LV;
-        bool ok = e < VCH && g < nrows && row >= 0 && gc >= 0 && ch < a.C;
+        // channel of the tensor read (with XM: an input channel of the tile's c0 / M ..)
+        const int ch = (XM ? c0 / M : c0) + cv * LV;
+        const int row = rbase + g, gc = cbase + col;
+        bool ok = e < VCH && g < nrows && row >= 0 && gc >= 0 && ch < a.CR;
         int sr = row, sc = gc;                  // position in the tensor read
         if constexpr (UPS) {
             ok = ok && (row & 1) == 0 && (gc & 1) == 0;
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
             sc = gc >> 1;
         }
         ok = ok && sr < a.IH && sc < a.IW;
-        const int off = ok ? ((sr * a.IW + sc) * a.C + ch) * 4 : kOutOfRange;
+        const int off = ok ? ((sr * a.IW + sc) * a.CR + ch) * 4 : kOutOfRange;
         if constexpr (LV == 4)
             stage[i] = buf_f4(rx, off);
         else
@@ -156,8 +175,16 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
-        if (e < VCH)
+        if constexpr (XM) {
+            // input channels ch .. ch+3 feed output slots M*ch .. M*ch + 4M - 1
+            if (e < VCH) {
+                const float4 v = stage[i];
+                lds[2 * e] = make_float4(v.x, v.x, v.y, v.y);
+                lds[2 * e + 1] = make_float4(v.z, v.z, v.w, v.w);
+            }
+        } else if (e < VCH) {
             reinterpret_cast<LoadT *>(lds)[e] = stage[i];
+        }
     }
     __syncthreads();
 
@@ -188,7 +215,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
 
     // 3. walk the staged rows
     constexpr int XW = PX + (KW - 1) * D;  // staged columns one thread reads per row
-    float *outp = out + (n * a.YH * a.YW) * a.C;
+    float *outp = out + (n * a.YH * a.YW) * a.CW;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -228,10 +255,23 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
                     if constexpr (DEC) {
                         const int c = ow + j;
                         if (cvalid && (r & 1) == 0 && (c & 1) == 0 && (c >> 1) < a.YW)
-                            store_vec<VEC>(outp + (((r >> 1) * a.YW + (c >> 1)) * a.C + cq),
+                            store_vec<VEC>(outp + (((r >> 1) * a.YW + (c >> 1)) * a.CW + cq),
                                            acc[m % R][j]);
+                    } else if (IG && M > 1) {
+                        // dx channel cq/M + k sums the dy channels (cq/M + k)*M + jj
+                        if (cvalid && ow + j < a.OW) {
+                            float sum[VEC / M];
+#pragma unroll
+                            for (int k = 0; k < VEC / M; ++k) {
+                                sum[k] = acc[m % R][j][k * M];
+#pragma unroll
+                                for (int jj = 1; jj < M; ++jj)
+                                    sum[k] += acc[m % R][j][k * M + jj];
+                            }
+                            store_vec<VEC / M>(outp + ((r * a.OW + ow + j) * a.CW + cq / M), sum);
+                        }
                     } else if (cvalid && ow + j < a.OW) {
-                        store_vec<VEC>(outp + ((r * a.OW + ow + j) * a.C + cq), acc[m % R][j]);
+                        store_vec<VEC>(outp + ((r * a.OW + ow + j) * a.CW + cq), acc[m % R][j]);
                     }
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)
@@ -246,46 +286,52 @@ typedef void (*TiledFn)(const float *, const void *, const float *, float *, Til
                         EpiArgs);
 
 // Kernel tables of the tiled NHWC kernel: [variant][f16 weights][mode], one
-// per stride (the stride-2 table is built from its own variant list).
-template <typename WT, int V, int MODE, int S>
+// per variant list: stride 1, stride 2, channel multiplier 2 (stride 1).
+constexpr int kTableS1 = 0, kTableS2 = 1, kTableM2 = 2;
+
+template <typename WT, int V, int MODE, int T>
 constexpr TiledFn tiled_fn()
 {
-    if constexpr (S == 1) {
+    if constexpr (T == kTableS1) {
         constexpr TiledVariant t = kTiledVariants[V];
-        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 1>;
-    } else {
+        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 1, 1>;
+    } else if constexpr (T == kTableS2) {
         constexpr TiledVariant t = kTiledS2Variants[V];
-        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 2>;
+        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 2, 1>;
+    } else {
+        constexpr TiledVariant t = kTiledM2Variants[V];
+        return &k_tiled_nhwc<WT, t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, MODE, 1, 2>;
     }
 }
 
-template <int V, int S>
+template <int V, int T>
 void fill_tiled(TiledFn (&row)[2][3])
 {
-    row[0][0] = tiled_fn<float, V, kModeFwd, S>();
-    row[0][1] = tiled_fn<float, V, kModeInputGrad, S>();
-    row[0][2] = tiled_fn<float, V, kModeFwdEpilogue, S>();
-    row[1][0] = tiled_fn<half_t, V, kModeFwd, S>();
-    row[1][1] = tiled_fn<half_t, V, kModeInputGrad, S>();
-    row[1][2] = tiled_fn<half_t, V, kModeFwdEpilogue, S>();
+    row[0][0] = tiled_fn<float, V, kModeFwd, T>();
+    row[0][1] = tiled_fn<float, V, kModeInputGrad, T>();
+    row[0][2] = tiled_fn<float, V, kModeFwdEpilogue, T>();
+    row[1][0] = tiled_fn<half_t, V, kModeFwd, T>();
+    row[1][1] = tiled_fn<half_t, V, kModeInputGrad, T>();
+    row[1][2] = tiled_fn<half_t, V, kModeFwdEpilogue, T>();
 }
 
-template <int S, int NVAR, int... Vs>
+template <int T, int NVAR, int... Vs>
 void fill_all_tiled(TiledFn (&fn)[NVAR][2][3], std::integer_sequence<int, Vs...>)
 {
-    (fill_tiled<Vs, S>(fn[Vs]), ...);
+    (fill_tiled<Vs, T>(fn[Vs]), ...);
 }
 
 struct TiledTable {
     TiledFn fn[kNumTiledVariants][2][3];
     TiledFn fn2[kNumTiledS2Variants][2][3];
+    TiledFn fnm[kNumTiledM2Variants][2][3];
     TiledTable()
     {
-        fill_all_tiled<1>(fn, std::make_integer_sequence<int, kNumTiledVariants>());
-        fill_all_tiled<2>(fn2, std::make_integer_sequence<int, kNumTiledS2Variants>());
+        fill_all_tiled<kTableS1>(fn, std::make_integer_sequence<int, kNumTiledVariants>());
+        fill_all_tiled<kTableS2>(fn2, std::make_integer_sequence<int, kNumTiledS2Variants>());
+        fill_all_tiled<kTableM2>(fnm, std::make_integer_sequence<int, kNumTiledM2Variants>());
     }
 };
-
 
 }  // namespace
 
@@ -293,13 +339,22 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
                       const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     static const TiledTable table;
-    const int nvar = p.stride == 1 ? kNumTiledVariants : kNumTiledS2Variants;
+    const bool m2 = p.mult == 2;
+    if ((p.mult != 1 && !m2) || (m2 && p.stride != 1))
+        return DWCONV_ERR_BAD_STRATEGY;
+    const int nvar = m2 ? kNumTiledM2Variants
+                        : p.stride == 1 ? kNumTiledVariants : kNumTiledS2Variants;
     if (pl.variant < 0 || pl.variant >= nvar)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledFn f = p.stride == 1 ? table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)]
-                              : table.fn2[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    const int wt16 = p.wtype == DWCONV_W_F16, mode = mode_of(p, ep);
+    TiledFn f = m2 ? table.fnm[pl.variant][wt16][mode]
+                   : p.stride == 1 ? table.fn[pl.variant][wt16][mode]
+                                   : table.fn2[pl.variant][wt16][mode];
     TiledArgs a;
-    a.N = p.N; a.C = p.C;
+    a.N = p.N;
+    a.C = p.mult * p.C;                                  // output (dy) channels
+    a.CR = p.op == DWCONV_OP_FWD ? p.C : p.mult * p.C;   // channels of the tensor read
+    a.CW = p.op == DWCONV_OP_FWD ? p.mult * p.C : p.C;   // channels of the tensor written
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
     a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW;

@@ -153,21 +153,25 @@ __global__ __launch_bounds__(256) void k_wgrad_gen(const float *__restrict__ x,
 // LV: floats per staging load, 4 (C % 4 == 0, 16-byte aligned tensors) or 1
 // (any C, one channel per thread).  At stride 2 a tile of TH x TW dy
 // positions reads 2*TH - 1 + (KH-1)*D rows and 2*TW - 1 + (KW-1)*D columns
-// of x, and dy position (m, j) meets x at (2m + kh*D, 2j + kw*D).
-template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int S>
+// of x, and dy position (m, j) meets x at (2m + kh*D, 2j + kw*D).  With a
+// channel multiplier M the walk runs over dy channels; the x tile is loaded
+// with the input channels only and each value is written to LDS M times, once
+// per dy channel that reads it.
+template <int KH, int KW, int D, int VEC, int CL, int PX, int G, int LV, int S, int M = 1>
 __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restrict__ x,
                                                           const float *__restrict__ dy,
                                                           float *__restrict__ part, WgradArgs a)
 {
     static_assert(LV == 4 || (LV == 1 && VEC == 1), "scalar staging: one channel per thread");
     static_assert(S == 1 || S == 2, "stride 1 or 2");
+    static_assert(M == 1 || (M == 2 && LV == 4 && S == 1), "multiplier 2: 16-byte staging");
     constexpr int R = (KH - 1) * D + 1, TW = PX * 256 / CL, CG = CL * VEC;
     constexpr int TH = (G - R) / S + 1;     // dy rows per row tile
     static_assert(G >= R && (G - R) % S == 0, "staged rows = S*(TH-1) + R");
-    constexpr int TWI = S * (TW - 1) + 1 + (KW - 1) * D, VPC = CG / LV, VPR = TWI * VPC;
+    constexpr int TWI = S * (TW - 1) + 1 + (KW - 1) * D, VPC = CG / (M * LV), VPR = TWI * VPC;
     constexpr int VCH = G * VPR, NV = (VCH + 255) / 256, KK = KH * KW, NP = 256 / CL;
     constexpr int XW = S * (PX - 1) + 1 + (KW - 1) * D;
-    constexpr int XF = VCH * LV;            // staged floats
+    constexpr int XF = G * TWI * CG;        // staged floats (dy channels)
     // the final per-(channel, tap) sums go through LDS in groups of TG taps
     constexpr int TGF = XF / (256 * VEC);
     constexpr int TG = TGF < 1 ? 1 : (TGF > KK + 1 ? KK + 1 : TGF);
@@ -189,7 +193,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     const int cq = c0 + q * VEC;
     const int ow = w0 + p * PX;
     const int cbase = S * w0 - a.pW;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + n * a.H * a.W * a.C, a.H * a.W * a.C * 4);
+    const int CX = a.C / M;                 // channels of x
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + n * a.H * a.W * CX, a.H * a.W * CX * 4);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(dy + n * a.OH * a.OW * a.C, a.OH * a.OW * a.C * 4);
 
     float acc[KK + 1][VEC];                 // taps kh*KW + kw, then the bias
@@ -214,10 +219,10 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
             const int rem = e - g * VPR;
             const int col = rem / VPC;
             const int cv = rem - col * VPC;
-            const int row = rbase + g, gc = cbase + col, ch = c0 + cv * LV;
+            const int row = rbase + g, gc = cbase + col, ch = c0 / M + cv * LV;   // x channel
             const bool ok = e < VCH && g < nrows && row >= 0 && row < a.H && gc >= 0 &&
-                            gc < a.W && ch < a.C;
-            const int off = ok ? ((row * a.W + gc) * a.C + ch) * 4 : kOutOfRange;
+                            gc < a.W && ch < CX;
+            const int off = ok ? ((row * a.W + gc) * CX + ch) * 4 : kOutOfRange;
             if constexpr (LV == 4)
                 stage[i] = buf_f4(rx, off);
             else
@@ -237,8 +242,16 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = tid + i * 256;
-            if (e < VCH)
-                reinterpret_cast<LoadT *>(lds4)[e] = stage[i];
+            if (e < VCH) {
+                if constexpr (M == 2) {
+                    // x channels ch .. ch+3 feed dy channel slots 2*ch .. 2*ch + 7
+                    const float4 v = stage[i];
+                    lds4[2 * e] = make_float4(v.x, v.x, v.y, v.y);
+                    lds4[2 * e + 1] = make_float4(v.z, v.z, v.w, v.w);
+                } else {
+                    reinterpret_cast<LoadT *>(lds4)[e] = stage[i];
+                }
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -519,31 +532,37 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ 
 
 typedef void (*WgradFn)(const float *, const float *, float *, WgradArgs);
 
-template <int V, int S>
+template <int V, int T>
 constexpr WgradFn wgrad_fn()
 {
-    if constexpr (S == 1) {
+    if constexpr (T == 1) {
         constexpr WgradVariant t = kWgradVariants[V];
-        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 1>;
-    } else {
+        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 1, 1>;
+    } else if constexpr (T == 2) {
         constexpr WgradVariant t = kWgradS2Variants[V];
-        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 2>;
+        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 2, 1>;
+    } else {
+        constexpr WgradVariant t = kWgradM2Variants[V];
+        return &k_wgrad_tiled_nhwc<t.kH, t.kW, t.d, t.vec, t.cl, t.px, t.g, t.lv, 1, 2>;
     }
 }
 
-template <int S, int NVAR, int... Vs>
+// T: 1 = stride 1, 2 = stride 2, 3 = channel multiplier 2 (stride 1)
+template <int T, int NVAR, int... Vs>
 void fill_wgrad(WgradFn (&fn)[NVAR], std::integer_sequence<int, Vs...>)
 {
-    ((fn[Vs] = wgrad_fn<Vs, S>()), ...);
+    ((fn[Vs] = wgrad_fn<Vs, T>()), ...);
 }
 
 struct WgradTable {
     WgradFn fn[kNumWgradVariants];
     WgradFn fn2[kNumWgradS2Variants];
+    WgradFn fnm[kNumWgradM2Variants];
     WgradTable()
     {
         fill_wgrad<1>(fn, std::make_integer_sequence<int, kNumWgradVariants>());
         fill_wgrad<2>(fn2, std::make_integer_sequence<int, kNumWgradS2Variants>());
+        fill_wgrad<3>(fnm, std::make_integer_sequence<int, kNumWgradM2Variants>());
     }
 };
 
@@ -592,10 +611,15 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.strip = pl.strip; a.chunks = (int)pl.chunks;
     if (pl.kind == KIND_WGRAD_TILED_NHWC) {
         static const WgradTable table;
-        const int nvar = p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
+        const bool m2 = p.mult == 2;
+        if ((p.mult != 1 && !m2) || (m2 && p.stride != 1))
+            return DWCONV_ERR_BAD_STRATEGY;
+        const int nvar = m2 ? kNumWgradM2Variants
+                            : p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
         if (pl.variant < 0 || pl.variant >= nvar)
             return DWCONV_ERR_BAD_STRATEGY;
-        hipLaunchKernelGGL(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
+        hipLaunchKernelGGL(m2 ? table.fnm[pl.variant]
+                              : p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
                            dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy, part, a);
     } else if (pl.kind == KIND_WGRAD_TILED_NCHW) {
         static const WgradNchwTable table;

@@ -322,7 +322,11 @@ def test_describe_ex_plans():
                                          pads=(0, 4, 3, 1), layout=dw.NCHW)
     assert name.startswith("tiled_nchw_s1")
     name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 112, 112, 32, 3, 3, mult=2)
-    assert name.startswith("direct_nhwc_s1_v1") and grid == (112 * 112 * 64 + 255) // 256
+    assert name.startswith("tiled_nhwc_s1") and "_m2_" in name     # multiplier 2: tiled
+    name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 112, 112, 32, 3, 3, mult=3)
+    assert name.startswith("direct_nhwc_s1_v1") and grid == (112 * 112 * 96 + 255) // 256
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 112, 112, 30, 3, 3, mult=2)
+    assert name.startswith("direct_nhwc")                          # C % 4 != 0
     name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 112, 112, 32, 3, 3, mult=2,
                                             layout=dw.NCHW)
     assert name.startswith("direct_nchw_s1") and grid == (112 * 112 * 32 + 255) // 256
@@ -342,6 +346,8 @@ def test_describe_ex_plans():
                                          pads=(0, 2, 2, 0))
     assert name.startswith("wgrad_tiled_nhwc")
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, 1, 64, 64, 32, 3, 3, mult=2)
+    assert name.startswith("wgrad_tiled_nhwc") and "_m2_" in name
+    name, _, _ = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, 1, 64, 64, 32, 3, 3, mult=4)
     assert name.startswith("wgrad_direct")
     a = dw.dwconv2d_weight_grad_workspace_size_ex(2, 9, 9, 5, 3, 3, mult=3, layout=dw.NCHW)
     assert a % (4 * 15 * 10) == 0 and a > 0
