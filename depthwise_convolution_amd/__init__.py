@@ -23,6 +23,7 @@ Tensor shapes: NHWC tensors are ``(N, H, W, C)``, NCHW tensors
 ``(mult*C,)``; ``pads`` is ``(top, bottom, left, right)``.
 """
 import ctypes
+import functools
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdwconv.so")
@@ -147,7 +148,7 @@ def _check_dev(t, name, dtypes):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
@@ -171,7 +172,8 @@ def _stream(t, stream):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int converts to the c_void_p argument type
+    return None if t is None else t.data_ptr()
 
 
 def _check_status(st, what):
@@ -352,13 +354,24 @@ def weight_grad(x, dy, kH, kW, stride=1, dilation=1, layout=NHWC, with_bias=True
 def _pads_arg(pads):
     if pads is None or len(pads) != 4:
         raise ValueError("pads must be (top, bottom, left, right)")
-    return (ctypes.c_int * 4)(*(int(v) for v in pads))
+    return _pads_array(tuple(int(v) for v in pads))
+
+
+@functools.lru_cache(maxsize=256)
+def _pads_array(pads):
+    # read-only for the library (const int *), so one array per pads tuple serves every call
+    return (ctypes.c_int * 4)(*pads)
 
 
 def _pads_or_same(pads, H, W, kH, kW, stride, dilation):
     if pads is None:
-        return dwconv2d_same_pads(PAD_SAME, H, W, kH, kW, stride, dilation)
+        return _same_pads_cached(H, W, kH, kW, stride, dilation)
     return tuple(int(v) for v in pads)
+
+
+@functools.lru_cache(maxsize=1024)
+def _same_pads_cached(H, W, kH, kW, stride, dilation):
+    return dwconv2d_same_pads(PAD_SAME, H, W, kH, kW, stride, dilation)
 
 
 def dwconv2d_same_pads(mode, H, W, kH, kW, stride=1, dilation=1):
@@ -371,6 +384,12 @@ def dwconv2d_same_pads(mode, H, W, kH, kW, stride=1, dilation=1):
 
 def dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads):
     """(Ho, Wo) of a padded problem."""
+    return _out_extents_cached(int(H), int(W), int(kH), int(kW), int(stride), int(dilation),
+                               tuple(int(v) for v in pads))
+
+
+@functools.lru_cache(maxsize=1024)
+def _out_extents_cached(H, W, kH, kW, stride, dilation, pads):
     ho, wo = ctypes.c_int(0), ctypes.c_int(0)
     st = lib().dwconv2d_out_extents(H, W, kH, kW, stride, dilation, _pads_arg(pads),
                                     ctypes.byref(ho), ctypes.byref(wo))
