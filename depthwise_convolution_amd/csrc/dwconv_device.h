@@ -247,12 +247,9 @@ struct NchwGeom {
     static constexpr int TH = G - R + 1;
     static constexpr int KK = KH * KW;
     static constexpr int LV = V4 ? 4 : 1;                      // floats per load
-    // staged columns beyond a tile's own: the window's d*(kW-1), plus up to
-    // 3 columns of alignment with 16-byte loads
-    static constexpr int EXTRA = V4 ? (D * (KW - 1) + 3 + 3) / 4 * 4 : D * (KW - 1);
     static constexpr int PBMAX = 16;                           // TX >= 16
-    // per-thread loads for the largest staged tile: G rows x (256*Q + PBMAX*EXTRA) floats
-    static constexpr int NV = (G * (256 * Q + PBMAX * EXTRA) / LV + 255) / 256;
+    // per-thread loads for the largest staged tile (every staged float)
+    static constexpr int NV = nchw_stage_loads(0, G, Q, KW, D, V4);
     static constexpr int NW = (PBMAX * KK + 255) / 256;
     static_assert(TH >= 1, "a workgroup must produce at least one output row");
 };

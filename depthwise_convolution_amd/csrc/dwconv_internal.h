@@ -152,6 +152,29 @@ constexpr TiledNchwVariant kTiledNchwVariants[] = {
 };
 constexpr int kNumTiledNchwVariants = sizeof(kTiledNchwVariants) / sizeof(kTiledNchwVariants[0]);
 
+// Per-thread staging loads of the tiled NCHW kernels (a compile-time bound
+// each kernel sizes its load registers with, and the planner checks its tile
+// against).  A workgroup stages g rows of pb planes, twl floats each, with
+// tx >= 16 threads per row, so pb <= 16; a row holds the tile's cols_per_thr
+// * tx columns plus at most `extra` more (the window's d*(kW-1) and, with
+// 16-byte loads, up to 3 alignment columns on each side).
+//   kind 0: every staged float, 4 or 1 per load (forward, input gradient at
+//           stride 1, weight gradient; cols_per_thr = s*q for the weight
+//           gradient's x rows at stride s);
+//   kind 1: the stride-2 input gradient's upsampled dy, one load per pair
+//           of staged columns of the even rows only.
+constexpr int nchw_extra_cols(int kW, int d, bool v4)
+{
+    return v4 ? (d * (kW - 1) + 3 + 3) / 4 * 4 : d * (kW - 1);
+}
+constexpr int nchw_stage_loads(int kind, int g, int cols_per_thr, int kW, int d, bool v4)
+{
+    return kind == 0 ? (g * (256 * cols_per_thr + 16 * nchw_extra_cols(kW, d, v4)) / (v4 ? 4 : 1) +
+                        255) / 256
+                     : ((g + 1) / 2 * ((256 * cols_per_thr + 16 * nchw_extra_cols(kW, d, false)) / 2 +
+                                       16) + 255) / 256;
+}
+
 // Variants of the tiled NCHW kernel at stride 2 (the tile covers the
 // stride-1 grid; the input gradient stages with 4-byte loads, v4 = 0).
 constexpr TiledNchwVariant kTiledNchwS2Variants[] = {

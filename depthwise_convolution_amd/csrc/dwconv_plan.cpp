@@ -225,8 +225,14 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->tw = tx * v.q;
     pl->hl = hl;
     pl->twl = (span + lv - 1) / lv * lv;
-    if (p.stride == 2 && p.op == DWCONV_OP_INPUT_GRAD)
+    const bool ups = p.stride == 2 && p.op == DWCONV_OP_INPUT_GRAD;
+    if (ups)
         pl->twl += pl->twl & 1;             // upsampled dy is staged in column pairs
+    // the kernel's per-thread load registers must cover the staged tile
+    const long long loads = ups ? (long long)pl->pb * ((v.g + 1) / 2) * (pl->twl / 2)
+                                : (long long)pl->pb * v.g * (pl->twl / lv);
+    if (loads > 256LL * nchw_stage_loads(ups ? 1 : 0, v.g, v.q, v.kW, v.d, v.v4 != 0))
+        return false;
     pl->th = v.g - R + 1;
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(pl->OW, pl->tw);
@@ -408,6 +414,10 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     pl->tw = tx * v.q;
     pl->hl = hl;
     pl->twl = (span + lv - 1) / lv * lv;
+    // the kernel's per-thread load registers must cover the staged x tile
+    if ((long long)pl->pb * v.g * (pl->twl / lv) >
+        256LL * nchw_stage_loads(0, v.g, p.stride * v.q, v.kW, v.d, v.v4 != 0))
+        return false;
     pl->th = (v.g - R) / p.stride + 1;                           // dy rows per row tile
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(p.Wo, pl->tw);

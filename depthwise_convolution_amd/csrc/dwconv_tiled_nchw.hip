@@ -51,9 +51,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     // loads per thread: the whole tile, or with the upsampled dy only its
     // even rows, one dy element per pair of staged columns (the twl/2 pairs
     // of a row: twl is even then)
-    constexpr int NV = UPS ? ((G + 1) / 2 * ((256 * Q + Gm::PBMAX * Gm::EXTRA) / 2 + Gm::PBMAX) +
-                              255) / 256
-                           : Gm::NV;
+    constexpr int NV = nchw_stage_loads(UPS ? 1 : 0, G, Q, KW, D, V4);
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
     const WT *w = reinterpret_cast<const WT *>(wv);

@@ -340,8 +340,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     constexpr int R = Gm::R, KK = Gm::KK, LV = Gm::LV;
     constexpr int TH = (G - R) / S + 1;                  // dy rows per row tile
     static_assert(G >= R && (G - R) % S == 0, "staged rows = S*(TH-1) + R");
-    // per-thread loads for the largest staged tile: G rows x (256*S*Q + 16*EXTRA) floats
-    constexpr int NV = (G * (256 * S * Q + Gm::PBMAX * Gm::EXTRA) / LV + 255) / 256;
+    // per-thread loads for the largest staged tile (x rows of S*Q columns per thread)
+    constexpr int NV = nchw_stage_loads(0, G, S * Q, KW, D, V4);
     constexpr int XW = S * (Q - 1) + 1 + (KW - 1) * D;
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
