@@ -10,13 +10,13 @@ namespace {
 // Tiled NCHW (forward, or input gradient with reversed taps).
 //
 // Channel-outer layout: each (n, c) plane is an image of its own, and the
-// weights of a plane are one kernel.  A workgroup of 256 threads covers PB
-// planes x TX threads per plane row (TX = 256/PB, a power of two >= W/Q so
-// narrow planes are packed several to a workgroup); each thread owns Q
-// adjacent output columns.  G input rows of every plane (the TH = G - R + 1
-// output rows plus the row halo) and HALO columns on each side are staged
-// in LDS in one pass, then the rows are walked with rolling accumulators as
-// in the NHWC kernel.  Loads are buffer loads over the whole tensor: rows
+// weights of a plane are one kernel.  A workgroup of 256 threads covers PB =
+// floor(256/TX) planes x TX threads per plane row (TX = clamp(ceil(Wo/Q), 16,
+// 256), so narrow planes are packed several to a workgroup; threads past
+// PB*TX idle through the walk); each thread owns Q adjacent output columns.
+// G input rows of every plane (the TH = G - R + 1 output rows plus the row
+// halo) and the column halo are staged in LDS in one pass, then the rows are
+// walked with rolling accumulators as in the NHWC kernel.  Loads are buffer loads over the whole tensor: rows
 // past the plane or the tensor read as zero, columns outside [0, W) are
 // given an out-of-range offset.
 // ---------------------------------------------------------------------------

@@ -75,7 +75,8 @@ extern "C" {
 
 #define DWCONV_OP_FWD        0 /* y  = dwconv(x; W, b)                        */
 #define DWCONV_OP_INPUT_GRAD 1 /* dx = dwconv_input_grad(dy; W)               */
-#define DWCONV_OP_WEIGHT_GRAD 2 /* dW, db = dwconv_weight_grad(x, dy) (planning only) */
+#define DWCONV_OP_WEIGHT_GRAD 2 /* dW, db = dwconv_weight_grad(x, dy): an op code of the
+                                   describe calls; run by the weight-gradient entry points */
 
 /* Padding modes of dwconv2d_same_pads. */
 #define DWCONV_PAD_SAME     0  /* symmetric: d*(k-1)/2 on every side (odd kernels)   */
