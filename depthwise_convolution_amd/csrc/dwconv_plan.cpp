@@ -385,8 +385,8 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     const long long co = (long long)p.mult * p.C, planes = p.N * co;
     if (4LL * p.N * p.C * p.H * p.W >= (1LL << 31) || 4LL * planes * p.Ho * p.Wo >= (1LL << 31))
         return false;
-    const TiledNchwVariant *table = p.stride == 1 ? kTiledNchwVariants : kWgradNchwS2Variants;
-    const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumWgradNchwS2Variants;
+    const TiledNchwVariant *table = p.stride == 1 ? kWgradNchwVariants : kWgradNchwS2Variants;
+    const int nvar = p.stride == 1 ? kNumWgradNchwVariants : kNumWgradNchwS2Variants;
     const bool v4ok = p.W % 4 == 0 && (ptr_bits & 15u) == 0;
     int best = -1;
     for (int i = 0; i < nvar; ++i) {

@@ -572,7 +572,7 @@ template <int V, int S>
 constexpr WgradNchwFn wgrad_nchw_fn()
 {
     if constexpr (S == 1) {
-        constexpr TiledNchwVariant t = kTiledNchwVariants[V];
+        constexpr TiledNchwVariant t = kWgradNchwVariants[V];
         return &k_wgrad_tiled_nchw<t.kH, t.kW, t.d, t.q, t.g, (t.v4 != 0), 1>;
     } else {
         constexpr TiledNchwVariant t = kWgradNchwS2Variants[V];
@@ -587,11 +587,11 @@ void fill_wgrad_nchw(WgradNchwFn (&fn)[NVAR], std::integer_sequence<int, Vs...>)
 }
 
 struct WgradNchwTable {
-    WgradNchwFn fn[kNumTiledNchwVariants];
+    WgradNchwFn fn[kNumWgradNchwVariants];
     WgradNchwFn fn2[kNumWgradNchwS2Variants];
     WgradNchwTable()
     {
-        fill_wgrad_nchw<1>(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
+        fill_wgrad_nchw<1>(fn, std::make_integer_sequence<int, kNumWgradNchwVariants>());
         fill_wgrad_nchw<2>(fn2, std::make_integer_sequence<int, kNumWgradNchwS2Variants>());
     }
 };
@@ -623,7 +623,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
                            dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy, part, a);
     } else if (pl.kind == KIND_WGRAD_TILED_NCHW) {
         static const WgradNchwTable table;
-        const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumWgradNchwS2Variants;
+        const int nvar = p.stride == 1 ? kNumWgradNchwVariants : kNumWgradNchwS2Variants;
         if (pl.variant < 0 || pl.variant >= nvar || pl.cl < 16 || pl.cl > 256 ||
             pl.pb != 256 / pl.cl)
             return DWCONV_ERR_BAD_STRATEGY;
