@@ -104,8 +104,8 @@ constexpr int kNumTiledM2Variants = sizeof(kTiledM2Variants) / sizeof(kTiledM2Va
 // planner sizes the strips for about kWgradTargetWorkgroups workgroups.
 struct WgradVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr WgradVariant kWgradVariants[] = {
-    {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
-    {5, 5, 1, 4, 16, 1, 8, 4},
+    {3, 3, 1, 2, 32, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
+    {5, 5, 1, 4, 8, 1, 8, 4},
     {7, 7, 1, 2, 32, 1, 10, 4},
     {7, 7, 2, 1, 64, 1, 16, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},
