@@ -177,11 +177,14 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 
 static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
-    if (p.mult != 1 || p.layout != DWCONV_LAYOUT_NCHW)
+    // a channel multiplier runs tiled in the forward (each output plane reads
+    // its input plane); its input gradient sums several planes and runs direct
+    if (p.layout != DWCONV_LAYOUT_NCHW || (p.mult != 1 && p.op != DWCONV_OP_FWD))
         return false;
     // buffer-load byte offsets are 31-bit: the tensor read and the weights must fit
-    const long long planes = (long long)p.N * p.C;
-    if (4LL * planes * pl->IH * pl->IW >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+    const long long planes = (long long)p.N * p.mult * p.C;     // planes of the walk
+    const long long co = (long long)p.mult * p.C;
+    if (4LL * p.N * p.C * pl->IH * pl->IW >= (1LL << 31) || 4LL * co * p.kH * p.kW >= (1LL << 31))
         return false;
     const TiledNchwVariant *table = p.stride == 1 ? kTiledNchwVariants : kTiledNchwS2Variants;
     const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumTiledNchwS2Variants;
@@ -240,8 +243,11 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->lds_bytes = 4 * (pl->pb * v.g * pl->twl + pl->pb * v.kH * v.kW);
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
-    std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s%d_k%dx%d_d%d_q%d_g%d_%s_tx%d_%s_%s",
-                  p.stride, v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, op_tag(p),
+    char mtag[16] = "";
+    if (p.mult != 1)
+        std::snprintf(mtag, sizeof mtag, "_m%d", p.mult);
+    std::snprintf(pl->name, sizeof pl->name, "tiled_nchw_s%d_k%dx%d_d%d_q%d_g%d_%s_tx%d%s_%s_%s",
+                  p.stride, v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, mtag, op_tag(p),
                   p.wtype ? "f16w" : "f32w");
     return true;
 }

@@ -21,7 +21,9 @@ namespace {
 // given an out-of-range offset.
 // ---------------------------------------------------------------------------
 struct TiledNchwArgs {
-    int planes, C;
+    int planes, C;          // planes (n, c) of the walk and their channels: the tensor
+                            // written in the forward, the tensor read in the input gradient
+    int mult;               // forward channel multiplier: walk plane p reads input plane p / mult
     int IH, IW, OH, OW;     // extents of the tensor read, and of the grid the tiles cover
     int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
     int pH, pW;             // top / left zero padding of the tensor read
@@ -73,7 +75,9 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes * a.IH * a.IW * 4);
+    // with a multiplier (forward only) plane n*C + o reads input plane n*(C/mult) + o/mult,
+    // which is (n*C + o) / mult
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes / a.mult * a.IH * a.IW * 4);
 
     // 1. all loads up front: weights of the workgroup's planes, the bias, the tile
     float wst[NW];
@@ -120,7 +124,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
             const int plane = pg * pbn + pl, row = rbase + g;
             const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
                             row < a.IH && col >= 0 && col < a.IW;
-            const int off = ok ? ((plane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
+            const int xplane = a.mult == 1 ? plane : plane / a.mult;
+            const int off = ok ? ((xplane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
             if constexpr (V4) {
                 const float4 v = buf_f4(rx, off);
                 sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
@@ -297,7 +302,9 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
     if (!f)
         return DWCONV_ERR_BAD_STRATEGY;
     TiledNchwArgs a;
-    a.planes = p.N * p.C; a.C = p.C;
+    if (p.mult != 1 && p.op != DWCONV_OP_FWD)
+        return DWCONV_ERR_BAD_STRATEGY;
+    a.planes = p.N * p.mult * p.C; a.C = p.mult * p.C; a.mult = p.mult;
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
     a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW; a.hl = pl.hl; a.twl = pl.twl;

@@ -1,5 +1,6 @@
-"""Channel multiplier 2 on the tiled NHWC kernels (forward, input gradient,
-weight gradient) against the oracle.
+"""Channel multipliers on the tiled kernels against the oracle: multiplier 2
+on the NHWC forward, input gradient and weight gradient, any multiplier on
+the NCHW forward.
 
 With a multiplier m, output channel o reads input channel o/m (Reactant.jl
 issue 331: a grouped convolution with groups = input channels; the MLX
@@ -144,3 +145,45 @@ def test_m2_tiled_random_within_bound(torch, idx, op):
         _within(got[1], ref[1], S[1], f"{wl.name} db")
     else:
         _within(got, ref, S, wl.name)
+
+
+# NCHW: the tiled forward takes any multiplier (output plane n*mC + o reads
+# input plane n*C + o/m); its input gradient runs on the direct kernel.
+NCHW_SHAPES = [
+    (2, 37, 75, 6, 3, 2, None),
+    (1, 56, 56, 16, 5, 3, (0, 0, 0, 0)),
+    (3, 30, 19, 5, 7, 2, None),
+    (1, 23, 300, 4, 3, 4, (-1, 2, 1, 0)),
+]
+
+
+def _wl_nchw(shape):
+    N, H, W, C, k, m, pads = shape
+    if pads is None:
+        pads = tuple(dw.dwconv2d_same_pads(dw.PAD_SAME, H, W, k, k, 1, 1))
+    return Workload(name=f"nchw_m{m}_{N}x{H}x{W}x{C}_k{k}_{pads}", N=N, H=H, W=W, C=C, kH=k,
+                    kW=k, pads=pads, mult=m, x_dist="uniform1", w_dist="uniform1",
+                    dy_dist="uniform1")
+
+
+@pytest.mark.parametrize("idx", range(len(NCHW_SHAPES)),
+                         ids=[_wl_nchw(s).name for s in NCHW_SHAPES])
+def test_nchw_multiplier_forward_tiled(torch, idx):
+    import oracle
+    from depthwise_convolution_amd.workloads import NCHW
+    wl = _wl_nchw(NCHW_SHAPES[idx])
+    name = dw.dwconv2d_describe_ex(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, 1, 1,
+                                   wl.pads, wl.mult, NCHW, 0, True, dw.STRATEGY_TILED)[0]
+    print(f"\n[case] nchw fwd {wl.name} {name}", flush=True)
+    assert name.startswith("tiled_nchw") and f"_m{wl.mult}_" in name
+    for integer, seed in ((True, 130 + idx), (False, 140 + idx)):
+        inp = wlmod.make_inputs(wl, NCHW, seed=seed, integer=integer)
+        ref, S = oracle.fwd_general(inp["x"], inp["w"], inp["b"], 1, 1, wl.pads, wl.mult, NCHW,
+                                    nthreads=NTHREADS)
+        got = dw.fwd(_dev(torch, inp["x"]), _dev(torch, inp["w"]), _dev(torch, inp["b"]), 1, 1,
+                     NCHW, dw.STRATEGY_TILED, pads=wl.pads, mult=wl.mult).cpu().numpy()
+        torch.cuda.synchronize()
+        if integer:
+            np.testing.assert_array_equal(got, ref.astype(np.float32))
+        else:
+            _within(got, ref, S, wl.name)
