@@ -69,11 +69,11 @@ enum Kind {
 struct TiledVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr TiledVariant kTiledVariants[] = {
     {3, 3, 1, 4, 32, 2, 8, 4},   {3, 3, 1, 4, 16, 1, 6, 4},   {3, 3, 1, 4, 8, 1, 3, 4},
-    {5, 5, 1, 4, 8, 1, 10, 4},   {5, 5, 1, 4, 16, 1, 12, 4},
+    {5, 5, 1, 4, 8, 1, 10, 4},
     {7, 7, 1, 1, 64, 1, 16, 4},  {7, 7, 1, 2, 16, 1, 14, 4},
     {7, 7, 2, 2, 16, 1, 20, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},  {1, 15, 1, 4, 16, 1, 2, 4},
-    {1, 31, 1, 2, 32, 1, 2, 4},  {1, 31, 1, 2, 64, 1, 2, 4},
+    {1, 31, 1, 2, 32, 1, 2, 4},
     // scalar staging (lv = 1): any channel count, e.g. a prime one
     {3, 3, 1, 1, 32, 2, 8, 1},   {5, 5, 1, 1, 32, 1, 12, 1},
     {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 20, 1},
@@ -85,7 +85,7 @@ constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants
 // covers the stride-1 grid, so g >= kH*d + 1 leaves at least two rows, one
 // of them even).
 constexpr TiledVariant kTiledS2Variants[] = {
-    {3, 3, 1, 4, 8, 2, 6, 4},   {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 1, 32, 1, 6, 1},
+    {3, 3, 1, 4, 8, 2, 6, 4},   {3, 3, 1, 1, 32, 1, 6, 1},
     {5, 5, 1, 4, 8, 1, 8, 4},   {5, 5, 1, 1, 32, 1, 8, 1},
 };
 constexpr int kNumTiledS2Variants = sizeof(kTiledS2Variants) / sizeof(kTiledS2Variants[0]);
@@ -94,7 +94,7 @@ constexpr int kNumTiledS2Variants = sizeof(kTiledS2Variants) / sizeof(kTiledS2Va
 // 1; cl*vec counts output channels; 16-byte staging, vec a multiple of 2).
 constexpr TiledVariant kTiledM2Variants[] = {
     {3, 3, 1, 4, 32, 2, 8, 4},  {3, 3, 1, 4, 16, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 3, 4},
-    {5, 5, 1, 4, 8, 1, 10, 4},  {5, 5, 1, 4, 16, 1, 12, 4},
+    {5, 5, 1, 4, 8, 1, 10, 4},
 };
 constexpr int kNumTiledM2Variants = sizeof(kTiledM2Variants) / sizeof(kTiledM2Variants[0]);
 
@@ -121,7 +121,7 @@ constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants
 // Variants of the tiled NHWC weight gradient at stride 2 (g = staged x rows
 // = 2*(dy rows) - 1 + (kH-1)*d).
 constexpr WgradVariant kWgradS2Variants[] = {
-    {3, 3, 1, 4, 8, 1, 7, 4},   {3, 3, 1, 4, 16, 1, 5, 4},
+    {3, 3, 1, 4, 8, 1, 7, 4},
     {5, 5, 1, 4, 8, 1, 7, 4},
     {3, 3, 1, 1, 32, 1, 7, 1},  {5, 5, 1, 1, 32, 1, 7, 1},
 };
