@@ -129,12 +129,22 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
 #pragma unroll
     for (int i = 0; i < NW; ++i)
         wst[i] = buf_w(rw, c0 * KK + tid + i * 256, (WT *)nullptr);
+    // bias and epilogue factors: one 16-byte load per array for 4 channels
+    // (C % 4 == 0 with 16-byte staging, so a vector is wholly in or out of range)
+    constexpr bool V4F = VEC == 4 && LV == 4;
     float bv[VEC];
+    if constexpr (V4F) {
+        const float4 b4 = buf_f4(rb, cq * 4);
+        bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+    } else {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v)
-        bv[v] = buf_f32(rb, (cq + v) * 4);
+        for (int v = 0; v < VEC; ++v)
+            bv[v] = buf_f32(rb, (cq + v) * 4);
+    }
     EpiChan ec[VEC];
-    if constexpr (EPI) {
+    if constexpr (EPI && V4F) {
+        epi_load4(ep, cq, a.C, ec);
+    } else if constexpr (EPI) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v)
             ec[v] = epi_load(ep, cq + v, a.C);
