@@ -178,13 +178,19 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     // a channel multiplier runs tiled in the forward (each output plane reads
-    // its input plane); its input gradient sums several planes and runs direct
-    if (p.layout != DWCONV_LAYOUT_NCHW || (p.mult != 1 && p.op != DWCONV_OP_FWD))
+    // its input plane) and, for 2 at stride 1, in the input gradient (each dx
+    // plane sums its 2 dy planes: mig planes staged per walk plane)
+    const bool igm = p.op == DWCONV_OP_INPUT_GRAD && p.mult != 1;
+    if (p.layout != DWCONV_LAYOUT_NCHW || (igm && (p.mult != 2 || p.stride != 1)))
         return false;
-    // buffer-load byte offsets are 31-bit: the tensor read and the weights must fit
-    const long long planes = (long long)p.N * p.mult * p.C;     // planes of the walk
+    const int mig = igm ? p.mult : 1;
+    // planes of the walk: the forward's output planes, or the input gradient's dx planes
     const long long co = (long long)p.mult * p.C;
-    if (4LL * p.N * p.C * pl->IH * pl->IW >= (1LL << 31) || 4LL * co * p.kH * p.kW >= (1LL << 31))
+    const long long planes = (long long)p.N * (p.op == DWCONV_OP_FWD ? co : p.C);
+    // buffer-load byte offsets are 31-bit: the tensor read and the weights must fit
+    const long long read_planes = p.op == DWCONV_OP_FWD ? (long long)p.N * p.C : p.N * co;
+    if (4LL * read_planes * pl->IH * pl->IW >= (1LL << 31) ||
+        4LL * co * p.kH * p.kW >= (1LL << 31))
         return false;
     const TiledNchwVariant *table = p.stride == 1 ? kTiledNchwVariants : kTiledNchwS2Variants;
     const int nvar = p.stride == 1 ? kNumTiledNchwVariants : kNumTiledNchwS2Variants;
@@ -233,14 +239,14 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
         pl->twl += pl->twl & 1;             // upsampled dy is staged in column pairs
     // the kernel's per-thread load registers must cover the staged tile
     const long long loads = ups ? (long long)pl->pb * ((v.g + 1) / 2) * (pl->twl / 2)
-                                : (long long)pl->pb * v.g * (pl->twl / lv);
-    if (loads > 256LL * nchw_stage_loads(ups ? 1 : 0, v.g, v.q, v.kW, v.d, v.v4 != 0))
+                                : (long long)pl->pb * mig * v.g * (pl->twl / lv);
+    if (loads > 256LL * nchw_stage_loads(ups ? 1 : 0, mig * v.g, v.q, v.kW, v.d, v.v4 != 0))
         return false;
     pl->th = v.g - R + 1;
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(pl->OW, pl->tw);
     pl->nst = ceil_div(pl->OH, pl->th);
-    pl->lds_bytes = 4 * (pl->pb * v.g * pl->twl + pl->pb * v.kH * v.kW);
+    pl->lds_bytes = 4 * mig * (pl->pb * v.g * pl->twl + pl->pb * v.kH * v.kW);
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
     char mtag[16] = "";

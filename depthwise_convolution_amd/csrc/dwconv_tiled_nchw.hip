@@ -36,7 +36,12 @@ struct TiledNchwArgs {
 // Stride 2 (S == 2) as in the NHWC kernel: the forward tiles the stride-1
 // grid and keeps its even positions, the input gradient stages dy
 // zero-upsampled (4-byte loads only) and skips the all-zero rows.
-template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, int MODE, int S>
+//
+// Input gradient with a channel multiplier M (M > 1, stride 1): dx plane
+// n*C + c sums the M dy planes (n*C + c)*M + j, j < M, each with its own
+// weights; a workgroup stages the M dy planes of each of its dx planes and
+// every thread adds all M of them into its accumulators.
+template <typename WT, int KH, int KW, int D, int Q, int G, bool V4, int MODE, int S, int M = 1>
 __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in,
                                                     const void *__restrict__ wv,
                                                     const float *__restrict__ bias,
@@ -47,13 +52,14 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     constexpr bool UPS = S == 2 && IG;        // staged input is the zero-upsampled dy
     constexpr bool DEC = S == 2 && !IG;       // output is the decimated stride-1 grid
     static_assert(!(UPS && V4), "upsampled staging uses 4-byte loads");
+    static_assert(M == 1 || (IG && S == 1), "a multiplier > 1 here: input gradient, stride 1");
     typedef NchwGeom<KH, KW, D, Q, G, V4> Gm;
     constexpr int R = Gm::R, TH = Gm::TH, KK = Gm::KK, LV = Gm::LV;
-    constexpr int NW = Gm::NW;
-    // loads per thread: the whole tile, or with the upsampled dy only its
-    // even rows, one dy element per pair of staged columns (the twl/2 pairs
-    // of a row: twl is even then)
-    constexpr int NV = nchw_stage_loads(UPS ? 1 : 0, G, Q, KW, D, V4);
+    constexpr int NW = (Gm::PBMAX * M * KK + 255) / 256;
+    // loads per thread: the whole tile (M planes per walk plane), or with the
+    // upsampled dy only its even rows, one dy element per pair of staged
+    // columns (the twl/2 pairs of a row: twl is even then)
+    constexpr int NV = nchw_stage_loads(UPS ? 1 : 0, M * G, Q, KW, D, V4);
     extern __shared__ float4 lds4[];
     float *lds = reinterpret_cast<float *>(lds4);
     const WT *w = reinterpret_cast<const WT *>(wv);
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const int txn = a.txn, pbn = a.pbn;
     const int tw = txn * Q, twl = a.twl;               // staged floats per plane row
     const int vpr = twl / LV;                          // loads per plane row
-    float *ldsw = lds + pbn * G * twl;
+    float *ldsw = lds + pbn * M * G * twl;
 
     int tile = blockIdx.x;
     const int pg = tile % a.nct;
@@ -73,21 +79,25 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const int nrows = min(TH, a.OH - h0) + R - 1;
     const int rbase = h0 - a.pH, cbase = w0 - a.hl;
 
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, M * a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
     // with a multiplier (forward only) plane n*C + o reads input plane n*(C/mult) + o/mult,
     // which is (n*C + o) / mult
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, a.planes / a.mult * a.IH * a.IW * 4);
+    // (with M > 1 the input gradient reads M dy planes per walk plane)
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in, M * (a.planes / a.mult) * a.IH * a.IW * 4);
 
     // 1. all loads up front: weights of the workgroup's planes, the bias, the tile
     float wst[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int e = tid + i * 256;
-        const int pl = e / KK, tap = e - pl * KK;
+        const int pj = e / KK, tap = e - pj * KK;      // pj = pl*M + j
+        const int pl = pj / M;
         const int plane = pg * pbn + pl;
         const bool ok = pl < pbn && plane < a.planes;
-        wst[i] = buf_w(rw, ok ? (plane % a.C) * KK + tap : kOutOfRange / 4, (WT *)nullptr);
+        // weight row of dy channel (plane % C)*M + j
+        const int row = (plane % a.C) * M + (pj - pl * M);
+        wst[i] = buf_w(rw, ok ? row * KK + tap : kOutOfRange / 4, (WT *)nullptr);
     }
     // threads past pbn * txn (when txn does not divide 256) idle along
     const int pli_raw = tid / txn, tx = tid - pli_raw * txn;
@@ -117,14 +127,16 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
                             col >= 0 && sr < a.IH && sc < a.IW;
             sv[i][0] = buf_f32(rx, ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange);
         } else {
-            const int pl = e / (G * vpr);
-            const int rem = e - pl * (G * vpr);
+            const int pj = e / (G * vpr);                  // pl*M + j
+            const int rem = e - pj * (G * vpr);
             const int g = rem / vpr;
             const int col = cbase + (rem - g * vpr) * LV;
-            const int plane = pg * pbn + pl, row = rbase + g;
+            const int pl = pj / M, plane = pg * pbn + pl, row = rbase + g;
             const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
                             row < a.IH && col >= 0 && col < a.IW;
-            const int xplane = a.mult == 1 ? plane : plane / a.mult;
+            // plane read: the forward's input plane (plane / mult), or dy plane plane*M + j
+            const int xplane = M > 1 ? (pg * pbn) * M + pj
+                                     : a.mult == 1 ? plane : plane / a.mult;
             const int off = ok ? ((xplane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
             if constexpr (V4) {
                 const float4 v = buf_f4(rx, off);
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int e = tid + i * 256;
-        if (e < pbn * KK)
+        if (e < pbn * M * KK)
             ldsw[e] = wst[i];
     }
 #pragma unroll
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
                 float2 *dst = reinterpret_cast<float2 *>(lds + (pl * G + g0 + 2 * ge) * twl);
                 dst[k] = c1 ? make_float2(0.0f, sv[i][0]) : make_float2(sv[i][0], 0.0f);
             }
-        } else if (e < pbn * G * vpr) {
+        } else if (e < pbn * M * G * vpr) {
             if constexpr (V4)
                 lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
             else
@@ -162,14 +174,16 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     __syncthreads();
 
     // 3. per-thread weights and rolling accumulators
-    float wr[KH][KW];
+    float wr[M][KH][KW];
 #pragma unroll
-    for (int kh = 0; kh < KH; ++kh)
+    for (int jm = 0; jm < M; ++jm)
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw) {
-            const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
-            wr[kh][kw] = ldsw[pli * KK + tap];
-        }
+        for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < KW; ++kw) {
+                const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
+                wr[jm][kh][kw] = ldsw[(pli * M + jm) * KK + tap];
+            }
     if constexpr (EPI)
         epi_finish(ec, ep);
     float acc[R][Q];
@@ -179,7 +193,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
         for (int j = 0; j < Q; ++j)
             acc[r][j] = bval;
     constexpr int XW = Q + (KW - 1) * D;
-    const float *rowbase = lds + pli * G * twl + tx * Q + (a.hl - a.pW);
+    const float *rowbase = lds + pli * M * G * twl + tx * Q + (a.hl - a.pW);
     const int oc = w0 + tx * Q;                        // first output column of this thread
     float *outp = out + my_plane * a.YH * a.YW;
     const bool vec_store = !DEC && (Q > 1) && (a.OW % Q == 0);
@@ -188,20 +202,24 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
         if (u < nrows) {
             // a staged row of the upsampled dy at an odd position is all zero
             if (!(UPS && ((rbase + u) & 1))) {
-                float xv[XW];
 #pragma unroll
-                for (int i = 0; i < XW; ++i)
-                    xv[i] = rowbase[u * twl + i];
+                for (int jm = 0; jm < M; ++jm) {
+                    float xv[XW];
 #pragma unroll
-                for (int kh = 0; kh < KH; ++kh) {
-                    const int m = u - kh * D;
-                    if (m >= 0 && m < TH && !(DEC && ((h0 + m) & 1))) {
-                        const int slot = m % R;
+                    for (int i = 0; i < XW; ++i)
+                        xv[i] = rowbase[(jm * G + u) * twl + i];
 #pragma unroll
-                        for (int kw = 0; kw < KW; ++kw)
+                    for (int kh = 0; kh < KH; ++kh) {
+                        const int m = u - kh * D;
+                        if (m >= 0 && m < TH && !(DEC && ((h0 + m) & 1))) {
+                            const int slot = m % R;
 #pragma unroll
-                            for (int j = 0; j < Q; ++j)
-                                acc[slot][j] = fmaf(wr[kh][kw], xv[j + kw * D], acc[slot][j]);
+                            for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                                for (int j = 0; j < Q; ++j)
+                                    acc[slot][j] =
+                                        fmaf(wr[jm][kh][kw], xv[j + kw * D], acc[slot][j]);
+                        }
                     }
                 }
             }
@@ -276,13 +294,31 @@ void fill_all_tiled_nchw(TiledNchwFn (&fn)[NVAR][2][3], std::integer_sequence<in
     (fill_tiled_nchw<Vs, S>(fn[Vs]), ...);
 }
 
+// the input gradient with a channel multiplier of 2 (stride 1): [variant][f16 weights]
+template <int... Vs>
+void fill_tiled_nchw_m2(TiledNchwFn (&fn)[kNumTiledNchwVariants][2],
+                        std::integer_sequence<int, Vs...>)
+{
+    ((fn[Vs][0] = &k_tiled_nchw<float, kTiledNchwVariants[Vs].kH, kTiledNchwVariants[Vs].kW,
+                                kTiledNchwVariants[Vs].d, kTiledNchwVariants[Vs].q,
+                                kTiledNchwVariants[Vs].g, (kTiledNchwVariants[Vs].v4 != 0),
+                                kModeInputGrad, 1, 2>,
+      fn[Vs][1] = &k_tiled_nchw<half_t, kTiledNchwVariants[Vs].kH, kTiledNchwVariants[Vs].kW,
+                                kTiledNchwVariants[Vs].d, kTiledNchwVariants[Vs].q,
+                                kTiledNchwVariants[Vs].g, (kTiledNchwVariants[Vs].v4 != 0),
+                                kModeInputGrad, 1, 2>),
+     ...);
+}
+
 struct TiledNchwTable {
     TiledNchwFn fn[kNumTiledNchwVariants][2][3];
     TiledNchwFn fn2[kNumTiledNchwS2Variants][2][3];
+    TiledNchwFn fnm[kNumTiledNchwVariants][2];
     TiledNchwTable()
     {
         fill_all_tiled_nchw<1>(fn, std::make_integer_sequence<int, kNumTiledNchwVariants>());
         fill_all_tiled_nchw<2>(fn2, std::make_integer_sequence<int, kNumTiledNchwS2Variants>());
+        fill_tiled_nchw_m2(fnm, std::make_integer_sequence<int, kNumTiledNchwVariants>());
     }
 };
 
@@ -296,15 +332,23 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
     if (pl.variant < 0 || pl.variant >= nvar || pl.cl < 16 || pl.cl > 256 ||
         pl.pb != 256 / pl.cl)
         return DWCONV_ERR_BAD_STRATEGY;
-    TiledNchwFn f = p.stride == 1
-                        ? table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)]
-                        : table.fn2[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    // the input gradient with a multiplier: 2 at stride 1 only
+    const bool igm = p.op == DWCONV_OP_INPUT_GRAD && p.mult != 1;
+    if (igm && (p.mult != 2 || p.stride != 1))
+        return DWCONV_ERR_BAD_STRATEGY;
+    const int wt16 = p.wtype == DWCONV_W_F16;
+    TiledNchwFn f = igm ? table.fnm[pl.variant][wt16]
+                        : p.stride == 1 ? table.fn[pl.variant][wt16][mode_of(p, ep)]
+                                        : table.fn2[pl.variant][wt16][mode_of(p, ep)];
     if (!f)
         return DWCONV_ERR_BAD_STRATEGY;
     TiledNchwArgs a;
-    if (p.mult != 1 && p.op != DWCONV_OP_FWD)
-        return DWCONV_ERR_BAD_STRATEGY;
-    a.planes = p.N * p.mult * p.C; a.C = p.mult * p.C; a.mult = p.mult;
+    if (igm) {
+        // walk over the dx planes; each reads its 2 dy planes
+        a.planes = p.N * p.C; a.C = p.C; a.mult = 1;
+    } else {
+        a.planes = p.N * p.mult * p.C; a.C = p.mult * p.C; a.mult = p.mult;
+    }
     a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
     a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW; a.hl = pl.hl; a.twl = pl.twl;

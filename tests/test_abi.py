@@ -312,8 +312,8 @@ def test_same_pads_and_out_extents():
 
 def test_describe_ex_plans():
     """Same plans as the SAME entry points for SAME pads; tiled kernels with
-    any pads; direct kernels for a multiplier and for shapes without a tile;
-    even kernels run direct."""
+    any pads and the multipliers they take; direct kernels for the other
+    multipliers and for shapes without a tile; even kernels run direct."""
     same = dw.dwconv2d_describe(dw.OP_FWD, 1, 512, 512, 256, 3, 3)
     assert dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 512, 512, 256, 3, 3, pads=(1, 1, 1, 1)) == same
     name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 512, 512, 256, 3, 3, pads=(0, 0, 0, 0))
@@ -328,6 +328,9 @@ def test_describe_ex_plans():
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 112, 112, 30, 3, 3, mult=2)
     assert name.startswith("direct_nhwc")                          # C % 4 != 0
     name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 112, 112, 32, 3, 3, mult=2,
+                                            layout=dw.NCHW)
+    assert name.startswith("tiled_nchw_s1") and "_m2_" in name    # dx sums 2 dy planes
+    name, grid, _ = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, 1, 112, 112, 32, 3, 3, mult=3,
                                             layout=dw.NCHW)
     assert name.startswith("direct_nchw_s1") and grid == (112 * 112 * 32 + 255) // 256
     name, _, _ = dw.dwconv2d_describe_ex(dw.OP_FWD, 1, 16, 16, 32, 2, 2, pads=(0, 1, 0, 1))

@@ -148,12 +148,16 @@ def test_m2_tiled_random_within_bound(torch, idx, op):
 
 
 # NCHW: the tiled forward takes any multiplier (output plane n*mC + o reads
-# input plane n*C + o/m); its input gradient runs on the direct kernel.
+# input plane n*C + o/m); the tiled input gradient takes a multiplier of 2
+# (dx plane n*C + c sums dy planes (n*C + c)*2 + j), others run direct.
 NCHW_SHAPES = [
     (2, 37, 75, 6, 3, 2, None),
     (1, 56, 56, 16, 5, 3, (0, 0, 0, 0)),
     (3, 30, 19, 5, 7, 2, None),
     (1, 23, 300, 4, 3, 4, (-1, 2, 1, 0)),
+    (2, 20, 64, 8, 3, 2, None),            # 16-byte staging
+    (1, 40, 64, 8, 5, 2, (1, 2, 2, 1)),
+    (1, 30, 19, 4, 7, 2, (0, 0, 0, 0)),
 ]
 
 
@@ -182,6 +186,29 @@ def test_nchw_multiplier_forward_tiled(torch, idx):
                                     nthreads=NTHREADS)
         got = dw.fwd(_dev(torch, inp["x"]), _dev(torch, inp["w"]), _dev(torch, inp["b"]), 1, 1,
                      NCHW, dw.STRATEGY_TILED, pads=wl.pads, mult=wl.mult).cpu().numpy()
+        torch.cuda.synchronize()
+        if integer:
+            np.testing.assert_array_equal(got, ref.astype(np.float32))
+        else:
+            _within(got, ref, S, wl.name)
+
+
+@pytest.mark.parametrize("idx", [i for i, s in enumerate(NCHW_SHAPES) if s[5] == 2],
+                         ids=[_wl_nchw(s).name for s in NCHW_SHAPES if s[5] == 2])
+def test_nchw_multiplier2_input_grad_tiled(torch, idx):
+    import oracle
+    from depthwise_convolution_amd.workloads import NCHW
+    wl = _wl_nchw(NCHW_SHAPES[idx])
+    name = dw.dwconv2d_describe_ex(dw.OP_INPUT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, 1, 1,
+                                   wl.pads, 2, NCHW, 0, False, dw.STRATEGY_TILED)[0]
+    print(f"\n[case] nchw ig {wl.name} {name}", flush=True)
+    assert name.startswith("tiled_nchw") and "_m2_" in name
+    for integer, seed in ((True, 150 + idx), (False, 160 + idx)):
+        inp = wlmod.make_inputs(wl, NCHW, seed=seed, integer=integer)
+        ref, S = oracle.input_grad_general(inp["dy"], inp["w"], wl.H, wl.W, 1, 1, wl.pads, 2,
+                                           NCHW, nthreads=NTHREADS)
+        got = dw.input_grad(_dev(torch, inp["dy"]), _dev(torch, inp["w"]), wl.H, wl.W, 1, 1,
+                            NCHW, dw.STRATEGY_TILED, pads=wl.pads, mult=2).cpu().numpy()
         torch.cuda.synchronize()
         if integer:
             np.testing.assert_array_equal(got, ref.astype(np.float32))

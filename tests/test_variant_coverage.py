@@ -1,18 +1,19 @@
 """Every compiled tiled-kernel variant can be chosen by the planner, and every
-(variant, op) pair the planner chooses is checked against the oracle.
+(variant, op, multiplier) the planner chooses is checked against the oracle.
 
 The variant tables of csrc/dwconv_internal.h are parsed and each entry's plan
 name prefix is derived from its fields (the names `dwconv2d_describe_ex`
 reports).  A sweep of small problems (kernel shapes, strides, dilations,
 multipliers, channel counts with and without whole 16-byte vectors, image
 shapes, both layouts, all three ops) through the describe call (host only)
-finds, for every (variant, op) that can run, the first problem that runs it.
+finds, for every (variant, op, multiplier) that can run, the first problem
+that runs it.
 
 * CPU: every table entry is reached by at least one op (a variant no problem
   can select would be compiled for nothing);
-* GPU: each (variant, op) pair runs its problem under the TILED strategy on
-  integer inputs, where every summation order is exact, and must equal the
-  oracle bit for bit.
+* GPU: each (variant, op, multiplier) runs its problem under the TILED
+  strategy on integer inputs, where every summation order is exact, and must
+  equal the oracle bit for bit.
 """
 import os
 import re
@@ -67,7 +68,8 @@ def _expected_prefixes():
 
 
 def _sweep():
-    """{(prefix, op): problem} with problem = (N, H, W, C, kH, kW, s, d, mult, layout)."""
+    """{(prefix, op, mult): problem} with problem = (N, H, W, C, kH, kW, s, d, mult,
+    layout): a kernel may have an instantiation per multiplier."""
     prefixes = _expected_prefixes()
     found = {}
     for kh, kw, d in ((3, 3, 1), (5, 5, 1), (7, 7, 1), (7, 7, 2), (1, 15, 1), (1, 31, 1)):
@@ -87,8 +89,8 @@ def _sweep():
                                 except dw.DwconvError:
                                     continue
                                 for p in prefixes:
-                                    if name.startswith(p) and (p, op) not in found:
-                                        found[(p, op)] = (1, h, w, c, kh, kw, s, d, m, layout)
+                                    if name.startswith(p) and (p, op, m) not in found:
+                                        found[(p, op, m)] = (1, h, w, c, kh, kw, s, d, m, layout)
     return prefixes, found
 
 
@@ -97,7 +99,7 @@ CASES = sorted(FOUND.items())
 
 
 def test_every_variant_is_reachable():
-    reached = {p for p, _ in FOUND}
+    reached = {p for p, _, _ in FOUND}
     missing = sorted(p for p in PREFIXES if p not in reached)
     assert not missing, f"variants no problem selects: {missing}"
     assert len(PREFIXES) > 50
@@ -105,13 +107,13 @@ def test_every_variant_is_reachable():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("key,prob", CASES,
-                         ids=[f"{p}op{op}" for (p, op), _ in CASES])
+                         ids=[f"{p}op{op}m{m}" for (p, op, m), _ in CASES])
 def test_every_variant_matches_oracle(key, prob):
     import torch
     import oracle
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a visible GPU")
-    prefix, op = key
+    prefix, op, _ = key
     n, h, w, c, kh, kw, s, d, m, layout = prob
     pads = tuple(dw.dwconv2d_same_pads(dw.PAD_SAME, h, w, kh, kw, s, d))
     wl = Workload(name="cover", N=n, H=h, W=w, C=c, kH=kh, kW=kw, stride=s, dilation=d,
