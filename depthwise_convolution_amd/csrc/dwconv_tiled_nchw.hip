@@ -113,13 +113,29 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     // (upsampled) rows; a pair k of staged columns (2k, 2k+1) holds one dy
     // element at its even column and a zero at the other
     const int g0 = rbase & 1, ge_n = (G - g0 + 1) / 2, hp = twl / 2, c1 = cbase & 1;
+    // otherwise load e = tid + i*256 is (pj, g, cv) = (e / (G*vpr), e / vpr % G,
+    // e % vpr): the pair (gq = e / vpr, cv) is stepped by 256 per load with no
+    // further division
+    int s_cv = tid % vpr, s_gq = tid / vpr;
+    const int d_gq = 256 / vpr, d_cv = 256 - d_gq * vpr;
+    // (upsampled staging: e is (pl, ge, k) = (e / (ge_n*hp), e / hp % ge_n,
+    // e % hp), stepped the same way; ge_n is one of two compile-time values)
+    const int u_k0 = tid % hp, u_gq0 = tid / hp;
+    const int u_dgq = 256 / hp, u_dk = 256 - u_dgq * hp;
+    constexpr int GEA = (G + 1) / 2, GEB = G / 2;
+    int u_k = u_k0, u_gq = u_gq0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
         if constexpr (UPS) {
-            const int pl = e / (ge_n * hp);
-            const int rem = e - pl * (ge_n * hp);
-            const int ge = rem / hp, k = rem - ge * hp;
+            const int pl = ge_n == GEA ? u_gq / GEA : u_gq / GEB;
+            const int ge = u_gq - pl * ge_n, k = u_k;
+            u_k += u_dk;
+            u_gq += u_dgq;
+            if (u_k >= hp) {
+                u_k -= hp;
+                ++u_gq;
+            }
             const int g = g0 + 2 * ge;
             const int plane = pg * pbn + pl, row = rbase + g, col = cbase + 2 * k + c1;
             const int sr = row >> 1, sc = col >> 1;    // position in dy (row, col are even)
@@ -127,10 +143,15 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
                             col >= 0 && sr < a.IH && sc < a.IW;
             sv[i][0] = buf_f32(rx, ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange);
         } else {
-            const int pj = e / (G * vpr);                  // pl*M + j
-            const int rem = e - pj * (G * vpr);
-            const int g = rem / vpr;
-            const int col = cbase + (rem - g * vpr) * LV;
+            const int pj = s_gq / G;                       // pl*M + j
+            const int g = s_gq - pj * G;
+            const int col = cbase + s_cv * LV;
+            s_cv += d_cv;
+            s_gq += d_gq;
+            if (s_cv >= vpr) {
+                s_cv -= vpr;
+                ++s_gq;
+            }
             const int pl = pj / M, plane = pg * pbn + pl, row = rbase + g;
             const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
                             row < a.IH && col >= 0 && col < a.IW;
@@ -147,6 +168,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
         }
     }
     // 2. into LDS
+    u_k = u_k0;
+    u_gq = u_gq0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int e = tid + i * 256;
@@ -157,10 +180,15 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
         if constexpr (UPS) {
+            const int pl = ge_n == GEA ? u_gq / GEA : u_gq / GEB;
+            const int ge = u_gq - pl * ge_n, k = u_k;
+            u_k += u_dk;
+            u_gq += u_dgq;
+            if (u_k >= hp) {
+                u_k -= hp;
+                ++u_gq;
+            }
             if (e < pbn * ge_n * hp) {
-                const int pl = e / (ge_n * hp);
-                const int rem = e - pl * (ge_n * hp);
-                const int ge = rem / hp, k = rem - ge * hp;
                 float2 *dst = reinterpret_cast<float2 *>(lds + (pl * G + g0 + 2 * ge) * twl);
                 dst[k] = c1 ? make_float2(0.0f, sv[i][0]) : make_float2(sv[i][0], 0.0f);
             }
