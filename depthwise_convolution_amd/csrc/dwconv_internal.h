@@ -47,11 +47,11 @@ Problem same_problem(int op, int wtype, int has_bias, int N, int H, int W, int C
 enum Kind {
     KIND_DIRECT_NHWC = 1,  // one thread per (n, row, col, channel vector); taps from global
     KIND_DIRECT_NCHW = 2,  // one thread per (n, channel, row, col); taps from global
-    KIND_TILED_NHWC = 3,   // stride 1: LDS row chunks with halo, rolling row accumulators
-    KIND_TILED_NCHW = 4,   // stride 1: LDS tiles of one or more planes, rolling row accumulators
+    KIND_TILED_NHWC = 3,   // stride 1 or 2: LDS row chunks with halo, rolling row accumulators
+    KIND_TILED_NCHW = 4,   // stride 1 or 2: LDS tiles of one or more planes, rolling row accumulators
     KIND_WGRAD_DIRECT = 5, // weight gradient, any layout/stride: lanes along the contiguous axis
-    KIND_WGRAD_TILED_NHWC = 6, // weight gradient, NHWC stride 1: LDS x tiles, strips of row tiles
-    KIND_WGRAD_TILED_NCHW = 7, // weight gradient, NCHW stride 1: LDS x plane rows, dy in registers
+    KIND_WGRAD_TILED_NHWC = 6, // weight gradient, NHWC stride 1 or 2: LDS x tiles, strips of row tiles
+    KIND_WGRAD_TILED_NCHW = 7, // weight gradient, NCHW stride 1 or 2: LDS x plane rows, dy in registers
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only

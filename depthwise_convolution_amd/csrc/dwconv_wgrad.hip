@@ -309,14 +309,14 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     }
 }
 
-// Stage 1, NCHW stride 1: the NCHW forward's tiling with the roles of the
-// operands changed.  A workgroup covers pb dy planes x tx threads per plane
-// row (Q adjacent columns each) and walks `strip` row tiles of one column
-// tile; per row tile it stages the G x rows (+ column halo) of its planes'
-// input planes in LDS and loads its dy values into registers, and every
-// thread accumulates x*dy for all kH*kW taps (and dy for the bias) of its
-// plane.  The tx threads of each plane are then added with a fixed tree in
-// LDS, TG taps at a time.
+// Stage 1, NCHW, stride 1 or 2: the NCHW forward's tiling with the roles of
+// the operands changed.  A workgroup covers pb dy planes x tx threads per
+// plane row (Q adjacent columns each) and walks `strip` row tiles of one
+// column tile; per row tile it stages the G x rows (+ column halo) of its
+// planes' input planes in LDS and loads its dy values into registers, and
+// every thread accumulates x*dy for all kH*kW taps (and dy for the bias) of
+// its plane.  At the end every thread parks its sums in LDS and each
+// (plane, tap) column is added over the plane's tx threads in thread order.
 struct WgradNchwArgs {
     int planes, C, mult;        // dy planes (N * C), dy channels, channel multiplier
     int H, W, OH, OW;           // x extents, dy extents
