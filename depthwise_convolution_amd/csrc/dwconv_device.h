@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
 #include <utility>
 
 #include "dwconv_internal.h"
@@ -283,6 +284,26 @@ inline int mode_of(const Problem &p, const EpiArgs &ep)
 }
 
 }  // namespace
+
+// Enqueue kernel k with its own launch status (hipLaunchKernel's return
+// value, not the thread's last-error slot, which other code may have left
+// set).  Arguments are converted to the kernel's parameter types.
+template <typename... P, typename... A>
+int launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t lds_bytes, hipStream_t st,
+                  A &&...args)
+{
+    static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+    std::tuple<P...> params(std::forward<A>(args)...);
+    return std::apply(
+        [&](auto &...q) {
+            void *argv[] = {static_cast<void *>(&q)...};
+            return hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, argv,
+                                   lds_bytes, st) == hipSuccess
+                       ? DWCONV_OK
+                       : DWCONV_ERR_LAUNCH;
+        },
+        params);
+}
 
 // Launchers of the kernel families (one translation unit each): each
 // enqueues its kernels on `st` and returns a DWCONV_ status.

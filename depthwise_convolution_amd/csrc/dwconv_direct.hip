@@ -179,7 +179,7 @@ DirectArgs direct_args(const Problem &p, const Plan &pl)
 }
 
 template <typename WT>
-void launch_direct_t(const Problem &p, const Plan &pl, const float *in, const void *wv,
+int launch_direct_t(const Problem &p, const Plan &pl, const float *in, const void *wv,
                    const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     const DirectArgs a = direct_args(p, pl);
@@ -188,9 +188,9 @@ void launch_direct_t(const Problem &p, const Plan &pl, const float *in, const vo
     const bool ig = p.op == DWCONV_OP_INPUT_GRAD;
     const int s = p.stride;
 #define DW_DIRECT_NHWC(V, IGV, SV) \
-    hipLaunchKernelGGL((k_direct_nhwc<WT, V, IGV, SV>), grid, block, 0, st, in, w, b, out, a, ep)
+    return launch_kernel(&k_direct_nhwc<WT, V, IGV, SV>, grid, block, 0, st, in, w, b, out, a, ep)
 #define DW_DIRECT_NCHW(IGV, SV) \
-    hipLaunchKernelGGL((k_direct_nchw<WT, IGV, SV>), grid, block, 0, st, in, w, b, out, a, ep)
+    return launch_kernel(&k_direct_nchw<WT, IGV, SV>, grid, block, 0, st, in, w, b, out, a, ep)
     if (pl.kind == KIND_DIRECT_NHWC) {
         if (pl.vec == 4) {
             if (!ig) { if (s == 1) DW_DIRECT_NHWC(4, false, 1); else DW_DIRECT_NHWC(4, false, 2); }
@@ -213,10 +213,8 @@ int launch_direct(const Problem &p, const Plan &pl, const float *in, const void 
                   const float *b, float *out, hipStream_t st, const EpiArgs &ep)
 {
     if (p.wtype == DWCONV_W_F16)
-        launch_direct_t<half_t>(p, pl, in, w, b, out, st, ep);
-    else
-        launch_direct_t<float>(p, pl, in, w, b, out, st, ep);
-    return DWCONV_OK;
+        return launch_direct_t<half_t>(p, pl, in, w, b, out, st, ep);
+    return launch_direct_t<float>(p, pl, in, w, b, out, st, ep);
 }
 
 }  // namespace dwconv

@@ -17,24 +17,17 @@ int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w
         ep.act = epi->act;
         ep.on = 1;
     }
-    int st = DWCONV_OK;
     switch (pl.kind) {
     case KIND_DIRECT_NHWC:
     case KIND_DIRECT_NCHW:
-        st = launch_direct(p, pl, in, w, bb, out, stream, ep);
-        break;
+        return launch_direct(p, pl, in, w, bb, out, stream, ep);
     case KIND_TILED_NHWC:
-        st = launch_tiled_nhwc(p, pl, in, w, bb, out, stream, ep);
-        break;
+        return launch_tiled_nhwc(p, pl, in, w, bb, out, stream, ep);
     case KIND_TILED_NCHW:
-        st = launch_tiled_nchw(p, pl, in, w, bb, out, stream, ep);
-        break;
+        return launch_tiled_nchw(p, pl, in, w, bb, out, stream, ep);
     default:
         return DWCONV_ERR_BAD_STRATEGY;
     }
-    if (st != DWCONV_OK)
-        return st;
-    return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
 }
 
 }  // namespace dwconv

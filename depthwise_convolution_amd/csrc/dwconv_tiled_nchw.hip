@@ -126,7 +126,6 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     int u_k = u_k0, u_gq = u_gq0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e = tid + i * 256;
         if constexpr (UPS) {
             const int pl = ge_n == GEA ? u_gq / GEA : u_gq / GEB;
             const int ge = u_gq - pl * ge_n, k = u_k;
@@ -383,9 +382,8 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
     a.txn = pl.cl;
     a.pbn = pl.pb;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
-    hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
-                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
-    return DWCONV_OK;
+    return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
+                         p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }
 
 

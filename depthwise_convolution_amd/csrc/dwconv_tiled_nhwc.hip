@@ -369,9 +369,8 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
     a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
-    hipLaunchKernelGGL(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
-                       p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
-    return DWCONV_OK;
+    return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
+                         p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }
 
 

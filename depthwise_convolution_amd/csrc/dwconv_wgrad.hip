@@ -609,6 +609,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     a.H = p.H; a.W = p.W; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
     a.pH = pl.pH; a.pW = pl.pW; a.OH = pl.OH; a.OW = pl.OW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.strip = pl.strip; a.chunks = (int)pl.chunks;
+    int st1;                                  // status of the stage-1 launch
     if (pl.kind == KIND_WGRAD_TILED_NHWC) {
         static const WgradTable table;
         const bool m2 = p.mult == 2;
@@ -618,9 +619,9 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
                             : p.stride == 1 ? kNumWgradVariants : kNumWgradS2Variants;
         if (pl.variant < 0 || pl.variant >= nvar)
             return DWCONV_ERR_BAD_STRATEGY;
-        hipLaunchKernelGGL(m2 ? table.fnm[pl.variant]
-                              : p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
-                           dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy, part, a);
+        st1 = launch_kernel(m2 ? table.fnm[pl.variant]
+                               : p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
+                            dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy, part, a);
     } else if (pl.kind == KIND_WGRAD_TILED_NCHW) {
         static const WgradNchwTable table;
         const int nvar = p.stride == 1 ? kNumWgradNchwVariants : kNumWgradNchwS2Variants;
@@ -634,8 +635,8 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.txn = pl.cl;
         g.pbn = pl.pb;
         g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.nrt;
-        hipLaunchKernelGGL(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
-                           dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, x, dy, part, g);
+        st1 = launch_kernel(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
+                            dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, x, dy, part, g);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
         WgradGenArgs g;
         g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;
@@ -644,21 +645,17 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.cl = pl.cl; g.ncg = pl.nct; g.ppc = pl.ppc; g.cpi = pl.cpi;
         const dim3 gr((unsigned)pl.grid), b(256);
         const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
-        if (nhwc && p.stride == 1)
-            hipLaunchKernelGGL((k_wgrad_gen<true, 1>), gr, b, 0, st, x, dy, part, g);
-        else if (nhwc)
-            hipLaunchKernelGGL((k_wgrad_gen<true, 2>), gr, b, 0, st, x, dy, part, g);
-        else if (p.stride == 1)
-            hipLaunchKernelGGL((k_wgrad_gen<false, 1>), gr, b, 0, st, x, dy, part, g);
-        else
-            hipLaunchKernelGGL((k_wgrad_gen<false, 2>), gr, b, 0, st, x, dy, part, g);
+        auto k = nhwc ? (p.stride == 1 ? &k_wgrad_gen<true, 1> : &k_wgrad_gen<true, 2>)
+                      : (p.stride == 1 ? &k_wgrad_gen<false, 1> : &k_wgrad_gen<false, 2>);
+        st1 = launch_kernel(k, gr, b, 0, st, x, dy, part, g);
     } else {
         return DWCONV_ERR_BAD_STRATEGY;
     }
-    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw, db,
-                       (int)pl.chunks, p.mult * p.C, p.kH * p.kW, w_upd,
-                       w_upd ? b_upd : nullptr, lr);
-    return hipGetLastError() == hipSuccess ? DWCONV_OK : DWCONV_ERR_LAUNCH;
+    if (st1 != DWCONV_OK)
+        return st1;
+    return launch_kernel(&k_wgrad_reduce, dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw,
+                         db, (int)pl.chunks, p.mult * p.C, p.kH * p.kW, w_upd,
+                         w_upd ? b_upd : nullptr, lr);
 }
 
 }  // namespace dwconv
