@@ -304,9 +304,9 @@ def main():
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the operator shards over N and C with no exchange; see DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py runs on one GPU only: there is no multi-GPU path (the operator "
+              "shards over images and channels with no exchange between GPUs, so each GPU "
+              "would run this same kernel on its own share)", file=sys.stderr)
         sys.exit(2)
 
     import torch
