@@ -102,6 +102,24 @@ __device__ __forceinline__ void store_vec(float *p, const float (&v)[V])
     }
 }
 
+// Workgroup -> tile order.  MI355X hands the workgroups of a launch to its
+// 8 XCDs in turn (workgroup b runs on XCD b % 8), and each XCD has an L2 of
+// its own.  The tiled kernels number their tiles so that tiles sharing halo
+// rows or columns are close in the numbering (in NCHW the row tiles of a
+// plane group are consecutive).  For problems up to a few hundred MiB the
+// plan has workgroup b take tile xcd_tile(b): XCD k then runs one
+// contiguous range of tiles, in order, so a halo that a tile shares with its
+// neighbours is read from HBM once into that XCD's L2.  Larger problems take
+// tile b: all XCDs sweep the tensor front to back together, which streams
+// from HBM faster than eight separate ranges.
+// A bijection of [0, nb): XCD k < nb % 8 takes nb / 8 + 1 tiles, the others
+// nb / 8.
+__device__ __forceinline__ int xcd_tile(int b, int nb)
+{
+    const int per = nb >> 3, extra = nb & 7, k = b & 7;
+    return k * per + min(k, extra) + (b >> 3);
+}
+
 // Raw buffer loads (gfx9 family buffer descriptors, stride 0): an offset at
 // or beyond the descriptor's byte count reads as zero in hardware, which
 // gives zero padding and tail handling without branches around the loads.

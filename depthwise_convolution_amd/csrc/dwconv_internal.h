@@ -116,6 +116,15 @@ constexpr WgradVariant kWgradVariants[] = {
     {1, 15, 1, 1, 32, 1, 2, 1}, {1, 31, 1, 1, 32, 1, 2, 1},
 };
 constexpr long long kWgradTargetWorkgroups = 512;
+
+// Tile order of the tiled kernels.  Below this many bytes of activations
+// (the tensor an op reads plus the one it writes, or x plus dy for the
+// weight gradient) each XCD takes a contiguous range of tiles, so the halos
+// neighbouring tiles share stay in one L2; from it on, all XCDs sweep the
+// tiles in order together, which streams a large tensor from HBM faster.
+// Measured on MI355X (NHWC and NCHW, all three ops): the per-XCD ranges are
+// 3-15% faster up to 374 MiB, equal at 512 MiB and 5% slower at 1 GiB.
+constexpr long long kXcdRangeMaxBytes = 448LL << 20;
 constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);
 
 // Variants of the tiled NHWC weight gradient at stride 2 (g = staged x rows
@@ -217,6 +226,7 @@ struct Plan {
     int nct, nwt, nst;  // tiled: channel tiles (NHWC) or plane groups (NCHW), column tiles,
                         // row tiles (weight gradient: strips of row tiles)
     int pb;             // tiled NCHW: planes per workgroup (256 / cl)
+    int xcd;            // tiled: 1 = each XCD takes a contiguous range of tiles, 0 = in order
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
     int hl, twl;        // tiled NCHW: staged columns left of a tile, staged floats per row
     int nrt;            // weight gradient, tiled: row tiles per image / plane

@@ -279,6 +279,15 @@ static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
                   op_tag(p), p.wtype ? "f16w" : "f32w");
 }
 
+// Tile order of a tiled plan (kXcdRangeMaxBytes): activations are the
+// tensor read and the tensor written, x and y (or dy and dx, x and dy).
+static int xcd_ranges(const Problem &p)
+{
+    const long long act =
+        4LL * p.N * p.C * ((long long)p.H * p.W + (long long)p.mult * p.Ho * p.Wo);
+    return act < kXcdRangeMaxBytes ? 1 : 0;
+}
+
 int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
 {
     if (p.op == DWCONV_OP_WEIGHT_GRAD)
@@ -305,6 +314,7 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         tiled = false;
     if (tiled) {
         *pl = t;
+        pl->xcd = xcd_ranges(p);
         return DWCONV_OK;
     }
     if (strategy == DWCONV_STRATEGY_TILED)
@@ -509,9 +519,10 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         Plan t = *pl;
         tiled = p.layout == DWCONV_LAYOUT_NHWC ? plan_wgrad_tiled(p, ptr_bits, &t)
                                                : plan_wgrad_tiled_nchw(p, ptr_bits, &t);
-        if (tiled)
+        if (tiled) {
             *pl = t;
-        else if (strategy == DWCONV_STRATEGY_TILED)
+            pl->xcd = xcd_ranges(p);
+        } else if (strategy == DWCONV_STRATEGY_TILED)
             return DWCONV_ERR_BAD_STRATEGY;
     }
     if (!tiled)

@@ -30,6 +30,7 @@ struct TiledNchwArgs {
     int hl, twl;            // staged columns left of a tile; staged floats per plane row
     int txn, pbn;           // threads per plane row (16..256), planes per workgroup (256 / txn)
     int nct, nwt, nst;      // plane groups, column tiles, row tiles
+    int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 0 = in order
 };
 
 
@@ -69,11 +70,13 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const int vpr = twl / LV;                          // loads per plane row
     float *ldsw = lds + pbn * M * G * twl;
 
-    int tile = blockIdx.x;
-    const int pg = tile % a.nct;
-    tile /= a.nct;
+    // tiles: row tile, column tile, plane group (fastest first), so the row
+    // tiles of a plane group, which share halo rows, are consecutive
+    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int st = tile % a.nst;
+    tile /= a.nst;
     const int wt = tile % a.nwt;
-    const int st = tile / a.nwt;
+    const int pg = tile / a.nwt;
     const int w0 = wt * tw, h0 = st * TH;
     const int tid = threadIdx.x;
     const int nrows = min(TH, a.OH - h0) + R - 1;
@@ -382,6 +385,7 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
     a.txn = pl.cl;
     a.pbn = pl.pb;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
+    a.xcd = pl.xcd;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }

@@ -28,6 +28,7 @@ struct TiledArgs {
     int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
     int pH, pW;             // top / left zero padding of the tensor read
     int nct, nwt, nst;      // channel tiles, column tiles, row tiles
+    int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 0 = in order
 };
 
 // LV: floats per staging load, 4 (16-byte loads: C % 4 == 0, 16-byte
@@ -97,7 +98,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     float *ldsw = ldsx + XF4 * 4;
     const WT *w = reinterpret_cast<const WT *>(wv);
 
-    int tile = blockIdx.x;
+    // tiles: channel tile, column tile, row tile, image (fastest first)
+    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
     const int ct = tile % a.nct;
     tile /= a.nct;
     const int wt = tile % a.nwt;
@@ -369,6 +371,7 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
     a.YH = pl.YH; a.YW = pl.YW;
     a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
+    a.xcd = pl.xcd;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }

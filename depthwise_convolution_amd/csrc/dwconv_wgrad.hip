@@ -23,6 +23,7 @@ struct WgradArgs {
     int nct, nwt, nsp;      // tiled: channel tiles, column tiles, strips
     int strip;              // tiled: row tiles per strip
     int chunks;             // rows of part[]
+    int xcd;                // tiled: tile order, 1 = per-XCD ranges (xcd_tile), 0 = in order
 };
 
 // Stage 1, any layout, stride, padding and multiplier.  Lanes run along the
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     __shared__ float4 lds4[(LDSF + 3) / 4];
     float *lds = reinterpret_cast<float *>(lds4);
 
-    int tile = blockIdx.x;
+    // tiles: channel tile, column tile, strip, image (fastest first)
+    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
     const int ct = tile % a.nct;
     tile /= a.nct;
     const int chunk = tile;                 // (n, strip, column tile): row of part[]
@@ -324,6 +326,7 @@ struct WgradNchwArgs {
     int txn, pbn;               // threads per plane row (16..256), planes per workgroup
     int nct, nwt, nsp, strip;   // plane groups, column tiles, strips, row tiles per strip
     int nrt;                    // row tiles per plane
+    int xcd;                    // tile order: 1 = per-XCD ranges (xcd_tile), 0 = in order
 };
 
 // At stride S = 2 a row tile of TH dy rows reads 2*TH - 1 + (kH-1)*d x rows,
@@ -348,11 +351,12 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
 
     const int txn = a.txn, pbn = a.pbn;
     const int tw = txn * Q, twl = a.twl, vpr = twl / LV;
-    int tile = blockIdx.x;
-    const int pg = tile % a.nct;
-    tile /= a.nct;
+    // tiles: strip, column tile, plane group (fastest first)
+    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int sp = tile % a.nsp;
+    tile /= a.nsp;
     const int wt = tile % a.nwt;
-    const int sp = tile / a.nwt;
+    const int pg = tile / a.nwt;
     const int w0 = wt * tw;
     const int tid = threadIdx.x;
     // threads past pbn * txn (when txn does not divide 256) idle along
@@ -609,6 +613,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     a.H = p.H; a.W = p.W; a.kH = p.kH; a.kW = p.kW; a.d = p.dilation;
     a.pH = pl.pH; a.pW = pl.pW; a.OH = pl.OH; a.OW = pl.OW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nsp = pl.nst; a.strip = pl.strip; a.chunks = (int)pl.chunks;
+    a.xcd = pl.xcd;
     int st1;                                  // status of the stage-1 launch
     if (pl.kind == KIND_WGRAD_TILED_NHWC) {
         static const WgradTable table;
@@ -635,6 +640,7 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.txn = pl.cl;
         g.pbn = pl.pb;
         g.nct = pl.nct; g.nwt = pl.nwt; g.nsp = pl.nst; g.strip = pl.strip; g.nrt = pl.nrt;
+        g.xcd = pl.xcd;
         st1 = launch_kernel(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
                             dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, x, dy, part, g);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
