@@ -151,57 +151,81 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
         for (int v = 0; v < VEC; ++v)
             ec[v] = epi_load(ep, cq + v, a.C);
     }
+    // Staged load e = tid + 256*i is vector cv of staged pixel (g, col):
+    // e = (g * TWI + col) * VPC + cv.  VPC is a power of two that divides
+    // 256, so cv (hence the channel) is the same for all of a thread's loads,
+    // and (g, col) advance by a fixed step from one load to the next.  A load
+    // with g < nrows (<= G) is one of the VCH staged loads.
+    static_assert((VPC & (VPC - 1)) == 0 && 256 % VPC == 0, "staging vectors per pixel");
+    constexpr int DG = 256 / VPR, DC = (256 % VPR) / VPC;
+    const int cv = tid % VPC;
+    // channel of the tensor read (with XM: an input channel of the tile's c0 / M ..)
+    const int ch = (XM ? c0 / M : c0) + cv * LV;
+    const bool chok = ch < a.CR;
+    int g = tid / VPR, col = (tid % VPR) / VPC;
+    // without upsampling the byte offset of (g, col) steps with them
+    // (unsigned: positions outside the image may wrap, they are not loaded)
+    const unsigned pstep = 4u * a.CR, rstep = pstep * a.IW;
+    unsigned uoff = (unsigned)(rbase + g) * rstep + (unsigned)(cbase + col) * pstep + 4u * ch;
     typedef typename VecT<LV>::type LoadT;
     LoadT stage[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e = tid + i * 256;
-        const int g = e / VPR;
-        const int rem = e - g * VPR;
-        const int col = rem / VPC;
-        const int cv = rem - col * VPC;
-        // channel of the tensor read (with XM: an input channel of the tile's c0 / M ..)
-        const int ch = (XM ? c0 / M : c0) + cv * LV;
-        const int row = rbase + g, gc = cbase + col;
-        bool ok = e < VCH && g < nrows && row >= 0 && gc >= 0 && ch < a.CR;
-        int sr = row, sc = gc;                  // position in the tensor read
-        if constexpr (UPS) {
-            ok = ok && (row & 1) == 0 && (gc & 1) == 0;
-            sr = row >> 1;
-            sc = gc >> 1;
+        if (i > 0) {
+            g += DG;
+            col += DC;
+            uoff += DG * rstep + DC * pstep;
+            if (col >= TWI) {
+                col -= TWI;
+                ++g;
+                uoff += rstep - TWI * pstep;
+            }
         }
-        ok = ok && sr < a.IH && sc < a.IW;
-        const int off = ok ? ((sr * a.IW + sc) * a.CR + ch) * 4 : kOutOfRange;
+        const int row = rbase + g, gc = cbase + col;
+        int off;
+        if constexpr (UPS) {
+            // upsampled position (row, gc) holds dy[row/2][gc/2] when both are even
+            const bool ok = chok && g < nrows && ((row | gc) & 1) == 0 &&
+                            (unsigned)row < 2u * (unsigned)a.IH &&
+                            (unsigned)gc < 2u * (unsigned)a.IW;
+            off = ok ? (((row >> 1) * a.IW + (gc >> 1)) * a.CR + ch) * 4 : kOutOfRange;
+        } else {
+            const bool ok = chok && g < nrows && (unsigned)row < (unsigned)a.IH &&
+                            (unsigned)gc < (unsigned)a.IW;
+            off = ok ? (int)uoff : kOutOfRange;
+        }
         if constexpr (LV == 4)
             stage[i] = buf_f4(rx, off);
         else
             stage[i] = buf_f32(rx, off);
     }
-    // 2. weights, then the tile, into LDS
+    // 2. weights, then the tile, into LDS (only a last, partial round of
+    // loads needs a bound)
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int e = tid + i * 256;
-        if (e < WF)
+        if ((i + 1) * 256 <= WF || e < WF)
             ldsw[e] = wst[i];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = tid + i * 256;
-        if constexpr (XM) {
-            // input channels ch .. ch+3 feed output slots M*ch .. M*ch + 4M - 1
-            if (e < VCH) {
+        if ((i + 1) * 256 <= VCH || e < VCH) {
+            if constexpr (XM) {
+                // input channels ch .. ch+3 feed output slots M*ch .. M*ch + 4M - 1
                 const float4 v = stage[i];
                 lds[2 * e] = make_float4(v.x, v.x, v.y, v.y);
                 lds[2 * e + 1] = make_float4(v.z, v.z, v.w, v.w);
+            } else {
+                reinterpret_cast<LoadT *>(lds)[e] = stage[i];
             }
-        } else if (e < VCH) {
-            reinterpret_cast<LoadT *>(lds)[e] = stage[i];
         }
     }
     __syncthreads();
 
     // per-thread weights (reversed taps for the input gradient)
     float wr[KH][KW][VEC];
+    const float *wq = ldsw + q * VEC * KK;
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
@@ -209,7 +233,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
-                wr[kh][kw][v] = ldsw[(q * VEC + v) * KK + tap];
+                wr[kh][kw][v] = wq[v * KK + tap];
             }
     if constexpr (EPI) {
 #pragma unroll
@@ -228,6 +252,9 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     // 3. walk the staged rows
     constexpr int XW = PX + (KW - 1) * D;  // staged columns one thread reads per row
     float *outp = out + (n * a.YH * a.YW) * a.CW;
+    // this thread's first output of the tile's first row (not DEC, not IG with M > 1)
+    float *orow = outp + ((h0 * a.OW + ow) * a.CW + cq);
+    const int ors = a.OW * a.CW;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -283,7 +310,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
                             store_vec<VEC / M>(outp + ((r * a.OW + ow + j) * a.CW + cq / M), sum);
                         }
                     } else if (cvalid && ow + j < a.OW) {
-                        store_vec<VEC>(outp + ((r * a.OW + ow + j) * a.CW + cq), acc[m % R][j]);
+                        store_vec<VEC>(orow + (m * ors + j * a.CW), acc[m % R][j]);
                     }
 #pragma unroll
                     for (int v = 0; v < VEC; ++v)

@@ -206,25 +206,46 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
         for (int v = 0; v < VEC; ++v)
             acc[t][v] = 0.0f;
 
+    // Staged load e = tid + 256*i is vector cv of staged pixel (g, col):
+    // e = (g * TWI + col) * VPC + cv.  VPC is a power of two that divides
+    // 256, so cv (hence the x channel) is the same for all of a thread's
+    // loads, and (g, col) and the byte offset advance by a fixed step from
+    // one load to the next.  A load with g < nrows (<= G) is one of the VCH
+    // staged loads.
+    static_assert((VPC & (VPC - 1)) == 0 && 256 % VPC == 0, "staging vectors per pixel");
+    constexpr int DG = 256 / VPR, DC = (256 % VPR) / VPC;
+    const int ch = c0 / M + (tid % VPC) * LV;             // x channel
+    const bool chok = ch < CX;
+    const int g0 = tid / VPR, col0 = (tid % VPR) / VPC;
+    const unsigned pstep = 4u * CX, rstep = pstep * a.W;
+
     const int t0 = sp * a.strip, t1 = min(t0 + a.strip, (a.OH + TH - 1) / TH);
     for (int tt = t0; tt < t1; ++tt) {
         const int h0 = tt * TH;
         const int nrows = S * (min(TH, a.OH - h0) - 1) + R;
         const int rbase = S * h0 - a.pH;
         // this row tile's x rows (+ halo) and, per thread, its dy values
+        // (unsigned offsets: positions outside the image may wrap, they are not loaded)
         typedef typename VecT<LV>::type LoadT;
         LoadT stage[NV];
+        int g = g0, col = col0;
+        unsigned uoff = (unsigned)(rbase + g) * rstep + (unsigned)(cbase + col) * pstep + 4u * ch;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int e = tid + i * 256;
-            const int g = e / VPR;
-            const int rem = e - g * VPR;
-            const int col = rem / VPC;
-            const int cv = rem - col * VPC;
-            const int row = rbase + g, gc = cbase + col, ch = c0 / M + cv * LV;   // x channel
-            const bool ok = e < VCH && g < nrows && row >= 0 && row < a.H && gc >= 0 &&
-                            gc < a.W && ch < CX;
-            const int off = ok ? ((row * a.W + gc) * CX + ch) * 4 : kOutOfRange;
+            if (i > 0) {
+                g += DG;
+                col += DC;
+                uoff += DG * rstep + DC * pstep;
+                if (col >= TWI) {
+                    col -= TWI;
+                    ++g;
+                    uoff += rstep - TWI * pstep;
+                }
+            }
+            const int row = rbase + g, gc = cbase + col;
+            const bool ok = chok && g < nrows && (unsigned)row < (unsigned)a.H &&
+                            (unsigned)gc < (unsigned)a.W;
+            const int off = ok ? (int)uoff : kOutOfRange;
             if constexpr (LV == 4)
                 stage[i] = buf_f4(rx, off);
             else
@@ -244,7 +265,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = tid + i * 256;
-            if (e < VCH) {
+            if ((i + 1) * 256 <= VCH || e < VCH) {
                 if constexpr (M == 2) {
                     // x channels ch .. ch+3 feed dy channel slots 2*ch .. 2*ch + 7
                     const float4 v = stage[i];
