@@ -148,6 +148,25 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Raw buffer load straight into LDS (the LDS flag of gfx950's buffer loads):
+// lane k of the wave writes its BYTES (4 or 16) to lds + k*BYTES, where
+// `lds` is the same in every lane; an offset outside the buffer writes
+// zeros.  The data reaches LDS asynchronously: drain the wave's vector
+// memory counter (vm_drain) before the barrier that hands the tile to the
+// other waves.
+template <int BYTES>
+__device__ __forceinline__ void buf_to_lds(__amdgpu_buffer_rsrc_t r, float *lds, int off)
+{
+    static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte loads");
+    auto *dst = (__attribute__((address_space(3))) void *)lds;
+    if constexpr (BYTES == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 typedef unsigned int u2_ext __attribute__((ext_vector_type(2)));
 
 // V consecutive floats (V = 1, 2 or 4) with one buffer load of matching width.

@@ -117,6 +117,10 @@ constexpr WgradVariant kWgradVariants[] = {
 };
 constexpr long long kWgradTargetWorkgroups = 512;
 
+// Dynamic LDS a plan may ask for (the launch default, without raising the
+// kernel's limit).
+constexpr int kMaxLdsBytes = 64 * 1024;
+
 // Tile order of the tiled kernels.  Below this many bytes of activations
 // (the tensor an op reads plus the one it writes, or x plus dy for the
 // weight gradient) each XCD takes a contiguous range of tiles, so the halos

@@ -449,7 +449,11 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     pl->chunks = (long long)p.N * pl->nwt * pl->nst;
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     const int kp = (p.kH * p.kW + 1) | 1;                        // per-thread sums, padded
-    pl->lds_bytes = 4 * std::max(pl->pb * v.g * pl->twl, kp * 256);
+    // the x tile (4-byte staging loads it into LDS by whole waves of 64)
+    const int tile_floats = (pl->pb * v.g * (pl->twl / lv) + 63) / 64 * 64 * lv;
+    pl->lds_bytes = 4 * std::max(tile_floats, kp * 256);
+    if (pl->lds_bytes > kMaxLdsBytes)
+        return false;
     pl->block = 256;
     std::snprintf(pl->name, sizeof pl->name, "wgrad_tiled_nchw_s%d_k%dx%d_d%d_q%d_g%d_%s_tx%d_s%d",
                   p.stride, v.kH, v.kW, v.d, v.q, v.g, v.v4 ? "v4" : "v1", tx, pl->strip);

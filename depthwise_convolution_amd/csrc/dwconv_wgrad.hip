@@ -397,54 +397,100 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     for (int t = 0; t <= KK; ++t)
         acc[t] = 0.0f;
 
+    // 16-byte staging (x rows of whole aligned vectors): each thread loads
+    // its share of the tile into registers before the barrier that ends the
+    // previous tile, so the loads overlap the other waves' last sums, then
+    // writes it to LDS.  4-byte staging (any row width) moves 4x as many
+    // loads, and there the index arithmetic dominates: those loads go from
+    // the buffer straight into LDS, with the indices stepped rather than
+    // divided.  Either way staged element e = tid + 256*i of a tile (LV
+    // floats) is LDS element e = (pl*G + g)*vpr + cv, for row g of the
+    // workgroup's plane pl and vector cv of the row.
+    const int nel = pbn * G * vpr;                     // staged elements of a tile
+    const int cv0 = tid % vpr, gq0 = tid / vpr;
+    const int d_gq = 256 / vpr, d_cv = 256 - d_gq * vpr;
+    const int wel = __builtin_amdgcn_readfirstlane(tid) & ~63;   // the wave's first element
+    const bool mx = a.mult != 1;
+
     const int t0 = sp * a.strip, t1 = min(t0 + a.strip, a.nrt);
     for (int tt = t0; tt < t1; ++tt) {
         const int h0 = tt * TH;
         const int nrows = S * (min(TH, a.OH - h0) - 1) + R;
         const int rbase = S * h0 - a.pH;
-        float sv[NV][LV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = tid + i * 256;
-            const int pl = e / (G * vpr);
-            const int rem = e - pl * (G * vpr);
-            const int g = rem / vpr;
-            const int col = cbase + (rem - g * vpr) * LV;
-            const int plane = pg * pbn + pl, row = rbase + g;
-            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 && row < a.H &&
-                            col >= 0 && col < a.W;
-            // x plane read by dy plane (n, o): (n, o / mult)
-            const int xplane = (plane / a.C) * CI + (plane % a.C) / a.mult;
-            const int off = ok ? ((xplane * a.H + row) * a.W + col) * 4 : kOutOfRange;
-            if constexpr (V4) {
-                const float4 v = buf_f4(rx, off);
-                sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
-            } else {
-                sv[i][0] = buf_f32(rx, off);
-            }
-        }
         float gv[TH][Q];
+        if constexpr (V4) {
+            float4 sv[NV];
 #pragma unroll
-        for (int m = 0; m < TH; ++m)
-#pragma unroll
-            for (int j = 0; j < Q; ++j) {
-                const bool ok = pvalid && h0 + m < a.OH && oc + j < a.OW;
-                gv[m][j] = buf_f32(rg, ok ? ((my_plane * a.OH + h0 + m) * a.OW + oc + j) * 4
-                                          : kOutOfRange);
+            for (int i = 0; i < NV; ++i) {
+                const int e = tid + i * 256;
+                const int pl = e / (G * vpr);
+                const int rem = e - pl * (G * vpr);
+                const int g = rem / vpr;
+                const int col = cbase + (rem - g * vpr) * LV;
+                const int plane = pg * pbn + pl, row = rbase + g;
+                const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
+                                row < a.H && col >= 0 && col < a.W;
+                // x plane read by dy plane (n, o): (n, o / mult)
+                const int xplane = (plane / a.C) * CI + (plane % a.C) / a.mult;
+                const int off = ok ? ((xplane * a.H + row) * a.W + col) * 4 : kOutOfRange;
+                sv[i] = buf_f4(rx, off);
             }
-        if (tt > t0)
-            __syncthreads();              // every thread done with the previous tile
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = tid + i * 256;
-            if (e < pbn * G * vpr) {
-                if constexpr (V4)
-                    lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
-                else
-                    lds[e] = sv[i][0];
+            for (int m = 0; m < TH; ++m)
+#pragma unroll
+                for (int j = 0; j < Q; ++j) {
+                    const bool ok = pvalid && h0 + m < a.OH && oc + j < a.OW;
+                    gv[m][j] = buf_f32(rg, ok ? ((my_plane * a.OH + h0 + m) * a.OW + oc + j) * 4
+                                              : kOutOfRange);
+                }
+            if (tt > t0)
+                __syncthreads();          // every thread done with the previous tile
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = tid + i * 256;
+                if (e < nel)
+                    lds4[e] = sv[i];
             }
+            __syncthreads();
+        } else {
+            if (tt > t0)
+                __syncthreads();          // every thread done with the previous tile
+            int s_cv = cv0, s_gq = gq0;
+            // recompute the load indices per tile (a few adds each) rather than
+            // let the compiler keep all NV of them in registers across the strip
+            asm volatile("" : "+v"(s_cv), "+v"(s_gq));
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int pl = s_gq / G, g = s_gq - pl * G;
+                const int col = cbase + s_cv;
+                s_cv += d_cv;
+                s_gq += d_gq;
+                if (s_cv >= vpr) {
+                    s_cv -= vpr;
+                    ++s_gq;
+                }
+                if (i * 256 + wel < nel) {  // the wave's run of 64 holds staged elements
+                    const int plane = pg * pbn + pl, row = rbase + g;
+                    const bool ok = pl < pbn && plane < a.planes && g < nrows &&
+                                    (unsigned)row < (unsigned)a.H &&
+                                    (unsigned)col < (unsigned)a.W;
+                    // x plane read by dy plane (n, o): (n, o / mult)
+                    const int xplane = mx ? (plane / a.C) * CI + (plane % a.C) / a.mult : plane;
+                    const int off = ok ? ((xplane * a.H + row) * a.W + col) * 4 : kOutOfRange;
+                    buf_to_lds<4>(rx, lds + i * 256 + wel, off);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < TH; ++m)
+#pragma unroll
+                for (int j = 0; j < Q; ++j) {
+                    const bool ok = pvalid && h0 + m < a.OH && oc + j < a.OW;
+                    gv[m][j] = buf_f32(rg, ok ? ((my_plane * a.OH + h0 + m) * a.OW + oc + j) * 4
+                                              : kOutOfRange);
+                }
+            vm_drain();                   // this wave's x rows are in LDS
+            __syncthreads();
         }
-        __syncthreads();
 #pragma unroll
         for (int m = 0; m < TH; ++m) {
 #pragma unroll
