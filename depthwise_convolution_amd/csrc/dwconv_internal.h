@@ -117,9 +117,10 @@ constexpr WgradVariant kWgradVariants[] = {
 };
 constexpr long long kWgradTargetWorkgroups = 512;
 
-// Dynamic LDS a plan may ask for (the launch default, without raising the
-// kernel's limit).
-constexpr int kMaxLdsBytes = 64 * 1024;
+// LDS a plan may ask for: all of a gfx950 workgroup's 160 KiB (dynamic LDS
+// above 64 KiB launches without raising a per-kernel limit on this target;
+// the 7x7 dilation-2 input gradient with a multiplier of 2 takes 98 KiB).
+constexpr int kMaxLdsBytes = 160 * 1024;
 
 // Tile order of the tiled kernels.  Below this many bytes of activations
 // (the tensor an op reads plus the one it writes, or x plus dy for the

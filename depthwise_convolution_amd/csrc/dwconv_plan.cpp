@@ -246,7 +246,11 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     pl->nct = (int)((planes + pl->pb - 1) / pl->pb);
     pl->nwt = ceil_div(pl->OW, pl->tw);
     pl->nst = ceil_div(pl->OH, pl->th);
-    pl->lds_bytes = 4 * mig * (pl->pb * v.g * pl->twl + pl->pb * v.kH * v.kW);
+    // the staged tile (whole waves of 64 staged elements), then the weights
+    const long long tile_el = (long long)mig * pl->pb * v.g * (pl->twl / lv);
+    pl->lds_bytes = (int)(4 * ((tile_el + 63) / 64 * 64 * lv + mig * pl->pb * v.kH * v.kW));
+    if (pl->lds_bytes > kMaxLdsBytes)
+        return false;
     pl->grid = (long long)pl->nct * pl->nwt * pl->nst;
     pl->block = 256;
     char mtag[16] = "";

@@ -68,7 +68,12 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const int txn = a.txn, pbn = a.pbn;
     const int tw = txn * Q, twl = a.twl;               // staged floats per plane row
     const int vpr = twl / LV;                          // loads per plane row
-    float *ldsw = lds + pbn * M * G * twl;
+    // 4-byte staging without upsampling loads the tile straight into LDS
+    // (buffer loads with the LDS flag: a wave writes 64 consecutive staged
+    // elements); the weights follow the tile after whole waves of elements
+    constexpr bool DMA = !UPS && !V4;
+    const int nel = pbn * M * G * vpr;                 // staged elements (LV floats each)
+    float *ldsw = lds + (nel + 63) / 64 * 64 * LV;
 
     // tiles: row tile, column tile, plane group (fastest first), so the row
     // tiles of a plane group, which share halo rows, are consecutive
@@ -121,6 +126,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     // further division
     int s_cv = tid % vpr, s_gq = tid / vpr;
     const int d_gq = 256 / vpr, d_cv = 256 - d_gq * vpr;
+    const int wel = __builtin_amdgcn_readfirstlane(tid) & ~63;   // the wave's first element
     // (upsampled staging: e is (pl, ge, k) = (e / (ge_n*hp), e / hp % ge_n,
     // e % hp), stepped the same way; ge_n is one of two compile-time values)
     const int u_k0 = tid % hp, u_gq0 = tid / hp;
@@ -164,8 +170,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
             if constexpr (V4) {
                 const float4 v = buf_f4(rx, off);
                 sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
-            } else {
-                sv[i][0] = buf_f32(rx, off);
+            } else if (i * 256 + wel < nel) {   // the wave's run of 64 holds staged elements
+                buf_to_lds<4>(rx, lds + i * 256 + wel, off);
             }
         }
     }
@@ -194,13 +200,12 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
                 float2 *dst = reinterpret_cast<float2 *>(lds + (pl * G + g0 + 2 * ge) * twl);
                 dst[k] = c1 ? make_float2(0.0f, sv[i][0]) : make_float2(sv[i][0], 0.0f);
             }
-        } else if (e < pbn * M * G * vpr) {
-            if constexpr (V4)
-                lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
-            else
-                lds[e] = sv[i][0];
+        } else if (V4 && e < nel) {
+            lds4[e] = make_float4(sv[i][0], sv[i][1], sv[i][2], sv[i][3]);
         }
     }
+    if constexpr (DMA)
+        vm_drain();                                    // this wave's tile loads are in LDS
     __syncthreads();
 
     // 3. per-thread weights and rolling accumulators
