@@ -133,9 +133,58 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const int u_dgq = 256 / hp, u_dk = 256 - u_dgq * hp;
     constexpr int GEA = (G + 1) / 2, GEB = G / 2;
     int u_k = u_k0, u_gq = u_gq0;
+    // Without upsampling, staged element (pj, g, cv) of the tile (pj = pl*M + j)
+    // is read from float offset ((xplane*IH + rbase + g)*IW + cbase + cv*LV).
+    // When the planes read are consecutive (xplane = xp0 + pj: no forward
+    // multiplier) that is obase + gq*IW + pj*(IH - G)*IW + cv*LV with
+    // gq = pj*G + g, and gq*IW steps along with gq.  The bounds checks are
+    // three unsigned compares against per-workgroup limits.
+    const int xp0 = pg * pbn * M;
+    const int pjlim = max(0, min(pbn, a.planes - pg * pbn)) * M;     // planes staged
+    const int glo = max(0, -rbase), gcnt = max(0, min(nrows, a.IH - rbase) - glo);
+    const int obase = (xp0 * a.IH + rbase) * a.IW + cbase;
+    const int pjst = (a.IH - G) * a.IW;
+    auto stage = [&](auto lin_t) {
+        constexpr bool LIN = decltype(lin_t)::value;
+        int s_gqw = s_gq * a.IW;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        if constexpr (UPS) {
+        for (int i = 0; i < NV; ++i) {
+            const int pj = s_gq / G;                       // pl*M + j
+            const int g = s_gq - pj * G;
+            const int cf = s_cv * LV, col = cbase + cf;
+            const int gw = s_gqw;
+            s_cv += d_cv;
+            s_gq += d_gq;
+            s_gqw += d_gq * a.IW;
+            if (s_cv >= vpr) {
+                s_cv -= vpr;
+                ++s_gq;
+                s_gqw += a.IW;
+            }
+            const bool ok = pj < pjlim && (unsigned)(g - glo) < (unsigned)gcnt &&
+                            (unsigned)col < (unsigned)a.IW;
+            int src;                                       // float offset in the tensor read
+            if constexpr (LIN) {
+                // unsigned: a row or plane outside the tensor may wrap; it is not loaded
+                src = (int)((unsigned)obase + (unsigned)gw + (unsigned)pj * (unsigned)pjst +
+                            (unsigned)cf);
+            } else {
+                // the forward with a multiplier: plane p reads input plane p / mult
+                const int xplane = (pg * pbn + pj) / a.mult;
+                src = (xplane * a.IH + rbase + g) * a.IW + col;
+            }
+            const int off = ok ? src * 4 : kOutOfRange;
+            if constexpr (V4) {
+                const float4 v = buf_f4(rx, off);
+                sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
+            } else if (i * 256 + wel < nel) {   // the wave's run of 64 holds staged elements
+                buf_to_lds<4>(rx, lds + i * 256 + wel, off);
+            }
+        }
+    };
+    if constexpr (UPS) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
             const int pl = ge_n == GEA ? u_gq / GEA : u_gq / GEB;
             const int ge = u_gq - pl * ge_n, k = u_k;
             u_k += u_dk;
@@ -150,30 +199,11 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
             const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
                             col >= 0 && sr < a.IH && sc < a.IW;
             sv[i][0] = buf_f32(rx, ok ? ((plane * a.IH + sr) * a.IW + sc) * 4 : kOutOfRange);
-        } else {
-            const int pj = s_gq / G;                       // pl*M + j
-            const int g = s_gq - pj * G;
-            const int col = cbase + s_cv * LV;
-            s_cv += d_cv;
-            s_gq += d_gq;
-            if (s_cv >= vpr) {
-                s_cv -= vpr;
-                ++s_gq;
-            }
-            const int pl = pj / M, plane = pg * pbn + pl, row = rbase + g;
-            const bool ok = pl < pbn && plane < a.planes && g < nrows && row >= 0 &&
-                            row < a.IH && col >= 0 && col < a.IW;
-            // plane read: the forward's input plane (plane / mult), or dy plane plane*M + j
-            const int xplane = M > 1 ? (pg * pbn) * M + pj
-                                     : a.mult == 1 ? plane : plane / a.mult;
-            const int off = ok ? ((xplane * a.IH + row) * a.IW + col) * 4 : kOutOfRange;
-            if constexpr (V4) {
-                const float4 v = buf_f4(rx, off);
-                sv[i][0] = v.x; sv[i][1] = v.y; sv[i][2] = v.z; sv[i][3] = v.w;
-            } else if (i * 256 + wel < nel) {   // the wave's run of 64 holds staged elements
-                buf_to_lds<4>(rx, lds + i * 256 + wel, off);
-            }
         }
+    } else if (M > 1 || a.mult == 1) {
+        stage(std::true_type{});
+    } else {
+        stage(std::false_type{});
     }
     // 2. into LDS
     u_k = u_k0;
