@@ -120,6 +120,17 @@ __device__ __forceinline__ int xcd_tile(int b, int nb)
     return k * per + min(k, extra) + (b >> 3);
 }
 
+// Band-local order (large NHWC problems): the tiles of a row band (the
+// channel and column tiles of one row tile, `band` of them, a multiple of
+// 8) are split into 8 runs of consecutive tiles, run k going to XCD k, so
+// most column neighbours share an L2 while all XCDs still sweep the tensor
+// band by band.  A bijection of [0, nb) when band divides nb.
+__device__ __forceinline__ int band_tile(int b, int band)
+{
+    const int run = band >> 3, k = b >> 3;
+    return (k / run) * band + (b & 7) * run + k % run;
+}
+
 // Raw buffer loads (gfx9 family buffer descriptors, stride 0): an offset at
 // or beyond the descriptor's byte count reads as zero in hardware, which
 // gives zero padding and tail handling without branches around the loads.

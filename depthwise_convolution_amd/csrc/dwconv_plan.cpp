@@ -319,6 +319,8 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (tiled) {
         *pl = t;
         pl->xcd = xcd_ranges(p);
+        if (!pl->xcd && pl->kind == KIND_TILED_NHWC && (pl->nct * pl->nwt) % 8 == 0)
+            pl->xcd = 2;
         return DWCONV_OK;
     }
     if (strategy == DWCONV_STRATEGY_TILED)

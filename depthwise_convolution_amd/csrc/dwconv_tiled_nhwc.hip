@@ -28,7 +28,8 @@ struct TiledArgs {
     int YH, YW;             // extents of the tensor written (the grid's, except stride-2 fwd)
     int pH, pW;             // top / left zero padding of the tensor read
     int nct, nwt, nst;      // channel tiles, column tiles, row tiles
-    int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 0 = in order
+    int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 2 = band-local
+                            // runs (band_tile), 0 = in order
 };
 
 // LV: floats per staging load, 4 (16-byte loads: C % 4 == 0, 16-byte
@@ -99,7 +100,9 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     const WT *w = reinterpret_cast<const WT *>(wv);
 
     // tiles: channel tile, column tile, row tile, image (fastest first)
-    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+    int tile = a.xcd == 1   ? xcd_tile(blockIdx.x, gridDim.x)
+               : a.xcd == 2 ? band_tile(blockIdx.x, a.nct * a.nwt)
+                            : blockIdx.x;
     const int ct = tile % a.nct;
     tile /= a.nct;
     const int wt = tile % a.nwt;
