@@ -129,9 +129,10 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 // tiles in order together, which streams a large tensor from HBM faster.
 // Measured on MI355X (NHWC and NCHW, all three ops): the per-XCD ranges are
 // 3-15% faster up to 374 MiB, equal at 512 MiB and 5% slower at 1 GiB.  From
-// it on the NHWC forward / input gradient keeps the band-by-band sweep but
-// splits each row band into 8 runs, one per XCD (when the band's tile count
-// is a multiple of 8): 1.5% faster on 512x512x256.
+// it the NHWC kernels keep the band-by-band sweep but split each row band
+// (a strip, for the weight gradient) into 8 runs, one per XCD, when the
+// band's tile count is a multiple of 8: 1.5% faster on the 512x512x256
+// forward / input gradient, 4% on its weight gradient.
 constexpr long long kXcdRangeMaxBytes = 448LL << 20;
 constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);
 
@@ -235,7 +236,7 @@ struct Plan {
                         // row tiles (weight gradient: strips of row tiles)
     int pb;             // tiled NCHW: planes per workgroup (256 / cl)
     int xcd;            // tiled: 1 = each XCD takes a contiguous range of tiles, 2 = band-local
-                        // runs (NHWC forward / input gradient), 0 = in order
+                        // runs (NHWC), 0 = in order
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
     int hl, twl;        // tiled NCHW: staged columns left of a tile, staged floats per row
     int nrt;            // weight gradient, tiled: row tiles per image / plane

@@ -532,6 +532,8 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         if (tiled) {
             *pl = t;
             pl->xcd = xcd_ranges(p);
+            if (!pl->xcd && pl->kind == KIND_WGRAD_TILED_NHWC && (pl->nct * pl->nwt) % 8 == 0)
+                pl->xcd = 2;
         } else if (strategy == DWCONV_STRATEGY_TILED)
             return DWCONV_ERR_BAD_STRATEGY;
     }

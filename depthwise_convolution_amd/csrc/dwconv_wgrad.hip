@@ -23,7 +23,8 @@ struct WgradArgs {
     int nct, nwt, nsp;      // tiled: channel tiles, column tiles, strips
     int strip;              // tiled: row tiles per strip
     int chunks;             // rows of part[]
-    int xcd;                // tiled: tile order, 1 = per-XCD ranges (xcd_tile), 0 = in order
+    int xcd;                // tiled: tile order, 1 = per-XCD ranges (xcd_tile), 2 = band-local
+                            // runs (band_tile, NHWC), 0 = in order
 };
 
 // Stage 1, any layout, stride, padding and multiplier.  Lanes run along the
@@ -181,7 +182,9 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     float *lds = reinterpret_cast<float *>(lds4);
 
     // tiles: channel tile, column tile, strip, image (fastest first)
-    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+    int tile = a.xcd == 1   ? xcd_tile(blockIdx.x, gridDim.x)
+               : a.xcd == 2 ? band_tile(blockIdx.x, a.nct * a.nwt)
+                            : blockIdx.x;
     const int ct = tile % a.nct;
     tile /= a.nct;
     const int chunk = tile;                 // (n, strip, column tile): row of part[]
