@@ -319,7 +319,10 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (tiled) {
         *pl = t;
         pl->xcd = xcd_ranges(p);
-        if (!pl->xcd && pl->kind == KIND_TILED_NHWC && (pl->nct * pl->nwt) % 8 == 0)
+        // large problems: row bands split over the XCDs (NHWC), or bands of
+        // 8 plane groups with one plane group's row tiles per XCD (NCHW)
+        if (!pl->xcd && (pl->kind == KIND_TILED_NHWC ? (pl->nct * pl->nwt) % 8 == 0
+                                                     : pl->nct % 8 == 0))
             pl->xcd = 2;
         return DWCONV_OK;
     }

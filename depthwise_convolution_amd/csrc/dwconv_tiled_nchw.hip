@@ -30,7 +30,8 @@ struct TiledNchwArgs {
     int hl, twl;            // staged columns left of a tile; staged floats per plane row
     int txn, pbn;           // threads per plane row (16..256), planes per workgroup (256 / txn)
     int nct, nwt, nst;      // plane groups, column tiles, row tiles
-    int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 0 = in order
+    int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 2 = bands of 8 plane
+                            // groups (band_tile), 0 = in order
 };
 
 
@@ -77,7 +78,10 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
 
     // tiles: row tile, column tile, plane group (fastest first), so the row
     // tiles of a plane group, which share halo rows, are consecutive
-    int tile = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+    // (2: bands of 8 plane groups, one plane group's row tiles per XCD)
+    int tile = a.xcd == 1   ? xcd_tile(blockIdx.x, gridDim.x)
+               : a.xcd == 2 ? band_tile(blockIdx.x, 8 * a.nst * a.nwt)
+                            : blockIdx.x;
     const int st = tile % a.nst;
     tile /= a.nst;
     const int wt = tile % a.nwt;
