@@ -178,8 +178,8 @@ constexpr int kNumTiledNchwVariants = sizeof(kTiledNchwVariants) / sizeof(kTiled
 constexpr TiledNchwVariant kWgradNchwVariants[] = {
     {3, 3, 1, 2, 8, 1},   {3, 3, 1, 2, 8, 0},
     {5, 5, 1, 1, 12, 1},  {5, 5, 1, 1, 12, 0},
-    {7, 7, 1, 1, 12, 1},  {7, 7, 1, 1, 12, 0},
-    {7, 7, 2, 1, 17, 1},  {7, 7, 2, 1, 17, 0},
+    {7, 7, 1, 1, 12, 1},  {7, 7, 1, 1, 21, 0},
+    {7, 7, 2, 1, 17, 1},  {7, 7, 2, 1, 23, 0},
     {1, 15, 1, 2, 2, 1},  {1, 15, 1, 2, 2, 0},
     {1, 31, 1, 2, 2, 1},  {1, 31, 1, 2, 2, 0},
 };
