@@ -107,7 +107,7 @@ constexpr WgradVariant kWgradVariants[] = {
     {3, 3, 1, 2, 32, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
     {5, 5, 1, 4, 8, 1, 8, 4},
     {7, 7, 1, 2, 32, 1, 10, 4},
-    {7, 7, 2, 1, 64, 1, 16, 4},
+    {7, 7, 2, 1, 64, 1, 17, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},
     {1, 31, 1, 2, 32, 1, 2, 4},
     // 4-byte staging (lv = 1): any channel count
