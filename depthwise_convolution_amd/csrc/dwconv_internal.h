@@ -166,7 +166,7 @@ constexpr TiledNchwVariant kTiledNchwVariants[] = {
     {3, 3, 1, 2, 8, 1},   {3, 3, 1, 2, 8, 0},
     {5, 5, 1, 2, 12, 1},  {5, 5, 1, 2, 12, 0},
     {7, 7, 1, 1, 16, 1},  {7, 7, 1, 1, 16, 0},
-    {7, 7, 2, 1, 23, 1},  {7, 7, 2, 1, 23, 0},
+    {7, 7, 2, 1, 27, 1},  {7, 7, 2, 1, 27, 0},
     {1, 15, 1, 2, 2, 1},  {1, 15, 1, 2, 2, 0},
     {1, 31, 1, 2, 2, 1},  {1, 31, 1, 2, 2, 0},
 };
