@@ -200,9 +200,10 @@ def cpu_baseline(wl, rows=None, min_seconds=10.0):
     step_s = dt * scale
     gbs = (wl.fwd_bytes() + wl.ig_bytes()) / step_s / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image ({rows / wl.H:.3g} of "
-                      f"the outputs), forward + input gradient, fp64 oracle, mean of {reps} "
-                      f"passes, time scaled x{scale:g}",
+            "sample": (f"the whole {wl.H}x{wl.W}x{wl.C} image" if rows == wl.H else
+                       f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image "
+                       f"({rows / wl.H:.3g} of the outputs, time scaled x{scale:g})") +
+                      f", forward + input gradient, fp64 oracle, mean of {reps} passes",
             "sample_seconds": round(total, 3), "passes": reps,
             "ms_per_step_est": round(step_s * 1e3, 1)}
 
