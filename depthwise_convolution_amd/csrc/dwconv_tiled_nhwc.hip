@@ -9,8 +9,9 @@ namespace {
 // ---------------------------------------------------------------------------
 // Tiled NHWC (forward, or input gradient with reversed taps).
 //
-// One workgroup = 256 threads = CL threads across channels x TW = 256/CL
-// pixels; each thread owns VEC consecutive channels of one output column.
+// One workgroup = 256 threads = CL threads across channels x 256/CL threads
+// across columns; each thread owns VEC consecutive channels of PX adjacent
+// output columns, so a tile is CL*VEC channels x TW = PX*256/CL columns.
 // The workgroup stages G input rows (its TH = G - R + 1 output rows plus the
 // (kH-1)*d row halo) of TW + (kW-1)*d columns (column halo) and CL*VEC
 // channels into LDS in one pass, together with its channels' weights, then
