@@ -111,8 +111,8 @@ constexpr WgradVariant kWgradVariants[] = {
     {1, 15, 1, 4, 32, 1, 2, 4},
     {1, 31, 1, 2, 32, 1, 2, 4},
     // 4-byte staging (lv = 1): any channel count
-    {3, 3, 1, 1, 32, 1, 6, 1},  {5, 5, 1, 1, 32, 1, 8, 1},
-    {7, 7, 1, 1, 32, 1, 10, 1}, {7, 7, 2, 1, 32, 1, 16, 1},
+    {3, 3, 1, 1, 32, 1, 10, 1}, {5, 5, 1, 1, 32, 1, 12, 1},
+    {7, 7, 1, 1, 32, 1, 16, 1}, {7, 7, 2, 1, 32, 1, 22, 1},
     {1, 15, 1, 1, 32, 1, 2, 1}, {1, 31, 1, 1, 32, 1, 2, 1},
 };
 constexpr long long kWgradTargetWorkgroups = 512;
