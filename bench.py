@@ -157,11 +157,39 @@ def describe(dw, wl, op, layout):
                                 wl.dilation, layout, wt, op == dw.OP_FWD)[0]
 
 
+_SPIN_CYCLES_PER_US = None
+
+
+def queue_ahead(torch, stream, us):
+    """Enqueue a spin kernel of about `us` microseconds on `stream`.  It
+    touches no memory; launches enqueued behind it then run back to back on
+    the device, instead of each one waiting for the host to submit it (for
+    launches of a few microseconds the binding's host time is longer than
+    the kernel)."""
+    global _SPIN_CYCLES_PER_US
+    if _SPIN_CYCLES_PER_US is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(10000)
+            a.record(stream)
+            torch.cuda._sleep(1000000)
+            b.record(stream)
+        stream.synchronize()
+        _SPIN_CYCLES_PER_US = 1e6 / max(1.0, a.elapsed_time(b) * 1e3)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
+
+
 def time_kernel(torch, fn, stream, iters, flush=None):
-    """Per-launch kernel time (us) from HIP events recorded on `stream`."""
+    """Per-launch kernel time (us) from HIP events recorded on `stream`.
+    Without `flush` the launches are queued behind a spin kernel, so the
+    events bracket device time only; with it, the 1 GiB pass before each
+    launch keeps the device busy while the host submits."""
     times = []
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    if flush is None:
+        queue_ahead(torch, stream, 200 + 150 * iters)
     with torch.cuda.stream(stream):
         for i in range(iters):
             if flush is not None:

@@ -105,9 +105,9 @@ constexpr int kNumTiledM2Variants = sizeof(kTiledM2Variants) / sizeof(kTiledM2Va
 struct WgradVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr WgradVariant kWgradVariants[] = {
     {3, 3, 1, 2, 32, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
-    {5, 5, 1, 4, 8, 1, 8, 4},
-    {7, 7, 1, 2, 32, 1, 10, 4},
-    {7, 7, 2, 1, 64, 1, 17, 4},
+    {5, 5, 1, 2, 16, 1, 12, 4},
+    {7, 7, 1, 1, 32, 1, 14, 4},
+    {7, 7, 2, 1, 32, 1, 22, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},
     {1, 31, 1, 2, 32, 1, 2, 4},
     // 4-byte staging (lv = 1): any channel count
