@@ -70,13 +70,13 @@ struct TiledVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr TiledVariant kTiledVariants[] = {
     {3, 3, 1, 4, 32, 1, 8, 4},   {3, 3, 1, 4, 16, 1, 6, 4},   {3, 3, 1, 4, 8, 1, 3, 4},
     {5, 5, 1, 4, 8, 1, 10, 4},
-    {7, 7, 1, 1, 64, 1, 16, 4},  {7, 7, 1, 2, 16, 1, 14, 4},
+    {7, 7, 1, 1, 32, 1, 16, 4},
     {7, 7, 2, 2, 16, 1, 20, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},  {1, 15, 1, 4, 16, 1, 2, 4},
     {1, 31, 1, 2, 32, 1, 2, 4},
     // scalar staging (lv = 1): any channel count, e.g. a prime one
     {3, 3, 1, 1, 32, 2, 8, 1},   {5, 5, 1, 1, 32, 1, 12, 1},
-    {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 20, 1},
+    {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 24, 1},
     {1, 15, 1, 1, 32, 1, 2, 1},  {1, 31, 1, 1, 32, 1, 2, 1},
 };
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);
@@ -105,7 +105,7 @@ constexpr int kNumTiledM2Variants = sizeof(kTiledM2Variants) / sizeof(kTiledM2Va
 struct WgradVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr WgradVariant kWgradVariants[] = {
     {3, 3, 1, 2, 32, 1, 6, 4},  {3, 3, 1, 4, 8, 1, 6, 4},
-    {5, 5, 1, 2, 16, 1, 12, 4},
+    {5, 5, 1, 2, 16, 1, 11, 4},
     {7, 7, 1, 1, 32, 1, 14, 4},
     {7, 7, 2, 1, 32, 1, 22, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},

@@ -94,7 +94,12 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     // loads per staged pixel / row / tile, and per thread
     constexpr int VPC = XM ? CG / (M * LV) : Gm::VPC, VPR = TWI * VPC, VCH = G * VPR;
     constexpr int NV = (VCH + 255) / 256;
-    constexpr int WF = Gm::WF, XF4 = Gm::XF4;
+    constexpr int WF = Gm::WF;
+    // 4-byte staging at stride 1 goes from the buffer straight into LDS, a
+    // wave's 64 consecutive elements per load, so its region is rounded up to
+    // 64 floats (at stride 2 it measured 2-4% slower than through registers)
+    constexpr bool DMA = LV == 1 && S == 1;
+    constexpr int XF4 = DMA ? (VCH + 63) / 64 * 16 : Gm::XF4;
     __shared__ float4 lds[XF4 + (WF + 3) / 4];
     float *ldsx = reinterpret_cast<float *>(lds);
     float *ldsw = ldsx + XF4 * 4;
@@ -172,7 +177,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     const unsigned pstep = 4u * a.CR, rstep = pstep * a.IW;
     unsigned uoff = (unsigned)(rbase + g) * rstep + (unsigned)(cbase + col) * pstep + 4u * ch;
     typedef typename VecT<LV>::type LoadT;
-    LoadT stage[NV];
+    LoadT stage[DMA ? 1 : NV];
+    const int wel = __builtin_amdgcn_readfirstlane(tid) & ~63;   // the wave's first element
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         if (i > 0) {
@@ -198,13 +204,17 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
                             (unsigned)gc < (unsigned)a.IW;
             off = ok ? (int)uoff : kOutOfRange;
         }
-        if constexpr (LV == 4)
+        if constexpr (DMA) {
+            if ((i + 1) * 256 <= VCH || i * 256 + wel < VCH)   // the wave's run holds staged loads
+                buf_to_lds<4>(rx, ldsx + i * 256 + wel, off);
+        } else if constexpr (LV == 4) {
             stage[i] = buf_f4(rx, off);
-        else
+        } else {
             stage[i] = buf_f32(rx, off);
+        }
     }
-    // 2. weights, then the tile, into LDS (only a last, partial round of
-    // loads needs a bound)
+    // 2. weights, then (unless loaded straight into LDS) the tile, into LDS
+    // (only a last, partial round of loads needs a bound)
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int e = tid + i * 256;
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
             ldsw[e] = wst[i];
     }
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
+    for (int i = 0; i < (DMA ? 0 : NV); ++i) {
         const int e = tid + i * 256;
         if ((i + 1) * 256 <= VCH || e < VCH) {
             if constexpr (XM) {
@@ -225,6 +235,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
             }
         }
     }
+    if constexpr (DMA)
+        vm_drain();                       // the barrier does not wait for the LDS loads
     __syncthreads();
 
     // per-thread weights (reversed taps for the input gradient)
