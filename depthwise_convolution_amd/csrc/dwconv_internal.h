@@ -76,7 +76,7 @@ constexpr TiledVariant kTiledVariants[] = {
     {1, 31, 1, 2, 32, 1, 2, 4},
     // scalar staging (lv = 1): any channel count, e.g. a prime one
     {3, 3, 1, 1, 32, 2, 8, 1},   {5, 5, 1, 1, 32, 1, 12, 1},
-    {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 24, 1},
+    {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 28, 1},
     {1, 15, 1, 1, 32, 1, 2, 1},  {1, 31, 1, 1, 32, 1, 2, 1},
 };
 constexpr int kNumTiledVariants = sizeof(kTiledVariants) / sizeof(kTiledVariants[0]);

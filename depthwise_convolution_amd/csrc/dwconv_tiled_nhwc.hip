@@ -14,7 +14,8 @@ namespace {
 // output columns, so a tile is CL*VEC channels x TW = PX*256/CL columns.
 // The workgroup stages G input rows (its TH = G - R + 1 output rows plus the
 // (kH-1)*d row halo) of TW + (kW-1)*d columns (column halo) and CL*VEC
-// channels into LDS in one pass, together with its channels' weights, then
+// channels into LDS in one pass (at stride 1 with buffer loads that write
+// LDS directly), together with its channels' weights, then
 // walks the rows: each thread reads its kW taps of a row from LDS and adds
 // the row into the R rolling accumulators of the output rows it touches;
 // after row u, output row u - (R-1) is complete and is stored.  Short-lived
@@ -95,11 +96,13 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     constexpr int VPC = XM ? CG / (M * LV) : Gm::VPC, VPR = TWI * VPC, VCH = G * VPR;
     constexpr int NV = (VCH + 255) / 256;
     constexpr int WF = Gm::WF;
-    // 4-byte staging at stride 1 goes from the buffer straight into LDS, a
-    // wave's 64 consecutive elements per load, so its region is rounded up to
-    // 64 floats (at stride 2 it measured 2-4% slower than through registers)
-    constexpr bool DMA = LV == 1 && S == 1;
-    constexpr int XF4 = DMA ? (VCH + 63) / 64 * 16 : Gm::XF4;
+    // At stride 1 the tile goes from the buffer straight into LDS (4- or
+    // 16-byte loads), a wave's 64 consecutive staged loads per instruction, so
+    // its region is rounded up to 64 loads.  At stride 2 that measured 2-4%
+    // slower than the copy through registers; the multiplier-2 forward, which
+    // writes every x value twice, takes the copy too.
+    constexpr bool DMA = S == 1 && !XM;
+    constexpr int XF4 = DMA ? (VCH + 63) / 64 * 16 * LV : Gm::XF4;
     __shared__ float4 lds[XF4 + (WF + 3) / 4];
     float *ldsx = reinterpret_cast<float *>(lds);
     float *ldsw = ldsx + XF4 * 4;
@@ -130,7 +133,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     // then the input tile.  All are buffer loads: weights of channels >= C,
     // a missing bias, and tile elements outside the image read as zero.
     // Loads complete in order, so the weights can be written to LDS while
-    // the tile is still in flight.
+    // the tile is still in flight (at stride 1 the tile loads write LDS
+    // themselves; a wait for all loads precedes the barrier).
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
     const __amdgpu_buffer_rsrc_t rx =
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
         }
         if constexpr (DMA) {
             if ((i + 1) * 256 <= VCH || i * 256 + wel < VCH)   // the wave's run holds staged loads
-                buf_to_lds<4>(rx, ldsx + i * 256 + wel, off);
+                buf_to_lds<4 * LV>(rx, ldsx + (i * 256 + wel) * LV, off);
         } else if constexpr (LV == 4) {
             stage[i] = buf_f4(rx, off);
         } else {
