@@ -177,14 +177,15 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
     // the final per-(channel, tap) sums go through LDS in groups of TG taps
     constexpr int TGF = XF / (256 * VEC);
     constexpr int TG = TGF < 1 ? 1 : (TGF > KK + 1 ? KK + 1 : TGF);
-    // 4-byte staging of 7x7 windows at stride 1 goes from the buffer straight
-    // into LDS, a wave's 64 consecutive elements per load (the tile's region
-    // rounded up to 64 floats).  It needs the barrier before the loads instead
-    // of after them: measured on MI355X it is 18-35% faster for 7x7 windows,
-    // whose tiles cost the most registers when copied through them, and up to
-    // 17% slower for 3x3 and 5x5 ones, which lose more by that barrier.
-    constexpr bool DMA = LV == 1 && S == 1 && KK >= 49;
-    constexpr int XFS = DMA ? (VCH + 63) / 64 * 64 : XF;
+    // For 7x7 windows at stride 1 the staged loads (4 or 16 bytes) go from
+    // the buffer straight into LDS, a wave's 64 consecutive loads per
+    // instruction (the tile's region rounded up to 64 loads).  That needs the
+    // barrier before the loads instead of after them: measured on MI355X it is
+    // 4-6% faster (16-byte) and 18-35% faster (4-byte) for 7x7 windows, whose
+    // tiles cost the most registers when copied through them, and up to 17%
+    // slower for 3x3 and 5x5 ones, which lose more by that barrier.
+    constexpr bool DMA = S == 1 && M == 1 && KK >= 49;
+    constexpr int XFS = DMA ? (VCH + 63) / 64 * 64 * LV : XF;
     constexpr int LDSF = (XFS > 256 * VEC * TG) ? XFS : 256 * VEC * TG;
     __shared__ float4 lds4[(LDSF + 3) / 4];
     float *lds = reinterpret_cast<float *>(lds4);
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nhwc(const float *__restric
             const int off = ok ? (int)uoff : kOutOfRange;
             if constexpr (DMA) {
                 if ((i + 1) * 256 <= VCH || i * 256 + wel < VCH)   // the wave's run holds staged loads
-                    buf_to_lds<4>(rx, lds + i * 256 + wel, off);
+                    buf_to_lds<4 * LV>(rx, lds + (i * 256 + wel) * LV, off);
             } else if constexpr (LV == 4) {
                 stage[i] = buf_f4(rx, off);
             } else {
