@@ -69,7 +69,7 @@ enum Kind {
 struct TiledVariant { int kH, kW, d, vec, cl, px, g, lv; };
 constexpr TiledVariant kTiledVariants[] = {
     {3, 3, 1, 4, 32, 1, 8, 4},   {3, 3, 1, 4, 16, 1, 6, 4},   {3, 3, 1, 4, 8, 1, 3, 4},
-    {5, 5, 1, 4, 8, 1, 10, 4},
+    {5, 5, 1, 1, 32, 1, 12, 4},
     {7, 7, 1, 1, 32, 1, 16, 4},
     {7, 7, 2, 2, 16, 1, 20, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},  {1, 15, 1, 4, 16, 1, 2, 4},
