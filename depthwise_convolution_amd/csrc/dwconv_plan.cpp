@@ -386,6 +386,24 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     }
     if (best < 0)
         return false;
+    // Stride 1, no multiplier: a channel tile that holds every channel gives
+    // each (image, strip, column tile) one workgroup; a later variant of the
+    // same shape that still fills 3/4 of its tiles with two or more of them
+    // is taken instead (3x3, 8x112x112x64 on MI355X: 20.0 -> 15.7 us; from
+    // two tiles on the wider tile stays faster: 512x512x256 95.5 against
+    // 124.4 us with the narrower one).
+    if (table == kWgradVariants && ceil_div((int)co, table[best].cl * table[best].vec) == 1) {
+        const WgradVariant &b = table[best];
+        for (int i = best + 1; i < nvar; ++i) {
+            const WgradVariant &v = table[i];
+            const int cg = v.cl * v.vec;
+            if (v.kH != b.kH || v.kW != b.kW || v.d != b.d || v.lv != b.lv ||
+                ceil_div((int)co, cg) < 2 || (double)co / (ceil_div((int)co, cg) * cg) < 0.75)
+                continue;
+            best = i;
+            break;
+        }
+    }
     const WgradVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
     pl->kind = KIND_WGRAD_TILED_NHWC;
