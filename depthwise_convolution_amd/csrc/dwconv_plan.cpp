@@ -109,6 +109,27 @@ static void set_extents(const Problem &p, Plan *pl)
     }
 }
 
+// When the chosen variant's channel tile holds every channel of the problem,
+// take a later variant of the same kernel shape and staging width whose tile
+// (of at least min_cg channels) the problem still fills to 3/4 with two or
+// more tiles: twice the workgroups for a problem that would otherwise give
+// each (image, row band, column tile) one.
+template <typename V>
+static int split_channel_tile(const V *table, int nvar, int best, long long co, int min_cg)
+{
+    const V &b = table[best];
+    if (ceil_div((int)co, b.cl * b.vec) != 1)
+        return best;
+    for (int i = best + 1; i < nvar; ++i) {
+        const V &v = table[i];
+        const int cg = v.cl * v.vec, nt = ceil_div((int)co, cg);
+        if (v.kH == b.kH && v.kW == b.kW && v.d == b.d && v.lv == b.lv && cg >= min_cg &&
+            nt >= 2 && (double)co / (nt * cg) >= 0.75)
+            return i;
+    }
+    return best;
+}
+
 static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     if (p.layout != DWCONV_LAYOUT_NHWC)
@@ -147,6 +168,11 @@ static bool plan_tiled_nhwc(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     }
     if (best < 0)
         return false;
+    // stride 1, no multiplier: 3x3 with 65-128 channels takes two 64-channel
+    // tiles (8x112x112x96 on MI355X: 14.4 -> 12.6 us); a 32-channel tile
+    // (3 staged rows, for small C) measured 20-40% slower at 48-64 channels
+    if (table == kTiledVariants)
+        best = split_channel_tile(table, nvar, best, co, 64);
     const TiledVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
     pl->kind = KIND_TILED_NHWC;
@@ -386,24 +412,11 @@ static bool plan_wgrad_tiled(const Problem &p, std::uintptr_t ptr_bits, Plan *pl
     }
     if (best < 0)
         return false;
-    // Stride 1, no multiplier: a channel tile that holds every channel gives
-    // each (image, strip, column tile) one workgroup; a later variant of the
-    // same shape that still fills 3/4 of its tiles with two or more of them
-    // is taken instead (3x3, 8x112x112x64 on MI355X: 20.0 -> 15.7 us; from
-    // two tiles on the wider tile stays faster: 512x512x256 95.5 against
-    // 124.4 us with the narrower one).
-    if (table == kWgradVariants && ceil_div((int)co, table[best].cl * table[best].vec) == 1) {
-        const WgradVariant &b = table[best];
-        for (int i = best + 1; i < nvar; ++i) {
-            const WgradVariant &v = table[i];
-            const int cg = v.cl * v.vec;
-            if (v.kH != b.kH || v.kW != b.kW || v.d != b.d || v.lv != b.lv ||
-                ceil_div((int)co, cg) < 2 || (double)co / (ceil_div((int)co, cg) * cg) < 0.75)
-                continue;
-            best = i;
-            break;
-        }
-    }
+    // stride 1, no multiplier: 3x3 with 48-64 channels takes two 32-channel
+    // tiles (8x112x112x64 on MI355X: 20.0 -> 15.7 us; from two tiles on the
+    // wider tile stays faster: 512x512x256 95.5 against 124.4 us)
+    if (table == kWgradVariants)
+        best = split_channel_tile(table, nvar, best, co, 0);
     const WgradVariant &v = table[best];
     const int R = (v.kH - 1) * v.d + 1;
     pl->kind = KIND_WGRAD_TILED_NHWC;

@@ -76,7 +76,7 @@ def _sweep():
         for layout in (wlmod.NHWC, wlmod.NCHW):
             for s in (1, 2):
                 for m in (1, 2):
-                    for c in (1, 4, 5, 8, 12, 20, 32, 40, 64, 96):
+                    for c in (1, 4, 5, 8, 12, 20, 32, 40, 64, 96, 256):
                         for h, w in ((13, 37), (9, 16), (1, 40)):
                             if kh > 1 and h == 1:
                                 continue
