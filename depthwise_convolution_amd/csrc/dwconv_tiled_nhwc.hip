@@ -14,8 +14,8 @@ namespace {
 // output columns, so a tile is CL*VEC channels x TW = PX*256/CL columns.
 // The workgroup stages G input rows (its TH = G - R + 1 output rows plus the
 // (kH-1)*d row halo) of TW + (kW-1)*d columns (column halo) and CL*VEC
-// channels into LDS in one pass (at stride 1 with buffer loads that write
-// LDS directly), together with its channels' weights, then
+// channels into LDS in one pass (with buffer loads that write LDS directly,
+// except 4-byte staging at stride 2), together with its channels' weights, then
 // walks the rows: each thread reads its kW taps of a row from LDS and adds
 // the row into the R rolling accumulators of the output rows it touches;
 // after row u, output row u - (R-1) is complete and is stored.  Short-lived
@@ -96,12 +96,13 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     constexpr int VPC = XM ? CG / (M * LV) : Gm::VPC, VPR = TWI * VPC, VCH = G * VPR;
     constexpr int NV = (VCH + 255) / 256;
     constexpr int WF = Gm::WF;
-    // At stride 1 the tile goes from the buffer straight into LDS (4- or
-    // 16-byte loads), a wave's 64 consecutive staged loads per instruction, so
-    // its region is rounded up to 64 loads.  At stride 2 that measured 2-4%
-    // slower than the copy through registers; the multiplier-2 forward, which
-    // writes every x value twice, takes the copy too.
-    constexpr bool DMA = S == 1 && !XM;
+    // The tile goes from the buffer straight into LDS (4- or 16-byte loads),
+    // a wave's 64 consecutive staged loads per instruction, so its region is
+    // rounded up to 64 loads.  At stride 2 only the 16-byte staging does so
+    // (4-byte measured 2-4% slower than the copy through registers, 16-byte
+    // mostly 2-8% faster); the multiplier-2 forward, which writes every x
+    // value twice, takes the copy too.
+    constexpr bool DMA = !XM && (S == 1 || LV == 4);
     constexpr int XF4 = DMA ? (VCH + 63) / 64 * 16 * LV : Gm::XF4;
     __shared__ float4 lds[XF4 + (WF + 3) / 4];
     float *ldsx = reinterpret_cast<float *>(lds);
@@ -133,8 +134,8 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     // then the input tile.  All are buffer loads: weights of channels >= C,
     // a missing bias, and tile elements outside the image read as zero.
     // Loads complete in order, so the weights can be written to LDS while
-    // the tile is still in flight (at stride 1 the tile loads write LDS
-    // themselves; a wait for all loads precedes the barrier).
+    // the tile is still in flight (where the tile loads write LDS
+    // themselves, a wait for all loads precedes the barrier).
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (!IG && bias) ? a.C * 4 : 0);
     const __amdgpu_buffer_rsrc_t rx =
