@@ -46,7 +46,8 @@ EXPORTS = ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_d
            "dwconv2d_strerror", "dwconv2d_version",
            "dwconv2d_same_pads", "dwconv2d_out_extents", "dwconv2d_launch_ex",
            "dwconv2d_describe_ex", "dwconv2d_weight_grad_workspace_size_ex",
-           "dwconv2d_weight_grad_ex", "dwconv2d_fwd_bn_act_ex", "dwconv2d_weight_grad_sgd_ex")
+           "dwconv2d_weight_grad_ex", "dwconv2d_fwd_bn_act_ex", "dwconv2d_weight_grad_sgd_ex",
+           "dwconv2d_describe_addr_ex")
 
 _lib = None
 
@@ -90,6 +91,8 @@ def lib():
     L.dwconv2d_launch_ex.argtypes = [i, vp, vp, i, vp, vp] + [i] * 9 + [ip, i, i, vp]
     L.dwconv2d_describe_ex.argtypes = [i] * 12 + [ip, i, i, ctypes.c_char_p, i,
                                                   ctypes.POINTER(ll), ip]
+    L.dwconv2d_describe_addr_ex.argtypes = [i] * 12 + [ip, i, i, ctypes.c_ulonglong,
+                                                       ctypes.c_char_p, i, ctypes.POINTER(ll), ip]
     L.dwconv2d_weight_grad_workspace_size_ex.argtypes = [i] * 9 + [ip, i, i, ctypes.POINTER(ll)]
     L.dwconv2d_weight_grad_ex.argtypes = [vp, vp, vp, vp, vp, ll] + [i] * 9 + [ip, i, i, vp]
     f32 = ctypes.c_float
@@ -447,6 +450,22 @@ def dwconv2d_describe_ex(op, N, H, W, C, kH, kW, stride=1, dilation=1, pads=None
                                     stride, dilation, _pads_arg(pads), _layout_code(layout),
                                     strategy, name, 128, ctypes.byref(grid), ctypes.byref(block))
     _check_status(st, "dwconv2d_describe_ex")
+    return name.value.decode(), grid.value, block.value
+
+
+def dwconv2d_describe_addr_ex(op, N, H, W, C, kH, kW, stride=1, dilation=1, pads=None, mult=1,
+                              layout=NHWC, wtype=W_F32, has_bias=False, strategy=STRATEGY_AUTO,
+                              addr_bits=0):
+    """(kernel name, grid, block) of a general-form launch whose tensor
+    addresses OR together to `addr_bits` (0: all 16-byte aligned)."""
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    name = ctypes.create_string_buffer(128)
+    grid, block = ctypes.c_longlong(0), ctypes.c_int(0)
+    st = lib().dwconv2d_describe_addr_ex(op, wtype, int(bool(has_bias)), N, H, W, C, mult, kH,
+                                         kW, stride, dilation, _pads_arg(pads),
+                                         _layout_code(layout), strategy, int(addr_bits), name,
+                                         128, ctypes.byref(grid), ctypes.byref(block))
+    _check_status(st, "dwconv2d_describe_addr_ex")
     return name.value.decode(), grid.value, block.value
 
 

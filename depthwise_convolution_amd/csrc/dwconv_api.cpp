@@ -70,8 +70,17 @@ int run(Problem p, const float *in, const void *w, const float *b, float *out, i
     if (st != DWCONV_OK)
         return st;
     Plan pl;
-    const std::uintptr_t bits = reinterpret_cast<std::uintptr_t>(in) |
-                                reinterpret_cast<std::uintptr_t>(out);
+    // the kernels' vector loads and stores (16-byte staging, 4-channel bias
+    // and BatchNorm loads, vector stores) are chosen only when every float
+    // array they touch is 16-byte aligned
+    std::uintptr_t bits = reinterpret_cast<std::uintptr_t>(in) |
+                          reinterpret_cast<std::uintptr_t>(out) |
+                          reinterpret_cast<std::uintptr_t>(b);
+    if (epi && epi->gamma)
+        bits |= reinterpret_cast<std::uintptr_t>(epi->gamma) |
+                reinterpret_cast<std::uintptr_t>(epi->beta) |
+                reinterpret_cast<std::uintptr_t>(epi->mean) |
+                reinterpret_cast<std::uintptr_t>(epi->var);
     st = dwconv::make_plan(p, strategy, bits, &pl);
     if (st != DWCONV_OK)
         return st;
@@ -94,12 +103,13 @@ int general_problem(int op, int wtype, int has_bias, int N, int H, int W, int C,
     return DWCONV_OK;
 }
 
-int describe(Problem p, int strategy, char *name, int name_len, long long *grid, int *block)
+int describe(Problem p, int strategy, char *name, int name_len, long long *grid, int *block,
+             std::uintptr_t addr_bits = 0)
 {
     if ((p.op == DWCONV_OP_INPUT_GRAD || p.op == DWCONV_OP_WEIGHT_GRAD) && p.has_bias)
         return DWCONV_ERR_BAD_OP;
     Plan pl;
-    const int st = dwconv::make_plan(p, strategy, 0, &pl);
+    const int st = dwconv::make_plan(p, strategy, addr_bits, &pl);
     if (st != DWCONV_OK)
         return st;
     if (name && name_len > 0) {
@@ -303,6 +313,20 @@ int dwconv2d_describe_ex(int op, int wtype, int has_bias, int N, int H, int W, i
     if (st != DWCONV_OK)
         return st;
     return describe(p, strategy, name, name_len, grid, block);
+}
+
+int dwconv2d_describe_addr_ex(int op, int wtype, int has_bias, int N, int H, int W, int C,
+                              int mult, int kH, int kW, int stride, int dilation, const int *pads,
+                              int layout, int strategy, unsigned long long addr_bits, char *name,
+                              int name_len, long long *grid, int *block)
+{
+    Problem p;
+    const int st = general_problem(op, wtype, has_bias, N, H, W, C, mult, kH, kW, stride,
+                                   dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    return describe(p, strategy, name, name_len, grid, block,
+                    static_cast<std::uintptr_t>(addr_bits));
 }
 
 int dwconv2d_weight_grad_workspace_size_ex(int N, int H, int W, int C, int mult, int kH, int kW,

@@ -32,6 +32,7 @@ struct TiledNchwArgs {
     int nct, nwt, nst;      // plane groups, column tiles, row tiles
     int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 2 = bands of 8 plane
                             // groups (band_tile), 0 = in order
+    int ost8;               // 1: the tensor written is 8-byte aligned (Q-wide vector stores)
 };
 
 
@@ -265,7 +266,9 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const float *rowbase = lds + pli * M * G * twl + tx * Q + (a.hl - a.pW);
     const int oc = w0 + tx * Q;                        // first output column of this thread
     float *outp = out + my_plane * a.YH * a.YW;
-    const bool vec_store = !DEC && (Q > 1) && (a.OW % Q == 0);
+    // Q-wide stores need an 8-byte aligned output (Q = 2) and whole vectors
+    // per row (OW % Q == 0 keeps every plane and row start on a vector)
+    const bool vec_store = !DEC && (Q > 1) && (a.OW % Q == 0) && a.ost8;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -425,6 +428,7 @@ int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const v
     a.pbn = pl.pb;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     a.xcd = pl.xcd;
+    a.ost8 = (reinterpret_cast<std::uintptr_t>(out) & 7u) == 0;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }

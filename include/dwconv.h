@@ -230,6 +230,18 @@ int dwconv2d_describe_ex(int op, int wtype, int has_bias, int N, int H, int W, i
                          int kH, int kW, int stride, int dilation, const int *pads, int layout,
                          int strategy, char *name, int name_len, long long *grid, int *block);
 
+/* dwconv2d_describe_ex for tensors at given addresses: addr_bits is the
+ * bitwise OR of the addresses the launch would pass (in, out and b for the
+ * forward and input gradient, plus the BatchNorm arrays of the fused
+ * forward; x and dy for the weight gradient).  The kernels use 16-byte
+ * loads and stores only when every one of those addresses is a multiple of
+ * 16; with addr_bits = 0 this is dwconv2d_describe_ex.  Host only; lets a
+ * caller see which kernel a tensor view at an offset gets. */
+int dwconv2d_describe_addr_ex(int op, int wtype, int has_bias, int N, int H, int W, int C,
+                              int mult, int kH, int kW, int stride, int dilation, const int *pads,
+                              int layout, int strategy, unsigned long long addr_bits, char *name,
+                              int name_len, long long *grid, int *block);
+
 /* Weight and bias gradients with explicit pads and a channel multiplier:
  * dw is [mult*C][kH][kW], db [mult*C] or NULL; workspace as for
  * dwconv2d_weight_grad, sized by dwconv2d_weight_grad_workspace_size_ex. */

@@ -434,3 +434,38 @@ def test_binding_shares_torch_hip_runtime():
                          timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+@pytest.mark.parametrize("off", [4, 8, 12])
+def test_plans_for_tensors_off_16_byte_alignment(off):
+    """A tensor view whose address is 4, 8 or 12 bytes past a 16-byte boundary
+    (a contiguous view at a storage offset of 1-3 floats) gets kernels that use
+    no 16-byte access: 4-byte staging (`_l1`, `_v1`) or 1-channel direct
+    kernels; at a multiple of 16 the plan is the aligned one."""
+    def name(op, layout, C, k, addr, s=1, d=1, H=56, W=56, mult=1, bias=False):
+        return dw.dwconv2d_describe_addr_ex(op, 2, H, W, C, k, k, stride=s, dilation=d,
+                                            mult=mult, layout=layout, has_bias=bias,
+                                            addr_bits=addr)[0]
+    for k, d in ((3, 1), (5, 1), (7, 1), (7, 2)):
+        for op in (dw.OP_FWD, dw.OP_INPUT_GRAD, dw.OP_WEIGHT_GRAD):
+            # NHWC: C % 4 == 0 takes 16-byte staging only when aligned
+            a = name(op, dw.NHWC, 128, k, 0, d=d)
+            u = name(op, dw.NHWC, 128, k, off, d=d)
+            assert "_l1" not in a and ("_l1" in u or "_v1" in u), (a, u)
+            assert name(op, dw.NHWC, 128, k, 16 + 32 * off, d=d) == a
+            # NCHW: whole 16-byte rows (W % 4 == 0) only when aligned
+            a = name(op, dw.NCHW, 32, k, 0, d=d)
+            u = name(op, dw.NCHW, 32, k, off, d=d)
+            assert "_v4" in a and "_v4" not in u, (a, u)
+    # the bias takes part in the forward's choice (its 4-channel loads)
+    assert "_l1" in name(dw.OP_FWD, dw.NHWC, 128, 3, off, bias=True)
+    # stride 2, and multiplier 2 (16-byte only): the 4-byte or direct kernels
+    assert "_l1" in name(dw.OP_FWD, dw.NHWC, 64, 3, off, s=2)
+    assert name(dw.OP_FWD, dw.NHWC, 32, 3, off, mult=2).startswith("direct_nhwc_s1_v1")
+    assert "_v1" in name(dw.OP_FWD, dw.NCHW, 32, 3, off, s=2)
+    # direct kernels: 4-channel vectors only when aligned
+    a = dw.dwconv2d_describe_addr_ex(dw.OP_FWD, 1, 9, 9, 8, 3, 3, layout=dw.NHWC,
+                                     strategy=dw.STRATEGY_DIRECT, addr_bits=0)[0]
+    u = dw.dwconv2d_describe_addr_ex(dw.OP_FWD, 1, 9, 9, 8, 3, 3, layout=dw.NHWC,
+                                     strategy=dw.STRATEGY_DIRECT, addr_bits=off)[0]
+    assert "_v4_" in a and "_v1_" in u

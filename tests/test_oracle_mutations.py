@@ -66,6 +66,11 @@ MUTANTS = [
      "const int o = (int)(t / ((long)kH * kW)), c = o % C;", 0),
     ("general_wgrad_left_pad_sign", "const int wi = wo * s + kw * d - pl;",
      "const int wi = wo * s + kw * d + pl;", 1),
+    ("dense_reads_x_channel_o",
+     "acc += (double)x[at(layout, C, H, W, n, c, hi, wi)] *\n                                       (double)wd[",
+     "acc += (double)x[at(layout, C, H, W, n, o, hi, wi)] *\n                                       (double)wd[", 0),
+    ("dense_filter_transposed", "(double)wd[(((size_t)o * C + c) * kH + kh) * kW + kw];",
+     "(double)wd[(((size_t)c * Co + o) * kH + kh) * kW + kw];", 0),
     ("weight_grad_swaps_dy_index", "(double)dy[at(layout, C, Ho, Wo, n, c, ho, wo)];\n                    acc += p;",
      "(double)dy[at(layout, C, Ho, Wo, n, c, wo % Ho, ho % Wo)];\n                    acc += p;", 0),
 ]
@@ -98,6 +103,8 @@ def _all_pins_pass(om):
         for layout in pins.LAYOUTS:
             checks.append(lambda p=path, l=layout: pins.test_golden_examples(om, p, l))
     checks.append(lambda: pins.test_half_decode_closed_forms(om))
+    for layout in pins.LAYOUTS:
+        checks.append(lambda l=layout: pins.test_dense_conv_golden(om, l))
     for case in pins.SMALL_CASES[:5]:
         for layout in pins.LAYOUTS:
             checks.append(lambda c=case, l=layout: pins.test_adjoint_identity(om, c, l))

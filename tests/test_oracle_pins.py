@@ -47,7 +47,8 @@ SMALL_CASES = [
 # --------------------------------------------------------------------------
 def _golden_files():
     return sorted(f for f in glob.glob(os.path.join(GOLDEN, "*.json"))
-                  if not f.endswith("half_decode.json"))
+                  if not f.endswith("half_decode.json")
+                  and not os.path.basename(f).startswith("dense_conv"))
 
 
 @pytest.mark.parametrize("path", _golden_files(), ids=lambda p: os.path.basename(p))
@@ -125,6 +126,27 @@ def test_depthwise_is_diagonal_dense_conv(oracle_mod, case, layout):
         wd[0, 1, kH // 2, kW // 2] = 1.0
         assert not np.array_equal(oracle_mod.dense_conv(x, wd, b, s, d, layout), y_dw) or \
             not np.any(from_layout(x, layout)[..., 1])
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_dense_conv_golden(oracle_mod, layout):
+    """The dense routine on a hand-worked two-channel example whose filters
+    are nonzero off the channel diagonal (tests/golden/dense_conv_*.json):
+    reading x channel o instead of c, or Wd transposed, fails it."""
+    g = json.load(open(os.path.join(GOLDEN, "dense_conv_two_channels_1x3.json")))
+    assert g["citation"]
+    x = to_layout(np.array(g["x_nhwc"], np.float32), layout)
+    wd = np.array(g["wd"], np.float32)
+    assert wd.shape == (g["Co"], g["C"], g["kH"], g["kW"])
+    b = np.array(g["b"], np.float32)
+    y = oracle_mod.dense_conv(x, wd, b, g["stride"], g["dilation"], layout)
+    np.testing.assert_array_equal(from_layout(y, layout), np.array(g["y_nhwc"], np.float64))
+    # the same arithmetic without the bias, by the definition written out here
+    x_l = np.array(g["x_nhwc"], np.float64)[0, 0]          # [w][c]
+    xp = np.pad(x_l, ((1, 1), (0, 0)))
+    want = np.array([[sum(wd[o, c, 0, k] * xp[w + k, c] for c in range(2) for k in range(3))
+                      for o in range(2)] for w in range(3)])
+    np.testing.assert_array_equal(from_layout(y, layout)[0, 0] - b, want)
 
 
 # --------------------------------------------------------------------------
