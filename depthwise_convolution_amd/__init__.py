@@ -39,15 +39,16 @@ STATUS = {
     0: "OK", -1: "NULL_PTR", -2: "BAD_DIM", -3: "BAD_STRIDE", -4: "BAD_DILATION",
     -5: "EVEN_KERNEL", -6: "BAD_LAYOUT", -7: "BAD_WTYPE", -8: "ALIAS", -9: "MISALIGNED",
     -10: "LAUNCH", -11: "BAD_OP", -12: "BAD_STRATEGY", -13: "WORKSPACE", -14: "BAD_PAD",
-    -15: "BAD_EPILOGUE",
+    -15: "BAD_EPILOGUE", -16: "SCRATCH",
 }
+SCRATCH_BYTES = 16 << 20     # DWCONV_SCRATCH_BYTES
 EXPORTS = ("dwconv2d_fwd", "dwconv2d_input_grad", "dwconv2d_launch", "dwconv2d_describe",
            "dwconv2d_weight_grad", "dwconv2d_weight_grad_workspace_size",
            "dwconv2d_strerror", "dwconv2d_version",
            "dwconv2d_same_pads", "dwconv2d_out_extents", "dwconv2d_launch_ex",
            "dwconv2d_describe_ex", "dwconv2d_weight_grad_workspace_size_ex",
            "dwconv2d_weight_grad_ex", "dwconv2d_fwd_bn_act_ex", "dwconv2d_weight_grad_sgd_ex",
-           "dwconv2d_describe_addr_ex")
+           "dwconv2d_describe_addr_ex", "dwconv2d_weight_grad_noalloc_ex")
 
 _lib = None
 
@@ -95,6 +96,7 @@ def lib():
                                                        ctypes.c_char_p, i, ctypes.POINTER(ll), ip]
     L.dwconv2d_weight_grad_workspace_size_ex.argtypes = [i] * 9 + [ip, i, i, ctypes.POINTER(ll)]
     L.dwconv2d_weight_grad_ex.argtypes = [vp, vp, vp, vp, vp, ll] + [i] * 9 + [ip, i, i, vp]
+    L.dwconv2d_weight_grad_noalloc_ex.argtypes = [vp, vp, vp, vp] + [i] * 9 + [ip, i, i, vp]
     f32 = ctypes.c_float
     L.dwconv2d_fwd_bn_act_ex.argtypes = ([vp, vp, i, vp, vp, vp, vp, vp, f32, i, vp] + [i] * 9 +
                                          [ip, i, i, vp])
@@ -511,6 +513,36 @@ def dwconv2d_weight_grad_ex(x, dy, dw, db, workspace, stride=1, dilation=1, pads
     _check_status(st, "dwconv2d_weight_grad_ex")
     return dw, db
 
+
+
+def dwconv2d_weight_grad_noalloc_ex(x, dy, dw, db, stride=1, dilation=1, pads=None, mult=1,
+                                    layout=NHWC, strategy=STRATEGY_AUTO, stream=None):
+    """dwconv2d_weight_grad_ex with the partial sums in the library's own
+    scratch array (no workspace, no allocation): for callers that cannot
+    allocate.  Calls that overlap on one GPU race on that array."""
+    import torch
+    lay = _layout_code(layout)
+    N, H, W, C = _dims(x, lay)
+    _check_dev(x, "x", (torch.float32,))
+    _check_dev(dy, "dy", (torch.float32,))
+    _check_dev(dw, "dw", (torch.float32,))
+    if dw.dim() != 3 or int(dw.shape[0]) != mult * C:
+        raise ValueError("dw must be (mult*C, kH, kW)")
+    kH, kW = int(dw.shape[1]), int(dw.shape[2])
+    pads = _pads_or_same(pads, H, W, kH, kW, stride, dilation)
+    if db is not None:
+        _check_dev(db, "db", (torch.float32,))
+        if tuple(db.shape) != (mult * C,):
+            raise ValueError("db must be (mult*C,)")
+    Ho, Wo = dwconv2d_out_extents(H, W, kH, kW, stride, dilation, pads)
+    if tuple(dy.shape) != _shape(lay, N, Ho, Wo, mult * C):
+        raise ValueError(f"dy shape {tuple(dy.shape)} != {_shape(lay, N, Ho, Wo, mult * C)}")
+    st = lib().dwconv2d_weight_grad_noalloc_ex(_ptr(x), _ptr(dy), _ptr(dw), _ptr(db), N, H, W,
+                                               C, mult, kH, kW, stride, dilation,
+                                               _pads_arg(pads), lay, strategy,
+                                               _stream(dw, stream))
+    _check_status(st, "dwconv2d_weight_grad_noalloc_ex")
+    return dw, db
 
 
 # ------------------------------------------------------------- fused epilogues

@@ -409,6 +409,38 @@ int dwconv2d_weight_grad_ex(const float *x, const float *dy, float *dw, float *d
     return wgrad(p, x, dy, dw, db, workspace, workspace_bytes, strategy, stream);
 }
 
+int dwconv2d_weight_grad_noalloc_ex(const float *x, const float *dy, float *dw, float *db,
+                                    int N, int H, int W, int C, int mult, int kH, int kW,
+                                    int stride, int dilation, const int *pads, int layout,
+                                    int strategy, void *stream)
+{
+    static_assert(DWCONV_SCRATCH_BYTES == dwconv::kScratchBytes, "one scratch size");
+    Problem p;
+    int st = general_problem(DWCONV_OP_WEIGHT_GRAD, DWCONV_W_F32, 0, N, H, W, C, mult, kH, kW,
+                             stride, dilation, pads, layout, &p);
+    if (st != DWCONV_OK)
+        return st;
+    st = dwconv::validate_problem(p);
+    if (st != DWCONV_OK)
+        return st;
+    if (!x || !dy || !dw)
+        return DWCONV_ERR_NULL_PTR;
+    // the plan the launch below makes (same pointers, same choice)
+    Plan pl;
+    st = dwconv::make_plan(p, strategy,
+                           reinterpret_cast<std::uintptr_t>(x) |
+                               reinterpret_cast<std::uintptr_t>(dy), &pl);
+    if (st != DWCONV_OK)
+        return st;
+    if (pl.workspace > dwconv::kScratchBytes)
+        return DWCONV_ERR_SCRATCH;
+    void *scr = nullptr;
+    st = dwconv::scratch_buffer(stream, &scr);
+    if (st != DWCONV_OK)
+        return st;
+    return wgrad(p, x, dy, dw, db, scr, dwconv::kScratchBytes, strategy, stream);
+}
+
 const char *dwconv2d_strerror(int status)
 {
     switch (status) {
@@ -429,6 +461,9 @@ const char *dwconv2d_strerror(int status)
     case DWCONV_ERR_BAD_PAD: return "pad out of range (|pad| >= 65536) or unknown padding mode";
     case DWCONV_ERR_BAD_EPILOGUE:
         return "bad epilogue: unknown activation, partial BatchNorm, bad eps or learning rate";
+    case DWCONV_ERR_SCRATCH:
+        return "allocation-free weight gradient: needs more than the library's 16 MiB scratch "
+               "array, or the stream is not on the current device";
     default: return "unknown status";
     }
 }

@@ -279,6 +279,17 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
                  float *db, void *workspace, void *stream, float *w_upd = nullptr,
                  float *b_upd = nullptr, float lr = 0.0f);
 
+// Scratch array held by the library on every GPU it runs on, for the
+// allocation-free weight gradient (its partial sums): bytes per device.
+constexpr long long kScratchBytes = 16LL << 20;
+
+// Device address of this library's scratch array on the device that
+// `stream` (a hipStream_t; NULL: the current device's) belongs to, which
+// must be the current device.  Looked up once per device.  Returns
+// DWCONV_OK, or DWCONV_ERR_SCRATCH when the stream is on another device or
+// the runtime cannot locate the array.
+int scratch_buffer(void *stream, void **ptr);
+
 // Enqueue the kernel of a plan made by make_plan on `stream` (a hipStream_t);
 // `epi` (forward only, may be NULL) is the fused epilogue.
 // Returns DWCONV_OK, or DWCONV_ERR_LAUNCH if the runtime reports an error.

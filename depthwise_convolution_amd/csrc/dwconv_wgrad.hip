@@ -4,6 +4,8 @@
 // launcher.
 #include "dwconv_device.h"
 
+#include <mutex>
+
 namespace dwconv {
 
 namespace {
@@ -693,7 +695,43 @@ struct WgradNchwTable {
     }
 };
 
+// The allocation-free weight gradient's partial sums live here: one array
+// of kScratchBytes per GPU, allocated when the code object is loaded and
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host the name stands for a host-side shadow): it passes the
+// device address scratch_buffer looks up.
+__device__ __align__(256) float scratch[kScratchBytes / 4];
+
+constexpr int kMaxScratchDevices = 64;
+
 }  // namespace
+
+int scratch_buffer(void *stream_v, void **ptr)
+{
+    static std::once_flag once[kMaxScratchDevices];
+    static void *addr[kMaxScratchDevices];
+    static hipError_t found[kMaxScratchDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return DWCONV_ERR_SCRATCH;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream_v);
+    if (st) {
+        int sdev = -1;
+        if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev)
+            return DWCONV_ERR_SCRATCH;
+    }
+    // once per device, with that device current: each GPU holds its own copy
+    // of the array at its own address
+    std::call_once(once[dev], [dev]() {
+        void *a = nullptr;
+        found[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        addr[dev] = a;
+    });
+    if (found[dev] != hipSuccess || !addr[dev])
+        return DWCONV_ERR_SCRATCH;
+    *ptr = addr[dev];
+    return DWCONV_OK;
+}
 
 int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *dy, float *dw,
                  float *db, void *workspace, void *stream_v, float *w_upd, float *b_upd,

@@ -65,6 +65,9 @@ extern "C" {
 #define DWCONV_ERR_BAD_EPILOGUE -15 /* unknown activation, BatchNorm pointers not all given
                                        or all NULL, eps negative or not finite, or a
                                        learning rate that is not finite               */
+#define DWCONV_ERR_SCRATCH     -16  /* allocation-free weight gradient: the problem needs more
+                                       than the library's scratch array holds, or the stream
+                                       is not on the current device                   */
 
 /* ---- enumerations (passed as int) -------------------------------------- */
 #define DWCONV_LAYOUT_NHWC 0   /* channel innermost (the ggml page's CWHN)    */
@@ -254,6 +257,30 @@ int dwconv2d_weight_grad_ex(const float *x, const float *dy, float *dw, float *d
                             int N, int H, int W, int C, int mult, int kH, int kW,
                             int stride, int dilation, const int *pads, int layout, int strategy,
                             void *stream);
+
+/* Allocation-free weight and bias gradients, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight training or
+ * serving loops, harnesses that forbid hipMalloc): dwconv2d_weight_grad_ex
+ * without the workspace arguments.  The per-tile partial sums go to a
+ * scratch array the library holds on each GPU (DWCONV_SCRATCH_BYTES = 16 MiB
+ * per device, allocated when the library's code is loaded on that device and
+ * kept until the process ends); nothing here calls hipMalloc, hipFree or an
+ * allocating library routine.  The stream must belong to the current device.
+ * A problem whose partial sums need more than the array holds (the
+ * workspace size dwconv2d_weight_grad_workspace_size_ex reports for the same
+ * arguments, up to the 16 MiB) returns DWCONV_ERR_SCRATCH before anything
+ * is enqueued.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (every partial sum is written before it is read,
+ * so nothing needs clearing): calls that may overlap on one GPU -- on
+ * different streams, or from different host threads -- race and must be
+ * serialised by the caller.  Results equal those of dwconv2d_weight_grad_ex
+ * with the same arguments, bit for bit (same kernels, same order). */
+#define DWCONV_SCRATCH_BYTES (16LL << 20)
+
+int dwconv2d_weight_grad_noalloc_ex(const float *x, const float *dy, float *dw, float *db,
+                                    int N, int H, int W, int C, int mult, int kH, int kW,
+                                    int stride, int dilation, const int *pads, int layout,
+                                    int strategy, void *stream);
 
 /* ---- fused epilogues ----------------------------------------------------
  *

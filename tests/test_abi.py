@@ -469,3 +469,28 @@ def test_plans_for_tensors_off_16_byte_alignment(off):
     u = dw.dwconv2d_describe_addr_ex(dw.OP_FWD, 1, 9, 9, 8, 3, 3, layout=dw.NHWC,
                                      strategy=dw.STRATEGY_DIRECT, addr_bits=off)[0]
     assert "_v4_" in a and "_v1_" in u
+
+
+def test_weight_grad_noalloc_rejects_before_touching_the_gpu(L):
+    """The allocation-free weight gradient validates like the workspace form,
+    and a problem whose partial sums need more than the library's scratch
+    array (its workspace size above DWCONV_SCRATCH_BYTES) is refused with
+    DWCONV_ERR_SCRATCH before any runtime call (fake addresses here)."""
+    assert dw.SCRATCH_BYTES == 16 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+DWCONV_SCRATCH_BYTES\s+\(16LL << 20\)", text)
+    f = L.dwconv2d_weight_grad_noalloc_ex
+    x, g, wgt = 0x10000, 0x40000000000, 0x80000000000
+    big = (64, 112, 112, 256, 7, 7)                  # 43.75 MiB of partial sums (NHWC)
+    pads = dw._pads_arg(dw.dwconv2d_same_pads(dw.PAD_SAME, 112, 112, 7, 7))
+    need = dw.dwconv2d_weight_grad_workspace_size_ex(*big[:4], 7, 7, 1, 1, None, 1, dw.NHWC)
+    assert need > dw.SCRATCH_BYTES
+    N, H, W, C, kH, kW = big
+    assert f(x, g, wgt, None, N, H, W, C, 1, kH, kW, 1, 1, pads, dw.NHWC, 0, None) == -16
+    assert L.dwconv2d_strerror(-16).decode().startswith("allocation-free")
+    # ordinary argument errors come first
+    assert f(None, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, pads, dw.NHWC, 0, None) == -1
+    assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 3, 1, pads, dw.NHWC, 0, None) == -3
+    assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, None, dw.NHWC, 0, None) == -1
+    assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, pads, 5, 0, None) == -6
+    assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, pads, dw.NHWC, 9, None) == -12
