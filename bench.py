@@ -1,14 +1,22 @@
 """Benchmark: depthwise conv2d forward + input gradient on one MI355X.
 
 A step is one forward and one input gradient of the 512x512x256 3x3 NHWC
-workload (fp32 activations and weights), inputs resident in HBM.  The JSON
-line reports whole-step effective HBM bandwidth (algorithmic bytes: x+y+W+b
-for the forward, dy+dx+W for the input gradient), the roofline of the
-dominant kernel timed with HIP events on its own stream, the CPU oracle timed
-on a bounded sample, and a per-workload table (forward and input gradient,
-both layouts, back-to-back "warm" and cache-flushed "cold" kernel times).
+workload (fp32 activations and weights), inputs resident in HBM.  The last
+stdout line is one short JSON object: whole-step effective HBM bandwidth
+(algorithmic bytes: x+y+W+b for the forward, dy+dx+W for the input
+gradient), the roofline of the dominant kernel timed with HIP events on its
+own stream, and the CPU oracle (single-precision timing build) on the host's
+cores.  Everything else -- the per-workload table (forward, input gradient,
+weight gradient and the fused ops in both layouts, each against its HBM or
+VALU floor, an empty-launch floor and a same-bytes copy, and the oracle's
+time on all cores and on one), the practical ceilings, the weight-gradient,
+fused and graph legs -- goes to a JSON detail file (--detail, default
+gpurun_out/bench_detail.json) and, one line per row, to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-table] [--no-cpu]
+                       [--detail PATH] [--table-only] [--calib-copy]
+       python bench.py --trace-table KERNEL_TRACE_CSV [--out MD]   (no GPU: summarise a
+                       rocprofv3 kernel trace of a --table-only run per workload)
 """
 import argparse
 import hashlib
@@ -16,18 +24,22 @@ import json
 import os
 import statistics
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+# fp32 FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+PEAK_VALU_TFLOPS = 78.6
 HEADLINE = "large_512x512x256_3x3"
 # the sources that decide the headline kernel's code and plan: a change to any
 # of them makes the recorded traffic counts stale
 KERNEL_SRCS = [os.path.join(ROOT, "depthwise_convolution_amd", "csrc", f)
                for f in ("dwconv_internal.h", "dwconv_device.h", "dwconv_tiled_nhwc.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_large_512x512x256_3x3_nhwc.json")
+OPS = ("fwd", "ig", "wgrad", "fwd_bn_relu6", "wgrad_sgd")
 
 
 def _log(msg):
@@ -57,30 +69,35 @@ def load_traffic(op):
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ problems
 def to_dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def make_problem(torch, wl, layout, seed=0):
-    from depthwise_convolution_amd import workloads
-    inp = workloads.make_inputs(wl, layout, seed=seed)
-    t = {k: (None if v is None else to_dev(torch, v)) for k, v in inp.items()}
-    shape_x = tuple(inp["x"].shape)
-    t["y"] = torch.empty(tuple(inp["dy"].shape), dtype=torch.float32, device="cuda")
-    t["dx"] = torch.empty(shape_x, dtype=torch.float32, device="cuda")
-    import depthwise_convolution_amd as dw
+def workspace_bytes(dw, wl, layout):
     if wl.general:
-        nws = dw.dwconv2d_weight_grad_workspace_size_ex(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
-                                                        wl.stride, wl.dilation, wl.pads,
-                                                        wl.mult, layout)
-    else:
-        nws = dw.dwconv2d_weight_grad_workspace_size(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
-                                                     wl.stride, wl.dilation, layout)
+        return dw.dwconv2d_weight_grad_workspace_size_ex(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                                         wl.stride, wl.dilation, wl.pads,
+                                                         wl.mult, layout)
+    return dw.dwconv2d_weight_grad_workspace_size(wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                                  wl.stride, wl.dilation, layout)
+
+
+def make_problem(torch, wl, layout, seed=0, inputs=None):
+    """Device tensors of a workload: x, w, b, dy (seeded draws), outputs y, dx,
+    dW, db, the weight-gradient workspace, BatchNorm arrays and the SGD step's
+    float32 weights / bias."""
+    from depthwise_convolution_amd import workloads
+    import depthwise_convolution_amd as dw
+    inp = inputs if inputs is not None else workloads.make_inputs(wl, layout, seed=seed)
+    t = {k: (None if v is None else to_dev(torch, v)) for k, v in inp.items()}
+    t["y"] = torch.empty(tuple(inp["dy"].shape), dtype=torch.float32, device="cuda")
+    t["dx"] = torch.empty(tuple(inp["x"].shape), dtype=torch.float32, device="cuda")
+    nws = workspace_bytes(dw, wl, layout)
     t["ws"] = torch.empty(max(4, (nws + 15) // 16 * 4), dtype=torch.float32, device="cuda")
     t["dW"] = torch.empty((wl.Co, wl.kH, wl.kW), dtype=torch.float32, device="cuda")
     t["db"] = torch.empty((wl.Co,), dtype=torch.float32, device="cuda")
-    # inference BatchNorm of the output channels (gamma, beta, mean, var) and
-    # float32 weights / bias for the SGD step (updated in place by each call)
+    # inference BatchNorm of the output channels (gamma, beta, mean, var)
     g = torch.Generator(device="cpu").manual_seed(seed + 1)
     t["bn"] = tuple((torch.rand(wl.Co, generator=g) * s + o).to("cuda")
                     for s, o in ((1.5, 0.5), (2.0, -1.0), (1.0, -0.5), (2.8, 0.2)))
@@ -89,74 +106,97 @@ def make_problem(torch, wl, layout, seed=0):
     return t
 
 
-def launch_fwd(dw, wl, t, layout, stream):
-    if wl.general:
-        dw.dwconv2d_launch_ex(dw.OP_FWD, t["x"], t["w"], t["b"], t["y"], wl.H, wl.W, wl.stride,
-                              wl.dilation, wl.pads, wl.mult, layout, dw.STRATEGY_AUTO, stream)
-    else:
-        dw.dwconv2d_fwd(t["x"], t["w"], t["b"], t["y"], wl.stride, wl.dilation, layout, stream)
+def second_set(torch, t):
+    """Another copy of the tensors a launch reads and writes, so back-to-back
+    launches can alternate between two disjoint buffer sets."""
+    u = dict(t)
+    for k in ("x", "dy", "y", "dx", "ws", "dW", "db"):
+        u[k] = t[k].clone()
+    return u
 
 
-def launch_ig(dw, wl, t, layout, stream):
-    if wl.general:
-        dw.dwconv2d_launch_ex(dw.OP_INPUT_GRAD, t["dy"], t["w"], None, t["dx"], wl.H, wl.W,
-                              wl.stride, wl.dilation, wl.pads, wl.mult, layout,
-                              dw.STRATEGY_AUTO, stream)
-    else:
-        dw.dwconv2d_input_grad(t["dy"], t["w"], t["dx"], wl.stride, wl.dilation, layout, stream)
-
-
-def launch_wgrad(dw, wl, t, layout, stream):
-    if wl.general:
-        dw.dwconv2d_weight_grad_ex(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
-                                   wl.dilation, wl.pads, wl.mult, layout, dw.STRATEGY_AUTO,
+# ------------------------------------------------------------------ launches
+def launch(dw, wl, t, layout, op, stream):
+    """Enqueue one op of a workload through the C ABI (the AUTO strategy)."""
+    g = wl.general
+    if op == "fwd":
+        if g:
+            dw.dwconv2d_launch_ex(dw.OP_FWD, t["x"], t["w"], t["b"], t["y"], wl.H, wl.W,
+                                  wl.stride, wl.dilation, wl.pads, wl.mult, layout,
+                                  dw.STRATEGY_AUTO, stream)
+        else:
+            dw.dwconv2d_fwd(t["x"], t["w"], t["b"], t["y"], wl.stride, wl.dilation, layout,
+                            stream)
+    elif op == "ig":
+        if g:
+            dw.dwconv2d_launch_ex(dw.OP_INPUT_GRAD, t["dy"], t["w"], None, t["dx"], wl.H, wl.W,
+                                  wl.stride, wl.dilation, wl.pads, wl.mult, layout,
+                                  dw.STRATEGY_AUTO, stream)
+        else:
+            dw.dwconv2d_input_grad(t["dy"], t["w"], t["dx"], wl.stride, wl.dilation, layout,
                                    stream)
+    elif op == "wgrad":
+        if g:
+            dw.dwconv2d_weight_grad_ex(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
+                                       wl.dilation, wl.pads, wl.mult, layout, dw.STRATEGY_AUTO,
+                                       stream)
+        else:
+            dw.dwconv2d_weight_grad(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
+                                    wl.dilation, layout, dw.STRATEGY_AUTO, stream)
+    elif op == "fwd_bn_relu6":
+        # forward with the fused BatchNorm + ReLU6 epilogue (MobileNetV2 block)
+        dw.dwconv2d_fwd_bn_act_ex(t["x"], t["w"], t["b"], t["y"], t["bn"], 1e-3, dw.ACT_RELU6,
+                                  wl.stride, wl.dilation, wl.pads, wl.mult, layout,
+                                  dw.STRATEGY_AUTO, stream)
+    elif op == "wgrad_sgd":
+        # weight + bias gradient with the fused SGD step (w, b updated in place)
+        dw.dwconv2d_weight_grad_sgd_ex(t["x"], t["dy"], t["w_sgd"], t["b_sgd"], 1e-4, t["ws"],
+                                       None, None, wl.stride, wl.dilation, wl.pads, wl.mult,
+                                       layout, dw.STRATEGY_AUTO, stream)
     else:
-        dw.dwconv2d_weight_grad(t["x"], t["dy"], t["dW"], t["db"], t["ws"], wl.stride,
-                                wl.dilation, layout, dw.STRATEGY_AUTO, stream)
+        raise ValueError(op)
 
 
-def launch_fwd_bn_act(dw, wl, t, layout, stream):
-    """Forward with the fused BatchNorm + ReLU6 epilogue (MobileNetV2 block)."""
-    dw.dwconv2d_fwd_bn_act_ex(t["x"], t["w"], t["b"], t["y"], t["bn"], 1e-3, dw.ACT_RELU6,
-                              wl.stride, wl.dilation, wl.pads, wl.mult, layout,
-                              dw.STRATEGY_AUTO, stream)
-
-
-def launch_wgrad_sgd(dw, wl, t, layout, stream):
-    """Weight + bias gradient with the fused SGD step (w, b updated in place)."""
-    dw.dwconv2d_weight_grad_sgd_ex(t["x"], t["dy"], t["w_sgd"], t["b_sgd"], 1e-4, t["ws"],
-                                   None, None, wl.stride, wl.dilation, wl.pads, wl.mult, layout,
-                                   dw.STRATEGY_AUTO, stream)
-
-
-def fwd_bn_act_bytes(wl):
-    """x + y + W + b + the four BatchNorm arrays."""
-    return wl.fwd_bytes() + 16 * wl.Co
-
-
-def wgrad_sgd_bytes(wl):
-    """x + dy + W and b read and written (the gradients are not written)."""
+def op_bytes(wl, op):
+    """Algorithmic HBM bytes of one call."""
+    if op == "fwd":
+        return wl.fwd_bytes()
+    if op == "ig":
+        return wl.ig_bytes()
+    if op == "wgrad":
+        return wl.wgrad_bytes()                       # x + dy + dW + db
+    if op == "fwd_bn_relu6":
+        return wl.fwd_bytes() + 16 * wl.Co            # + the four BatchNorm arrays
+    # x + dy read, W and b read and written (the gradients are not written)
     return (4 * wl.N * wl.H * wl.W * wl.C + 4 * wl.N * wl.Ho * wl.Wo * wl.Co
             + 8 * wl.Co * wl.kH * wl.kW + 8 * wl.Co)
 
 
-def wgrad_bytes(wl):
-    """Algorithmic bytes of the weight + bias gradient: x + dy + dW + db."""
-    return wl.wgrad_bytes()
+def op_flops(wl, op):
+    """Algorithmic fp32 flops: every dy / y element meets every tap once (one
+    FMA = 2 flops) in all three ops."""
+    return 2 * wl.kH * wl.kW * wl.N * wl.Ho * wl.Wo * wl.Co
+
+
+def floors(wl, op):
+    """(bound, floor us): the larger of the HBM time of the algorithmic bytes
+    at 8 TB/s and the VALU time of the algorithmic flops at 78.6 TFLOP/s."""
+    t_hbm = op_bytes(wl, op) / PEAK_HBM_GBS / 1e3
+    t_alu = op_flops(wl, op) / PEAK_VALU_TFLOPS / 1e6
+    return ("hbm", t_hbm) if t_hbm >= t_alu else ("alu", t_alu)
 
 
 def describe(dw, wl, op, layout):
     """Kernel name of an op of a workload under the AUTO strategy."""
-    wt = 0 if op == dw.OP_WEIGHT_GRAD else int(wl.fp16_weights)
-    if wl.general:
-        return dw.dwconv2d_describe_ex(op, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
-                                       wl.dilation, wl.pads, wl.mult, layout, wt,
-                                       op == dw.OP_FWD)[0]
-    return dw.dwconv2d_describe(op, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
-                                wl.dilation, layout, wt, op == dw.OP_FWD)[0]
+    opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD,
+           "fwd_bn_relu6": dw.OP_FWD, "wgrad_sgd": dw.OP_WEIGHT_GRAD}[op]
+    wt = 0 if opc == dw.OP_WEIGHT_GRAD else int(wl.fp16_weights)
+    return dw.dwconv2d_describe_ex(opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
+                                   wl.dilation, wl.pads, wl.mult, layout, wt,
+                                   opc == dw.OP_FWD)[0]
 
 
+# ------------------------------------------------------------------ timing
 _SPIN_CYCLES_PER_US = None
 
 
@@ -180,97 +220,194 @@ def queue_ahead(torch, stream, us):
         torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
 
 
-def time_kernel(torch, fn, stream, iters, flush=None):
-    """Per-launch kernel time (us) from HIP events recorded on `stream`.
-    Without `flush` the launches are queued behind a spin kernel, so the
-    events bracket device time only; with it, the 1 GiB pass before each
-    launch keeps the device busy while the host submits."""
-    times = []
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    if flush is None:
-        queue_ahead(torch, stream, 200 + 150 * iters)
+def amortised(torch, stream, calls, n=40, host_us=60.0):
+    """Per-call device time (us) of n back-to-back calls that cycle through
+    `calls` (e.g. the same op on two disjoint buffer sets), between two events,
+    all queued behind a spin kernel so the device never waits for the host."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for i in range(iters):
-            if flush is not None:
-                flush.add_(1.0)          # 1 GiB read+write: evicts L2 and the 256 MB MALL
-            starts[i].record(stream)
-            fn()
-            ends[i].record(stream)
+        for c in calls:
+            c()
+    queue_ahead(torch, stream, 300 + host_us * (n + 2))
+    with torch.cuda.stream(stream):
+        calls[0]()
+        calls[-1]()
+        a.record(stream)
+        for i in range(n):
+            calls[i % len(calls)]()
+        b.record(stream)
     stream.synchronize()
-    for s, e in zip(starts, ends):
-        times.append(s.elapsed_time(e) * 1000.0)
-    return times
+    return a.elapsed_time(b) * 1e3 / n
 
 
-def cpu_baseline(wl, rows=None, min_seconds=10.0):
-    """The oracle (as it stands) on the first `rows` rows of the workload's
-    image, forward and input gradient, repeated until about `min_seconds` of
-    CPU work; the mean pass is scaled to the whole step."""
-    import oracle
-    from depthwise_convolution_amd import workloads
-    rows = wl.H if rows is None else rows
-    sub = workloads.Workload(name=wl.name + "_rows", N=wl.N, H=rows, W=wl.W, C=wl.C, kH=wl.kH,
-                             kW=wl.kW, stride=wl.stride, dilation=wl.dilation)
-    inp = workloads.make_inputs(sub, workloads.NHWC, seed=0)
-    threads = max(1, min(16, os.cpu_count() or 1))
-    reps, total = 0, 0.0
-    while reps == 0 or total < min_seconds:
-        t0 = time.perf_counter()
-        oracle.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, workloads.NHWC,
-                   nthreads=threads)
-        oracle.input_grad(inp["dy"], inp["w"], rows, wl.W, wl.stride, wl.dilation,
-                          workloads.NHWC, nthreads=threads)
-        total += time.perf_counter() - t0
-        reps += 1
-    dt = total / reps
-    scale = wl.H / rows
-    step_s = dt * scale
-    gbs = (wl.fwd_bytes() + wl.ig_bytes()) / step_s / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": (f"the whole {wl.H}x{wl.W}x{wl.C} image" if rows == wl.H else
-                       f"rows 0..{rows - 1} of the {wl.H}x{wl.W}x{wl.C} image "
-                       f"({rows / wl.H:.3g} of the outputs, time scaled x{scale:g})") +
-                      f", forward + input gradient, fp64 oracle, mean of {reps} passes",
-            "sample_seconds": round(total, 3), "passes": reps,
-            "ms_per_step_est": round(step_s * 1e3, 1)}
+def cold_median(torch, stream, call, flush, sink, reps=5):
+    """Median of `reps` single-call times, each after a read-only pass over a
+    1 GiB buffer (evicts L2 and the 256 MB Infinity Cache without leaving
+    dirty lines for the timed call to write back); two events around the
+    call, so an event pair's own overhead is in it (`event_pair_us`)."""
+    times = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        with torch.cuda.stream(stream):
+            torch.sum(flush, 0, out=sink)
+            ev[0].record(stream)
+            call()
+            ev[1].record(stream)
+        stream.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    return statistics.median(times)
 
 
-def per_config_table(torch, dw, iters=20):
+# ------------------------------------------------------------------ CPU oracle
+def cpu_threads():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n or 1)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class CpuOracle:
+    """The oracle's timing build (same source, single-precision accumulation,
+    -O3 -march=native, OpenMP), compiled on this host; the parity build is
+    restored on close."""
+
+    def __init__(self):
+        import oracle
+        from oracle import build as obuild
+        self.oracle = oracle
+        self.dir = tempfile.mkdtemp(prefix="dwconv_cpu_")
+        self.prev = oracle.swap_library(obuild.build_timing(self.dir))
+
+    def close(self):
+        import shutil
+        self.oracle.restore_library(self.prev)
+        shutil.rmtree(self.dir, ignore_errors=True)
+
+    def run(self, wl, inp, layout, op, threads):
+        o = self.oracle
+        if op == "fwd":
+            if wl.general:
+                o.fwd_general(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, wl.pads,
+                              wl.mult, layout, nthreads=threads, with_sum=False)
+            else:
+                o.fwd(inp["x"], inp["w"], inp["b"], wl.stride, wl.dilation, layout,
+                      nthreads=threads, with_sum=False)
+        else:
+            if wl.general:
+                o.input_grad_general(inp["dy"], inp["w"], wl.H, wl.W, wl.stride, wl.dilation,
+                                     wl.pads, wl.mult, layout, nthreads=threads, with_sum=False)
+            else:
+                o.input_grad(inp["dy"], inp["w"], wl.H, wl.W, wl.stride, wl.dilation, layout,
+                             nthreads=threads, with_sum=False)
+
+    def time(self, wl, inp, layout, op, threads, reps=3):
+        """Median of `reps` timed runs (us) after one untimed run."""
+        self.run(wl, inp, layout, op, threads)
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            self.run(wl, inp, layout, op, threads)
+            ts.append((time.perf_counter() - t0) * 1e6)
+        return statistics.median(ts)
+
+
+def cpu_baseline(cpu, wl, inp, threads):
+    """The oracle on the host's cores: the headline step (forward + input
+    gradient of the whole image), median of 3 each, and on one thread."""
+    fwd = cpu.time(wl, inp, 0, "fwd", threads)
+    ig = cpu.time(wl, inp, 0, "ig", threads)
+    fwd1 = cpu.time(wl, inp, 0, "fwd", 1, reps=1)
+    ig1 = cpu.time(wl, inp, 0, "ig", 1, reps=1)
+    step_bytes = wl.fwd_bytes() + wl.ig_bytes()
+    return {
+        "value": round(step_bytes / (fwd + ig) / 1e3, 2), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"whole {wl.H}x{wl.W}x{wl.C} {wl.kH}x{wl.kW} NHWC image, fwd + ig, oracle "
+                   f"timing build (fp32 accumulation, -O3 -march=native), median of 3"),
+        "detail": {"fwd_us": round(fwd, 1), "ig_us": round(ig, 1),
+                   "fwd_us_1thread": round(fwd1, 1), "ig_us_1thread": round(ig1, 1),
+                   "GBs_1thread": round(step_bytes / (fwd1 + ig1) / 1e3, 2),
+                   "cpu_model": cpu_model()}}
+
+
+# ------------------------------------------------------------------ legs
+def per_config_table(torch, dw, cpu, threads, only=None):
+    """Every workload (not parity-only), both layouts, all ops: amortised
+    back-to-back device time, cold single-call time, the op's HBM / VALU
+    floor, a same-bytes copy for problems up to 8 MB, and the oracle's forward
+    and input-gradient times on all cores (median of 3) and on one thread."""
     from depthwise_convolution_amd import workloads
     rows = []
-    flush = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")   # 1 GiB
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")   # 1 GiB
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
     for name, wl in workloads.WORKLOADS.items():
-        if "parity_only" in wl.tags:
+        if "parity_only" in wl.tags or (only and name not in only):
             continue
         for layout in (workloads.NHWC, workloads.NCHW):
-            t = make_problem(torch, wl, layout, seed=0)
-            for op, fn, nbytes in (("fwd", launch_fwd, wl.fwd_bytes()),
-                                   ("ig", launch_ig, wl.ig_bytes()),
-                                   ("wgrad", launch_wgrad, wgrad_bytes(wl)),
-                                   ("fwd_bn_relu6", launch_fwd_bn_act, fwd_bn_act_bytes(wl)),
-                                   ("wgrad_sgd", launch_wgrad_sgd, wgrad_sgd_bytes(wl))):
+            inp = workloads.make_inputs(wl, layout, seed=0)
+            t = make_problem(torch, wl, layout, inputs=inp)
+            t2 = second_set(torch, t)
+            for op in OPS:
                 if op.startswith("wgrad") and wl.fp16_weights:
                     continue              # the weight gradient does not read the weights
-                call = (lambda f=fn: f(dw, wl, t, layout, stream))
-                opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD,
-                       "fwd_bn_relu6": dw.OP_FWD, "wgrad_sgd": dw.OP_WEIGHT_GRAD}[op]
-                kname = describe(dw, wl, opc, layout)
-                time_kernel(torch, call, stream, 3)
-                warm = statistics.median(time_kernel(torch, call, stream, iters))
-                cold = statistics.median(time_kernel(torch, call, stream, max(5, iters // 4),
-                                                     flush))
-                rows.append({"workload": name, "layout": workloads.LAYOUT_NAMES[layout],
-                             "op": op, "kernel": kname, "bytes": nbytes,
-                             "warm_us": round(warm, 2), "cold_us": round(cold, 2),
-                             "warm_GBs": round(nbytes / warm / 1e3, 1),
-                             "cold_GBs": round(nbytes / cold / 1e3, 1),
-                             "cold_pct_peak": round(100 * nbytes / cold / 1e3 / PEAK_HBM_GBS, 1)})
-            del t
-        _log(f"[table] {name} done")
+                nbytes = op_bytes(wl, op)
+                calls = [(lambda tt=tt: launch(dw, wl, tt, layout, op, stream)) for tt in (t, t2)]
+                am = amortised(torch, stream, calls)
+                cold = cold_median(torch, stream, calls[0], flush, sink)
+                bound, floor_us = floors(wl, op)
+                row = {"workload": name, "layout": workloads.LAYOUT_NAMES[layout], "op": op,
+                       "kernel": describe(dw, wl, op, layout), "bytes": nbytes,
+                       "flops": op_flops(wl, op),
+                       "us": round(am, 2), "cold_us": round(cold, 2),
+                       "GBs": round(nbytes / am / 1e3, 1),
+                       "pct_hbm_peak": round(100 * nbytes / am / 1e3 / PEAK_HBM_GBS, 1),
+                       "TFLOPs": round(op_flops(wl, op) / am / 1e6, 2),
+                       "bound": bound, "floor_us": round(floor_us, 3),
+                       "frac_of_bound": round(floor_us / am, 3)}
+                if nbytes <= 8 * 1000 * 1000 and op in ("fwd", "ig"):
+                    half = max(1, nbytes // 8)           # floats each way
+                    src = [torch.ones(half, device="cuda") for _ in range(2)]
+                    dst = [torch.empty(half, device="cuda") for _ in range(2)]
+                    cp = [(lambda i=i: dst[i].copy_(src[i])) for i in range(2)]
+                    row["copy_same_bytes_us"] = round(amortised(torch, stream, cp), 2)
+                    del src, dst
+                if cpu is not None and op in ("fwd", "ig"):
+                    row["cpu_us"] = round(cpu.time(wl, inp, layout, op, threads), 1)
+                    row["cpu_us_1thread"] = round(cpu.time(wl, inp, layout, op, 1, reps=1), 1)
+                    row["cpu_threads"] = threads
+                rows.append(row)
+                _log("[row] " + json.dumps(row))
+            del t, t2
+        torch.cuda.empty_cache()
     del flush
     return rows
+
+
+def launch_floor(torch, stream, flush, sink):
+    """The smallest launch: an empty kernel (a zero-cycle spin), back to back
+    (amortised, queued ahead) and as one call between two events after the
+    read-only flush (the overhead in every `cold_us`)."""
+    k = (lambda: torch.cuda._sleep(0))
+    with torch.cuda.stream(stream):
+        am = amortised(torch, stream, [k], n=200, host_us=10.0)
+    ev = cold_median(torch, stream, k, flush, sink, reps=9)
+    return {"empty_launch_us": round(am, 3), "event_pair_us": round(ev, 3),
+            "note": "empty kernel (torch.cuda._sleep(0)): 200 back-to-back launches between "
+                    "two events, queued behind a spin kernel; and one launch between two "
+                    "events after the 1 GiB read-only flush, median of 9"}
 
 
 def graph_leg(torch, dw, reps=20):
@@ -286,9 +423,8 @@ def graph_leg(torch, dw, reps=20):
     stream = torch.cuda.Stream()
 
     def step():
-        launch_fwd(dw, wl, t, layout, stream)
-        launch_ig(dw, wl, t, layout, stream)
-        launch_wgrad(dw, wl, t, layout, stream)
+        for op in ("fwd", "ig", "wgrad"):
+            launch(dw, wl, t, layout, op, stream)
 
     def wall(fn, n):
         torch.cuda.synchronize()
@@ -312,7 +448,7 @@ def graph_leg(torch, dw, reps=20):
     torch.cuda.synchronize()
     g.replay()
     graph_us = min(wall(g.replay, 1) for _ in range(5)) / reps
-    nbytes = wl.fwd_bytes() + wl.ig_bytes() + wgrad_bytes(wl)
+    nbytes = wl.fwd_bytes() + wl.ig_bytes() + wl.wgrad_bytes()
     del g, t
     return {"workload": wl.name + " nhwc", "step": "fwd + ig + wgrad (4 kernels)",
             "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
@@ -320,18 +456,139 @@ def graph_leg(torch, dw, reps=20):
             "timing": f"best of 3 (eager) / 5 (graph) runs of {reps} steps, wall clock"}
 
 
+def headline_extras(torch, dw, wl, t, layout, stream, n_rep=40):
+    """Weight gradient and fused ops of the headline workload, and the plain
+    copies of its forward's bytes, each timed like the roofline leg
+    (back-to-back calls alternating between two disjoint buffer sets)."""
+    t2 = second_set(torch, t)
+    out = {}
+    for op in ("wgrad", "wgrad_sgd", "fwd", "fwd_bn_relu6"):
+        calls = [(lambda tt=tt: launch(dw, wl, tt, layout, op, stream)) for tt in (t, t2)]
+        us = amortised(torch, stream, calls, n=n_rep)
+        out[op] = {"kernel": describe(dw, wl, op, layout), "us": round(us, 2),
+                   "pct_hbm_peak": round(100 * op_bytes(wl, op) / us / 1e3 / PEAK_HBM_GBS, 1)}
+    # practical ceilings: the forward's bytes (256 MiB read + 256 MiB written)
+    # through the runtime's device copy and through torch's elementwise kernel
+    cp = [(lambda: t["y"].copy_(t["x"])), (lambda: t2["y"].copy_(t2["x"]))]
+    ew = [(lambda: torch.mul(t["x"], 1.0, out=t["y"])),
+          (lambda: torch.mul(t2["x"], 1.0, out=t2["y"]))]
+    copy_bytes = 2 * t["x"].numel() * 4
+    copy_us = amortised(torch, stream, cp, n=n_rep)
+    ew_us = amortised(torch, stream, ew, n=n_rep)
+    out["ceilings"] = {"copy_bytes": copy_bytes,
+                       "runtime_copy_us": round(copy_us, 2),
+                       "runtime_copy_GBs": round(copy_bytes / copy_us / 1e3, 1),
+                       "elementwise_copy_us": round(ew_us, 2),
+                       "elementwise_copy_GBs": round(copy_bytes / ew_us / 1e3, 1)}
+    del t2
+    return out
+
+
+# ------------------------------------------------------------------ trace table
+def trace_table(csv_path, out_path=None):
+    """Summarise a rocprofv3 kernel-trace CSV of `bench.py --table-only` per
+    workload: each (kernel, grid) is matched to the workloads/layouts/ops
+    whose plan launches it (the describe call's kernel shape and grid), and
+    the per-dispatch durations give median / mean / min.  No GPU needed."""
+    import csv
+    import re
+    import depthwise_convolution_amd as dw
+    from depthwise_convolution_amd import workloads
+    durs = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            grid = int(r.get("Grid_Size_X", r.get("Grid_Size", "0")) or 0)
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            durs.setdefault((name, grid), []).append(d)
+
+    def tmpl(name):
+        m = re.search(r"(k_\w+)<(.*)>", name)
+        return (m.group(1), m.group(2).replace(" ", "")) if m else (name, "")
+
+    # wgrad rows: the first (partial-sum) kernel; the fixed-order reduction
+    # that follows it is a separate dispatch of 3-5 us
+    lines = ["| workload | layout | op | kernel | calls | median us | mean us | min us | "
+             "floor us (bound) | median frac of floor |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, wl in workloads.WORKLOADS.items():
+        if "parity_only" in wl.tags:
+            continue
+        for layout in (0, 1):
+            for op in ("fwd", "ig", "wgrad"):
+                if op == "wgrad" and wl.fp16_weights:
+                    continue
+                opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
+                kname, grid, block = dw.dwconv2d_describe_ex(
+                    opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation, wl.pads,
+                    wl.mult, layout, 0 if op == "wgrad" else int(wl.fp16_weights), op == "fwd")
+                fam = {"tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
+                       "stream_nhwc": "k_stream_nhwc",
+                       "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
+                       "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc",
+                       "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
+                       "wgrad_direct": "k_wgrad_gen"}
+                kfam = next((v for k, v in sorted(fam.items(), key=lambda kv: -len(kv[0]))
+                             if kname.startswith(k)), None)
+                cands = []
+                for (kn, g), ds in durs.items():
+                    f, args = tmpl(kn)
+                    if f != kfam or g != grid * block:
+                        continue
+                    parts = args.split(",")
+                    if op != "wgrad" and parts[0] in ("float", "_Float16", "half"):
+                        if (parts[0] != "float") != bool(wl.fp16_weights):
+                            continue
+                    # the op in the template arguments: the tiled kernels' mode
+                    # (0 forward, 1 input gradient) third from last, the
+                    # streaming kernel's last; the direct kernels' input-gradient flag
+                    if op != "wgrad":
+                        want = {"fwd": "0", "ig": "1"}[op]
+                        if kfam.startswith("k_tiled") and parts[-3] != want:
+                            continue
+                        if kfam.startswith("k_stream") and parts[-1] != want:
+                            continue
+                        if kfam.startswith("k_direct"):
+                            flags = [q for q in parts if q in ("true", "false")]
+                            if flags and flags[0] != ("true" if op == "ig" else "false"):
+                                continue
+                    cands.append((kn, ds))
+                if not cands:
+                    continue
+                kn, ds = max(cands, key=lambda c: len(c[1]))
+                bound, floor_us = floors(wl, op)
+                med = statistics.median(ds)
+                lines.append(f"| {name} | {workloads.LAYOUT_NAMES[layout]} | {op} | "
+                             f"`{kname}` | {len(ds)} | {med:.2f} | {statistics.mean(ds):.2f} | "
+                             f"{min(ds):.2f} | {floor_us:.2f} ({bound}) | "
+                             f"{floor_us / med:.3f} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text
+
+
+# ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # 50 untimed steps (~10 ms): the first ~100 steps of a process run ~6%
-    # slower while the device settles, measured on MI355X
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-table", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--table-only", action="store_true",
+                    help="only the per-workload table (for a profiler run)")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated workload names for the table (default: all)")
+    ap.add_argument("--detail", default=os.path.join("gpurun_out", "bench_detail.json"))
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
+    ap.add_argument("--trace-table", default="", help="summarise a kernel-trace CSV and exit")
+    ap.add_argument("--out", default="")
     args = ap.parse_args()
+    if args.trace_table:
+        print(trace_table(args.trace_table, args.out or None))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: there is no multi-GPU path (the operator "
               "shards over images and channels with no exchange between GPUs, so each GPU "
@@ -346,21 +603,38 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dw.lib()
+    detail = {"bench_detail_of": "bench.py", "argv": sys.argv[1:]}
+    threads = cpu_threads()
+    cpu = None if args.no_cpu else CpuOracle()
+    only = [s for s in args.workloads.split(",") if s]
+    if args.table_only:
+        detail["per_config"] = per_config_table(torch, dw, cpu, threads, only)
+        _write_detail(args.detail, detail)
+        if cpu:
+            cpu.close()
+        return
+
     wl = workloads.WORKLOADS[HEADLINE]
     layout = workloads.NHWC
     _log(f"[bench] generating {HEADLINE} inputs")
-    t = make_problem(torch, wl, layout, seed=0)
+    inp = workloads.make_inputs(wl, layout, seed=0)
+    t = make_problem(torch, wl, layout, inputs=inp)
     stream = torch.cuda.Stream()
 
     def step():
-        launch_fwd(dw, wl, t, layout, stream)
-        launch_ig(dw, wl, t, layout, stream)
+        launch(dw, wl, t, layout, "fwd", stream)
+        launch(dw, wl, t, layout, "ig", stream)
 
+    # warmup: the requested steps, and at least 100 steps and 50 ms of them
+    # (the device takes ~10 ms of steady work before its step time settles)
     _log("[bench] warmup")
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
+    n_warm, t_warm = 0, time.perf_counter()
+    while n_warm < args.warmup or n_warm < 100 or time.perf_counter() - t_warm < 0.05:
+        with torch.cuda.stream(stream):
+            for _ in range(10):
+                step()
+        n_warm += 10
+        torch.cuda.synchronize()
 
     # timed region: K steps, wall clock between device-wide synchronisations
     torch.cuda.synchronize()
@@ -371,211 +645,76 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     _log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms")
-    # per-kernel durations: the same steps again, untimed by the wall clock,
-    # with HIP events on the launch stream around every kernel
+    # per-kernel durations: HIP events on the launch stream around every
+    # kernel of 50 more steps (each pair of events adds its own overhead)
     n_ev = min(args.steps, 50)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
     with torch.cuda.stream(stream):
         for i in range(n_ev):
             ev[i][0].record(stream)
-            launch_fwd(dw, wl, t, layout, stream)
+            launch(dw, wl, t, layout, "fwd", stream)
             ev[i][1].record(stream)
-            launch_ig(dw, wl, t, layout, stream)
+            launch(dw, wl, t, layout, "ig", stream)
             ev[i][2].record(stream)
     torch.cuda.synchronize()
-    fwd_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    ig_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    fwd_avg = statistics.mean(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+    ig_avg = statistics.mean(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
 
     step_bytes = wl.fwd_bytes() + wl.ig_bytes()
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    fwd_avg, ig_avg = statistics.mean(fwd_us), statistics.mean(ig_us)
-    dom, dom_bytes = ("fwd", wl.fwd_bytes()) if fwd_avg >= ig_avg else ("ig", wl.ig_bytes())
-    dom_kernel = dw.dwconv2d_describe(dw.OP_FWD if dom == "fwd" else dw.OP_INPUT_GRAD, wl.N,
-                                      wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation,
-                                      layout, 0, dom == "fwd")[0]
+    dom = "fwd" if fwd_avg >= ig_avg else "ig"
+    dom_bytes = op_bytes(wl, dom)
     # Dominant kernel's launch duration with the event overhead amortised: two
     # events around 40 back-to-back launches that alternate between two
     # disjoint buffer sets (256 MiB in / out each), so no launch finds its
     # input in the 256 MB Infinity Cache.
-    alt = {"x": t["dy"] if dom == "fwd" else t["x"], "y": t["dx"] if dom == "fwd" else t["y"]}
-    assert t["x"].shape == t["dy"].shape, "the alternating-buffer timing needs stride 1"
+    alt = {"x": t["dy"], "y": t["dx"], "dy": t["x"], "dx": t["y"]}
     k_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     n_rep = 40
     with torch.cuda.stream(stream):
         for i in range(n_rep + 4):
             if i == 4:
                 k_ev[0].record(stream)
-            if dom == "fwd":
-                src, dst = (t["x"], t["y"]) if i % 2 == 0 else (alt["x"], alt["y"])
-                dw.dwconv2d_fwd(src, t["w"], t["b"], dst, wl.stride, wl.dilation, layout, stream)
-            else:
-                src, dst = (t["dy"], t["dx"]) if i % 2 == 0 else (alt["y"], alt["x"])
-                dw.dwconv2d_input_grad(src, t["w"], dst, wl.stride, wl.dilation, layout, stream)
+            launch(dw, wl, t if i % 2 == 0 else dict(t, **alt), layout, dom, stream)
         k_ev[1].record(stream)
     torch.cuda.synchronize()
     dom_us = k_ev[0].elapsed_time(k_ev[1]) * 1e3 / n_rep
     achieved = dom_bytes / dom_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic(dom), "kernel": dom_kernel,
-                "avg_launch_us": round(dom_us, 2),
-                "avg_launch_us_events_each_launch": round(fwd_avg if dom == "fwd" else ig_avg, 2),
-                "algorithmic_bytes_per_launch": dom_bytes}
-
+                "traffic": load_traffic(dom), "kernel": describe(dw, wl, dom, layout),
+                "avg_launch_us": round(dom_us, 2)}
     result = {
         "metric": "effective HBM bandwidth of depthwise conv2d forward + input-gradient "
                   "(x+y+W+b and dy+dx+W bytes)",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic, seeded numpy: x, dy ~ N(0,1); W ~ N(0,1/9); b ~ U(-0.1,0.1)",
+        "data": "synthetic, seeded: x, dy ~ N(0,1); W ~ N(0,1/9); b ~ U(-0.1,0.1)",
         "config": {"workload": HEADLINE, "N": wl.N, "H": wl.H, "W": wl.W, "C": wl.C,
-                   "kernel": f"{wl.kH}x{wl.kW}", "stride": wl.stride, "dilation": wl.dilation,
-                   "layout": "nhwc", "weights": "f32"},
+                   "kernel": f"{wl.kH}x{wl.kW}", "layout": "nhwc", "weights": "f32"},
         "fwd_us": round(fwd_avg, 2), "ig_us": round(ig_avg, 2),
-        "fwd_pct_peak": round(100 * wl.fwd_bytes() / fwd_avg / 1e3 / PEAK_HBM_GBS, 1),
-        "ig_pct_peak": round(100 * wl.ig_bytes() / ig_avg / 1e3 / PEAK_HBM_GBS, 1),
         "roofline": roofline,
+        "cpu_baseline": None,
     }
-    # Weight gradient, fused epilogues: timed like the roofline launch (two
-    # events around back-to-back launches alternating between two disjoint
-    # buffer sets, so no launch reads what the previous one left in the
-    # 256 MB Infinity Cache).  The second set for the weight gradient is a
-    # copy of x and dy.
-    x2, dy2 = t["x"].clone(), t["dy"].clone()
-    ws, dW, db, bn = t["ws"], t["dW"], t["db"], t["bn"]
-
-    def amortised(calls, n=40, what=""):
-        """Median per-call time (us) of n back-to-back calls with an event
-        between consecutive calls; a stall of the whole device (seen now and
-        then on this machine, tens of milliseconds, outside any kernel's
-        control) would otherwise dominate a mean, so it is reported apart."""
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        with torch.cuda.stream(stream):
-            for c in calls:
-                c()
-            ev[0].record(stream)
-            for i in range(n):
-                calls[i % len(calls)]()
-                ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
-        med = statistics.median(us)
-        if max(us) > 3 * med:
-            _log(f"[bench] {what}: one call took {max(us):.0f} us (median {med:.1f} us)")
-        return med
-
-    def wgrad_call(xx, gg):
-        return lambda: dw.dwconv2d_weight_grad(xx, gg, dW, db, ws, wl.stride, wl.dilation,
-                                               layout, dw.STRATEGY_AUTO, stream)
-
-    def sgd_call(xx, gg):
-        return lambda: dw.dwconv2d_weight_grad_sgd_ex(xx, gg, t["w_sgd"], t["b_sgd"], 1e-4, ws,
-                                                      None, None, wl.stride, wl.dilation, None,
-                                                      1, layout, dw.STRATEGY_AUTO, stream)
-
-    def fused_call(src, dst):
-        return lambda: dw.dwconv2d_fwd_bn_act_ex(src, t["w"], t["b"], dst, bn, 1e-3,
-                                                 dw.ACT_RELU6, wl.stride, wl.dilation, None, 1,
-                                                 layout, dw.STRATEGY_AUTO, stream)
-
-    def fwd_call(src, dst):
-        return lambda: dw.dwconv2d_fwd(src, t["w"], t["b"], dst, wl.stride, wl.dilation, layout,
-                                       stream)
-
-    wg_us = amortised([wgrad_call(t["x"], t["dy"]), wgrad_call(x2, dy2)], what="wgrad")
-    sgd_us = amortised([sgd_call(t["x"], t["dy"]), sgd_call(x2, dy2)], what="wgrad_sgd")
-    fwd_ref_us = amortised([fwd_call(t["x"], t["y"]), fwd_call(t["dy"], t["dx"])], what="fwd")
-    epi_us = amortised([fused_call(t["x"], t["y"]), fused_call(t["dy"], t["dx"])],
-                       what="fwd_bn_relu6")
-    # practical ceilings in the same run: a device copy of the headline
-    # forward's bytes (256 MiB read + 256 MiB written, alternating two buffer
-    # pairs like the roofline leg) and the smallest launch of this library
-    c_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    with torch.cuda.stream(stream):
-        for src, dst in ((t["x"], t["y"]), (t["dy"], t["dx"])):
-            dst.copy_(src)
-        c_ev[0].record(stream)
-        for i in range(n_rep):
-            if i % 2 == 0:
-                t["y"].copy_(t["x"])
-            else:
-                t["dx"].copy_(t["dy"])
-        c_ev[1].record(stream)
-    torch.cuda.synchronize()
-    copy_us = c_ev[0].elapsed_time(c_ev[1]) * 1e3 / n_rep
-    # the same bytes through torch's elementwise kernel (out = in * 1)
-    with torch.cuda.stream(stream):
-        torch.mul(t["x"], 1.0, out=t["y"])
-        c_ev[0].record(stream)
-        for i in range(n_rep):
-            if i % 2 == 0:
-                torch.mul(t["x"], 1.0, out=t["y"])
-            else:
-                torch.mul(t["dy"], 1.0, out=t["dx"])
-        c_ev[1].record(stream)
-    torch.cuda.synchronize()
-    ew_us = c_ev[0].elapsed_time(c_ev[1]) * 1e3 / n_rep
-    copy_bytes = 2 * t["x"].numel() * 4
-    from depthwise_convolution_amd import workloads as _wls
-    tiny = _wls.WORKLOADS["tiny_16x16x8_3x3"]
-    tt = make_problem(torch, tiny, layout, seed=0)
-    # GPU-side time of the smallest launch: 20 forwards of 16x16x8 captured in
-    # a graph, replayed (the host cost of the Python binding is not in it)
-    g_tiny = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        launch_fwd(dw, tiny, tt, layout, stream)
-    stream.synchronize()
-    with torch.cuda.graph(g_tiny, stream=stream):
-        for _ in range(20):
-            launch_fwd(dw, tiny, tt, layout, stream)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        g_tiny.replay()
-        c_ev[0].record(stream)
-        for _ in range(5):
-            g_tiny.replay()
-        c_ev[1].record(stream)
-    torch.cuda.synchronize()
-    tiny_us = c_ev[0].elapsed_time(c_ev[1]) * 1e3 / 100
-    del g_tiny, tt
-    best_copy_gbs = copy_bytes / min(copy_us, ew_us) / 1e3
-    result["ceilings"] = {
-        "copy_bytes": copy_bytes,
-        "runtime_copy_us": round(copy_us, 2),
-        "runtime_copy_GBs": round(copy_bytes / copy_us / 1e3, 1),
-        "elementwise_copy_us": round(ew_us, 2),
-        "elementwise_copy_GBs": round(copy_bytes / ew_us / 1e3, 1),
-        "headline_frac_of_best_copy": round(result["roofline"]["achieved"] / best_copy_gbs, 3),
-        "tiny_fwd_launch_us_in_graph": round(tiny_us, 2),
-        "timing": "copies: two events around 40 back-to-back copies alternating x->y and "
-                  "dy->dx (256 MiB each way), as the roofline leg times its kernel; the "
-                  "runtime copy is Tensor.copy_ (device-to-device memcpy), the elementwise "
-                  "copy torch.mul(src, 1, out=dst); tiny launch: 20 forwards of 16x16x8 3x3 "
-                  "captured in a HIP graph, replayed 5 times, per launch"}
-    del x2, dy2
-    result["wgrad"] = {
-        "kernel": dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
-                                       wl.stride, wl.dilation, layout)[0],
-        "us": round(wg_us, 2), "algorithmic_bytes": wgrad_bytes(wl),
-        "GBs": round(wgrad_bytes(wl) / wg_us / 1e3, 1),
-        "pct_peak": round(100 * wgrad_bytes(wl) / wg_us / 1e3 / PEAK_HBM_GBS, 1),
-        "timing": "median over 40 back-to-back calls (partial sums + reduction each) with an "
-                  "event between calls, alternating between two copies of x and dy"}
-    result["fused"] = {
-        "timing": "median over 40 back-to-back calls with an event between calls, "
-                  "alternating between two disjoint buffer sets",
-        "fwd_bn_relu6_us": round(epi_us, 2), "fwd_us_same_timing": round(fwd_ref_us, 2),
-        "fwd_bn_relu6_pct_peak": round(100 * fwd_bn_act_bytes(wl) / epi_us / 1e3 /
-                                       PEAK_HBM_GBS, 1),
-        "wgrad_sgd_us": round(sgd_us, 2),
-        "wgrad_sgd_pct_peak": round(100 * wgrad_sgd_bytes(wl) / sgd_us / 1e3 / PEAK_HBM_GBS, 1),
-        "note": "one pass each: the BatchNorm + ReLU6 epilogue is applied in the forward's "
-                "store, the SGD step in the weight-gradient reduction"}
+    detail["headline"] = {"warmup_steps_run": n_warm, "fwd_us_events_each_launch":
+                          round(fwd_avg, 2), "ig_us_events_each_launch": round(ig_avg, 2),
+                          "dominant": dom, "algorithmic_bytes_per_launch": dom_bytes,
+                          "roofline": roofline}
+    _log(f"[bench] headline {json.dumps(result)}")
+    detail["headline_extras"] = headline_extras(torch, dw, wl, t, layout, stream, n_rep)
+    best = max(detail["headline_extras"]["ceilings"]["runtime_copy_GBs"],
+               detail["headline_extras"]["ceilings"]["elementwise_copy_GBs"])
+    detail["headline_extras"]["ceilings"]["headline_frac_of_best_copy"] = round(achieved / best, 3)
     del t
     torch.cuda.empty_cache()
-    result["graph"] = graph_leg(torch, dw)
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    detail["launch_floor"] = launch_floor(torch, stream, flush, sink)
+    del flush
+    detail["graph"] = graph_leg(torch, dw)
+    _log(f"[bench] floor {json.dumps(detail['launch_floor'])} graph {json.dumps(detail['graph'])}")
     if args.calib_copy:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
         # readings calibrate the counters of the kernels above
@@ -584,17 +723,32 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        result["calib_copy_bytes"] = src.numel() * 4
+        detail["calib_copy_bytes"] = src.numel() * 4
         del src, dst
-    if not args.no_cpu:
-        _log("[bench] cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(wl)
-    else:
-        result["cpu_baseline"] = None
+    if cpu is not None:
+        _log("[bench] cpu baseline (oracle timing build)")
+        cb = cpu_baseline(cpu, wl, inp, threads)
+        detail["cpu_baseline"] = cb
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    del inp
     if not args.no_table:
         _log("[bench] per-workload table")
-        result["per_config"] = per_config_table(torch, dw)
+        detail["per_config"] = per_config_table(torch, dw, cpu, threads, only)
+    if cpu is not None:
+        cpu.close()
+    detail["result"] = result
+    _write_detail(args.detail, detail)
     print(json.dumps(result), flush=True)
+
+
+def _write_detail(path, detail):
+    if not path:
+        return
+    d = os.path.dirname(os.path.abspath(path))
+    os.makedirs(d, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(detail, f, indent=1)
+    _log(f"[bench] detail written to {path}")
 
 
 if __name__ == "__main__":

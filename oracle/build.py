@@ -24,5 +24,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_timing(out_dir: str, verbose: bool = False) -> str:
+    """The CPU timing baseline: the same source with single-precision
+    accumulation (-DDWO_ACC_T=float), -O3 -march=native, OpenMP.  Built on
+    the host that runs it (the instruction set follows that CPU), into
+    `out_dir`; not used for parity."""
+    lib = os.path.join(out_dir, "libdwconv_oracle_f32.so")
+    cmd = ["gcc", "-std=c99", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared",
+           "-DDWO_ACC_T=float", "-o", lib, SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -40,13 +40,24 @@
  * values of the products that entered it; callers use it to size the
  * rounding bound 1e-5*S + 1e-6 that a float32 implementation must meet.
  *
- * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/build.py).
+ * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/build.py).  The same
+ * source built with -DDWO_ACC_T=float (oracle/build.py, build_timing) is the
+ * CPU timing baseline: the forward and the input gradient then form each
+ * product and accumulate in single precision, as a float32 implementation
+ * would; every other line is the same.  The parity build accumulates in
+ * double.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+
+#ifndef DWO_ACC_T
+#define DWO_ACC_T double
+#endif
+/* accumulation type of dwo_fwd and dwo_input_grad (double for parity) */
+typedef DWO_ACC_T acc_t;
 
 /* ------------------------------------------------------------------ */
 /* IEEE 754 binary16 -> double, from the format's definition:           */
@@ -112,7 +123,7 @@ int dwo_fwd(const float *x, const void *w, int wtype, const float *b,
         const int n = (int)(nc / C), c = (int)(nc % C);
         for (int ho = 0; ho < Ho; ++ho)
             for (int wo = 0; wo < Wo; ++wo) {
-                double acc = b ? (double)b[c] : 0.0, sabs = 0.0;
+                acc_t acc = b ? (acc_t)b[c] : 0, sabs = 0;
                 for (int kh = 0; kh < kH; ++kh) {
                     const int hi = ho * s + kh * d - pH;
                     if (hi < 0 || hi >= H)
@@ -121,8 +132,8 @@ int dwo_fwd(const float *x, const void *w, int wtype, const float *b,
                         const int wi = wo * s + kw * d - pW;
                         if (wi < 0 || wi >= W)
                             continue;
-                        const double t = (double)x[at(layout, C, H, W, n, c, hi, wi)] *
-                                         wtap(w, wtype, kH, kW, c, kh, kw);
+                        const acc_t t = (acc_t)x[at(layout, C, H, W, n, c, hi, wi)] *
+                                        (acc_t)wtap(w, wtype, kH, kW, c, kh, kw);
                         acc += t;
                         sabs += fabs(t);
                     }
@@ -161,7 +172,7 @@ int dwo_input_grad(const float *dy, const void *w, int wtype,
         const int n = (int)(nc / C), c = (int)(nc % C);
         for (int h = 0; h < H; ++h)
             for (int x_w = 0; x_w < W; ++x_w) {
-                double acc = 0.0, sabs = 0.0;
+                acc_t acc = 0, sabs = 0;
                 for (int kh = 0; kh < kH; ++kh) {
                     const int th = h + kh * d - pH;        /* row on the upsampled grid */
                     if (th < 0 || th >= H || th % s != 0)  /* padding, or an inserted zero */
@@ -170,8 +181,8 @@ int dwo_input_grad(const float *dy, const void *w, int wtype,
                         const int tw = x_w + kw * d - pW;
                         if (tw < 0 || tw >= W || tw % s != 0)
                             continue;
-                        const double t = wtap(w, wtype, kH, kW, c, kH - 1 - kh, kW - 1 - kw) *
-                                         (double)dy[at(layout, C, Ho, Wo, n, c, th / s, tw / s)];
+                        const acc_t t = (acc_t)wtap(w, wtype, kH, kW, c, kH - 1 - kh, kW - 1 - kw) *
+                                        (acc_t)dy[at(layout, C, Ho, Wo, n, c, th / s, tw / s)];
                         acc += t;
                         sabs += fabs(t);
                     }

@@ -23,14 +23,14 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "dwconv_oracle.c")
 # (name, old text, new text, which occurrence (0-based) or None for all)
 MUTANTS = [
     ("fwd_flipped_kernel",
-     "(double)x[at(layout, C, H, W, n, c, hi, wi)] *\n                                         wtap(w, wtype, kH, kW, c, kh, kw)",
-     "(double)x[at(layout, C, H, W, n, c, hi, wi)] *\n                                         wtap(w, wtype, kH, kW, c, kH - 1 - kh, kW - 1 - kw)", 0),
+     "(acc_t)x[at(layout, C, H, W, n, c, hi, wi)] *\n                                        (acc_t)wtap(w, wtype, kH, kW, c, kh, kw)",
+     "(acc_t)x[at(layout, C, H, W, n, c, hi, wi)] *\n                                        (acc_t)wtap(w, wtype, kH, kW, c, kH - 1 - kh, kW - 1 - kw)", 0),
     ("padding_ignores_dilation", "const int pH = d * (kH - 1) / 2, pW = d * (kW - 1) / 2;",
      "const int pH = (kH - 1) / 2, pW = (kW - 1) / 2;", None),
     ("fwd_odd_stride_phase", "const int hi = ho * s + kh * d - pH;",
      "const int hi = ho * s + (s - 1) + kh * d - pH;", 0),
-    ("fwd_drops_bias", "double acc = b ? (double)b[c] : 0.0, sabs = 0.0;",
-     "double acc = 0.0, sabs = 0.0;", 0),
+    ("fwd_drops_bias", "acc_t acc = b ? (acc_t)b[c] : 0, sabs = 0;",
+     "acc_t acc = 0, sabs = 0;", 0),
     ("fwd_drops_last_column_tap", "for (int kw = 0; kw < kW; ++kw) {\n                        const int wi = wo * s + kw * d - pW;",
      "for (int kw = 0; kw < kW - 1; ++kw) {\n                        const int wi = wo * s + kw * d - pW;", 0),
     ("fwd_uses_filter_of_channel_0", "wtap(w, wtype, kH, kW, c, kh, kw);",
