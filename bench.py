@@ -396,6 +396,34 @@ def per_config_table(torch, dw, cpu, threads, only=None):
     return rows
 
 
+def calibration_kernels(torch, dw, workloads, detail, layout, stream):
+    """Kernels of known HBM traffic, whose FETCH_SIZE / WRITE_SIZE counter
+    readings calibrate the counters of the kernels above: a plain 256 MiB
+    device copy, and the 1x1 tiled forward of 512x512x256 (its input read
+    once through the same 16-byte loads into LDS as the 3x3 kernels, its
+    output written once), alternating two buffer sets so neither finds its
+    input in the Infinity Cache."""
+    src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    detail["calib_copy_bytes"] = src.numel() * 4
+    sets = [(torch.randn(1, 512, 512, 256, device="cuda"),
+             torch.empty(1, 512, 512, 256, device="cuda")) for _ in range(2)]
+    w1 = torch.randn(256, 1, 1, device="cuda")
+    b1 = torch.randn(256, device="cuda")
+    detail["calib_1x1_kernel"] = describe(dw, workloads.Workload(
+        name="calib", N=1, H=512, W=512, C=256, kH=1, kW=1), "fwd", layout)
+    for i in range(6):
+        xx, yy = sets[i % 2]
+        dw.dwconv2d_fwd(xx, w1, b1, yy, 1, 1, layout, stream)
+    torch.cuda.synchronize()
+    detail["calib_1x1_bytes"] = {"read": 512 * 512 * 256 * 4 + 256 * 8,
+                                 "written": 512 * 512 * 256 * 4}
+    del src, dst, sets
+
+
 def launch_floor(torch, stream, flush, sink):
     """The smallest launch: an empty kernel (a zero-cycle spin), back to back
     (amortised, queued ahead) and as one call between two events after the
@@ -485,13 +513,137 @@ def headline_extras(torch, dw, wl, t, layout, stream, n_rep=40):
 
 
 # ------------------------------------------------------------------ trace table
+def _match_dispatches(dw, wl, layout, op, by_kernel):
+    """The (kernel name, grid) entries of `by_kernel` (a dict keyed by the
+    trace's kernel name and grid size in threads) that a plan of (workload,
+    layout, op) launches: the kernel family and grid from the describe call,
+    the weight type and the op from the template arguments."""
+    import re
+    opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
+    kname, grid, block = dw.dwconv2d_describe_ex(
+        opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation, wl.pads,
+        wl.mult, layout, 0 if op == "wgrad" else int(wl.fp16_weights), op == "fwd")
+    fam = {"tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
+           "stream_nhwc": "k_stream_nhwc", "stream_nchw": "k_stream_nchw",
+           "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
+           "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc", "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
+           "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_direct": "k_wgrad_gen"}
+    kfam = next((v for k, v in sorted(fam.items(), key=lambda kv: -len(kv[0]))
+                 if kname.startswith(k)), None)
+    out = []
+    for (kn, g), vals in by_kernel.items():
+        m = re.search(r"(k_\w+)<(.*)>", kn)
+        f, args = (m.group(1), m.group(2).replace(" ", "")) if m else (kn, "")
+        if f != kfam or g != grid * block:
+            continue
+        parts = args.split(",")
+        if op != "wgrad":
+            if parts[0] in ("float", "_Float16", "half") and \
+                    (parts[0] != "float") != bool(wl.fp16_weights):
+                continue
+            # the op in the template arguments: the tiled kernels' mode (0
+            # forward, 1 input gradient) third from last, the streaming
+            # kernels' last; the direct kernels' input-gradient flag
+            want = {"fwd": "0", "ig": "1"}[op]
+            if kfam.startswith("k_tiled") and parts[-3] != want:
+                continue
+            if kfam.startswith("k_stream") and parts[-1] != want:
+                continue
+            if kfam.startswith("k_direct"):
+                flags = [q for q in parts if q in ("true", "false")]
+                if flags and flags[0] != ("true" if op == "ig" else "false"):
+                    continue
+        out.append((kn, vals))
+    return kname, out
+
+
+def counter_table(fetch_csv, write_csv, out_path=None):
+    """HBM traffic per workload from two rocprofv3 --pmc runs of `bench.py
+    --table-only --calib-copy` (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch): the counters of the runtime's 256 MiB device copy calibrate
+    them (bytes moved / counter reading), and the 1x1 tiled forward of
+    512x512x256, which reads its input and writes its output exactly once
+    through the same 16-byte loads into LDS as the tiled kernels, checks the
+    calibration.  Per (workload, layout, op): median counter per dispatch,
+    scaled, against the algorithmic bytes.  No GPU needed."""
+    import csv
+    import depthwise_convolution_amd as dw
+    from depthwise_convolution_amd import workloads
+
+    def load(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (r["Kernel_Name"], int(r.get("Grid_Size", "0") or 0))
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    kib = 1024.0
+    copy_bytes = 256 * 1024 * 1024
+
+    # the copy of the calibration leg is the largest copyBuffer dispatch
+    cf = max((statistics.median(v) for (k, g), v in fetch.items() if "copyBuffer" in k),
+             default=None)
+    cw = max((statistics.median(v) for (k, g), v in write.items() if "copyBuffer" in k),
+             default=None)
+    sf = copy_bytes / (cf * kib) if cf else None
+    sw = copy_bytes / (cw * kib) if cw else None
+    one = workloads.Workload(name="calib_1x1", N=1, H=512, W=512, C=256, kH=1, kW=1)
+    lines = [f"Calibration: 256 MiB device copy reads FETCH_SIZE = {cf:.1f} KiB and writes "
+             f"WRITE_SIZE = {cw:.1f} KiB per dispatch: FETCH_SIZE x {sf:.4f}, WRITE_SIZE x "
+             f"{sw:.4f}." if sf and sw else "Calibration: no copy dispatch found."]
+    _, m1 = _match_dispatches(dw, one, workloads.NHWC, "fwd", fetch)
+    _, m1w = _match_dispatches(dw, one, workloads.NHWC, "fwd", write)
+    if m1 and m1w and sf and sw:
+        r1 = statistics.median(m1[0][1]) * kib * sf
+        w1 = statistics.median(m1w[0][1]) * kib * sw
+        lines.append(f"Check: the 1x1 tiled forward of 512x512x256 (reads 268,437,504 B, writes "
+                     f"268,435,456 B) measures {r1:,.0f} B read ({r1 / 268437504:.3f}x) and "
+                     f"{w1:,.0f} B written ({w1 / 268435456:.3f}x) with this calibration.")
+    lines += ["", "| workload | layout | op | kernel | dispatches | read MiB | written MiB | "
+              "HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|"]
+    rows = {}
+    for name, wl in workloads.WORKLOADS.items():
+        if "parity_only" in wl.tags:
+            continue
+        for layout in (0, 1):
+            for op in ("fwd", "ig", "wgrad"):
+                if op == "wgrad" and wl.fp16_weights:
+                    continue
+                kname, mf = _match_dispatches(dw, wl, layout, op, fetch)
+                _, mw = _match_dispatches(dw, wl, layout, op, write)
+                if not mf or not mw or not sf:
+                    continue
+                kf = max(mf, key=lambda c: len(c[1]))
+                kw = max(mw, key=lambda c: len(c[1]))
+                rb = statistics.median(kf[1]) * kib * sf
+                wb = statistics.median(kw[1]) * kib * sw
+                alg = op_bytes(wl, op)
+                rows[(name, workloads.LAYOUT_NAMES[layout], op)] = {
+                    "kernel": kname, "hbm_bytes_per_launch": round(rb + wb),
+                    "read_bytes": round(rb), "written_bytes": round(wb),
+                    "algorithmic_bytes": alg, "ratio": round((rb + wb) / alg, 3)}
+                lines.append(f"| {name} | {workloads.LAYOUT_NAMES[layout]} | {op} | `{kname}` | "
+                             f"{len(kf[1])} | {rb / 2**20:.2f} | {wb / 2**20:.2f} | "
+                             f"{rb + wb:,.0f} | {alg:,} | {(rb + wb) / alg:.3f} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text, rows, (sf, sw)
+
+
 def trace_table(csv_path, out_path=None):
     """Summarise a rocprofv3 kernel-trace CSV of `bench.py --table-only` per
     workload: each (kernel, grid) is matched to the workloads/layouts/ops
     whose plan launches it (the describe call's kernel shape and grid), and
-    the per-dispatch durations give median / mean / min.  No GPU needed."""
+    the per-dispatch durations give median / mean / min (for the weight
+    gradient: its first, partial-sum kernel; the fixed-order reduction that
+    follows is a dispatch of its own, 3-5 us).  No GPU needed."""
     import csv
-    import re
     import depthwise_convolution_amd as dw
     from depthwise_convolution_amd import workloads
     durs = {}
@@ -502,12 +654,6 @@ def trace_table(csv_path, out_path=None):
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             durs.setdefault((name, grid), []).append(d)
 
-    def tmpl(name):
-        m = re.search(r"(k_\w+)<(.*)>", name)
-        return (m.group(1), m.group(2).replace(" ", "")) if m else (name, "")
-
-    # wgrad rows: the first (partial-sum) kernel; the fixed-order reduction
-    # that follows it is a separate dispatch of 3-5 us
     lines = ["| workload | layout | op | kernel | calls | median us | mean us | min us | "
              "floor us (bound) | median frac of floor |", "|---|---|---|---|---|---|---|---|---|---|"]
     for name, wl in workloads.WORKLOADS.items():
@@ -517,41 +663,7 @@ def trace_table(csv_path, out_path=None):
             for op in ("fwd", "ig", "wgrad"):
                 if op == "wgrad" and wl.fp16_weights:
                     continue
-                opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
-                kname, grid, block = dw.dwconv2d_describe_ex(
-                    opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation, wl.pads,
-                    wl.mult, layout, 0 if op == "wgrad" else int(wl.fp16_weights), op == "fwd")
-                fam = {"tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
-                       "stream_nhwc": "k_stream_nhwc",
-                       "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
-                       "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc",
-                       "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
-                       "wgrad_direct": "k_wgrad_gen"}
-                kfam = next((v for k, v in sorted(fam.items(), key=lambda kv: -len(kv[0]))
-                             if kname.startswith(k)), None)
-                cands = []
-                for (kn, g), ds in durs.items():
-                    f, args = tmpl(kn)
-                    if f != kfam or g != grid * block:
-                        continue
-                    parts = args.split(",")
-                    if op != "wgrad" and parts[0] in ("float", "_Float16", "half"):
-                        if (parts[0] != "float") != bool(wl.fp16_weights):
-                            continue
-                    # the op in the template arguments: the tiled kernels' mode
-                    # (0 forward, 1 input gradient) third from last, the
-                    # streaming kernel's last; the direct kernels' input-gradient flag
-                    if op != "wgrad":
-                        want = {"fwd": "0", "ig": "1"}[op]
-                        if kfam.startswith("k_tiled") and parts[-3] != want:
-                            continue
-                        if kfam.startswith("k_stream") and parts[-1] != want:
-                            continue
-                        if kfam.startswith("k_direct"):
-                            flags = [q for q in parts if q in ("true", "false")]
-                            if flags and flags[0] != ("true" if op == "ig" else "false"):
-                                continue
-                    cands.append((kn, ds))
+                kname, cands = _match_dispatches(dw, wl, layout, op, durs)
                 if not cands:
                     continue
                 kn, ds = max(cands, key=lambda c: len(c[1]))
@@ -584,10 +696,25 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     ap.add_argument("--trace-table", default="", help="summarise a kernel-trace CSV and exit")
+    ap.add_argument("--counter-table", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--traffic-json", default="",
+                    help="with --counter-table: also write the headline kernel's traffic file")
     ap.add_argument("--out", default="")
     args = ap.parse_args()
     if args.trace_table:
         print(trace_table(args.trace_table, args.out or None))
+        return
+    if args.counter_table:
+        text, rows, (sf, sw) = counter_table(*args.counter_table, args.out or None)
+        print(text)
+        if args.traffic_json:
+            ops = {op: rows[(HEADLINE, "nhwc", op)] for op in ("fwd", "ig", "wgrad")
+                   if (HEADLINE, "nhwc", op) in rows}
+            with open(args.traffic_json, "w") as f:
+                json.dump({"workload": HEADLINE + " nhwc",
+                           "kernel_source_sha256": kernel_source_digest(),
+                           "fetch_scale": sf, "write_scale": sw, "ops": ops}, f, indent=1)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: there is no multi-GPU path (the operator "
@@ -609,6 +736,8 @@ def main():
     only = [s for s in args.workloads.split(",") if s]
     if args.table_only:
         detail["per_config"] = per_config_table(torch, dw, cpu, threads, only)
+        if args.calib_copy:
+            calibration_kernels(torch, dw, workloads, detail, workloads.NHWC, torch.cuda.Stream())
         _write_detail(args.detail, detail)
         if cpu:
             cpu.close()
@@ -716,15 +845,7 @@ def main():
     detail["graph"] = graph_leg(torch, dw)
     _log(f"[bench] floor {json.dumps(detail['launch_floor'])} graph {json.dumps(detail['graph'])}")
     if args.calib_copy:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
-        # readings calibrate the counters of the kernels above
-        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        detail["calib_copy_bytes"] = src.numel() * 4
-        del src, dst
+        calibration_kernels(torch, dw, workloads, detail, layout, stream)
     if cpu is not None:
         _log("[bench] cpu baseline (oracle timing build)")
         cb = cpu_baseline(cpu, wl, inp, threads)

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdwconv.so")
 HOST_SOURCES = ["dwconv_api.cpp", "dwconv_plan.cpp"]
 HIP_SOURCES = ["dwconv_direct.hip", "dwconv_tiled_nhwc.hip", "dwconv_tiled_nchw.hip",
-               "dwconv_wgrad.hip", "dwconv_launch.hip"]
+               "dwconv_wgrad.hip", "dwconv_launch.hip", "dwconv_stream.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -361,5 +361,11 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
                       const float *b, float *out, hipStream_t st, const EpiArgs &ep);
 int launch_tiled_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
                       const float *b, float *out, hipStream_t st, const EpiArgs &ep);
+int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const void *w,
+                       const float *b, float *out, hipStream_t st, const EpiArgs &ep);
+int launch_stream_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
+                       const float *b, float *out, hipStream_t st, const EpiArgs &ep);
+int launch_wgrad_stream_nchw(const Problem &p, const Plan &pl, const float *x, const float *dy,
+                             float *part, hipStream_t st);
 
 }  // namespace dwconv

@@ -52,6 +52,9 @@ enum Kind {
     KIND_WGRAD_DIRECT = 5, // weight gradient, any layout/stride: lanes along the contiguous axis
     KIND_WGRAD_TILED_NHWC = 6, // weight gradient, NHWC stride 1 or 2: LDS x tiles, strips of row tiles
     KIND_WGRAD_TILED_NCHW = 7, // weight gradient, NCHW stride 1 or 2: LDS x plane rows, dy in registers
+    KIND_STREAM_NHWC = 8,  // stride 1, many taps: rows streamed through registers, phases of D
+    KIND_STREAM_NCHW = 9,  // the same with lanes along plane columns, rows staged per wave
+    KIND_WGRAD_STREAM_NCHW = 10, // weight gradient, NCHW stride 1: the NCHW row walk, tap sums per lane
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
@@ -67,13 +70,22 @@ enum Kind {
 // their channel tile.  The planner takes the first one whose channel tile
 // the problem fills to at least 3/4.
 struct TiledVariant { int kH, kW, d, vec, cl, px, g, lv; };
+// (The 32-channel 3x3 tile takes 2 output rows of 4 staged rows and 2
+// channels per thread: 1x112x112x32 forward 3.42 -> 3.08 us and input
+// gradient 3.38 -> 3.06 us against 1 output row and 4 channels per thread;
+// taller tiles (6-10 staged rows, fewer and longer workgroups) were slower,
+// 3.4-4.5 us.)
 constexpr TiledVariant kTiledVariants[] = {
-    {3, 3, 1, 4, 32, 1, 8, 4},   {3, 3, 1, 4, 16, 1, 6, 4},   {3, 3, 1, 4, 8, 1, 3, 4},
+    {3, 3, 1, 4, 32, 1, 8, 4},   {3, 3, 1, 4, 16, 1, 6, 4},   {3, 3, 1, 2, 16, 1, 4, 4},
     {5, 5, 1, 1, 32, 1, 12, 4},
     {7, 7, 1, 1, 32, 1, 16, 4},
     {7, 7, 2, 2, 16, 1, 20, 4},
     {1, 15, 1, 4, 32, 1, 2, 4},  {1, 15, 1, 4, 16, 1, 2, 4},
     {1, 31, 1, 2, 32, 1, 2, 4},
+    // 1x1 (a per-channel scale and bias): no halo, so its HBM traffic is the
+    // tensors themselves, which calibrates the traffic counters of the
+    // kernels above (the same 16-byte loads straight into LDS)
+    {1, 1, 1, 4, 32, 1, 8, 4},
     // scalar staging (lv = 1): any channel count, e.g. a prime one
     {3, 3, 1, 1, 32, 2, 8, 1},   {5, 5, 1, 1, 32, 1, 12, 1},
     {7, 7, 1, 1, 32, 1, 14, 1},  {7, 7, 2, 1, 32, 1, 28, 1},
@@ -97,6 +109,66 @@ constexpr TiledVariant kTiledM2Variants[] = {
     {5, 5, 1, 4, 8, 1, 10, 4},
 };
 constexpr int kNumTiledM2Variants = sizeof(kTiledM2Variants) / sizeof(kTiledM2Variants[0]);
+
+// Variants of the row-streaming NHWC kernel (stride 1, no multiplier, any
+// channel count and alignment): a wave computes `cl` channels x 64/cl column
+// groups of `px` adjacent output columns x `th` output rows of one dilation
+// phase (the sub-grid of rows and columns D apart), with `nb` input rows in
+// registers.  The AUTO strategy takes a variant when the problem gives at
+// least `minw` waves (smaller problems finish sooner on the tiled kernels'
+// short-lived workgroups).
+// Measured on MI355X (amortised launches, 64x30x19x128 7x7): forward 15.1 ->
+// 9.9 us against the tiled kernel, dilation 2 26.4 -> 9.6 us; 5 rows per
+// wave beat 4, 6 and 10 (d = 1) and 8 beat 5 and 15 (d = 2); 32- and
+// 16-channel lane groups measured 2-40% slower than 64 (a prime channel
+// count included: its 64-channel tiles start mid cache line, and narrower
+// groups touch more lines per load); 4 rows in registers 1-3% slower than 3.
+// At 1x30x19x128 the tiled kernel is faster (7x7: 4.8 against 5.7 us).  For
+// 5x5 and 3x3 windows (HBM-bound) the tiled kernel stays faster
+// (32x56x56x128 5x5: 20.2 against 21.5 us).
+struct StreamVariant { int kH, kW, d, cl, px, th, nb, minw; };
+constexpr StreamVariant kStreamVariants[] = {
+    {7, 7, 1, 64, 5, 5, 3, 1024}, {7, 7, 2, 64, 5, 8, 3, 1024},
+};
+constexpr int kNumStreamVariants = sizeof(kStreamVariants) / sizeof(kStreamVariants[0]);
+
+// Variants of the row-streaming NCHW kernel (stride 1, no multiplier): each
+// lane computes `px` adjacent output columns of one plane for `th` output
+// rows of one dilation phase; a wave stages each input row in `nl` loads of
+// 64 elements (its planes' rows with the column halo) and keeps `nb` rows in
+// registers, so lanes per plane row and planes per wave follow from the
+// plane width at plan time; `minw` as for NHWC.
+// Measured (64x30x19x128): 7x7 forward 19.5 -> 17.5 us, dilation 2 27.2 ->
+// 23.7 us (1x30x19x128 d = 2: 10.9 -> 7.1 us; d = 1 stays tiled there: 7.1
+// against 10.1 us).  Lanes reading their own columns from global memory
+// (no LDS row) measured 29-45 us: 5x the L1 requests per FMA of NHWC.
+struct StreamNchwVariant { int kH, kW, d, px, th, nl, nb, minw; };
+constexpr StreamNchwVariant kStreamNchwVariants[] = {
+    {7, 7, 1, 1, 30, 2, 6, 1024}, {7, 7, 2, 1, 15, 2, 6, 128},
+};
+constexpr int kNumStreamNchwVariants = sizeof(kStreamNchwVariants) / sizeof(kStreamNchwVariants[0]);
+
+// LDS floats of one staged row slot of the row-streaming NCHW kernel (the
+// planes of a wave, each at a bank-spreading pitch).
+constexpr int kStreamNchwSlot = 256;
+
+// Variants of the row-streaming NCHW weight gradient (stride 1, no
+// multiplier): the NCHW walk's lanes and staging (one column per lane), dy
+// rows per unit `th`, `nl` loads per staged x row, `nb` rows in flight;
+// AUTO takes it from `minw` waves.  Measured (both stages, 64x30x19x128):
+// 7x7 31.3 -> 25.6 us against the tiled kernel, 7x7 d2 53.3 -> 38.4 us
+// (1x30x19x128 d2: 16.3 -> 13.2 us; d1 stays tiled there, 13.6 against
+// 16.0 us); half the rows per unit measured 12-40% slower.
+struct WgradStreamVariant { int kH, kW, d, th, nl, nb, minw; };
+constexpr WgradStreamVariant kWgradStreamVariants[] = {
+    {7, 7, 1, 30, 2, 6, 1024}, {7, 7, 2, 15, 2, 6, 128},
+};
+constexpr int kNumWgradStreamVariants =
+    sizeof(kWgradStreamVariants) / sizeof(kWgradStreamVariants[0]);
+
+// Cache policy of the row-streaming kernel's stores (gfx950 buffer-store
+// cache-policy bits: 2 = non-temporal): outputs are written once.
+constexpr int kStreamStoreAux = 2;
 
 // Compile-time variants of the tiled NHWC weight-gradient kernel: workgroup
 // geometry as for the forward (vec, cl, px, g, lv).  A workgroup walks a strip of

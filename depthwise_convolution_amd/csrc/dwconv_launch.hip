@@ -25,6 +25,10 @@ int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w
         return launch_tiled_nhwc(p, pl, in, w, bb, out, stream, ep);
     case KIND_TILED_NCHW:
         return launch_tiled_nchw(p, pl, in, w, bb, out, stream, ep);
+    case KIND_STREAM_NHWC:
+        return launch_stream_nhwc(p, pl, in, w, bb, out, stream, ep);
+    case KIND_STREAM_NCHW:
+        return launch_stream_nchw(p, pl, in, w, bb, out, stream, ep);
     default:
         return DWCONV_ERR_BAD_STRATEGY;
     }

@@ -288,6 +288,119 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     return true;
 }
 
+// Row-streaming NHWC kernel: stride 1, no multiplier, a listed kernel shape.
+// Any channel count and 4-byte alignment (4-byte loads and stores).
+static bool plan_stream_nhwc(const Problem &p, Plan *pl)
+{
+    if (p.layout != DWCONV_LAYOUT_NHWC || p.stride != 1 || p.mult != 1 ||
+        p.op == DWCONV_OP_WEIGHT_GRAD)
+        return false;
+    int best = -1;
+    for (int i = 0; i < kNumStreamVariants; ++i) {
+        const StreamVariant &v = kStreamVariants[i];
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const StreamVariant &v = kStreamVariants[best];
+    // byte offsets within a row (the lane's columns, up to (kW-1)*d past the
+    // row on either side) and row starts within an image are 32-bit
+    const long long cb = 4LL * p.C;
+    if (cb * (std::max(pl->IW, pl->OW) + 2LL * v.d * v.kW + 2LL * v.px * v.d) >= (1LL << 31) ||
+        cb * pl->IH * pl->IW >= (1LL << 31) || cb * pl->OH * pl->OW >= (1LL << 31) ||
+        4LL * p.C * p.kH * p.kW >= (1LL << 31))
+        return false;
+    const int d = v.d;
+    const int ohs = ceil_div(pl->OH, d), ows = ceil_div(pl->OW, d);   // phase sub-grid
+    pl->kind = KIND_STREAM_NHWC;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = v.cl;
+    pl->tw = v.px * (64 / v.cl);                  // output columns of a wave
+    pl->th = v.th;
+    pl->nct = ceil_div(p.C, v.cl);
+    pl->nwt = ceil_div(ows, pl->tw);
+    pl->nst = ceil_div(ohs, v.th);
+    pl->pb = d * d;                               // phases
+    pl->YH = pl->OH;
+    pl->YW = pl->OW;
+    pl->total = (long long)p.N * pl->nst * pl->pb * pl->nwt;      // wave units per channel tile
+    if (pl->total * 4 >= (1LL << 31))
+        return false;
+    pl->grid = pl->nct * ((pl->total + 3) / 4);
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name, "stream_nhwc_s1_k%dx%d_d%d_cl%d_px%d_th%d_%s_%s",
+                  v.kH, v.kW, v.d, v.cl, v.px, v.th, op_tag(p), p.wtype ? "f16w" : "f32w");
+    return true;
+}
+
+// Row-streaming NCHW kernel: stride 1, no multiplier, a listed kernel shape,
+// 4-byte alignment.
+static bool plan_stream_nchw(const Problem &p, Plan *pl)
+{
+    if (p.layout != DWCONV_LAYOUT_NCHW || p.stride != 1 || p.mult != 1 ||
+        p.op == DWCONV_OP_WEIGHT_GRAD)
+        return false;
+    int best = -1;
+    for (int i = 0; i < kNumStreamNchwVariants; ++i) {
+        const StreamNchwVariant &v = kStreamNchwVariants[i];
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const StreamNchwVariant &v = kStreamNchwVariants[best];
+    const long long planes = (long long)p.N * p.C;
+    // byte offsets into the whole tensor are 32-bit (and below the
+    // out-of-range offset)
+    if (4LL * planes * pl->IH * pl->IW >= (1LL << 31) ||
+        4LL * planes * pl->OH * pl->OW >= (1LL << 31) || 4LL * p.C * p.kH * p.kW >= (1LL << 31))
+        return false;
+    const int d = v.d;
+    const int ohs = ceil_div(pl->OH, d), ows = ceil_div(pl->OW, d);   // phase sub-grid
+    int lpr = ceil_div(ows, v.px), ncb = 1;
+    if (lpr > 64) {
+        ncb = ceil_div(lpr, 64);
+        lpr = 64;
+    }
+    // staged columns of a plane row, and their LDS pitch: the next value
+    // congruent to lpr mod 32, so the lanes of a half-wave read distinct
+    // banks; the planes of a wave must fit its loads and its row slot
+    const int pitch = lpr * v.px + v.kW - 1;
+    const int lpitch = pitch + ((lpr - pitch) % 32 + 32) % 32;
+    const int ppw = std::min(std::min(64 / lpr, 64 * v.nl / pitch), kStreamNchwSlot / lpitch);
+    if (ppw < 1)
+        return false;
+    pl->kind = KIND_STREAM_NCHW;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = lpr;
+    pl->pb = ppw;
+    pl->hl = pitch;
+    pl->twl = lpitch;
+    pl->tw = lpr * v.px;
+    pl->th = v.th;
+    pl->nwt = ncb;
+    pl->nst = ceil_div(ohs, v.th);
+    pl->nct = d * d;                              // phases
+    pl->YH = pl->OH;
+    pl->YW = pl->OW;
+    pl->total = (planes + ppw - 1) / ppw * pl->nct * pl->nst * ncb;   // wave units
+    if (pl->total * 4 >= (1LL << 31))
+        return false;
+    pl->grid = (pl->total + 3) / 4;
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name,
+                  "stream_nchw_s1_k%dx%d_d%d_px%d_th%d_nl%d_lpr%d_%s_%s", v.kH, v.kW, v.d, v.px,
+                  v.th, v.nl, lpr, op_tag(p), p.wtype ? "f16w" : "f32w");
+    return true;
+}
+
 static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     // channels of the tensor written: mult*C for the forward, C for the input gradient
@@ -326,13 +439,32 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (st != DWCONV_OK)
         return st;
     if (strategy != DWCONV_STRATEGY_AUTO && strategy != DWCONV_STRATEGY_DIRECT &&
-        strategy != DWCONV_STRATEGY_TILED)
+        strategy != DWCONV_STRATEGY_TILED && strategy != DWCONV_STRATEGY_STREAM)
         return DWCONV_ERR_BAD_STRATEGY;
     std::memset(pl, 0, sizeof *pl);
     set_extents(p, pl);
     if (strategy == DWCONV_STRATEGY_DIRECT) {
         plan_direct(p, ptr_bits, pl);
         return DWCONV_OK;
+    }
+    if (strategy == DWCONV_STRATEGY_STREAM)
+        return (p.layout == DWCONV_LAYOUT_NHWC ? plan_stream_nhwc(p, pl) : plan_stream_nchw(p, pl))
+                   ? DWCONV_OK
+                   : DWCONV_ERR_BAD_STRATEGY;
+    // AUTO: the row-streaming kernel for the windows it has variants for,
+    // when the problem gives enough waves
+    if (strategy == DWCONV_STRATEGY_AUTO) {
+        Plan t = *pl;
+        const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
+        if (nhwc ? plan_stream_nhwc(p, &t) : plan_stream_nchw(p, &t)) {
+            const long long waves = nhwc ? t.nct * t.total : t.total;
+            const int minw = nhwc ? kStreamVariants[t.variant].minw
+                                  : kStreamNchwVariants[t.variant].minw;
+            if (waves >= minw) {
+                *pl = t;
+                return DWCONV_OK;
+            }
+        }
     }
     // Tiled kernels: AUTO takes them when they apply and, for NHWC, when the
     // channel count fills at least half of a channel tile.
@@ -500,6 +632,61 @@ static bool plan_wgrad_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Pla
     return true;
 }
 
+// Row-streaming NCHW weight gradient: stride 1, no multiplier, a listed
+// kernel shape; the NCHW walk's geometry over dy (the forward's output).
+static bool plan_wgrad_stream_nchw(const Problem &p, Plan *pl)
+{
+    if (p.layout != DWCONV_LAYOUT_NCHW || p.stride != 1 || p.mult != 1)
+        return false;
+    int best = -1;
+    for (int i = 0; i < kNumWgradStreamVariants; ++i) {
+        const WgradStreamVariant &v = kWgradStreamVariants[i];
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const WgradStreamVariant &v = kWgradStreamVariants[best];
+    const long long planes = (long long)p.N * p.C;
+    if (4LL * planes * p.H * p.W >= (1LL << 31) || 4LL * planes * p.Ho * p.Wo >= (1LL << 31))
+        return false;
+    const int d = v.d;
+    const int ohs = ceil_div(p.Ho, d), ows = ceil_div(p.Wo, d);
+    int lpr = ows, ncb = 1;
+    if (lpr > 64) {
+        ncb = ceil_div(lpr, 64);
+        lpr = 64;
+    }
+    const int pitch = lpr + v.kW - 1;
+    const int lpitch = pitch + ((lpr - pitch) % 32 + 32) % 32;
+    const int ppw = std::min(std::min(64 / lpr, 64 * v.nl / pitch), kStreamNchwSlot / lpitch);
+    if (ppw < 1)
+        return false;
+    pl->kind = KIND_WGRAD_STREAM_NCHW;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = lpr;
+    pl->pb = ppw;
+    pl->hl = pitch;
+    pl->twl = lpitch;
+    pl->tw = lpr;
+    pl->th = v.th;
+    pl->nwt = ncb;
+    pl->nst = ceil_div(ohs, v.th);
+    pl->nct = d * d;
+    pl->total = (planes + ppw - 1) / ppw * pl->nct * pl->nst * ncb;
+    if (pl->total * 4 >= (1LL << 31))
+        return false;
+    pl->chunks = (long long)p.N * pl->nct * pl->nst * ncb;
+    pl->grid = (pl->total + 3) / 4;
+    pl->block = 256;
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_stream_nchw_s1_k%dx%d_d%d_th%d_nl%d_lpr%d",
+                  v.kH, v.kW, v.d, v.th, v.nl, lpr);
+    return true;
+}
+
 static void plan_wgrad_direct(const Problem &p, Plan *pl)
 {
     // any layout / stride / padding / multiplier: the generic kernel, with
@@ -554,12 +741,23 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (st != DWCONV_OK)
         return st;
     if (strategy != DWCONV_STRATEGY_AUTO && strategy != DWCONV_STRATEGY_DIRECT &&
-        strategy != DWCONV_STRATEGY_TILED)
+        strategy != DWCONV_STRATEGY_TILED && strategy != DWCONV_STRATEGY_STREAM)
         return DWCONV_ERR_BAD_STRATEGY;
     std::memset(pl, 0, sizeof *pl);
     set_extents(p, pl);
     bool tiled = false;
-    if (strategy != DWCONV_STRATEGY_DIRECT) {
+    if (strategy == DWCONV_STRATEGY_STREAM || strategy == DWCONV_STRATEGY_AUTO) {
+        Plan t = *pl;
+        if (plan_wgrad_stream_nchw(p, &t) &&
+            (strategy == DWCONV_STRATEGY_STREAM ||
+             t.total >= kWgradStreamVariants[t.variant].minw)) {
+            *pl = t;
+            tiled = true;
+        } else if (strategy == DWCONV_STRATEGY_STREAM) {
+            return DWCONV_ERR_BAD_STRATEGY;
+        }
+    }
+    if (!tiled && strategy != DWCONV_STRATEGY_DIRECT) {
         Plan t = *pl;
         tiled = p.layout == DWCONV_LAYOUT_NHWC ? plan_wgrad_tiled(p, ptr_bits, &t)
                                                : plan_wgrad_tiled_nchw(p, ptr_bits, &t);

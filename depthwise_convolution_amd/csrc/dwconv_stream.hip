@@ -1,0 +1,684 @@
+// dwconv_stream.hip -- the row-streaming NHWC kernel (stride 1; forward,
+// input gradient, forward with the epilogue) for windows with many taps, and
+// its launcher.
+#include "dwconv_device.h"
+
+namespace dwconv {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Row-streaming NHWC kernel (windows of many taps: the work is the kH*kW
+// FMAs per output, so the design goal is a straight run of FMAs).
+//
+// Every wave is an independent unit: its 64 lanes are CL consecutive
+// channels x 64/CL column groups of PX adjacent output columns, of TH output
+// rows of one image (CL < 64 for channel counts that would leave much of a
+// 64-channel tile empty).  The wave walks
+// the TH + kH - 1 input rows its outputs read, top to bottom.  For each row
+// every lane loads its channel at the PX + kW - 1 columns it needs straight
+// into registers (a wave load reads CL consecutive channels of 64/CL pixels:
+// coalesced runs of 4*CL bytes), NB - 1 rows ahead of the row it computes, and
+// folds the row into kH rolling accumulators per column (the row's taps for
+// each of the kH output rows it touches); after row u, output row
+// u - (kH - 1) is complete and is stored.  No LDS tile and no barrier: the
+// columns a lane needs are its own loads, the rows stream through registers.
+//
+// Zero padding costs nothing: each row is read through a buffer descriptor
+// that covers exactly that image row (no bytes for a row outside the image),
+// and the lane's column offsets are fixed for the whole walk, so a column
+// left of the image (a negative offset) or right of it reads zero in
+// hardware.  Stores go through a descriptor of the output row the same way,
+// so columns and rows past the output and channels past C are dropped.
+//
+// Dilation D > 1 is split into its D*D phases: output rows D*i + ar and
+// columns D*j + ac read only input rows and columns of one phase, D apart,
+// so each phase is a dilation-1 correlation on its sub-grid, and a unit
+// works on one phase: kH rolling accumulators and PX + kW - 1 staged
+// columns, as for D = 1, instead of (kH-1)*D + 1 and PX + (kW-1)*D.
+//
+// Workgroups of 4 waves share a channel tile, whose weights they stage once
+// through LDS (coalesced); each lane then holds its channel's kH*kW taps
+// (reversed for the input gradient) in registers.
+// ---------------------------------------------------------------------------
+struct StreamArgs {
+    int C;                  // channels of both tensors (no multiplier)
+    int IH, IW, OH, OW;     // extents of the tensor read and the tensor written
+    int pH, pW;             // top / left zero padding of the tensor read
+    int nct;                // channel tiles of CL
+    int ncg, nrt, nph;      // column groups per sub-grid row, row tiles, phases (D*D)
+    int upc;                // units per channel tile: N * nrt * nph * ncg
+};
+
+__device__ __forceinline__ int floor_div(int a, int b)
+{
+    return (a >= 0 ? a : a - b + 1) / b;
+}
+
+template <typename WT, int KH, int KW, int D, int CL, int PX, int TH, int NB, int MODE>
+__global__ __launch_bounds__(256) void k_stream_nhwc(const float *__restrict__ in,
+                                                     const void *__restrict__ wv,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ out, StreamArgs a,
+                                                     EpiArgs ep)
+{
+    constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
+    constexpr int KK = KH * KW, G = TH + KH - 1, XW = PX + KW - 1;
+    // NB rows in registers: the one in use and NB - 1 in flight
+    static_assert(NB >= 2, "at least one row in flight");
+    constexpr int NWL = (CL * KK + 255) / 256;
+    static_assert(CL == 16 || CL == 32 || CL == 64, "channels per lane group");
+    __shared__ float wl[NWL * 256];
+    const WT *w = reinterpret_cast<const WT *>(wv);
+    const int ct = blockIdx.x % a.nct;
+    const int lane = threadIdx.x & 63;
+    const int ch = lane % CL, cs = lane / CL;          // channel in the tile, column group
+    // the wave's unit (wave-uniform); a wave past the last unit only helps
+    // stage the weights
+    const int unit = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / a.nct) * 4 +
+                                                    (int)(threadIdx.x >> 6));
+    const bool live = unit < a.upc;
+    const int c0 = ct * CL, c = c0 + ch;
+    const bool cok = c < a.C;
+
+    // 1. the unit: column block (fastest), phase, row tile, image
+    int t = live ? unit : 0;
+    const int cg = t % a.ncg;
+    t /= a.ncg;
+    const int ph = t % a.nph;
+    t /= a.nph;
+    const int rt = t % a.nrt;
+    const int n = t / a.nrt;
+    const int ar = ph / D, ac = ph - (ph / D) * D;
+    // output sub-row i (row D*i + ar) with tap kh reads input row
+    // D*i + ar + D*kh - pH = D*(i + kh + tr) + br, 0 <= br < D
+    const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+    const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
+    const int i0 = rt * TH, j0 = (cg * (64 / CL) + cs) * PX;
+
+    // the lane's byte offsets within a row: staged column k, output column jj
+    int vin[XW], vout[PX];
+#pragma unroll
+    for (int k = 0; k < XW; ++k)
+        vin[k] = cok ? (D * (j0 + tc + k) + bc) * (a.C * 4) + c * 4 : kOutOfRange;
+#pragma unroll
+    for (int jj = 0; jj < PX; ++jj)
+        vout[jj] = cok ? (ac + D * (j0 + jj)) * (a.C * 4) + c * 4 : kOutOfRange;
+    const int row_bytes_in = a.IW * a.C * 4, row_bytes_out = a.OW * a.C * 4;
+    const float *img_in = in + (long long)n * a.IH * a.IW * a.C;
+    float *img_out = out + (long long)n * a.OH * a.OW * a.C;
+
+    float xb[NB][XW];
+    auto load_row = [&](int g, float (&dst)[XW]) {
+        const int ir = D * (i0 + tr + g) + br;
+        const bool ok = live && (unsigned)ir < (unsigned)a.IH;
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(img_in + (ok ? ir : 0) * a.IW * a.C, ok ? row_bytes_in : 0);
+#pragma unroll
+        for (int k = 0; k < XW; ++k)
+            dst[k] = buf_f32(r, vin[k]);
+    };
+    // the first rows are on their way while the weights are staged
+#pragma unroll
+    for (int g = 0; g < NB - 1; ++g)
+        load_row(g, xb[g]);
+
+    // 2. the channel tile's weights (CL * KK contiguous values; channels
+    // past C read as zero) into LDS, then into registers
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    float wst[NWL];
+#pragma unroll
+    for (int i = 0; i < NWL; ++i)
+        wst[i] = buf_w(rw, c0 * KK + (int)threadIdx.x + i * 256, (WT *)nullptr);
+    const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), cok ? c * 4 : kOutOfRange)
+                                   : 0.0f;
+    EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
+    if constexpr (EPI)
+        ec = epi_load(ep, cok ? c : a.C, a.C);
+#pragma unroll
+    for (int i = 0; i < NWL; ++i)
+        wl[threadIdx.x + i * 256] = wst[i];
+    __syncthreads();
+    if (!live)
+        return;                                       // a whole wave; no barrier follows
+    float wr[KH][KW];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+            wr[kh][kw] = wl[ch * KK + (IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw)];
+    if constexpr (EPI)
+        epi_finish(ec, ep);
+
+    // 3. walk the rows
+    float acc[KH][PX];
+#pragma unroll
+    for (int r = 0; r < KH; ++r)
+#pragma unroll
+        for (int jj = 0; jj < PX; ++jj)
+            acc[r][jj] = bv;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        if (u + NB - 1 < G)
+            load_row(u + NB - 1, xb[(u + NB - 1) % NB]);
+        const float(&x)[XW] = xb[u % NB];
+        // rows outside the image hold zeros: skip their FMAs (uniform branch)
+        const int ir = D * (i0 + tr + u) + br;
+        if ((unsigned)ir < (unsigned)a.IH) {
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh;                 // output row this tap row feeds
+                if (m >= 0 && m < TH) {
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                        for (int jj = 0; jj < PX; ++jj)
+                            acc[m % KH][jj] = fmaf(wr[kh][kw], x[jj + kw], acc[m % KH][jj]);
+                }
+            }
+        }
+        const int m = u - (KH - 1);                   // output row completed by row u
+        if (m >= 0) {
+            float (&v)[PX] = acc[m % KH];
+            if constexpr (EPI) {
+                const EpiChan e1[1] = {ec};
+                epi_block(v, e1, ep.act);
+            }
+            const int oh = ar + D * (i0 + m);
+            const bool ok = oh < a.OH;
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(img_out + (ok ? oh : 0) * a.OW * a.C, ok ? row_bytes_out : 0);
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[jj]), ro,
+                                                      vout[jj], 0, kStreamStoreAux);
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                v[jj] = bv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-streaming NCHW kernel: the same walk with lanes along the columns of
+// plane rows.  A wave holds PPW planes x LPR lanes per plane row, each lane
+// PX adjacent output columns of its plane (narrow planes are packed several
+// to a wave; lanes past PPW*LPR idle).  The columns a lane needs overlap its
+// neighbours', so each input row is staged once per wave: NL coalesced
+// loads of 64 consecutive staged elements (PPW plane rows of LPR*PX +
+// kW - 1 columns, columns outside the plane read as zero through an
+// out-of-range offset) go into a ring of three row slots in the wave's own
+// LDS, and each lane reads its PX + kW - 1 taps from there.  A row is
+// loaded into registers several rows ahead (a staged row costs a lane only
+// NL registers) and written to one of two LDS slots just before it is read.
+// The slots are private to the wave and the wave's LDS operations run in
+// order, so no barrier is needed.  A row's
+// offset is the wave-uniform soffset of the loads, and a row outside the
+// planes reads through a descriptor of no bytes.  A lane's weights are its
+// channel's (a wave touches PPW channels: a few cache lines per load).
+// Dilation is split into phases as in NHWC: the staged columns are one
+// phase's, D apart.
+// ---------------------------------------------------------------------------
+struct StreamNchwArgs {
+    int C, planes;          // channels; planes (n, c) of both tensors
+    int IH, IW, OH, OW;     // plane extents of the tensor read and the tensor written
+    int pH, pW;             // top / left zero padding of the tensor read
+    int lpr, ppw, pitch;    // lanes per plane row, planes per wave, staged columns per plane
+    int lpitch;             // LDS floats per staged plane row (pitch rounded up to lpr mod 32)
+    int ncb, nrt, nph;      // column blocks (waves across a sub-grid row), row tiles, phases
+    int units;              // waves: plane groups * phases * row tiles * column blocks
+};
+
+__device__ __forceinline__ float buf_f32_s(__amdgpu_buffer_rsrc_t r, int off, int soff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
+
+template <typename WT, int KH, int KW, int D, int PX, int TH, int NL, int NB, int MODE>
+__global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ in,
+                                                     const void *__restrict__ wv,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ out, StreamNchwArgs a,
+                                                     EpiArgs ep)
+{
+    constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
+    constexpr int KK = KH * KW, G = TH + KH - 1, XW = PX + KW - 1;
+    // NB rows in registers (NL values per lane each: the one being written to
+    // LDS and NB - 1 in flight), two LDS slots used in turn
+    static_assert(NB >= 2, "at least one row in flight");
+    // a row slot: up to kStreamNchwSlot floats of staged plane rows, then a
+    // 64-float area the staging lanes past the last plane write to
+    constexpr int SLOT = kStreamNchwSlot + 64;
+    __shared__ float ring[4][2][SLOT];
+    const WT *w = reinterpret_cast<const WT *>(wv);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int unit = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + wave);
+    if (unit >= a.units)
+        return;                                       // a whole wave; this kernel has no barrier
+    // the unit: column block (fastest), row tile, phase, plane group
+    int t = unit;
+    const int cb = t % a.ncb;
+    t /= a.ncb;
+    const int rt = t % a.nrt;
+    t /= a.nrt;
+    const int ph = t % a.nph;
+    const int pg = t / a.nph;
+    const int ar = ph / D, ac = ph - (ph / D) * D;
+    const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+    const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
+    const int i0 = rt * TH, jb = cb * a.lpr * PX;    // first sub-column of the column block
+
+    // staging: element e = i*64 + lane of a row is column k = e % pitch of
+    // plane slot e / pitch, sub-grid column jb + tc + k; it goes to LDS float
+    // (e / pitch) * lpitch + k of the row's slot.  With lpitch = lpr (mod 32)
+    // the float a lane reads (plane slot ps, column cgl*PX + k) sits at
+    // lane + k (mod 32) for PX = 1: the 32 lanes of a half-wave read 32
+    // different banks.
+    int src[NL], dst[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = i * 64 + lane, pse = e / a.pitch, k = e - pse * a.pitch;
+        const int plane = pg * a.ppw + pse, col = D * (jb + tc + k) + bc;
+        const bool ok = pse < a.ppw && plane < a.planes && (unsigned)col < (unsigned)a.IW;
+        src[i] = ok ? (plane * a.IH * a.IW + col) * 4 : kOutOfRange;
+        dst[i] = pse < a.ppw ? pse * a.lpitch + k : kStreamNchwSlot + lane;
+    }
+    const int in_bytes = a.planes * a.IH * a.IW * 4, out_bytes = a.planes * a.OH * a.OW * 4;
+    float (*slots)[SLOT] = ring[wave];
+    float st[NB][NL];                                 // a staged row between load and LDS write
+    auto load_row = [&](int g, float (&dst)[NL]) {
+        const int ir = D * (i0 + tr + g) + br;
+        const bool ok = (unsigned)ir < (unsigned)a.IH;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(in, ok ? in_bytes : 0);
+        const int soff = ok ? ir * a.IW * 4 : 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            dst[i] = buf_f32_s(r, src[i], soff);
+    };
+#pragma unroll
+    for (int g = 0; g < NB - 1; ++g)
+        load_row(g, st[g]);
+
+    // the lane's plane and columns
+    const int ps = lane / a.lpr, cgl = lane - ps * a.lpr;
+    const int plane = pg * a.ppw + ps;
+    const bool pok = ps < a.ppw && plane < a.planes;
+    const int c = pok ? plane % a.C : 0;
+    const int rd = min(ps, a.ppw - 1) * a.lpitch + cgl * PX;   // the lane's first staged column
+    int vout[PX];
+#pragma unroll
+    for (int jj = 0; jj < PX; ++jj) {
+        const int oc = ac + D * (jb + cgl * PX + jj);
+        vout[jj] = pok && oc < a.OW ? (plane * a.OH * a.OW + oc) * 4 : kOutOfRange;
+    }
+    // weights (reversed taps for the input gradient) and bias of the lane's channel
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    float wr[KH][KW];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+            const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
+            wr[kh][kw] = buf_w(rw, pok ? c * KK + tap : kOutOfRange / 4, (WT *)nullptr);
+        }
+    const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
+                                   : 0.0f;
+    EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
+    if constexpr (EPI) {
+        ec = epi_load(ep, pok ? c : a.C, a.C);
+        epi_finish(ec, ep);
+    }
+    float acc[KH][PX];
+#pragma unroll
+    for (int r = 0; r < KH; ++r)
+#pragma unroll
+        for (int jj = 0; jj < PX; ++jj)
+            acc[r][jj] = bv;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        // row u into its slot, row u + 2 on its way
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            slots[u % 2][dst[i]] = st[u % NB][i];
+        if (u + NB - 1 < G)
+            load_row(u + NB - 1, st[(u + NB - 1) % NB]);
+        const int ir = D * (i0 + tr + u) + br;
+        if ((unsigned)ir < (unsigned)a.IH) {
+            float x[XW];
+#pragma unroll
+            for (int k = 0; k < XW; ++k)
+                x[k] = slots[u % 2][rd + k];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh;
+                if (m >= 0 && m < TH) {
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                        for (int jj = 0; jj < PX; ++jj)
+                            acc[m % KH][jj] = fmaf(wr[kh][kw], x[jj + kw], acc[m % KH][jj]);
+                }
+            }
+        }
+        const int m = u - (KH - 1);
+        if (m >= 0) {
+            float (&v)[PX] = acc[m % KH];
+            if constexpr (EPI) {
+                const EpiChan e1[1] = {ec};
+                epi_block(v, e1, ep.act);
+            }
+            const int oh = ar + D * (i0 + m);
+            const bool ok = oh < a.OH;
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, ok ? out_bytes : 0);
+            const int soff = ok ? oh * a.OW * 4 : 0;
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[jj]), ro,
+                                                      vout[jj], soff, kStreamStoreAux);
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                v[jj] = bv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-streaming NCHW weight gradient (stage 1): the lanes and the staged x
+// rows of the NCHW walk above, with the roles of the operands changed
+// (LeanMlir "Depthwise" weight-VJP: dW[c,kh,kw] is the sum over positions
+// of x at the tap times dy).  A lane (one column of one plane, of one
+// dilation phase) keeps its last kH dy values in registers; each x row u
+// read from LDS meets dy rows u - kh, kh < kH, and is added into the lane's
+// kH*kW tap sums (and dy into the bias sum).  At the end the LPR lanes of
+// each plane are added in a fixed tree order through lane permutes, and one
+// lane per plane writes the plane's KK + 1 sums as a chunk of the partial
+// sums part[chunk][c][tap], chunk = the unit's (image, phase, row tile,
+// column block); the fixed-order reduction kernel adds the chunks.
+// ---------------------------------------------------------------------------
+template <int KH, int KW, int D, int TH, int NL, int NB>
+__global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restrict__ x,
+                                                           const float *__restrict__ dy,
+                                                           float *__restrict__ part,
+                                                           StreamNchwArgs a)
+{
+    constexpr int KK = KH * KW, G = TH + KH - 1, XW = KW;     // one column per lane
+    constexpr int RG = KH + NB - 1;                            // dy values in registers
+    constexpr int SLOT = kStreamNchwSlot + 64;
+    static_assert(NB >= 2, "at least one row in flight");
+    __shared__ float ring[4][2][SLOT];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int unit = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + wave);
+    if (unit >= a.units)
+        return;                                       // a whole wave; this kernel has no barrier
+    int t = unit;
+    const int cb = t % a.ncb;
+    t /= a.ncb;
+    const int rt = t % a.nrt;
+    t /= a.nrt;
+    const int ph = t % a.nph;
+    const int pg = t / a.nph;
+    const int ar = ph / D, ac = ph - (ph / D) * D;
+    const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+    const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
+    const int i0 = rt * TH, jb = cb * a.lpr;
+
+    // x staging as in the NCHW walk (element e of a row -> plane slot e / pitch,
+    // column e % pitch; LDS at a bank-spreading pitch)
+    int src[NL], dst[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = i * 64 + lane, pse = e / a.pitch, k = e - pse * a.pitch;
+        const int plane = pg * a.ppw + pse, col = D * (jb + tc + k) + bc;
+        const bool ok = pse < a.ppw && plane < a.planes && (unsigned)col < (unsigned)a.IW;
+        src[i] = ok ? (plane * a.IH * a.IW + col) * 4 : kOutOfRange;
+        dst[i] = pse < a.ppw ? pse * a.lpitch + k : kStreamNchwSlot + lane;
+    }
+    const int x_bytes = a.planes * a.IH * a.IW * 4, dy_bytes = a.planes * a.OH * a.OW * 4;
+    float (*slots)[SLOT] = ring[wave];
+    float st[NB][NL];
+    auto load_x = [&](int g, float (&d)[NL]) {
+        const int ir = D * (i0 + tr + g) + br;
+        const bool ok = (unsigned)ir < (unsigned)a.IH;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(x, ok ? x_bytes : 0);
+        const int soff = ok ? ir * a.IW * 4 : 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            d[i] = buf_f32_s(r, src[i], soff);
+    };
+    // the lane's plane, its dy column, and its dy values (row m in gv[m % RG])
+    const int ps = lane / a.lpr, cgl = lane - ps * a.lpr;
+    const int plane = pg * a.ppw + ps;
+    const bool pok = ps < a.ppw && plane < a.planes;
+    const int rd = min(ps, a.ppw - 1) * a.lpitch + cgl;
+    const int oc = ac + D * (jb + cgl);
+    const int vg = pok && oc < a.OW ? (plane * a.OH * a.OW + oc) * 4 : kOutOfRange;
+    float gv[RG];
+    auto load_dy = [&](int m) {
+        const int oh = ar + D * (i0 + m);
+        const bool ok = m < TH && oh < a.OH;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(dy, ok ? dy_bytes : 0);
+        gv[m % RG] = buf_f32_s(r, vg, ok ? oh * a.OW * 4 : 0);
+    };
+#pragma unroll
+    for (int g = 0; g < NB - 1; ++g) {
+        load_x(g, st[g]);
+        load_dy(g);
+    }
+    float acc[KK + 1];
+#pragma unroll
+    for (int q = 0; q <= KK; ++q)
+        acc[q] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            slots[u % 2][dst[i]] = st[u % NB][i];
+        if (u + NB - 1 < G) {
+            load_x(u + NB - 1, st[(u + NB - 1) % NB]);
+            if (u + NB - 1 < TH)
+                load_dy(u + NB - 1);
+        }
+        if (u < TH)
+            acc[KK] += gv[u % RG];                    // the bias sum
+        const int ir = D * (i0 + tr + u) + br;
+        if ((unsigned)ir < (unsigned)a.IH) {
+            float xv[XW];
+#pragma unroll
+            for (int k = 0; k < XW; ++k)
+                xv[k] = slots[u % 2][rd + k];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh;                 // dy row this x row meets at tap row kh
+                if (m >= 0 && m < TH) {
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw)
+                        acc[kh * KW + kw] = fmaf(xv[kw], gv[m % RG], acc[kh * KW + kw]);
+                }
+            }
+        }
+    }
+    // add the lpr lanes of each plane (a fixed tree over lane offsets 32 .. 1,
+    // within the plane's lanes), then the plane's first lane writes its chunk
+    const bool keep[6] = {cgl + 32 < a.lpr, cgl + 16 < a.lpr, cgl + 8 < a.lpr,
+                          cgl + 4 < a.lpr, cgl + 2 < a.lpr, cgl + 1 < a.lpr};
+#pragma unroll
+    for (int q = 0; q <= KK; ++q) {
+        float v = acc[q];
+#pragma unroll
+        for (int st2 = 0; st2 < 6; ++st2) {
+            const int off = 32 >> st2;
+            const float o = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(((lane + off) & 63) * 4,
+                                                    __builtin_bit_cast(int, v)));
+            v = keep[st2] ? v + o : v;
+        }
+        acc[q] = v;
+    }
+    if (pok && cgl == 0) {
+        const int n = plane / a.C, c = plane - n * a.C;
+        const int chunk = ((n * a.nph + ph) * a.nrt + rt) * a.ncb + cb;
+        float *dstp = part + ((long long)chunk * a.C + c) * (KK + 1);
+#pragma unroll
+        for (int q = 0; q <= KK; ++q)
+            dstp[q] = acc[q];
+    }
+}
+
+typedef void (*WgradStreamFn)(const float *, const float *, float *, StreamNchwArgs);
+
+template <int... Vs>
+void fill_wgrad_stream(WgradStreamFn (&fn)[kNumWgradStreamVariants],
+                       std::integer_sequence<int, Vs...>)
+{
+    ((fn[Vs] = &k_wgrad_stream_nchw<kWgradStreamVariants[Vs].kH, kWgradStreamVariants[Vs].kW,
+                                    kWgradStreamVariants[Vs].d, kWgradStreamVariants[Vs].th,
+                                    kWgradStreamVariants[Vs].nl, kWgradStreamVariants[Vs].nb>),
+     ...);
+}
+
+struct WgradStreamTable {
+    WgradStreamFn fn[kNumWgradStreamVariants];
+    WgradStreamTable()
+    {
+        fill_wgrad_stream(fn, std::make_integer_sequence<int, kNumWgradStreamVariants>());
+    }
+};
+
+typedef void (*StreamNchwFn)(const float *, const void *, const float *, float *,
+                             StreamNchwArgs, EpiArgs);
+
+template <typename WT, int V, int MODE>
+constexpr StreamNchwFn stream_nchw_fn()
+{
+    constexpr StreamNchwVariant t = kStreamNchwVariants[V];
+    return &k_stream_nchw<WT, t.kH, t.kW, t.d, t.px, t.th, t.nl, t.nb, MODE>;
+}
+
+template <int V>
+void fill_stream_nchw(StreamNchwFn (&row)[2][3])
+{
+    row[0][0] = stream_nchw_fn<float, V, kModeFwd>();
+    row[0][1] = stream_nchw_fn<float, V, kModeInputGrad>();
+    row[0][2] = stream_nchw_fn<float, V, kModeFwdEpilogue>();
+    row[1][0] = stream_nchw_fn<half_t, V, kModeFwd>();
+    row[1][1] = stream_nchw_fn<half_t, V, kModeInputGrad>();
+    row[1][2] = stream_nchw_fn<half_t, V, kModeFwdEpilogue>();
+}
+
+template <int... Vs>
+void fill_all_stream_nchw(StreamNchwFn (&fn)[kNumStreamNchwVariants][2][3],
+                          std::integer_sequence<int, Vs...>)
+{
+    (fill_stream_nchw<Vs>(fn[Vs]), ...);
+}
+
+struct StreamNchwTable {
+    StreamNchwFn fn[kNumStreamNchwVariants][2][3];
+    StreamNchwTable()
+    {
+        fill_all_stream_nchw(fn, std::make_integer_sequence<int, kNumStreamNchwVariants>());
+    }
+};
+
+typedef void (*StreamFn)(const float *, const void *, const float *, float *, StreamArgs,
+                         EpiArgs);
+
+template <typename WT, int V, int MODE>
+constexpr StreamFn stream_fn()
+{
+    constexpr StreamVariant t = kStreamVariants[V];
+    return &k_stream_nhwc<WT, t.kH, t.kW, t.d, t.cl, t.px, t.th, t.nb, MODE>;
+}
+
+template <int V>
+void fill_stream(StreamFn (&row)[2][3])
+{
+    row[0][0] = stream_fn<float, V, kModeFwd>();
+    row[0][1] = stream_fn<float, V, kModeInputGrad>();
+    row[0][2] = stream_fn<float, V, kModeFwdEpilogue>();
+    row[1][0] = stream_fn<half_t, V, kModeFwd>();
+    row[1][1] = stream_fn<half_t, V, kModeInputGrad>();
+    row[1][2] = stream_fn<half_t, V, kModeFwdEpilogue>();
+}
+
+template <int... Vs>
+void fill_all_stream(StreamFn (&fn)[kNumStreamVariants][2][3], std::integer_sequence<int, Vs...>)
+{
+    (fill_stream<Vs>(fn[Vs]), ...);
+}
+
+struct StreamTable {
+    StreamFn fn[kNumStreamVariants][2][3];
+    StreamTable()
+    {
+        fill_all_stream(fn, std::make_integer_sequence<int, kNumStreamVariants>());
+    }
+};
+
+}  // namespace
+
+int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const void *w,
+                       const float *b, float *out, hipStream_t st, const EpiArgs &ep)
+{
+    static const StreamTable table;
+    if (p.mult != 1 || p.stride != 1 || pl.variant < 0 || pl.variant >= kNumStreamVariants)
+        return DWCONV_ERR_BAD_STRATEGY;
+    StreamFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    StreamArgs a;
+    a.C = p.C;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.pH = pl.pH; a.pW = pl.pW;
+    a.nct = pl.nct; a.ncg = pl.nwt; a.nrt = pl.nst; a.nph = pl.pb;
+    a.upc = (int)pl.total;
+    return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
+                         p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
+}
+
+int launch_stream_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
+                       const float *b, float *out, hipStream_t st, const EpiArgs &ep)
+{
+    static const StreamNchwTable table;
+    if (p.mult != 1 || p.stride != 1 || pl.variant < 0 || pl.variant >= kNumStreamNchwVariants)
+        return DWCONV_ERR_BAD_STRATEGY;
+    const StreamNchwVariant &v = kStreamNchwVariants[pl.variant];
+    if (pl.pb < 1 || pl.cl < 1 || pl.pb * pl.cl > 64 || pl.pb * pl.hl > 64 * v.nl ||
+        pl.pb * pl.twl > kStreamNchwSlot || pl.twl < pl.hl)
+        return DWCONV_ERR_BAD_STRATEGY;      // the staged row must fit the wave's slot
+    StreamNchwFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    StreamNchwArgs a;
+    a.C = p.C;
+    a.planes = p.N * p.C;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.pH = pl.pH; a.pW = pl.pW;
+    a.lpr = pl.cl; a.ppw = pl.pb; a.pitch = pl.hl; a.lpitch = pl.twl;
+    a.ncb = pl.nwt; a.nrt = pl.nst; a.nph = pl.nct;
+    a.units = (int)pl.total;
+    return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
+                         p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
+}
+
+int launch_wgrad_stream_nchw(const Problem &p, const Plan &pl, const float *x, const float *dy,
+                             float *part, hipStream_t st)
+{
+    static const WgradStreamTable table;
+    if (p.mult != 1 || p.stride != 1 || pl.variant < 0 || pl.variant >= kNumWgradStreamVariants)
+        return DWCONV_ERR_BAD_STRATEGY;
+    const WgradStreamVariant &v = kWgradStreamVariants[pl.variant];
+    if (pl.pb < 1 || pl.cl < 1 || pl.pb * pl.cl > 64 || pl.pb * pl.hl > 64 * v.nl ||
+        pl.pb * pl.twl > kStreamNchwSlot || pl.twl < pl.hl)
+        return DWCONV_ERR_BAD_STRATEGY;      // the staged row must fit the wave's slot
+    StreamNchwArgs a;
+    a.C = p.C;
+    a.planes = p.N * p.C;
+    a.IH = p.H; a.IW = p.W; a.OH = p.Ho; a.OW = p.Wo;
+    a.pH = pl.pH; a.pW = pl.pW;
+    a.lpr = pl.cl; a.ppw = pl.pb; a.pitch = pl.hl; a.lpitch = pl.twl;
+    a.ncb = pl.nwt; a.nrt = pl.nst; a.nph = pl.nct;
+    a.units = (int)pl.total;
+    return launch_kernel(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy,
+                         part, a);
+}
+
+}  // namespace dwconv

@@ -774,6 +774,8 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
         g.xcd = pl.xcd;
         st1 = launch_kernel(p.stride == 1 ? table.fn[pl.variant] : table.fn2[pl.variant],
                             dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, x, dy, part, g);
+    } else if (pl.kind == KIND_WGRAD_STREAM_NCHW) {
+        st1 = launch_wgrad_stream_nchw(p, pl, x, dy, part, st);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
         WgradGenArgs g;
         g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;

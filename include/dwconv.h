@@ -100,6 +100,14 @@ extern "C" {
 #define DWCONV_STRATEGY_TILED  2 /* LDS-staged input rows with halo, register-blocked
                                     output rows; applies where a tiled kernel exists
                                     for the (layout, stride, kernel, dilation)    */
+#define DWCONV_STRATEGY_STREAM 3 /* each wave walks its rows with the input streamed
+                                    through registers (NHWC: lanes along 64 channels;
+                                    NCHW: lanes along plane columns, each row staged
+                                    once per wave), dilation split into its phases;
+                                    applies at stride 1 without a multiplier to the
+                                    forward and input gradient (both layouts) and the
+                                    NCHW weight gradient, for the kernel shapes it has
+                                    variants for (7x7, dilation 1 or 2)            */
 
 /*
  * Forward.  x: input [N,H,W,C] / [N,C,H,W] float32.  w: [C][kH][kW] of type
@@ -155,8 +163,8 @@ int dwconv2d_describe(int op, int wtype, int has_bias, int N, int H, int W, int 
  * `workspace`, a caller-owned device buffer of at least the size that
  * dwconv2d_weight_grad_workspace_size reports for the same arguments
  * (16-byte aligned; its contents on entry do not matter), and a second
- * kernel adds them up.  strategy: DWCONV_STRATEGY_AUTO / DIRECT / TILED as
- * for dwconv2d_launch.  Errors as above, plus DWCONV_ERR_WORKSPACE when the
+ * kernel adds them up.  strategy: DWCONV_STRATEGY_AUTO / DIRECT / TILED /
+ * STREAM as for dwconv2d_launch.  Errors as above, plus DWCONV_ERR_WORKSPACE when the
  * workspace is NULL, misaligned or too small.
  */
 int dwconv2d_weight_grad_workspace_size(int N, int H, int W, int C, int kH, int kW,

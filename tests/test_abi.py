@@ -162,7 +162,8 @@ def test_tiled_grid_covers_problem(wl_name):
     from depthwise_convolution_amd.workloads import WORKLOADS
     wl = WORKLOADS[wl_name]
     name, grid, block = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
-                                             wl.stride, wl.dilation)
+                                             wl.stride, wl.dilation,
+                                             strategy=dw.STRATEGY_TILED)
     assert name.startswith("tiled_nhwc") and block == 256
     vec = int(re.search(r"_v(\d+)_", name).group(1))
     cl = int(re.search(r"_cl(\d+)_", name).group(1))
@@ -173,6 +174,42 @@ def test_tiled_grid_covers_problem(wl_name):
     assert th >= 1 and (cg % 4 == 0 or "_l1_" in name)
     nct, nwt, nst = -(-wl.C // cg), -(-wl.W // tw), -(-wl.H // th)
     assert grid == wl.N * nct * nwt * nst
+
+
+@pytest.mark.parametrize("wl_name", ["asr_n64_30x19x128_7x7", "asr_n64_30x19x128_7x7_d2",
+                                     "prime_n64_30x19x131_7x7", "asr_n1_30x19x128_7x7"])
+def test_stream_grid_covers_problem(wl_name):
+    """The row-streaming grid: per channel tile, one wave per (image, row
+    tile, dilation phase, column block) of the phase sub-grid (rows and
+    columns d apart), four waves per workgroup; AUTO takes it only with at
+    least 1024 waves."""
+    from depthwise_convolution_amd.workloads import WORKLOADS
+    wl = WORKLOADS[wl_name]
+    name, grid, block = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                             wl.stride, wl.dilation,
+                                             strategy=dw.STRATEGY_STREAM)
+    assert name.startswith("stream_nhwc") and block == 256
+    d = wl.dilation
+    cl = int(re.search(r"_cl(\d+)_", name).group(1))
+    px = int(re.search(r"_px(\d+)_", name).group(1))
+    th = int(re.search(r"_th(\d+)_", name).group(1))
+    hs, ws = -(-wl.H // d), -(-wl.W // d)
+    units = wl.N * -(-hs // th) * d * d * -(-ws // (px * 64 // cl))
+    nct = -(-wl.C // cl)
+    assert grid == nct * -(-units // 4)
+    auto = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
+                                wl.dilation)[0]
+    assert auto.startswith("stream_") == (nct * units >= 1024)
+    # NCHW: lanes along plane columns, planes packed per wave
+    name, grid, _ = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
+                                         wl.stride, wl.dilation, dw.NCHW,
+                                         strategy=dw.STRATEGY_STREAM)
+    px = int(re.search(r"_px(\d+)_", name).group(1))
+    th = int(re.search(r"_th(\d+)_", name).group(1))
+    lpr = int(re.search(r"_lpr(\d+)_", name).group(1))
+    assert lpr == min(64, -(-ws // px))
+    ppw = (grid * 4) // (d * d * -(-hs // th) * -(-ws // (64 * px)))
+    assert 1 <= -(-wl.N * wl.C // max(1, 64 // lpr)) <= grid * 4
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -442,21 +479,30 @@ def test_plans_for_tensors_off_16_byte_alignment(off):
     (a contiguous view at a storage offset of 1-3 floats) gets kernels that use
     no 16-byte access: 4-byte staging (`_l1`, `_v1`) or 1-channel direct
     kernels; at a multiple of 16 the plan is the aligned one."""
-    def name(op, layout, C, k, addr, s=1, d=1, H=56, W=56, mult=1, bias=False):
+    def name(op, layout, C, k, addr, s=1, d=1, H=56, W=56, mult=1, bias=False,
+             st=dw.STRATEGY_AUTO):
         return dw.dwconv2d_describe_addr_ex(op, 2, H, W, C, k, k, stride=s, dilation=d,
                                             mult=mult, layout=layout, has_bias=bias,
-                                            addr_bits=addr)[0]
+                                            strategy=st, addr_bits=addr)[0]
+    T = dw.STRATEGY_TILED
     for k, d in ((3, 1), (5, 1), (7, 1), (7, 2)):
         for op in (dw.OP_FWD, dw.OP_INPUT_GRAD, dw.OP_WEIGHT_GRAD):
             # NHWC: C % 4 == 0 takes 16-byte staging only when aligned
-            a = name(op, dw.NHWC, 128, k, 0, d=d)
-            u = name(op, dw.NHWC, 128, k, off, d=d)
+            a = name(op, dw.NHWC, 128, k, 0, d=d, st=T)
+            u = name(op, dw.NHWC, 128, k, off, d=d, st=T)
             assert "_l1" not in a and ("_l1" in u or "_v1" in u), (a, u)
-            assert name(op, dw.NHWC, 128, k, 16 + 32 * off, d=d) == a
+            assert name(op, dw.NHWC, 128, k, 16 + 32 * off, d=d, st=T) == a
             # NCHW: whole 16-byte rows (W % 4 == 0) only when aligned
-            a = name(op, dw.NCHW, 32, k, 0, d=d)
-            u = name(op, dw.NCHW, 32, k, off, d=d)
+            a = name(op, dw.NCHW, 32, k, 0, d=d, st=T)
+            u = name(op, dw.NCHW, 32, k, off, d=d, st=T)
             assert "_v4" in a and "_v4" not in u, (a, u)
+    # the row-streaming kernels use 4-byte accesses only: the same plan at
+    # any 4-byte alignment
+    for lay in (dw.NHWC, dw.NCHW):
+        for k, d in ((7, 1), (7, 2)):
+            a = name(dw.OP_FWD, lay, 128, k, 0, d=d, st=dw.STRATEGY_STREAM)
+            assert a.startswith("stream_") and \
+                name(dw.OP_FWD, lay, 128, k, off, d=d, st=dw.STRATEGY_STREAM) == a
     # the bias takes part in the forward's choice (its 4-channel loads)
     assert "_l1" in name(dw.OP_FWD, dw.NHWC, 128, 3, off, bias=True)
     # stride 2, and multiplier 2 (16-byte only): the 4-byte or direct kernels

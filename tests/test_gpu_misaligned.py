@@ -17,7 +17,8 @@ from depthwise_convolution_amd.workloads import NHWC, NCHW
 
 pytestmark = pytest.mark.gpu
 LNAME = {NHWC: "nhwc", NCHW: "nchw"}
-STRATS = {"auto": dw.STRATEGY_AUTO, "direct": dw.STRATEGY_DIRECT, "tiled": dw.STRATEGY_TILED}
+STRATS = {"auto": dw.STRATEGY_AUTO, "direct": dw.STRATEGY_DIRECT, "tiled": dw.STRATEGY_TILED,
+          "stream": dw.STRATEGY_STREAM}
 # (kH, kW, dilation); N=2, H=19, W=20 spans several tiles with a ragged tail,
 # C=36 fills a 16-byte-staged NHWC channel tile when aligned, W % 4 == 0 gives
 # the NCHW 16-byte rows when aligned
@@ -77,12 +78,19 @@ def test_misaligned_views_match_oracle(torch, oracle_mod, layout, k, op, strat, 
     st = STRATS[strat]
     # every float array at the same offset; the weights too
     w = _at_offset(torch, inp["w"], off)
-    name = dw.dwconv2d_describe_addr_ex(
-        {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op],
-        N, H, W, C, kH, kW, dilation=d, layout=layout, has_bias=op == "fwd", strategy=st,
-        addr_bits=4 * off)[0]
+    try:
+        name = dw.dwconv2d_describe_addr_ex(
+            {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op],
+            N, H, W, C, kH, kW, dilation=d, layout=layout, has_bias=op == "fwd", strategy=st,
+            addr_bits=4 * off)[0]
+    except dw.DwconvError as e:
+        if e.status == -12 and strat == "stream":
+            pytest.skip("no streaming kernel for this problem")
+        raise
     print(f"\n[case] {what} kernel={name}", flush=True)
-    assert "_v4" not in name and ("_l1" in name or "_v1" in name or "direct" in name), name
+    # 4-byte loads and stores only (the streaming kernels use no other)
+    assert "_v4" not in name and ("_l1" in name or "_v1" in name or "direct" in name or
+                                  "stream_" in name), name
     if op == "fwd":
         x = _at_offset(torch, inp["x"], off)
         b = _at_offset(torch, inp["b"], off)

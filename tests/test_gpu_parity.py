@@ -110,12 +110,13 @@ def test_workload_parity_full_size(torch, wl_name, layout, op):
 STRAT_WL = [n for n, w in WORKLOADS.items() if "large" not in w.tags]
 STRAT_CASES = [(n, l, o, s) for n in STRAT_WL for l in LAYOUTS
                for o in (dw.OP_FWD, dw.OP_INPUT_GRAD)
-               for s in (dw.STRATEGY_DIRECT, dw.STRATEGY_TILED)]
+               for s in (dw.STRATEGY_DIRECT, dw.STRATEGY_TILED, dw.STRATEGY_STREAM)]
+SNAME = {dw.STRATEGY_AUTO: "auto", dw.STRATEGY_DIRECT: "direct", dw.STRATEGY_TILED: "tiled",
+         dw.STRATEGY_STREAM: "stream"}
 
 
 @pytest.mark.parametrize("wl_name,layout,op,strategy", STRAT_CASES,
-                         ids=[_case_id(*c[:3]) + ("-direct" if c[3] == 1 else "-tiled")
-                              for c in STRAT_CASES])
+                         ids=[_case_id(*c[:3]) + "-" + SNAME[c[3]] for c in STRAT_CASES])
 def test_workload_parity_each_strategy(torch, wl_name, layout, op, strategy):
     wl = WORKLOADS[wl_name]
     name, _, _ = _describe(wl, layout, op, strategy)
@@ -150,17 +151,22 @@ INT_WL = ["tiny_16x16x8_3x3", "mobilenet_112x112x32_3x3", "mobilenet_s2_224x224x
           "mobilenet_m2_112x112x32_3x3", "reactant_4x4x4_3x3_m2_valid"]
 INT_CASES = [(n, l, o, s) for n in INT_WL for l in LAYOUTS for o in (dw.OP_FWD, dw.OP_INPUT_GRAD)
              for s in (dw.STRATEGY_AUTO, dw.STRATEGY_DIRECT)]
+INT_CASES += [(n, l, o, dw.STRATEGY_STREAM)
+              for n in ("asr_n64_30x19x128_7x7", "asr_n64_30x19x128_7x7_d2",
+                        "prime_n64_30x19x131_7x7", "asr_n1_30x19x128_7x7_d2")
+              for l in LAYOUTS for o in (dw.OP_FWD, dw.OP_INPUT_GRAD)]
 
 
 @pytest.mark.parametrize("wl_name,layout,op,strategy", INT_CASES,
-                         ids=[_case_id(*c[:3]) + ("-auto" if c[3] == 0 else "-direct")
-                              for c in INT_CASES])
+                         ids=[_case_id(*c[:3]) + "-" + SNAME[c[3]] for c in INT_CASES])
 def test_integer_inputs_bit_exact(torch, wl_name, layout, op, strategy):
     """Integer inputs: every partial sum is exact, so any summation order must
     give the oracle's value bit for bit."""
     wl = WORKLOADS[wl_name]
     if wl.fp16_weights:
         pytest.skip("integer weights are drawn as fp32")
+    if _describe(wl, layout, op, strategy)[0] is None:
+        pytest.skip("no kernel of this strategy for the problem")
     print(f"\n[case] int {_case_id(wl_name, layout, op)} strategy={strategy}", flush=True)
     inp, ref, _ = _oracle_case(wl_name, layout, op, integer=True)
     got = _run_gpu(torch, wl, inp, layout, op, strategy)
@@ -188,7 +194,8 @@ def test_f16_weights_bitwise_equal_f32_weights(torch, wl_name, layout, op):
 
 
 @pytest.mark.parametrize("wl_name", ["large_512x512x256_3x3", "effnet_n32_56x56x128_5x5",
-                                     "mobilenet_112x112x32_3x3"])
+                                     "mobilenet_112x112x32_3x3", "asr_n64_30x19x128_7x7",
+                                     "asr_n64_30x19x128_7x7_d2", "prime_n64_30x19x131_7x7"])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_deterministic_and_no_stray_writes(torch, wl_name, layout):
     """Two runs give identical bits; guard bands around the output stay

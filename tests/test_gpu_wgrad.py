@@ -97,9 +97,12 @@ def test_weight_grad_full_size(torch, wl_name, layout):
                                      "asr_n1_30x19x128_7x7_d2", "asr_n1_1x24x256_1x31",
                                      "prime_n1_30x19x131_7x7", "mobilenet_s2_xla_224x224x32_3x3",
                                      "effnet_n32_56x56x128_5x5_valid",
-                                     "mobilenet_m2_112x112x32_3x3", "reactant_4x4x4_3x3_m2_valid"])
+                                     "mobilenet_m2_112x112x32_3x3", "reactant_4x4x4_3x3_m2_valid",
+                                     "asr_n64_30x19x128_7x7", "prime_n64_30x19x131_7x7",
+                                     "asr_n64_30x19x128_7x7_d2"])
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("strategy", [dw.STRATEGY_DIRECT, dw.STRATEGY_TILED])
+@pytest.mark.parametrize("strategy", [dw.STRATEGY_DIRECT, dw.STRATEGY_TILED,
+                                      dw.STRATEGY_STREAM])
 def test_weight_grad_integer_bit_exact(torch, wl_name, layout, strategy):
     wl = WORKLOADS[wl_name]
     if not _has_strategy(wl, layout, strategy):
@@ -177,7 +180,8 @@ def test_weight_grad_padded_and_multiplier_shapes(torch, idx, layout):
     print(f"\n[case] wgrad {wl}", flush=True)
     inp = wlmod.make_inputs(wl, layout, seed=200 + idx)
     dW, SW, db, Sb = _ref(wl, inp, layout)
-    for strategy in (dw.STRATEGY_AUTO, dw.STRATEGY_DIRECT, dw.STRATEGY_TILED):
+    for strategy in (dw.STRATEGY_AUTO, dw.STRATEGY_DIRECT, dw.STRATEGY_TILED,
+                     dw.STRATEGY_STREAM):
         if not _has_strategy(wl, layout, strategy):
             continue
         gW, gb = _gpu(torch, wl, inp, layout, strategy)

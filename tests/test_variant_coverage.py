@@ -11,8 +11,8 @@ that runs it.
 
 * CPU: every table entry is reached by at least one op (a variant no problem
   can select would be compiled for nothing);
-* GPU: each (variant, op, multiplier) runs its problem under the TILED
-  strategy on integer inputs, where every summation order is exact, and must
+* GPU: each (variant, op, multiplier) runs its problem under its strategy
+  on integer inputs, where every summation order is exact, and must
   equal the oracle bit for bit.
 """
 import os
@@ -64,6 +64,12 @@ def _expected_prefixes():
                         ("kWgradNchwVariants", 1, True), ("kWgradNchwS2Variants", 2, True)):
         for v in _table(src, name, 6):
             out[nchw(v, s, wg)] = name
+    for kh, kw, d, cl, px, th, nb, minw in _table(src, "kStreamVariants", 8):
+        out[f"stream_nhwc_s1_k{kh}x{kw}_d{d}_cl{cl}_px{px}_th{th}_"] = "kStreamVariants"
+    for kh, kw, d, px, th, nl, nb, minw in _table(src, "kStreamNchwVariants", 8):
+        out[f"stream_nchw_s1_k{kh}x{kw}_d{d}_px{px}_th{th}_nl{nl}_"] = "kStreamNchwVariants"
+    for kh, kw, d, th, nl, nb, minw in _table(src, "kWgradStreamVariants", 7):
+        out[f"wgrad_stream_nchw_s1_k{kh}x{kw}_d{d}_th{th}_nl{nl}_"] = "kWgradStreamVariants"
     return out
 
 
@@ -72,7 +78,8 @@ def _sweep():
     layout): a kernel may have an instantiation per multiplier."""
     prefixes = _expected_prefixes()
     found = {}
-    for kh, kw, d in ((3, 3, 1), (5, 5, 1), (7, 7, 1), (7, 7, 2), (1, 15, 1), (1, 31, 1)):
+    for kh, kw, d in ((3, 3, 1), (5, 5, 1), (7, 7, 1), (7, 7, 2), (1, 15, 1), (1, 31, 1),
+                      (1, 1, 1)):
         for layout in (wlmod.NHWC, wlmod.NCHW):
             for s in (1, 2):
                 for m in (1, 2):
@@ -82,15 +89,17 @@ def _sweep():
                                 continue
                             pads = dw.dwconv2d_same_pads(dw.PAD_SAME, h, w, kh, kw, s, d)
                             for op in (dw.OP_FWD, dw.OP_INPUT_GRAD, dw.OP_WEIGHT_GRAD):
-                                try:
-                                    name = dw.dwconv2d_describe_ex(
-                                        op, 1, h, w, c, kh, kw, s, d, pads, m, layout, 0,
-                                        op == dw.OP_FWD, dw.STRATEGY_TILED)[0]
-                                except dw.DwconvError:
-                                    continue
-                                for p in prefixes:
-                                    if name.startswith(p) and (p, op, m) not in found:
-                                        found[(p, op, m)] = (1, h, w, c, kh, kw, s, d, m, layout)
+                                for st in (dw.STRATEGY_TILED, dw.STRATEGY_STREAM):
+                                    try:
+                                        name = dw.dwconv2d_describe_ex(
+                                            op, 1, h, w, c, kh, kw, s, d, pads, m, layout, 0,
+                                            op == dw.OP_FWD, st)[0]
+                                    except dw.DwconvError:
+                                        continue
+                                    for p in prefixes:
+                                        if name.startswith(p) and (p, op, m) not in found:
+                                            found[(p, op, m)] = (1, h, w, c, kh, kw, s, d, m,
+                                                                 layout, st)
     return prefixes, found
 
 
@@ -114,14 +123,13 @@ def test_every_variant_matches_oracle(key, prob):
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a visible GPU")
     prefix, op, _ = key
-    n, h, w, c, kh, kw, s, d, m, layout = prob
+    n, h, w, c, kh, kw, s, d, m, layout, st = prob
     pads = tuple(dw.dwconv2d_same_pads(dw.PAD_SAME, h, w, kh, kw, s, d))
     wl = Workload(name="cover", N=n, H=h, W=w, C=c, kH=kh, kW=kw, stride=s, dilation=d,
                   pads=pads, mult=m)
     print(f"\n[case] {prefix} op={op} {prob}", flush=True)
     inp = wlmod.make_inputs(wl, layout, seed=7, integer=True)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
-    st = dw.STRATEGY_TILED
     if op == dw.OP_FWD:
         ref, _ = oracle.fwd_general(inp["x"], inp["w"], inp["b"], s, d, pads, m, layout,
                                     nthreads=NTHREADS)
