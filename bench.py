@@ -220,10 +220,16 @@ def queue_ahead(torch, stream, us):
         torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
 
 
-def amortised(torch, stream, calls, n=40, host_us=60.0):
+def amortised(torch, stream, calls, n=40, host_us=60.0, reps=3):
     """Per-call device time (us) of n back-to-back calls that cycle through
     `calls` (e.g. the same op on two disjoint buffer sets), between two events,
-    all queued behind a spin kernel so the device never waits for the host."""
+    all queued behind a spin kernel so the device never waits for the host;
+    the median of `reps` such runs."""
+    return statistics.median(_amortised_once(torch, stream, calls, n, host_us)
+                             for _ in range(reps))
+
+
+def _amortised_once(torch, stream, calls, n, host_us):
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         for c in calls:
@@ -513,16 +519,21 @@ def headline_extras(torch, dw, wl, t, layout, stream, n_rep=40):
 
 
 # ------------------------------------------------------------------ trace table
-def _match_dispatches(dw, wl, layout, op, by_kernel):
-    """The (kernel name, grid) entries of `by_kernel` (a dict keyed by the
-    trace's kernel name and grid size in threads) that a plan of (workload,
-    layout, op) launches: the kernel family and grid from the describe call,
-    the weight type and the op from the template arguments."""
+def _row_matcher(dw, wl, layout, op):
+    """The kernel name the plan of (workload, layout, op) reports and a
+    predicate on a trace's (kernel name, grid size in threads) that accepts
+    that plan's main kernel: the family and grid from the describe call, the
+    weight type and the op from the template arguments where the kernel is a
+    template (the weight-gradient and direct kernels take their shape at run
+    time, so several workloads share one name; `_assign_rows` tells them
+    apart by dispatch order)."""
     import re
-    opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD}[op]
+    opc = {"fwd": dw.OP_FWD, "ig": dw.OP_INPUT_GRAD, "wgrad": dw.OP_WEIGHT_GRAD,
+           "fwd_bn_relu6": dw.OP_FWD, "wgrad_sgd": dw.OP_WEIGHT_GRAD}[op]
     kname, grid, block = dw.dwconv2d_describe_ex(
         opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation, wl.pads,
-        wl.mult, layout, 0 if op == "wgrad" else int(wl.fp16_weights), op == "fwd")
+        wl.mult, layout, 0 if opc == dw.OP_WEIGHT_GRAD else int(wl.fp16_weights),
+        opc == dw.OP_FWD)
     fam = {"tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
            "stream_nhwc": "k_stream_nhwc", "stream_nchw": "k_stream_nchw",
            "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
@@ -530,105 +541,158 @@ def _match_dispatches(dw, wl, layout, op, by_kernel):
            "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_direct": "k_wgrad_gen"}
     kfam = next((v for k, v in sorted(fam.items(), key=lambda kv: -len(kv[0]))
                  if kname.startswith(k)), None)
-    out = []
-    for (kn, g), vals in by_kernel.items():
-        m = re.search(r"(k_\w+)<(.*)>", kn)
-        f, args = (m.group(1), m.group(2).replace(" ", "")) if m else (kn, "")
-        if f != kfam or g != grid * block:
+    # the tiled and streaming kernels' mode: 0 forward, 1 input gradient,
+    # 2 forward with the BatchNorm + activation epilogue
+    want = {"fwd": "0", "ig": "1", "fwd_bn_relu6": "2"}.get(op)
+
+    def match(kn, g):
+        m = re.search(r"(k_\w+)(?:<(.*?)>)?\(", kn)
+        if not m or m.group(1) != kfam or g != grid * block:
+            return False
+        parts = (m.group(2) or "").replace(" ", "").split(",")
+        if want is None:
+            return True
+        if parts[0] in ("float", "_Float16", "half") and \
+                (parts[0] != "float") != bool(wl.fp16_weights):
+            return False
+        # the mode in the template arguments: the tiled kernels' third from
+        # last, the streaming kernels' last; the direct kernels' input-gradient
+        # flag (their epilogue is a run-time argument)
+        if kfam.startswith("k_tiled") and parts[-3] != want:
+            return False
+        if kfam.startswith("k_stream") and parts[-1] != want:
+            return False
+        if kfam.startswith("k_direct"):
+            flags = [q for q in parts if q in ("true", "false")]
+            if flags and flags[0] != ("true" if want == "1" else "false"):
+                return False
+        return True
+    return kname, match
+
+
+def _assign_rows(dw, order, seq):
+    """Split `seq`, the trace's dispatches in issue order as (kernel name,
+    grid threads, value), over `order`, the (workload, layout, op) rows in
+    the order the table ran them: a row takes the run of dispatches that
+    match its kernel from its first match on, skipping other programs'
+    kernels (flush, copies, spin) and the fixed-order weight-gradient
+    reduction, up to the first dwconv kernel it does not launch.  Adjacent
+    rows always differ in layout or op, hence in kernel.  Returns one
+    (reported name, trace name, values) per row."""
+    out, cursor = [], 0
+    for wl, layout, op in order:
+        kname, match = _row_matcher(dw, wl, layout, op)
+        i = cursor
+        while i < len(seq) and not match(seq[i][0], seq[i][1]):
+            i += 1
+        if i == len(seq):
+            out.append((kname, None, []))
             continue
-        parts = args.split(",")
-        if op != "wgrad":
-            if parts[0] in ("float", "_Float16", "half") and \
-                    (parts[0] != "float") != bool(wl.fp16_weights):
-                continue
-            # the op in the template arguments: the tiled kernels' mode (0
-            # forward, 1 input gradient) third from last, the streaming
-            # kernels' last; the direct kernels' input-gradient flag
-            want = {"fwd": "0", "ig": "1"}[op]
-            if kfam.startswith("k_tiled") and parts[-3] != want:
-                continue
-            if kfam.startswith("k_stream") and parts[-1] != want:
-                continue
-            if kfam.startswith("k_direct"):
-                flags = [q for q in parts if q in ("true", "false")]
-                if flags and flags[0] != ("true" if op == "ig" else "false"):
+        vals, tname, j = [], seq[i][0], i
+        while j < len(seq):
+            n, g, v = seq[j]
+            if match(n, g):
+                vals.append(v)
+            elif "dwconv::" in n and "k_wgrad_reduce" not in n:
+                break
+            j += 1
+        out.append((kname, tname, vals))
+        cursor = j
+    return out
+
+
+def _table_order(detail_path):
+    """The (workload, layout, op) rows of a `bench.py` detail file, in the
+    order its per-workload table ran them."""
+    from depthwise_convolution_amd import workloads
+    with open(detail_path) as f:
+        rows = json.load(f)["per_config"]
+    lay = {v: k for k, v in workloads.LAYOUT_NAMES.items()}
+    return [(workloads.WORKLOADS[r["workload"]], lay[r["layout"]], r["op"]) for r in rows]
+
+
+def _dispatch_seq(csv_path, counter=None):
+    """(kernel name, grid threads, value) per dispatch in dispatch order: the
+    counter's reading for a --pmc CSV, the duration in us for a kernel trace."""
+    import csv
+    seq = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if counter is not None:
+                if r.get("Counter_Name") != counter:
                     continue
-        out.append((kn, vals))
-    return kname, out
+                v = float(r["Counter_Value"])
+            else:
+                v = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            g = int(r.get("Grid_Size_X", r.get("Grid_Size", "0")) or 0)
+            seq.append((int(r.get("Dispatch_Id", 0) or 0), int(r["Start_Timestamp"]),
+                        r["Kernel_Name"], g, v))
+    seq.sort(key=lambda s: (s[1], s[0]) if counter is None else (s[0], s[1]))
+    return [s[2:] for s in seq]
 
 
-def counter_table(fetch_csv, write_csv, out_path=None):
+def counter_table(fetch_csv, write_csv, detail_path, out_path=None):
     """HBM traffic per workload from two rocprofv3 --pmc runs of `bench.py
     --table-only --calib-copy` (FETCH_SIZE, then WRITE_SIZE, KiB per
-    dispatch): the counters of the runtime's 256 MiB device copy calibrate
-    them (bytes moved / counter reading), and the 1x1 tiled forward of
-    512x512x256, which reads its input and writes its output exactly once
-    through the same 16-byte loads into LDS as the tiled kernels, checks the
-    calibration.  Per (workload, layout, op): median counter per dispatch,
-    scaled, against the algorithmic bytes.  No GPU needed."""
-    import csv
+    dispatch) and that run's detail file (the row order): the counters of
+    the runtime's 256 MiB device copies calibrate them (bytes moved /
+    counter reading), and the 1x1 tiled forward of 512x512x256, which reads
+    its input and writes its output exactly once through the same 16-byte
+    loads into LDS as the tiled kernels, checks the calibration.  Per
+    (workload, layout, op): median counter per dispatch, scaled, against
+    the algorithmic bytes.  No GPU needed."""
     import depthwise_convolution_amd as dw
     from depthwise_convolution_amd import workloads
 
-    def load(path, counter):
-        vals = {}
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if r.get("Counter_Name") != counter:
-                    continue
-                key = (r["Kernel_Name"], int(r.get("Grid_Size", "0") or 0))
-                vals.setdefault(key, []).append(float(r["Counter_Value"]))
-        return vals
-
-    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    fseq, wseq = _dispatch_seq(fetch_csv, "FETCH_SIZE"), _dispatch_seq(write_csv, "WRITE_SIZE")
     kib = 1024.0
     copy_bytes = 256 * 1024 * 1024
 
-    # the copy of the calibration leg is the largest copyBuffer dispatch
-    cf = max((statistics.median(v) for (k, g), v in fetch.items() if "copyBuffer" in k),
-             default=None)
-    cw = max((statistics.median(v) for (k, g), v in write.items() if "copyBuffer" in k),
-             default=None)
-    sf = copy_bytes / (cf * kib) if cf else None
-    sw = copy_bytes / (cw * kib) if cw else None
+    def calib(seq):
+        # the 256 MiB copies: the runtime copy dispatches within 10 % of the
+        # largest reading (the smaller same-bytes copies share their grid)
+        vals = [v for n, g, v in seq if "copyBuffer" in n]
+        if not vals:
+            return None, 0
+        big = [v for v in vals if v >= 0.9 * max(vals)]
+        return copy_bytes / (statistics.median(big) * kib), len(big)
+
+    (sf, nf), (sw, nw) = calib(fseq), calib(wseq)
     one = workloads.Workload(name="calib_1x1", N=1, H=512, W=512, C=256, kH=1, kW=1)
-    lines = [f"Calibration: 256 MiB device copy reads FETCH_SIZE = {cf:.1f} KiB and writes "
-             f"WRITE_SIZE = {cw:.1f} KiB per dispatch: FETCH_SIZE x {sf:.4f}, WRITE_SIZE x "
-             f"{sw:.4f}." if sf and sw else "Calibration: no copy dispatch found."]
-    _, m1 = _match_dispatches(dw, one, workloads.NHWC, "fwd", fetch)
-    _, m1w = _match_dispatches(dw, one, workloads.NHWC, "fwd", write)
-    if m1 and m1w and sf and sw:
-        r1 = statistics.median(m1[0][1]) * kib * sf
-        w1 = statistics.median(m1w[0][1]) * kib * sw
+    lines = [f"Calibration: {nf} / {nw} runtime copies of 256 MiB read FETCH_SIZE = "
+             f"{copy_bytes / sf / kib:.1f} KiB and write WRITE_SIZE = {copy_bytes / sw / kib:.1f} "
+             f"KiB per dispatch (medians): FETCH_SIZE x {sf:.4f}, WRITE_SIZE x {sw:.4f} "
+             f"give bytes." if sf and sw else "Calibration: no copy dispatch found."]
+    (_, _, v1f), = _assign_rows(dw, [(one, workloads.NHWC, "fwd")], fseq)
+    (_, _, v1w), = _assign_rows(dw, [(one, workloads.NHWC, "fwd")], wseq)
+    if v1f and v1w and sf and sw:
+        r1 = statistics.median(v1f) * kib * sf
+        w1 = statistics.median(v1w) * kib * sw
         lines.append(f"Check: the 1x1 tiled forward of 512x512x256 (reads 268,437,504 B, writes "
-                     f"268,435,456 B) measures {r1:,.0f} B read ({r1 / 268437504:.3f}x) and "
-                     f"{w1:,.0f} B written ({w1 / 268435456:.3f}x) with this calibration.")
-    lines += ["", "| workload | layout | op | kernel | dispatches | read MiB | written MiB | "
+                     f"268,435,456 B; {len(v1f)} dispatches) measures {r1:,.0f} B read "
+                     f"({r1 / 268437504:.3f}x) and {w1:,.0f} B written ({w1 / 268435456:.3f}x) "
+                     f"with this calibration.")
+    lines += ["", "Per dispatch, median over the row's dispatches (warm-up, back-to-back and "
+              "cold calls; weight gradient: its partial-sum kernel, the reduction excluded).",
+              "", "| workload | layout | op | kernel | dispatches | read MiB | written MiB | "
               "HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|"]
+    order = _table_order(detail_path)
     rows = {}
-    for name, wl in workloads.WORKLOADS.items():
-        if "parity_only" in wl.tags:
+    for (wl, layout, op), (kname, _, vf), (_, _, vw) in zip(
+            order, _assign_rows(dw, order, fseq), _assign_rows(dw, order, wseq)):
+        if not vf or not vw or not sf:
             continue
-        for layout in (0, 1):
-            for op in ("fwd", "ig", "wgrad"):
-                if op == "wgrad" and wl.fp16_weights:
-                    continue
-                kname, mf = _match_dispatches(dw, wl, layout, op, fetch)
-                _, mw = _match_dispatches(dw, wl, layout, op, write)
-                if not mf or not mw or not sf:
-                    continue
-                kf = max(mf, key=lambda c: len(c[1]))
-                kw = max(mw, key=lambda c: len(c[1]))
-                rb = statistics.median(kf[1]) * kib * sf
-                wb = statistics.median(kw[1]) * kib * sw
-                alg = op_bytes(wl, op)
-                rows[(name, workloads.LAYOUT_NAMES[layout], op)] = {
-                    "kernel": kname, "hbm_bytes_per_launch": round(rb + wb),
-                    "read_bytes": round(rb), "written_bytes": round(wb),
-                    "algorithmic_bytes": alg, "ratio": round((rb + wb) / alg, 3)}
-                lines.append(f"| {name} | {workloads.LAYOUT_NAMES[layout]} | {op} | `{kname}` | "
-                             f"{len(kf[1])} | {rb / 2**20:.2f} | {wb / 2**20:.2f} | "
-                             f"{rb + wb:,.0f} | {alg:,} | {(rb + wb) / alg:.3f} |")
+        rb = statistics.median(vf) * kib * sf
+        wb = statistics.median(vw) * kib * sw
+        alg = op_bytes(wl, op)
+        lname = workloads.LAYOUT_NAMES[layout]
+        rows[(wl.name, lname, op)] = {
+            "kernel": kname, "hbm_bytes_per_launch": round(rb + wb),
+            "read_bytes": round(rb), "written_bytes": round(wb),
+            "algorithmic_bytes": alg, "ratio": round((rb + wb) / alg, 3)}
+        lines.append(f"| {wl.name} | {lname} | {op} | `{kname}` | {len(vf)} | "
+                     f"{rb / 2**20:.2f} | {wb / 2**20:.2f} | {rb + wb:,.0f} | {alg:,} | "
+                     f"{(rb + wb) / alg:.3f} |")
     text = "\n".join(lines) + "\n"
     if out_path:
         with open(out_path, "w") as f:
@@ -636,43 +700,28 @@ def counter_table(fetch_csv, write_csv, out_path=None):
     return text, rows, (sf, sw)
 
 
-def trace_table(csv_path, out_path=None):
-    """Summarise a rocprofv3 kernel-trace CSV of `bench.py --table-only` per
-    workload: each (kernel, grid) is matched to the workloads/layouts/ops
-    whose plan launches it (the describe call's kernel shape and grid), and
-    the per-dispatch durations give median / mean / min (for the weight
-    gradient: its first, partial-sum kernel; the fixed-order reduction that
-    follows is a dispatch of its own, 3-5 us).  No GPU needed."""
-    import csv
+def trace_table(csv_path, detail_path, out_path=None):
+    """Summarise a rocprofv3 kernel-trace CSV of a `bench.py` run per
+    workload, with that run's detail file giving the table's row order: each
+    row's dispatches (`_assign_rows`) give median / mean / min device time
+    (for the weight gradient: its first, partial-sum kernel; the fixed-order
+    reduction that follows is a dispatch of its own, 3-5 us).  No GPU
+    needed."""
     import depthwise_convolution_amd as dw
     from depthwise_convolution_amd import workloads
-    durs = {}
-    with open(csv_path) as f:
-        for r in csv.DictReader(f):
-            name = r.get("Kernel_Name", "")
-            grid = int(r.get("Grid_Size_X", r.get("Grid_Size", "0")) or 0)
-            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            durs.setdefault((name, grid), []).append(d)
-
+    seq = _dispatch_seq(csv_path)
+    order = _table_order(detail_path)
     lines = ["| workload | layout | op | kernel | calls | median us | mean us | min us | "
              "floor us (bound) | median frac of floor |", "|---|---|---|---|---|---|---|---|---|---|"]
-    for name, wl in workloads.WORKLOADS.items():
-        if "parity_only" in wl.tags:
+    for (wl, layout, op), (kname, _, ds) in zip(order, _assign_rows(dw, order, seq)):
+        if not ds:
             continue
-        for layout in (0, 1):
-            for op in ("fwd", "ig", "wgrad"):
-                if op == "wgrad" and wl.fp16_weights:
-                    continue
-                kname, cands = _match_dispatches(dw, wl, layout, op, durs)
-                if not cands:
-                    continue
-                kn, ds = max(cands, key=lambda c: len(c[1]))
-                bound, floor_us = floors(wl, op)
-                med = statistics.median(ds)
-                lines.append(f"| {name} | {workloads.LAYOUT_NAMES[layout]} | {op} | "
-                             f"`{kname}` | {len(ds)} | {med:.2f} | {statistics.mean(ds):.2f} | "
-                             f"{min(ds):.2f} | {floor_us:.2f} ({bound}) | "
-                             f"{floor_us / med:.3f} |")
+        bound, floor_us = floors(wl, op)
+        med = statistics.median(ds)
+        lines.append(f"| {wl.name} | {workloads.LAYOUT_NAMES[layout]} | {op} | "
+                     f"`{kname}` | {len(ds)} | {med:.2f} | {statistics.mean(ds):.2f} | "
+                     f"{min(ds):.2f} | {floor_us:.2f} ({bound}) | "
+                     f"{floor_us / med:.3f} |")
     text = "\n".join(lines) + "\n"
     if out_path:
         with open(out_path, "w") as f:
@@ -680,7 +729,6 @@ def trace_table(csv_path, out_path=None):
     return text
 
 
-# ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -703,10 +751,11 @@ def main():
     ap.add_argument("--out", default="")
     args = ap.parse_args()
     if args.trace_table:
-        print(trace_table(args.trace_table, args.out or None))
+        print(trace_table(args.trace_table, args.detail, args.out or None))
         return
     if args.counter_table:
-        text, rows, (sf, sw) = counter_table(*args.counter_table, args.out or None)
+        text, rows, (sf, sw) = counter_table(*args.counter_table, args.detail,
+                                             args.out or None)
         print(text)
         if args.traffic_json:
             ops = {op: rows[(HEADLINE, "nhwc", op)] for op in ("fwd", "ig", "wgrad")

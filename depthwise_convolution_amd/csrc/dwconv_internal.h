@@ -166,9 +166,14 @@ constexpr WgradStreamVariant kWgradStreamVariants[] = {
 constexpr int kNumWgradStreamVariants =
     sizeof(kWgradStreamVariants) / sizeof(kWgradStreamVariants[0]);
 
-// Cache policy of the row-streaming kernel's stores (gfx950 buffer-store
-// cache-policy bits: 2 = non-temporal): outputs are written once.
+// Cache policy of the row-streaming kernels' stores (gfx950 buffer-store
+// cache-policy bits: 2 = non-temporal, 0 = write-back).  NHWC: a store
+// covers whole 256-byte pixels of 64 channels, written once, non-temporal.
+// NCHW: a store writes one row (OW floats) of each plane of the wave, and
+// the row before and after, stored later, share its first and last cache
+// lines; write-back lets L2 merge those partial lines before they go to HBM.
 constexpr int kStreamStoreAux = 2;
+constexpr int kStreamNchwStoreAux = 0;
 
 // Compile-time variants of the tiled NHWC weight-gradient kernel: workgroup
 // geometry as for the forward (vec, cl, px, g, lv).  A workgroup walks a strip of

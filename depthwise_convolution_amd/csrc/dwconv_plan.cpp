@@ -288,6 +288,16 @@ static bool plan_tiled_nchw(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     return true;
 }
 
+// Tile order of a tiled or NHWC row-streaming plan (kXcdRangeMaxBytes):
+// activations are the tensor read and the tensor written, x and y (or dy
+// and dx, x and dy).
+static int xcd_ranges(const Problem &p)
+{
+    const long long act =
+        4LL * p.N * p.C * ((long long)p.H * p.W + (long long)p.mult * p.Ho * p.Wo);
+    return act < kXcdRangeMaxBytes ? 1 : 0;
+}
+
 // Row-streaming NHWC kernel: stride 1, no multiplier, a listed kernel shape.
 // Any channel count and 4-byte alignment (4-byte loads and stores).
 static bool plan_stream_nhwc(const Problem &p, Plan *pl)
@@ -332,6 +342,7 @@ static bool plan_stream_nhwc(const Problem &p, Plan *pl)
         return false;
     pl->grid = pl->nct * ((pl->total + 3) / 4);
     pl->block = 256;
+    pl->xcd = xcd_ranges(p);
     std::snprintf(pl->name, sizeof pl->name, "stream_nhwc_s1_k%dx%d_d%d_cl%d_px%d_th%d_%s_%s",
                   v.kH, v.kW, v.d, v.cl, v.px, v.th, op_tag(p), p.wtype ? "f16w" : "f32w");
     return true;
@@ -420,15 +431,6 @@ static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
     std::snprintf(pl->name, sizeof pl->name, "direct_%s_s%d_v%d_%s_%s",
                   p.layout == DWCONV_LAYOUT_NHWC ? "nhwc" : "nchw", p.stride, pl->vec,
                   op_tag(p), p.wtype ? "f16w" : "f32w");
-}
-
-// Tile order of a tiled plan (kXcdRangeMaxBytes): activations are the
-// tensor read and the tensor written, x and y (or dy and dx, x and dy).
-static int xcd_ranges(const Problem &p)
-{
-    const long long act =
-        4LL * p.N * p.C * ((long long)p.H * p.W + (long long)p.mult * p.Ho * p.Wo);
-    return act < kXcdRangeMaxBytes ? 1 : 0;
 }
 
 int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)

@@ -48,6 +48,7 @@ struct StreamArgs {
     int nct;                // channel tiles of CL
     int ncg, nrt, nph;      // column groups per sub-grid row, row tiles, phases (D*D)
     int upc;                // units per channel tile: N * nrt * nph * ncg
+    int xcd;                // workgroup order: 1 = per-XCD ranges (xcd_tile), 0 = in order
 };
 
 __device__ __forceinline__ int floor_div(int a, int b)
@@ -70,12 +71,15 @@ __global__ __launch_bounds__(256) void k_stream_nhwc(const float *__restrict__ i
     static_assert(CL == 16 || CL == 32 || CL == 64, "channels per lane group");
     __shared__ float wl[NWL * 256];
     const WT *w = reinterpret_cast<const WT *>(wv);
-    const int ct = blockIdx.x % a.nct;
+    // the workgroup's place: per-XCD ranges put the row tiles of an image,
+    // which share kH - 1 halo rows, on one XCD and so in one L2
+    const int blk = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int ct = blk % a.nct;
     const int lane = threadIdx.x & 63;
     const int ch = lane % CL, cs = lane / CL;          // channel in the tile, column group
     // the wave's unit (wave-uniform); a wave past the last unit only helps
     // stage the weights
-    const int unit = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / a.nct) * 4 +
+    const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 +
                                                     (int)(threadIdx.x >> 6));
     const bool live = unit < a.upc;
     const int c0 = ct * CL, c = c0 + ch;
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
 #pragma unroll
             for (int jj = 0; jj < PX; ++jj)
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[jj]), ro,
-                                                      vout[jj], soff, kStreamStoreAux);
+                                                      vout[jj], soff, kStreamNchwStoreAux);
 #pragma unroll
             for (int jj = 0; jj < PX; ++jj)
                 v[jj] = bv;
@@ -632,6 +636,7 @@ int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const 
     a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.ncg = pl.nwt; a.nrt = pl.nst; a.nph = pl.pb;
     a.upc = (int)pl.total;
+    a.xcd = pl.xcd;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }
