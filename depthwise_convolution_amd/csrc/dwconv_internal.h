@@ -55,6 +55,7 @@ enum Kind {
     KIND_STREAM_NHWC = 8,  // stride 1, many taps: rows streamed through registers, phases of D
     KIND_STREAM_NCHW = 9,  // the same with lanes along plane columns, rows staged per wave
     KIND_WGRAD_STREAM_NCHW = 10, // weight gradient, NCHW stride 1: the NCHW row walk, tap sums per lane
+    KIND_WGRAD_STREAM_NHWC = 11, // weight gradient, NHWC stride 1: the NHWC row walk, tap sums per lane
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
@@ -166,6 +167,17 @@ constexpr WgradStreamVariant kWgradStreamVariants[] = {
 constexpr int kNumWgradStreamVariants =
     sizeof(kWgradStreamVariants) / sizeof(kWgradStreamVariants[0]);
 
+// Variants of the row-streaming NHWC weight gradient (stride 1, no
+// multiplier): the NHWC walk's waves (64 channels x `px` columns x `th` dy
+// rows of one phase), `nb` x rows in flight; AUTO takes it from `minw`
+// waves.
+struct WgradStreamNhwcVariant { int kH, kW, d, px, th, nb, minw; };
+constexpr WgradStreamNhwcVariant kWgradStreamNhwcVariants[] = {
+    {7, 7, 1, 5, 5, 3, 1024}, {7, 7, 2, 5, 8, 3, 1024},
+};
+constexpr int kNumWgradStreamNhwcVariants =
+    sizeof(kWgradStreamNhwcVariants) / sizeof(kWgradStreamNhwcVariants[0]);
+
 // Cache policy of the row-streaming kernels' stores (gfx950 buffer-store
 // cache-policy bits: 2 = non-temporal, 0 = write-back).  NHWC: a store
 // covers whole 256-byte pixels of 64 channels, written once, non-temporal.
@@ -213,6 +225,16 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 // input gradient takes bands of 8 plane groups, one plane group's row tiles
 // per XCD in order (the plane-group count a multiple of 8): 2-3% faster.
 constexpr long long kXcdRangeMaxBytes = 448LL << 20;
+
+// Weight-gradient reduction: up to this many columns (channels x (taps + 1))
+// the reduction kernel spreads each column's chunks over 16 slices (16
+// columns per workgroup), above it over 8 (32 columns, whole 128-byte runs
+// per load).  Measured against 4 slices of 64 columns (the earlier shape):
+// 64x30x19x128 7x7 NHWC (384 chunks) 21.6 -> 19.6 us, 7x7 d2 NCHW 38.2 ->
+// 36.9 us, 64x1x24x256 1x31 NHWC 17.2 -> 16.4 us, 8x224x224x32 3x3 s2 NHWC
+// (320 columns, 266 chunks) 9.7 -> 7.8 us with 16 slices; within 3% on the
+// rest of the workloads.
+constexpr int kReduceFewColumns = 512;
 constexpr int kNumWgradVariants = sizeof(kWgradVariants) / sizeof(kWgradVariants[0]);
 
 // Variants of the tiled NHWC weight gradient at stride 2 (g = staged x rows
@@ -325,6 +347,7 @@ struct Plan {
     long long chunks;   // weight gradient: partial sums per weight (rows of the workspace)
     long long workspace;// weight gradient: workspace bytes
     long long grid2;    // weight gradient: workgroups of the reduction kernel
+    int red_s;          // weight gradient: chunk slices per reduction workgroup (4 or 16)
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
                         // (tiled NHWC stride-2 forward: OH, OW = the stride-1 grid it tiles)

@@ -689,6 +689,53 @@ static bool plan_wgrad_stream_nchw(const Problem &p, Plan *pl)
     return true;
 }
 
+// Row-streaming NHWC weight gradient: stride 1, no multiplier, a listed
+// kernel shape.  One chunk of partial sums per workgroup (four waves).
+static bool plan_wgrad_stream_nhwc(const Problem &p, Plan *pl)
+{
+    if (p.layout != DWCONV_LAYOUT_NHWC || p.stride != 1 || p.mult != 1)
+        return false;
+    int best = -1;
+    for (int i = 0; i < kNumWgradStreamNhwcVariants; ++i) {
+        const WgradStreamNhwcVariant &v = kWgradStreamNhwcVariants[i];
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const WgradStreamNhwcVariant &v = kWgradStreamNhwcVariants[best];
+    // byte offsets within a row (a lane's columns, up to (kW-1)*d past the
+    // row on either side) and row starts within an image are 32-bit
+    const long long cb = 4LL * p.C;
+    if (cb * (std::max(p.W, pl->OW) + 2LL * v.d * v.kW + 2LL * v.px * v.d) >= (1LL << 31) ||
+        cb * p.H * p.W >= (1LL << 31) || cb * pl->OH * pl->OW >= (1LL << 31))
+        return false;
+    const int d = v.d;
+    const int ohs = ceil_div(pl->OH, d), ows = ceil_div(pl->OW, d);   // phase sub-grid
+    pl->kind = KIND_WGRAD_STREAM_NHWC;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = 64;
+    pl->tw = v.px;
+    pl->th = v.th;
+    pl->nct = ceil_div(p.C, 64);
+    pl->nwt = ceil_div(ows, v.px);
+    pl->nst = ceil_div(ohs, v.th);
+    pl->pb = d * d;                               // phases
+    pl->total = (long long)p.N * pl->nst * pl->pb * pl->nwt;      // wave units per channel tile
+    if (pl->total * 4 >= (1LL << 31))
+        return false;
+    pl->chunks = (pl->total + 3) / 4;             // one per workgroup of a channel tile
+    pl->grid = pl->nct * pl->chunks;
+    pl->block = 256;
+    pl->xcd = xcd_ranges(p);
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_stream_nhwc_s1_k%dx%d_d%d_px%d_th%d", v.kH,
+                  v.kW, v.d, v.px, v.th);
+    return true;
+}
+
 static void plan_wgrad_direct(const Problem &p, Plan *pl)
 {
     // any layout / stride / padding / multiplier: the generic kernel, with
@@ -750,14 +797,18 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     bool tiled = false;
     if (strategy == DWCONV_STRATEGY_STREAM || strategy == DWCONV_STRATEGY_AUTO) {
         Plan t = *pl;
-        if (plan_wgrad_stream_nchw(p, &t) &&
-            (strategy == DWCONV_STRATEGY_STREAM ||
-             t.total >= kWgradStreamVariants[t.variant].minw)) {
-            *pl = t;
-            tiled = true;
-        } else if (strategy == DWCONV_STRATEGY_STREAM) {
-            return DWCONV_ERR_BAD_STRATEGY;
+        const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
+        if (nhwc ? plan_wgrad_stream_nhwc(p, &t) : plan_wgrad_stream_nchw(p, &t)) {
+            const long long waves = nhwc ? t.nct * t.total : t.total;
+            const int minw = nhwc ? kWgradStreamNhwcVariants[t.variant].minw
+                                  : kWgradStreamVariants[t.variant].minw;
+            if (strategy == DWCONV_STRATEGY_STREAM || waves >= minw) {
+                *pl = t;
+                tiled = true;
+            }
         }
+        if (!tiled && strategy == DWCONV_STRATEGY_STREAM)
+            return DWCONV_ERR_BAD_STRATEGY;
     }
     if (!tiled && strategy != DWCONV_STRATEGY_DIRECT) {
         Plan t = *pl;
@@ -777,7 +828,10 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (pl->chunks * cols >= (1LL << 31))
         return DWCONV_ERR_BAD_DIM;
     pl->workspace = 4 * pl->chunks * cols;
-    pl->grid2 = (cols + 63) / 64;
+    // the reduction: 8 chunk slices of 32 columns per workgroup (128-byte
+    // runs), 16 slices of 16 columns when there are few columns
+    pl->red_s = cols <= kReduceFewColumns ? 16 : 8;
+    pl->grid2 = (cols + 256 / pl->red_s - 1) / (256 / pl->red_s);
     return DWCONV_OK;
 }
 

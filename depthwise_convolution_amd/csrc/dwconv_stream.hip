@@ -388,6 +388,145 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
 }
 
 // ---------------------------------------------------------------------------
+// Row-streaming NHWC weight gradient (stage 1): the NHWC walk's waves (64
+// channels, one per lane, x PX output columns x TH output rows of one
+// dilation phase) with the roles of the operands changed (LeanMlir
+// "Depthwise" weight-VJP: dW[c,kh,kw] is the sum over positions of x at the
+// tap times dy, db[c] the sum of dy).  A lane loads its channel's x row (PX
+// + kW - 1 columns) and dy row (PX columns) straight into registers, rows
+// ahead of use; it keeps the dy rows of the last kH output rows, and each x
+// row u meets dy rows u - kh for its kH*kW tap sums (PX FMAs per tap).  The
+// workgroup's four waves add their sums in LDS in wave order, and the
+// workgroup writes them as one contiguous run of its chunk of the partial
+// sums part[chunk][c][tap]; the fixed-order reduction kernel adds the
+// chunks.
+// ---------------------------------------------------------------------------
+template <int KH, int KW, int D, int PX, int TH, int NB>
+__global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restrict__ x,
+                                                           const float *__restrict__ dy,
+                                                           float *__restrict__ part,
+                                                           StreamArgs a)
+{
+    constexpr int KK = KH * KW, G = TH + KH - 1, XW = PX + KW - 1, KP = KK + 1;
+    constexpr int RG = KH + NB - 1;                   // dy rows in registers
+    constexpr int LP = 65;                            // LDS pitch of a sum row
+    static_assert(NB >= 2, "at least one row in flight");
+    __shared__ float red[3][KP * LP];
+    const int blk = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int ct = blk % a.nct;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave's unit; a wave past the last unit adds zeros
+    const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 + wave);
+    const bool live = unit < a.upc;
+    const int c = ct * 64 + lane;
+    const bool cok = c < a.C;
+    // the unit: column block (fastest), phase, row tile, image
+    int t = live ? unit : 0;
+    const int cg = t % a.ncg;
+    t /= a.ncg;
+    const int ph = t % a.nph;
+    t /= a.nph;
+    const int rt = t % a.nrt;
+    const int n = t / a.nrt;
+    const int ar = ph / D, ac = ph - (ph / D) * D;
+    const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+    const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
+    const int i0 = rt * TH, j0 = cg * PX;
+    int vin[XW], vg[PX];
+#pragma unroll
+    for (int k = 0; k < XW; ++k)
+        vin[k] = cok ? (D * (j0 + tc + k) + bc) * (a.C * 4) + c * 4 : kOutOfRange;
+#pragma unroll
+    for (int jj = 0; jj < PX; ++jj)
+        vg[jj] = cok ? (ac + D * (j0 + jj)) * (a.C * 4) + c * 4 : kOutOfRange;
+    const int row_x = a.IW * a.C * 4, row_g = a.OW * a.C * 4;
+    const float *img_x = x + (long long)n * a.IH * a.IW * a.C;
+    const float *img_g = dy + (long long)n * a.OH * a.OW * a.C;
+    float xb[NB][XW], gb[RG][PX];
+    auto load_x = [&](int g, float (&d)[XW]) {
+        const int ir = D * (i0 + tr + g) + br;
+        const bool ok = live && (unsigned)ir < (unsigned)a.IH;
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(img_x + (ok ? ir : 0) * a.IW * a.C, ok ? row_x : 0);
+#pragma unroll
+        for (int k = 0; k < XW; ++k)
+            d[k] = buf_f32(r, vin[k]);
+    };
+    auto load_g = [&](int m, float (&d)[PX]) {
+        const int oh = ar + D * (i0 + m);
+        const bool ok = live && m < TH && oh < a.OH;
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(img_g + (ok ? oh : 0) * a.OW * a.C, ok ? row_g : 0);
+#pragma unroll
+        for (int jj = 0; jj < PX; ++jj)
+            d[jj] = buf_f32(r, vg[jj]);
+    };
+#pragma unroll
+    for (int g = 0; g < NB - 1; ++g) {
+        load_x(g, xb[g]);
+        if (g < TH)
+            load_g(g, gb[g % RG]);
+    }
+    float acc[KP];
+#pragma unroll
+    for (int q = 0; q < KP; ++q)
+        acc[q] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        // x row u + NB - 1 and dy row u + NB - 1 on their way
+        if (u + NB - 1 < G) {
+            load_x(u + NB - 1, xb[(u + NB - 1) % NB]);
+            if (u + NB - 1 < TH)
+                load_g(u + NB - 1, gb[(u + NB - 1) % RG]);
+        }
+        if (u < TH) {
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                acc[KK] += gb[u % RG][jj];            // the bias sum
+        }
+        const int ir = D * (i0 + tr + u) + br;
+        if ((unsigned)ir < (unsigned)a.IH) {
+            const float(&xv)[XW] = xb[u % NB];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh;                 // dy row this x row meets at tap row kh
+                if (m >= 0 && m < TH) {
+#pragma unroll
+                    for (int jj = 0; jj < PX; ++jj)
+#pragma unroll
+                        for (int kw = 0; kw < KW; ++kw)
+                            acc[kh * KW + kw] =
+                                fmaf(xv[jj + kw], gb[m % RG][jj], acc[kh * KW + kw]);
+                }
+            }
+        }
+    }
+    // waves 1-3 park their sums; wave 0 adds the four in wave order and
+    // parks the total in wave 1's rows
+    if (wave > 0) {
+#pragma unroll
+        for (int q = 0; q < KP; ++q)
+            red[wave - 1][q * LP + lane] = acc[q];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < KP; ++q)
+            red[0][q * LP + lane] = ((acc[q] + red[0][q * LP + lane]) + red[1][q * LP + lane]) +
+                                    red[2][q * LP + lane];
+    }
+    __syncthreads();
+    // the chunk's channels c0 .. c0 + 63 are KP * 64 consecutive floats of part
+    const int chunk = blk / a.nct, c0 = ct * 64;
+    const int nc = min(64, a.C - c0);
+    float *dst = part + ((long long)chunk * a.C + c0) * KP;
+    for (int e = threadIdx.x; e < nc * KP; e += 256) {
+        const int cl = e / KP, q = e - cl * KP;
+        dst[e] = red[0][q * LP + cl];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Row-streaming NCHW weight gradient (stage 1): the lanes and the staged x
 // rows of the NCHW walk above, with the roles of the operands changed
 // (LeanMlir "Depthwise" weight-VJP: dW[c,kh,kw] is the sum over positions
@@ -621,6 +760,31 @@ struct StreamTable {
     }
 };
 
+typedef void (*WgradStreamNhwcFn)(const float *, const float *, float *, StreamArgs);
+
+template <int V>
+constexpr WgradStreamNhwcFn wgrad_stream_nhwc_fn()
+{
+    constexpr WgradStreamNhwcVariant t = kWgradStreamNhwcVariants[V];
+    return &k_wgrad_stream_nhwc<t.kH, t.kW, t.d, t.px, t.th, t.nb>;
+}
+
+template <int... Vs>
+void fill_wgrad_stream_nhwc(WgradStreamNhwcFn (&fn)[kNumWgradStreamNhwcVariants],
+                            std::integer_sequence<int, Vs...>)
+{
+    ((fn[Vs] = wgrad_stream_nhwc_fn<Vs>()), ...);
+}
+
+struct WgradStreamNhwcTable {
+    WgradStreamNhwcFn fn[kNumWgradStreamNhwcVariants];
+    WgradStreamNhwcTable()
+    {
+        fill_wgrad_stream_nhwc(fn,
+                               std::make_integer_sequence<int, kNumWgradStreamNhwcVariants>());
+    }
+};
+
 }  // namespace
 
 int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const void *w,
@@ -662,6 +826,25 @@ int launch_stream_nchw(const Problem &p, const Plan &pl, const float *in, const 
     a.units = (int)pl.total;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
+}
+
+int launch_wgrad_stream_nhwc(const Problem &p, const Plan &pl, const float *x, const float *dy,
+                             float *part, hipStream_t st)
+{
+    static const WgradStreamNhwcTable table;
+    if (p.mult != 1 || p.stride != 1 || pl.variant < 0 ||
+        pl.variant >= kNumWgradStreamNhwcVariants || pl.cl != 64 ||
+        pl.chunks != (pl.total + 3) / 4 || pl.grid != pl.nct * pl.chunks)
+        return DWCONV_ERR_BAD_STRATEGY;
+    StreamArgs a;
+    a.C = p.C;
+    a.IH = p.H; a.IW = p.W; a.OH = pl.OH; a.OW = pl.OW;
+    a.pH = pl.pH; a.pW = pl.pW;
+    a.nct = pl.nct; a.ncg = pl.nwt; a.nrt = pl.nst; a.nph = pl.pb;
+    a.upc = (int)pl.total;
+    a.xcd = pl.xcd;
+    return launch_kernel(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy,
+                         part, a);
 }
 
 int launch_wgrad_stream_nchw(const Problem &p, const Plan &pl, const float *x, const float *dy,

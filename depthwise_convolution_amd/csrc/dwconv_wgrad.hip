@@ -565,55 +565,68 @@ __global__ __launch_bounds__(256) void k_wgrad_tiled_nchw(const float *__restric
     }
 }
 
-// Stage 2: 64 columns of part[] per workgroup, one per lane, so every wave
-// load is one coalesced run; wave w adds the chunks w, w+4, w+8, ... with 8
-// independent partial sums (8 loads in flight), combined in a fixed order,
-// and the 4 waves are added in a fixed order in LDS.  The result depends
-// only on the partial sums, never on timing.
+// Stage 2: 256 / S columns of part[] per workgroup and S chunk slices:
+// thread t adds column t % (256 / S) over the chunks t / (256 / S) + k*S,
+// k = 0, 1, ..., with 8 independent partial sums (8 loads in flight)
+// combined in a fixed order, and the S slices are added in LDS in a fixed
+// pairwise tree.  The plan takes S = 8 (32-column runs, whole 128-byte
+// lines per load) and S = 16 when there are few columns (more workgroups).
+// The result depends only on the partial sums, never on timing.
 // With w_upd, the LeanMlir page's SGD step is fused in: w_upd -= lr * dW and,
 // with b_upd, b_upd -= lr * db (one rounding each: fmaf(-lr, grad, old)).
 constexpr int kReduceUnroll = 8;
 
+template <int S>
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ part,
                                                       float *__restrict__ dw,
                                                       float *__restrict__ db, int chunks,
                                                       int C, int KK, float *__restrict__ w_upd,
                                                       float *__restrict__ b_upd, float lr)
 {
-    __shared__ float red[4][64];
+    constexpr int CPW = 256 / S;
+    __shared__ float red[S][CPW];
     const int cols = C * (KK + 1);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + lane;
+    const int cl = threadIdx.x % CPW, sl = threadIdx.x / CPW;
+    const int col = blockIdx.x * CPW + cl;
     const bool valid = col < cols;
     float s[kReduceUnroll];
 #pragma unroll
     for (int u = 0; u < kReduceUnroll; ++u)
         s[u] = 0.0f;
     if (valid) {
-        int r = wv;
-        for (; r + 4 * (kReduceUnroll - 1) < chunks; r += 4 * kReduceUnroll) {
+        int r = sl;
+        for (; r + S * (kReduceUnroll - 1) < chunks; r += S * kReduceUnroll) {
             float v[kReduceUnroll];
 #pragma unroll
             for (int u = 0; u < kReduceUnroll; ++u)
-                v[u] = part[(long long)(r + 4 * u) * cols + col];
+                v[u] = part[(long long)(r + S * u) * cols + col];
 #pragma unroll
             for (int u = 0; u < kReduceUnroll; ++u)
                 s[u] += v[u];
         }
 #pragma unroll
         for (int u = 0; u < kReduceUnroll - 1; ++u)
-            if (r + 4 * u < chunks)
-                s[u] += part[(long long)(r + 4 * u) * cols + col];
+            if (r + S * u < chunks)
+                s[u] += part[(long long)(r + S * u) * cols + col];
     }
 #pragma unroll
     for (int w = kReduceUnroll / 2; w > 0; w >>= 1)
 #pragma unroll
         for (int u = 0; u < w; ++u)
             s[u] += s[u + w];
-    red[wv][lane] = s[0];
+    red[sl][cl] = s[0];
     __syncthreads();
-    if (wv == 0 && valid) {
-        const float g = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    if (sl == 0 && valid) {
+        float v[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            v[i] = red[i][cl];
+#pragma unroll
+        for (int w = S / 2; w > 0; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i)
+                v[i] += v[i + w];
+        const float g = v[0];
         const int c = col / (KK + 1), tap = col - c * (KK + 1);
         if (tap < KK) {
             if (dw)
@@ -776,6 +789,8 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
                             dim3((unsigned)pl.grid), dim3(256), pl.lds_bytes, st, x, dy, part, g);
     } else if (pl.kind == KIND_WGRAD_STREAM_NCHW) {
         st1 = launch_wgrad_stream_nchw(p, pl, x, dy, part, st);
+    } else if (pl.kind == KIND_WGRAD_STREAM_NHWC) {
+        st1 = launch_wgrad_stream_nhwc(p, pl, x, dy, part, st);
     } else if (pl.kind == KIND_WGRAD_DIRECT) {
         WgradGenArgs g;
         g.N = p.N; g.C = p.mult * p.C; g.mult = p.mult;
@@ -792,7 +807,14 @@ int launch_wgrad(const Problem &p, const Plan &pl, const float *x, const float *
     }
     if (st1 != DWCONV_OK)
         return st1;
-    return launch_kernel(&k_wgrad_reduce, dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw,
+    const int cols = p.mult * p.C * (p.kH * p.kW + 1);
+    if ((pl.red_s != 4 && pl.red_s != 8 && pl.red_s != 16) ||
+        pl.grid2 != (cols + 256 / pl.red_s - 1) / (256 / pl.red_s))
+        return DWCONV_ERR_BAD_STRATEGY;
+    return launch_kernel(pl.red_s == 16  ? &k_wgrad_reduce<16>
+                         : pl.red_s == 8 ? &k_wgrad_reduce<8>
+                                         : &k_wgrad_reduce<4>,
+                         dim3((unsigned)pl.grid2), dim3(256), 0, st, part, dw,
                          db, (int)pl.chunks, p.mult * p.C, p.kH * p.kW, w_upd,
                          w_upd ? b_upd : nullptr, lr);
 }

@@ -253,8 +253,13 @@ def test_weight_grad_workspace_and_plans():
     d = dw.dwconv2d_weight_grad_workspace_size(1, 512, 512, 256, 3, 3,
                                                 strategy=dw.STRATEGY_DIRECT)
     assert d > 0 and d % (4 * 256 * 10) == 0
-    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7)
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7,
+                                      strategy=dw.STRATEGY_TILED)
     assert name.startswith("wgrad_tiled_nhwc") and "_l1_" in name    # any C, 4-byte staging
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7)
+    assert name.startswith("wgrad_stream_nhwc")                      # AUTO: enough waves
+    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 30, 19, 131, 7, 7)
+    assert name.startswith("wgrad_tiled_nhwc")                       # AUTO: too few waves
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 3, 3, stride=2)
     assert name.startswith("wgrad_tiled_nhwc_s2")
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 7, 7, stride=2)

@@ -91,34 +91,35 @@ def test_stream_matches_oracle(torch, oracle_mod, layout, k, d, shape, pads, op)
             assert np.all(err <= 1e-5 * S + 1e-6), f"max err/bound {np.max(err / (1e-5 * S + 1e-6))}"
 
 
-WG_CASES = [(k, d, shp, pads) for (k, d) in ((7, 1), (7, 2)) for shp in SHAPES + [(2, 40, 33, 5)]
-            for pads in PADS]
+WG_CASES = [(l, k, d, shp, pads) for l in (NHWC, NCHW) for (k, d) in ((7, 1), (7, 2))
+            for shp in SHAPES + [(2, 40, 33, 5)] for pads in PADS]
 
 
-@pytest.mark.parametrize("k,d,shape,pads", WG_CASES,
-                         ids=[_cid((NCHW, k, d, shp, pads, "wgrad")) for k, d, shp, pads in WG_CASES])
-def test_stream_weight_grad_matches_oracle(torch, oracle_mod, k, d, shape, pads):
-    """The row-streaming NCHW weight and bias gradients: integer inputs bit
-    for bit, random inputs within the bound (the lane sums of each plane are
-    added in a fixed tree order, the chunks by the fixed-order reduction)."""
+@pytest.mark.parametrize("layout,k,d,shape,pads", WG_CASES,
+                         ids=[_cid((l, k, d, shp, pads, "wgrad")) for l, k, d, shp, pads in WG_CASES])
+def test_stream_weight_grad_matches_oracle(torch, oracle_mod, layout, k, d, shape, pads):
+    """The row-streaming weight and bias gradients: integer inputs bit for
+    bit, random inputs within the bound (NCHW: the lane sums of each plane
+    added in a fixed tree order; NHWC: the four waves of a workgroup added
+    in wave order; the chunks by the fixed-order reduction)."""
     N, H, W, C = shape
     pads = _pads(pads, H, W, k, d)
     try:
         dw.dwconv2d_out_extents(H, W, k, k, 1, d, pads)
     except dw.DwconvError:
         pytest.skip("no output position with these pads")
-    name = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, N, H, W, C, k, k, 1, d, pads, 1, NCHW, 0,
+    name = dw.dwconv2d_describe_ex(dw.OP_WEIGHT_GRAD, N, H, W, C, k, k, 1, d, pads, 1, layout, 0,
                                    False, dw.STRATEGY_STREAM)[0]
-    print(f"\n[case] wgrad {k}x{k} d{d} {shape} {pads} kernel={name}", flush=True)
-    assert name.startswith("wgrad_stream_nchw")
+    print(f"\n[case] wgrad {LNAME[layout]} {k}x{k} d{d} {shape} {pads} kernel={name}", flush=True)
+    assert name.startswith("wgrad_stream_" + LNAME[layout])
     wl = wlmod.Workload(name="streamwg", N=N, H=H, W=W, C=C, kH=k, kW=k, dilation=d, pads=pads,
                         x_dist="uniform1", w_dist="uniform1", dy_dist="uniform1")
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
     for integer in (True, False):
-        inp = wlmod.make_inputs(wl, NCHW, seed=k + d, integer=integer)
-        rW, SW = oracle_mod.weight_grad_general(inp["x"], inp["dy"], k, k, 1, d, pads, 1, NCHW)
-        rb, Sb = oracle_mod.bias_grad(inp["dy"], NCHW)
-        gW, gb = dw.weight_grad(dev(inp["x"]), dev(inp["dy"]), k, k, 1, d, NCHW,
+        inp = wlmod.make_inputs(wl, layout, seed=k + d, integer=integer)
+        rW, SW = oracle_mod.weight_grad_general(inp["x"], inp["dy"], k, k, 1, d, pads, 1, layout)
+        rb, Sb = oracle_mod.bias_grad(inp["dy"], layout)
+        gW, gb = dw.weight_grad(dev(inp["x"]), dev(inp["dy"]), k, k, 1, d, layout,
                                 strategy=dw.STRATEGY_STREAM, pads=pads)
         torch.cuda.synchronize()
         gW, gb = gW.cpu().numpy(), gb.cpu().numpy()

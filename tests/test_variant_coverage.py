@@ -70,6 +70,8 @@ def _expected_prefixes():
         out[f"stream_nchw_s1_k{kh}x{kw}_d{d}_px{px}_th{th}_nl{nl}_"] = "kStreamNchwVariants"
     for kh, kw, d, th, nl, nb, minw in _table(src, "kWgradStreamVariants", 7):
         out[f"wgrad_stream_nchw_s1_k{kh}x{kw}_d{d}_th{th}_nl{nl}_"] = "kWgradStreamVariants"
+    for kh, kw, d, px, th, nb, minw in _table(src, "kWgradStreamNhwcVariants", 7):
+        out[f"wgrad_stream_nhwc_s1_k{kh}x{kw}_d{d}_px{px}_th{th}"] = "kWgradStreamNhwcVariants"
     return out
 
 
