@@ -538,7 +538,8 @@ def _row_matcher(dw, wl, layout, op):
            "stream_nhwc": "k_stream_nhwc", "stream_nchw": "k_stream_nchw",
            "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
            "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc", "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
-           "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_direct": "k_wgrad_gen"}
+           "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_stream_nhwc": "k_wgrad_stream_nhwc",
+           "wgrad_direct": "k_wgrad_gen"}
     kfam = next((v for k, v in sorted(fam.items(), key=lambda kv: -len(kv[0]))
                  if kname.startswith(k)), None)
     # the tiled and streaming kernels' mode: 0 forward, 1 input gradient,
@@ -729,6 +730,151 @@ def trace_table(csv_path, detail_path, out_path=None):
     return text
 
 
+def detail_table(detail_path, out_path=None):
+    """The per-workload table of a `bench.py` detail file as markdown, with
+    the run's floors, ceilings, CPU baseline and graph leg.  No GPU needed."""
+    with open(detail_path) as f:
+        d = json.load(f)
+    res = d.get("result", {})
+    lines = []
+    if res:
+        roof = res.get("roofline", {})
+        lines += [f"Headline: {res.get('config', {}).get('workload')} {res.get('config', {}).get('layout')}"
+                  f" fwd + ig, {res.get('value')} {res.get('unit')} ({res.get('ms_per_step')} ms per "
+                  f"step); dominant kernel `{roof.get('kernel')}` {roof.get('avg_launch_us')} us per "
+                  f"launch = {roof.get('achieved')} GB/s = {roof.get('frac')} of 8 TB/s.", ""]
+    lf = d.get("launch_floor")
+    if lf:
+        lines += [f"Launch floor: empty kernel back to back {lf['empty_launch_us']} us; one launch "
+                  f"between two events after the flush {lf['event_pair_us']} us.", ""]
+    ce = d.get("headline_extras", {}).get("ceilings")
+    if ce:
+        lines += [f"Ceilings (headline forward's bytes, {ce['copy_bytes']:,} B): runtime copy "
+                  f"{ce['runtime_copy_us']} us ({ce['runtime_copy_GBs']} GB/s), elementwise copy "
+                  f"{ce['elementwise_copy_us']} us ({ce['elementwise_copy_GBs']} GB/s); headline "
+                  f"kernel at {ce['headline_frac_of_best_copy']} of the better copy.", ""]
+    cb = d.get("cpu_baseline") or res.get("cpu_baseline")
+    if cb:
+        det = cb.get("detail", {})
+        lines += [f"CPU baseline: {cb.get('value')} {cb.get('unit')} on {cb.get('cores')} threads "
+                  f"({det.get('cpu_model', '?')}); {cb.get('sample')}.", ""]
+    g = d.get("graph")
+    if g:
+        lines += [f"Graph leg ({g['workload']}, {g['step']}): eager {g['eager_us_per_step']} us "
+                  f"per step, replayed graph {g['graph_us_per_step']} us per step.", ""]
+    lines += ["Per workload: `us` = amortised device time per call (40 calls alternating two "
+              "buffer sets, median of 3 runs); `cold` = one call after a read-only 1 GiB pass "
+              "(median of 5, an event pair's overhead included); floor = the larger of the HBM "
+              "(8 TB/s) and VALU (78.6 TFLOP/s) floors; copy = a device copy of the same bytes, "
+              "amortised the same way (problems up to 8 MB); CPU = the oracle's timing build on "
+              "all cores (median of 3) and on one thread.", "",
+              "| workload | layout | op | kernel | us | cold us | floor us (bound) | "
+              "floor / us | GB/s | % of 8 TB/s | copy us | CPU us (threads) | CPU 1-thread us |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in d.get("per_config", []):
+        cpu = (f"{r['cpu_us']:,.1f} ({r.get('cpu_threads')})" if "cpu_us" in r else "")
+        lines.append(f"| {r['workload']} | {r['layout']} | {r['op']} | `{r['kernel']}` | "
+                     f"{r['us']} | {r['cold_us']} | {r['floor_us']} ({r['bound']}) | "
+                     f"{r['frac_of_bound']} | {r['GBs']} | {r['pct_hbm_peak']} | "
+                     f"{r.get('copy_same_bytes_us', '')} | {cpu} | "
+                     f"{r.get('cpu_us_1thread', '')} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text
+
+
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVE_CYCLES",
+               "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU")
+
+
+def sq_table(csv_path, detail_path, out_path=None):
+    """Instruction counters per workload row from a rocprofv3 --pmc run of
+    `bench.py --table-only` (the SQ_COUNTERS) and that run's detail file.
+    Per row, medians over the row's dispatches (the weight gradient: its
+    partial-sum kernel): VALU, LDS and SALU instructions per wave, the FMA
+    wave-instructions the op needs per wave (flops / 2 / 64) against the
+    VALU ones, the VALU issue time of the whole launch at one wave64 FMA per
+    4 cycles on each of 1024 SIMDs at 2.4 GHz, and the share of wave cycles
+    spent waiting to issue (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, both in
+    quad-cycles).  No GPU needed."""
+    import csv
+    import depthwise_convolution_amd as dw
+    from depthwise_convolution_amd import workloads
+    by_id = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            did = int(r["Dispatch_Id"])
+            e = by_id.setdefault(did, [r["Kernel_Name"], int(r.get("Grid_Size", "0") or 0), {}])
+            e[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    seq = [tuple(by_id[k]) for k in sorted(by_id)]
+    order = _table_order(detail_path)
+    lines = ["| workload | layout | op | kernel | waves | VALU / wave | FMA / wave | FMA share | "
+             "VALU issue us | LDS / wave | SALU / wave | waiting to issue |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (wl, layout, op), (kname, _, vals) in zip(order, _assign_rows(dw, order, seq)):
+        if not vals or any(c not in vals[0] for c in SQ_COUNTERS):
+            continue
+        med = {c: statistics.median(v[c] for v in vals) for c in SQ_COUNTERS}
+        waves = med["SQ_WAVES"]
+        valu = med["SQ_INSTS_VALU"] / waves
+        fma = op_flops(wl, op) / 2 / 64 / waves
+        issue_us = med["SQ_INSTS_VALU"] * 4 / 1024 / 2.4e3
+        lines.append(f"| {wl.name} | {workloads.LAYOUT_NAMES[layout]} | {op} | `{kname}` | "
+                     f"{waves:.0f} | {valu:.0f} | {fma:.0f} | {fma / valu:.2f} | {issue_us:.2f} | "
+                     f"{med['SQ_INSTS_LDS'] / waves:.0f} | {med['SQ_INSTS_SALU'] / waves:.0f} | "
+                     f"{med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES']:.2f} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text
+
+
+def headline_trace(csv_path, detail_path, out_path=None):
+    """The headline kernels in a rocprofv3 kernel trace of the default
+    `bench.py` run: per-dispatch statistics of the forward and input-gradient
+    kernels against the bench's amortised figure from the same run, and the
+    kernels with the most device time.  No GPU needed."""
+    import depthwise_convolution_amd as dw
+    from depthwise_convolution_amd import workloads
+    with open(detail_path) as f:
+        d = json.load(f)
+    roof = d.get("headline", {}).get("roofline", {})
+    seq = _dispatch_seq(csv_path)
+    wl = workloads.WORKLOADS[HEADLINE]
+    lines = [f"Bench (same run): dominant kernel `{roof.get('kernel')}`, {roof.get('avg_launch_us')} "
+             f"us per launch amortised (40 back-to-back launches over two buffer sets) = "
+             f"{roof.get('achieved')} GB/s, frac {roof.get('frac')} of 8 TB/s.", "",
+             "| op | kernel | dispatches | mean us | median us | min us | GB/s at the median | "
+             "frac of 8 TB/s at the median |", "|---|---|---|---|---|---|---|---|"]
+    for op in ("fwd", "ig"):
+        kname, match = _row_matcher(dw, wl, workloads.NHWC, op)
+        ds = [v for n, g, v in seq if match(n, g)]
+        if not ds:
+            continue
+        med = statistics.median(ds)
+        gbs = op_bytes(wl, op) / med / 1e3
+        lines.append(f"| {op} | `{kname}` | {len(ds)} | {statistics.mean(ds):.2f} | {med:.2f} | "
+                     f"{min(ds):.2f} | {gbs:.1f} | {gbs / PEAK_HBM_GBS:.4f} |")
+    tot = {}
+    for n, g, v in seq:
+        k = (n.replace("(anonymous namespace)::", "").split("(")[0][:90], g)
+        t = tot.setdefault(k, [0.0, 0])
+        t[0] += v
+        t[1] += 1
+    lines += ["", "Kernels by total device time in the trace (name, grid in threads):", "",
+              "| kernel | grid | calls | total ms | mean us |", "|---|---|---|---|---|"]
+    for (n, g), (t, c) in sorted(tot.items(), key=lambda kv: -kv[1][0])[:15]:
+        lines.append(f"| `{n}` | {g} | {c} | {t / 1e3:.2f} | {t / c:.2f} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -748,8 +894,22 @@ def main():
                     help="summarise two --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--traffic-json", default="",
                     help="with --counter-table: also write the headline kernel's traffic file")
+    ap.add_argument("--detail-table", action="store_true",
+                    help="write the detail file's per-workload table as markdown and exit")
+    ap.add_argument("--sq-table", default="", help="summarise an SQ counter CSV and exit")
+    ap.add_argument("--headline-trace", default="",
+                    help="summarise the headline kernels of a kernel-trace CSV and exit")
     ap.add_argument("--out", default="")
     args = ap.parse_args()
+    if args.detail_table:
+        print(detail_table(args.detail, args.out or None))
+        return
+    if args.sq_table:
+        print(sq_table(args.sq_table, args.detail, args.out or None))
+        return
+    if args.headline_trace:
+        print(headline_trace(args.headline_trace, args.detail, args.out or None))
+        return
     if args.trace_table:
         print(trace_table(args.trace_table, args.detail, args.out or None))
         return

@@ -53,5 +53,49 @@ def build(verbose: bool = False, extra_hipcc=()) -> str:
     return LIB
 
 
+def resource_usage():
+    """Per-kernel resources of the gfx950 code as the compiler reports them
+    (its kernel-resource-usage remarks): {demangled name: {"VGPRs", "SGPRs",
+    "LDS", "scratch", "occupancy"}}.  Compiles the kernel files again, device
+    side only, without touching the library."""
+    import re
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    keys = {"VGPRs": "VGPRs", "TotalSGPRs": "SGPRs", "LDS Size [bytes/block]": "LDS",
+            "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy"}
+    out = {}
+    with tempfile.TemporaryDirectory(prefix="dwconv_res_") as tmp:
+        for src in HIP_SOURCES:
+            r = subprocess.run([hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-c",
+                                os.path.join(CSRC, src), "-o", os.path.join(tmp, src + ".o"),
+                                "-Rpass-analysis=kernel-resource-usage"],
+                               check=True, capture_output=True, text=True)
+            name = None
+            for line in r.stderr.splitlines():
+                m = re.search(r"remark:\s+Function Name: (\S+)", line)
+                if m:
+                    name = m.group(1)
+                    out[name] = {}
+                    continue
+                m = re.search(r"remark:\s+([^:]+): (\d+) \[", line)
+                if name and m and m.group(1).strip() in keys:
+                    out[name][keys[m.group(1).strip()]] = int(m.group(2))
+    # GNU c++filt does not know _Float16 (DF16_): demangle it as half, then rename
+    names = [n.replace("DF16_", "Dh") for n in out]
+    dem = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    return {d.replace("dwconv::(anonymous namespace)::", "").replace("half", "_Float16"): v
+            for d, v in zip(dem, out.values())}
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    if "--resources" in sys.argv:
+        res = resource_usage()
+        print("| kernel | VGPRs | SGPRs | LDS bytes / workgroup | scratch bytes / lane | "
+              "waves / SIMD |\n|---|---|---|---|---|---|")
+        for k in sorted(res):
+            v = res[k]
+            print(f"| `{k.split('(')[0]}` | {v.get('VGPRs')} | {v.get('SGPRs')} | {v.get('LDS')} | "
+                  f"{v.get('scratch')} | {v.get('occupancy')} |")
+    else:
+        print(build(verbose=True))
