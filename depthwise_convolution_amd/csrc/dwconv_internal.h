@@ -197,8 +197,14 @@ constexpr WgradVariant kWgradVariants[] = {
     {5, 5, 1, 2, 16, 1, 11, 4},
     {7, 7, 1, 1, 32, 1, 14, 4},
     {7, 7, 2, 1, 32, 1, 22, 4},
-    {1, 15, 1, 4, 32, 1, 2, 4},
-    {1, 31, 1, 2, 32, 1, 2, 4},
+    // 1xK: one-row tiles 24 columns wide (64 channels x 6 columns per
+    // thread): the column halo of a tile is kW - 1 columns, so narrow tiles
+    // stage mostly halo (8 columns: 38 staged for 8 used at 1x31) and split
+    // one-row images into several chunks.  64x1x24x256 1x31, both stages:
+    // 16.4 -> 8.75 us against 8-column, two-row tiles; 64x1x24x128 1x15
+    // 8.9 -> 6.2 us; 1x1x24x256 1x31 7.5 -> 6.6 us.
+    {1, 15, 1, 1, 64, 6, 1, 4},
+    {1, 31, 1, 1, 64, 6, 1, 4},
     // 4-byte staging (lv = 1): any channel count
     {3, 3, 1, 1, 32, 1, 10, 1}, {5, 5, 1, 1, 32, 1, 12, 1},
     {7, 7, 1, 1, 32, 1, 16, 1}, {7, 7, 2, 1, 32, 1, 22, 1},
