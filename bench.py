@@ -575,16 +575,24 @@ def _assign_rows(dw, order, seq):
     """Split `seq`, the trace's dispatches in issue order as (kernel name,
     grid threads, value), over `order`, the (workload, layout, op) rows in
     the order the table ran them: a row takes the run of dispatches that
-    match its kernel from its first match on, skipping other programs'
-    kernels (flush, copies, spin) and the fixed-order weight-gradient
-    reduction, up to the first dwconv kernel it does not launch.  Adjacent
-    rows always differ in layout or op, hence in kernel.  Returns one
-    (reported name, trace name, values) per row."""
+    match its kernel, skipping other programs' kernels (flush, copies, spin)
+    and the fixed-order weight-gradient reduction, up to the first dwconv
+    kernel it does not launch.  The first row may start after other dwconv
+    kernels (the legs that run before the table); every later row starts
+    with the next dwconv kernel after the row before it, or has no
+    dispatches.  Adjacent rows always differ in layout or op, hence in
+    kernel.  Returns one (reported name, trace name, values) per row."""
+    def own_kernel(n):
+        return "dwconv::" in n and "k_wgrad_reduce" not in n
+
     out, cursor = [], 0
-    for wl, layout, op in order:
+    for r, (wl, layout, op) in enumerate(order):
         kname, match = _row_matcher(dw, wl, layout, op)
         i = cursor
         while i < len(seq) and not match(seq[i][0], seq[i][1]):
+            if r > 0 and own_kernel(seq[i][0]):
+                i = len(seq)              # another row's kernel: this row ran nothing
+                break
             i += 1
         if i == len(seq):
             out.append((kname, None, []))
@@ -594,7 +602,7 @@ def _assign_rows(dw, order, seq):
             n, g, v = seq[j]
             if match(n, g):
                 vals.append(v)
-            elif "dwconv::" in n and "k_wgrad_reduce" not in n:
+            elif own_kernel(n):
                 break
             j += 1
         out.append((kname, tname, vals))
