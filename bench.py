@@ -577,21 +577,24 @@ def _assign_rows(dw, order, seq):
     the order the table ran them: a row takes the run of dispatches that
     match its kernel, skipping other programs' kernels (flush, copies, spin)
     and the fixed-order weight-gradient reduction, up to the first dwconv
-    kernel it does not launch.  The first row may start after other dwconv
-    kernels (the legs that run before the table); every later row starts
-    with the next dwconv kernel after the row before it, or has no
-    dispatches.  Adjacent rows always differ in layout or op, hence in
-    kernel.  Returns one (reported name, trace name, values) per row."""
+    kernel it does not launch.  A row that meets the next row's kernel
+    before its own ran nothing (it takes no later row's dispatches of a
+    kernel the two share); dispatches no row claims (legs before the table,
+    a trace of an older plan) are skipped.  Adjacent rows always differ in
+    layout or op, hence in kernel.  Returns one (reported name, trace name,
+    values) per row."""
     def own_kernel(n):
         return "dwconv::" in n and "k_wgrad_reduce" not in n
 
+    matchers = [_row_matcher(dw, wl, layout, op) for wl, layout, op in order]
     out, cursor = [], 0
-    for r, (wl, layout, op) in enumerate(order):
-        kname, match = _row_matcher(dw, wl, layout, op)
+    for r in range(len(order)):
+        kname, match = matchers[r]
+        nxt = matchers[r + 1][1] if r > 0 and r + 1 < len(order) else None
         i = cursor
         while i < len(seq) and not match(seq[i][0], seq[i][1]):
-            if r > 0 and own_kernel(seq[i][0]):
-                i = len(seq)              # another row's kernel: this row ran nothing
+            if nxt is not None and nxt(seq[i][0], seq[i][1]):
+                i = len(seq)              # the next row's kernel: this row ran nothing
                 break
             i += 1
         if i == len(seq):
