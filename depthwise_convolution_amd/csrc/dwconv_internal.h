@@ -145,7 +145,7 @@ constexpr int kNumStreamVariants = sizeof(kStreamVariants) / sizeof(kStreamVaria
 // (no LDS row) measured 29-45 us: 5x the L1 requests per FMA of NHWC.
 struct StreamNchwVariant { int kH, kW, d, px, th, nl, nb, minw; };
 constexpr StreamNchwVariant kStreamNchwVariants[] = {
-    {7, 7, 1, 1, 30, 2, 6, 1024}, {7, 7, 2, 1, 15, 2, 6, 128},
+    {7, 7, 1, 1, 30, 2, 6, 1024}, {7, 7, 2, 1, 15, 2, 6, 64},
 };
 constexpr int kNumStreamNchwVariants = sizeof(kStreamNchwVariants) / sizeof(kStreamNchwVariants[0]);
 
@@ -162,7 +162,7 @@ constexpr int kStreamNchwSlot = 256;
 // 16.0 us); half the rows per unit measured 12-40% slower.
 struct WgradStreamVariant { int kH, kW, d, th, nl, nb, minw; };
 constexpr WgradStreamVariant kWgradStreamVariants[] = {
-    {7, 7, 1, 30, 2, 6, 1024}, {7, 7, 2, 15, 2, 6, 128},
+    {7, 7, 1, 30, 2, 6, 1024}, {7, 7, 2, 15, 2, 6, 64},
 };
 constexpr int kNumWgradStreamVariants =
     sizeof(kWgradStreamVariants) / sizeof(kWgradStreamVariants[0]);
