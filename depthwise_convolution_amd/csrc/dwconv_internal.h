@@ -237,7 +237,7 @@ constexpr long long kXcdRangeMaxBytes = 448LL << 20;
 // columns per workgroup), above it over 8 (32 columns, whole 128-byte runs
 // per load).  Measured against 4 slices of 64 columns (the earlier shape):
 // 64x30x19x128 7x7 NHWC (384 chunks) 21.6 -> 19.6 us, 7x7 d2 NCHW 38.2 ->
-// 36.9 us, 64x1x24x256 1x31 NHWC 17.2 -> 16.4 us, 8x224x224x32 3x3 s2 NHWC
+// 36.9 us, 64x1x24x256 1x31 NHWC 17.2 -> 16.4 us, 1x224x224x32 3x3 s2 NHWC
 // (320 columns, 266 chunks) 9.7 -> 7.8 us with 16 slices; within 3% on the
 // rest of the workloads.
 constexpr int kReduceFewColumns = 512;
