@@ -354,6 +354,10 @@ struct Plan {
     long long workspace;// weight gradient: workspace bytes
     long long grid2;    // weight gradient: workgroups of the reduction kernel
     int red_s;          // weight gradient: chunk slices per reduction workgroup (4 or 16)
+    int tail_cl;        // row-streaming NHWC: channels per lane group of the tail tile (0 =
+                        // none; nct then counts every channel tile)
+    int tail_ncg;       // row-streaming NHWC: column groups per sub-grid row of the tail tile
+    long long tail_units;// row-streaming NHWC: units (waves) of the tail tile
     int pH, pW;
     int IH, IW, OH, OW; // extents of the tensor read (in) and written (out) by this op
                         // (tiled NHWC stride-2 forward: OH, OW = the stride-1 grid it tiles)

@@ -319,7 +319,7 @@ static bool plan_stream_nhwc(const Problem &p, Plan *pl)
     // byte offsets within a row (the lane's columns, up to (kW-1)*d past the
     // row on either side) and row starts within an image are 32-bit
     const long long cb = 4LL * p.C;
-    if (cb * (std::max(pl->IW, pl->OW) + 2LL * v.d * v.kW + 2LL * v.px * v.d) >= (1LL << 31) ||
+    if (cb * (std::max(pl->IW, pl->OW) + 2LL * v.d * v.kW + 8LL * v.px * v.d) >= (1LL << 31) ||
         cb * pl->IH * pl->IW >= (1LL << 31) || cb * pl->OH * pl->OW >= (1LL << 31) ||
         4LL * p.C * p.kH * p.kW >= (1LL << 31))
         return false;
@@ -331,20 +331,41 @@ static bool plan_stream_nhwc(const Problem &p, Plan *pl)
     pl->cl = v.cl;
     pl->tw = v.px * (64 / v.cl);                  // output columns of a wave
     pl->th = v.th;
-    pl->nct = ceil_div(p.C, v.cl);
+    // the last C % cl channels, when they fill at most half of a tile, take a
+    // tail tile of 16 or 32 channels per lane group (4 or 2 column groups,
+    // so 4x or 2x fewer waves for them).  Measured at 64x30x19xC 7x7
+    // (forward, against full-width tiles only): 16 lanes win 3-14% with at
+    // most one full tile or C % 4 == 0 (C = 3, 65, 67, 132, 136, 144) but
+    // lose 3-12% with two or more full tiles and C % 4 != 0 (C = 129-139),
+    // where 32 lanes win 9-10% (C = 129-139, 147, 150); with three or more
+    // full tiles and odd C both lose (C = 195, 259: +4.5% with 32 lanes),
+    // and with dilation 2 (the phase sub-grid is narrower than a 16-lane
+    // wave's columns) they lose 2-8%.
+    const int rem = p.C % v.cl, full = p.C / v.cl;
+    pl->tail_cl = 0;
+    if (rem != 0 && 2 * rem <= v.cl && d == 1 && full <= 2)
+        pl->tail_cl = (rem <= 16 && (p.C % 4 == 0 || full <= 1)) ? 16 : 32;
+    if (pl->tail_cl >= v.cl)
+        pl->tail_cl = 0;
+    pl->nct = pl->tail_cl ? p.C / v.cl : ceil_div(p.C, v.cl);
     pl->nwt = ceil_div(ows, pl->tw);
     pl->nst = ceil_div(ohs, v.th);
     pl->pb = d * d;                               // phases
     pl->YH = pl->OH;
     pl->YW = pl->OW;
     pl->total = (long long)p.N * pl->nst * pl->pb * pl->nwt;      // wave units per channel tile
+    pl->tail_ncg = pl->tail_cl ? ceil_div(ows, v.px * (64 / pl->tail_cl)) : 0;
+    pl->tail_units = (long long)p.N * pl->nst * pl->pb * pl->tail_ncg;
     if (pl->total * 4 >= (1LL << 31))
         return false;
-    pl->grid = pl->nct * ((pl->total + 3) / 4);
+    pl->grid = pl->nct * ((pl->total + 3) / 4) + (pl->tail_units + 3) / 4;
     pl->block = 256;
     pl->xcd = xcd_ranges(p);
-    std::snprintf(pl->name, sizeof pl->name, "stream_nhwc_s1_k%dx%d_d%d_cl%d_px%d_th%d_%s_%s",
-                  v.kH, v.kW, v.d, v.cl, v.px, v.th, op_tag(p), p.wtype ? "f16w" : "f32w");
+    char tail[8] = "";
+    if (pl->tail_cl)
+        std::snprintf(tail, sizeof tail, "t%d_", pl->tail_cl);
+    std::snprintf(pl->name, sizeof pl->name, "stream_nhwc_s1_k%dx%d_d%d_cl%d_px%d_th%d_%s%s_%s",
+                  v.kH, v.kW, v.d, v.cl, v.px, v.th, tail, op_tag(p), p.wtype ? "f16w" : "f32w");
     return true;
 }
 
@@ -459,7 +480,7 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         Plan t = *pl;
         const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
         if (nhwc ? plan_stream_nhwc(p, &t) : plan_stream_nchw(p, &t)) {
-            const long long waves = nhwc ? t.nct * t.total : t.total;
+            const long long waves = nhwc ? t.nct * t.total + t.tail_units : t.total;
             const int minw = nhwc ? kStreamVariants[t.variant].minw
                                   : kStreamNchwVariants[t.variant].minw;
             if (waves >= minw) {
@@ -799,7 +820,7 @@ int make_wgrad_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         Plan t = *pl;
         const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
         if (nhwc ? plan_wgrad_stream_nhwc(p, &t) : plan_wgrad_stream_nchw(p, &t)) {
-            const long long waves = nhwc ? t.nct * t.total : t.total;
+            const long long waves = nhwc ? t.nct * t.total + t.tail_units : t.total;
             const int minw = nhwc ? kWgradStreamNhwcVariants[t.variant].minw
                                   : kWgradStreamVariants[t.variant].minw;
             if (strategy == DWCONV_STRATEGY_STREAM || waves >= minw) {

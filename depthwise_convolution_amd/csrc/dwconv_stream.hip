@@ -49,6 +49,9 @@ struct StreamArgs {
     int ncg, nrt, nph;      // column groups per sub-grid row, row tiles, phases (D*D)
     int upc;                // units per channel tile: N * nrt * nph * ncg
     int xcd;                // workgroup order: 1 = per-XCD ranges (xcd_tile), 0 = in order
+    int mblk;               // forward / input gradient: workgroups of the nct CL-wide tiles
+    int tcl, tncg, tupc;    // ... and of the tail tile: its channels per lane group (0 =
+                            // none), column groups per sub-grid row, units
 };
 
 __device__ __forceinline__ int floor_div(int a, int b)
@@ -56,12 +59,16 @@ __device__ __forceinline__ int floor_div(int a, int b)
     return (a >= 0 ? a : a - b + 1) / b;
 }
 
+// One workgroup's work: 4 units (waves) of the channel tile that starts at
+// channel c0, with CL channels x 64/CL column groups per wave; `ncg` column
+// blocks per sub-grid row, `upc` units in the tile.  `wl` holds at least
+// CL * kH * kW floats.  Every thread of the workgroup calls it (a barrier).
 template <typename WT, int KH, int KW, int D, int CL, int PX, int TH, int NB, int MODE>
-__global__ __launch_bounds__(256) void k_stream_nhwc(const float *__restrict__ in,
-                                                     const void *__restrict__ wv,
-                                                     const float *__restrict__ bias,
-                                                     float *__restrict__ out, StreamArgs a,
-                                                     EpiArgs ep)
+__device__ __forceinline__ void stream_nhwc_tile(const float *__restrict__ in, const WT *w,
+                                                 const float *__restrict__ bias,
+                                                 float *__restrict__ out, const StreamArgs &a,
+                                                 const EpiArgs &ep, float *wl, int c0,
+                                                 int unit, int ncg, int upc)
 {
     constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
     constexpr int KK = KH * KW, G = TH + KH - 1, XW = PX + KW - 1;
@@ -69,26 +76,17 @@ __global__ __launch_bounds__(256) void k_stream_nhwc(const float *__restrict__ i
     static_assert(NB >= 2, "at least one row in flight");
     constexpr int NWL = (CL * KK + 255) / 256;
     static_assert(CL == 16 || CL == 32 || CL == 64, "channels per lane group");
-    __shared__ float wl[NWL * 256];
-    const WT *w = reinterpret_cast<const WT *>(wv);
-    // the workgroup's place: per-XCD ranges put the row tiles of an image,
-    // which share kH - 1 halo rows, on one XCD and so in one L2
-    const int blk = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-    const int ct = blk % a.nct;
     const int lane = threadIdx.x & 63;
     const int ch = lane % CL, cs = lane / CL;          // channel in the tile, column group
-    // the wave's unit (wave-uniform); a wave past the last unit only helps
-    // stage the weights
-    const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 +
-                                                    (int)(threadIdx.x >> 6));
-    const bool live = unit < a.upc;
-    const int c0 = ct * CL, c = c0 + ch;
+    // a wave past the last unit only helps stage the weights
+    const bool live = unit < upc;
+    const int c = c0 + ch;
     const bool cok = c < a.C;
 
     // 1. the unit: column block (fastest), phase, row tile, image
     int t = live ? unit : 0;
-    const int cg = t % a.ncg;
-    t /= a.ncg;
+    const int cg = t % ncg;
+    t /= ncg;
     const int ph = t % a.nph;
     t /= a.nph;
     const int rt = t % a.nrt;
@@ -200,6 +198,68 @@ __global__ __launch_bounds__(256) void k_stream_nhwc(const float *__restrict__ i
             for (int jj = 0; jj < PX; ++jj)
                 v[jj] = bv;
         }
+    }
+}
+
+// Position of workgroup L of the merged order: the tail workgroups (bt of
+// them) are spread among the mblk main ones in proportion, segment j being
+// main workgroups [j*mblk/bt, (j+1)*mblk/bt) followed by tail workgroup j.
+// Returns the main workgroup index, or -1 - j for tail workgroup j.
+__device__ __forceinline__ int merged_block(int L, int mblk, int bt)
+{
+    if (bt == 0)
+        return L;
+    auto start = [&](int j) { return (int)((long long)j * mblk / bt) + j; };
+    int j = (int)((long long)L * bt / (mblk + bt));
+    while (j + 1 < bt && start(j + 1) <= L)
+        ++j;
+    while (j > 0 && start(j) > L)
+        --j;
+    const int m_end = (int)((long long)(j + 1) * mblk / bt);   // main workgroups before tail j
+    return L - j < m_end ? L - j : -1 - j;
+}
+
+// The kernel: the main workgroups (mblk of them) run the nct channel tiles of
+// CL channels (channel tile fastest, so the tiles of one place run
+// together), the others the narrow tail tile of tcl < CL channels (channels
+// nct*CL onwards, the last C % CL of them), whose wider column groups need
+// fewer units: a few leftover channels take a few lanes of 4x or 2x fewer
+// waves instead of a few lanes of a full 64-lane unit per place.  The tail
+// workgroups are interleaved with the main ones in proportion, so that an
+// XCD's range holds the tail of the images whose main tiles it runs (the
+// tail channels share cache lines with the next pixel's first channels).
+template <typename WT, int KH, int KW, int D, int CL, int PX, int TH, int NB, int MODE>
+__global__ __launch_bounds__(256) void k_stream_nhwc(const float *__restrict__ in,
+                                                     const void *__restrict__ wv,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ out, StreamArgs a,
+                                                     EpiArgs ep)
+{
+    __shared__ float wl[(CL * KH * KW + 255) / 256 * 256];
+    const WT *w = reinterpret_cast<const WT *>(wv);
+    // the workgroup's place: per-XCD ranges put the row tiles of an image,
+    // which share kH - 1 halo rows, on one XCD and so in one L2
+    const int L = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int blk = merged_block(L, a.mblk, (int)gridDim.x - a.mblk);
+    const int wave = (int)(threadIdx.x >> 6);
+    if (blk >= 0) {
+        const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 + wave);
+        stream_nhwc_tile<WT, KH, KW, D, CL, PX, TH, NB, MODE>(
+            in, w, bias, out, a, ep, wl, (blk % a.nct) * CL, unit, a.ncg, a.upc);
+        return;
+    }
+    const int unit = __builtin_amdgcn_readfirstlane((-1 - blk) * 4 + wave);
+    if constexpr (CL > 16) {
+        if (a.tcl == 16) {
+            stream_nhwc_tile<WT, KH, KW, D, 16, PX, TH, NB, MODE>(
+                in, w, bias, out, a, ep, wl, a.nct * CL, unit, a.tncg, a.tupc);
+            return;
+        }
+    }
+    if constexpr (CL > 32) {
+        if (a.tcl == 32)
+            stream_nhwc_tile<WT, KH, KW, D, 32, PX, TH, NB, MODE>(
+                in, w, bias, out, a, ep, wl, a.nct * CL, unit, a.tncg, a.tupc);
     }
 }
 
@@ -793,6 +853,12 @@ int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const 
     static const StreamTable table;
     if (p.mult != 1 || p.stride != 1 || pl.variant < 0 || pl.variant >= kNumStreamVariants)
         return DWCONV_ERR_BAD_STRATEGY;
+    const StreamVariant &v = kStreamVariants[pl.variant];
+    const long long mblk = pl.nct * ((pl.total + 3) / 4);
+    if (pl.cl != v.cl || (pl.tail_cl != 0 && pl.tail_cl != 16 && pl.tail_cl != 32) ||
+        pl.tail_cl >= v.cl || (pl.tail_cl == 0) != (pl.tail_units == 0) ||
+        pl.nct * v.cl + pl.tail_cl < p.C || pl.grid != mblk + (pl.tail_units + 3) / 4)
+        return DWCONV_ERR_BAD_STRATEGY;       // the tiles must cover the channels
     StreamFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
     StreamArgs a;
     a.C = p.C;
@@ -801,6 +867,8 @@ int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const 
     a.nct = pl.nct; a.ncg = pl.nwt; a.nrt = pl.nst; a.nph = pl.pb;
     a.upc = (int)pl.total;
     a.xcd = pl.xcd;
+    a.mblk = (int)mblk;
+    a.tcl = pl.tail_cl; a.tncg = pl.tail_ncg; a.tupc = (int)pl.tail_units;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }
@@ -843,6 +911,8 @@ int launch_wgrad_stream_nhwc(const Problem &p, const Plan &pl, const float *x, c
     a.nct = pl.nct; a.ncg = pl.nwt; a.nrt = pl.nst; a.nph = pl.pb;
     a.upc = (int)pl.total;
     a.xcd = pl.xcd;
+    a.mblk = (int)pl.grid;
+    a.tcl = a.tncg = a.tupc = 0;
     return launch_kernel(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy,
                          part, a);
 }

@@ -181,8 +181,10 @@ def test_tiled_grid_covers_problem(wl_name):
 def test_stream_grid_covers_problem(wl_name):
     """The row-streaming grid: per channel tile, one wave per (image, row
     tile, dilation phase, column block) of the phase sub-grid (rows and
-    columns d apart), four waves per workgroup; AUTO takes it only with at
-    least 1024 waves."""
+    columns d apart), four waves per workgroup; with dilation 1 and at most
+    two full tiles, the last C % 64 channels, when at most 32, form a tail
+    tile of 16 or 32 channels per lane group whose waves span 4 or 2 column
+    blocks; AUTO takes it only with at least 1024 waves."""
     from depthwise_convolution_amd.workloads import WORKLOADS
     wl = WORKLOADS[wl_name]
     name, grid, block = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
@@ -195,11 +197,17 @@ def test_stream_grid_covers_problem(wl_name):
     th = int(re.search(r"_th(\d+)_", name).group(1))
     hs, ws = -(-wl.H // d), -(-wl.W // d)
     units = wl.N * -(-hs // th) * d * d * -(-ws // (px * 64 // cl))
-    nct = -(-wl.C // cl)
-    assert grid == nct * -(-units // 4)
+    rem, full = wl.C % cl, wl.C // cl
+    tcl = 0
+    if rem and 2 * rem <= cl and d == 1 and full <= 2:
+        tcl = 16 if rem <= 16 and (wl.C % 4 == 0 or full <= 1) else 32
+    assert (f"_t{tcl}_" in name) == (tcl > 0)
+    nct = wl.C // cl if tcl else -(-wl.C // cl)
+    tunits = wl.N * -(-hs // th) * d * d * -(-ws // (px * 64 // tcl)) if tcl else 0
+    assert grid == nct * -(-units // 4) + -(-tunits // 4)
     auto = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride,
                                 wl.dilation)[0]
-    assert auto.startswith("stream_") == (nct * units >= 1024)
+    assert auto.startswith("stream_") == (nct * units + tunits >= 1024)
     # NCHW: lanes along plane columns, planes packed per wave
     name, grid, _ = dw.dwconv2d_describe(dw.OP_FWD, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW,
                                          wl.stride, wl.dilation, dw.NCHW,

@@ -1,6 +1,7 @@
 """GPU parity of the row-streaming kernels (strategy STREAM, both layouts).
 
-Shapes with ragged channel tiles (a prime channel count), images narrower
+Shapes with ragged channel tiles (a prime channel count; NHWC tail tiles of
+16 and 32 channels per lane group, alone and after full tiles), images narrower
 and shorter than a wave's columns and rows, a single row or column, planes
 wider than 64 lane groups, SAME / asymmetric / cropping pads, dilation 1 and
 2 (the phase split), forward, input gradient and the fused BatchNorm + ReLU6
@@ -18,7 +19,7 @@ from depthwise_convolution_amd.workloads import NHWC, NCHW
 pytestmark = pytest.mark.gpu
 LNAME = {NHWC: "nhwc", NCHW: "nchw"}
 SHAPES = [(2, 13, 19, 131), (1, 30, 19, 128), (3, 7, 5, 64), (1, 1, 24, 40), (2, 9, 1, 70),
-          (1, 9, 150, 3), (1, 70, 9, 2)]
+          (1, 9, 150, 3), (1, 70, 9, 2), (2, 11, 23, 91), (1, 5, 47, 24)]
 PADS = ["same", (0, 3, 2, 1), (-1, 2, 0, 0)]
 
 
