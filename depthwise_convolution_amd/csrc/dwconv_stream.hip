@@ -378,13 +378,16 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
     }
     // weights (reversed taps for the input gradient) and bias of the lane's channel
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    // one per-lane base, the tap a constant on top (folded into the loads'
+    // immediate offsets; an out-of-range base stays out of range)
+    const int wb = pok ? c * KK : kOutOfRange / 4;
     float wr[KH][KW];
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
         for (int kw = 0; kw < KW; ++kw) {
             const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
-            wr[kh][kw] = buf_w(rw, pok ? c * KK + tap : kOutOfRange / 4, (WT *)nullptr);
+            wr[kh][kw] = buf_w(rw, wb + tap, (WT *)nullptr);
         }
     const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
                                    : 0.0f;
@@ -407,12 +410,14 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
             slots[u % 2][dst[i]] = st[u % NB][i];
         if (u + NB - 1 < G)
             load_row(u + NB - 1, st[(u + NB - 1) % NB]);
-        const int ir = D * (i0 + tr + u) + br;
-        if ((unsigned)ir < (unsigned)a.IH) {
-            float x[XW];
+        // keep the loads NB - 1 rows ahead: the scheduler would otherwise
+        // sink them towards their use to save registers
+        __builtin_amdgcn_sched_barrier(0);
+        float x[XW];
 #pragma unroll
-            for (int k = 0; k < XW; ++k)
-                x[k] = slots[u % 2][rd + k];
+        for (int k = 0; k < XW; ++k)
+            x[k] = slots[u % 2][rd + k];
+        {
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh) {
                 const int m = u - kh;
