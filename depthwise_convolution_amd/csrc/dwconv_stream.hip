@@ -599,9 +599,8 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restri
 // dilation phase) keeps its last kH dy values in registers; each x row u
 // read from LDS meets dy rows u - kh, kh < kH, and is added into the lane's
 // kH*kW tap sums (and dy into the bias sum).  At the end the LPR lanes of
-// each plane are added in a fixed tree order through lane permutes, and one
-// lane per plane writes the plane's KK + 1 sums as a chunk of the partial
-// sums part[chunk][c][tap], chunk = the unit's (image, phase, row tile,
+// each plane are added in lane order through the wave's LDS, and the plane's
+// KK + 1 sums are written as a chunk of the partial sums part[chunk][c][tap], chunk = the unit's (image, phase, row tile,
 // column block); the fixed-order reduction kernel adds the chunks.
 // ---------------------------------------------------------------------------
 template <int KH, int KW, int D, int TH, int NL, int NB>
@@ -688,8 +687,11 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
             if (u + NB - 1 < TH)
                 load_dy(u + NB - 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (u < TH)
             acc[KK] += gv[u % RG];                    // the bias sum
+        // rows outside the planes are skipped (here, unlike the forward walk,
+        // running their FMAs on the zeros in LDS measured 256 registers)
         const int ir = D * (i0 + tr + u) + br;
         if ((unsigned)ir < (unsigned)a.IH) {
             float xv[XW];
@@ -707,30 +709,41 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
             }
         }
     }
-    // add the lpr lanes of each plane (a fixed tree over lane offsets 32 .. 1,
-    // within the plane's lanes), then the plane's first lane writes its chunk
-    const bool keep[6] = {cgl + 32 < a.lpr, cgl + 16 < a.lpr, cgl + 8 < a.lpr,
-                          cgl + 4 < a.lpr, cgl + 2 < a.lpr, cgl + 1 < a.lpr};
+    // add the lpr lanes of each plane through the wave's own ring (no other
+    // wave touches it; a wave's LDS operations run in order): in rounds of QB
+    // sums, every lane parks its QB sums (sum q at q * 65 + lane), then output
+    // o < ppw * QB adds plane o / QB's lpr values of sum o % QB in lane order
+    // and is stored into the plane's chunk of the partial sums.  Every lane
+    // runs the same read iterations and only the store is predicated: the
+    // reads of a round must precede the next round's writes in the wave, and
+    // with a read loop that some lanes skip the compiler may issue those
+    // lanes' next writes first (each thread alone has no such dependence);
+    // the empty asm keeps the compiler from moving LDS accesses across rounds
+    constexpr int QB = 9, QP = 65;
+    static_assert(QB * QP <= 2 * SLOT, "a round fits the wave's ring");
+    float *rr = &ring[wave][0][0];
+    const int n_out = a.ppw * QB;
 #pragma unroll
-    for (int q = 0; q <= KK; ++q) {
-        float v = acc[q];
+    for (int r = 0; r * QB <= KK; ++r) {
 #pragma unroll
-        for (int st2 = 0; st2 < 6; ++st2) {
-            const int off = 32 >> st2;
-            const float o = __builtin_bit_cast(
-                float, __builtin_amdgcn_ds_bpermute(((lane + off) & 63) * 4,
-                                                    __builtin_bit_cast(int, v)));
-            v = keep[st2] ? v + o : v;
+        for (int qq = 0; qq < QB; ++qq)
+            if (r * QB + qq <= KK)
+                rr[qq * QP + lane] = acc[r * QB + qq];
+        for (int o0 = 0; o0 < n_out; o0 += 64) {
+            const int o = o0 + lane;
+            const bool live = o < n_out;
+            const int ps2 = live ? o / QB : 0, qq = live ? o - ps2 * QB : 0;
+            float v = 0.0f;
+            for (int l = 0; l < a.lpr; ++l)
+                v += rr[qq * QP + ps2 * a.lpr + l];
+            const int q = r * QB + qq, plane2 = pg * a.ppw + ps2;
+            if (live && q <= KK && plane2 < a.planes) {
+                const int n = plane2 / a.C, c = plane2 - n * a.C;
+                const int chunk = ((n * a.nph + ph) * a.nrt + rt) * a.ncb + cb;
+                part[((long long)chunk * a.C + c) * (KK + 1) + q] = v;
+            }
         }
-        acc[q] = v;
-    }
-    if (pok && cgl == 0) {
-        const int n = plane / a.C, c = plane - n * a.C;
-        const int chunk = ((n * a.nph + ph) * a.nrt + rt) * a.ncb + cb;
-        float *dstp = part + ((long long)chunk * a.C + c) * (KK + 1);
-#pragma unroll
-        for (int q = 0; q <= KK; ++q)
-            dstp[q] = acc[q];
+        asm volatile("" ::: "memory");
     }
 }
 
