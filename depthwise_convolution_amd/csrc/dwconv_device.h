@@ -311,6 +311,27 @@ __device__ __forceinline__ void epi_block(float (&v)[N], const EpiChan (&e)[NE],
     }
 }
 
+// The same epilogue with ReLU and ReLU6 taken by selects and one branch left,
+// for SiLU: for kernels that store a value or two per row, where a branch on
+// the activation at every store costs more than the selects (the results
+// are those of epi_block, NaN included).
+template <int N, int NE>
+__device__ __forceinline__ void epi_block_sel(float (&v)[N], const EpiChan (&e)[NE], int act)
+{
+    const bool clamp = act == DWCONV_ACT_RELU || act == DWCONV_ACT_RELU6;
+    const float hi = act == DWCONV_ACT_RELU6 ? 6.0f : __builtin_inff();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float t = fmaf(v[i] - e[i % NE].mu, e[i % NE].inv, e[i % NE].be);
+        v[i] = clamp ? fminf(fmaxf(t, 0.0f), hi) : t;
+    }
+    if (act == DWCONV_ACT_SILU) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = __fdividef(v[i], 1.0f + __expf(-v[i]));
+    }
+}
+
 template <int KH, int KW, int D, int Q, int G, bool V4>
 struct NchwGeom {
     static constexpr int R = (KH - 1) * D + 1;

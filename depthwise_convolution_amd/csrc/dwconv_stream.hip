@@ -184,7 +184,7 @@ __device__ __forceinline__ void stream_nhwc_tile(const float *__restrict__ in, c
             float (&v)[PX] = acc[m % KH];
             if constexpr (EPI) {
                 const EpiChan e1[1] = {ec};
-                epi_block(v, e1, ep.act);
+                epi_block_sel(v, e1, ep.act);
             }
             const int oh = ar + D * (i0 + m);
             const bool ok = oh < a.OH;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
             float (&v)[PX] = acc[m % KH];
             if constexpr (EPI) {
                 const EpiChan e1[1] = {ec};
-                epi_block(v, e1, ep.act);
+                epi_block_sel(v, e1, ep.act);
             }
             const int oh = ar + D * (i0 + m);
             const bool ok = oh < a.OH;
