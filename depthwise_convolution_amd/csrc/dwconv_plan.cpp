@@ -298,6 +298,25 @@ static int xcd_ranges(const Problem &p)
     return act < kXcdRangeMaxBytes ? 1 : 0;
 }
 
+// Channels per lane group of the row-streaming NHWC walks' tail tile (0 =
+// none) for 64-channel tiles: the last C % 64 channels, when they fill at
+// most half of a tile, run as a tile of 16 or 32 channels per lane group (4
+// or 2 column groups, so 4x or 2x fewer waves for them).  Measured at
+// 64x30x19xC 7x7 (forward, against full-width tiles only): 16 lanes win
+// 3-14% with at most one full tile or C % 4 == 0 (C = 3, 65, 67, 132, 136,
+// 144) but lose 3-12% with two or more full tiles and C % 4 != 0 (C =
+// 129-139), where 32 lanes win 9-10% (C = 129-139, 147, 150); with three or
+// more full tiles and odd C both lose (C = 195, 259: +4.5% with 32 lanes),
+// and with dilation 2 (the phase sub-grid is narrower than a 16-lane wave's
+// columns) they lose 2-8%.
+static int stream_tail_cl(const Problem &p, int d)
+{
+    const int rem = p.C % 64, full = p.C / 64;
+    if (rem == 0 || 2 * rem > 64 || d != 1 || full > 2)
+        return 0;
+    return (rem <= 16 && (p.C % 4 == 0 || full <= 1)) ? 16 : 32;
+}
+
 // Row-streaming NHWC kernel: stride 1, no multiplier, a listed kernel shape.
 // Any channel count and 4-byte alignment (4-byte loads and stores).
 static bool plan_stream_nhwc(const Problem &p, Plan *pl)
@@ -331,22 +350,7 @@ static bool plan_stream_nhwc(const Problem &p, Plan *pl)
     pl->cl = v.cl;
     pl->tw = v.px * (64 / v.cl);                  // output columns of a wave
     pl->th = v.th;
-    // the last C % cl channels, when they fill at most half of a tile, take a
-    // tail tile of 16 or 32 channels per lane group (4 or 2 column groups,
-    // so 4x or 2x fewer waves for them).  Measured at 64x30x19xC 7x7
-    // (forward, against full-width tiles only): 16 lanes win 3-14% with at
-    // most one full tile or C % 4 == 0 (C = 3, 65, 67, 132, 136, 144) but
-    // lose 3-12% with two or more full tiles and C % 4 != 0 (C = 129-139),
-    // where 32 lanes win 9-10% (C = 129-139, 147, 150); with three or more
-    // full tiles and odd C both lose (C = 195, 259: +4.5% with 32 lanes),
-    // and with dilation 2 (the phase sub-grid is narrower than a 16-lane
-    // wave's columns) they lose 2-8%.
-    const int rem = p.C % v.cl, full = p.C / v.cl;
-    pl->tail_cl = 0;
-    if (rem != 0 && 2 * rem <= v.cl && d == 1 && full <= 2)
-        pl->tail_cl = (rem <= 16 && (p.C % 4 == 0 || full <= 1)) ? 16 : 32;
-    if (pl->tail_cl >= v.cl)
-        pl->tail_cl = 0;
+    pl->tail_cl = v.cl == 64 ? stream_tail_cl(p, d) : 0;
     pl->nct = pl->tail_cl ? p.C / v.cl : ceil_div(p.C, v.cl);
     pl->nwt = ceil_div(ows, pl->tw);
     pl->nst = ceil_div(ohs, v.th);
@@ -730,7 +734,7 @@ static bool plan_wgrad_stream_nhwc(const Problem &p, Plan *pl)
     // byte offsets within a row (a lane's columns, up to (kW-1)*d past the
     // row on either side) and row starts within an image are 32-bit
     const long long cb = 4LL * p.C;
-    if (cb * (std::max(p.W, pl->OW) + 2LL * v.d * v.kW + 2LL * v.px * v.d) >= (1LL << 31) ||
+    if (cb * (std::max(p.W, pl->OW) + 2LL * v.d * v.kW + 8LL * v.px * v.d) >= (1LL << 31) ||
         cb * p.H * p.W >= (1LL << 31) || cb * pl->OH * pl->OW >= (1LL << 31))
         return false;
     const int d = v.d;
@@ -741,19 +745,28 @@ static bool plan_wgrad_stream_nhwc(const Problem &p, Plan *pl)
     pl->cl = 64;
     pl->tw = v.px;
     pl->th = v.th;
-    pl->nct = ceil_div(p.C, 64);
+    // leftover channels as a narrower tail tile, as in the forward walk; its
+    // workgroups write their partial sums into the first chunks and zeros
+    // into the rest of the tail channels' chunks
+    pl->tail_cl = stream_tail_cl(p, d);
+    pl->nct = pl->tail_cl ? p.C / 64 : ceil_div(p.C, 64);
     pl->nwt = ceil_div(ows, v.px);
     pl->nst = ceil_div(ohs, v.th);
     pl->pb = d * d;                               // phases
     pl->total = (long long)p.N * pl->nst * pl->pb * pl->nwt;      // wave units per channel tile
+    pl->tail_ncg = pl->tail_cl ? ceil_div(ows, v.px * (64 / pl->tail_cl)) : 0;
+    pl->tail_units = (long long)p.N * pl->nst * pl->pb * pl->tail_ncg;
     if (pl->total * 4 >= (1LL << 31))
         return false;
     pl->chunks = (pl->total + 3) / 4;             // one per workgroup of a channel tile
-    pl->grid = pl->nct * pl->chunks;
+    pl->grid = pl->nct * pl->chunks + (pl->tail_units + 3) / 4;
     pl->block = 256;
     pl->xcd = xcd_ranges(p);
-    std::snprintf(pl->name, sizeof pl->name, "wgrad_stream_nhwc_s1_k%dx%d_d%d_px%d_th%d", v.kH,
-                  v.kW, v.d, v.px, v.th);
+    char tail[8] = "";
+    if (pl->tail_cl)
+        std::snprintf(tail, sizeof tail, "_t%d", pl->tail_cl);
+    std::snprintf(pl->name, sizeof pl->name, "wgrad_stream_nhwc_s1_k%dx%d_d%d_px%d_th%d%s", v.kH,
+                  v.kW, v.d, v.px, v.th, tail);
     return true;
 }
 

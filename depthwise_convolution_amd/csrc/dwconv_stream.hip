@@ -466,29 +466,35 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
 // sums part[chunk][c][tap]; the fixed-order reduction kernel adds the
 // chunks.
 // ---------------------------------------------------------------------------
-template <int KH, int KW, int D, int PX, int TH, int NB>
-__global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restrict__ x,
-                                                           const float *__restrict__ dy,
-                                                           float *__restrict__ part,
-                                                           StreamArgs a)
+// One workgroup's work: 4 units of the channel tile starting at channel c0,
+// CL channels x 64/CL column groups per wave (ncg column blocks per
+// sub-grid row, upc units), summed into chunk `chunk` of the partial sums;
+// `zstep` > 0 (a tail tile) also writes zeros for its channels into chunks
+// chunk + zstep, chunk + 2 zstep, ... below nchunks, which hold no units of
+// that tile.  Every thread of the workgroup calls it (barriers).
+template <int KH, int KW, int D, int PX, int TH, int NB, int CL>
+__device__ __forceinline__ void wgrad_stream_nhwc_tile(const float *__restrict__ x,
+                                                       const float *__restrict__ dy,
+                                                       float *__restrict__ part,
+                                                       const StreamArgs &a, float *red, int c0,
+                                                       int unit, int ncg, int upc, int chunk,
+                                                       int zstep, int nchunks)
 {
     constexpr int KK = KH * KW, G = TH + KH - 1, XW = PX + KW - 1, KP = KK + 1;
     constexpr int RG = KH + NB - 1;                   // dy rows in registers
     constexpr int LP = 65;                            // LDS pitch of a sum row
     static_assert(NB >= 2, "at least one row in flight");
-    __shared__ float red[3][KP * LP];
-    const int blk = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-    const int ct = blk % a.nct;
+    static_assert(CL == 16 || CL == 32 || CL == 64, "channels per lane group");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // the wave's unit; a wave past the last unit adds zeros
-    const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 + wave);
-    const bool live = unit < a.upc;
-    const int c = ct * 64 + lane;
+    const int ch = lane % CL, cs = lane / CL;          // channel in the tile, column group
+    // a wave past the last unit adds zeros
+    const bool live = unit < upc;
+    const int c = c0 + ch;
     const bool cok = c < a.C;
     // the unit: column block (fastest), phase, row tile, image
     int t = live ? unit : 0;
-    const int cg = t % a.ncg;
-    t /= a.ncg;
+    const int cg = t % ncg;
+    t /= ncg;
     const int ph = t % a.nph;
     t /= a.nph;
     const int rt = t % a.nrt;
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restri
     const int ar = ph / D, ac = ph - (ph / D) * D;
     const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
     const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
-    const int i0 = rt * TH, j0 = cg * PX;
+    const int i0 = rt * TH, j0 = (cg * (64 / CL) + cs) * PX;
     int vin[XW], vg[PX];
 #pragma unroll
     for (int k = 0; k < XW; ++k)
@@ -571,24 +577,68 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restri
     if (wave > 0) {
 #pragma unroll
         for (int q = 0; q < KP; ++q)
-            red[wave - 1][q * LP + lane] = acc[q];
+            red[(wave - 1) * KP * LP + q * LP + lane] = acc[q];
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
         for (int q = 0; q < KP; ++q)
-            red[0][q * LP + lane] = ((acc[q] + red[0][q * LP + lane]) + red[1][q * LP + lane]) +
-                                    red[2][q * LP + lane];
+            red[q * LP + lane] = ((acc[q] + red[q * LP + lane]) + red[KP * LP + q * LP + lane]) +
+                                 red[2 * KP * LP + q * LP + lane];
     }
     __syncthreads();
-    // the chunk's channels c0 .. c0 + 63 are KP * 64 consecutive floats of part
-    const int chunk = blk / a.nct, c0 = ct * 64;
-    const int nc = min(64, a.C - c0);
+    // the chunk's channels c0 .. c0 + nc - 1 are KP * nc consecutive floats
+    // of part; a channel's 64 / CL column groups are added in group order
+    const int nc = min(CL, a.C - c0);
     float *dst = part + ((long long)chunk * a.C + c0) * KP;
     for (int e = threadIdx.x; e < nc * KP; e += 256) {
         const int cl = e / KP, q = e - cl * KP;
-        dst[e] = red[0][q * LP + cl];
+        float v = red[q * LP + cl];
+#pragma unroll
+        for (int g = 1; g < 64 / CL; ++g)
+            v += red[q * LP + g * CL + cl];
+        dst[e] = v;
     }
+    if (zstep > 0) {
+        for (int z = chunk + zstep; z < nchunks; z += zstep) {
+            float *zd = part + ((long long)z * a.C + c0) * KP;
+            for (int e = threadIdx.x; e < nc * KP; e += 256)
+                zd[e] = 0.0f;
+        }
+    }
+}
+
+// The kernel: main workgroups (the nct 64-channel tiles, chunk = the
+// workgroup's unit group) interleaved in proportion with those of the tail
+// tile of tcl < 64 channels, as in the forward walk.
+template <int KH, int KW, int D, int PX, int TH, int NB>
+__global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restrict__ x,
+                                                           const float *__restrict__ dy,
+                                                           float *__restrict__ part,
+                                                           StreamArgs a)
+{
+    __shared__ float red[3 * (KH * KW + 1) * 65];
+    const int L = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int bt = (int)gridDim.x - a.mblk;
+    const int blk = merged_block(L, a.mblk, bt);
+    const int wave = (int)(threadIdx.x >> 6);
+    const int nchunks = a.mblk / max(a.nct, 1);
+    if (blk >= 0) {
+        const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 + wave);
+        wgrad_stream_nhwc_tile<KH, KW, D, PX, TH, NB, 64>(x, dy, part, a, red, (blk % a.nct) * 64,
+                                                          unit, a.ncg, a.upc, blk / a.nct, 0,
+                                                          nchunks);
+        return;
+    }
+    const int j = -1 - blk;
+    const int unit = __builtin_amdgcn_readfirstlane(j * 4 + wave);
+    const int tchunks = (a.upc + 3) / 4;              // chunks of a full tile's units
+    if (a.tcl == 16)
+        wgrad_stream_nhwc_tile<KH, KW, D, PX, TH, NB, 16>(x, dy, part, a, red, a.nct * 64, unit,
+                                                          a.tncg, a.tupc, j, bt, tchunks);
+    else if (a.tcl == 32)
+        wgrad_stream_nhwc_tile<KH, KW, D, PX, TH, NB, 32>(x, dy, part, a, red, a.nct * 64, unit,
+                                                          a.tncg, a.tupc, j, bt, tchunks);
 }
 
 // ---------------------------------------------------------------------------
@@ -918,10 +968,14 @@ int launch_wgrad_stream_nhwc(const Problem &p, const Plan &pl, const float *x, c
                              float *part, hipStream_t st)
 {
     static const WgradStreamNhwcTable table;
+    const long long bt = (pl.tail_units + 3) / 4;
     if (p.mult != 1 || p.stride != 1 || pl.variant < 0 ||
         pl.variant >= kNumWgradStreamNhwcVariants || pl.cl != 64 ||
-        pl.chunks != (pl.total + 3) / 4 || pl.grid != pl.nct * pl.chunks)
-        return DWCONV_ERR_BAD_STRATEGY;
+        pl.chunks != (pl.total + 3) / 4 || pl.grid != pl.nct * pl.chunks + bt ||
+        (pl.tail_cl != 0 && pl.tail_cl != 16 && pl.tail_cl != 32) ||
+        (pl.tail_cl == 0) != (pl.tail_units == 0) || bt > pl.chunks ||
+        pl.nct * 64 + pl.tail_cl < p.C)
+        return DWCONV_ERR_BAD_STRATEGY;       // the tiles must cover the channels
     StreamArgs a;
     a.C = p.C;
     a.IH = p.H; a.IW = p.W; a.OH = pl.OH; a.OW = pl.OW;
@@ -929,8 +983,8 @@ int launch_wgrad_stream_nhwc(const Problem &p, const Plan &pl, const float *x, c
     a.nct = pl.nct; a.ncg = pl.nwt; a.nrt = pl.nst; a.nph = pl.pb;
     a.upc = (int)pl.total;
     a.xcd = pl.xcd;
-    a.mblk = (int)pl.grid;
-    a.tcl = a.tncg = a.tupc = 0;
+    a.mblk = (int)(pl.nct * pl.chunks);
+    a.tcl = pl.tail_cl; a.tncg = pl.tail_ncg; a.tupc = (int)pl.tail_units;
     return launch_kernel(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy,
                          part, a);
 }
