@@ -264,8 +264,14 @@ def test_weight_grad_workspace_and_plans():
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7,
                                       strategy=dw.STRATEGY_TILED)
     assert name.startswith("wgrad_tiled_nhwc") and "_l1_" in name    # any C, 4-byte staging
-    name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7)
+    name, grid, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 131, 7, 7)
     assert name.startswith("wgrad_stream_nhwc")                      # AUTO: enough waves
+    # two 64-channel tiles of 64 * 6 * 4 units (image, 5-row tile, 5-column
+    # block) and a 32-lane tail tile for the last 3 channels, whose waves span
+    # 2 column blocks (2 * 64 * 6 units), four units per workgroup
+    assert name.endswith("_t32") and grid == 2 * (64 * 6 * 4) // 4 + (64 * 6 * 2) // 4
+    name, grid, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 64, 30, 19, 128, 7, 7)
+    assert "_t" not in name.split("_th")[1] and grid == 2 * (64 * 6 * 4) // 4
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 30, 19, 131, 7, 7)
     assert name.startswith("wgrad_tiled_nhwc")                       # AUTO: too few waves
     name, _, _ = dw.dwconv2d_describe(dw.OP_WEIGHT_GRAD, 1, 224, 224, 32, 3, 3, stride=2)
