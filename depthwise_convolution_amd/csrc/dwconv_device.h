@@ -164,16 +164,18 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off)
 // `lds` is the same in every lane; an offset outside the buffer writes
 // zeros.  The data reaches LDS asynchronously: drain the wave's vector
 // memory counter (vm_drain) before the barrier that hands the tile to the
-// other waves.
-template <int BYTES>
+// other waves.  NT: the non-temporal cache policy (for data no other
+// workgroup reads).
+template <int BYTES, bool NT = false>
 __device__ __forceinline__ void buf_to_lds(__amdgpu_buffer_rsrc_t r, float *lds, int off)
 {
     static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte loads");
     auto *dst = (__attribute__((address_space(3))) void *)lds;
+    constexpr int aux = NT ? 2 : 0;
     if constexpr (BYTES == 4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, off, 0, 0, aux);
     else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, aux);
 }
 
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

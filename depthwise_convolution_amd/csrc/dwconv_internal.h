@@ -345,6 +345,8 @@ struct Plan {
     int xcd;            // tiled: 1 = each XCD takes a contiguous range of tiles, 2 = band-local
                         // runs (NHWC) or plane-group bands (NCHW forward / input gradient),
                         // 0 = in order
+    int ntl;            // tiled: 1 = a tile's rows that no other tile stages load
+                        // non-temporally (activations too large for the Infinity Cache)
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup
     int hl, twl;        // tiled NCHW: staged columns left of a tile, staged floats per row
     int nrt;            // weight gradient, tiled: row tiles per image / plane

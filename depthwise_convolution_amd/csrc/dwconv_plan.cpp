@@ -504,6 +504,12 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (tiled) {
         *pl = t;
         pl->xcd = xcd_ranges(p);
+        // tensors larger than the Infinity Cache stream past it: rows only
+        // one tile stages load non-temporally there (512x512x256 3x3 NHWC:
+        // 92.2 -> 88.5 us); smaller ones keep them (32x56x56x128 5x5 NHWC,
+        // whose buffers stay cache-resident between calls: 19.0 -> 25.8 us
+        // with them non-temporal)
+        pl->ntl = pl->kind == KIND_TILED_NHWC && !pl->xcd;
         // large problems: row bands split over the XCDs (NHWC), or bands of
         // 8 plane groups with one plane group's row tiles per XCD (NCHW)
         if (!pl->xcd && (pl->kind == KIND_TILED_NHWC ? (pl->nct * pl->nwt) % 8 == 0

@@ -32,6 +32,7 @@ struct TiledArgs {
     int nct, nwt, nst;      // channel tiles, column tiles, row tiles
     int xcd;                // tile order: 1 = per-XCD ranges (xcd_tile), 2 = band-local
                             // runs (band_tile), 0 = in order
+    int ntl;                // 1: staged rows that no other tile stages load non-temporally
 };
 
 // LV: floats per staging load, 4 (16-byte loads: C % 4 == 0, 16-byte
@@ -210,8 +211,17 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
             off = ok ? (int)uoff : kOutOfRange;
         }
         if constexpr (DMA) {
-            if ((i + 1) * 256 <= VCH || i * 256 + wel < VCH)   // the wave's run holds staged loads
-                buf_to_lds<4 * LV>(rx, ldsx + (i * 256 + wel) * LV, off);
+            if ((i + 1) * 256 <= VCH || i * 256 + wel < VCH) {  // the wave's run holds staged loads
+                // a wave whose loads all lie in rows R-1 .. TH-1 (rows the row
+                // tiles above and below do not stage; wave-uniform) may load
+                // them non-temporally: for tensors too large for the Infinity
+                // Cache it streams them past it
+                const int e0 = i * 256 + wel;
+                if (S == 1 && a.ntl && e0 / VPR >= R - 1 && (e0 + 63) / VPR <= TH - 1)
+                    buf_to_lds<4 * LV, true>(rx, ldsx + (i * 256 + wel) * LV, off);
+                else
+                    buf_to_lds<4 * LV>(rx, ldsx + (i * 256 + wel) * LV, off);
+            }
         } else if constexpr (LV == 4) {
             stage[i] = buf_f4(rx, off);
         } else {
@@ -420,6 +430,7 @@ int launch_tiled_nhwc(const Problem &p, const Plan &pl, const float *in, const v
     a.pH = pl.pH; a.pW = pl.pW;
     a.nct = pl.nct; a.nwt = pl.nwt; a.nst = pl.nst;
     a.xcd = pl.xcd;
+    a.ntl = pl.ntl;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }
