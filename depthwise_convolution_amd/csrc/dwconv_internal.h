@@ -161,6 +161,9 @@ constexpr int kStreamNchwSlot = 256;
 // (1x30x19x128 d2: 16.3 -> 13.2 us; d1 stays tiled there, 13.6 against
 // 16.0 us); half the rows per unit measured 12-40% slower.
 struct WgradStreamVariant { int kH, kW, d, th, nl, nb, minw; };
+// Waves above which a unit of the row-streaming NCHW weight gradient walks
+// all row phases of its column phase (dilation > 1).
+constexpr long long kWgradStreamPhaseWaves = 4096;
 constexpr WgradStreamVariant kWgradStreamVariants[] = {
     {7, 7, 1, 30, 2, 6, 1024}, {7, 7, 2, 15, 2, 6, 64},
 };
@@ -345,6 +348,7 @@ struct Plan {
     int xcd;            // tiled: 1 = each XCD takes a contiguous range of tiles, 2 = band-local
                         // runs (NHWC) or plane-group bands (NCHW forward / input gradient),
                         // 0 = in order
+    int rpu;            // row-streaming NCHW weight gradient: row phases a unit walks (1 or d)
     int ntl;            // tiled: 1 = a tile's rows that no other tile stages load
                         // non-temporally (activations too large for the Infinity Cache)
     int lds_bytes;      // tiled NCHW: dynamic LDS per workgroup

@@ -289,8 +289,10 @@ struct StreamNchwArgs {
     int pH, pW;             // top / left zero padding of the tensor read
     int lpr, ppw, pitch;    // lanes per plane row, planes per wave, staged columns per plane
     int lpitch;             // LDS floats per staged plane row (pitch rounded up to lpr mod 32)
-    int ncb, nrt, nph;      // column blocks (waves across a sub-grid row), row tiles, phases
-    int units;              // waves: plane groups * phases * row tiles * column blocks
+    int ncb, nrt, nph;      // column blocks (waves across a sub-grid row), row tiles, phase
+                            // units (phases / rpu)
+    int units;              // waves: plane groups * phase units * row tiles * column blocks
+    int rpu;                // weight gradient: row phases a unit walks in turn (1 or D)
 };
 
 __device__ __forceinline__ float buf_f32_s(__amdgpu_buffer_rsrc_t r, int off, int soff)
@@ -669,15 +671,19 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
     const int unit = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + wave);
     if (unit >= a.units)
         return;                                       // a whole wave; this kernel has no barrier
+    // the unit: column block, row tile, phase unit pu, plane group.  A phase
+    // unit is one phase (rpu = 1) or a column phase whose D row phases the
+    // unit walks in turn into the same tap sums (rpu = D: a phase is a set of
+    // positions, and the sums run over all of them)
     int t = unit;
     const int cb = t % a.ncb;
     t /= a.ncb;
     const int rt = t % a.nrt;
     t /= a.nrt;
-    const int ph = t % a.nph;
+    const int pu = t % a.nph;
     const int pg = t / a.nph;
-    const int ar = ph / D, ac = ph - (ph / D) * D;
-    const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+    const int rpu = D == 1 ? 1 : a.rpu;           // a compile-time single pass without dilation
+    const int ar0 = rpu == 1 ? pu / D : 0, ac = rpu == 1 ? pu - (pu / D) * D : pu;
     const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
     const int i0 = rt * TH, jb = cb * a.lpr;
 
@@ -694,67 +700,72 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
     }
     const int x_bytes = a.planes * a.IH * a.IW * 4, dy_bytes = a.planes * a.OH * a.OW * 4;
     float (*slots)[SLOT] = ring[wave];
-    float st[NB][NL];
-    auto load_x = [&](int g, float (&d)[NL]) {
-        const int ir = D * (i0 + tr + g) + br;
-        const bool ok = (unsigned)ir < (unsigned)a.IH;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(x, ok ? x_bytes : 0);
-        const int soff = ok ? ir * a.IW * 4 : 0;
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-            d[i] = buf_f32_s(r, src[i], soff);
-    };
-    // the lane's plane, its dy column, and its dy values (row m in gv[m % RG])
+    // the lane's plane, its dy column (row phases share it)
     const int ps = lane / a.lpr, cgl = lane - ps * a.lpr;
     const int plane = pg * a.ppw + ps;
     const bool pok = ps < a.ppw && plane < a.planes;
     const int rd = min(ps, a.ppw - 1) * a.lpitch + cgl;
     const int oc = ac + D * (jb + cgl);
     const int vg = pok && oc < a.OW ? (plane * a.OH * a.OW + oc) * 4 : kOutOfRange;
-    float gv[RG];
-    auto load_dy = [&](int m) {
-        const int oh = ar + D * (i0 + m);
-        const bool ok = m < TH && oh < a.OH;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(dy, ok ? dy_bytes : 0);
-        gv[m % RG] = buf_f32_s(r, vg, ok ? oh * a.OW * 4 : 0);
-    };
-#pragma unroll
-    for (int g = 0; g < NB - 1; ++g) {
-        load_x(g, st[g]);
-        load_dy(g);
-    }
     float acc[KK + 1];
 #pragma unroll
     for (int q = 0; q <= KK; ++q)
         acc[q] = 0.0f;
+#pragma unroll 1
+    for (int ar = ar0; ar < ar0 + rpu; ++ar) {
+        const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+        float st[NB][NL];
+        auto load_x = [&](int g, float (&d)[NL]) {
+            const int ir = D * (i0 + tr + g) + br;
+            const bool ok = (unsigned)ir < (unsigned)a.IH;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(x, ok ? x_bytes : 0);
+            const int soff = ok ? ir * a.IW * 4 : 0;
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
+            for (int i = 0; i < NL; ++i)
+                d[i] = buf_f32_s(r, src[i], soff);
+        };
+        // the lane's dy values of this row phase (row m in gv[m % RG])
+        float gv[RG];
+        auto load_dy = [&](int m) {
+            const int oh = ar + D * (i0 + m);
+            const bool ok = m < TH && oh < a.OH;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(dy, ok ? dy_bytes : 0);
+            gv[m % RG] = buf_f32_s(r, vg, ok ? oh * a.OW * 4 : 0);
+        };
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-            slots[u % 2][dst[i]] = st[u % NB][i];
-        if (u + NB - 1 < G) {
-            load_x(u + NB - 1, st[(u + NB - 1) % NB]);
-            if (u + NB - 1 < TH)
-                load_dy(u + NB - 1);
+        for (int g = 0; g < NB - 1; ++g) {
+            load_x(g, st[g]);
+            load_dy(g);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (u < TH)
-            acc[KK] += gv[u % RG];                    // the bias sum
-        // rows outside the planes are skipped (here, unlike the forward walk,
-        // running their FMAs on the zeros in LDS measured 256 registers)
-        const int ir = D * (i0 + tr + u) + br;
-        if ((unsigned)ir < (unsigned)a.IH) {
-            float xv[XW];
 #pragma unroll
-            for (int k = 0; k < XW; ++k)
-                xv[k] = slots[u % 2][rd + k];
+        for (int u = 0; u < G; ++u) {
 #pragma unroll
-            for (int kh = 0; kh < KH; ++kh) {
-                const int m = u - kh;                 // dy row this x row meets at tap row kh
-                if (m >= 0 && m < TH) {
+            for (int i = 0; i < NL; ++i)
+                slots[u % 2][dst[i]] = st[u % NB][i];
+            if (u + NB - 1 < G) {
+                load_x(u + NB - 1, st[(u + NB - 1) % NB]);
+                if (u + NB - 1 < TH)
+                    load_dy(u + NB - 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (u < TH)
+                acc[KK] += gv[u % RG];                    // the bias sum
+            // rows outside the planes are skipped (here, unlike the forward walk,
+            // running their FMAs on the zeros in LDS measured 256 registers)
+            const int ir = D * (i0 + tr + u) + br;
+            if ((unsigned)ir < (unsigned)a.IH) {
+                float xv[XW];
 #pragma unroll
-                    for (int kw = 0; kw < KW; ++kw)
-                        acc[kh * KW + kw] = fmaf(xv[kw], gv[m % RG], acc[kh * KW + kw]);
+                for (int k = 0; k < XW; ++k)
+                    xv[k] = slots[u % 2][rd + k];
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh) {
+                    const int m = u - kh;                 // dy row this x row meets at tap row kh
+                    if (m >= 0 && m < TH) {
+#pragma unroll
+                        for (int kw = 0; kw < KW; ++kw)
+                            acc[kh * KW + kw] = fmaf(xv[kw], gv[m % RG], acc[kh * KW + kw]);
+                    }
                 }
             }
         }
@@ -789,7 +800,7 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
             const int q = r * QB + qq, plane2 = pg * a.ppw + ps2;
             if (live && q <= KK && plane2 < a.planes) {
                 const int n = plane2 / a.C, c = plane2 - n * a.C;
-                const int chunk = ((n * a.nph + ph) * a.nrt + rt) * a.ncb + cb;
+                const int chunk = ((n * a.nph + pu) * a.nrt + rt) * a.ncb + cb;
                 part[((long long)chunk * a.C + c) * (KK + 1) + q] = v;
             }
         }
@@ -960,6 +971,7 @@ int launch_stream_nchw(const Problem &p, const Plan &pl, const float *in, const 
     a.lpr = pl.cl; a.ppw = pl.pb; a.pitch = pl.hl; a.lpitch = pl.twl;
     a.ncb = pl.nwt; a.nrt = pl.nst; a.nph = pl.nct;
     a.units = (int)pl.total;
+    a.rpu = 1;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }
@@ -1007,6 +1019,9 @@ int launch_wgrad_stream_nchw(const Problem &p, const Plan &pl, const float *x, c
     a.lpr = pl.cl; a.ppw = pl.pb; a.pitch = pl.hl; a.lpitch = pl.twl;
     a.ncb = pl.nwt; a.nrt = pl.nst; a.nph = pl.nct;
     a.units = (int)pl.total;
+    a.rpu = pl.rpu;
+    if (a.rpu != 1 && a.rpu != v.d)
+        return DWCONV_ERR_BAD_STRATEGY;
     return launch_kernel(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy,
                          part, a);
 }
