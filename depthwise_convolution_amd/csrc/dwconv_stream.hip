@@ -624,12 +624,10 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restri
     const int bt = (int)gridDim.x - a.mblk;
     const int blk = merged_block(L, a.mblk, bt);
     const int wave = (int)(threadIdx.x >> 6);
-    const int nchunks = a.mblk / max(a.nct, 1);
     if (blk >= 0) {
         const int unit = __builtin_amdgcn_readfirstlane((blk / a.nct) * 4 + wave);
         wgrad_stream_nhwc_tile<KH, KW, D, PX, TH, NB, 64>(x, dy, part, a, red, (blk % a.nct) * 64,
-                                                          unit, a.ncg, a.upc, blk / a.nct, 0,
-                                                          nchunks);
+                                                          unit, a.ncg, a.upc, blk / a.nct, 0, 0);
         return;
     }
     const int j = -1 - blk;
