@@ -559,3 +559,34 @@ def test_weight_grad_noalloc_rejects_before_touching_the_gpu(L):
     assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, None, dw.NHWC, 0, None) == -1
     assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, pads, 5, 0, None) == -6
     assert f(x, g, wgt, None, 1, 8, 8, 4, 1, 3, 3, 1, 1, pads, dw.NHWC, 9, None) == -12
+
+
+@pytest.mark.parametrize("C", [3, 16, 24, 32, 33, 40, 64, 65, 67, 96, 128, 129, 131, 132, 144,
+                               150, 160, 161, 195, 196, 259])
+@pytest.mark.parametrize("op", ["fwd", "wgrad"])
+def test_stream_tail_tile_rule(C, op):
+    """The row-streaming NHWC walks' tail tile, for 64x30x19xC 7x7: the last
+    C % 64 channels (at most 32 of them) run with 16 channels per lane group
+    when there is at most one full tile or C % 4 == 0, else with 32, and only
+    with dilation 1 and at most two full tiles (the measured region); the grid
+    is the full tiles' workgroups plus the tail's, whose waves span 64 / lanes
+    column blocks of 5 columns."""
+    opc = dw.OP_FWD if op == "fwd" else dw.OP_WEIGHT_GRAD
+    for d in (1, 2):
+        pads = tuple(dw.dwconv2d_same_pads(dw.PAD_SAME, 30, 19, 7, 7, 1, d))
+        name, grid, _ = dw.dwconv2d_describe_ex(opc, 64, 30, 19, C, 7, 7, 1, d, pads, 1, dw.NHWC,
+                                                0, op == "fwd", dw.STRATEGY_STREAM)
+        rem, full = C % 64, C // 64
+        tcl = 0
+        if rem and 2 * rem <= 64 and d == 1 and full <= 2:
+            tcl = 16 if rem <= 16 and (C % 4 == 0 or full <= 1) else 32
+        if tcl:
+            assert (f"_t{tcl}_" if op == "fwd" else f"_t{tcl}") in name, name
+        else:
+            assert "_t16" not in name and "_t32" not in name, name
+        th = 5 if d == 1 else 8
+        hs, ws = -(-30 // d), -(-19 // d)
+        units = 64 * -(-hs // th) * d * d * -(-ws // 5)
+        nct = full if tcl else -(-C // 64)
+        tunits = 64 * -(-hs // th) * d * d * -(-ws // (5 * 64 // tcl)) if tcl else 0
+        assert grid == nct * -(-units // 4) + -(-tunits // 4), (name, grid)
