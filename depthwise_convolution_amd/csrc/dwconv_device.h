@@ -290,8 +290,8 @@ __device__ __forceinline__ float apply_epi(float z, EpiChan e, int act)
 
 // The epilogue over a block of N values (value i of channel factors e[i % NE]),
 // with one branch on the activation for the whole block.  SiLU uses the
-// hardware exponential and reciprocal (a few ulp, far inside the tolerance
-// its tests derive).
+// hardware exponential and the compiler's fast division (a few ulp, far
+// inside the tolerance its tests derive).
 template <int N, int NE>
 __device__ __forceinline__ void epi_block(float (&v)[N], const EpiChan (&e)[NE], int act)
 {
