@@ -173,3 +173,35 @@ def test_stream_f16_weights_and_epilogue(torch, oracle_mod, layout, kd):
     ref, _ = oracle_mod.batchnorm_act(z, bn, 0.25, oracle_mod.ACT_RELU6, layout)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y.cpu().numpy(), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("C", [67, 144, 150])
+def test_stream_tail_tiles_full_size(torch, oracle_mod, C):
+    """The NHWC walks' tail tile at 64 images (thousands of workgroups, the
+    tail's interleaved among the full tiles' under per-XCD ranges): C = 67
+    (16 lanes after one full tile), 144 (16 lanes after two, C % 4 == 0) and
+    150 (32 lanes).  Forward, input gradient and weight gradient on integer
+    inputs, bit for bit against the oracle."""
+    N, H, W, k = 64, 30, 19, 7
+    wl = wlmod.Workload(name="tailfull", N=N, H=H, W=W, C=C, kH=k, kW=k)
+    pads = _pads("same", H, W, k, 1)
+    want = "_t16" if C in (67, 144) else "_t32"
+    names = [dw.dwconv2d_describe_ex(op, N, H, W, C, k, k, 1, 1, pads, 1, NHWC, 0,
+                                     op == dw.OP_FWD, dw.STRATEGY_AUTO)[0]
+             for op in (dw.OP_FWD, dw.OP_INPUT_GRAD, dw.OP_WEIGHT_GRAD)]
+    print(f"\n[case] tail full size C={C} kernels={names}", flush=True)
+    assert all(want in nm for nm in names), names
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    inp = wlmod.make_inputs(wl, NHWC, seed=C, integer=True)
+    y = dw.fwd(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), 1, 1, NHWC)
+    dx = dw.input_grad(dev(inp["dy"]), dev(inp["w"]), H, W, 1, 1, NHWC)
+    gW, gb = dw.weight_grad(dev(inp["x"]), dev(inp["dy"]), k, k, 1, 1, NHWC)
+    torch.cuda.synchronize()
+    ry, _ = oracle_mod.fwd(inp["x"], inp["w"], inp["b"], 1, 1, NHWC)
+    rdx, _ = oracle_mod.input_grad_general(inp["dy"], inp["w"], H, W, 1, 1, pads, 1, NHWC)
+    rW, _ = oracle_mod.weight_grad_general(inp["x"], inp["dy"], k, k, 1, 1, pads, 1, NHWC)
+    rb, _ = oracle_mod.bias_grad(inp["dy"], NHWC)
+    np.testing.assert_array_equal(y.cpu().numpy(), ry.astype(np.float32))
+    np.testing.assert_array_equal(dx.cpu().numpy(), rdx.astype(np.float32))
+    np.testing.assert_array_equal(gW.cpu().numpy(), rW.astype(np.float32))
+    np.testing.assert_array_equal(gb.cpu().numpy(), rb.astype(np.float32))
