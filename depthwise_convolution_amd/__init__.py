@@ -33,6 +33,7 @@ NHWC, NCHW = 0, 1
 W_F32, W_F16 = 0, 1
 OP_FWD, OP_INPUT_GRAD, OP_WEIGHT_GRAD = 0, 1, 2
 STRATEGY_AUTO, STRATEGY_DIRECT, STRATEGY_TILED, STRATEGY_STREAM = 0, 1, 2, 3
+STRATEGY_STREAM_PLANES = 4
 PAD_SAME, PAD_XLA_SAME = 0, 1
 ACT_NONE, ACT_RELU, ACT_RELU6, ACT_SILU = 0, 1, 2, 3
 STATUS = {

@@ -388,6 +388,9 @@ int launch_stream_nhwc(const Problem &p, const Plan &pl, const float *in, const 
                        const float *b, float *out, hipStream_t st, const EpiArgs &ep);
 int launch_stream_nchw(const Problem &p, const Plan &pl, const float *in, const void *w,
                        const float *b, float *out, hipStream_t st, const EpiArgs &ep);
+int launch_stream_nchw_planes(const Problem &p, const Plan &pl, const float *in,
+                              const void *w, const float *b, float *out, hipStream_t st,
+                              const EpiArgs &ep);
 int launch_wgrad_stream_nchw(const Problem &p, const Plan &pl, const float *x, const float *dy,
                              float *part, hipStream_t st);
 int launch_wgrad_stream_nhwc(const Problem &p, const Plan &pl, const float *x, const float *dy,

@@ -56,6 +56,8 @@ enum Kind {
     KIND_STREAM_NCHW = 9,  // the same with lanes along plane columns, rows staged per wave
     KIND_WGRAD_STREAM_NCHW = 10, // weight gradient, NCHW stride 1: the NCHW row walk, tap sums per lane
     KIND_WGRAD_STREAM_NHWC = 11, // weight gradient, NHWC stride 1: the NHWC row walk, tap sums per lane
+    KIND_STREAM_NCHW_PLANES = 12, // NCHW stride 1, many taps: the NHWC walk with one plane per lane,
+                                  // rows and output rows transposed through LDS
 };
 
 // Compile-time variants of the tiled NHWC kernel.  A tiled plan exists only
@@ -148,6 +150,25 @@ constexpr StreamNchwVariant kStreamNchwVariants[] = {
     {7, 7, 1, 1, 30, 2, 6, 1024}, {7, 7, 2, 1, 15, 2, 6, 64},
 };
 constexpr int kNumStreamNchwVariants = sizeof(kStreamNchwVariants) / sizeof(kStreamNchwVariants[0]);
+
+// Variants of the plane-per-lane NCHW kernel (stride 1, no multiplier): a
+// wave takes 16 planes x 4 lane groups of `px` columns (4*px output columns)
+// and `th` output rows of one row phase; it stages a row's in-image columns
+// with `nl` loads per lane (so planes at most 4*nl columns wide, or the
+// staged window if narrower, take the variant), `nb` rows ahead; AUTO takes
+// the first variant that fits from `minw` waves (kNever: never).
+// Measured on MI355X (64x30x19x128 7x7, rocprof medians, forward), against
+// the lane-along-columns kernel: dilation 2 14.5 against 16.2 us; dilation 1
+// 14.8 against 14.3 us, so AUTO keeps the other kernel there.  3 or 4 rows
+// ahead instead of 2, and 6 rows per unit instead of 5, measured the same.
+constexpr int kNever = 1 << 30;
+struct StreamPlanesVariant { int kH, kW, d, px, th, nl, nb, minw; };
+constexpr StreamPlanesVariant kStreamPlanesVariants[] = {
+    {7, 7, 1, 5, 5, 5, 2, kNever}, {7, 7, 1, 5, 5, 7, 2, kNever},
+    {7, 7, 2, 5, 5, 5, 2, 1024}, {7, 7, 2, 5, 5, 8, 2, 1024},
+};
+constexpr int kNumStreamPlanesVariants =
+    sizeof(kStreamPlanesVariants) / sizeof(kStreamPlanesVariants[0]);
 
 // LDS floats of one staged row slot of the row-streaming NCHW kernel (the
 // planes of a wave, each at a bank-spreading pitch).

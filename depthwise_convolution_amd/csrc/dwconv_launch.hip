@@ -29,6 +29,8 @@ int launch_plan(const Problem &p, const Plan &pl, const float *in, const void *w
         return launch_stream_nhwc(p, pl, in, w, bb, out, stream, ep);
     case KIND_STREAM_NCHW:
         return launch_stream_nchw(p, pl, in, w, bb, out, stream, ep);
+    case KIND_STREAM_NCHW_PLANES:
+        return launch_stream_nchw_planes(p, pl, in, w, bb, out, stream, ep);
     default:
         return DWCONV_ERR_BAD_STRATEGY;
     }

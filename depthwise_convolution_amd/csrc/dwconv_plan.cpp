@@ -437,6 +437,58 @@ static bool plan_stream_nchw(const Problem &p, Plan *pl)
     return true;
 }
 
+// Plane-per-lane NCHW kernel: stride 1, no multiplier, a listed kernel
+// shape, 4-byte alignment.
+static bool plan_stream_nchw_planes(const Problem &p, Plan *pl)
+{
+    if (p.layout != DWCONV_LAYOUT_NCHW || p.stride != 1 || p.mult != 1 ||
+        p.op == DWCONV_OP_WEIGHT_GRAD)
+        return false;
+    // the first variant whose loads cover a window's in-image columns for
+    // 16 planes (a window spans 4*px + d*(kW-1) columns)
+    int best = -1;
+    for (int i = 0; i < kNumStreamPlanesVariants; ++i) {
+        const StreamPlanesVariant &v = kStreamPlanesVariants[i];
+        const int win = std::min(4 * v.px + v.d * (v.kW - 1), pl->IW);
+        if (v.kH == p.kH && v.kW == p.kW && v.d == p.dilation && 16 * win <= 64 * v.nl) {
+            best = i;
+            break;
+        }
+    }
+    if (best < 0)
+        return false;
+    const StreamPlanesVariant &v = kStreamPlanesVariants[best];
+    const long long planes = (long long)p.N * p.C;
+    // byte offsets into the whole tensor are 32-bit (and below the
+    // out-of-range offset), plane indices too
+    if (4LL * (planes + 64) * pl->IH * pl->IW >= (1LL << 31) ||
+        4LL * (planes + 64) * pl->OH * pl->OW >= (1LL << 31) ||
+        4LL * p.C * p.kH * p.kW >= (1LL << 31))
+        return false;
+    pl->kind = KIND_STREAM_NCHW_PLANES;
+    pl->variant = best;
+    pl->vec = 1;
+    pl->cl = 16;                                  // planes per wave
+    pl->tw = 4 * v.px;                            // output columns of a wave
+    pl->th = v.th;
+    pl->nct = (int)((planes + 15) / 16);          // plane groups
+    pl->nwt = ceil_div(pl->OW, pl->tw);           // column blocks
+    pl->nst = ceil_div(ceil_div(pl->OH, v.d), v.th);   // row tiles per row phase
+    pl->pb = v.d;                                 // row phases
+    pl->YH = pl->OH;
+    pl->YW = pl->OW;
+    pl->total = (long long)pl->nct * v.d * pl->nst * pl->nwt;   // waves
+    if (pl->total * 64 >= (1LL << 31))
+        return false;
+    pl->grid = (pl->total + 3) / 4;
+    pl->block = 256;
+    pl->xcd = xcd_ranges(p);
+    std::snprintf(pl->name, sizeof pl->name,
+                  "stream_nchw_planes_s1_k%dx%d_d%d_px%d_th%d_nl%d_%s_%s", v.kH, v.kW, v.d,
+                  v.px, v.th, v.nl, op_tag(p), p.wtype ? "f16w" : "f32w");
+    return true;
+}
+
 static void plan_direct(const Problem &p, std::uintptr_t ptr_bits, Plan *pl)
 {
     // channels of the tensor written: mult*C for the forward, C for the input gradient
@@ -466,7 +518,8 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
     if (st != DWCONV_OK)
         return st;
     if (strategy != DWCONV_STRATEGY_AUTO && strategy != DWCONV_STRATEGY_DIRECT &&
-        strategy != DWCONV_STRATEGY_TILED && strategy != DWCONV_STRATEGY_STREAM)
+        strategy != DWCONV_STRATEGY_TILED && strategy != DWCONV_STRATEGY_STREAM &&
+        strategy != DWCONV_STRATEGY_STREAM_PLANES)
         return DWCONV_ERR_BAD_STRATEGY;
     std::memset(pl, 0, sizeof *pl);
     set_extents(p, pl);
@@ -478,10 +531,19 @@ int make_plan(Problem &p, int strategy, std::uintptr_t ptr_bits, Plan *pl)
         return (p.layout == DWCONV_LAYOUT_NHWC ? plan_stream_nhwc(p, pl) : plan_stream_nchw(p, pl))
                    ? DWCONV_OK
                    : DWCONV_ERR_BAD_STRATEGY;
-    // AUTO: the row-streaming kernel for the windows it has variants for,
-    // when the problem gives enough waves
+    if (strategy == DWCONV_STRATEGY_STREAM_PLANES)
+        return plan_stream_nchw_planes(p, pl) ? DWCONV_OK : DWCONV_ERR_BAD_STRATEGY;
+    // AUTO: the row-streaming kernels for the windows they have variants
+    // for, when the problem gives enough waves (NCHW: one plane per lane
+    // first)
     if (strategy == DWCONV_STRATEGY_AUTO) {
         Plan t = *pl;
+        if (plan_stream_nchw_planes(p, &t) &&
+            t.total >= kStreamPlanesVariants[t.variant].minw) {
+            *pl = t;
+            return DWCONV_OK;
+        }
+        t = *pl;
         const bool nhwc = p.layout == DWCONV_LAYOUT_NHWC;
         if (nhwc ? plan_stream_nhwc(p, &t) : plan_stream_nchw(p, &t)) {
             const long long waves = nhwc ? t.nct * t.total + t.tail_units : t.total;

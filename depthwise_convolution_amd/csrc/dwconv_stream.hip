@@ -455,6 +455,255 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
 }
 
 // ---------------------------------------------------------------------------
+// Plane-per-lane NCHW walk (stride 1): the NHWC walk's lanes on NCHW data.
+// A wave takes 16 consecutive planes (n, c) x 4 lane groups, TH output rows
+// of one row phase, and a block of 4*PX output columns; lane group cg is
+// column phase cg % D and the PX adjacent sub-grid columns (cg / D)*PX ..
+// of that phase.  Each lane then runs the NHWC walk: kH rolling accumulators
+// per column, PX + kW - 1 staged columns per input row, kH*kW*PX FMAs per
+// row.  Waves are independent units (no barrier).
+//
+// The transposes go through the wave's own LDS.  A plane's row segment is
+// a contiguous run in NCHW, so the wave loads each input row of its 16
+// planes as consecutive (plane, column) elements over the in-image columns
+// of its window only: coalesced runs, loaded NB rows before the row is
+// staged.  The row goes to one of three LDS slots (plane p at p*SP, whose
+// columns outside the image were zeroed once) two rows before its FMAs, and
+// its taps are read into registers one row before them; SP (4 mod 8) puts
+// the 64 lanes' taps in 64 different banks.  Completed
+// output rows go the other way: each lane writes its PX columns into a row
+// buffer (plane p at p*4*PX), and the wave reads it back in (plane, column)
+// order and stores contiguous runs.  A wave's LDS operations run in order,
+// so no barrier is needed.
+//
+// Zero padding: rows outside the image are neither staged nor folded in (a
+// wave-uniform branch).  Stores of rows past OH, columns past OW and planes
+// past the last go through out-of-range offsets and are dropped.
+// ---------------------------------------------------------------------------
+struct StreamPlanesArgs {
+    int C, planes;          // channels; planes (n, c) of both tensors
+    int IH, IW, OH, OW;     // plane extents of the tensor read and the tensor written
+    int pH, pW;             // top / left zero padding of the tensor read
+    int ncb, nrt;           // column blocks of 4*PX output columns, row tiles per phase
+    int units;              // waves: plane groups * D row phases * nrt * ncb
+    int xcd;                // 1: per-XCD ranges of workgroups (xcd_tile)
+};
+
+// True when lane l = 4*ps + cg reading staged column D*k + (cg % D) +
+// D*(cg / D)*PX of plane ps (plane pitch SP) hits 64 different banks for
+// every tap k.
+constexpr bool planes_pitch_ok(int sp, int d, int px, int xw)
+{
+    for (int k = 0; k < xw; ++k) {
+        unsigned long long seen = 0;
+        for (int l = 0; l < 64; ++l) {
+            const int cg = l % 4, ps = l / 4;
+            const int a = ps * sp + cg % d + d * (cg / d) * px + d * k;
+            const unsigned long long bit = 1ull << (a % 64);
+            if (seen & bit)
+                return false;
+            seen |= bit;
+        }
+    }
+    return true;
+}
+
+template <typename WT, int KH, int KW, int D, int PX, int TH, int NL, int NB, int MODE>
+__global__ __launch_bounds__(256) void k_stream_nchw_planes(const float *__restrict__ in,
+                                                            const void *__restrict__ wv,
+                                                            const float *__restrict__ bias,
+                                                            float *__restrict__ out,
+                                                            StreamPlanesArgs a, EpiArgs ep)
+{
+    constexpr bool IG = MODE == kModeInputGrad, EPI = MODE == kModeFwdEpilogue;
+    constexpr int KK = KH * KW, G = TH + KH - 1, XW = PX + KW - 1;
+    static_assert(4 % D == 0, "the 4 lane groups split into D column phases");
+    static_assert(NB >= 2, "at least one row in flight");
+    constexpr int BW = 4 * PX;                        // output columns of the block
+    constexpr int WS = BW + D * (KW - 1);             // staged columns
+    constexpr int SP = (WS + 3) / 8 * 8 + 4;          // LDS floats per staged plane row
+    static_assert(planes_pitch_ok(SP, D, PX, XW), "tap reads free of bank conflicts");
+    constexpr int SLOT = 16 * SP + 64;                // + where unused staging lanes write
+    constexpr int NSLOT = 3;                          // row u read, u + 1 in LDS, u + 2 written
+    static_assert(NL >= 1 && 64 * NL <= 16 * WS + 63, "staging loads per lane and row");
+    constexpr int OB = 16 * BW;                       // row buffer: plane p at p*BW
+    static_assert(OB % 64 == 0, "the row buffer is whole wave loads");
+    __shared__ float lds[4][NSLOT * SLOT + OB];
+    const WT *w = reinterpret_cast<const WT *>(wv);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = a.xcd ? xcd_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int unit = __builtin_amdgcn_readfirstlane(blk * 4 + wave);
+    if (unit >= a.units)
+        return;                                       // a whole wave; this kernel has no barrier
+    float *slots = lds[wave], *obuf = lds[wave] + NSLOT * SLOT;
+
+    // the unit: column block (fastest), row tile, row phase, plane group
+    int t = unit;
+    const int cb = t % a.ncb;
+    t /= a.ncb;
+    const int rt = t % a.nrt;
+    t /= a.nrt;
+    const int ar = t % D;
+    const int p0 = (t / D) * 16;                      // first plane
+    const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
+    const int i0 = rt * TH, oc0 = cb * BW, s0 = oc0 - a.pW;
+    // in-image columns of the window: [lo, hi), staged at lo - s0 ..
+    const int lo = max(s0, 0), hi = min(s0 + WS, a.IW);
+    const int cnt = max(hi - lo, 0), nel = 16 * cnt;
+    const int in_bytes = a.planes * a.IH * a.IW * 4, out_bytes = a.planes * a.OH * a.OW * 4;
+
+    // staging: element e = lane + 64*i is in-image column lo + e % cnt of
+    // plane e / cnt; it goes to LDS float (e / cnt)*SP + lo - s0 + e % cnt
+    // (the plan makes 64*NL >= 16*cnt; elements past that read zero and go
+    // to the slot's spare floats)
+    int src[NL], dst[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = lane + 64 * i, sp = cnt ? e / cnt : 0, col = e - sp * cnt;
+        const bool ok = e < nel && p0 + sp < a.planes;
+        src[i] = ok ? ((p0 + sp) * a.IH * a.IW + lo + col) * 4 : kOutOfRange;
+        dst[i] = e < nel ? sp * SP + lo - s0 + col : 16 * SP + lane;
+    }
+    float st[NB][NL];
+    auto row_ok = [&](int g) {
+        return (unsigned)(D * (i0 + tr + g) + br) < (unsigned)a.IH;
+    };
+    auto load_row = [&](int g, float (&v)[NL]) {
+        const int ir = D * (i0 + tr + g) + br;
+        const bool ok = (unsigned)ir < (unsigned)a.IH;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(in, ok ? in_bytes : 0);
+        const int soff = ok ? ir * a.IW * 4 : 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            v[i] = buf_f32_s(r, src[i], soff);
+    };
+    auto stage_row = [&](int g, const float (&v)[NL]) {
+        float *sl = slots + (g % 3) * SLOT;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            sl[dst[i]] = v[i];
+    };
+#pragma unroll
+    for (int g = 0; g < NB && g < G; ++g)
+        load_row(g, st[g]);
+
+    // the lane's plane, channel and columns
+    const int ps = lane >> 2, cg = lane & 3;
+    const int plane = p0 + ps;
+    const bool pok = plane < a.planes;
+    const int c = pok ? plane % a.C : 0;
+    const int ac = cg % D, gq = cg / D;
+    const int rb = ps * SP + ac + D * gq * PX;        // staged column of tap 0
+    const int ob = ps * BW + ac + D * gq * PX;        // row-buffer float of column 0
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, a.C * KK * (int)sizeof(WT));
+    const int wb = pok ? c * KK : kOutOfRange / 4;
+    float wr[KH][KW];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+            const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
+            wr[kh][kw] = buf_w(rw, wb + tap, (WT *)nullptr);
+        }
+    const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
+                                   : 0.0f;
+    EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
+    if constexpr (EPI) {
+        ec = epi_load(ep, pok ? c : a.C, a.C);
+        epi_finish(ec, ep);
+    }
+    // the lane's share of a row-buffer store: float f = lane + 64*i is
+    // column f % BW of plane f / BW
+    constexpr int NST = OB / 64;
+    int sof[NST];
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+        const int f = lane + 64 * i, sp = f / BW, oc = oc0 + f - sp * BW;
+        sof[i] = p0 + sp < a.planes && oc < a.OW ? ((p0 + sp) * a.OH * a.OW + oc) * 4
+                                                : kOutOfRange;
+    }
+
+    // zero the slots once: columns outside the image are never written
+    for (int i = lane; i < NSLOT * SLOT; i += 64)
+        slots[i] = 0.0f;
+    float acc[KH][PX];
+#pragma unroll
+    for (int r = 0; r < KH; ++r)
+#pragma unroll
+        for (int jj = 0; jj < PX; ++jj)
+            acc[r][jj] = bv;
+    // a row's taps are read from LDS one row before its FMAs, so their
+    // latency hides behind the FMAs of the row before
+    float xr[2][XW];
+    auto read_taps = [&](int g, float (&x)[XW]) {
+        const float *sl = slots + (g % 3) * SLOT + rb;
+#pragma unroll
+        for (int k = 0; k < XW; ++k)
+            x[k] = sl[D * k];
+    };
+    // row g's registers are st[g % NB]: row g + NB loads as soon as row g is
+    // staged, NB rows before it is staged itself
+#pragma unroll
+    for (int g = 0; g < 2 && g < G; ++g) {
+        if (row_ok(g))
+            stage_row(g, st[g % NB]);
+        if (g + NB < G)
+            load_row(g + NB, st[g % NB]);
+    }
+    if (row_ok(0))
+        read_taps(0, xr[0]);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        // row u + 2 into its slot and row u + 2 + NB into its registers; row
+        // u + 1's taps on their way
+        if (u + 2 < G && row_ok(u + 2))
+            stage_row(u + 2, st[(u + 2) % NB]);
+        if (u + 2 + NB < G)
+            load_row(u + 2 + NB, st[(u + 2) % NB]);
+        if (u + 1 < G && row_ok(u + 1))
+            read_taps(u + 1, xr[(u + 1) % 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (row_ok(u)) {
+            const float (&x)[XW] = xr[u % 2];
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+                const int m = u - kh;
+                if (m >= 0 && m < TH) {
+#pragma unroll
+                    for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                        for (int jj = 0; jj < PX; ++jj)
+                            acc[m % KH][jj] = fmaf(wr[kh][kw], x[jj + kw], acc[m % KH][jj]);
+                }
+            }
+        }
+        const int m = u - (KH - 1);                   // output row completed by row u
+        if (m >= 0) {
+            float (&v)[PX] = acc[m % KH];
+            if constexpr (EPI) {
+                const EpiChan e1[1] = {ec};
+                epi_block_sel(v, e1, ep.act);
+            }
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                obuf[ob + D * jj] = v[jj];
+#pragma unroll
+            for (int jj = 0; jj < PX; ++jj)
+                v[jj] = bv;
+            const int oh = ar + D * (i0 + m);
+            const bool ok = oh < a.OH;
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, ok ? out_bytes : 0);
+            const int soff = ok ? oh * a.OW * 4 : 0;
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(unsigned, obuf[lane + 64 * i]), ro, sof[i], soff,
+                    kStreamNchwStoreAux);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Row-streaming NHWC weight gradient (stage 1): the NHWC walk's waves (64
 // channels, one per lane, x PX output columns x TH output rows of one
 // dilation phase) with the roles of the operands changed (LeanMlir
@@ -862,6 +1111,43 @@ struct StreamNchwTable {
     }
 };
 
+typedef void (*StreamPlanesFn)(const float *, const void *, const float *, float *,
+                               StreamPlanesArgs, EpiArgs);
+
+template <typename WT, int V, int MODE>
+constexpr StreamPlanesFn stream_planes_fn()
+{
+    constexpr StreamPlanesVariant t = kStreamPlanesVariants[V];
+    return &k_stream_nchw_planes<WT, t.kH, t.kW, t.d, t.px, t.th, t.nl, t.nb, MODE>;
+}
+
+template <int V>
+void fill_stream_planes(StreamPlanesFn (&row)[2][3])
+{
+    row[0][0] = stream_planes_fn<float, V, kModeFwd>();
+    row[0][1] = stream_planes_fn<float, V, kModeInputGrad>();
+    row[0][2] = stream_planes_fn<float, V, kModeFwdEpilogue>();
+    row[1][0] = stream_planes_fn<half_t, V, kModeFwd>();
+    row[1][1] = stream_planes_fn<half_t, V, kModeInputGrad>();
+    row[1][2] = stream_planes_fn<half_t, V, kModeFwdEpilogue>();
+}
+
+template <int... Vs>
+void fill_all_stream_planes(StreamPlanesFn (&fn)[kNumStreamPlanesVariants][2][3],
+                            std::integer_sequence<int, Vs...>)
+{
+    (fill_stream_planes<Vs>(fn[Vs]), ...);
+}
+
+struct StreamPlanesTable {
+    StreamPlanesFn fn[kNumStreamPlanesVariants][2][3];
+    StreamPlanesTable()
+    {
+        fill_all_stream_planes(fn,
+                               std::make_integer_sequence<int, kNumStreamPlanesVariants>());
+    }
+};
+
 typedef void (*StreamFn)(const float *, const void *, const float *, float *, StreamArgs,
                          EpiArgs);
 
@@ -970,6 +1256,39 @@ int launch_stream_nchw(const Problem &p, const Plan &pl, const float *in, const 
     a.ncb = pl.nwt; a.nrt = pl.nst; a.nph = pl.nct;
     a.units = (int)pl.total;
     a.rpu = 1;
+    return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
+                         p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
+}
+
+int launch_stream_nchw_planes(const Problem &p, const Plan &pl, const float *in,
+                              const void *w, const float *b, float *out, hipStream_t st,
+                              const EpiArgs &ep)
+{
+    static const StreamPlanesTable table;
+    if (p.mult != 1 || p.stride != 1 || pl.variant < 0 || pl.variant >= kNumStreamPlanesVariants)
+        return DWCONV_ERR_BAD_STRATEGY;
+    const StreamPlanesVariant &v = kStreamPlanesVariants[pl.variant];
+    const long long planes = (long long)p.N * p.C;
+    auto cdiv = [](int x, int y) { return (x + y - 1) / y; };
+    // the loads must cover a window's in-image columns for 16 planes
+    const int win = 4 * v.px + v.d * (v.kW - 1);
+    if (16 * (pl.IW < win ? pl.IW : win) > 64 * v.nl)
+        return DWCONV_ERR_BAD_STRATEGY;
+    // the workgroups must cover every plane group, row phase, row tile and
+    // column block of the tensor written
+    if (pl.tw != 4 * v.px || pl.th != v.th || pl.nwt != cdiv(pl.OW, pl.tw) ||
+        pl.nst != cdiv(cdiv(pl.OH, v.d), v.th) ||
+        pl.total != (planes + 15) / 16 * v.d * pl.nst * pl.nwt || pl.grid != (pl.total + 3) / 4)
+        return DWCONV_ERR_BAD_STRATEGY;
+    StreamPlanesFn f = table.fn[pl.variant][p.wtype == DWCONV_W_F16][mode_of(p, ep)];
+    StreamPlanesArgs a;
+    a.C = p.C;
+    a.planes = (int)planes;
+    a.IH = pl.IH; a.IW = pl.IW; a.OH = pl.OH; a.OW = pl.OW;
+    a.pH = pl.pH; a.pW = pl.pW;
+    a.ncb = pl.nwt; a.nrt = pl.nst;
+    a.units = (int)pl.total;
+    a.xcd = pl.xcd;
     return launch_kernel(f, dim3((unsigned)pl.grid), dim3(256), 0, st, in, w,
                          p.op == DWCONV_OP_FWD ? b : nullptr, out, a, ep);
 }

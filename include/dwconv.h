@@ -108,6 +108,13 @@ extern "C" {
                                     forward and input gradient (both layouts) and the
                                     NCHW weight gradient, for the kernel shapes it has
                                     variants for (7x7, dilation 1 or 2)            */
+#define DWCONV_STRATEGY_STREAM_PLANES 4 /* NCHW only: the NHWC row walk with one plane
+                                    per lane group (16 planes x 4 column groups per
+                                    wave), input rows and output rows transposed
+                                    through the wave's LDS; stride 1
+                                    without a multiplier, forward and input gradient,
+                                    for the kernel shapes it has variants for (7x7,
+                                    dilation 1 or 2)                              */
 
 /*
  * Forward.  x: input [N,H,W,C] / [N,C,H,W] float32.  w: [C][kH][kW] of type

@@ -220,6 +220,33 @@ def test_stream_grid_covers_problem(wl_name):
     assert 1 <= -(-wl.N * wl.C // max(1, 64 // lpr)) <= grid * 4
 
 
+@pytest.mark.parametrize("shape,d", [((64, 30, 19, 128), 1), ((64, 30, 19, 128), 2),
+                                     ((64, 30, 19, 131), 2), ((2, 13, 19, 131), 1),
+                                     ((1, 9, 150, 3), 2), ((3, 40, 41, 5), 1)])
+def test_stream_planes_plan(shape, d):
+    """The plane-per-lane NCHW plan: one wave per 16 planes x row phase x
+    row tile x 20-column block, four waves per workgroup; the staging loads
+    per lane cover 16 planes' in-image window columns (5 loads when the
+    window or the plane is at most 20 columns wide); AUTO takes it at
+    dilation 2 from 1024 waves and never at dilation 1."""
+    N, H, W, C = shape
+    pads = tuple(dw.dwconv2d_same_pads(dw.PAD_SAME, H, W, 7, 7, 1, d))
+    for op in (dw.OP_FWD, dw.OP_INPUT_GRAD):
+        name, grid, block = dw.dwconv2d_describe_ex(op, N, H, W, C, 7, 7, 1, d, pads, 1, dw.NCHW,
+                                                    0, op == dw.OP_FWD,
+                                                    dw.STRATEGY_STREAM_PLANES)
+        assert name.startswith(f"stream_nchw_planes_s1_k7x7_d{d}_px5_th5_") and block == 256
+        th = 5
+        waves = -(-N * C // 16) * d * -(-(-(-H // d)) // th) * -(-W // 20)
+        assert grid == -(-waves // 4)
+        win = min(20 + 6 * d, W)
+        nl = int(re.search(r"_nl(\d+)_", name).group(1))
+        assert nl == (5 if 16 * win <= 320 else (7 if d == 1 else 8))
+        auto = dw.dwconv2d_describe_ex(op, N, H, W, C, 7, 7, 1, d, pads, 1, dw.NCHW, 0,
+                                       op == dw.OP_FWD, dw.STRATEGY_AUTO)[0]
+        assert auto.startswith("stream_nchw_planes_") == (d == 2 and waves >= 1024)
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 4, 4, 4)

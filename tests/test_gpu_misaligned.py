@@ -18,7 +18,7 @@ from depthwise_convolution_amd.workloads import NHWC, NCHW
 pytestmark = pytest.mark.gpu
 LNAME = {NHWC: "nhwc", NCHW: "nchw"}
 STRATS = {"auto": dw.STRATEGY_AUTO, "direct": dw.STRATEGY_DIRECT, "tiled": dw.STRATEGY_TILED,
-          "stream": dw.STRATEGY_STREAM}
+          "stream": dw.STRATEGY_STREAM, "planes": dw.STRATEGY_STREAM_PLANES}
 # (kH, kW, dilation); N=2, H=19, W=20 spans several tiles with a ragged tail,
 # C=36 fills a 16-byte-staged NHWC channel tile when aligned, W % 4 == 0 gives
 # the NCHW 16-byte rows when aligned
@@ -84,7 +84,7 @@ def test_misaligned_views_match_oracle(torch, oracle_mod, layout, k, op, strat, 
             N, H, W, C, kH, kW, dilation=d, layout=layout, has_bias=op == "fwd", strategy=st,
             addr_bits=4 * off)[0]
     except dw.DwconvError as e:
-        if e.status == -12 and strat == "stream":
+        if e.status == -12 and strat in ("stream", "planes"):
             pytest.skip("no streaming kernel for this problem")
         raise
     print(f"\n[case] {what} kernel={name}", flush=True)

@@ -33,8 +33,9 @@ NTHREADS = max(1, min(16, os.cpu_count() or 1))
 def _table(src, name, nfields):
     body = src[src.index(name + "[] = {"):]
     body = body[:body.index("};")]
-    pat = r"\{" + r",\s*".join([r"(-?\d+)"] * nfields) + r"\}"
-    return [tuple(int(v) for v in m.groups()) for m in re.finditer(pat, body)]
+    pat = r"\{" + r",\s*".join([r"(-?\d+|kNever)"] * nfields) + r"\}"
+    return [tuple(-1 if v == "kNever" else int(v) for v in m.groups())
+            for m in re.finditer(pat, body)]
 
 
 def _expected_prefixes():
@@ -68,6 +69,9 @@ def _expected_prefixes():
         out[f"stream_nhwc_s1_k{kh}x{kw}_d{d}_cl{cl}_px{px}_th{th}_"] = "kStreamVariants"
     for kh, kw, d, px, th, nl, nb, minw in _table(src, "kStreamNchwVariants", 8):
         out[f"stream_nchw_s1_k{kh}x{kw}_d{d}_px{px}_th{th}_nl{nl}_"] = "kStreamNchwVariants"
+    for kh, kw, d, px, th, nl, nb, minw in _table(src, "kStreamPlanesVariants", 8):
+        out[f"stream_nchw_planes_s1_k{kh}x{kw}_d{d}_px{px}_th{th}_nl{nl}_"] = \
+            "kStreamPlanesVariants"
     for kh, kw, d, th, nl, nb, minw in _table(src, "kWgradStreamVariants", 7):
         out[f"wgrad_stream_nchw_s1_k{kh}x{kw}_d{d}_th{th}_nl{nl}_"] = "kWgradStreamVariants"
     for kh, kw, d, px, th, nb, minw in _table(src, "kWgradStreamNhwcVariants", 7):
@@ -91,7 +95,8 @@ def _sweep():
                                 continue
                             pads = dw.dwconv2d_same_pads(dw.PAD_SAME, h, w, kh, kw, s, d)
                             for op in (dw.OP_FWD, dw.OP_INPUT_GRAD, dw.OP_WEIGHT_GRAD):
-                                for st in (dw.STRATEGY_TILED, dw.STRATEGY_STREAM):
+                                for st in (dw.STRATEGY_TILED, dw.STRATEGY_STREAM,
+                                           dw.STRATEGY_STREAM_PLANES):
                                     try:
                                         name = dw.dwconv2d_describe_ex(
                                             op, 1, h, w, c, kh, kw, s, d, pads, m, layout, 0,
