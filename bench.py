@@ -536,6 +536,7 @@ def _row_matcher(dw, wl, layout, op):
         opc == dw.OP_FWD)
     fam = {"tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
            "stream_nhwc": "k_stream_nhwc", "stream_nchw": "k_stream_nchw",
+           "stream_nchw_planes": "k_stream_nchw_planes",
            "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
            "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc", "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
            "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_stream_nhwc": "k_wgrad_stream_nhwc",
