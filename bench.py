@@ -11,7 +11,8 @@ weight gradient and the fused ops in both layouts, each against its HBM or
 VALU floor, an empty-launch floor and a same-bytes copy, and the oracle's
 time on all cores and on one), the practical ceilings, the weight-gradient,
 fused and graph legs -- goes to a JSON detail file (--detail, default
-gpurun_out/bench_detail.json) and, one line per row, to stderr.
+dwconv_bench_detail.json in the system's temporary directory) and, one line
+per row, to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-table] [--no-cpu]
                        [--detail PATH] [--table-only] [--calib-copy]
@@ -898,7 +899,8 @@ def main():
                     help="only the per-workload table (for a profiler run)")
     ap.add_argument("--workloads", default="",
                     help="comma-separated workload names for the table (default: all)")
-    ap.add_argument("--detail", default=os.path.join("gpurun_out", "bench_detail.json"))
+    ap.add_argument("--detail",
+                    default=os.path.join(tempfile.gettempdir(), "dwconv_bench_detail.json"))
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     ap.add_argument("--trace-table", default="", help="summarise a kernel-trace CSV and exit")
