@@ -44,6 +44,7 @@
 
 #include <cstdint>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "dwconv_internal.h"
@@ -276,6 +277,79 @@ __device__ __forceinline__ void epi_finish(EpiChan &e, const EpiArgs &ep)
         e.inv = e.inv / sqrtf(e.var + ep.eps);
 }
 
+// The tiled and row-streaming kernels fold the affine step into the
+// channel's weights and bias once per thread: act(inv*(sum w*x + b - mu) +
+// be) = act(sum (w*inv)*x + ((b - mu)*inv + be)), the same quantity in
+// another rounding order, so that each output pays for the activation only.
+__device__ __forceinline__ float epi_fold_bias(float b, const EpiChan &e)
+{
+    return fmaf(b - e.mu, e.inv, e.be);
+}
+
+// The fold for a thread of one channel: its taps and its bias.
+template <int KH, int KW>
+__device__ __forceinline__ void epi_fold(float (&wr)[KH][KW], float &bv, const EpiChan &e)
+{
+    bv = epi_fold_bias(bv, e);
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+            wr[kh][kw] *= e.inv;
+}
+
+// The activation alone (after the fold), fixed at compile time.  SiLU uses
+// the hardware exponential and the compiler's fast division (a few ulp, far
+// inside the tolerance its tests derive).
+template <int ACT, int N>
+__device__ __forceinline__ void epi_act_c(float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if constexpr (ACT == DWCONV_ACT_RELU)
+            v[i] = fmaxf(v[i], 0.0f);
+        else if constexpr (ACT == DWCONV_ACT_RELU6)
+            v[i] = fminf(fmaxf(v[i], 0.0f), 6.0f);
+        else if constexpr (ACT == DWCONV_ACT_SILU)
+            v[i] = __fdividef(v[i], 1.0f + __expf(-v[i]));
+    }
+}
+
+// Calls f(std::integral_constant<int, act>) for the run-time activation, so
+// that a kernel holds one copy of its walk per activation instead of a
+// branch at every store.
+template <typename F>
+__device__ __forceinline__ void with_act(int act, F &&f)
+{
+    if (act == DWCONV_ACT_RELU)
+        f(std::integral_constant<int, DWCONV_ACT_RELU>());
+    else if (act == DWCONV_ACT_RELU6)
+        f(std::integral_constant<int, DWCONV_ACT_RELU6>());
+    else if (act == DWCONV_ACT_SILU)
+        f(std::integral_constant<int, DWCONV_ACT_SILU>());
+    else
+        f(std::integral_constant<int, DWCONV_ACT_NONE>());
+}
+
+// The activation alone (after the fold): ReLU and ReLU6 by selects, one
+// branch for SiLU (same results as epi_act_c, NaN included): the
+// row-streaming walks, whose fully unrolled walks are too long to hold one
+// copy per activation.
+template <int N>
+__device__ __forceinline__ void epi_act_sel(float (&v)[N], int act)
+{
+    const bool clamp = act == DWCONV_ACT_RELU || act == DWCONV_ACT_RELU6;
+    const float hi = act == DWCONV_ACT_RELU6 ? 6.0f : __builtin_inff();
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = clamp ? fminf(fmaxf(v[i], 0.0f), hi) : v[i];
+    if (act == DWCONV_ACT_SILU) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = __fdividef(v[i], 1.0f + __expf(-v[i]));
+    }
+}
+
 __device__ __forceinline__ EpiChan epi_chan(const EpiArgs &ep, int c, int channels)
 {
     EpiChan e = epi_load(ep, c, channels);
@@ -286,52 +360,6 @@ __device__ __forceinline__ EpiChan epi_chan(const EpiArgs &ep, int c, int channe
 __device__ __forceinline__ float apply_epi(float z, EpiChan e, int act)
 {
     return apply_act(fmaf(z - e.mu, e.inv, e.be), act);
-}
-
-// The epilogue over a block of N values (value i of channel factors e[i % NE]),
-// with one branch on the activation for the whole block.  SiLU uses the
-// hardware exponential and the compiler's fast division (a few ulp, far
-// inside the tolerance its tests derive).
-template <int N, int NE>
-__device__ __forceinline__ void epi_block(float (&v)[N], const EpiChan (&e)[NE], int act)
-{
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        v[i] = fmaf(v[i] - e[i % NE].mu, e[i % NE].inv, e[i % NE].be);
-    if (act == DWCONV_ACT_RELU) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            v[i] = fmaxf(v[i], 0.0f);
-    } else if (act == DWCONV_ACT_RELU6) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            v[i] = fminf(fmaxf(v[i], 0.0f), 6.0f);
-    } else if (act == DWCONV_ACT_SILU) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            v[i] = __fdividef(v[i], 1.0f + __expf(-v[i]));
-    }
-}
-
-// The same epilogue with ReLU and ReLU6 taken by selects and one branch left,
-// for SiLU: for kernels that store a value or two per row, where a branch on
-// the activation at every store costs more than the selects (the results
-// are those of epi_block, NaN included).
-template <int N, int NE>
-__device__ __forceinline__ void epi_block_sel(float (&v)[N], const EpiChan (&e)[NE], int act)
-{
-    const bool clamp = act == DWCONV_ACT_RELU || act == DWCONV_ACT_RELU6;
-    const float hi = act == DWCONV_ACT_RELU6 ? 6.0f : __builtin_inff();
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const float t = fmaf(v[i] - e[i % NE].mu, e[i % NE].inv, e[i % NE].be);
-        v[i] = clamp ? fminf(fmaxf(t, 0.0f), hi) : t;
-    }
-    if (act == DWCONV_ACT_SILU) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            v[i] = __fdividef(v[i], 1.0f + __expf(-v[i]));
-    }
 }
 
 template <int KH, int KW, int D, int Q, int G, bool V4>

@@ -132,8 +132,8 @@ __device__ __forceinline__ void stream_nhwc_tile(const float *__restrict__ in, c
 #pragma unroll
     for (int i = 0; i < NWL; ++i)
         wst[i] = buf_w(rw, c0 * KK + (int)threadIdx.x + i * 256, (WT *)nullptr);
-    const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), cok ? c * 4 : kOutOfRange)
-                                   : 0.0f;
+    float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), cok ? c * 4 : kOutOfRange)
+                             : 0.0f;
     EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
     if constexpr (EPI)
         ec = epi_load(ep, cok ? c : a.C, a.C);
@@ -149,8 +149,10 @@ __device__ __forceinline__ void stream_nhwc_tile(const float *__restrict__ in, c
 #pragma unroll
         for (int kw = 0; kw < KW; ++kw)
             wr[kh][kw] = wl[ch * KK + (IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw)];
-    if constexpr (EPI)
+    if constexpr (EPI) {
         epi_finish(ec, ep);
+        epi_fold(wr, bv, ec);
+    }
 
     // 3. walk the rows
     float acc[KH][PX];
@@ -182,10 +184,8 @@ __device__ __forceinline__ void stream_nhwc_tile(const float *__restrict__ in, c
         const int m = u - (KH - 1);                   // output row completed by row u
         if (m >= 0) {
             float (&v)[PX] = acc[m % KH];
-            if constexpr (EPI) {
-                const EpiChan e1[1] = {ec};
-                epi_block_sel(v, e1, ep.act);
-            }
+            if constexpr (EPI)
+                epi_act_sel(v, ep.act);
             const int oh = ar + D * (i0 + m);
             const bool ok = oh < a.OH;
             const __amdgpu_buffer_rsrc_t ro =
@@ -391,12 +391,13 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
             const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
             wr[kh][kw] = buf_w(rw, wb + tap, (WT *)nullptr);
         }
-    const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
-                                   : 0.0f;
+    float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
+                             : 0.0f;
     EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
     if constexpr (EPI) {
         ec = epi_load(ep, pok ? c : a.C, a.C);
         epi_finish(ec, ep);
+        epi_fold(wr, bv, ec);
     }
     float acc[KH][PX];
 #pragma unroll
@@ -435,10 +436,8 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
         const int m = u - (KH - 1);
         if (m >= 0) {
             float (&v)[PX] = acc[m % KH];
-            if constexpr (EPI) {
-                const EpiChan e1[1] = {ec};
-                epi_block_sel(v, e1, ep.act);
-            }
+            if constexpr (EPI)
+                epi_act_sel(v, ep.act);
             const int oh = ar + D * (i0 + m);
             const bool ok = oh < a.OH;
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, ok ? out_bytes : 0);
@@ -605,12 +604,13 @@ __global__ __launch_bounds__(256) void k_stream_nchw_planes(const float *__restr
             const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
             wr[kh][kw] = buf_w(rw, wb + tap, (WT *)nullptr);
         }
-    const float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
-                                   : 0.0f;
+    float bv = (!IG && bias) ? buf_f32(make_rsrc(bias, a.C * 4), pok ? c * 4 : kOutOfRange)
+                             : 0.0f;
     EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
     if constexpr (EPI) {
         ec = epi_load(ep, pok ? c : a.C, a.C);
         epi_finish(ec, ep);
+        epi_fold(wr, bv, ec);
     }
     // the lane's share of a row-buffer store: float f = lane + 64*i is
     // column f % BW of plane f / BW
@@ -680,10 +680,8 @@ __global__ __launch_bounds__(256) void k_stream_nchw_planes(const float *__restr
         const int m = u - (KH - 1);                   // output row completed by row u
         if (m >= 0) {
             float (&v)[PX] = acc[m % KH];
-            if constexpr (EPI) {
-                const EpiChan e1[1] = {ec};
-                epi_block_sel(v, e1, ep.act);
-            }
+            if constexpr (EPI)
+                epi_act_sel(v, ep.act);
 #pragma unroll
             for (int jj = 0; jj < PX; ++jj)
                 obuf[ob + D * jj] = v[jj];

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     const int pli = min(pli_raw, pbn - 1);             // in-range LDS addresses for idle threads
     const int my_plane = pg * pbn + pli;
     const bool pvalid = pli_raw < pbn && my_plane < a.planes;
-    const float bval = buf_f32(rb, pvalid ? (my_plane % a.C) * 4 : kOutOfRange);
+    float bval = buf_f32(rb, pvalid ? (my_plane % a.C) * 4 : kOutOfRange);
     EpiChan ec{0.0f, 1.0f, 0.0f, 0.0f};
     if constexpr (EPI)
         ec = epi_load(ep, pvalid ? my_plane % a.C : a.C, a.C);
@@ -254,8 +254,17 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
                 const int tap = IG ? (KH - 1 - kh) * KW + (KW - 1 - kw) : kh * KW + kw;
                 wr[jm][kh][kw] = ldsw[(pli * M + jm) * KK + tap];
             }
-    if constexpr (EPI)
+    if constexpr (EPI) {
         epi_finish(ec, ep);
+        bval = epi_fold_bias(bval, ec);
+#pragma unroll
+        for (int jm = 0; jm < M; ++jm)
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw)
+                    wr[jm][kh][kw] *= ec.inv;
+    }
     float acc[R][Q];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -269,6 +278,10 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
     // Q-wide stores need an 8-byte aligned output (Q = 2) and whole vectors
     // per row (OW % Q == 0 keeps every plane and row start on a vector)
     const bool vec_store = !DEC && (Q > 1) && (a.OW % Q == 0) && a.ost8;
+    // the walk, with the activation of the fused epilogue as a constant:
+    // one copy of the walk per activation, no branch at the stores
+    auto walk = [&](auto act_c) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -297,10 +310,8 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
             }
             const int m = u - (R - 1);
             if (m >= 0) {
-                if constexpr (EPI) {
-                    const EpiChan e1[1] = {ec};
-                    epi_block(acc[m % R], e1, ep.act);
-                }
+                if constexpr (EPI)
+                    epi_act_c<ACT>(acc[m % R]);
                 const int r = h0 + m;
                 float *dst = outp + r * a.OW + oc;
                 if constexpr (DEC) {
@@ -329,6 +340,11 @@ __global__ __launch_bounds__(256) void k_tiled_nchw(const float *__restrict__ in
             }
         }
     }
+    };
+    if constexpr (EPI)
+        with_act(ep.act, walk);
+    else
+        walk(std::integral_constant<int, DWCONV_ACT_NONE>());
 }
 
 typedef void (*TiledNchwFn)(const float *, const void *, const float *, float *, TiledNchwArgs,

@@ -268,8 +268,15 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
             }
     if constexpr (EPI) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
+        for (int v = 0; v < VEC; ++v) {
             epi_finish(ec[v], ep);
+            bv[v] = epi_fold_bias(bv[v], ec[v]);
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw)
+                    wr[kh][kw][v] *= ec[v].inv;
+        }
     }
     float acc[R][PX][VEC];
 #pragma unroll
@@ -286,6 +293,10 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
     // this thread's first output of the tile's first row (not DEC, not IG with M > 1)
     float *orow = outp + ((h0 * a.OW + ow) * a.CW + cq);
     const int ors = a.OW * a.CW;
+    // the walk, with the activation of the fused epilogue as a constant:
+    // one copy of the walk per activation, no branch at the stores
+    auto walk = [&](auto act_c) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         if (u < nrows) {
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
 #pragma unroll
                 for (int j = 0; j < PX; ++j) {
                     if constexpr (EPI)
-                        epi_block(acc[m % R][j], ec, ep.act);
+                        epi_act_c<ACT>(acc[m % R][j]);
                     if constexpr (DEC) {
                         const int c = ow + j;
                         if (cvalid && (r & 1) == 0 && (c & 1) == 0 && (c >> 1) < a.YW)
@@ -350,6 +361,11 @@ __global__ __launch_bounds__(256) void k_tiled_nhwc(const float *__restrict__ in
             }
         }
     }
+    };
+    if constexpr (EPI)
+        with_act(ep.act, walk);
+    else
+        walk(std::integral_constant<int, DWCONV_ACT_NONE>());
 }
 
 typedef void (*TiledFn)(const float *, const void *, const float *, float *, TiledArgs,
