@@ -469,11 +469,11 @@ __global__ __launch_bounds__(256) void k_stream_nchw(const float *__restrict__ i
 // staged.  The row goes to one of three LDS slots (plane p at p*SP, whose
 // columns outside the image were zeroed once) two rows before its FMAs, and
 // its taps are read into registers one row before them; SP (4 mod 8) puts
-// the 64 lanes' taps in 64 different banks.  Completed
-// output rows go the other way: each lane writes its PX columns into a row
-// buffer (plane p at p*4*PX), and the wave reads it back in (plane, column)
-// order and stores contiguous runs.  A wave's LDS operations run in order,
-// so no barrier is needed.
+// the 64 lanes' taps in 64 different banks.  Completed output rows go the
+// other way: each lane writes its PX columns into a row buffer (plane p at
+// p*4*PX), and the wave reads it back in (plane, column) order and stores
+// contiguous runs.  A wave's LDS operations run in order, so no barrier is
+// needed.
 //
 // Zero padding: rows outside the image are neither staged nor folded in (a
 // wave-uniform branch).  Stores of rows past OH, columns past OW and planes
