@@ -900,7 +900,7 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nhwc(const float *__restri
 // KK + 1 sums are written as a chunk of the partial sums part[chunk][c][tap], chunk = the unit's (image, phase, row tile,
 // column block); the fixed-order reduction kernel adds the chunks.
 // ---------------------------------------------------------------------------
-template <int KH, int KW, int D, int TH, int NL, int NB>
+template <int KH, int KW, int D, int TH, int NL, int NB, int RPU>
 __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restrict__ x,
                                                            const float *__restrict__ dy,
                                                            float *__restrict__ part,
@@ -927,7 +927,8 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
     t /= a.nrt;
     const int pu = t % a.nph;
     const int pg = t / a.nph;
-    const int rpu = D == 1 ? 1 : a.rpu;           // a compile-time single pass without dilation
+    static_assert(RPU == 1 || RPU == D, "one row phase or all of them");
+    constexpr int rpu = RPU;
     const int ar0 = rpu == 1 ? pu / D : 0, ac = rpu == 1 ? pu - (pu / D) * D : pu;
     const int tc = floor_div(ac - a.pW, D), bc = ac - a.pW - D * tc;
     const int i0 = rt * TH, jb = cb * a.lpr;
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
 #pragma unroll
     for (int q = 0; q <= KK; ++q)
         acc[q] = 0.0f;
-#pragma unroll 1
+#pragma unroll
     for (int ar = ar0; ar < ar0 + rpu; ++ar) {
         const int tr = floor_div(ar - a.pH, D), br = ar - a.pH - D * tr;
         float st[NB][NL];
@@ -1055,18 +1056,24 @@ __global__ __launch_bounds__(256) void k_wgrad_stream_nchw(const float *__restri
 
 typedef void (*WgradStreamFn)(const float *, const float *, float *, StreamNchwArgs);
 
-template <int... Vs>
-void fill_wgrad_stream(WgradStreamFn (&fn)[kNumWgradStreamVariants],
-                       std::integer_sequence<int, Vs...>)
+template <int V>
+void fill_wgrad_stream_row(WgradStreamFn (&row)[2])
 {
-    ((fn[Vs] = &k_wgrad_stream_nchw<kWgradStreamVariants[Vs].kH, kWgradStreamVariants[Vs].kW,
-                                    kWgradStreamVariants[Vs].d, kWgradStreamVariants[Vs].th,
-                                    kWgradStreamVariants[Vs].nl, kWgradStreamVariants[Vs].nb>),
-     ...);
+    constexpr WgradStreamVariant t = kWgradStreamVariants[V];
+    row[0] = &k_wgrad_stream_nchw<t.kH, t.kW, t.d, t.th, t.nl, t.nb, 1>;
+    row[1] = &k_wgrad_stream_nchw<t.kH, t.kW, t.d, t.th, t.nl, t.nb, t.d>;
 }
 
+template <int... Vs>
+void fill_wgrad_stream(WgradStreamFn (&fn)[kNumWgradStreamVariants][2],
+                       std::integer_sequence<int, Vs...>)
+{
+    (fill_wgrad_stream_row<Vs>(fn[Vs]), ...);
+}
+
+// [variant][0: one row phase per unit, 1: all d row phases per unit]
 struct WgradStreamTable {
-    WgradStreamFn fn[kNumWgradStreamVariants];
+    WgradStreamFn fn[kNumWgradStreamVariants][2];
     WgradStreamTable()
     {
         fill_wgrad_stream(fn, std::make_integer_sequence<int, kNumWgradStreamVariants>());
@@ -1337,7 +1344,8 @@ int launch_wgrad_stream_nchw(const Problem &p, const Plan &pl, const float *x, c
     a.rpu = pl.rpu;
     if (a.rpu != 1 && a.rpu != v.d)
         return DWCONV_ERR_BAD_STRATEGY;
-    return launch_kernel(table.fn[pl.variant], dim3((unsigned)pl.grid), dim3(256), 0, st, x, dy,
+    return launch_kernel(table.fn[pl.variant][a.rpu == 1 ? 0 : 1], dim3((unsigned)pl.grid),
+                         dim3(256), 0, st, x, dy,
                          part, a);
 }
 
