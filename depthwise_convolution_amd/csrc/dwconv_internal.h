@@ -180,13 +180,15 @@ constexpr int kStreamNchwSlot = 256;
 // AUTO takes it from `minw` waves.  Measured (both stages, 64x30x19x128):
 // 7x7 31.3 -> 25.6 us against the tiled kernel, 7x7 d2 53.3 -> 38.4 us
 // (1x30x19x128 d2: 16.3 -> 13.2 us; d1 stays tiled there, 13.6 against
-// 16.0 us); half the rows per unit measured 12-40% slower.
+// 16.0 us); half the rows per unit measured 12-40% slower.  4 rows in
+// flight instead of 6 (stage 1, same-box A/B): d1 17.4 -> 16.9 us, d2 19.8
+// -> 19.1 us (3 or 5: d2 19.2, 19.5 us).
 struct WgradStreamVariant { int kH, kW, d, th, nl, nb, minw; };
 // Waves above which a unit of the row-streaming NCHW weight gradient walks
 // all row phases of its column phase (dilation > 1).
 constexpr long long kWgradStreamPhaseWaves = 4096;
 constexpr WgradStreamVariant kWgradStreamVariants[] = {
-    {7, 7, 1, 30, 2, 6, 1024}, {7, 7, 2, 15, 2, 6, 64},
+    {7, 7, 1, 30, 2, 4, 1024}, {7, 7, 2, 15, 2, 4, 64},
 };
 constexpr int kNumWgradStreamVariants =
     sizeof(kWgradStreamVariants) / sizeof(kWgradStreamVariants[0]);
