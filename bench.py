@@ -520,6 +520,23 @@ def headline_extras(torch, dw, wl, t, layout, stream, n_rep=40):
 
 
 # ------------------------------------------------------------------ trace table
+# plan-name prefix -> the HIP kernel (family) that runs it
+PLAN_KERNEL_FAMILIES = {
+    "tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
+    "stream_nhwc": "k_stream_nhwc", "stream_nchw": "k_stream_nchw",
+    "stream_nchw_planes": "k_stream_nchw_planes",
+    "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
+    "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc", "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
+    "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_stream_nhwc": "k_wgrad_stream_nhwc",
+    "wgrad_direct": "k_wgrad_gen"}
+
+
+def kernel_family(plan_name):
+    """The kernel family of a plan name (longest matching prefix), or None."""
+    return next((v for k, v in sorted(PLAN_KERNEL_FAMILIES.items(), key=lambda kv: -len(kv[0]))
+                 if plan_name.startswith(k)), None)
+
+
 def _row_matcher(dw, wl, layout, op):
     """The kernel name the plan of (workload, layout, op) reports and a
     predicate on a trace's (kernel name, grid size in threads) that accepts
@@ -535,15 +552,7 @@ def _row_matcher(dw, wl, layout, op):
         opc, wl.N, wl.H, wl.W, wl.C, wl.kH, wl.kW, wl.stride, wl.dilation, wl.pads,
         wl.mult, layout, 0 if opc == dw.OP_WEIGHT_GRAD else int(wl.fp16_weights),
         opc == dw.OP_FWD)
-    fam = {"tiled_nhwc": "k_tiled_nhwc", "tiled_nchw": "k_tiled_nchw",
-           "stream_nhwc": "k_stream_nhwc", "stream_nchw": "k_stream_nchw",
-           "stream_nchw_planes": "k_stream_nchw_planes",
-           "direct_nhwc": "k_direct_nhwc", "direct_nchw": "k_direct_nchw",
-           "wgrad_tiled_nhwc": "k_wgrad_tiled_nhwc", "wgrad_tiled_nchw": "k_wgrad_tiled_nchw",
-           "wgrad_stream_nchw": "k_wgrad_stream_nchw", "wgrad_stream_nhwc": "k_wgrad_stream_nhwc",
-           "wgrad_direct": "k_wgrad_gen"}
-    kfam = next((v for k, v in sorted(fam.items(), key=lambda kv: -len(kv[0]))
-                 if kname.startswith(k)), None)
+    kfam = kernel_family(kname)
     # the tiled and streaming kernels' mode: 0 forward, 1 input gradient,
     # 2 forward with the BatchNorm + activation epilogue
     want = {"fwd": "0", "ig": "1", "fwd_bn_relu6": "2"}.get(op)

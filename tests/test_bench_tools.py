@@ -129,3 +129,31 @@ def test_detail_table_renders_every_row(tmp_path):
     text = bench.detail_table(str(detail))
     assert text.count("| w1 | nhwc |") == 3
     assert "100.0 (16)" in text and "Launch floor: empty kernel back to back 1.5 us" in text
+
+
+def test_every_bench_row_plan_has_a_kernel_family():
+    """Every plan the per-workload table runs (each workload, layout and op,
+    and each kernel the strategies can select for the 7x7 windows) names a
+    kernel family the trace and counter summaries know, so no row is left
+    without its kernel."""
+    names = set()
+    for wl in workloads.WORKLOADS.values():
+        for layout in (workloads.NHWC, workloads.NCHW):
+            for op in bench.OPS:
+                if op.startswith("wgrad") and wl.fp16_weights:
+                    continue
+                names.add(bench._row_matcher(dw, wl, layout, op)[0])
+    for st in (dw.STRATEGY_TILED, dw.STRATEGY_STREAM, dw.STRATEGY_STREAM_PLANES,
+               dw.STRATEGY_DIRECT):
+        for d in (1, 2):
+            for layout in (workloads.NHWC, workloads.NCHW):
+                try:
+                    names.add(dw.dwconv2d_describe(dw.OP_FWD, 64, 30, 19, 128, 7, 7, 1, d, layout,
+                                                   strategy=st)[0])
+                except dw.DwconvError:
+                    pass
+    missing = sorted(n for n in names if bench.kernel_family(n) is None)
+    assert not missing, missing
+    assert bench.kernel_family("stream_nchw_planes_s1_k7x7_d2_px5_th5_nl5_fwd_f32w") == \
+        "k_stream_nchw_planes"
+
